@@ -1,0 +1,56 @@
+"""The oracle's pins are not vacuous: each plausible mistake planted in a copy
+of the oracle (on the CPU) must make tests/test_oracle_pins.py fail."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = {
+    "silu_prime_dropped": ("return s * (1.0 + x * (1.0 - s))", "return s"),
+    "U2_sign": ("U2 = (e2 * V).T @ H", "U2 = -(e2 * V).T @ H"),
+    "U1_transposed": ("U1 = (e1 * G * B * silu_prime(A)).T @ K",
+                      "U1 = ((e1 * G * B * silu_prime(A)).T @ K).T"),
+    "G_transposed_W2": ("G = V @ W2\n", "G = V @ W2.T\n"),
+    "mean_not_sum": ("U2 = (e2 * V).T @ H", "U2 = (e2 * V).T @ H / K.shape[0]"),
+    "lr_columns_swapped": ("e1, e2, e3 = lr[:, 0:1], lr[:, 1:2], lr[:, 2:3]",
+                           "e1, e2, e3 = lr[:, 2:3], lr[:, 1:2], lr[:, 0:1]"),
+    "renorm_over_columns": ("n_old = np.linalg.norm(W_old, axis=1, keepdims=True)\n"
+                            "    n_new = np.linalg.norm(W_new, axis=1, keepdims=True)",
+                            "n_old = np.linalg.norm(W_old, axis=0, keepdims=True)\n"
+                            "    n_new = np.linalg.norm(W_new, axis=0, keepdims=True)"),
+    "renorm_to_unit": ("return W_new * (n_old / n_new)", "return W_new / n_new"),
+    "ns_coefficient": ("NS_COEFFS = (3.4445, -4.7750, 2.0315)", "NS_COEFFS = (3.4445, -4.7750, 2.0)"),
+    "ns_product_order": ("X = a * X + B @ X", "X = a * X + X @ B"),
+    "momentum_sign": ("return beta_mean * M - U", "return beta_mean * M + U"),
+    "momentum_last_beta": ("bm = float(np.mean(beta))", "bm = float(beta[-1])"),
+    "order_swapped": ("if (f & APPLY) and (order == APPLY_THEN_UPDATE or not (f & UPDATE)):",
+                      "if (f & APPLY) and (order == UPDATE_THEN_APPLY or not (f & UPDATE)):"),
+    "gd_sign": ("Wn = [w + u for w, u in zip(W, U)]", "Wn = [w - u for w, u in zip(W, U)]"),
+    "muon_sign": ("Wn = [w + newton_schulz5(u, ns_steps) for w, u in zip(W, U)]",
+                  "Wn = [w - newton_schulz5(u, ns_steps) for w, u in zip(W, U)]"),
+    "apply_W1_for_W3": ("B = X @ W3.T\n    return", "B = X @ W1.T\n    return"),
+    "apply_only_chunk_updates": ("if f & UPDATE:\n            bt", "if True:\n            bt"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    a, b = MUTATIONS[name]
+    src = open(os.path.join(ROOT, "oracle", "lact_oracle.py")).read()
+    assert src.count(a) == 1, f"mutation anchor for {name} not found exactly once"
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "oracle", "__init__.py"), pkg / "__init__.py")
+    (pkg / "lact_oracle.py").write_text(src.replace(a, b))
+    env = dict(os.environ, PYTHONPATH=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-c",
+                        "import sys; sys.path.insert(0, %r); import oracle; "
+                        "assert oracle.__file__.startswith(%r); "
+                        "import pytest; sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', %r]))"
+                        % (str(tmp_path), str(tmp_path), os.path.join(ROOT, "tests", "test_oracle_pins.py"))],
+                       cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, f"{name} not caught:\n{r.stdout[-2000:]}\n{r.stderr[-2000:]}"

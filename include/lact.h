@@ -1,0 +1,185 @@
+/*
+ * lact.h -- C ABI of liblact, the MI355X (gfx950) LaCT fast-weight layer.
+ *
+ * The layer (Large-Chunk Test-Time Training) keeps, per instance
+ * (batch x head), a SwiGLU fast-weight MLP
+ *
+ *     f_W(x) = W2 (silu(W1 x) * (W3 x)),   W1, W3: [dh x d],  W2: [d x dh],
+ *
+ * updates it once per large chunk of tokens from the lr-weighted gradient of
+ * the loss -<f_W(k), v> summed over the chunk, and applies it to the chunk's
+ * queries.  Sources, by page title and labelled part:
+ *   "大块测试时训练（LaCT）技术解析" (dpshk.com) §2.1: update = gradient summed
+ *       over the whole chunk (eqs. 4-5); apply = updated weights on all
+ *       queries (eq. 2); §2.2.1: L2 weight normalisation (eq. 8), Muon
+ *       (eqs. 9-10); §2.2.2: context-parallel gradient sum.
+ *   "LaCT：以大分块更新人工智能的临时记忆" (iplexlaw.co.kr): sections
+ *       "局部注意力与非线性记忆相互补充" (SwiGLU memory, negative inner-product
+ *       loss, per-token lr, GD / momentum / Muon, L2 normalisation) and
+ *       "更新顺序必须遵守信息可见范围" (apply-then-update for language,
+ *       update-then-apply for posed image sets, video updates only on clean
+ *       chunks).
+ *   "LaCT架构核心思想解析" (gsyq.cn) §1.2 (three fast-weight matrices,
+ *       momentum with per-token beta, W <- L2norm(W - M)) and §2.1
+ *       (lr laid out as [(b nh), l, 3]).
+ *
+ * Conventions fixed by this library where the pages leave a choice:
+ *   - lr[..., j-1] scales the gradient of W_j (j = 1, 2, 3).
+ *   - U_j = -sum_{i in chunk} lr_ij dl_i/dW_j (a sum, not a mean).
+ *     GD: W' = W + U.  MOMENTUM: M <- mean_chunk(beta) M - U, W' = W - M.
+ *     MUON: W' = W + NS(U), NS = ns_iters quintic Newton-Schulz steps with
+ *     (a, b, c) = (3.4445, -4.7750, 2.0315) on X0 = U / (||U||_F + 1e-7).
+ *   - Renormalisation (unless LACT_NO_RENORM): every row of each updated
+ *     matrix (rows of the stored [rows x cols] arrays: an output unit's
+ *     fan-in) is rescaled to the L2 norm it had before the update.
+ *
+ * Memory: every tensor argument is a caller-owned DEVICE pointer, contiguous,
+ * innermost dimension fastest; host arrays (bounds, flags) are read during
+ * the call only.  The library allocates no device memory, keeps no pointer
+ * after returning, and frees nothing.  All device work is enqueued on
+ * `stream` (a hipStream_t; NULL = the legacy default stream) without any
+ * host synchronisation; completion is observed through the stream.
+ *
+ * Layouts (n = n_inst, D = d = dh):
+ *   q, k, v, o : [n, L, D]   io_dtype (F32 or BF16)
+ *   lr         : [n, L, 3]   float32 (post-softplus learning rates)
+ *   beta       : [n, L]      float32 (post-sigmoid momentum coefficients)
+ *   W1, W3     : [n, D, D]   float32, row j = fan-in vector of hidden unit j
+ *   W2         : [n, D, D]   float32, row r = fan-in vector of output unit r
+ *   M1, M2, M3 : same shapes as W1, W2, W3 (momentum state)
+ *   ws         : workspace, >= lact_workspace_size(...) bytes, 256-B aligned
+ *
+ * Errors: every argument is validated before any device work; on a negative
+ * status other than LACT_ERR_HIP nothing was enqueued and W, M, o are
+ * untouched.  LACT_ERR_HIP means a HIP call failed while enqueuing; W, M and
+ * o are then undefined.  lact_last_error() returns a thread-local text for
+ * the last failure on the calling thread.  No C++ exception crosses the ABI.
+ * Calls that share a workspace must not overlap on the device (order them
+ * on one stream).
+ */
+#ifndef LACT_H
+#define LACT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LACT_OK = 0,
+    LACT_ERR_INVALID_ARG = -1,        /* null/misaligned pointer, bad size, bad schedule */
+    LACT_ERR_UNSUPPORTED = -2,        /* d != dh, d not a multiple of 64 in [64, 1024],
+                                         device is not gfx950 */
+    LACT_ERR_WORKSPACE_TOO_SMALL = -3,
+    LACT_ERR_NO_DEVICE = -4,          /* no HIP device visible */
+    LACT_ERR_HIP = -5                 /* a HIP runtime call failed */
+} lact_status;
+
+typedef enum { LACT_DTYPE_F32 = 0, LACT_DTYPE_BF16 = 1 } lact_dtype;
+typedef enum { LACT_OPT_GD = 0, LACT_OPT_MOMENTUM = 1, LACT_OPT_MUON = 2 } lact_opt;
+typedef enum { LACT_APPLY_THEN_UPDATE = 0, LACT_UPDATE_THEN_APPLY = 1 } lact_order;
+
+/* per-chunk schedule flags */
+#define LACT_CHUNK_UPDATE 1u
+#define LACT_CHUNK_APPLY 2u
+
+/* lact_problem.flags */
+#define LACT_NO_RENORM 1u
+
+typedef struct {
+    int32_t n_inst;     /* B * nh independent instances (>= 0) */
+    int32_t d;          /* model width per head */
+    int32_t dh;         /* fast-weight hidden width; must equal d */
+    int32_t io_dtype;   /* lact_dtype of q, k, v, o */
+    int32_t opt;        /* lact_opt */
+    int32_t ns_iters;   /* Newton-Schulz steps for MUON, 0..16 (5 = standard) */
+    int32_t rec_planes; /* bf16 planes per fp32 operand in the state
+                           recurrence (update products, Newton-Schulz):
+                           1 = bf16, 2 = bf16x2, 3 = bf16x3 (fp32-grade);
+                           0 = default (3 for F32 io, else 1).  F32 io always
+                           uses 3 planes for every product. */
+    uint32_t flags;     /* LACT_NO_RENORM */
+} lact_problem;
+
+/*
+ * Bytes of workspace needed by lact_layer_forward with the same schedule
+ * arguments.  For lact_chunk_update / lact_apply over Lc tokens pass
+ * L = chunk = Lc, order = 0, bounds = flags = NULL, n_chunks = 0.
+ * Returns 0 (and sets lact_last_error) if the arguments are invalid.
+ */
+size_t lact_workspace_size(const lact_problem* p, int64_t L, int64_t chunk, int32_t order,
+                           const int64_t* bounds, const uint8_t* flags, int32_t n_chunks);
+
+/*
+ * One chunk update (steps: forward products on k and v, SwiGLU backward
+ * epilogue, weight-gradient contractions over the chunk, optimiser, row
+ * renormalisation) for Lc tokens per instance.  k, v are [n, seq_stride, D]
+ * (the first Lc tokens of each instance are used), lr [n, seq_stride, 3],
+ * beta [n, seq_stride] (MOMENTUM only, else may be NULL).  W1..W3 are read
+ * and overwritten with the updated weights; M1..M3 likewise for MOMENTUM
+ * (else may be NULL).  Lc == 0 is a no-op.
+ */
+lact_status lact_chunk_update(const lact_problem* p, const void* k, const void* v,
+                              const float* lr, const float* beta, int64_t Lc,
+                              int64_t seq_stride, float* W1, float* W2, float* W3,
+                              float* M1, float* M2, float* M3, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * Apply the fast weights to Lq queries per instance:
+ * o = W2 (silu(W1 q) * (W3 q)).  q, o are [n, seq_stride, D] (first Lq
+ * tokens used).  W1..W3 are read only.
+ */
+lact_status lact_apply(const lact_problem* p, const void* q, int64_t Lq, int64_t seq_stride,
+                       const float* W1, const float* W2, const float* W3, void* o,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The layer over a whole sequence of L tokens per instance.
+ * Schedule: if bounds == NULL and flags == NULL, chunks are uniform of
+ * `chunk` tokens (the last takes the remainder) and every chunk is
+ * UPDATE|APPLY.  Otherwise bounds[0..n_chunks] (host array, bounds[0] = 0,
+ * strictly increasing, bounds[n_chunks] = L) and flags[0..n_chunks-1]
+ * (host array of LACT_CHUNK_* bits) define it.
+ * Order: LACT_APPLY_THEN_UPDATE -- an UPDATE|APPLY chunk is applied with the
+ * weights before its own update (shifted block-causal);
+ * LACT_UPDATE_THEN_APPLY -- it is applied after its own update.  An
+ * APPLY-only chunk reads the current weights; an UPDATE-only chunk writes no
+ * output.  Rows of o outside APPLY chunks are left untouched.  The final
+ * state is written back to W1..W3 (and M1..M3 for MOMENTUM).
+ */
+lact_status lact_layer_forward(const lact_problem* p, const void* q, const void* k,
+                               const void* v, const float* lr, const float* beta, int64_t L,
+                               int64_t chunk, int32_t order, const int64_t* bounds,
+                               const uint8_t* flags, int32_t n_chunks, float* W1, float* W2,
+                               float* W3, float* M1, float* M2, float* M3, void* o, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* lact_status_str(lact_status s);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* lact_last_error(void);
+
+/*
+ * Per-kernel timing (diagnostics).  While enabled on the calling thread,
+ * every launch of a library kernel of class `kclass` (see LACT_K_*) is
+ * bracketed by HIP events recorded on the launch stream.  lact_timing_read
+ * synchronises those events and returns the summed milliseconds and the
+ * number of launches since the last reset.
+ */
+#define LACT_K_FWD 0       /* forward products on q / k, v with fused epilogues */
+#define LACT_K_OUT 1       /* apply output product o = Hq W2^T */
+#define LACT_K_DW 2        /* weight-gradient contractions (split over tokens) */
+#define LACT_K_OPT 3       /* optimiser step + row renormalisation */
+#define LACT_K_NS 4        /* Newton-Schulz products and reductions */
+#define LACT_K_COUNT 5
+lact_status lact_timing_enable(int32_t kclass, int32_t on);
+lact_status lact_timing_read(int32_t kclass, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LACT_H */

@@ -1,0 +1,252 @@
+"""Thin ctypes binding of liblact (include/lact.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Torch tensors supply device memory (data_ptr) and the current HIP
+stream; nothing here computes any part of the layer.  If liblact.so is
+missing the import fails loudly -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblact.so")
+
+# values mirror include/lact.h
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_WORKSPACE_TOO_SMALL = -3
+ERR_NO_DEVICE = -4
+ERR_HIP = -5
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+OPT_GD = 0
+OPT_MOMENTUM = 1
+OPT_MUON = 2
+APPLY_THEN_UPDATE = 0
+UPDATE_THEN_APPLY = 1
+CHUNK_UPDATE = 1
+CHUNK_APPLY = 2
+NO_RENORM = 1
+
+K_FWD, K_OUT, K_DW, K_OPT, K_NS = range(5)
+K_NAMES = {K_FWD: "fwd", K_OUT: "apply_out", K_DW: "dw", K_OPT: "opt", K_NS: "newton_schulz"}
+
+EXPORTS = ["lact_workspace_size", "lact_chunk_update", "lact_apply", "lact_layer_forward",
+           "lact_status_str", "lact_last_error", "lact_timing_enable", "lact_timing_read"]
+
+
+class LactError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"liblact status {status}: {detail}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("n_inst", ctypes.c_int32), ("d", ctypes.c_int32), ("dh", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("opt", ctypes.c_int32), ("ns_iters", ctypes.c_int32),
+                ("rec_planes", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m test_layers_amd.build` "
+                          "(the LaCT layer has no non-HIP implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    P = ctypes.POINTER(Problem)
+    L.lact_workspace_size.restype = sz
+    L.lact_workspace_size.argtypes = [P, i64, i64, i32, vp, vp, i32]
+    L.lact_chunk_update.restype = i32
+    L.lact_chunk_update.argtypes = [P, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lact_apply.restype = i32
+    L.lact_apply.argtypes = [P, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+    L.lact_layer_forward.restype = i32
+    L.lact_layer_forward.argtypes = [P, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lact_status_str.restype = ctypes.c_char_p
+    L.lact_status_str.argtypes = [i32]
+    L.lact_last_error.restype = ctypes.c_char_p
+    L.lact_last_error.argtypes = []
+    L.lact_timing_enable.restype = i32
+    L.lact_timing_enable.argtypes = [i32, i32]
+    L.lact_timing_read.restype = i32
+    L.lact_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().lact_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != OK:
+        raise LactError(status, f"{lib().lact_status_str(status).decode()}: {last_error()}")
+
+
+def problem(n_inst: int, d: int, io_dtype: int, opt: int, rec_planes: int = 0, ns_iters: int = 5,
+            renorm: bool = True, dh: Optional[int] = None) -> Problem:
+    return Problem(n_inst, d, d if dh is None else dh, io_dtype, opt, ns_iters, rec_planes,
+                   0 if renorm else NO_RENORM)
+
+
+# ----------------------------------------------------------------- raw-pointer calls
+def _sched(bounds, flags):
+    # either may be None: the library reports a half-given schedule itself
+    if bounds is None and flags is None:
+        return None, None, 0, None
+    b = None if bounds is None else (ctypes.c_int64 * len(bounds))(*[int(x) for x in bounds])
+    f = None if flags is None else (ctypes.c_uint8 * len(flags))(*[int(x) for x in flags])
+    nc = len(flags) if flags is not None else len(bounds) - 1
+    cast = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
+    return cast(b), cast(f), nc, (b, f)
+
+
+def workspace_size(p: Problem, L: int, chunk: int = 0, order: int = 0,
+                   bounds: Optional[Sequence[int]] = None, flags: Optional[Sequence[int]] = None) -> int:
+    bp, fp, nc, _keep = _sched(bounds, flags)
+    n = lib().lact_workspace_size(ctypes.byref(p), L, chunk, order, bp, fp, nc)
+    if n == 0:
+        raise LactError(ERR_INVALID_ARG, last_error())
+    return n
+
+
+def layer_forward_ptr(p: Problem, q, k, v, lr, beta, L, chunk, order, bounds, flags,
+                      W1, W2, W3, M1, M2, M3, o, ws, ws_bytes, stream) -> int:
+    bp, fp, nc, _keep = _sched(bounds, flags)
+    return lib().lact_layer_forward(ctypes.byref(p), q, k, v, lr, beta, L, chunk, order, bp, fp, nc,
+                                    W1, W2, W3, M1, M2, M3, o, ws, ws_bytes, stream)
+
+
+def chunk_update_ptr(p: Problem, k, v, lr, beta, Lc, seq_stride, W1, W2, W3, M1, M2, M3,
+                     ws, ws_bytes, stream) -> int:
+    return lib().lact_chunk_update(ctypes.byref(p), k, v, lr, beta, Lc, seq_stride, W1, W2, W3,
+                                   M1, M2, M3, ws, ws_bytes, stream)
+
+
+def apply_ptr(p: Problem, q, Lq, seq_stride, W1, W2, W3, o, ws, ws_bytes, stream) -> int:
+    return lib().lact_apply(ctypes.byref(p), q, Lq, seq_stride, W1, W2, W3, o, ws, ws_bytes, stream)
+
+
+def timing_enable(kclass: int, on: bool = True) -> None:
+    check(lib().lact_timing_enable(kclass, 1 if on else 0))
+
+
+def timing_read(kclass: int):
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    check(lib().lact_timing_read(kclass, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+# ----------------------------------------------------------------- torch-tensor calls
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _io_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise ValueError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _workspace(nbytes, workspace, device):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace smaller than the {nbytes} bytes needed")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def layer_forward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, o=None, *,
+                  chunk: int = 0, order: int = APPLY_THEN_UPDATE, opt: int = OPT_GD,
+                  bounds=None, flags=None, rec_planes: int = 0, ns_iters: int = 5,
+                  renorm: bool = True, workspace=None, stream=None):
+    """q, k, v [n, L, D] (fp32 or bf16), lr [n, L, 3] fp32, beta [n, L] fp32
+    (momentum) or None, W1, W2, W3 [n, D, D] fp32 (updated in place), M1..M3
+    (momentum state, updated in place).  Returns o [n, L, D] (allocated with
+    torch.zeros if not given; rows of non-APPLY chunks keep their values)."""
+    torch = _torch()
+    n, L, D = q.shape
+    io = _io_dtype(q)
+    p = problem(n, D, io, opt, rec_planes, ns_iters, renorm)
+    if o is None:
+        o = torch.zeros_like(q)
+    need = workspace_size(p, L, chunk, order, bounds, flags)
+    ws = _workspace(need, workspace, q.device)
+    f32 = torch.float32
+    st = layer_forward_ptr(p, _ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"),
+                           _ptr(lr, f32, "lr"), _ptr(beta, f32, "beta"), L, chunk, order, bounds, flags,
+                           _ptr(W1, f32, "W1"), _ptr(W2, f32, "W2"), _ptr(W3, f32, "W3"),
+                           _ptr(M1, f32, "M1"), _ptr(M2, f32, "M2"), _ptr(M3, f32, "M3"),
+                           _ptr(o, q.dtype, "o"), ws.data_ptr(), ws.numel(), _stream(stream))
+    check(st)
+    return o
+
+
+def chunk_update(k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, Lc: Optional[int] = None,
+                 opt: int = OPT_GD, rec_planes: int = 0, ns_iters: int = 5, renorm: bool = True,
+                 workspace=None, stream=None):
+    torch = _torch()
+    n, S, D = k.shape
+    Lc = S if Lc is None else Lc
+    p = problem(n, D, _io_dtype(k), opt, rec_planes, ns_iters, renorm)
+    ws = _workspace(workspace_size(p, Lc, max(Lc, 1)), workspace, k.device)
+    f32 = torch.float32
+    check(chunk_update_ptr(p, _ptr(k, k.dtype, "k"), _ptr(v, k.dtype, "v"), _ptr(lr, f32, "lr"),
+                           _ptr(beta, f32, "beta"), Lc, S, _ptr(W1, f32, "W1"), _ptr(W2, f32, "W2"),
+                           _ptr(W3, f32, "W3"), _ptr(M1, f32, "M1"), _ptr(M2, f32, "M2"),
+                           _ptr(M3, f32, "M3"), ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def apply(q, W1, W2, W3, o=None, *, Lq: Optional[int] = None, workspace=None, stream=None):
+    torch = _torch()
+    n, S, D = q.shape
+    Lq = S if Lq is None else Lq
+    p = problem(n, D, _io_dtype(q), OPT_GD)
+    if o is None:
+        o = torch.zeros_like(q)
+    ws = _workspace(workspace_size(p, Lq, max(Lq, 1)), workspace, q.device)
+    f32 = torch.float32
+    check(apply_ptr(p, _ptr(q, q.dtype, "q"), Lq, S, _ptr(W1, f32, "W1"), _ptr(W2, f32, "W2"),
+                    _ptr(W3, f32, "W3"), _ptr(o, q.dtype, "o"), ws.data_ptr(), ws.numel(),
+                    _stream(stream)))
+    return o
+
+
+lib()  # fail at import time if the library is missing

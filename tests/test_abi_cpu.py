@@ -1,0 +1,179 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/lact.h declares, the header is valid C11, and every validation path
+returns its error code before any device work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lact.h")
+
+lact = pytest.importorskip("test_layers_amd.lact", reason="liblact.so not built")
+
+FAKE = 1 << 20   # an aligned non-null address; never dereferenced by validation
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lact_\w+)\s*\(", txt)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(lact.EXPORTS)
+    L = lact.lib()
+    for nm in names:
+        assert hasattr(L, nm), nm
+
+
+def test_header_is_c11(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "lact.h"\nint main(void){lact_problem p; (void)p; '
+                   'return (int)LACT_OK + LACT_CHUNK_APPLY;}\n')
+    r = subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    L = lact.lib()
+    for s in [0, -1, -2, -3, -4, -5]:
+        assert len(L.lact_status_str(s)) > 0
+    assert L.lact_status_str(7) == b"unknown status"
+
+
+def P(**kw):
+    base = dict(n_inst=2, d=128, io_dtype=lact.DTYPE_BF16, opt=lact.OPT_GD)
+    base.update(kw)
+    return lact.problem(**base)
+
+
+def fwd(p, L=512, chunk=128, order=0, bounds=None, flags=None, ws_bytes=None, **ptrs):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lr=FAKE, beta=FAKE, W1=FAKE, W2=FAKE, W3=FAKE,
+             M1=FAKE, M2=FAKE, M3=FAKE, o=FAKE, ws=FAKE)
+    a.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return lact.layer_forward_ptr(p, a["q"], a["k"], a["v"], a["lr"], a["beta"], L, chunk, order,
+                                  bounds, flags, a["W1"], a["W2"], a["W3"], a["M1"], a["M2"], a["M3"],
+                                  a["o"], a["ws"], ws_bytes, None)
+
+
+def test_null_problem():
+    st = lact.lib().lact_layer_forward(None, None, None, None, None, None, 0, 1, 0, None, None, 0,
+                                       None, None, None, None, None, None, None, None, 0, None)
+    assert st == lact.ERR_INVALID_ARG
+    assert "problem" in lact.last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=128, dh=64), lact.ERR_UNSUPPORTED),
+    (dict(d=96), lact.ERR_UNSUPPORTED),
+    (dict(d=32), lact.ERR_UNSUPPORTED),
+    (dict(d=2048), lact.ERR_UNSUPPORTED),
+    (dict(io_dtype=5), lact.ERR_INVALID_ARG),
+    (dict(opt=9), lact.ERR_INVALID_ARG),
+    (dict(opt=lact.OPT_MUON, ns_iters=0), lact.ERR_INVALID_ARG),
+    (dict(rec_planes=4), lact.ERR_INVALID_ARG),
+    (dict(n_inst=-1), lact.ERR_INVALID_ARG),
+])
+def test_bad_problem(kw, code):
+    assert fwd(P(**kw)) == code
+    assert lact.last_error() != ""
+
+
+def test_bad_flags_field():
+    p = P()
+    p.flags = 0x10
+    assert fwd(p) == lact.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args", [
+    dict(order=2),
+    dict(chunk=0),
+    dict(L=-1),
+    dict(bounds=[0, 100, 512], flags=None),
+    dict(bounds=[1, 100, 512], flags=[3, 3]),
+    dict(bounds=[0, 100, 100, 512], flags=[3, 3, 3]),
+    dict(bounds=[0, 300, 200, 512], flags=[3, 3, 3]),
+    dict(bounds=[0, 100, 500], flags=[3, 3]),
+    dict(bounds=[0, 100, 512], flags=[3, 4]),
+])
+def test_bad_schedule(args):
+    assert fwd(P(), **args) == lact.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("ptrs,opt", [
+    (dict(q=None), lact.OPT_GD),
+    (dict(o=None), lact.OPT_GD),
+    (dict(k=None), lact.OPT_GD),
+    (dict(v=None), lact.OPT_GD),
+    (dict(lr=None), lact.OPT_GD),
+    (dict(W2=None), lact.OPT_GD),
+    (dict(beta=None), lact.OPT_MOMENTUM),
+    (dict(M3=None), lact.OPT_MOMENTUM),
+    (dict(k=FAKE + 2), lact.OPT_GD),
+    (dict(W1=FAKE + 4), lact.OPT_GD),
+    (dict(ws=FAKE + 16), lact.OPT_GD),
+])
+def test_bad_pointers(ptrs, opt):
+    assert fwd(P(opt=opt), **ptrs) == lact.ERR_INVALID_ARG
+
+
+def test_pointers_not_needed_by_the_schedule_may_be_null():
+    # update-only schedule: q and o are never touched; GD: beta and M unused
+    p = P()
+    st = fwd(p, L=256, bounds=[0, 256], flags=[lact.CHUNK_UPDATE], q=None, o=None, beta=None,
+             M1=None, M2=None, M3=None)
+    assert st not in (lact.ERR_INVALID_ARG,), lact.last_error()
+
+
+def test_workspace_too_small():
+    p = P()
+    need = lact.workspace_size(p, 512, 128)
+    assert fwd(p, ws_bytes=need - 1) == lact.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_noop_calls_need_no_device():
+    assert fwd(P(n_inst=0)) == lact.OK
+    assert fwd(P(), L=0, chunk=16) == lact.OK
+    assert lact.chunk_update_ptr(P(), FAKE, FAKE, FAKE, None, 0, 0, FAKE, FAKE, FAKE,
+                                 None, None, None, FAKE, 1 << 30, None) == lact.OK
+    assert lact.apply_ptr(P(), FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == lact.OK
+
+
+def test_chunk_update_and_apply_validation():
+    p = P()
+    assert lact.chunk_update_ptr(p, FAKE, FAKE, FAKE, None, 64, 32, FAKE, FAKE, FAKE,
+                                 None, None, None, FAKE, 1 << 30, None) == lact.ERR_INVALID_ARG
+    assert lact.chunk_update_ptr(P(opt=lact.OPT_MOMENTUM), FAKE, FAKE, FAKE, None, 64, 64, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == lact.ERR_INVALID_ARG
+    assert lact.apply_ptr(p, None, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == lact.ERR_INVALID_ARG
+    assert lact.apply_ptr(p, FAKE, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == lact.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_size_properties():
+    p = P()
+    a = lact.workspace_size(p, 512, 128)
+    b = lact.workspace_size(p, 4096, 1024)
+    assert 0 < a < b
+    m = lact.workspace_size(P(opt=lact.OPT_MUON), 512, 128)
+    assert m > a
+    with pytest.raises(lact.LactError):
+        lact.workspace_size(P(d=96), 512, 128)
+    # explicit schedule equal to the uniform one gives the same size
+    assert lact.workspace_size(p, 512, 128, 0, [0, 128, 256, 384, 512], [3, 3, 3, 3]) == a
+    # the view-set schedule: one long update chunk, then the targets
+    v = lact.workspace_size(P(n_inst=6, d=128), 200704, 0, 1, [0, 196608, 200704], [1, 2])
+    assert v > 6 * 196608 * 3 * 128 * 2
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fwd(P()) == lact.ERR_NO_DEVICE

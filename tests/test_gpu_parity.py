@@ -1,0 +1,178 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, on
+the same seeded inputs.  Gates: max|gpu - ref| / max|ref| <= 1e-4 for fp32
+inputs and <= 2e-2 for bf16 inputs, per instance, on the APPLY rows of o and
+on the final state."""
+import numpy as np
+import pytest
+
+import oracle as O
+from test_layers_amd import workloads as W
+from parity_util import compare, from_dev, log, rel_err, run_gpu, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def lact():
+    from test_layers_amd import lact as L
+    return L
+
+
+def _gate(io):
+    return 1e-4 if io == W.DTYPE_F32 else 2e-2
+
+
+def _rand_inputs(n, L, D, io, seed, raw=False):
+    wl = W.Workload(99, "unit", n, D, L, (0, L), (3,), 0, W.OPT_GD, io, not raw, 1, _gate(io))
+    return W.generate(wl, seed=seed)
+
+
+# ------------------------------------------------------------------ apply alone
+@pytest.mark.parametrize("D", [64, 128, 384])
+@pytest.mark.parametrize("io", [W.DTYPE_F32, W.DTYPE_BF16])
+def test_apply_matches_oracle(lact, D, io):
+    log(f"apply D={D} io={io}")
+    n, L = 2, 300
+    inp = _rand_inputs(n, L, D, io, seed=D + io)
+    q = to_dev(inp.q, torch)
+    Ws = [to_dev(w, torch) for w in (inp.W1, inp.W2, inp.W3)]
+    o = lact.apply(q, *Ws)
+    torch.cuda.synchronize()
+    g = from_dev(o, torch)
+    err = 0.0
+    for i in range(n):
+        ref = O.apply(O.f64(inp.W1[i]), O.f64(inp.W2[i]), O.f64(inp.W3[i]), O.f64(inp.q[i]))
+        err = max(err, rel_err(g[i], ref))
+    log(f"  err={err:.3e}")
+    assert err <= _gate(io)
+
+
+def test_apply_respects_seq_stride_and_leaves_other_rows(lact):
+    n, S, Lq, D = 2, 400, 257, 128
+    inp = _rand_inputs(n, S, D, W.DTYPE_BF16, seed=5)
+    q = to_dev(inp.q, torch)
+    Ws = [to_dev(w, torch) for w in (inp.W1, inp.W2, inp.W3)]
+    o = torch.full_like(q, 7.0)
+    lact.apply(q, *Ws, o, Lq=Lq)
+    torch.cuda.synchronize()
+    g = from_dev(o, torch)
+    assert np.all(g[:, Lq:] == 7.0)
+    for i in range(n):
+        ref = O.apply(O.f64(inp.W1[i]), O.f64(inp.W2[i]), O.f64(inp.W3[i]), O.f64(inp.q[i][:Lq]))
+        assert rel_err(g[i, :Lq], ref) <= 2e-2
+
+
+# ------------------------------------------------------------------ one chunk update
+@pytest.mark.parametrize("opt", [W.OPT_GD, W.OPT_MOMENTUM, W.OPT_MUON])
+@pytest.mark.parametrize("io,planes", [(W.DTYPE_F32, 3), (W.DTYPE_BF16, 1), (W.DTYPE_BF16, 2),
+                                       (W.DTYPE_BF16, 3)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_chunk_update_matches_oracle(lact, opt, io, planes, D):
+    log(f"chunk_update opt={opt} io={io} planes={planes} D={D}")
+    n, Lc = 2, 300
+    inp = _rand_inputs(n, Lc, D, io, seed=10 * D + opt)
+    rng = np.random.default_rng(1)
+    beta = rng.uniform(0.5, 0.99, (n, Lc)).astype(np.float32)
+    M0 = [rng.standard_normal((n, D, D)).astype(np.float32) * 0.01 for _ in range(3)]
+    k, v, lr = to_dev(inp.k, torch), to_dev(inp.v, torch), to_dev(inp.lr, torch)
+    Ws = [to_dev(w, torch).clone() for w in (inp.W1, inp.W2, inp.W3)]
+    Ms = [to_dev(m, torch).clone() for m in M0] if opt == W.OPT_MOMENTUM else [None] * 3
+    lact.chunk_update(k, v, lr, to_dev(beta, torch) if opt == W.OPT_MOMENTUM else None,
+                      *Ws, *Ms, opt=opt, rec_planes=planes)
+    torch.cuda.synchronize()
+    errs = {}
+    for i in range(n):
+        Wr, Mr = O.update_step([O.f64(inp.W1[i]), O.f64(inp.W2[i]), O.f64(inp.W3[i])],
+                               [O.f64(m[i]) for m in M0], O.f64(inp.k[i]), O.f64(inp.v[i]),
+                               O.f64(inp.lr[i]), O.f64(beta[i]), opt)
+        for j, nm in enumerate(["W1", "W2", "W3"]):
+            errs[nm] = max(errs.get(nm, 0), rel_err(from_dev(Ws[j], torch)[i], Wr[j]))
+            if opt == W.OPT_MOMENTUM:
+                errs["M" + nm[1]] = max(errs.get("M" + nm[1], 0), rel_err(from_dev(Ms[j], torch)[i], Mr[j]))
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    gate = _gate(io) if planes == 1 or io == W.DTYPE_F32 else 1e-3
+    assert max(errs.values()) <= gate, errs
+
+
+# ------------------------------------------------------------------ layer at reduced sizes
+SMALL = {
+    1: W.CONFIGS[1],
+    2: W.CONFIGS[2].scaled(n_inst=2, L=3 * 512 + 200, chunk=512),
+    3: W.CONFIGS[3].scaled(n_inst=2, L=2 * 1024 + 300, chunk=1024),
+}
+
+
+def _small_viewset():
+    c = W.CONFIGS[4]
+    b, f = (0, 4000, 4500), (W.UPDATE, W.APPLY)
+    import dataclasses
+    return dataclasses.replace(c, n_inst=2, L=4500, bounds=b, flags=f)
+
+
+def _small_video():
+    c = W.CONFIGS[5]
+    import dataclasses
+    b, f = W.video_schedule(3, 700)
+    return dataclasses.replace(c, n_inst=3, L=b[-1], bounds=b, flags=f)
+
+
+SMALL[4] = _small_viewset()
+SMALL[5] = _small_video()
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_layer_reduced_size(lact, cid):
+    wl = SMALL[cid]
+    log(f"layer reduced cfg{cid}: n={wl.n_inst} D={wl.D} L={wl.L} chunks={wl.n_chunks}")
+    inp = W.generate(wl)
+    gpu = run_gpu(wl, inp, torch, lact)
+    errs = compare(wl, inp, gpu)
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= wl.tol, errs
+
+
+@pytest.mark.parametrize("order", [W.APPLY_THEN_UPDATE, W.UPDATE_THEN_APPLY])
+def test_layer_orders_and_no_renorm(lact, order):
+    wl = W.CONFIGS[2].scaled(n_inst=2, L=1000, chunk=384)
+    inp = W.generate(wl, seed=3)
+    for renorm in (True, False):
+        log(f"order={order} renorm={renorm}")
+        gpu = run_gpu(wl, inp, torch, lact, order=order, renorm=renorm)
+        errs = compare(wl, inp, gpu, order=order, renorm=renorm)
+        log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+        assert max(errs.values()) <= wl.tol, errs
+
+
+def test_layer_is_deterministic(lact):
+    wl = W.CONFIGS[3].scaled(n_inst=2, L=1500, chunk=512)
+    inp = W.generate(wl, seed=4)
+    a = run_gpu(wl, inp, torch, lact)
+    b = run_gpu(wl, inp, torch, lact)
+    for key in ["o", "W1", "W2", "W3"]:
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_resume_equals_single_call(lact):
+    """Chunks [0, c) then [c, n) with the state carried equal one call (bitwise:
+    every kernel reduces in a fixed order)."""
+    wl = W.CONFIGS[2].scaled(n_inst=2, L=1536, chunk=512)
+    inp = W.generate(wl, seed=6)
+    full = run_gpu(wl, inp, torch, lact)
+    q, k, v = to_dev(inp.q, torch), to_dev(inp.k, torch), to_dev(inp.v, torch)
+    lr, beta = to_dev(inp.lr, torch), to_dev(inp.beta, torch)
+    Ws = [to_dev(w, torch).clone() for w in (inp.W1, inp.W2, inp.W3)]
+    Ms = [torch.zeros_like(w) for w in Ws]
+    o = torch.zeros_like(q)
+    s = 1024
+    sl = lambda t: t[:, :s].contiguous()
+    o1 = lact.layer_forward(sl(q), sl(k), sl(v), sl(lr), sl(beta), *Ws, *Ms, chunk=512,
+                            opt=W.OPT_MOMENTUM)
+    tl = lambda t: t[:, s:].contiguous()
+    o2 = lact.layer_forward(tl(q), tl(k), tl(v), tl(lr), tl(beta), *Ws, *Ms, chunk=512,
+                            opt=W.OPT_MOMENTUM)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], 1), full["o"])
+    for j, key in enumerate(["W1", "W2", "W3"]):
+        assert torch.equal(Ws[j], full[key])

@@ -1,0 +1,205 @@
+"""Benchmark of the LaCT fast-weight layer forward (update + apply) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+One step = one whole layer forward over the workload's sequence (every chunk:
+forward products, SwiGLU backward epilogue, weight-gradient contraction,
+optimiser + renorm, apply), inputs resident in HBM.  The default workload is
+the 760M-LM-shaped layer: 4 heads, d = dh = 384, 32,768 tokens in chunks of
+2,048, bf16 q/k/v, fp32 fast weights, momentum, apply-then-update.  Prints one
+JSON line.
+
+The fast weights are not reset between steps: every step runs the same
+kernels on the state the previous step left (same work, like the next 32K
+tokens of a longer sequence).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+PEAK_FP32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12         # bytes/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default: the 760M LM layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work to sample")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain device copy of known size (PMC counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_flops(wl, lact):
+    """Algorithmic FLOPs per step, per kernel class."""
+    from test_layers_amd import workloads as W
+    D, n = wl.D, wl.n_inst
+    upd = sum(b - a for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags) if f & W.UPDATE)
+    app = sum(b - a for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags) if f & W.APPLY)
+    n_upd = sum(1 for f in wl.flags if f & W.UPDATE)
+    return {
+        lact.K_FWD: (6.0 * upd + 4.0 * app) * D * D * n,   # K W1^T, K W3^T, V W2; Q W1^T, Q W3^T
+        lact.K_OUT: 2.0 * app * D * D * n,                  # Hq W2^T
+        lact.K_DW: 6.0 * upd * D * D * n,                   # three contractions over tokens
+        lact.K_OPT: 0.0,
+        lact.K_NS: (30.0 * D ** 3 * 3 * n * n_upd) if wl.opt == W.OPT_MUON else 0.0,
+    }
+
+
+def opt_bytes(wl, S):
+    """Minimum HBM bytes of the optimiser kernel per update step: S fp32
+    partials of the three direction matrices read, W (and M) read and written."""
+    from test_layers_amd import workloads as W
+    D, n = wl.D, wl.n_inst
+    mats = 3 * D * D * 4 * n
+    per = S * mats + 2 * mats + (2 * mats if wl.opt == W.OPT_MOMENTUM else 0)
+    return per
+
+
+def cpu_baseline(wl, inp, budget):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    done = 0
+    for i in range(wl.n_inst):
+        O.forward_instance(inp.q[i], inp.k[i], inp.v[i], inp.lr[i],
+                           None if inp.beta is None else inp.beta[i],
+                           inp.W1[i], inp.W2[i], inp.W3[i], wl.bounds, wl.flags, wl.order, wl.opt)
+        done += 1
+        if time.perf_counter() - t0 >= budget:
+            break
+    dt = time.perf_counter() - t0
+    tokens = wl.tokens * done / wl.n_inst
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {wl.n_inst} instances (heads), whole sequence each, "
+                      f"{dt:.1f} s, numpy fp64"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from test_layers_amd import lact
+    from test_layers_amd import workloads as W
+
+    if args.copy_calib:
+        # plain copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE counters
+        nbytes = 1 << 30
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": nbytes, "launches": 5}))
+        return
+
+    wl = W.CONFIGS[args.config]
+    inp = W.generate(wl, threads=16)
+    dev = lambda x: None if x is None else (
+        torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() if x.dtype == np.uint16
+        else torch.from_numpy(np.ascontiguousarray(x)).cuda())
+    q, k, v, lr, beta = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.lr), dev(inp.beta)
+    Ws = [dev(inp.W1), dev(inp.W2), dev(inp.W3)]
+    Ms = [torch.zeros_like(w) for w in Ws] if wl.opt == W.OPT_MOMENTUM else [None] * 3
+    o = torch.zeros_like(q)
+    p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes)
+    bounds, flags = list(wl.bounds), list(wl.flags)
+    ws = torch.empty(lact.workspace_size(p, wl.L, 0, wl.order, bounds, flags), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lact.layer_forward(q, k, v, lr, beta, *Ws, *Ms, o, order=wl.order, opt=wl.opt,
+                           bounds=bounds, flags=flags, rec_planes=wl.rec_planes, workspace=ws,
+                           stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt / args.steps * 1e3
+    tokens = wl.tokens
+    value = tokens * args.steps / dt
+    flops = W.algorithmic_flops(wl)["total"]
+
+    # per-kernel HIP-event timing over the same number of steps
+    kf = kernel_flops(wl, lact)
+    for kc in lact.K_NAMES:
+        lact.timing_enable(kc, True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per = {}
+    for kc, name in lact.K_NAMES.items():
+        ms, nl = lact.timing_read(kc)
+        lact.timing_enable(kc, False)
+        if nl:
+            per[name] = {"ms_per_step": ms / args.steps, "launches_per_step": nl / args.steps,
+                         "avg_launch_us": ms / nl * 1e3, "kc": kc}
+    dom = max(per.items(), key=lambda kv: kv[1]["ms_per_step"])
+    dname, d = dom
+    if kf[d["kc"]] > 0:
+        per_launch = kf[d["kc"]] / (d["launches_per_step"])
+        achieved = per_launch / (d["avg_launch_us"] * 1e-6)
+        roof = {"kernel": dname, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": None,
+                "flops_per_launch": per_launch, "avg_launch_us": d["avg_launch_us"]}
+    else:
+        nb = opt_bytes(wl, 1) / d["launches_per_step"] * (1 if True else 0)
+        achieved = nb / (d["avg_launch_us"] * 1e-6)
+        roof = {"kernel": dname, "bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None,
+                "bytes_per_launch": nb, "avg_launch_us": d["avg_launch_us"]}
+    kernels = {k: {kk: round(vv, 4) for kk, vv in v.items() if kk != "kc"} for k, v in per.items()}
+
+    out = {
+        "metric": "LaCT layer tokens/sec (update+apply) and % bf16 MFMA peak, 1xMI355X",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.io_dtype == W.DTYPE_BF16 else "f32",
+        "data": "synthetic (seeded generator; no dataset, random-init fast weights)",
+        "config": {"workload": wl.name, "n_inst": wl.n_inst, "d": wl.D, "dh": wl.D, "seq_len": wl.L,
+                   "max_chunk": wl.max_chunk, "n_chunks": wl.n_chunks,
+                   "opt": ["gd", "momentum", "muon"][wl.opt],
+                   "order": ["apply_then_update", "update_then_apply"][wl.order],
+                   "rec_planes": wl.rec_planes, "global_batch": 1},
+        "algorithmic_tflop_per_step": flops / 1e12,
+        "layer_frac_bf16_peak": flops / (ms_per_step * 1e-3) / PEAK_BF16,
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

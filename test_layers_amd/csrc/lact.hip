@@ -11,10 +11,11 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "lact.h"
-#include "lact_kernels.hpp"
+#include "lact_direct.hpp"
 
 using namespace lact;
 
@@ -172,27 +173,64 @@ void build_plan(int32_t order, const std::vector<int64_t>& b, const std::vector<
 }
 
 // --------------------------------------------------------------- tiling heuristics
+constexpr int LDS_MAX = 160 * 1024;
+
+// workgroups of 128x128 GEMM tiles -> tile edge
 int gemm_tile(int64_t wgs128) { return wgs128 >= 200 ? 128 : 64; }
 
-int dw_tile(const lact_problem& p) { return p.d >= 128 ? 128 : 64; }
+// the column-k operand tile of the contraction must not overhang D
+int dw_tile(const lact_problem& p) { return p.d % 128 == 0 ? 128 : 64; }
 
-// split of the chunk's tokens for the weight-gradient contraction
+// split of the chunk's tokens for the weight-gradient contraction; split
+// lengths are multiples of 64 tokens
 void dw_split(const lact_problem& p, int64_t C, int& S, int64_t& kps) {
   const int bt = dw_tile(p);
   const int64_t tiles = (int64_t)(3 * p.d / bt) * (p.d / bt) * std::max(1, p.n_inst);
-  int64_t s = (512 + tiles - 1) / tiles;
+  // about two workgroups per CU, with instances x splits a multiple of the 8
+  // XCDs so that every XCD receives whole (instance, split) groups of tiles
+  int64_t s = std::max<int64_t>(1, (512 + tiles / 2) / tiles);
+  const int64_t n = std::max(1, p.n_inst);
+  for (int k = 0; k < 8 && (n * s) % 8 != 0; ++k) ++s;
+  if ((n * s) % 8 != 0) s = std::max<int64_t>(1, (512 + tiles / 2) / tiles);
   s = std::min<int64_t>(s, std::max<int64_t>(1, C / 256));
   s = std::max<int64_t>(1, std::min<int64_t>(s, 64));
-  kps = ((C + s - 1) / s + BK - 1) / BK * BK;
-  if (kps <= 0) kps = BK;
+  kps = ((C + s - 1) / s + 63) / 64 * 64;
   S = (int)((C + kps - 1) / kps);
   if (S < 1) S = 1;
 }
 
+// hidden-column block of the update forward tile: the one whose workgroup
+// count fills the chip best (ties go to the wider block)
+int upd_bj(const lact_problem& p, int64_t C) {
+  const int64_t tt = (C + FBT - 1) / FBT;
+  int best = 64;
+  double best_eff = -1;
+  const bool direct = profile_of(p) == PBF16;   // direct-load tiles fit BJ <= 96
+  for (int bj : {128, 96, 64}) {
+    if (direct && bj == 128) continue;
+    if (p.d % bj) continue;
+    const int64_t wgs = tt * (p.d / bj) * p.n_inst;
+    const int64_t rounds = (wgs + 255) / 256;
+    const double eff = (double)wgs / (double)(rounds * 256);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = bj;
+    }
+  }
+  return best;
+}
+
+int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
+
 // --------------------------------------------------------------- workspace layout
 struct Ws {
-  size_t e = 0, h = 0, part = 0, u = 0, am = 0, bm = 0, xa = 0, xb = 0, rowsq = 0, total = 0;
+  size_t e = 0, h = 0, part = 0, bpart = 0, snap = 0, u = 0, am = 0, bm = 0, xa = 0, xb = 0, rowsq = 0, total = 0;
+  size_t snap_slot = 0;   // bytes per snapshot slot (W1, W2, W3, W2^T)
   int S = 1;
+  int nslots = 1;
+  int64_t ldE = 0;
+  int64_t h_rows = 0;
+  int max_tt = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -209,19 +247,30 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   };
   // the token split count is not monotone in the chunk length (rounding of
   // the split size), so size the partials for the largest count of any step
-  int S = 1;
+  int S = 1, nupd = 0;
+  int64_t h_rows = 0;
   for (const Step& st : plan.steps) {
+    h_rows += st.app_len;
     if (st.upd_len == 0) continue;
+    ++nupd;
     int s_ = 1;
     int64_t kps = 0;
     dw_split(p, st.upd_len, s_, kps);
     S = std::max(S, s_);
   }
   w.S = S;
-  w.e = take(n * (size_t)plan.max_upd * 3 * D * rec_size(f));
-  w.h = take(n * (size_t)plan.max_app * D * app_size(f));
+  w.nslots = nupd + 1;
+  w.ldE = round64(plan.max_upd);
+  w.h_rows = h_rows;
+  w.max_tt = (int)((plan.max_upd + FBT - 1) / FBT);
+  const size_t snap_el = (f == PF32) ? 4 : 2;
+  w.snap_slot = align256(4 * n * D * D * snap_el);
+  w.e = take(n * 3 * D * (size_t)w.ldE * rec_size(f));
+  w.h = take(n * (size_t)h_rows * D * app_size(f));
   const size_t mats = n * 3 * D * D * sizeof(float);
   w.part = take(plan.max_upd > 0 ? (size_t)S * mats : 0);
+  w.bpart = take(p.opt == LACT_OPT_MOMENTUM ? n * (size_t)w.max_tt * sizeof(float) : 0);
+  w.snap = take(w.snap_slot * (size_t)w.nslots);
   if (p.opt == LACT_OPT_MUON && plan.max_upd > 0) {
     w.u = take(mats);
     w.am = take(mats);
@@ -306,46 +355,117 @@ struct Ptrs {
   char* ws = nullptr;
 };
 
-template <typename TIO_, int PIO_, int PWU_, int PWA_, typename TREC_, int PREC_, typename TAPP_, int PAPP_>
+// TIO/PIO: inputs; TS/PS: weight snapshots (apply, and the update forward in
+// plain bf16); PWU: planes of fp32 weights in the update forward when it reads
+// the master copy; TREC/PREC: update terms and Newton-Schulz operands;
+// TAPP/PAPP: gated hidden of the queries.
+template <typename TIO_, int PIO_, typename TS_, int PS_, int PWU_, typename TREC_, int PREC_, typename TAPP_,
+          int PAPP_>
 struct ProfT {
   using TIO = TIO_;
+  using TS = TS_;
   using TREC = TREC_;
   using TAPP = TAPP_;
-  static constexpr int PIO = PIO_, PWU = PWU_, PWA = PWA_, PREC = PREC_, PAPP = PAPP_;
+  static constexpr int PIO = PIO_, PS = PS_, PWU = PWU_, PREC = PREC_, PAPP = PAPP_;
+  static constexpr bool UPD_FROM_SNAP = (PWU_ == 0);
 };
-using ProfF32 = ProfT<float, 3, 3, 3, float, 3, float, 3>;
-using ProfBF16 = ProfT<bf16_t, 1, 1, 1, bf16_t, 1, bf16_t, 1>;
-using ProfBF16X2 = ProfT<bf16_t, 1, 2, 1, float, 2, bf16_t, 1>;
-using ProfBF16X3 = ProfT<bf16_t, 1, 3, 1, float, 3, bf16_t, 1>;
+using ProfF32 = ProfT<float, 3, float, 3, 3, float, 3, float, 3>;
+using ProfBF16 = ProfT<bf16_t, 1, bf16_t, 1, 0, bf16_t, 1, bf16_t, 1>;
+using ProfBF16X2 = ProfT<bf16_t, 1, bf16_t, 1, 2, float, 2, bf16_t, 1>;
+using ProfBF16X3 = ProfT<bf16_t, 1, bf16_t, 1, 3, float, 3, bf16_t, 1>;
 
+// k-stage depth and buffering that fit the LDS
+constexpr int pick_bk(int planes_sum) { return planes_sum <= 2 ? 64 : 32; }
+constexpr int stage_words(int rows_a, int pa, int rows_b, int pb, int bk) { return (rows_a * pa + rows_b * pb) * (bk + 8); }
+constexpr int pick_stages(int words) { return 2 * words * 2 + 4096 <= LDS_MAX ? 2 : 1; }
+
+template <typename TA, int PA, bool CA, typename TB, int PB, bool CB, typename TC, int BM>
+lact_status launch_gemm_t(const GemmArgs& g, int64_t grid, hipStream_t s) {
+  if constexpr (sizeof(TA) == 2 && sizeof(TB) == 2) {
+    // both operands bf16: direct-load kernel, 4-deep LDS ring
+    hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, BM, 2>), dim3((unsigned)grid), dim3(NT), 0, s, g);
+    HIP_TRY(hipGetLastError());
+    return LACT_OK;
+  }
+  constexpr int BKK = pick_bk(PA + PB);
+  constexpr int ST = pick_stages(stage_words(BM, PA, BM, PB, BKK));
+  hipLaunchKernelGGL((gemm_kernel<TA, PA, CA, TB, PB, CB, TC, BM, BM, BKK, ST>), dim3((unsigned)grid), dim3(NT), 0, s,
+                     g);
+  HIP_TRY(hipGetLastError());
+  return LACT_OK;
+}
+
+// fills in per-group tile counts and launches
 template <typename TA, int PA, bool CA, typename TB, int PB, bool CB, typename TC>
 lact_status launch_gemm(GemmArgs g, int tile, int kclass, hipStream_t s) {
-  const int64_t tiles = (int64_t)((g.M + tile - 1) / tile) * ((g.N + tile - 1) / tile);
-  const int64_t grid = tiles * g.batch * g.splits;
+  int64_t grid = 0;
+  for (int i = 0; i < g.ngroups; ++i) {
+    const int64_t t = (int64_t)((g.g[i].M + tile - 1) / tile) * ((g.N + tile - 1) / tile) * g.batch * g.splits;
+    if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+    g.g[i].tiles = (int)t;
+    grid += t;
+  }
   if (grid <= 0) return LACT_OK;
   if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
   KernelTimer kt(kclass, s);
-  if (tile == 128)
-    hipLaunchKernelGGL((gemm_kernel<TA, PA, CA, TB, PB, CB, TC, 128, 128>), dim3((unsigned)grid), dim3(NT), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_kernel<TA, PA, CA, TB, PB, CB, TC, 64, 64>), dim3((unsigned)grid), dim3(NT), 0, s, g);
-  HIP_TRY(hipGetLastError());
-  return LACT_OK;
+  if (tile == 128) return launch_gemm_t<TA, PA, CA, TB, PB, CB, TC, 128>(g, grid, s);
+  return launch_gemm_t<TA, PA, CA, TB, PB, CB, TC, 64>(g, grid, s);
 }
 
 GemmArgs gemm_args() {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
+  g.ngroups = 1;
   g.splits = 1;
+  g.batch = 1;
   g.alpha = 1.f;
   g.m_switch = 1 << 30;
+  g.trans_from = 1 << 30;
   return g;
+}
+
+// bf16 snapshot profile: direct-load kernels
+constexpr bool direct_fits(int bytes) { return bytes + 1024 <= LDS_MAX; }
+
+template <typename PT, int BJ>
+lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
+  if constexpr (PT::UPD_FROM_SNAP && (BJ == 64 || BJ == 96)) {
+    hipLaunchKernelGGL((dupd_fwd_kernel<BJ, 64, 2>), dim3((unsigned)grid), dim3(NT), 0, s, ua);
+    HIP_TRY(hipGetLastError());
+    return LACT_OK;
+  }
+  using TW = typename std::conditional<PT::UPD_FROM_SNAP, typename PT::TS, float>::type;
+  constexpr int PW = PT::UPD_FROM_SNAP ? PT::PS : PT::PWU;
+  constexpr int BKK = pick_bk(PT::PIO + PW);
+  constexpr int words = (2 * PT::PIO * FBT + 3 * PW * BJ) * (BKK + 8);
+  constexpr int ST = pick_stages(words);
+  hipLaunchKernelGGL((upd_fwd_kernel<typename PT::TIO, PT::PIO, TW, PW, typename PT::TREC, BJ, BKK, ST>),
+                     dim3((unsigned)grid), dim3(NT), 0, s, ua);
+  HIP_TRY(hipGetLastError());
+  return LACT_OK;
+}
+
+template <typename PT, int BJ>
+lact_status launch_app_fwd(const AppFwdArgs& aa, int64_t grid, hipStream_t s) {
+  if constexpr (sizeof(typename PT::TIO) == 2 && sizeof(typename PT::TS) == 2) {
+    hipLaunchKernelGGL((dapp_fwd_kernel<BJ, 32, 3>), dim3((unsigned)grid), dim3(NT), 0, s, aa);
+    HIP_TRY(hipGetLastError());
+    return LACT_OK;
+  }
+  constexpr int BKK = pick_bk(PT::PIO + PT::PS);
+  constexpr int words = (PT::PIO * FBT + 2 * PT::PS * BJ) * (BKK + 8);
+  constexpr int ST = pick_stages(words);
+  hipLaunchKernelGGL((app_fwd_kernel<typename PT::TIO, PT::PIO, typename PT::TS, PT::PS, typename PT::TAPP, BJ, BKK, ST>),
+                     dim3((unsigned)grid), dim3(NT), 0, s, aa);
+  HIP_TRY(hipGetLastError());
+  return LACT_OK;
 }
 
 template <typename PT>
 lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, const Plan& plan, const Ws& w,
                       hipStream_t s) {
   using TIO = typename PT::TIO;
+  using TS = typename PT::TS;
   using TREC = typename PT::TREC;
   using TAPP = typename PT::TAPP;
   const int n = p.n_inst, D = p.d;
@@ -353,86 +473,85 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
   const int64_t DD = (int64_t)D * D;
   const int64_t x_bs = seq_stride * D;
   char* ws = P.ws;
+  const size_t snap_mat = (size_t)n * DD * sizeof(TS);
+  // snapshot slot k holds the weights after k updates: W1, W2, W3, W2^T
+  auto slot = [&](int k, int m) -> void* { return ws + w.snap + (size_t)k * w.snap_slot + (size_t)m * snap_mat; };
+
+  {
+    const int64_t n4 = (int64_t)n * DD / 4;
+    hipLaunchKernelGGL(snap_kernel<TS>, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), 0, s, P.W1, P.W2, P.W3,
+                       slot(0, 0), slot(0, 1), slot(0, 2), sizeof(TS) == 2 ? slot(0, 3) : nullptr, (int64_t)n * DD, D);
+    HIP_TRY(hipGetLastError());
+  }
+
+  // ---------------------------------------------------------------- recurrence
+  int nu = 0;   // updates done so far
   for (const Step& st : plan.steps) {
-    // ---- forward tiles (apply hidden + update terms), all on the current weights
-    FwdArgs fa;
-    memset(&fa, 0, sizeof(fa));
-    fa.q = P.q;
-    fa.k = P.k;
-    fa.v = P.v;
-    fa.x_bs = x_bs;
-    fa.lr = P.lr;
-    fa.lr_bs = seq_stride * 3;
-    fa.W1 = P.W1;
-    fa.W2 = P.W2;
-    fa.W3 = P.W3;
-    fa.E = ws + w.e;
-    fa.e_bs = st.upd_len * 3 * D;
-    fa.H = ws + w.h;
-    fa.h_bs = st.app_len * D;
-    fa.D = D;
-    fa.upd_t0 = st.upd_t0;
-    fa.upd_len = st.upd_len;
-    fa.app_t0 = st.app_t0;
-    fa.app_len = st.app_len;
-    fa.upd_tiles = (int)((st.upd_len + FBT - 1) / FBT) * (D / FBJ);
-    fa.app_tiles = (int)((st.app_len + FBT - 1) / FBT) * (D / FBJ);
-    const int64_t fgrid = (int64_t)n * (fa.upd_tiles + fa.app_tiles);
-    if (fgrid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
-    if (fgrid > 0) {
-      KernelTimer kt(LACT_K_FWD, s);
-      hipLaunchKernelGGL((fwd_kernel<TIO, PT::PIO, PT::PWU, PT::PWA, TREC, TAPP>), dim3((unsigned)fgrid), dim3(NT), 0,
-                         s, fa);
-      HIP_TRY(hipGetLastError());
+    if (st.upd_len == 0) continue;
+    const int64_t C = st.upd_len;
+    // forward products on k, v and the SwiGLU backward terms
+    UpdFwdArgs ua;
+    memset(&ua, 0, sizeof(ua));
+    ua.k = P.k;
+    ua.v = P.v;
+    ua.x_bs = x_bs;
+    ua.lr = P.lr;
+    ua.lr_bs = seq_stride * 3;
+    ua.beta = p.opt == LACT_OPT_MOMENTUM ? P.beta : nullptr;
+    ua.beta_bs = seq_stride;
+    ua.bpart = reinterpret_cast<float*>(ws + w.bpart);
+    if (PT::UPD_FROM_SNAP) {
+      ua.W1 = slot(nu, 0);
+      ua.W3 = slot(nu, 2);
+      ua.W2x = slot(nu, 3);
+    } else {
+      ua.W1 = P.W1;
+      ua.W3 = P.W3;
+      ua.W2x = P.W2;
     }
-    // ---- apply output: o[t, r] = sum_j Hq[t, j] W2[r, j]
-    if (st.app_len > 0) {
-      GemmArgs g = gemm_args();
-      g.A = ws + w.h;
-      g.lda = D;
-      g.a_bs = st.app_len * D;
-      g.B = P.W2;
-      g.ldb = D;
-      g.b_bs = DD;
-      g.C = static_cast<char*>(P.o) + (size_t)st.app_t0 * D * io_size(p);
-      g.ldc = D;
-      g.c_bs = x_bs;
-      g.M = (int)st.app_len;
-      g.N = D;
-      g.K = D;
-      g.kps = D;
-      g.batch = n;
-      const int64_t w128 = ((st.app_len + 127) / 128) * (D / 128 > 0 ? D / 128 : 1) * n;
-      lact_status r = launch_gemm<TAPP, PT::PAPP, false, float, PT::PWA, false, TIO>(g, gemm_tile(w128), LACT_K_OUT, s);
+    ua.E = ws + w.e;
+    ua.ldE = round64(C);
+    ua.D = D;
+    ua.upd_t0 = st.upd_t0;
+    ua.upd_len = C;
+    ua.tiles_t = (int)((C + FBT - 1) / FBT);
+    {
+      const int bj = upd_bj(p, C);
+      const int64_t grid = (int64_t)n * ua.tiles_t * (D / bj);
+      if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+      KernelTimer kt(LACT_K_FWD, s);
+      lact_status r = bj == 128 ? launch_upd_fwd<PT, 128>(ua, grid, s)
+                      : bj == 96 ? launch_upd_fwd<PT, 96>(ua, grid, s)
+                                 : launch_upd_fwd<PT, 64>(ua, grid, s);
       if (r) return r;
     }
-    if (st.upd_len == 0) continue;
-    // ---- weight-gradient contraction over the chunk's tokens (split over tokens)
+    // weight-gradient contraction over the chunk's tokens (split over tokens)
     int S;
     int64_t kps;
-    dw_split(p, st.upd_len, S, kps);
+    dw_split(p, C, S, kps);
     if (S > w.S) return fail(LACT_ERR_UNSUPPORTED, "internal: token split %d exceeds workspace plan %d", S, w.S);
     {
       GemmArgs g = gemm_args();
-      g.A = ws + w.e;              // (m, t) = E[t, m], m over [U1 | U3 | U2^T] rows
-      g.lda = 3 * D;
-      g.a_bs = st.upd_len * 3 * D;
-      g.B = static_cast<const char*>(P.k) + (size_t)st.upd_t0 * D * io_size(p);
+      g.g[0].A = ws + w.e;         // (m, t) = E[m, t]: rows U1 | U3 | U2^T terms
+      g.lda = ua.ldE;
+      g.a_bs = 3 * D * ua.ldE;
+      g.g[0].B = static_cast<const char*>(P.k) + (size_t)st.upd_t0 * D * io_size(p);
       g.B2 = static_cast<const char*>(P.v) + (size_t)st.upd_t0 * D * io_size(p);
       g.m_switch = 2 * D;
+      g.trans_from = 2 * D;        // the U2 block is stored as U2 (not U2^T)
       g.ldb = D;
       g.b_bs = x_bs;
-      g.C = ws + w.part;
+      g.g[0].C = ws + w.part;
       g.ldc = D;
       g.c_bs = 3 * DD;
       g.c_ss = (int64_t)n * 3 * DD;
-      g.M = 3 * D;
+      g.g[0].M = 3 * D;
       g.N = D;
-      g.K = st.upd_len;
+      g.K = C;
       g.kps = kps;
       g.batch = n;
       g.splits = S;
-      lact_status r = launch_gemm<TREC, PT::PREC, true, TIO, PT::PIO, true, float>(g, dw_tile(p), LACT_K_DW, s);
+      lact_status r = launch_gemm<TREC, PT::PREC, false, TIO, PT::PIO, true, float>(g, dw_tile(p), LACT_K_DW, s);
       if (r) return r;
     }
     OptArgs oa;
@@ -446,16 +565,19 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     oa.D = D;
     oa.opt = p.opt;
     oa.renorm = (p.flags & LACT_NO_RENORM) ? 0 : 1;
-    oa.beta = P.beta;
-    oa.beta_bs = seq_stride;
-    oa.beta_t0 = st.upd_t0;
-    oa.beta_len = st.upd_len;
+    oa.bpart = reinterpret_cast<const float*>(ws + w.bpart);
+    oa.nbp = ua.tiles_t;
+    oa.inv_len = 1.0f / (float)C;
+    oa.snap[0] = slot(nu + 1, 0);
+    oa.snap[1] = slot(nu + 1, 2);
+    oa.snap[2] = slot(nu + 1, 1);
+    oa.snapT2 = sizeof(TS) == 2 ? slot(nu + 1, 3) : nullptr;
     if (p.opt != LACT_OPT_MUON) {
       oa.src = reinterpret_cast<const float*>(ws + w.part);
       oa.src_ss = (int64_t)n * 3 * DD;
       oa.splits = S;
     } else {
-      // ---- Muon: U = sum of partials, then quintic Newton-Schulz on every matrix
+      // Muon: U = sum of partials, then quintic Newton-Schulz on every matrix
       float* U = reinterpret_cast<float*>(ws + w.u);
       float* rowsq = reinterpret_cast<float*>(ws + w.rowsq);
       {
@@ -479,13 +601,14 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
         GemmArgs g = gemm_args();
         g.lda = g.ldb = g.ldc = g.ldcin = D;
         g.a_bs = g.b_bs = g.c_bs = g.cin_bs = DD;
-        g.M = g.N = D;
+        g.g[0].M = D;
+        g.N = D;
         g.K = g.kps = D;
         g.batch = nb;
         // A = X X^T (X = s U on the first step)
-        g.A = Xin;
-        g.B = Xin;
-        g.C = Am;
+        g.g[0].A = Xin;
+        g.g[0].B = Xin;
+        g.g[0].C = Am;
         if (first) {
           g.rowsq = rowsq;
           g.rowsq_n = D;
@@ -496,18 +619,18 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
         // B = b A + c A A   (A is symmetric: A A = A A^T)
         g.rowsq = nullptr;
         g.alpha_pow = 0;
-        g.A = Am;
-        g.B = Am;
-        g.C = Bm;
+        g.g[0].A = Am;
+        g.g[0].B = Am;
+        g.g[0].C = Bm;
         g.Cin = Am;
         g.alpha = cc;
         g.beta = cb;
         r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
         if (r) return r;
         // X' = a X + B X
-        g.A = Bm;
-        g.B = Xin;     // element (n = j, k) = X[k, j]: column-k source
-        g.C = Xout;
+        g.g[0].A = Bm;
+        g.g[0].B = Xin;  // element (n = j, k) = X[k, j]: column-k source
+        g.g[0].C = Xout;
         g.Cin = Xin;
         g.alpha = 1.f;
         g.beta = ca;
@@ -527,10 +650,85 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     }
     {
       KernelTimer kt(LACT_K_OPT, s);
-      const size_t lds = 0;
-      hipLaunchKernelGGL(opt_kernel, dim3((unsigned)(n * 3 * (D / OPT_ROWS))), dim3(NT), lds, s, oa);
+      hipLaunchKernelGGL(opt_kernel<TS>, dim3((unsigned)(n * 3 * (D / OPT_ROWS))), dim3(NT), 0, s, oa);
       HIP_TRY(hipGetLastError());
     }
+    ++nu;
+  }
+
+  // ---------------------------------------------------------------- apply (all chunks)
+  std::vector<AppGroup> groups;
+  {
+    int u = 0;
+    int64_t h0 = 0;
+    for (const Step& st : plan.steps) {
+      if (st.app_len > 0) {
+        AppGroup ag;
+        memset(&ag, 0, sizeof(ag));
+        ag.t0 = st.app_t0;
+        ag.len = st.app_len;
+        ag.h0 = h0;
+        ag.W1 = slot(u, 0);
+        ag.W3 = slot(u, 2);
+        groups.push_back(ag);
+        h0 += st.app_len;
+      }
+      if (st.upd_len > 0) ++u;
+    }
+  }
+  const int abj = D % 128 == 0 ? 128 : 64;
+  for (size_t g0 = 0; g0 < groups.size(); g0 += MAXG) {
+    const int ng = (int)std::min<size_t>(MAXG, groups.size() - g0);
+    AppFwdArgs aa;
+    memset(&aa, 0, sizeof(aa));
+    aa.ngroups = ng;
+    aa.q = P.q;
+    aa.x_bs = x_bs;
+    aa.H = ws + w.h;
+    aa.h_bs = w.h_rows * D;
+    aa.D = D;
+    int64_t grid = 0;
+    for (int i = 0; i < ng; ++i) {
+      aa.g[i] = groups[g0 + i];
+      const int64_t t = ((aa.g[i].len + FBT - 1) / FBT) * (D / abj) * n;
+      if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+      aa.g[i].tiles = (int)t;
+      grid += t;
+    }
+    if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+    {
+      KernelTimer kt(LACT_K_FWD, s);
+      lact_status r = abj == 128 ? launch_app_fwd<PT, 128>(aa, grid, s) : launch_app_fwd<PT, 64>(aa, grid, s);
+      if (r) return r;
+    }
+    // o[t, r] = sum_j Hq[t, j] W2[r, j]
+    GemmArgs g = gemm_args();
+    g.ngroups = ng;
+    int64_t wgs128 = 0;
+    for (int i = 0; i < ng; ++i) {
+      const AppGroup& ag = aa.g[i];
+      g.g[i].A = static_cast<const char*>(aa.H) + (size_t)ag.h0 * D * app_size(profile_of(p));
+      int u = 0;
+      // the snapshot this group reads is the one its W1 came from
+      for (int k = 0; k < w.nslots; ++k)
+        if (slot(k, 0) == ag.W1) u = k;
+      g.g[i].B = slot(u, 1);
+      g.g[i].C = static_cast<char*>(P.o) + (size_t)ag.t0 * D * io_size(p);
+      g.g[i].M = (int)ag.len;
+      wgs128 += ((ag.len + 127) / 128) * std::max(1, D / 128) * n;
+    }
+    g.lda = D;
+    g.a_bs = w.h_rows * D;
+    g.ldb = D;
+    g.b_bs = DD;
+    g.ldc = D;
+    g.c_bs = x_bs;
+    g.N = D;
+    g.K = g.kps = D;
+    g.batch = n;
+    lact_status r =
+        launch_gemm<TAPP, PT::PAPP, false, TS, PT::PS, false, TIO>(g, gemm_tile(wgs128), LACT_K_OUT, s);
+    if (r) return r;
   }
   return LACT_OK;
 }

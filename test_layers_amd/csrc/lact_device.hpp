@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lact {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -49,6 +51,14 @@ template <> struct io_traits<bf16_t> {
   static constexpr int VE = 8;
   __device__ static void store(bf16_t* p, float x) { p->x = (uint16_t)f2bf(x); }
 };
+
+// four consecutive values as one vector store (16 B fp32 / 8 B bf16)
+__device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16_t* p, const float (&v)[4]) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(f2bf(v[0]) | (f2bf(v[1]) << 16), f2bf(v[2]) | (f2bf(v[3]) << 16));
+}
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
@@ -212,7 +222,11 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 // acc[i][j] += sum over plane pairs of A[i] * B[j] for one 32-wide k slice.
 // Smaller plane pairs go first (they carry the low-order bits).
-template <int PA, int PB, int FM, int FN, int SA, int SB>
+// SWAP = false: acc[i][j] lane l holds C rows 4*(l/16)+r, column l%16 of the
+//               16x16 block (4 consecutive rows per lane);
+// SWAP = true:  the operands enter the MFMA in the other order, so lane l
+//               holds row l%16, columns 4*(l/16)+r (4 consecutive columns).
+template <int PA, int PB, int FM, int FN, int SA, int SB, bool SWAP = false>
 __device__ __forceinline__ void mma_tile(f32x4 (&acc)[FM][FN], const uint16_t* la, int pla_stride,
                                          int arow0, const uint16_t* lb, int plb_stride, int brow0,
                                          int kk, int lane) {
@@ -236,7 +250,64 @@ __device__ __forceinline__ void mma_tile(f32x4 (&acc)[FM][FN], const uint16_t* l
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma(a[pa][i], b[pb][j], acc[i][j]);
+            for (int j = 0; j < FN; ++j) {
+              if constexpr (SWAP) acc[i][j] = mfma(b[pb][j], a[pa][i], acc[i][j]);
+              else acc[i][j] = mfma(a[pa][i], b[pb][j], acc[i][j]);
+            }
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Software pipeline over nk k-stages.  Tiles are fetched two stages ahead
+// into two alternating register sets (fetch(IC<set>, stage)), written to one
+// of two LDS buffers (put(IC<set>, IC<buf>)) a full stage after their loads
+// were issued, and consumed by compute(IC<buf>); one barrier per stage.  With
+// LDS_STAGES = 1 the single buffer is rewritten between two barriers.
+template <int LDS_STAGES, class F, class P, class C>
+__device__ __forceinline__ void pipeline(int nk, F&& fetch, P&& put, C&& compute) {
+  if (nk <= 0) return;
+  fetch(IC<0>{}, 0);
+  if (nk > 1) fetch(IC<1>{}, 1);
+  if constexpr (LDS_STAGES == 2) {
+    put(IC<0>{}, IC<0>{});
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      if (kt + 2 < nk) fetch(IC<0>{}, kt + 2);
+      compute(IC<0>{});
+      if (kt + 1 < nk) put(IC<1>{}, IC<1>{});
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      if (kt + 3 < nk) fetch(IC<1>{}, kt + 3);
+      compute(IC<1>{});
+      if (kt + 2 < nk) put(IC<0>{}, IC<0>{});
+      __syncthreads();
+    }
+  } else {
+    for (int kt = 0; kt < nk; kt += 2) {
+      put(IC<0>{}, IC<0>{});
+      __syncthreads();
+      if (kt + 2 < nk) fetch(IC<0>{}, kt + 2);
+      compute(IC<0>{});
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      put(IC<1>{}, IC<0>{});
+      __syncthreads();
+      if (kt + 3 < nk) fetch(IC<1>{}, kt + 3);
+      compute(IC<0>{});
+      __syncthreads();
+    }
+  }
+}
+
+// Workgroup b runs on XCD b % 8 (round-robin dispatch; each XCD has its own
+// L2).  Map it to a logical index so that each XCD receives one contiguous
+// block of logical indices: tiles that share operands then share an L2.
+constexpr int NXCD = 8;
+__device__ __forceinline__ int xcd_remap(int b, int nwg) {
+  const int per = nwg / NXCD, rem = nwg % NXCD;
+  const int x = b % NXCD, s = b / NXCD;
+  return x < rem ? x * (per + 1) + s : rem * (per + 1) + (x - rem) * per + s;
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

@@ -1,0 +1,571 @@
+// bf16 kernels built on gfx950's direct global->LDS loads.
+//
+// Tiles are copied from global memory into LDS with global_load_lds_dwordx4
+// (16 bytes per lane, landing at the wave's LDS base + 16 * lane), so no
+// staging registers are needed and several k-stages can be in flight.  LDS
+// rows hold 16-byte chunks XOR-swizzled by row to keep fragment reads free of
+// bank conflicts.  Operands whose k index is the slow dimension in memory (a
+// token-major activation contracted over tokens) are read into MFMA
+// fragments with ds_read_b64_tr_b16: in each 16-lane group, output lane i,
+// element r is element (i % 4) of source lane 4r + i/4, so source lane j
+// points at row 8g + j/4, columns 4(j % 4) .. +3 of the tile and two such
+// reads give lane (g, i) the 8 consecutive k of column i.
+#pragma once
+#include "lact_kernels.hpp"
+
+namespace lact {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt that only waits for vector-memory counts <= N (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies (the
+// fence would wait for every in-flight direct load); the empty asm keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Byte offset of an LDS location (generic pointer to __shared__ memory).
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One global_load_lds_dwordx4: 16 bytes per lane from g to LDS byte offset
+// m0 + 16 * lane.  Issued from asm because the compiler, unable to tell ring
+// buffers apart, would otherwise wait for every in-flight copy before each
+// LDS read; completion is tracked with explicit vmcnt waits instead.  The
+// instruction has no register outputs.
+__device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(m0)
+               : "memory", "m0");
+}
+
+// LDS tile of R rows x CC bf16 columns (CC = 32, 64 or 128), filled by NW
+// waves.  Chunk c (16 bytes) of row r is stored at chunk swz(r, c) of that
+// row.  The swizzle spreads the rows a fragment read touches over distinct
+// bank groups: 8 rows x 16 B for row-k reads of 64- and 128-byte rows, and
+// for 256-byte rows read with ds_read_b64_tr_b16, the 32-byte column pairs of
+// rows r..r+3 and r+8..r+11 (two 16-lane groups) over all eight 32-byte slots.
+template <int R, int CC, int NW = 4>
+struct DTile {
+  static constexpr int CPR = CC / 8;
+  static constexpr int BYTES = R * CC * 2;
+  static constexpr int CHUNKS = R * CPR;
+  static constexpr int INSTR = CHUNKS / (WAVE * NW);   // loads per wave
+  static_assert(CHUNKS % (WAVE * NW) == 0, "tile must be a whole number of workgroup loads");
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row width");
+  __device__ static __forceinline__ int swz(int r, int c) {
+    if constexpr (CPR == 4) return c ^ ((r >> 1) & 3);
+    else if constexpr (CPR == 8) return c ^ (r & 7);
+    else return c ^ ((((r & 3) | (((r >> 3) & 1) << 2))) << 1);
+  }
+  __device__ static __forceinline__ int phys(int row, int chunk) { return row * CPR + swz(row, chunk); }
+
+  // Per-lane global pointers of the tile's loads for one stage: rows
+  // r0 .. r0+R-1 (clamped to rmax) of a row-major bf16 matrix with row stride
+  // ld elements, columns c0 .. c0+CC-1.  Later stages are reached by adding a
+  // byte offset, so the address arithmetic is paid once per kernel.
+  struct Plan {
+    const char* p[INSTR];
+  };
+  __device__ static __forceinline__ Plan plan(const bf16_t* base, int64_t ld, int64_t r0, int64_t rmax, int64_t c0,
+                                              int wave, int lane) {
+    Plan pl;
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int q = (i * NW + wave) * WAVE + lane;
+      const int row = q / CPR, slot = q % CPR;
+      const int c = swz(row, slot);   // swz is an involution in c
+      const int64_t gr = min(r0 + row, rmax);
+      pl.p[i] = reinterpret_cast<const char*>(base + gr * ld + c0 + c * 8);
+    }
+    return pl;
+  }
+  // load i of the stage (0 <= i < INSTR)
+  __device__ static __forceinline__ void issue_one(char* tile, const Plan& pl, int64_t byte_off, int wave, int i) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_off(tile) + (uint32_t)((i * NW + wave) * WAVE * 16));
+    dma16(pl.p[i] + byte_off, m0);
+  }
+  __device__ static __forceinline__ void issue_one(char* tile, const bf16_t* base, int64_t ld, int64_t r0, int64_t rmax,
+                                                   int64_t c0, int wave, int lane, int i) {
+    const int q = (i * NW + wave) * WAVE + lane;
+    const int row = q / CPR, slot = q % CPR;
+    const int64_t gr = min(r0 + row, rmax);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_off(tile) + (uint32_t)((i * NW + wave) * WAVE * 16));
+    dma16(base + gr * ld + c0 + swz(row, slot) * 8, m0);
+  }
+  __device__ static __forceinline__ void issue(char* tile, const Plan& pl, int64_t byte_off, int wave) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_off(tile) + (uint32_t)(wave * WAVE * 16));
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) dma16(pl.p[i] + byte_off, m0 + (uint32_t)(i * NW * WAVE * 16));
+  }
+  // one-off load with full address arithmetic (ragged last stage)
+  __device__ static __forceinline__ void issue(char* tile, const bf16_t* base, int64_t ld, int64_t r0, int64_t rmax,
+                                               int64_t c0, int wave, int lane) {
+    issue(tile, plan(base, ld, r0, rmax, c0, wave, lane), 0, wave);
+  }
+};
+
+// fragment of a tile whose rows are the MFMA row index and columns are k
+template <class T>
+__device__ __forceinline__ bf16x8 dfrag_row(const char* tile, int row0, int kk, int lane) {
+  const int row = row0 + (lane & 15);
+  const int chunk = (kk >> 3) + (lane >> 4);
+  return *reinterpret_cast<const bf16x8*>(tile + T::phys(row, chunk) * 16);
+}
+
+// fragment of a tile whose rows are k and columns are the MFMA row index
+template <class T>
+__device__ __forceinline__ bf16x8 dfrag_col(const char* tile, int n0, int kk, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = kk + 8 * g + (j >> 2);
+  const int col = n0 + 4 * (j & 3);
+  const int chunk = col >> 3, half = (col >> 2) & 1;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(tile + T::phys(row, chunk) * 16 + half * 8));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(tile + T::phys(row + 4, chunk) * 16 + half * 8));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <class T, bool COLK>
+__device__ __forceinline__ bf16x8 dfrag(const char* tile, int r0, int kk, int lane) {
+  if constexpr (COLK) return dfrag_col<T>(tile, r0, kk, lane);
+  else return dfrag_row<T>(tile, r0, kk, lane);
+}
+
+// Direct-load pipeline over nk stages with an NST-deep LDS ring: stage s is
+// issued NST-1 iterations before it is consumed.  issue(s, buf) must emit
+// exactly LPS global_load_lds per wave.
+template <int NST, int LPS, class I, class C>
+__device__ __forceinline__ void dpipeline(int nk, I&& issue, C&& compute) {
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt is complete once at most min(NST-2, nk-1-kt) later stages are in flight
+    const int later = min(NST - 2, nk - 1 - kt);
+    if constexpr (NST >= 4) {
+      if (later >= 2) wait_vm<2 * LPS>();
+      else if (later == 1) wait_vm<LPS>();
+      else wait_vm<0>();
+    } else if constexpr (NST == 3) {
+      if (later >= 1) wait_vm<LPS>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    bar();
+    if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
+    compute(kt % NST);
+  }
+}
+
+// Same ring, but the loads of the stage being prefetched are spread over the
+// MFMA groups of the stage being computed: compute(buf, hook) calls
+// hook(slot, nslots) after each group, and the hook issues loads
+// [slot * LPS / nslots, (slot + 1) * LPS / nslots) of the prefetched stage via
+// issue_one(stage, buf, index).  A wave blocked on a full memory queue then
+// stalls between MFMA groups instead of ahead of all of them.
+template <int NST, int LPS, class I, class C>
+__device__ __forceinline__ void dpipeline_il(int nk, I&& issue_one, C&& compute) {
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk)
+#pragma unroll
+      for (int i = 0; i < LPS; ++i) issue_one(s, s, i);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int later = min(NST - 2, nk - 1 - kt);
+    if constexpr (NST >= 4) {
+      if (later >= 2) wait_vm<2 * LPS>();
+      else if (later == 1) wait_vm<LPS>();
+      else wait_vm<0>();
+    } else if constexpr (NST == 3) {
+      if (later >= 1) wait_vm<LPS>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    bar();
+    const int ns = kt + NST - 1;
+    const bool nxt = ns < nk;
+    const int nb = ns % NST;
+    compute(kt % NST, [&](int slot, int nslots) {
+      if (nxt) {
+#pragma unroll
+        for (int i = 0; i < LPS; ++i)
+          if (i * nslots >= slot * LPS && i * nslots < (slot + 1) * LPS) issue_one(ns, nb, i);
+      }
+    });
+  }
+}
+
+// =========================================================================
+// bf16 GEMM (same contract as gemm_kernel; A, B bf16; 16x16x32 MFMA with the
+// swapped operand order so that each lane owns 4 consecutive output columns)
+template <bool CA, bool CB, typename TC, int BM, int BN, int NST>
+__global__ __launch_bounds__(NT) void dgemm_kernel(GemmArgs g) {
+  constexpr int BKK = 64;
+  // row-k tiles: BM x 64 (8 chunks per row); column-k tiles: 64 x BM
+  using TA = typename std::conditional<CA, DTile<BKK, BM>, DTile<BM, BKK>>::type;
+  using TB = typename std::conditional<CB, DTile<BKK, BN>, DTile<BN, BKK>>::type;
+  constexpr int STAGE = TA::BYTES + TB::BYTES;
+  constexpr int LPS = TA::INSTR + TB::INSTR;
+  constexpr int FM = BM / 32, FN = BN / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+  __shared__ float s_scale;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int gi = 0;
+  while (gi + 1 < g.ngroups && bid >= g.g[gi].tiles) bid -= g.g[gi++].tiles;
+  const GemmGroup& G = g.g[gi];
+  const int M = G.M;
+  const int tn_count = (g.N + BN - 1) / BN;
+  const int tm_count = (M + BM - 1) / BM;
+  const int tiles = tm_count * tn_count;
+  const int tile = bid % tiles;
+  bid /= tiles;
+  const int split = bid % g.splits;
+  const int b = bid / g.splits;
+  const int tm = tile / tn_count, tn = tile % tn_count;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const bf16_t* A = reinterpret_cast<const bf16_t*>(G.A) + b * g.a_bs;
+  const void* Bsrc = (g.B2 != nullptr && m0 >= g.m_switch) ? g.B2 : G.B;
+  const bf16_t* B = reinterpret_cast<const bf16_t*>(Bsrc) + b * g.b_bs;
+  const int64_t kbeg = (int64_t)split * g.kps;
+  const int64_t kend = min(g.K, kbeg + g.kps);
+  const int nk = kbeg < kend ? (int)((kend - kbeg + BKK - 1) / BKK) : 0;
+  // rows past the data are clamped: for row-k operands they are outputs that
+  // are never stored; for column-k operands they are k positions the other
+  // operand holds as zeros (callers pad it) or that lie in the valid range
+  const int64_t kmax = g.K - 1;
+
+  // column-k operands step BKK rows per stage, row-k operands BKK columns
+  const typename TA::Plan pa = CA ? TA::plan(A, g.lda, kbeg, kmax, m0, wave, lane) : TA::plan(A, g.lda, m0, M - 1, kbeg, wave, lane);
+  const typename TB::Plan pb = CB ? TB::plan(B, g.ldb, kbeg, kmax, n0, wave, lane) : TB::plan(B, g.ldb, n0, g.N - 1, kbeg, wave, lane);
+  const int64_t sa = CA ? (int64_t)BKK * g.lda * 2 : (int64_t)BKK * 2;
+  const int64_t sb = CB ? (int64_t)BKK * g.ldb * 2 : (int64_t)BKK * 2;
+  auto issue_one = [&](int s, int buf, int idx) {
+    char* st = smem + buf * STAGE;
+    const int64_t k0 = kbeg + (int64_t)s * BKK;
+    const bool ragged = k0 + BKK - 1 > kmax;   // a column-k stage past the data must clamp rows
+    if (idx < TA::INSTR) {
+      if (CA && ragged) TA::issue_one(st, A, g.lda, k0, kmax, m0, wave, lane, idx);
+      else TA::issue_one(st, pa, s * sa, wave, idx);
+    } else {
+      const int i = idx - TA::INSTR;
+      if (CB && ragged) TB::issue_one(st + TA::BYTES, B, g.ldb, k0, kmax, n0, wave, lane, i);
+      else TB::issue_one(st + TA::BYTES, pb, s * sb, wave, i);
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, auto&& hook) {
+    const char* st = smem + buf * STAGE;
+    constexpr int NSLOT = (BKK / 32) * FM;
+#pragma unroll
+    for (int kk = 0; kk < BKK; kk += 32) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = dfrag<TA, CA>(st, wm * (BM / 2) + i * 16, kk, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = dfrag<TB, CB>(st + TA::BYTES, wn * (BN / 2) + j * 16, kk, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma(bfr[j], af[i], acc[i][j]);
+        hook((kk / 32) * FM + i, NSLOT);
+      }
+    }
+  };
+  dpipeline_il<NST, LPS>(nk, issue_one, compute);
+
+  float alpha = g.alpha, beta = g.beta;
+  if (g.rowsq != nullptr) {
+    if (wave == 0) {
+      float s = 0.f;
+      const float* rq = g.rowsq + (int64_t)b * g.rowsq_n;
+      for (int i = lane; i < g.rowsq_n; i += WAVE) s += rq[i];
+      s = wave_sum(s);
+      if (lane == 0) s_scale = 1.0f / (sqrtf(s) + 1e-7f);
+    }
+    __syncthreads();
+    const float sc = s_scale;
+    for (int i = 0; i < g.alpha_pow; ++i) alpha *= sc;
+    for (int i = 0; i < g.beta_pow; ++i) beta *= sc;
+  }
+  TC* C = reinterpret_cast<TC*>(G.C) + b * g.c_bs + split * g.c_ss;
+  const float* Cin = g.Cin ? g.Cin + b * g.cin_bs : nullptr;
+  const bool trans = m0 >= g.trans_from;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int nq = n0 + wn * (BN / 2) + j * 16 + 4 * (lane >> 4);
+      if (nq >= g.N) continue;
+      float val[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) val[r] = alpha * acc[i][j][r];
+      if (Cin) {
+        const float4 c = *reinterpret_cast<const float4*>(Cin + (int64_t)m * g.ldcin + nq);
+        val[0] += beta * c.x;
+        val[1] += beta * c.y;
+        val[2] += beta * c.z;
+        val[3] += beta * c.w;
+      }
+      if (trans) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          io_traits<TC>::store(C + (int64_t)(g.trans_from + nq + r) * g.ldc + (m - g.trans_from), val[r]);
+      } else {
+        store4(C + (int64_t)m * g.ldc + nq, val);
+      }
+    }
+  }
+}
+
+// =========================================================================
+// bf16 update forward tile (same contract as upd_fwd_kernel with bf16
+// snapshots: W2 operand from the transposed snapshot)
+template <int BJ, int BKK, int NST>
+__global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
+  using TX = DTile<FBT, BKK>;   // K, V: 128 tokens x 64 k
+  using TW = DTile<BJ, BKK>;    // W1, W3, W2^T rows: BJ x 64 k
+  constexpr int STAGE = 2 * TX::BYTES + 3 * TW::BYTES;
+  constexpr int LPS = 2 * TX::INSTR + 3 * TW::INSTR;
+  constexpr int FN = BJ / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+  __shared__ float s_red[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int D = a.D;
+  const int njb = D / BJ;
+  const int per_inst = a.tiles_t * njb;
+  const int lbid = xcd_remap(blockIdx.x, gridDim.x);
+  const int inst = lbid / per_inst;
+  const int tile = lbid % per_inst;
+  const int tb = tile / njb, jb = tile % njb;
+  const int64_t t0 = a.upd_t0 + (int64_t)tb * FBT;
+  const int64_t tend = a.upd_t0 + a.upd_len;
+  const int j0 = jb * BJ;
+  const int64_t DD = (int64_t)D * D;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + inst * a.x_bs;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + inst * a.x_bs;
+  const bf16_t* W1 = reinterpret_cast<const bf16_t*>(a.W1) + inst * DD;
+  const bf16_t* W3 = reinterpret_cast<const bf16_t*>(a.W3) + inst * DD;
+  const bf16_t* W2T = reinterpret_cast<const bf16_t*>(a.W2x) + inst * DD;
+
+  if (a.beta != nullptr && jb == 0) {
+    float bsum = 0.f;
+    if (tid < FBT && t0 + tid < tend) bsum = a.beta[inst * a.beta_bs + t0 + tid];
+    bsum = wave_sum(bsum);
+    if (lane == 0 && wave < 2) s_red[wave] = bsum;
+    __syncthreads();
+    if (tid == 0) a.bpart[(int64_t)inst * a.tiles_t + tb] = s_red[0] + s_red[1];
+  }
+
+  const typename TX::Plan pk = TX::plan(K, D, t0, tend - 1, 0, wave, lane);
+  const typename TX::Plan pv = TX::plan(V, D, t0, tend - 1, 0, wave, lane);
+  const typename TW::Plan p1 = TW::plan(W1, D, j0, D - 1, 0, wave, lane);
+  const typename TW::Plan p3 = TW::plan(W3, D, j0, D - 1, 0, wave, lane);
+  const typename TW::Plan p2 = TW::plan(W2T, D, j0, D - 1, 0, wave, lane);
+  auto issue_one = [&](int s, int buf, int idx) {
+    char* st = smem + buf * STAGE;
+    const int64_t off = (int64_t)s * BKK * 2;
+    char* w = st + 2 * TX::BYTES;
+    if (idx < TX::INSTR) TX::issue_one(st, pk, off, wave, idx);
+    else if (idx < 2 * TX::INSTR) TX::issue_one(st + TX::BYTES, pv, off, wave, idx - TX::INSTR);
+    else if (idx < 2 * TX::INSTR + TW::INSTR) TW::issue_one(w, p1, off, wave, idx - 2 * TX::INSTR);
+    else if (idx < 2 * TX::INSTR + 2 * TW::INSTR) TW::issue_one(w + TW::BYTES, p3, off, wave, idx - 2 * TX::INSTR - TW::INSTR);
+    else TW::issue_one(w + 2 * TW::BYTES, p2, off, wave, idx - 2 * TX::INSTR - 2 * TW::INSTR);
+  };
+  f32x4 accA[4][FN], accB[4][FN], accG[4][FN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) accA[i][j] = accB[i][j] = accG[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, auto&& hook) {
+    const char* st = smem + buf * STAGE;
+    const char* w = st + 2 * TX::BYTES;
+    constexpr int NSLOT = (BKK / 32) * 4;
+#pragma unroll
+    for (int kk = 0; kk < BKK; kk += 32) {
+      bf16x8 fk[4], fv[4], f1[FN], f3[FN], f2[FN];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fk[i] = dfrag_row<TX>(st, wm * 64 + i * 16, kk, lane);
+        fv[i] = dfrag_row<TX>(st + TX::BYTES, wm * 64 + i * 16, kk, lane);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        f1[j] = dfrag_row<TW>(w, wn * (BJ / 2) + j * 16, kk, lane);
+        f3[j] = dfrag_row<TW>(w + TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+        f2[j] = dfrag_row<TW>(w + 2 * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          accA[i][j] = mfma(fk[i], f1[j], accA[i][j]);
+          accB[i][j] = mfma(fk[i], f3[j], accB[i][j]);
+          accG[i][j] = mfma(fv[i], f2[j], accG[i][j]);
+        }
+        hook((kk / 32) * 4 + i, NSLOT);
+      }
+    }
+  };
+  dpipeline_il<NST, LPS>(D / BKK, issue_one, compute);
+
+  bf16_t* E = reinterpret_cast<bf16_t*>(a.E) + inst * 3 * (int64_t)D * a.ldE;
+  const float* lr = a.lr + inst * a.lr_bs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t tq = t0 + wm * 64 + i * 16 + 4 * (lane >> 4);
+    const int64_t trel = tq - a.upd_t0;
+    if (trel >= a.ldE) continue;
+    float e1[4], e2[4], e3[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = tq + r < tend;
+      e1[r] = ok ? lr[(tq + r) * 3 + 0] : 0.f;
+      e2[r] = ok ? lr[(tq + r) * 3 + 1] : 0.f;
+      e3[r] = ok ? lr[(tq + r) * 3 + 2] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = j0 + wn * (BJ / 2) + j * 16 + (lane & 15);
+      float u1[4], u3[4], u2[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = accA[i][j][r], bb = accB[i][j][r], gg = accG[i][j][r];
+        const float sg = fast_sigmoid(x);
+        const float s = x * sg;
+        const float sp = sg * (1.0f + x * (1.0f - sg));
+        u1[r] = e1[r] * gg * bb * sp;
+        u3[r] = e3[r] * gg * s;
+        u2[r] = e2[r] * s * bb;
+      }
+      store4(E + (int64_t)col * a.ldE + trel, u1);
+      store4(E + (int64_t)(D + col) * a.ldE + trel, u3);
+      store4(E + (int64_t)(2 * D + col) * a.ldE + trel, u2);
+    }
+  }
+}
+
+// =========================================================================
+// bf16 apply forward tile (same contract as app_fwd_kernel)
+template <int BJ, int BKK, int NST>
+__global__ __launch_bounds__(NT) void dapp_fwd_kernel(AppFwdArgs a) {
+  using TX = DTile<FBT, BKK>;
+  using TW = DTile<BJ, BKK>;
+  constexpr int STAGE = TX::BYTES + 2 * TW::BYTES;
+  constexpr int LPS = TX::INSTR + 2 * TW::INSTR;
+  constexpr int FN = BJ / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int D = a.D;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int gi = 0;
+  while (gi + 1 < a.ngroups && bid >= a.g[gi].tiles) bid -= a.g[gi++].tiles;
+  const AppGroup& G = a.g[gi];
+  const int njb = D / BJ;
+  const int tiles_t = (int)((G.len + FBT - 1) / FBT);
+  const int per_inst = tiles_t * njb;
+  const int inst = bid / per_inst;
+  const int tile = bid % per_inst;
+  const int tb = tile / njb, jb = tile % njb;
+  const int64_t t0 = G.t0 + (int64_t)tb * FBT;
+  const int64_t tend = G.t0 + G.len;
+  const int j0 = jb * BJ;
+  const int64_t DD = (int64_t)D * D;
+  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + inst * a.x_bs;
+  const bf16_t* W1 = reinterpret_cast<const bf16_t*>(G.W1) + inst * DD;
+  const bf16_t* W3 = reinterpret_cast<const bf16_t*>(G.W3) + inst * DD;
+
+  const typename TX::Plan pq = TX::plan(Q, D, t0, tend - 1, 0, wave, lane);
+  const typename TW::Plan p1 = TW::plan(W1, D, j0, D - 1, 0, wave, lane);
+  const typename TW::Plan p3 = TW::plan(W3, D, j0, D - 1, 0, wave, lane);
+  auto issue_one = [&](int s, int buf, int idx) {
+    char* st = smem + buf * STAGE;
+    const int64_t off = (int64_t)s * BKK * 2;
+    if (idx < TX::INSTR) TX::issue_one(st, pq, off, wave, idx);
+    else if (idx < TX::INSTR + TW::INSTR) TW::issue_one(st + TX::BYTES, p1, off, wave, idx - TX::INSTR);
+    else TW::issue_one(st + TX::BYTES + TW::BYTES, p3, off, wave, idx - TX::INSTR - TW::INSTR);
+  };
+  f32x4 accA[4][FN], accB[4][FN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) accA[i][j] = accB[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, auto&& hook) {
+    const char* st = smem + buf * STAGE;
+    constexpr int NSLOT = (BKK / 32) * 4;
+#pragma unroll
+    for (int kk = 0; kk < BKK; kk += 32) {
+      bf16x8 fq[4], f1[FN], f3[FN];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fq[i] = dfrag_row<TX>(st, wm * 64 + i * 16, kk, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        f1[j] = dfrag_row<TW>(st + TX::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+        f3[j] = dfrag_row<TW>(st + TX::BYTES + TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          accA[i][j] = mfma(f1[j], fq[i], accA[i][j]);   // swapped: lane owns 4 columns of one token
+          accB[i][j] = mfma(f3[j], fq[i], accB[i][j]);
+        }
+        hook((kk / 32) * 4 + i, NSLOT);
+      }
+    }
+  };
+  dpipeline_il<NST, LPS>(D / BKK, issue_one, compute);
+
+  bf16_t* H = reinterpret_cast<bf16_t*>(a.H) + inst * a.h_bs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + wm * 64 + i * 16 + (lane & 15);
+    if (t >= tend) continue;
+    bf16_t* Hr = H + (G.h0 + (t - G.t0)) * (int64_t)D;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = j0 + wn * (BJ / 2) + j * 16 + 4 * (lane >> 4);
+      float h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = accA[i][j][r];
+        h[r] = x * fast_sigmoid(x) * accB[i][j][r];
+      }
+      store4(Hr + col, h);
+    }
+  }
+}
+
+}  // namespace lact

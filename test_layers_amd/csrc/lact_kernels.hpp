@@ -1,213 +1,315 @@
 // gfx950 kernels of the LaCT fast-weight layer forward.
 //
-//   fwd_kernel   -- per (instance, 128-token block, 64-column block) tile:
-//                   apply tiles compute Aq = Q W1^T, Bq = Q W3^T and store
-//                   Hq = silu(Aq) * Bq; update tiles compute A = K W1^T,
-//                   B = K W3^T, G = V W2 and store the SwiGLU backward terms
-//                   lr1*G*B*silu'(A), lr3*G*silu(A), lr2*silu(A)*B
-//                   ("大块测试时训练（LaCT）技术解析" §2.1, eqs. 2 and 4-5).
-//   gemm_kernel  -- batched C = alpha*A B^T + beta*Cin with fp32 output and
-//                   optional split over K (the weight-gradient contraction
-//                   over the chunk's tokens, the apply output product and the
-//                   Newton-Schulz products).
-//   reduce_rows_kernel -- sums split-K partials, emits per-row sums of squares.
-//   opt_kernel   -- GD / momentum / Muon step and row L2 renormalisation
-//                   ("大块测试时训练（LaCT）技术解析" §2.2.1 eq. 8;
-//                   "LaCT架构核心思想解析" §1.2).
+// Update path (once per update chunk, on the current fast weights):
+//   upd_fwd_kernel -- per (instance, 128-token block, BJ hidden columns):
+//                     A = K W1^T, B = K W3^T, G = V W2 on MFMA, then the SwiGLU
+//                     backward terms lr1*G*B*silu'(A), lr3*G*silu(A),
+//                     lr2*silu(A)*B in registers, stored token-fastest
+//                     ("大块测试时训练（LaCT）技术解析" §2.1, eqs. 4-5).
+//   gemm_kernel    -- weight-gradient contraction over the chunk's tokens
+//                     (split over tokens, fp32 partials), Newton-Schulz
+//                     products, apply output product.
+//   opt_kernel     -- sums the partials, GD / momentum step, row L2
+//                     renormalisation ("大块测试时训练（LaCT）技术解析" §2.2.1
+//                     eq. 8; "LaCT架构核心思想解析" §1.2), and writes the bf16
+//                     snapshot of the new weights.
+//   reduce_rows_kernel -- Muon: sums partials, per-row sums of squares.
+// Apply path (after the recurrence, all chunks at once, each chunk on the
+// snapshot of the weights it reads):
+//   app_fwd_kernel -- Hq = silu(Q W1^T) * (Q W3^T);  gemm_kernel: o = Hq W2^T.
 #pragma once
 #include "lact_device.hpp"
 
 namespace lact {
 
-constexpr int NT = 256;   // threads per workgroup (4 waves)
-constexpr int BK = 32;    // k per LDS stage (one MFMA k-slice)
+constexpr int NT = 256;   // threads per workgroup (4 waves, 2 x 2)
+
+template <typename T, int P, int ROWS, int BK, bool COLK>
+__device__ __forceinline__ void load_tile(typename LoaderSel<T, P, ROWS, BK, NT, COLK>::type& L, const T* base,
+                                          int64_t ld, int64_t r0, int64_t rvalid, int64_t k0, int64_t kvalid,
+                                          int tid) {
+  if constexpr (COLK) L.load(base, ld, r0, rvalid, k0, kvalid, tid);
+  else L.load(base, ld, r0, rvalid, k0, tid);
+}
 
 // =========================================================================
-// fused forward tiles
-struct FwdArgs {
-  const void* q;
+// update forward tiles
+struct UpdFwdArgs {
   const void* k;
   const void* v;
-  int64_t x_bs;          // elements between instances in q/k/v (seq_stride * D)
+  int64_t x_bs;          // elements between instances in k/v (seq_stride * D)
   const float* lr;
-  int64_t lr_bs;         // seq_stride * 3
-  const float* W1;
-  const float* W2;
-  const float* W3;
-  void* E;               // [n, upd_len, 3D] update terms (token rows relative to upd_t0)
-  int64_t e_bs;
-  void* H;               // [n, app_len, D] gated hidden of the queries
-  int64_t h_bs;
+  int64_t lr_bs;
+  const float* beta;     // momentum: per-token beta (partial sums per token block), else null
+  int64_t beta_bs;
+  float* bpart;          // [n, tiles_t] beta partial sums
+  const void* W1;        // [n, D, D] (bf16 snapshot or fp32 master)
+  const void* W3;
+  const void* W2x;       // bf16: W2^T snapshot [n, dh, d]; fp32: W2 master [n, d, dh]
+  void* E;               // [n, 3D, ldE] update terms, token-fastest: rows U1 | U3 | U2^T terms
+  int64_t ldE;
   int D;
   int64_t upd_t0;
   int64_t upd_len;
-  int64_t app_t0;
-  int64_t app_len;
-  int upd_tiles;         // per instance
-  int app_tiles;
+  int tiles_t;           // token blocks per instance
 };
 
 constexpr int FBT = 128;  // tokens per forward tile
-constexpr int FBJ = 64;   // hidden columns per forward tile
 
-template <typename TIO, int PIO, int PWU, int PWA, typename TREC, typename TAPP>
-__global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
-  using G_T = TileGeom<FBT, BK>;
-  using G_J = TileGeom<FBJ, BK>;
-  constexpr int UPD_LDS = 2 * PIO * G_T::PLANE + 3 * PWU * G_J::PLANE;
-  constexpr int APP_LDS = PIO * G_T::PLANE + 2 * PWA * G_J::PLANE;
-  constexpr int LDS = UPD_LDS > APP_LDS ? UPD_LDS : APP_LDS;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[LDS];
+template <typename TIO, int PIO, typename TW, int PW, typename TREC, int BJ, int BK, int STAGES>
+__global__ __launch_bounds__(NT) void upd_fwd_kernel(UpdFwdArgs a) {
+  // W2 operand (element (j, r) = W2[r, j]): from the transposed bf16 snapshot
+  // as a row-k source, or from the fp32 master as a column-k source.
+  constexpr bool W2COL = sizeof(TW) == 4;
+  using GT = TileGeom<FBT, BK>;
+  using GJ = TileGeom<BJ, BK>;
+  constexpr int STAGE = 2 * PIO * GT::PLANE + 3 * PW * GJ::PLANE;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * STAGE];
+  __shared__ float s_red[2];
+  constexpr int FN = BJ / 32;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;        // 2x2 waves: 64 tokens x 32 columns each
+  const int wm = wave >> 1, wn = wave & 1;
   const int D = a.D;
-  const int njb = D / FBJ;
-  const int per_inst = a.upd_tiles + a.app_tiles;
-  const int inst = blockIdx.x / per_inst;
-  const int tile = blockIdx.x % per_inst;
-  const float* W1 = a.W1 + (int64_t)inst * D * D;
-  const float* W2 = a.W2 + (int64_t)inst * D * D;
-  const float* W3 = a.W3 + (int64_t)inst * D * D;
+  const int njb = D / BJ;
+  const int per_inst = a.tiles_t * njb;
+  const int lbid = xcd_remap(blockIdx.x, gridDim.x);
+  const int inst = lbid / per_inst;
+  const int tile = lbid % per_inst;
+  const int tb = tile / njb, jb = tile % njb;
+  const int64_t t0 = a.upd_t0 + (int64_t)tb * FBT;
+  const int64_t tend = a.upd_t0 + a.upd_len;
+  const int j0 = jb * BJ;
+  const int64_t DD = (int64_t)D * D;
+  const TIO* K = reinterpret_cast<const TIO*>(a.k) + inst * a.x_bs;
+  const TIO* V = reinterpret_cast<const TIO*>(a.v) + inst * a.x_bs;
+  const TW* W1 = reinterpret_cast<const TW*>(a.W1) + inst * DD;
+  const TW* W3 = reinterpret_cast<const TW*>(a.W3) + inst * DD;
+  const TW* W2 = reinterpret_cast<const TW*>(a.W2x) + inst * DD;
 
-  if (tile < a.upd_tiles) {
-    // ------------------------------------------------------------ update tile
-    const int tb = tile / njb, jb = tile % njb;
-    const int64_t t0 = a.upd_t0 + (int64_t)tb * FBT;
-    const int64_t tend = a.upd_t0 + a.upd_len;
-    const int j0 = jb * FBJ;
-    const TIO* K = reinterpret_cast<const TIO*>(a.k) + inst * a.x_bs;
-    const TIO* V = reinterpret_cast<const TIO*>(a.v) + inst * a.x_bs;
-    uint16_t* lK = smem;
-    uint16_t* lV = lK + PIO * G_T::PLANE;
-    uint16_t* l1 = lV + PIO * G_T::PLANE;
-    uint16_t* l3 = l1 + PWU * G_J::PLANE;
-    uint16_t* l2 = l3 + PWU * G_J::PLANE;
-    RowKLoader<TIO, PIO, FBT, BK, NT> LK, LV;
-    RowKLoader<float, PWU, FBJ, BK, NT> L1, L3;
-    ColKLoader<float, PWU, FBJ, BK, NT> L2;
-    f32x4 accA[4][2], accB[4][2], accG[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) accA[i][j] = accB[i][j] = accG[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.beta != nullptr && jb == 0) {
+    // partial sum of beta over this token block (for the chunk mean)
+    float bsum = 0.f;
+    if (tid < FBT && t0 + tid < tend) bsum = a.beta[inst * a.beta_bs + t0 + tid];
+    bsum = wave_sum(bsum);
+    if (lane == 0 && wave < 2) s_red[wave] = bsum;
+    __syncthreads();
+    if (tid == 0) a.bpart[(int64_t)inst * a.tiles_t + tb] = s_red[0] + s_red[1];
+  }
 
-    auto fetch = [&](int k0) {
-      LK.load(K, D, t0, tend, k0, tid);
-      LV.load(V, D, t0, tend, k0, tid);
-      L1.load(W1, D, j0, D, k0, tid);
-      L3.load(W3, D, j0, D, k0, tid);
-      L2.load(W2, D, j0, D, k0, D, tid);   // element (j, r) = W2[r, j]
-    };
-    fetch(0);
-    for (int k0 = 0; k0 < D; k0 += BK) {
-      __syncthreads();
-      LK.store(lK, tid);
-      LV.store(lV, tid);
-      L1.store(l1, tid);
-      L3.store(l3, tid);
-      L2.store(l2, tid);
-      __syncthreads();
-      if (k0 + BK < D) fetch(k0 + BK);
-      mma_tile<PIO, PWU, 4, 2, G_T::STRIDE, G_J::STRIDE>(accA, lK, G_T::PLANE, wm * 64, l1, G_J::PLANE, wn * 32, 0, lane);
-      mma_tile<PIO, PWU, 4, 2, G_T::STRIDE, G_J::STRIDE>(accB, lK, G_T::PLANE, wm * 64, l3, G_J::PLANE, wn * 32, 0, lane);
-      mma_tile<PIO, PWU, 4, 2, G_T::STRIDE, G_J::STRIDE>(accG, lV, G_T::PLANE, wm * 64, l2, G_J::PLANE, wn * 32, 0, lane);
+  RowKLoader<TIO, PIO, FBT, BK, NT> LK[2], LV[2];
+  RowKLoader<TW, PW, BJ, BK, NT> L1[2], L3[2];
+  typename LoaderSel<TW, PW, BJ, BK, NT, W2COL>::type L2[2];
+  f32x4 accA[4][FN], accB[4][FN], accG[4][FN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) accA[i][j] = accB[i][j] = accG[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto fetch = [&](auto set, int kt) {
+    constexpr int r = decltype(set)::value;
+    const int k0 = kt * BK;
+    LK[r].load(K, D, t0, tend, k0, tid);
+    LV[r].load(V, D, t0, tend, k0, tid);
+    L1[r].load(W1, D, j0, D, k0, tid);
+    L3[r].load(W3, D, j0, D, k0, tid);
+    load_tile<TW, PW, BJ, BK, W2COL>(L2[r], W2, D, j0, D, k0, D, tid);
+  };
+  auto put = [&](auto set, auto buf) {
+    constexpr int r = decltype(set)::value;
+    uint16_t* b = smem + decltype(buf)::value * STAGE;
+    LK[r].store(b, tid);
+    LV[r].store(b + PIO * GT::PLANE, tid);
+    uint16_t* w = b + 2 * PIO * GT::PLANE;
+    L1[r].store(w, tid);
+    L3[r].store(w + PW * GJ::PLANE, tid);
+    L2[r].store(w + 2 * PW * GJ::PLANE, tid);
+  };
+  auto compute = [&](auto buf) {
+    const uint16_t* b = smem + decltype(buf)::value * STAGE;
+    const uint16_t* lK = b;
+    const uint16_t* lV = b + PIO * GT::PLANE;
+    const uint16_t* w = b + 2 * PIO * GT::PLANE;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      mma_tile<PIO, PW, 4, FN, GT::STRIDE, GJ::STRIDE>(accA, lK, GT::PLANE, wm * 64, w, GJ::PLANE, wn * (BJ / 2), kk, lane);
+      mma_tile<PIO, PW, 4, FN, GT::STRIDE, GJ::STRIDE>(accB, lK, GT::PLANE, wm * 64, w + PW * GJ::PLANE, GJ::PLANE,
+                                                       wn * (BJ / 2), kk, lane);
+      mma_tile<PIO, PW, 4, FN, GT::STRIDE, GJ::STRIDE>(accG, lV, GT::PLANE, wm * 64, w + 2 * PW * GJ::PLANE,
+                                                       GJ::PLANE, wn * (BJ / 2), kk, lane);
     }
-    // SwiGLU backward epilogue in registers
-    TREC* E = reinterpret_cast<TREC*>(a.E) + inst * a.e_bs;
-    const float* lr = a.lr + inst * a.lr_bs;
+  };
+  pipeline<STAGES>(D / BK, fetch, put, compute);
+
+  // SwiGLU backward epilogue; every token of the padded row is written (zeros
+  // past the chunk end) so the contraction can read whole 16-byte vectors.
+  TREC* E = reinterpret_cast<TREC*>(a.E) + inst * 3 * (int64_t)D * a.ldE;
+  const float* lr = a.lr + inst * a.lr_bs;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4; ++i) {
+    const int64_t tq = t0 + wm * 64 + i * 16 + 4 * (lane >> 4);   // first of 4 tokens
+    const int64_t trel = tq - a.upd_t0;
+    if (trel >= a.ldE) continue;
+    float e1[4], e2[4], e3[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = tq + r < tend;
+      e1[r] = ok ? lr[(tq + r) * 3 + 0] : 0.f;
+      e2[r] = ok ? lr[(tq + r) * 3 + 1] : 0.f;
+      e3[r] = ok ? lr[(tq + r) * 3 + 2] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = j0 + wn * (BJ / 2) + j * 16 + (lane & 15);
+      float u1[4], u3[4], u2[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-        if (t >= tend) continue;
-        const float e1 = lr[t * 3 + 0], e2 = lr[t * 3 + 1], e3 = lr[t * 3 + 2];
-        TREC* Er = E + (t - a.upd_t0) * (3 * (int64_t)D);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = j0 + wn * 32 + j * 16 + (lane & 15);
-          const float x = accA[i][j][r], b = accB[i][j][r], g = accG[i][j][r];
-          const float sg = fast_sigmoid(x);
-          const float s = x * sg;
-          const float sp = sg * (1.0f + x * (1.0f - sg));
-          io_traits<TREC>::store(Er + col, e1 * g * b * sp);
-          io_traits<TREC>::store(Er + D + col, e3 * g * s);
-          io_traits<TREC>::store(Er + 2 * D + col, e2 * s * b);
-        }
+        const float x = accA[i][j][r], b = accB[i][j][r], g = accG[i][j][r];
+        const float sg = fast_sigmoid(x);
+        const float s = x * sg;
+        const float sp = sg * (1.0f + x * (1.0f - sg));
+        u1[r] = e1[r] * g * b * sp;
+        u3[r] = e3[r] * g * s;
+        u2[r] = e2[r] * s * b;
       }
-    }
-  } else {
-    // ------------------------------------------------------------ apply tile
-    const int at = tile - a.upd_tiles;
-    const int tb = at / njb, jb = at % njb;
-    const int64_t t0 = a.app_t0 + (int64_t)tb * FBT;
-    const int64_t tend = a.app_t0 + a.app_len;
-    const int j0 = jb * FBJ;
-    const TIO* Q = reinterpret_cast<const TIO*>(a.q) + inst * a.x_bs;
-    uint16_t* lQ = smem;
-    uint16_t* l1 = lQ + PIO * G_T::PLANE;
-    uint16_t* l3 = l1 + PWA * G_J::PLANE;
-    RowKLoader<TIO, PIO, FBT, BK, NT> LQ;
-    RowKLoader<float, PWA, FBJ, BK, NT> L1, L3;
-    f32x4 accA[4][2], accB[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) accA[i][j] = accB[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto fetch = [&](int k0) {
-      LQ.load(Q, D, t0, tend, k0, tid);
-      L1.load(W1, D, j0, D, k0, tid);
-      L3.load(W3, D, j0, D, k0, tid);
-    };
-    fetch(0);
-    for (int k0 = 0; k0 < D; k0 += BK) {
-      __syncthreads();
-      LQ.store(lQ, tid);
-      L1.store(l1, tid);
-      L3.store(l3, tid);
-      __syncthreads();
-      if (k0 + BK < D) fetch(k0 + BK);
-      mma_tile<PIO, PWA, 4, 2, G_T::STRIDE, G_J::STRIDE>(accA, lQ, G_T::PLANE, wm * 64, l1, G_J::PLANE, wn * 32, 0, lane);
-      mma_tile<PIO, PWA, 4, 2, G_T::STRIDE, G_J::STRIDE>(accB, lQ, G_T::PLANE, wm * 64, l3, G_J::PLANE, wn * 32, 0, lane);
-    }
-    TAPP* H = reinterpret_cast<TAPP*>(a.H) + inst * a.h_bs;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-        if (t >= tend) continue;
-        TAPP* Hr = H + (t - a.app_t0) * (int64_t)D;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = j0 + wn * 32 + j * 16 + (lane & 15);
-          const float x = accA[i][j][r];
-          io_traits<TAPP>::store(Hr + col, x * fast_sigmoid(x) * accB[i][j][r]);
-        }
-      }
+      store4(E + (int64_t)col * a.ldE + trel, u1);
+      store4(E + (int64_t)(D + col) * a.ldE + trel, u3);
+      store4(E + (int64_t)(2 * D + col) * a.ldE + trel, u2);
     }
   }
 }
 
 // =========================================================================
-// generic batched GEMM:  C[m, n] = alpha * sum_k A(m, k) B(n, k) + beta * Cin[m, n]
+// apply forward tiles, grouped by the weight snapshot they read
+constexpr int MAXG = 24;
+
+struct AppGroup {
+  int64_t t0;            // first token of the group's apply range
+  int64_t len;
+  int64_t h0;            // row offset of the group in the Hq buffer
+  const void* W1;        // snapshot [n, D, D]
+  const void* W3;
+  int tiles;             // workgroups of this group
+};
+
+struct AppFwdArgs {
+  AppGroup g[MAXG];
+  int ngroups;
+  const void* q;
+  int64_t x_bs;
+  void* H;               // [n, h_rows, D]
+  int64_t h_bs;
+  int D;
+};
+
+template <typename TIO, int PIO, typename TW, int PW, typename TAPP, int BJ, int BK, int STAGES>
+__global__ __launch_bounds__(NT) void app_fwd_kernel(AppFwdArgs a) {
+  using GT = TileGeom<FBT, BK>;
+  using GJ = TileGeom<BJ, BK>;
+  constexpr int STAGE = PIO * GT::PLANE + 2 * PW * GJ::PLANE;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * STAGE];
+  constexpr int FN = BJ / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int D = a.D;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int gi = 0;
+  while (gi + 1 < a.ngroups && bid >= a.g[gi].tiles) bid -= a.g[gi++].tiles;
+  const AppGroup& G = a.g[gi];
+  const int njb = D / BJ;
+  const int tiles_t = (int)((G.len + FBT - 1) / FBT);
+  const int per_inst = tiles_t * njb;
+  const int inst = bid / per_inst;
+  const int tile = bid % per_inst;
+  const int tb = tile / njb, jb = tile % njb;
+  const int64_t t0 = G.t0 + (int64_t)tb * FBT;
+  const int64_t tend = G.t0 + G.len;
+  const int j0 = jb * BJ;
+  const int64_t DD = (int64_t)D * D;
+  const TIO* Q = reinterpret_cast<const TIO*>(a.q) + inst * a.x_bs;
+  const TW* W1 = reinterpret_cast<const TW*>(G.W1) + inst * DD;
+  const TW* W3 = reinterpret_cast<const TW*>(G.W3) + inst * DD;
+
+  RowKLoader<TIO, PIO, FBT, BK, NT> LQ[2];
+  RowKLoader<TW, PW, BJ, BK, NT> L1[2], L3[2];
+  f32x4 accA[4][FN], accB[4][FN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) accA[i][j] = accB[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto fetch = [&](auto set, int kt) {
+    constexpr int r = decltype(set)::value;
+    const int k0 = kt * BK;
+    LQ[r].load(Q, D, t0, tend, k0, tid);
+    L1[r].load(W1, D, j0, D, k0, tid);
+    L3[r].load(W3, D, j0, D, k0, tid);
+  };
+  auto put = [&](auto set, auto buf) {
+    constexpr int r = decltype(set)::value;
+    uint16_t* b = smem + decltype(buf)::value * STAGE;
+    LQ[r].store(b, tid);
+    L1[r].store(b + PIO * GT::PLANE, tid);
+    L3[r].store(b + PIO * GT::PLANE + PW * GJ::PLANE, tid);
+  };
+  // swapped MFMA order: each lane ends with 4 consecutive hidden columns of one token
+  auto compute = [&](auto buf) {
+    const uint16_t* b = smem + decltype(buf)::value * STAGE;
+    const uint16_t* w = b + PIO * GT::PLANE;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      mma_tile<PIO, PW, 4, FN, GT::STRIDE, GJ::STRIDE, true>(accA, b, GT::PLANE, wm * 64, w, GJ::PLANE, wn * (BJ / 2),
+                                                             kk, lane);
+      mma_tile<PIO, PW, 4, FN, GT::STRIDE, GJ::STRIDE, true>(accB, b, GT::PLANE, wm * 64, w + PW * GJ::PLANE,
+                                                             GJ::PLANE, wn * (BJ / 2), kk, lane);
+    }
+  };
+  pipeline<STAGES>(D / BK, fetch, put, compute);
+  TAPP* H = reinterpret_cast<TAPP*>(a.H) + inst * a.h_bs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + wm * 64 + i * 16 + (lane & 15);
+    if (t >= tend) continue;
+    TAPP* Hr = H + (G.h0 + (t - G.t0)) * (int64_t)D;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = j0 + wn * (BJ / 2) + j * 16 + 4 * (lane >> 4);
+      float h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = accA[i][j][r];
+        h[r] = x * fast_sigmoid(x) * accB[i][j][r];
+      }
+      store4(Hr + col, h);
+    }
+  }
+}
+
+// =========================================================================
+// grouped batched GEMM:  C[m, n] = alpha * sum_k A(m, k) B(n, k) + beta * Cin[m, n]
 //   A(m, k): row-k source A[m * lda + k]   or column-k source A[k * lda + m]
 //   B(n, k): row-k source B[n * ldb + k]   or column-k source B[k * ldb + n]
-// K may be split over gridDim: split s covers k in [s*kps, min(K, (s+1)*kps))
-// and writes its own partial C + s * c_ss.
-struct GemmArgs {
+// Groups share every stride and N, K; each has its own A, B, C and M.  K may
+// be split: split s covers k in [s*kps, min(K, (s+1)*kps)) and writes its
+// own partial C + s * c_ss.  Rows m >= trans_from are stored transposed into
+// the square block that starts at row trans_from.
+struct GemmGroup {
   const void* A;
-  int64_t lda, a_bs;
   const void* B;
-  int64_t ldb, b_bs;
-  const void* B2;        // B operand for m-tiles at or beyond m_switch (else unused)
-  int m_switch;
   void* C;
-  int64_t ldc, c_bs, c_ss;
+  int M;
+  int tiles;             // workgroups of this group
+};
+
+struct GemmArgs {
+  GemmGroup g[MAXG];
+  int ngroups;
+  int64_t lda, a_bs, ldb, b_bs, ldc, c_bs, c_ss;
+  const void* B2;        // B operand for m-tiles at or beyond m_switch (group 0 only)
+  int m_switch;
+  int trans_from;
   const float* Cin;
   int64_t ldcin, cin_bs;
-  int M, N;
+  int N;
   int64_t K, kps;
   int batch, splits;
   float alpha, beta;
@@ -217,22 +319,25 @@ struct GemmArgs {
   int rowsq_n, alpha_pow, beta_pow;
 };
 
-template <typename TA, int PA, bool CA, typename TB, int PB, bool CB, typename TC, int BM, int BN>
+template <typename TA, int PA, bool CA, typename TB, int PB, bool CB, typename TC, int BM, int BN, int BK, int STAGES>
 __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   using GA = TileGeom<BM, BK>;
   using GB = TileGeom<BN, BK>;
   constexpr int FM = BM / 32, FN = BN / 32;     // 2x2 waves, wave tile (BM/2) x (BN/2)
-  __shared__ __attribute__((aligned(16))) uint16_t smem[PA * GA::PLANE + PB * GB::PLANE];
+  constexpr int STAGE = PA * GA::PLANE + PB * GB::PLANE;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES * STAGE];
   __shared__ float s_scale;
-  uint16_t* lA = smem;
-  uint16_t* lB = smem + PA * GA::PLANE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int gi = 0;
+  while (gi + 1 < g.ngroups && bid >= g.g[gi].tiles) bid -= g.g[gi++].tiles;
+  const GemmGroup& G = g.g[gi];
+  const int M = G.M;
   const int tn_count = (g.N + BN - 1) / BN;
-  const int tm_count = (g.M + BM - 1) / BM;
+  const int tm_count = (M + BM - 1) / BM;
   const int tiles = tm_count * tn_count;
-  int bid = blockIdx.x;
   const int tile = bid % tiles;
   bid /= tiles;
   const int split = bid % g.splits;
@@ -240,19 +345,25 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   const int tm = tile / tn_count, tn = tile % tn_count;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const TA* A = reinterpret_cast<const TA*>(g.A) + b * g.a_bs;
-  const void* Bsrc = (g.B2 != nullptr && m0 >= g.m_switch) ? g.B2 : g.B;
+  const TA* A = reinterpret_cast<const TA*>(G.A) + b * g.a_bs;
+  const void* Bsrc = (g.B2 != nullptr && m0 >= g.m_switch) ? g.B2 : G.B;
   const TB* B = reinterpret_cast<const TB*>(Bsrc) + b * g.b_bs;
   const int64_t kbeg = (int64_t)split * g.kps;
   const int64_t kend = min(g.K, kbeg + g.kps);
 
-  typename LoaderSel<TA, PA, BM, BK, NT, CA>::type LA;
-  typename LoaderSel<TB, PB, BN, BK, NT, CB>::type LB;
-  auto fetch = [&](int64_t k0) {
-    if constexpr (CA) LA.load(A, g.lda, m0, g.M, k0, kend, tid);
-    else LA.load(A, g.lda, m0, g.M, k0, tid);
-    if constexpr (CB) LB.load(B, g.ldb, n0, g.N, k0, kend, tid);
-    else LB.load(B, g.ldb, n0, g.N, k0, tid);
+  typename LoaderSel<TA, PA, BM, BK, NT, CA>::type LA[2];
+  typename LoaderSel<TB, PB, BN, BK, NT, CB>::type LB[2];
+  auto fetch = [&](auto set, int64_t kt) {
+    constexpr int r = decltype(set)::value;
+    const int64_t k0 = kbeg + kt * BK;
+    load_tile<TA, PA, BM, BK, CA>(LA[r], A, g.lda, m0, M, k0, kend, tid);
+    load_tile<TB, PB, BN, BK, CB>(LB[r], B, g.ldb, n0, g.N, k0, kend, tid);
+  };
+  auto put = [&](auto set, auto buf) {
+    constexpr int r = decltype(set)::value;
+    uint16_t* b = smem + decltype(buf)::value * STAGE;
+    LA[r].store(b, tid);
+    LB[r].store(b + PA * GA::PLANE, tid);
   };
 
   f32x4 acc[FM][FN];
@@ -260,17 +371,17 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (kbeg < kend) fetch(kbeg);
-  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
-    __syncthreads();
-    LA.store(lA, tid);
-    LB.store(lB, tid);
-    __syncthreads();
-    if (k0 + BK < kend) fetch(k0 + BK);
-    mma_tile<PA, PB, FM, FN, GA::STRIDE, GB::STRIDE>(acc, lA, GA::PLANE, wm * (BM / 2), lB, GB::PLANE,
-                                                     wn * (BN / 2), 0, lane);
-  }
+  // swapped MFMA order: each lane ends with 4 consecutive columns of one row
+  auto compute = [&](auto buf) {
+    const uint16_t* la = smem + decltype(buf)::value * STAGE;
+    const uint16_t* lb = la + PA * GA::PLANE;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32)
+      mma_tile<PA, PB, FM, FN, GA::STRIDE, GB::STRIDE, true>(acc, la, GA::PLANE, wm * (BM / 2), lb, GB::PLANE,
+                                                             wn * (BN / 2), kk, lane);
+  };
+  const int64_t nk = kbeg < kend ? (kend - kbeg + BK - 1) / BK : 0;
+  pipeline<STAGES>((int)nk, fetch, put, compute);
 
   float alpha = g.alpha, beta = g.beta;
   if (g.rowsq != nullptr) {
@@ -286,23 +397,37 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < g.alpha_pow; ++i) alpha *= sc;
     for (int i = 0; i < g.beta_pow; ++i) beta *= sc;
   }
-  TC* C = reinterpret_cast<TC*>(g.C) + b * g.c_bs + split * g.c_ss;
+  TC* C = reinterpret_cast<TC*>(G.C) + b * g.c_bs + split * g.c_ss;
   const float* Cin = g.Cin ? g.Cin + b * g.cin_bs : nullptr;
+  const bool trans = m0 >= g.trans_from;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
+    if (m >= M) continue;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4) + r;
-      if (m >= g.M) continue;
+    for (int j = 0; j < FN; ++j) {
+      const int nq = n0 + wn * (BN / 2) + j * 16 + 4 * (lane >> 4);   // 4 columns nq .. nq+3
+      if (nq >= g.N) continue;
+      float val[4];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
-        if (n >= g.N) continue;
-        float val = alpha * acc[i][j][r];
-        if (Cin) val += beta * Cin[(int64_t)m * g.ldcin + n];
-        io_traits<TC>::store(C + (int64_t)m * g.ldc + n, val);
+      for (int r = 0; r < 4; ++r) val[r] = alpha * acc[i][j][r];
+      if (Cin) {
+        const float4 c = *reinterpret_cast<const float4*>(Cin + (int64_t)m * g.ldcin + nq);
+        val[0] += beta * c.x;
+        val[1] += beta * c.y;
+        val[2] += beta * c.z;
+        val[3] += beta * c.w;
+      }
+      if (trans) {
+        // row m of the block is stored as column m - trans_from
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          io_traits<TC>::store(C + (int64_t)(g.trans_from + nq + r) * g.ldc + (m - g.trans_from), val[r]);
+      } else {
+        store4(C + (int64_t)m * g.ldc + nq, val);
       }
     }
+  }
 }
 
 // =========================================================================
@@ -314,102 +439,120 @@ __global__ __launch_bounds__(NT) void reduce_rows_kernel(const float* P, int64_t
   const int64_t row = (int64_t)blockIdx.x * (NT / WAVE) + (threadIdx.x >> 6);
   if (row >= rows) return;
   float ss = 0.f;
-  for (int e = lane; e < D; e += WAVE) {
-    float u = 0.f;
-    for (int s = 0; s < splits; ++s) u += P[s * p_ss + row * D + e];
-    U[row * D + e] = u;
-    ss += u * u;
+  for (int e4 = lane; e4 < D / 4; e4 += WAVE) {
+    const float4* src = reinterpret_cast<const float4*>(P + row * D) + e4;
+    float4 u = src[0];
+    for (int s = 1; s < splits; ++s) {
+      const float4 x = src[s * p_ss / 4];
+      u.x += x.x;
+      u.y += x.y;
+      u.z += x.z;
+      u.w += x.w;
+    }
+    reinterpret_cast<float4*>(U + row * D)[e4] = u;
+    ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
   }
   ss = wave_sum(ss);
   if (lane == 0) rowsq[row] = ss;
 }
 
 // =========================================================================
-// optimiser step + row renormalisation.
-// src holds, per instance, the stacked direction [U1; U3; U2^T] ([3D, D]) as
-// `splits` partials to be summed in order.  Workgroup = 16 rows of one matrix.
+// optimiser step + row renormalisation + snapshot of the new weights.
+// src: per instance the stacked direction [U1; U3; U2] ([3D, D], natural
+// layouts) as `splits` partials summed in order.  One wave per row.
 struct OptArgs {
   const float* src;
   int64_t src_ss;        // elements between partials
   int splits;
   float* W[3];           // W1, W3, W2 (matching the stacked source blocks)
   float* M[3];
-  const float* beta;     // momentum only
-  int64_t beta_bs;
-  int64_t beta_t0;
-  int64_t beta_len;
+  const float* bpart;    // momentum: beta partial sums [n, nbp]
+  int nbp;
+  float inv_len;         // 1 / chunk length
   int D;
   int opt;               // 0 GD, 1 momentum, 2 Muon
   int renorm;
+  // snapshot of the new weights (bf16 or fp32, natural layout) and, for
+  // bf16, the transposed W2 snapshot used by the next update's forward
+  void* snap[3];
+  void* snapT2;
 };
 
-constexpr int OPT_ROWS = 16;
-constexpr int OPT_MAXPL = 16;   // D / 64 elements per lane, D <= 1024
+constexpr int OPT_RPW = 2;                // rows per wave
+constexpr int OPT_ROWS = OPT_RPW * 4;     // rows per workgroup
+constexpr int OPT_VPL = 4;                // float4 per lane per row (D <= 1024)
 
+template <typename TS>
 __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
-  __shared__ float s_src[1024 * (OPT_ROWS + 1)];
-  __shared__ float s_red[NT / WAVE];
+  __shared__ uint16_t s_t[OPT_ROWS * 1024];   // transposed-snapshot staging (bf16 W2 rows)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int D = a.D;
   const int rblocks = D / OPT_ROWS;
-  int bid = blockIdx.x;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int rb = bid % rblocks;
   bid /= rblocks;
   const int mat = bid % 3;
   const int inst = bid / 3;
-  const int r0 = rb * OPT_ROWS;
   const int64_t DD = (int64_t)D * D;
   const float* src = a.src + inst * 3 * DD + mat * DD;
 
   float bm = 0.f;
   if (a.opt == 1) {
-    const float* bt = a.beta + inst * a.beta_bs + a.beta_t0;
     float s = 0.f;
-    for (int64_t i = tid; i < a.beta_len; i += NT) s += bt[i];
-    s = wave_sum(s);
-    if (lane == 0) s_red[wave] = s;
-    __syncthreads();
-    bm = (s_red[0] + s_red[1] + s_red[2] + s_red[3]) / (float)a.beta_len;
-  }
-  if (mat == 2) {
-    // W2 row r is column r of the transposed block: stage 16 columns in LDS
-    for (int idx = tid; idx < D * OPT_ROWS; idx += NT) {
-      const int j = idx / OPT_ROWS, rr = idx % OPT_ROWS;
-      float u = 0.f;
-      for (int s = 0; s < a.splits; ++s) u += src[s * a.src_ss + (int64_t)j * D + r0 + rr];
-      s_src[j * (OPT_ROWS + 1) + rr] = u;
-    }
-    __syncthreads();
+    for (int i = lane; i < a.nbp; i += WAVE) s += a.bpart[(int64_t)inst * a.nbp + i];
+    bm = wave_sum(s) * a.inv_len;
   }
   float* W = a.W[mat] + inst * DD;
   float* M = a.M[mat] ? a.M[mat] + inst * DD : nullptr;
-  for (int rr = wave; rr < OPT_ROWS; rr += NT / WAVE) {
-    const int row = r0 + rr;
-    float wn[OPT_MAXPL];
-    float so = 0.f, sn = 0.f;
+  TS* snap = a.snap[mat] ? reinterpret_cast<TS*>(a.snap[mat]) + inst * DD : nullptr;
+  const int nv = D / 4;
 #pragma unroll
-    for (int i = 0; i < OPT_MAXPL; ++i) {
-      const int e = lane + i * WAVE;
-      if (e >= D) continue;
-      float u;
-      if (mat == 2) {
-        u = s_src[e * (OPT_ROWS + 1) + rr];
-      } else {
-        u = 0.f;
-        for (int s = 0; s < a.splits; ++s) u += src[s * a.src_ss + (int64_t)row * D + e];
+  for (int rr = 0; rr < OPT_RPW; ++rr) {
+    const int lrow = wave * OPT_RPW + rr;
+    const int row = rb * OPT_ROWS + lrow;
+    float4 u[OPT_VPL], w[OPT_VPL];
+#pragma unroll
+    for (int i = 0; i < OPT_VPL; ++i) {
+      const int e4 = lane + i * WAVE;
+      if (e4 < nv) {
+        const float4* s0 = reinterpret_cast<const float4*>(src + (int64_t)row * D) + e4;
+        u[i] = s0[0];
+        w[i] = reinterpret_cast<const float4*>(W + (int64_t)row * D)[e4];
       }
-      const float w = W[(int64_t)row * D + e];
-      float x;
-      if (a.opt == 1) {
-        const float m = bm * M[(int64_t)row * D + e] - u;
-        M[(int64_t)row * D + e] = m;
-        x = w - m;
-      } else {
-        x = w + u;
+    }
+    for (int s = 1; s < a.splits; ++s) {
+#pragma unroll
+      for (int i = 0; i < OPT_VPL; ++i) {
+        const int e4 = lane + i * WAVE;
+        if (e4 < nv) {
+          const float4 x = reinterpret_cast<const float4*>(src + s * a.src_ss + (int64_t)row * D)[e4];
+          u[i].x += x.x;
+          u[i].y += x.y;
+          u[i].z += x.z;
+          u[i].w += x.w;
+        }
       }
-      wn[i] = x;
-      so += w * w;
-      sn += x * x;
+    }
+    float so = 0.f, sn = 0.f;
+    float4 x[OPT_VPL];
+#pragma unroll
+    for (int i = 0; i < OPT_VPL; ++i) {
+      const int e4 = lane + i * WAVE;
+      if (e4 < nv) {
+        if (a.opt == 1) {
+          float4 m = reinterpret_cast<const float4*>(M + (int64_t)row * D)[e4];
+          m.x = bm * m.x - u[i].x;
+          m.y = bm * m.y - u[i].y;
+          m.z = bm * m.z - u[i].z;
+          m.w = bm * m.w - u[i].w;
+          reinterpret_cast<float4*>(M + (int64_t)row * D)[e4] = m;
+          x[i] = make_float4(w[i].x - m.x, w[i].y - m.y, w[i].z - m.z, w[i].w - m.w);
+        } else {
+          x[i] = make_float4(w[i].x + u[i].x, w[i].y + u[i].y, w[i].z + u[i].z, w[i].w + u[i].w);
+        }
+        so += w[i].x * w[i].x + w[i].y * w[i].y + w[i].z * w[i].z + w[i].w * w[i].w;
+        sn += x[i].x * x[i].x + x[i].y * x[i].y + x[i].z * x[i].z + x[i].w * x[i].w;
+      }
     }
     float scale = 1.f;
     if (a.renorm) {
@@ -418,9 +561,64 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
       scale = sqrtf(so) / sqrtf(sn);
     }
 #pragma unroll
-    for (int i = 0; i < OPT_MAXPL; ++i) {
-      const int e = lane + i * WAVE;
-      if (e < D) W[(int64_t)row * D + e] = wn[i] * scale;
+    for (int i = 0; i < OPT_VPL; ++i) {
+      const int e4 = lane + i * WAVE;
+      if (e4 < nv) {
+        const float4 y = make_float4(x[i].x * scale, x[i].y * scale, x[i].z * scale, x[i].w * scale);
+        reinterpret_cast<float4*>(W + (int64_t)row * D)[e4] = y;
+        if (snap) {
+          const float yy[4] = {y.x, y.y, y.z, y.w};
+          store4(snap + (int64_t)row * D + 4 * e4, yy);
+        }
+        if constexpr (sizeof(TS) == 2) {
+          if (mat == 2 && a.snapT2) {
+            s_t[(4 * e4 + 0) * OPT_ROWS + lrow] = (uint16_t)f2bf(y.x);
+            s_t[(4 * e4 + 1) * OPT_ROWS + lrow] = (uint16_t)f2bf(y.y);
+            s_t[(4 * e4 + 2) * OPT_ROWS + lrow] = (uint16_t)f2bf(y.z);
+            s_t[(4 * e4 + 3) * OPT_ROWS + lrow] = (uint16_t)f2bf(y.w);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (sizeof(TS) == 2) {
+    if (mat == 2 && a.snapT2) {
+      // W2^T[j, r0 .. r0 + 7] = 8 bf16 = one 16-byte store per j
+      __syncthreads();
+      uint16_t* T = reinterpret_cast<uint16_t*>(a.snapT2) + inst * DD;
+      const int r0 = rb * OPT_ROWS;
+      for (int j = tid; j < D; j += NT)
+        *reinterpret_cast<uint4*>(T + (int64_t)j * D + r0) = *reinterpret_cast<const uint4*>(s_t + j * OPT_ROWS);
+    }
+  }
+}
+
+// =========================================================================
+// snapshot of caller weights: fp32 -> TS (natural) and, for bf16, W2^T
+template <typename TS>
+__global__ __launch_bounds__(NT) void snap_kernel(const float* W1, const float* W2, const float* W3, void* s1,
+                                                   void* s2, void* s3, void* sT2, int64_t n_dd, int D) {
+  const int64_t i4 = (int64_t)blockIdx.x * NT + threadIdx.x;   // float4 index
+  if (i4 * 4 >= n_dd) return;
+  const float* src[3] = {W1, W2, W3};
+  void* dst[3] = {s1, s2, s3};
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const float4 x = reinterpret_cast<const float4*>(src[m])[i4];
+    const float v[4] = {x.x, x.y, x.z, x.w};
+    store4(reinterpret_cast<TS*>(dst[m]) + i4 * 4, v);
+  }
+  if constexpr (sizeof(TS) == 2) {
+    if (sT2) {
+      const float4 x = reinterpret_cast<const float4*>(W2)[i4];
+      const float v[4] = {x.x, x.y, x.z, x.w};
+      const int64_t e = i4 * 4;
+      const int64_t DD = (int64_t)D * D;
+      const int64_t inst = e / DD, rem = e % DD;
+      const int r = (int)(rem / D), c = (int)(rem % D);
+      uint16_t* T = reinterpret_cast<uint16_t*>(sT2) + inst * DD;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) T[(int64_t)(c + q) * D + r] = (uint16_t)f2bf(v[q]);
     }
   }
 }

@@ -47,11 +47,13 @@ def kernel_flops(wl, lact):
     app = sum(b - a for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags) if f & W.APPLY)
     n_upd = sum(1 for f in wl.flags if f & W.UPDATE)
     return {
-        lact.K_FWD: (6.0 * upd + 4.0 * app) * D * D * n,   # K W1^T, K W3^T, V W2; Q W1^T, Q W3^T
+        lact.K_UPD: 6.0 * upd * D * D * n,                  # K W1^T, K W3^T, V W2
+        lact.K_APP: 4.0 * app * D * D * n,                  # Q W1^T, Q W3^T
         lact.K_OUT: 2.0 * app * D * D * n,                  # Hq W2^T
         lact.K_DW: 6.0 * upd * D * D * n,                   # three contractions over tokens
         lact.K_OPT: 0.0,
         lact.K_NS: (30.0 * D ** 3 * 3 * n * n_upd) if wl.opt == W.OPT_MUON else 0.0,
+        lact.K_SNAP: 0.0,
     }
 
 

@@ -94,7 +94,7 @@ typedef struct {
     int32_t dh;         /* fast-weight hidden width; must equal d */
     int32_t io_dtype;   /* lact_dtype of q, k, v, o */
     int32_t opt;        /* lact_opt */
-    int32_t ns_iters;   /* Newton-Schulz steps for MUON, 0..16 (5 = standard) */
+    int32_t ns_iters;   /* Newton-Schulz steps for MUON, 1..16 (5 = standard) */
     int32_t rec_planes; /* bf16 planes per fp32 operand in the state
                            recurrence (update products, Newton-Schulz):
                            1 = bf16, 2 = bf16x2, 3 = bf16x3 (fp32-grade);
@@ -164,18 +164,20 @@ const char* lact_status_str(lact_status s);
 const char* lact_last_error(void);
 
 /*
- * Per-kernel timing (diagnostics).  While enabled on the calling thread,
- * every launch of a library kernel of class `kclass` (see LACT_K_*) is
- * bracketed by HIP events recorded on the launch stream.  lact_timing_read
- * synchronises those events and returns the summed milliseconds and the
- * number of launches since the last reset.
+ * Per-kernel timing (diagnostics; process-wide, not for concurrent use).
+ * While enabled, every launch of a library kernel of class `kclass` (see
+ * LACT_K_*) is bracketed by HIP events recorded on the launch stream.
+ * lact_timing_read synchronises those events and returns the summed
+ * milliseconds and the number of launches since the previous read.
  */
-#define LACT_K_FWD 0       /* forward products on q / k, v with fused epilogues */
-#define LACT_K_OUT 1       /* apply output product o = Hq W2^T */
-#define LACT_K_DW 2        /* weight-gradient contractions (split over tokens) */
-#define LACT_K_OPT 3       /* optimiser step + row renormalisation */
-#define LACT_K_NS 4        /* Newton-Schulz products and reductions */
-#define LACT_K_COUNT 5
+#define LACT_K_UPD 0       /* update forward: k W1^T, k W3^T, v W2 + SwiGLU backward terms */
+#define LACT_K_APP 1       /* apply forward: q W1^T, q W3^T -> gated hidden */
+#define LACT_K_OUT 2       /* apply output product o = Hq W2^T */
+#define LACT_K_DW 3        /* weight-gradient contractions (split over tokens) */
+#define LACT_K_OPT 4       /* optimiser step + row renormalisation + weight snapshot */
+#define LACT_K_NS 5        /* Newton-Schulz products and reductions */
+#define LACT_K_SNAP 6      /* snapshot of the caller's weights at call start */
+#define LACT_K_COUNT 7
 lact_status lact_timing_enable(int32_t kclass, int32_t on);
 lact_status lact_timing_read(int32_t kclass, double* total_ms, int64_t* launches);
 

@@ -183,18 +183,20 @@ int dw_tile(const lact_problem& p) { return p.d % 128 == 0 ? 128 : 64; }
 
 // split of the chunk's tokens for the weight-gradient contraction; split
 // lengths are multiples of 64 tokens
+int64_t round128(int64_t x) { return (x + 127) / 128 * 128; }
+
 void dw_split(const lact_problem& p, int64_t C, int& S, int64_t& kps) {
   const int bt = dw_tile(p);
   const int64_t tiles = (int64_t)(3 * p.d / bt) * (p.d / bt) * std::max(1, p.n_inst);
-  // about two workgroups per CU, with instances x splits a multiple of the 8
-  // XCDs so that every XCD receives whole (instance, split) groups of tiles
-  int64_t s = std::max<int64_t>(1, (512 + tiles / 2) / tiles);
+  // about one (8-wave) workgroup per CU, with instances x splits a multiple
+  // of the 8 XCDs so that every XCD receives whole (instance, split) groups
+  int64_t s = std::max<int64_t>(1, (256 + tiles / 2) / tiles);
   const int64_t n = std::max(1, p.n_inst);
   for (int k = 0; k < 8 && (n * s) % 8 != 0; ++k) ++s;
   if ((n * s) % 8 != 0) s = std::max<int64_t>(1, (512 + tiles / 2) / tiles);
   s = std::min<int64_t>(s, std::max<int64_t>(1, C / 256));
   s = std::max<int64_t>(1, std::min<int64_t>(s, 64));
-  kps = ((C + s - 1) / s + 63) / 64 * 64;
+  kps = round128((C + s - 1) / s);
   S = (int)((C + kps - 1) / kps);
   if (S < 1) S = 1;
 }
@@ -220,7 +222,6 @@ int upd_bj(const lact_problem& p, int64_t C) {
   return best;
 }
 
-int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 
 // --------------------------------------------------------------- workspace layout
 struct Ws {
@@ -260,7 +261,7 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   }
   w.S = S;
   w.nslots = nupd + 1;
-  w.ldE = round64(plan.max_upd);
+  w.ldE = round128(plan.max_upd);
   w.h_rows = h_rows;
   w.max_tt = (int)((plan.max_upd + FBT - 1) / FBT);
   const size_t snap_el = (f == PF32) ? 4 : 2;
@@ -382,8 +383,20 @@ constexpr int pick_stages(int words) { return 2 * words * 2 + 4096 <= LDS_MAX ? 
 template <typename TA, int PA, bool CA, typename TB, int PB, bool CB, typename TC, int BM>
 lact_status launch_gemm_t(const GemmArgs& g, int64_t grid, hipStream_t s) {
   if constexpr (sizeof(TA) == 2 && sizeof(TB) == 2) {
-    // both operands bf16: direct-load kernel, 4-deep LDS ring
-    hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, BM, 2>), dim3((unsigned)grid), dim3(NT), 0, s, g);
+    // both operands bf16: direct-load kernel (8 waves).  A k stage of width W
+    // must not cross a split boundary, and its reads past K must stay within
+    // a row-k operand's zero padding (column-k operands clamp their rows)
+    auto fits = [&](int64_t W) {
+      return (g.splits == 1 || g.kps % W == 0) && (g.K % W == 0 || g.kpad >= (g.K + W - 1) / W * W);
+    };
+    if (fits(128)) {
+      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 128, 2>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
+    } else if (fits(64)) {
+      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 64, 3>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
+    } else {
+      return fail(LACT_ERR_UNSUPPORTED, "internal: contraction length %lld / split %lld not 64-aligned",
+                  (long long)g.K, (long long)g.kps);
+    }
     HIP_TRY(hipGetLastError());
     return LACT_OK;
   }
@@ -479,6 +492,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
 
   {
     const int64_t n4 = (int64_t)n * DD / 4;
+    KernelTimer kt(LACT_K_SNAP, s);
     hipLaunchKernelGGL(snap_kernel<TS>, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), 0, s, P.W1, P.W2, P.W3,
                        slot(0, 0), slot(0, 1), slot(0, 2), sizeof(TS) == 2 ? slot(0, 3) : nullptr, (int64_t)n * DD, D);
     HIP_TRY(hipGetLastError());
@@ -510,7 +524,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       ua.W2x = P.W2;
     }
     ua.E = ws + w.e;
-    ua.ldE = round64(C);
+    ua.ldE = round128(C);
     ua.D = D;
     ua.upd_t0 = st.upd_t0;
     ua.upd_len = C;
@@ -519,7 +533,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       const int bj = upd_bj(p, C);
       const int64_t grid = (int64_t)n * ua.tiles_t * (D / bj);
       if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
-      KernelTimer kt(LACT_K_FWD, s);
+      KernelTimer kt(LACT_K_UPD, s);
       lact_status r = bj == 128 ? launch_upd_fwd<PT, 128>(ua, grid, s)
                       : bj == 96 ? launch_upd_fwd<PT, 96>(ua, grid, s)
                                  : launch_upd_fwd<PT, 64>(ua, grid, s);
@@ -549,6 +563,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       g.N = D;
       g.K = C;
       g.kps = kps;
+      g.kpad = ua.ldE;             // the update forward zero-fills E up to ldE
       g.batch = n;
       g.splits = S;
       lact_status r = launch_gemm<TREC, PT::PREC, false, TIO, PT::PIO, true, float>(g, dw_tile(p), LACT_K_DW, s);
@@ -650,7 +665,10 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     }
     {
       KernelTimer kt(LACT_K_OPT, s);
-      hipLaunchKernelGGL(opt_kernel<TS>, dim3((unsigned)(n * 3 * (D / OPT_ROWS))), dim3(NT), 0, s, oa);
+      const dim3 og((unsigned)(n * 3 * (D / OPT_ROWS)));
+      if (D <= 256) hipLaunchKernelGGL((opt_kernel<TS, 1>), og, dim3(NT), 0, s, oa);
+      else if (D <= 512) hipLaunchKernelGGL((opt_kernel<TS, 2>), og, dim3(NT), 0, s, oa);
+      else hipLaunchKernelGGL((opt_kernel<TS, 4>), og, dim3(NT), 0, s, oa);
       HIP_TRY(hipGetLastError());
     }
     ++nu;
@@ -697,7 +715,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     }
     if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
     {
-      KernelTimer kt(LACT_K_FWD, s);
+      KernelTimer kt(LACT_K_APP, s);
       lact_status r = abj == 128 ? launch_app_fwd<PT, 128>(aa, grid, s) : launch_app_fwd<PT, 64>(aa, grid, s);
       if (r) return r;
     }

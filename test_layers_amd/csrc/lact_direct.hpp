@@ -58,7 +58,7 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
 // bank groups: 8 rows x 16 B for row-k reads of 64- and 128-byte rows, and
 // for 256-byte rows read with ds_read_b64_tr_b16, the 32-byte column pairs of
 // rows r..r+3 and r+8..r+11 (two 16-lane groups) over all eight 32-byte slots.
-template <int R, int CC, int NW = 4>
+template <int R, int CC, int NW = 4, bool TR = false>
 struct DTile {
   static constexpr int CPR = CC / 8;
   static constexpr int BYTES = R * CC * 2;
@@ -66,9 +66,11 @@ struct DTile {
   static constexpr int INSTR = CHUNKS / (WAVE * NW);   // loads per wave
   static_assert(CHUNKS % (WAVE * NW) == 0, "tile must be a whole number of workgroup loads");
   static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row width");
+  // TR: the tile is read with ds_read_b64_tr_b16 (rows = k); otherwise with
+  // 16-byte row reads (rows = the MFMA row index)
   __device__ static __forceinline__ int swz(int r, int c) {
     if constexpr (CPR == 4) return c ^ ((r >> 1) & 3);
-    else if constexpr (CPR == 8) return c ^ (r & 7);
+    else if constexpr (!TR || CPR == 8) return c ^ (r & 7);
     else return c ^ ((((r & 3) | (((r >> 3) & 1) << 2))) << 1);
   }
   __device__ static __forceinline__ int phys(int row, int chunk) { return row * CPR + swz(row, chunk); }
@@ -215,36 +217,43 @@ __device__ __forceinline__ void dpipeline_il(int nk, I&& issue_one, C&& compute)
 }
 
 // =========================================================================
-// bf16 GEMM (same contract as gemm_kernel; A, B bf16; 16x16x32 MFMA with the
-// swapped operand order so that each lane owns 4 consecutive output columns)
-template <bool CA, bool CB, typename TC, int BM, int BN, int NST>
-__global__ __launch_bounds__(NT) void dgemm_kernel(GemmArgs g) {
-  constexpr int BKK = 64;
-  // row-k tiles: BM x 64 (8 chunks per row); column-k tiles: 64 x BM
-  using TA = typename std::conditional<CA, DTile<BKK, BM>, DTile<BM, BKK>>::type;
-  using TB = typename std::conditional<CB, DTile<BKK, BN>, DTile<BN, BKK>>::type;
+// bf16 GEMM (same contract as gemm_kernel; A, B bf16).  T x T output tile,
+// 8 waves: wave w owns quadrant (w & 3) of the tile and k half (w >> 2) of
+// every BKK stage (two waves per SIMD); the two k halves are summed through
+// LDS at the end.  The swapped MFMA operand order leaves each lane with 4
+// consecutive output columns.
+constexpr int DG_THREADS = 512;
+
+template <bool CA, bool CB, typename TC, int T, int BKK, int NST>
+__global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
+  constexpr int NW = 8, KH = BKK / 2, NKK = KH / 32;
+  using TA = typename std::conditional<CA, DTile<BKK, T, NW, true>, DTile<T, BKK, NW>>::type;
+  using TB = typename std::conditional<CB, DTile<BKK, T, NW, true>, DTile<T, BKK, NW>>::type;
   constexpr int STAGE = TA::BYTES + TB::BYTES;
   constexpr int LPS = TA::INSTR + TB::INSTR;
-  constexpr int FM = BM / 32, FN = BN / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+  constexpr int FM = T / 32, FN = T / 32;                 // quadrant T/2 x T/2
+  constexpr int RED = 4 * FM * FN * 256 * 4;              // k-half reduction buffer (bytes)
+  constexpr int SMEM = NST * STAGE > RED ? NST * STAGE : RED;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   __shared__ float s_scale;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int q = wave & 3, kh = wave >> 2;
+  const int wm = q >> 1, wn = q & 1;
   int bid = xcd_remap(blockIdx.x, gridDim.x);
   int gi = 0;
   while (gi + 1 < g.ngroups && bid >= g.g[gi].tiles) bid -= g.g[gi++].tiles;
   const GemmGroup& G = g.g[gi];
   const int M = G.M;
-  const int tn_count = (g.N + BN - 1) / BN;
-  const int tm_count = (M + BM - 1) / BM;
+  const int tn_count = (g.N + T - 1) / T;
+  const int tm_count = (M + T - 1) / T;
   const int tiles = tm_count * tn_count;
   const int tile = bid % tiles;
   bid /= tiles;
   const int split = bid % g.splits;
   const int b = bid / g.splits;
   const int tm = tile / tn_count, tn = tile % tn_count;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * T, n0 = tn * T;
 
   const bf16_t* A = reinterpret_cast<const bf16_t*>(G.A) + b * g.a_bs;
   const void* Bsrc = (g.B2 != nullptr && m0 >= g.m_switch) ? g.B2 : G.B;
@@ -283,48 +292,67 @@ __global__ __launch_bounds__(NT) void dgemm_kernel(GemmArgs g) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf, auto&& hook) {
     const char* st = smem + buf * STAGE;
-    constexpr int NSLOT = (BKK / 32) * FM;
 #pragma unroll
-    for (int kk = 0; kk < BKK; kk += 32) {
+    for (int t = 0; t < NKK; ++t) {
+      const int kk = kh * KH + t * 32;
       bf16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = dfrag<TA, CA>(st, wm * (BM / 2) + i * 16, kk, lane);
+      for (int i = 0; i < FM; ++i) af[i] = dfrag<TA, CA>(st, wm * (T / 2) + i * 16, kk, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = dfrag<TB, CB>(st + TA::BYTES, wn * (BN / 2) + j * 16, kk, lane);
+      for (int j = 0; j < FN; ++j) bfr[j] = dfrag<TB, CB>(st + TA::BYTES, wn * (T / 2) + j * 16, kk, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma(bfr[j], af[i], acc[i][j]);
-        hook((kk / 32) * FM + i, NSLOT);
+        hook(t * FM + i, NKK * FM);
       }
     }
   };
   dpipeline_il<NST, LPS>(nk, issue_one, compute);
 
+  // sum the two k halves (fixed order: half 0 + half 1)
+  bar();
+  float* red = reinterpret_cast<float*>(smem);
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        *reinterpret_cast<f32x4*>(red + ((q * FM + i) * FN + j) * 256 + lane * 4) = acc[i][j];
+  }
+  bar();
+  if (kh == 0) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] += *reinterpret_cast<const f32x4*>(red + ((q * FM + i) * FN + j) * 256 + lane * 4);
+  }
+
   float alpha = g.alpha, beta = g.beta;
   if (g.rowsq != nullptr) {
     if (wave == 0) {
-      float s = 0.f;
+      float sq = 0.f;
       const float* rq = g.rowsq + (int64_t)b * g.rowsq_n;
-      for (int i = lane; i < g.rowsq_n; i += WAVE) s += rq[i];
-      s = wave_sum(s);
-      if (lane == 0) s_scale = 1.0f / (sqrtf(s) + 1e-7f);
+      for (int i = lane; i < g.rowsq_n; i += WAVE) sq += rq[i];
+      sq = wave_sum(sq);
+      if (lane == 0) s_scale = 1.0f / (sqrtf(sq) + 1e-7f);
     }
     __syncthreads();
     const float sc = s_scale;
     for (int i = 0; i < g.alpha_pow; ++i) alpha *= sc;
     for (int i = 0; i < g.beta_pow; ++i) beta *= sc;
   }
+  if (kh == 1) return;
   TC* C = reinterpret_cast<TC*>(G.C) + b * g.c_bs + split * g.c_ss;
   const float* Cin = g.Cin ? g.Cin + b * g.cin_bs : nullptr;
   const bool trans = m0 >= g.trans_from;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
+    const int m = m0 + wm * (T / 2) + i * 16 + (lane & 15);
     if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int nq = n0 + wn * (BN / 2) + j * 16 + 4 * (lane >> 4);
+      const int nq = n0 + wn * (T / 2) + j * 16 + 4 * (lane >> 4);
       if (nq >= g.N) continue;
       float val[4];
 #pragma unroll

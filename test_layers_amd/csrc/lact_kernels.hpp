@@ -311,6 +311,7 @@ struct GemmArgs {
   int64_t ldcin, cin_bs;
   int N;
   int64_t K, kps;
+  int64_t kpad;          // row-k operands are readable, and zero, from K up to kpad (0: no padding)
   int batch, splits;
   float alpha, beta;
   // optional scale s = 1 / (sqrt(sum of rowsq[b * rowsq_n ...]) + 1e-7):
@@ -480,9 +481,11 @@ struct OptArgs {
 
 constexpr int OPT_RPW = 2;                // rows per wave
 constexpr int OPT_ROWS = OPT_RPW * 4;     // rows per workgroup
-constexpr int OPT_VPL = 4;                // float4 per lane per row (D <= 1024)
+constexpr int OPT_MAXS = 8;               // partials loaded per batch
 
-template <typename TS>
+// VPL = float4 per lane per row (D <= 256 * VPL).  Every load of a batch (all
+// partials of both rows, W, M) is issued before any arithmetic consumes it.
+template <typename TS, int VPL>
 __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
   __shared__ uint16_t s_t[OPT_ROWS * 1024];   // transposed-snapshot staging (bf16 W2 rows)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -495,63 +498,83 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
   const int inst = bid / 3;
   const int64_t DD = (int64_t)D * D;
   const float* src = a.src + inst * 3 * DD + mat * DD;
-
-  float bm = 0.f;
-  if (a.opt == 1) {
-    float s = 0.f;
-    for (int i = lane; i < a.nbp; i += WAVE) s += a.bpart[(int64_t)inst * a.nbp + i];
-    bm = wave_sum(s) * a.inv_len;
-  }
   float* W = a.W[mat] + inst * DD;
   float* M = a.M[mat] ? a.M[mat] + inst * DD : nullptr;
   TS* snap = a.snap[mat] ? reinterpret_cast<TS*>(a.snap[mat]) + inst * DD : nullptr;
   const int nv = D / 4;
+  const int row0 = rb * OPT_ROWS + wave * OPT_RPW;
+
+  float4 u[OPT_RPW][VPL], w[OPT_RPW][VPL], m[OPT_RPW][VPL];
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int rr = 0; rr < OPT_RPW; ++rr)
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e4 = lane + i * WAVE;
+      const int64_t o = (int64_t)(row0 + rr) * D;
+      const bool ok = e4 < nv;
+      u[rr][i] = z4;
+      w[rr][i] = ok ? reinterpret_cast<const float4*>(W + o)[e4] : z4;
+      m[rr][i] = (ok && a.opt == 1) ? reinterpret_cast<const float4*>(M + o)[e4] : z4;
+    }
+  for (int s0 = 0; s0 < a.splits; s0 += OPT_MAXS) {
+    float4 x[OPT_MAXS][OPT_RPW][VPL];
+#pragma unroll
+    for (int s = 0; s < OPT_MAXS; ++s)
+#pragma unroll
+      for (int rr = 0; rr < OPT_RPW; ++rr)
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          const int e4 = lane + i * WAVE;
+          x[s][rr][i] = (s0 + s < a.splits && e4 < nv)
+                            ? reinterpret_cast<const float4*>(src + (s0 + s) * a.src_ss + (int64_t)(row0 + rr) * D)[e4]
+                            : z4;
+        }
+#pragma unroll
+    for (int s = 0; s < OPT_MAXS; ++s)   // fixed order: partial 0, 1, 2, ...
+#pragma unroll
+      for (int rr = 0; rr < OPT_RPW; ++rr)
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          u[rr][i].x += x[s][rr][i].x;
+          u[rr][i].y += x[s][rr][i].y;
+          u[rr][i].z += x[s][rr][i].z;
+          u[rr][i].w += x[s][rr][i].w;
+        }
+  }
+
+  float bm = 0.f;
+  if (a.opt == 1) {
+    float sb = 0.f;
+    for (int i = lane; i < a.nbp; i += WAVE) sb += a.bpart[(int64_t)inst * a.nbp + i];
+    bm = wave_sum(sb) * a.inv_len;
+  }
 #pragma unroll
   for (int rr = 0; rr < OPT_RPW; ++rr) {
     const int lrow = wave * OPT_RPW + rr;
-    const int row = rb * OPT_ROWS + lrow;
-    float4 u[OPT_VPL], w[OPT_VPL];
-#pragma unroll
-    for (int i = 0; i < OPT_VPL; ++i) {
-      const int e4 = lane + i * WAVE;
-      if (e4 < nv) {
-        const float4* s0 = reinterpret_cast<const float4*>(src + (int64_t)row * D) + e4;
-        u[i] = s0[0];
-        w[i] = reinterpret_cast<const float4*>(W + (int64_t)row * D)[e4];
-      }
-    }
-    for (int s = 1; s < a.splits; ++s) {
-#pragma unroll
-      for (int i = 0; i < OPT_VPL; ++i) {
-        const int e4 = lane + i * WAVE;
-        if (e4 < nv) {
-          const float4 x = reinterpret_cast<const float4*>(src + s * a.src_ss + (int64_t)row * D)[e4];
-          u[i].x += x.x;
-          u[i].y += x.y;
-          u[i].z += x.z;
-          u[i].w += x.w;
-        }
-      }
-    }
+    const int row = row0 + rr;
     float so = 0.f, sn = 0.f;
-    float4 x[OPT_VPL];
+    float4 xn[VPL];
 #pragma unroll
-    for (int i = 0; i < OPT_VPL; ++i) {
+    for (int i = 0; i < VPL; ++i) {
       const int e4 = lane + i * WAVE;
       if (e4 < nv) {
         if (a.opt == 1) {
-          float4 m = reinterpret_cast<const float4*>(M + (int64_t)row * D)[e4];
-          m.x = bm * m.x - u[i].x;
-          m.y = bm * m.y - u[i].y;
-          m.z = bm * m.z - u[i].z;
-          m.w = bm * m.w - u[i].w;
-          reinterpret_cast<float4*>(M + (int64_t)row * D)[e4] = m;
-          x[i] = make_float4(w[i].x - m.x, w[i].y - m.y, w[i].z - m.z, w[i].w - m.w);
+          float4 mm = m[rr][i];
+          mm.x = bm * mm.x - u[rr][i].x;
+          mm.y = bm * mm.y - u[rr][i].y;
+          mm.z = bm * mm.z - u[rr][i].z;
+          mm.w = bm * mm.w - u[rr][i].w;
+          reinterpret_cast<float4*>(M + (int64_t)row * D)[e4] = mm;
+          xn[i] = make_float4(w[rr][i].x - mm.x, w[rr][i].y - mm.y, w[rr][i].z - mm.z, w[rr][i].w - mm.w);
         } else {
-          x[i] = make_float4(w[i].x + u[i].x, w[i].y + u[i].y, w[i].z + u[i].z, w[i].w + u[i].w);
+          xn[i] = make_float4(w[rr][i].x + u[rr][i].x, w[rr][i].y + u[rr][i].y, w[rr][i].z + u[rr][i].z,
+                              w[rr][i].w + u[rr][i].w);
         }
-        so += w[i].x * w[i].x + w[i].y * w[i].y + w[i].z * w[i].z + w[i].w * w[i].w;
-        sn += x[i].x * x[i].x + x[i].y * x[i].y + x[i].z * x[i].z + x[i].w * x[i].w;
+        so += w[rr][i].x * w[rr][i].x + w[rr][i].y * w[rr][i].y + w[rr][i].z * w[rr][i].z + w[rr][i].w * w[rr][i].w;
+        sn += xn[i].x * xn[i].x + xn[i].y * xn[i].y + xn[i].z * xn[i].z + xn[i].w * xn[i].w;
+      } else {
+        xn[i] = z4;
       }
     }
     float scale = 1.f;
@@ -561,10 +584,10 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
       scale = sqrtf(so) / sqrtf(sn);
     }
 #pragma unroll
-    for (int i = 0; i < OPT_VPL; ++i) {
+    for (int i = 0; i < VPL; ++i) {
       const int e4 = lane + i * WAVE;
       if (e4 < nv) {
-        const float4 y = make_float4(x[i].x * scale, x[i].y * scale, x[i].z * scale, x[i].w * scale);
+        const float4 y = make_float4(xn[i].x * scale, xn[i].y * scale, xn[i].z * scale, xn[i].w * scale);
         reinterpret_cast<float4*>(W + (int64_t)row * D)[e4] = y;
         if (snap) {
           const float yy[4] = {y.x, y.y, y.z, y.w};

@@ -33,8 +33,9 @@ CHUNK_UPDATE = 1
 CHUNK_APPLY = 2
 NO_RENORM = 1
 
-K_FWD, K_OUT, K_DW, K_OPT, K_NS = range(5)
-K_NAMES = {K_FWD: "fwd", K_OUT: "apply_out", K_DW: "dw", K_OPT: "opt", K_NS: "newton_schulz"}
+K_UPD, K_APP, K_OUT, K_DW, K_OPT, K_NS, K_SNAP = range(7)
+K_NAMES = {K_UPD: "update_fwd", K_APP: "apply_fwd", K_OUT: "apply_out", K_DW: "dw", K_OPT: "opt",
+           K_NS: "newton_schulz", K_SNAP: "snapshot"}
 
 EXPORTS = ["lact_workspace_size", "lact_chunk_update", "lact_apply", "lact_layer_forward",
            "lact_status_str", "lact_last_error", "lact_timing_enable", "lact_timing_read"]

@@ -665,9 +665,12 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     }
     {
       KernelTimer kt(LACT_K_OPT, s);
-      const dim3 og((unsigned)(n * 3 * (D / OPT_ROWS)));
-      if (D <= 256) hipLaunchKernelGGL((opt_kernel<TS, 1>), og, dim3(NT), 0, s, oa);
-      else if (D <= 512) hipLaunchKernelGGL((opt_kernel<TS, 2>), og, dim3(NT), 0, s, oa);
+      oa.rpw = opt_rpw(D);
+      const dim3 og((unsigned)(n * 3 * (D / (4 * oa.rpw))));
+      const int vpl = (oa.rpw * D + 255) / 256;
+      if (vpl == 1) hipLaunchKernelGGL((opt_kernel<TS, 1>), og, dim3(NT), 0, s, oa);
+      else if (vpl == 2) hipLaunchKernelGGL((opt_kernel<TS, 2>), og, dim3(NT), 0, s, oa);
+      else if (vpl == 3) hipLaunchKernelGGL((opt_kernel<TS, 3>), og, dim3(NT), 0, s, oa);
       else hipLaunchKernelGGL((opt_kernel<TS, 4>), og, dim3(NT), 0, s, oa);
       HIP_TRY(hipGetLastError());
     }

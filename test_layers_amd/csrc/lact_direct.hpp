@@ -385,8 +385,11 @@ __global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
   constexpr int STAGE = 2 * TX::BYTES + 3 * TW::BYTES;
   constexpr int LPS = 2 * TX::INSTR + 3 * TW::INSTR;
   constexpr int FN = BJ / 32;
+  constexpr int ET_BYTES = 3 * BJ * FBT * 2;   // update terms of the tile, staged for full-line stores
+  static_assert(ET_BYTES <= NST * STAGE, "staging fits the ring");
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
   __shared__ float s_red[2];
+  __shared__ float s_lr[FBT * 3];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -414,6 +417,17 @@ __global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
     if (lane == 0 && wave < 2) s_red[wave] = bsum;
     __syncthreads();
     if (tid == 0) a.bpart[(int64_t)inst * a.tiles_t + tb] = s_red[0] + s_red[1];
+  }
+
+  // the tile's learning rates, held in registers through the main loop
+  float lrv[2];
+  {
+    const float* lr = a.lr + inst * a.lr_bs + t0 * 3;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int x = tid + e * NT;
+      lrv[e] = (x < FBT * 3 && t0 + x / 3 < tend) ? lr[x] : 0.f;
+    }
   }
 
   const typename TX::Plan pk = TX::plan(K, D, t0, tend - 1, 0, wave, lane);
@@ -468,24 +482,28 @@ __global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
   };
   dpipeline_il<NST, LPS>(D / BKK, issue_one, compute);
 
-  bf16_t* E = reinterpret_cast<bf16_t*>(a.E) + inst * 3 * (int64_t)D * a.ldE;
-  const float* lr = a.lr + inst * a.lr_bs;
+  // Epilogue: SwiGLU backward terms into an LDS copy of the tile's E rows
+  // (row = term x hidden column, 128 tokens = 256 bytes, 16-byte chunks
+  // XOR-swizzled by row), then whole rows to global memory.
+  bar();   // every wave is done reading the ring
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    if (tid + e * NT < FBT * 3) s_lr[tid + e * NT] = lrv[e];
+  __syncthreads();
+  char* et = smem;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t tq = t0 + wm * 64 + i * 16 + 4 * (lane >> 4);
-    const int64_t trel = tq - a.upd_t0;
-    if (trel >= a.ldE) continue;
+    const int tl = wm * 64 + i * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
     float e1[4], e2[4], e3[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = tq + r < tend;
-      e1[r] = ok ? lr[(tq + r) * 3 + 0] : 0.f;
-      e2[r] = ok ? lr[(tq + r) * 3 + 1] : 0.f;
-      e3[r] = ok ? lr[(tq + r) * 3 + 2] : 0.f;
+      e1[r] = s_lr[(tl + r) * 3 + 0];
+      e2[r] = s_lr[(tl + r) * 3 + 1];
+      e3[r] = s_lr[(tl + r) * 3 + 2];
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int col = j0 + wn * (BJ / 2) + j * 16 + (lane & 15);
+      const int col = wn * (BJ / 2) + j * 16 + (lane & 15);
       float u1[4], u3[4], u2[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -497,9 +515,31 @@ __global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
         u3[r] = e3[r] * gg * s;
         u2[r] = e2[r] * s * bb;
       }
-      store4(E + (int64_t)col * a.ldE + trel, u1);
-      store4(E + (int64_t)(D + col) * a.ldE + trel, u3);
-      store4(E + (int64_t)(2 * D + col) * a.ldE + trel, u2);
+      const int chunk = tl >> 3, half = (tl >> 2) & 1;
+      const float* terms[3] = {u1, u3, u2};
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        const int row = m * BJ + col;
+        const int off = row * (FBT * 2) + ((chunk ^ (row & 15)) << 4) + (half << 3);
+        uint2 pk2;
+        pk2.x = f2bf(terms[m][0]) | (f2bf(terms[m][1]) << 16);
+        pk2.y = f2bf(terms[m][2]) | (f2bf(terms[m][3]) << 16);
+        *reinterpret_cast<uint2*>(et + off) = pk2;
+      }
+    }
+  }
+  __syncthreads();
+  // E rows U1 | U3 | U2-terms, token-fastest; the tile's 128 tokens lie
+  // inside the row's ldE (zero terms past the chunk end)
+  bf16_t* E = reinterpret_cast<bf16_t*>(a.E) + inst * 3 * (int64_t)D * a.ldE + (t0 - a.upd_t0);
+  constexpr int ROWS = 3 * BJ;
+  for (int r0 = 0; r0 < ROWS; r0 += 4 * (NT / WAVE)) {
+    const int row = r0 + wave * 4 + (lane >> 4);
+    if (row < ROWS) {
+      const int c = lane & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(et + row * (FBT * 2) + ((c ^ (row & 15)) << 4));
+      const int m = row / BJ, col = row % BJ;
+      *reinterpret_cast<uint4*>(E + (int64_t)(m * D + j0 + col) * a.ldE + c * 8) = v;
     }
   }
 }

@@ -471,6 +471,7 @@ struct OptArgs {
   int nbp;
   float inv_len;         // 1 / chunk length
   int D;
+  int rpw;               // rows per wave: 4 (D <= 256), 2 (D <= 512) or 1
   int opt;               // 0 GD, 1 momentum, 2 Muon
   int renorm;
   // snapshot of the new weights (bf16 or fp32, natural layout) and, for
@@ -479,68 +480,80 @@ struct OptArgs {
   void* snapT2;
 };
 
-constexpr int OPT_RPW = 2;                // rows per wave
-constexpr int OPT_ROWS = OPT_RPW * 4;     // rows per workgroup
 constexpr int OPT_MAXS = 8;               // partials loaded per batch
 
-// VPL = float4 per lane per row (D <= 256 * VPL).  Every load of a batch (all
-// partials of both rows, W, M) is issued before any arithmetic consumes it.
+__host__ __device__ constexpr int opt_rpw(int D) { return D <= 256 ? 4 : D <= 512 ? 2 : 1; }
+
+// Optimiser step, one matrix row block per workgroup.  A wave owns rpw
+// consecutive rows, i.e. one contiguous span of rpw * D floats that its lanes
+// cover with VPL float4 each (lane + 64 i); lanes past the span load its last
+// float4 (always in bounds) and drop it, so every load is a plain 16-byte
+// load issued before any arithmetic consumes it.  Row sums of squares are
+// wave reductions per row.
 template <typename TS, int VPL>
 __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
-  __shared__ uint16_t s_t[OPT_ROWS * 1024];   // transposed-snapshot staging (bf16 W2 rows)
+  __shared__ uint16_t s_t[4096];   // transposed-snapshot staging: rows_wg x D bf16 (rows_wg * D <= 4096)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int D = a.D;
-  const int rblocks = D / OPT_ROWS;
+  const int D = a.D, rpw = a.rpw, rows_wg = 4 * rpw;
+  const int rblocks = D / rows_wg;
   int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int rb = bid % rblocks;
   bid /= rblocks;
   const int mat = bid % 3;
   const int inst = bid / 3;
   const int64_t DD = (int64_t)D * D;
-  const float* src = a.src + inst * 3 * DD + mat * DD;
-  float* W = a.W[mat] + inst * DD;
-  float* M = a.M[mat] ? a.M[mat] + inst * DD : nullptr;
-  TS* snap = a.snap[mat] ? reinterpret_cast<TS*>(a.snap[mat]) + inst * DD : nullptr;
   const int nv = D / 4;
-  const int row0 = rb * OPT_ROWS + wave * OPT_RPW;
+  const int span = rpw * nv;
+  const int row0 = rb * rows_wg + wave * rpw;
+  const int64_t base4 = (int64_t)row0 * nv;
+  const float4* src = reinterpret_cast<const float4*>(a.src + inst * 3 * DD + mat * DD) + base4;
+  float4* W = reinterpret_cast<float4*>(a.W[mat] + inst * DD) + base4;
+  float4* M = a.M[mat] ? reinterpret_cast<float4*>(a.M[mat] + inst * DD) + base4 : nullptr;
+  TS* snap = a.snap[mat] ? reinterpret_cast<TS*>(a.snap[mat]) + inst * DD + base4 * 4 : nullptr;
+  const int64_t ss4 = a.src_ss / 4;
 
-  float4 u[OPT_RPW][VPL], w[OPT_RPW][VPL], m[OPT_RPW][VPL];
+  int ix[VPL], rid[VPL];
+  bool ok[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int idx = lane + i * WAVE;
+    ok[i] = idx < span;
+    ix[i] = min(idx, span - 1);
+    rid[i] = ix[i] / nv;
+  }
+  float4 u[VPL], w[VPL], m[VPL];
   const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int rr = 0; rr < OPT_RPW; ++rr)
+  for (int i = 0; i < VPL; ++i) {
+    w[i] = W[ix[i]];
+    m[i] = z4;
+    u[i] = z4;
+  }
+  if (a.opt == 1) {
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e4 = lane + i * WAVE;
-      const int64_t o = (int64_t)(row0 + rr) * D;
-      const bool ok = e4 < nv;
-      u[rr][i] = z4;
-      w[rr][i] = ok ? reinterpret_cast<const float4*>(W + o)[e4] : z4;
-      m[rr][i] = (ok && a.opt == 1) ? reinterpret_cast<const float4*>(M + o)[e4] : z4;
-    }
+    for (int i = 0; i < VPL; ++i) m[i] = M[ix[i]];
+  }
   for (int s0 = 0; s0 < a.splits; s0 += OPT_MAXS) {
-    float4 x[OPT_MAXS][OPT_RPW][VPL];
+    float4 x[OPT_MAXS][VPL];
 #pragma unroll
-    for (int s = 0; s < OPT_MAXS; ++s)
+    for (int s = 0; s < OPT_MAXS; ++s) {
+      if (s0 + s < a.splits) {
 #pragma unroll
-      for (int rr = 0; rr < OPT_RPW; ++rr)
+        for (int i = 0; i < VPL; ++i) x[s][i] = src[(int64_t)(s0 + s) * ss4 + ix[i]];
+      } else {
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-          const int e4 = lane + i * WAVE;
-          x[s][rr][i] = (s0 + s < a.splits && e4 < nv)
-                            ? reinterpret_cast<const float4*>(src + (s0 + s) * a.src_ss + (int64_t)(row0 + rr) * D)[e4]
-                            : z4;
-        }
+        for (int i = 0; i < VPL; ++i) x[s][i] = z4;
+      }
+    }
 #pragma unroll
     for (int s = 0; s < OPT_MAXS; ++s)   // fixed order: partial 0, 1, 2, ...
 #pragma unroll
-      for (int rr = 0; rr < OPT_RPW; ++rr)
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-          u[rr][i].x += x[s][rr][i].x;
-          u[rr][i].y += x[s][rr][i].y;
-          u[rr][i].z += x[s][rr][i].z;
-          u[rr][i].w += x[s][rr][i].w;
-        }
+      for (int i = 0; i < VPL; ++i) {
+        u[i].x += x[s][i].x;
+        u[i].y += x[s][i].y;
+        u[i].z += x[s][i].z;
+        u[i].w += x[s][i].w;
+      }
   }
 
   float bm = 0.f;
@@ -549,69 +562,67 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
     for (int i = lane; i < a.nbp; i += WAVE) sb += a.bpart[(int64_t)inst * a.nbp + i];
     bm = wave_sum(sb) * a.inv_len;
   }
+  float4 xn[VPL], mm[VPL];
+  float so[4] = {0.f, 0.f, 0.f, 0.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rr = 0; rr < OPT_RPW; ++rr) {
-    const int lrow = wave * OPT_RPW + rr;
-    const int row = row0 + rr;
-    float so = 0.f, sn = 0.f;
-    float4 xn[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e4 = lane + i * WAVE;
-      if (e4 < nv) {
-        if (a.opt == 1) {
-          float4 mm = m[rr][i];
-          mm.x = bm * mm.x - u[rr][i].x;
-          mm.y = bm * mm.y - u[rr][i].y;
-          mm.z = bm * mm.z - u[rr][i].z;
-          mm.w = bm * mm.w - u[rr][i].w;
-          reinterpret_cast<float4*>(M + (int64_t)row * D)[e4] = mm;
-          xn[i] = make_float4(w[rr][i].x - mm.x, w[rr][i].y - mm.y, w[rr][i].z - mm.z, w[rr][i].w - mm.w);
-        } else {
-          xn[i] = make_float4(w[rr][i].x + u[rr][i].x, w[rr][i].y + u[rr][i].y, w[rr][i].z + u[rr][i].z,
-                              w[rr][i].w + u[rr][i].w);
-        }
-        so += w[rr][i].x * w[rr][i].x + w[rr][i].y * w[rr][i].y + w[rr][i].z * w[rr][i].z + w[rr][i].w * w[rr][i].w;
-        sn += xn[i].x * xn[i].x + xn[i].y * xn[i].y + xn[i].z * xn[i].z + xn[i].w * xn[i].w;
-      } else {
-        xn[i] = z4;
-      }
+  for (int i = 0; i < VPL; ++i) {
+    if (a.opt == 1) {
+      mm[i] = make_float4(bm * m[i].x - u[i].x, bm * m[i].y - u[i].y, bm * m[i].z - u[i].z, bm * m[i].w - u[i].w);
+      xn[i] = make_float4(w[i].x - mm[i].x, w[i].y - mm[i].y, w[i].z - mm[i].z, w[i].w - mm[i].w);
+    } else {
+      mm[i] = z4;
+      xn[i] = make_float4(w[i].x + u[i].x, w[i].y + u[i].y, w[i].z + u[i].z, w[i].w + u[i].w);
     }
-    float scale = 1.f;
-    if (a.renorm) {
-      so = wave_sum(so);
-      sn = wave_sum(sn);
-      scale = sqrtf(so) / sqrtf(sn);
-    }
+    const float o2 = ok[i] ? w[i].x * w[i].x + w[i].y * w[i].y + w[i].z * w[i].z + w[i].w * w[i].w : 0.f;
+    const float n2 = ok[i] ? xn[i].x * xn[i].x + xn[i].y * xn[i].y + xn[i].z * xn[i].z + xn[i].w * xn[i].w : 0.f;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e4 = lane + i * WAVE;
-      if (e4 < nv) {
-        const float4 y = make_float4(xn[i].x * scale, xn[i].y * scale, xn[i].z * scale, xn[i].w * scale);
-        reinterpret_cast<float4*>(W + (int64_t)row * D)[e4] = y;
-        if (snap) {
-          const float yy[4] = {y.x, y.y, y.z, y.w};
-          store4(snap + (int64_t)row * D + 4 * e4, yy);
-        }
-        if constexpr (sizeof(TS) == 2) {
-          if (mat == 2 && a.snapT2) {
-            s_t[(4 * e4 + 0) * OPT_ROWS + lrow] = (uint16_t)f2bf(y.x);
-            s_t[(4 * e4 + 1) * OPT_ROWS + lrow] = (uint16_t)f2bf(y.y);
-            s_t[(4 * e4 + 2) * OPT_ROWS + lrow] = (uint16_t)f2bf(y.z);
-            s_t[(4 * e4 + 3) * OPT_ROWS + lrow] = (uint16_t)f2bf(y.w);
-          }
-        }
+    for (int r = 0; r < 4; ++r) {
+      so[r] += rid[i] == r ? o2 : 0.f;
+      sn[r] += rid[i] == r ? n2 : 0.f;
+    }
+  }
+  float scale[4] = {1.f, 1.f, 1.f, 1.f};
+  if (a.renorm) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r < rpw) scale[r] = sqrtf(wave_sum(so[r])) / sqrtf(wave_sum(sn[r]));
+  }
+  const bool stage_t = sizeof(TS) == 2 && mat == 2 && a.snapT2 != nullptr;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if (!ok[i]) continue;
+    const float sc = rid[i] == 0 ? scale[0] : rid[i] == 1 ? scale[1] : rid[i] == 2 ? scale[2] : scale[3];
+    const float4 y = make_float4(xn[i].x * sc, xn[i].y * sc, xn[i].z * sc, xn[i].w * sc);
+    W[ix[i]] = y;
+    if (a.opt == 1) M[ix[i]] = mm[i];
+    const float yy[4] = {y.x, y.y, y.z, y.w};
+    if (snap) store4(snap + (int64_t)ix[i] * 4, yy);
+    if constexpr (sizeof(TS) == 2) {
+      if (stage_t) {
+        const int lrow = wave * rpw + rid[i];
+        const int c = 4 * (ix[i] - rid[i] * nv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s_t[(c + q) * rows_wg + lrow] = (uint16_t)f2bf(yy[q]);
       }
     }
   }
   if constexpr (sizeof(TS) == 2) {
-    if (mat == 2 && a.snapT2) {
-      // W2^T[j, r0 .. r0 + 7] = 8 bf16 = one 16-byte store per j
+    if (stage_t) {
+      // W2^T[j, r0 .. r0 + rows_wg - 1]: rows_wg contiguous bf16 per j
       __syncthreads();
-      uint16_t* T = reinterpret_cast<uint16_t*>(a.snapT2) + inst * DD;
-      const int r0 = rb * OPT_ROWS;
-      for (int j = tid; j < D; j += NT)
-        *reinterpret_cast<uint4*>(T + (int64_t)j * D + r0) = *reinterpret_cast<const uint4*>(s_t + j * OPT_ROWS);
+      uint16_t* T = reinterpret_cast<uint16_t*>(a.snapT2) + inst * DD + rb * rows_wg;
+      if (rows_wg == 4) {
+        for (int j = tid; j < D; j += NT)
+          *reinterpret_cast<uint2*>(T + (int64_t)j * D) = *reinterpret_cast<const uint2*>(s_t + j * 4);
+      } else if (rows_wg == 8) {
+        for (int j = tid; j < D; j += NT)
+          *reinterpret_cast<uint4*>(T + (int64_t)j * D) = *reinterpret_cast<const uint4*>(s_t + j * 8);
+      } else {
+        for (int j = tid; j < D; j += NT) {
+          *reinterpret_cast<uint4*>(T + (int64_t)j * D) = *reinterpret_cast<const uint4*>(s_t + j * 16);
+          *reinterpret_cast<uint4*>(T + (int64_t)j * D + 8) = *reinterpret_cast<const uint4*>(s_t + j * 16 + 8);
+        }
+      }
     }
   }
 }

@@ -389,10 +389,8 @@ lact_status launch_gemm_t(const GemmArgs& g, int64_t grid, hipStream_t s) {
     auto fits = [&](int64_t W) {
       return (g.splits == 1 || g.kps % W == 0) && (g.K % W == 0 || g.kpad >= (g.K + W - 1) / W * W);
     };
-    if (fits(128)) {
-      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 128, 2>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
-    } else if (fits(64)) {
-      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 64, 3>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
+    if (fits(64)) {
+      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 64, 4>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
     } else {
       return fail(LACT_ERR_UNSUPPORTED, "internal: contraction length %lld / split %lld not 64-aligned",
                   (long long)g.K, (long long)g.kps);

@@ -480,7 +480,7 @@ struct OptArgs {
   void* snapT2;
 };
 
-constexpr int OPT_MAXS = 8;               // partials loaded per batch
+constexpr int OPT_MAXS = 4;               // partials loaded per batch
 
 __host__ __device__ constexpr int opt_rpw(int D) { return D <= 256 ? 4 : D <= 512 ? 2 : 1; }
 

@@ -441,7 +441,7 @@ constexpr bool direct_fits(int bytes) { return bytes + 1024 <= LDS_MAX; }
 template <typename PT, int BJ>
 lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
   if constexpr (PT::UPD_FROM_SNAP && (BJ == 64 || BJ == 96)) {
-    hipLaunchKernelGGL((dupd_fwd_kernel<BJ, 64, 2>), dim3((unsigned)grid), dim3(NT), 0, s, ua);
+    hipLaunchKernelGGL((dupd_fwd_kernel<BJ, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, ua);
     HIP_TRY(hipGetLastError());
     return LACT_OK;
   }

@@ -24,10 +24,13 @@ struct bf16_t { uint16_t x; };  // storage type of bf16 tensors (raw bits)
 
 constexpr int WAVE = 64;
 
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);   // round to nearest even (finite inputs)
-  return u >> 16;
+// float -> bf16 bits, round to nearest even (gfx950's conversion instruction)
+__device__ __forceinline__ uint32_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two floats -> packed bf16 pair (lo in bits 0..15), one conversion instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -57,7 +60,7 @@ __device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ void store4(bf16_t* p, const float (&v)[4]) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(f2bf(v[0]) | (f2bf(v[1]) << 16), f2bf(v[2]) | (f2bf(v[3]) << 16));
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
@@ -316,6 +319,7 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float fast_sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// logistic function with the hardware reciprocal (1 ulp) instead of an IEEE division
+__device__ __forceinline__ float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 }  // namespace lact

@@ -378,13 +378,26 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
 // =========================================================================
 // bf16 update forward tile (same contract as upd_fwd_kernel with bf16
 // snapshots: W2 operand from the transposed snapshot)
+// waves that issue the W tile loads: the largest count that divides the tile
+constexpr int upd_w_waves(int bj, int bkk) {
+  return (bj * (bkk / 8)) % (WAVE * 8) == 0 ? 8 : (bj * (bkk / 8)) % (WAVE * 6) == 0 ? 6 : 4;
+}
+
+// 8 waves: wave w owns tokens 32 (w >> 1) .. +31 and hidden columns
+// (BJ / 2)(w & 1) .. +BJ/2-1 of the 128 x BJ tile (two waves per SIMD keep
+// the MFMA pipes fed).  K and V tiles are loaded by all eight waves, the W
+// tiles by the first upd_w_waves; with a two-stage ring every wait is for
+// all of a wave's loads, so unequal per-wave load counts are fine.
 template <int BJ, int BKK, int NST>
-__global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
-  using TX = DTile<FBT, BKK>;   // K, V: 128 tokens x 64 k
-  using TW = DTile<BJ, BKK>;    // W1, W3, W2^T rows: BJ x 64 k
+__global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
+  static_assert(NST == 2, "per-wave load counts differ: only full waits");
+  constexpr int NWV = DG_THREADS / WAVE;
+  constexpr int WW = upd_w_waves(BJ, BKK);
+  using TX = DTile<FBT, BKK, NWV>;   // K, V: 128 tokens x BKK
+  using TW = DTile<BJ, BKK, WW>;     // W1, W3, W2^T rows: BJ x BKK
   constexpr int STAGE = 2 * TX::BYTES + 3 * TW::BYTES;
-  constexpr int LPS = 2 * TX::INSTR + 3 * TW::INSTR;
-  constexpr int FN = BJ / 32;
+  constexpr int LPS = 2 * TX::INSTR + 3 * TW::INSTR;   // loads per stage of a W-loading wave
+  constexpr int FM = 2, FN = BJ / 32;
   constexpr int ET_BYTES = 3 * BJ * FBT * 2;   // update terms of the tile, staged for full-line stores
   static_assert(ET_BYTES <= NST * STAGE, "staging fits the ring");
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
@@ -410,57 +423,48 @@ __global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
   const bf16_t* W3 = reinterpret_cast<const bf16_t*>(a.W3) + inst * DD;
   const bf16_t* W2T = reinterpret_cast<const bf16_t*>(a.W2x) + inst * DD;
 
-  if (a.beta != nullptr && jb == 0) {
-    float bsum = 0.f;
-    if (tid < FBT && t0 + tid < tend) bsum = a.beta[inst * a.beta_bs + t0 + tid];
-    bsum = wave_sum(bsum);
-    if (lane == 0 && wave < 2) s_red[wave] = bsum;
-    __syncthreads();
-    if (tid == 0) a.bpart[(int64_t)inst * a.tiles_t + tb] = s_red[0] + s_red[1];
-  }
-
-  // the tile's learning rates, held in registers through the main loop
-  float lrv[2];
+  // the tile's learning rates and momentum coefficients, held in registers
+  // through the main loop (used by the epilogue)
+  float lrv = 0.f, bval = 0.f;
   {
     const float* lr = a.lr + inst * a.lr_bs + t0 * 3;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int x = tid + e * NT;
-      lrv[e] = (x < FBT * 3 && t0 + x / 3 < tend) ? lr[x] : 0.f;
-    }
+    if (tid < FBT * 3 && t0 + tid / 3 < tend) lrv = lr[tid];
+    if (a.beta != nullptr && jb == 0 && tid < FBT && t0 + tid < tend) bval = a.beta[inst * a.beta_bs + t0 + tid];
   }
 
+  const bool wload = wave < WW;
   const typename TX::Plan pk = TX::plan(K, D, t0, tend - 1, 0, wave, lane);
   const typename TX::Plan pv = TX::plan(V, D, t0, tend - 1, 0, wave, lane);
-  const typename TW::Plan p1 = TW::plan(W1, D, j0, D - 1, 0, wave, lane);
-  const typename TW::Plan p3 = TW::plan(W3, D, j0, D - 1, 0, wave, lane);
-  const typename TW::Plan p2 = TW::plan(W2T, D, j0, D - 1, 0, wave, lane);
+  const typename TW::Plan p1 = TW::plan(W1, D, j0, D - 1, 0, wload ? wave : 0, lane);
+  const typename TW::Plan p3 = TW::plan(W3, D, j0, D - 1, 0, wload ? wave : 0, lane);
+  const typename TW::Plan p2 = TW::plan(W2T, D, j0, D - 1, 0, wload ? wave : 0, lane);
   auto issue_one = [&](int s, int buf, int idx) {
     char* st = smem + buf * STAGE;
     const int64_t off = (int64_t)s * BKK * 2;
     char* w = st + 2 * TX::BYTES;
     if (idx < TX::INSTR) TX::issue_one(st, pk, off, wave, idx);
     else if (idx < 2 * TX::INSTR) TX::issue_one(st + TX::BYTES, pv, off, wave, idx - TX::INSTR);
+    else if (!wload) return;
     else if (idx < 2 * TX::INSTR + TW::INSTR) TW::issue_one(w, p1, off, wave, idx - 2 * TX::INSTR);
     else if (idx < 2 * TX::INSTR + 2 * TW::INSTR) TW::issue_one(w + TW::BYTES, p3, off, wave, idx - 2 * TX::INSTR - TW::INSTR);
     else TW::issue_one(w + 2 * TW::BYTES, p2, off, wave, idx - 2 * TX::INSTR - 2 * TW::INSTR);
   };
-  f32x4 accA[4][FN], accB[4][FN], accG[4][FN];
+  f32x4 accA[FM][FN], accB[FM][FN], accG[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) accA[i][j] = accB[i][j] = accG[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf, auto&& hook) {
     const char* st = smem + buf * STAGE;
     const char* w = st + 2 * TX::BYTES;
-    constexpr int NSLOT = (BKK / 32) * 4;
+    constexpr int NSLOT = (BKK / 32) * FM;
 #pragma unroll
     for (int kk = 0; kk < BKK; kk += 32) {
-      bf16x8 fk[4], fv[4], f1[FN], f3[FN], f2[FN];
+      bf16x8 fk[FM], fv[FM], f1[FN], f3[FN], f2[FN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fk[i] = dfrag_row<TX>(st, wm * 64 + i * 16, kk, lane);
-        fv[i] = dfrag_row<TX>(st + TX::BYTES, wm * 64 + i * 16, kk, lane);
+      for (int i = 0; i < FM; ++i) {
+        fk[i] = dfrag_row<TX>(st, wm * 32 + i * 16, kk, lane);
+        fv[i] = dfrag_row<TX>(st + TX::BYTES, wm * 32 + i * 16, kk, lane);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -469,14 +473,14 @@ __global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
         f2[j] = dfrag_row<TW>(w + 2 * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           accA[i][j] = mfma(fk[i], f1[j], accA[i][j]);
           accB[i][j] = mfma(fk[i], f3[j], accB[i][j]);
           accG[i][j] = mfma(fv[i], f2[j], accG[i][j]);
         }
-        hook((kk / 32) * 4 + i, NSLOT);
+        hook((kk / 32) * FM + i, NSLOT);
       }
     }
   };
@@ -486,14 +490,17 @@ __global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
   // (row = term x hidden column, 128 tokens = 256 bytes, 16-byte chunks
   // XOR-swizzled by row), then whole rows to global memory.
   bar();   // every wave is done reading the ring
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-    if (tid + e * NT < FBT * 3) s_lr[tid + e * NT] = lrv[e];
+  if (tid < FBT * 3) s_lr[tid] = lrv;
+  if (a.beta != nullptr && jb == 0) {
+    const float bs = wave_sum(bval);
+    if (lane == 0 && wave < 2) s_red[wave] = bs;
+  }
   __syncthreads();
+  if (a.beta != nullptr && jb == 0 && tid == 0) a.bpart[(int64_t)inst * a.tiles_t + tb] = s_red[0] + s_red[1];
   char* et = smem;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tl = wm * 64 + i * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
+  for (int i = 0; i < FM; ++i) {
+    const int tl = wm * 32 + i * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
     float e1[4], e2[4], e3[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -522,8 +529,8 @@ __global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
         const int row = m * BJ + col;
         const int off = row * (FBT * 2) + ((chunk ^ (row & 15)) << 4) + (half << 3);
         uint2 pk2;
-        pk2.x = f2bf(terms[m][0]) | (f2bf(terms[m][1]) << 16);
-        pk2.y = f2bf(terms[m][2]) | (f2bf(terms[m][3]) << 16);
+        pk2.x = pack_bf16x2(terms[m][0], terms[m][1]);
+        pk2.y = pack_bf16x2(terms[m][2], terms[m][3]);
         *reinterpret_cast<uint2*>(et + off) = pk2;
       }
     }
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(NT) void dupd_fwd_kernel(UpdFwdArgs a) {
   // inside the row's ldE (zero terms past the chunk end)
   bf16_t* E = reinterpret_cast<bf16_t*>(a.E) + inst * 3 * (int64_t)D * a.ldE + (t0 - a.upd_t0);
   constexpr int ROWS = 3 * BJ;
-  for (int r0 = 0; r0 < ROWS; r0 += 4 * (NT / WAVE)) {
+  for (int r0 = 0; r0 < ROWS; r0 += 4 * NWV) {
     const int row = r0 + wave * 4 + (lane >> 4);
     if (row < ROWS) {
       const int c = lane & 15;

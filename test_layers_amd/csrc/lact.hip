@@ -389,7 +389,14 @@ lact_status launch_gemm_t(const GemmArgs& g, int64_t grid, hipStream_t s) {
     auto fits = [&](int64_t W) {
       return (g.splits == 1 || g.kps % W == 0) && (g.K % W == 0 || g.kpad >= (g.K + W - 1) / W * W);
     };
-    if (fits(64)) {
+    // short contractions (a few stages per tile): a two-stage 64-wide ring
+    // that leaves room for two workgroups per CU, so one's prologue and
+    // epilogue overlap the other's main loop; long ones: 128-wide stages
+    if (g.kps <= 512 && fits(64)) {
+      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
+    } else if (fits(128)) {
+      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 128, 2>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
+    } else if (fits(64)) {
       hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 64, 4>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
     } else {
       return fail(LACT_ERR_UNSUPPORTED, "internal: contraction length %lld / split %lld not 64-aligned",

@@ -554,7 +554,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
 // =========================================================================
 // bf16 apply forward tile (same contract as app_fwd_kernel)
 template <int BJ, int BKK, int NST>
-__global__ __launch_bounds__(NT) void dapp_fwd_kernel(AppFwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
   using TX = DTile<FBT, BKK>;
   using TW = DTile<BJ, BKK>;
   constexpr int STAGE = TX::BYTES + 2 * TW::BYTES;

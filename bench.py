@@ -68,7 +68,9 @@ def opt_bytes(wl, S):
 
 
 def cpu_baseline(wl, inp, budget):
-    """The oracle as it stands, on a bounded sample of the same workload."""
+    """The oracle as it stands, on a bounded sample of the same workload:
+    whole instances (heads), each over the whole sequence, until about
+    `budget` seconds of CPU work have been done."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -77,18 +79,51 @@ def cpu_baseline(wl, inp, budget):
         threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     done = 0
-    for i in range(wl.n_inst):
+    while time.perf_counter() - t0 < budget:
+        i = done % wl.n_inst
         O.forward_instance(inp.q[i], inp.k[i], inp.v[i], inp.lr[i],
                            None if inp.beta is None else inp.beta[i],
                            inp.W1[i], inp.W2[i], inp.W3[i], wl.bounds, wl.flags, wl.order, wl.opt)
         done += 1
-        if time.perf_counter() - t0 >= budget:
-            break
     dt = time.perf_counter() - t0
     tokens = wl.tokens * done / wl.n_inst
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {wl.n_inst} instances (heads), whole sequence each, "
-                      f"{dt:.1f} s, numpy fp64"}
+            "sample": f"{done} instance passes (heads, cycling over the {wl.n_inst} of the workload), "
+                      f"whole {wl.L}-token sequence each, {dt:.1f} s, numpy fp64"}
+
+
+SRC_FILES = ("lact.hip", "lact_device.hpp", "lact_kernels.hpp", "lact_direct.hpp")
+
+
+def source_sha():
+    """Hash of the kernel sources; counter-derived traffic is reported only
+    for the exact sources the counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    here = os.path.dirname(os.path.abspath(__file__))
+    for f in SRC_FILES:
+        with open(os.path.join(here, "test_layers_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def pmc_traffic(kernel, workload):
+    """HBM bytes per launch of a kernel class from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's
+    reading), or None when absent or taken on other sources."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha() or t.get("workload") != workload:
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
 
 
 def main():
@@ -165,13 +200,13 @@ def main():
         per_launch = kf[d["kc"]] / (d["launches_per_step"])
         achieved = per_launch / (d["avg_launch_us"] * 1e-6)
         roof = {"kernel": dname, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": pmc_traffic(dname, wl.name),
                 "flops_per_launch": per_launch, "avg_launch_us": d["avg_launch_us"]}
     else:
         nb = opt_bytes(wl, 1) / d["launches_per_step"] * (1 if True else 0)
         achieved = nb / (d["avg_launch_us"] * 1e-6)
         roof = {"kernel": dname, "bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": pmc_traffic(dname, wl.name),
                 "bytes_per_launch": nb, "avg_launch_us": d["avg_launch_us"]}
     kernels = {k: {kk: round(vv, 4) for kk, vv in v.items() if kk != "kc"} for k, v in per.items()}
 

@@ -4,6 +4,7 @@
 // precision dispatch and kernel launches for the C ABI in include/lact.h.
 // All device work is asynchronous on the caller's stream.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cstdarg>
@@ -51,28 +52,54 @@ TimingState& timing() {
   return t;
 }
 
+// While timing is enabled for its class, a KernelTimer scope hands its two
+// events to the first kernel launched inside it (LACT_LAUNCH), whose dispatch
+// records them at kernel start and end: the execution time alone, the window
+// a kernel trace reports, without the gap before the dispatch.
+struct KernelTimer;
+KernelTimer*& current_timer() {
+  static thread_local KernelTimer* t = nullptr;
+  return t;
+}
 struct KernelTimer {
   hipEvent_t a = nullptr, b = nullptr;
-  hipStream_t s;
   int kc;
-  KernelTimer(int kclass, hipStream_t st) : s(st), kc(kclass) {
+  bool launched = false;
+  KernelTimer* prev;
+  KernelTimer(int kclass, hipStream_t) : kc(kclass), prev(current_timer()) {
+    current_timer() = this;
     TimingState& t = timing();
     std::lock_guard<std::mutex> g(t.mu);
     if (!t.on[kc]) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      if (a) (void)hipEventDestroy(a);
       a = b = nullptr;
-      return;
     }
-    (void)hipEventRecord(a, s);
   }
   ~KernelTimer() {
+    current_timer() = prev;
     if (!a) return;
-    (void)hipEventRecord(b, s);
+    if (!launched) {
+      (void)hipEventDestroy(a);
+      (void)hipEventDestroy(b);
+      return;
+    }
     TimingState& t = timing();
     std::lock_guard<std::mutex> g(t.mu);
     t.ev[kc].push_back({a, b});
   }
 };
+
+#define LACT_LAUNCH(kernel, grid, block, stream, ...)                                    \
+  do {                                                                                   \
+    KernelTimer* kt_ = current_timer();                                                  \
+    if (kt_ && kt_->a && !kt_->launched) {                                               \
+      kt_->launched = true;                                                              \
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, kt_->a, kt_->b, 0, __VA_ARGS__); \
+    } else {                                                                             \
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);                   \
+    }                                                                                    \
+  } while (0)
 
 // --------------------------------------------------------------- device check
 lact_status check_device() {
@@ -393,11 +420,11 @@ lact_status launch_gemm_t(const GemmArgs& g, int64_t grid, hipStream_t s) {
     // that leaves room for two workgroups per CU, so one's prologue and
     // epilogue overlap the other's main loop; long ones: 128-wide stages
     if (g.kps <= 512 && fits(64)) {
-      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
+      LACT_LAUNCH((dgemm_kernel<CA, CB, TC, BM, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), s, g);
     } else if (fits(128)) {
-      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 128, 2>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
+      LACT_LAUNCH((dgemm_kernel<CA, CB, TC, BM, 128, 2>), dim3((unsigned)grid), dim3(DG_THREADS), s, g);
     } else if (fits(64)) {
-      hipLaunchKernelGGL((dgemm_kernel<CA, CB, TC, BM, 64, 4>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, g);
+      LACT_LAUNCH((dgemm_kernel<CA, CB, TC, BM, 64, 4>), dim3((unsigned)grid), dim3(DG_THREADS), s, g);
     } else {
       return fail(LACT_ERR_UNSUPPORTED, "internal: contraction length %lld / split %lld not 64-aligned",
                   (long long)g.K, (long long)g.kps);
@@ -407,7 +434,7 @@ lact_status launch_gemm_t(const GemmArgs& g, int64_t grid, hipStream_t s) {
   }
   constexpr int BKK = pick_bk(PA + PB);
   constexpr int ST = pick_stages(stage_words(BM, PA, BM, PB, BKK));
-  hipLaunchKernelGGL((gemm_kernel<TA, PA, CA, TB, PB, CB, TC, BM, BM, BKK, ST>), dim3((unsigned)grid), dim3(NT), 0, s,
+  LACT_LAUNCH((gemm_kernel<TA, PA, CA, TB, PB, CB, TC, BM, BM, BKK, ST>), dim3((unsigned)grid), dim3(NT), s,
                      g);
   HIP_TRY(hipGetLastError());
   return LACT_OK;
@@ -448,7 +475,7 @@ constexpr bool direct_fits(int bytes) { return bytes + 1024 <= LDS_MAX; }
 template <typename PT, int BJ>
 lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
   if constexpr (PT::UPD_FROM_SNAP && (BJ == 64 || BJ == 96)) {
-    hipLaunchKernelGGL((dupd_fwd_kernel<BJ, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), 0, s, ua);
+    LACT_LAUNCH((dupd_fwd_kernel<BJ, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
     HIP_TRY(hipGetLastError());
     return LACT_OK;
   }
@@ -457,8 +484,8 @@ lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
   constexpr int BKK = pick_bk(PT::PIO + PW);
   constexpr int words = (2 * PT::PIO * FBT + 3 * PW * BJ) * (BKK + 8);
   constexpr int ST = pick_stages(words);
-  hipLaunchKernelGGL((upd_fwd_kernel<typename PT::TIO, PT::PIO, TW, PW, typename PT::TREC, BJ, BKK, ST>),
-                     dim3((unsigned)grid), dim3(NT), 0, s, ua);
+  LACT_LAUNCH((upd_fwd_kernel<typename PT::TIO, PT::PIO, TW, PW, typename PT::TREC, BJ, BKK, ST>),
+                     dim3((unsigned)grid), dim3(NT), s, ua);
   HIP_TRY(hipGetLastError());
   return LACT_OK;
 }
@@ -466,15 +493,15 @@ lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
 template <typename PT, int BJ>
 lact_status launch_app_fwd(const AppFwdArgs& aa, int64_t grid, hipStream_t s) {
   if constexpr (sizeof(typename PT::TIO) == 2 && sizeof(typename PT::TS) == 2) {
-    hipLaunchKernelGGL((dapp_fwd_kernel<BJ, 32, 3>), dim3((unsigned)grid), dim3(NT), 0, s, aa);
+    LACT_LAUNCH((dapp_fwd_kernel<BJ, 32, 3>), dim3((unsigned)grid), dim3(NT), s, aa);
     HIP_TRY(hipGetLastError());
     return LACT_OK;
   }
   constexpr int BKK = pick_bk(PT::PIO + PT::PS);
   constexpr int words = (PT::PIO * FBT + 2 * PT::PS * BJ) * (BKK + 8);
   constexpr int ST = pick_stages(words);
-  hipLaunchKernelGGL((app_fwd_kernel<typename PT::TIO, PT::PIO, typename PT::TS, PT::PS, typename PT::TAPP, BJ, BKK, ST>),
-                     dim3((unsigned)grid), dim3(NT), 0, s, aa);
+  LACT_LAUNCH((app_fwd_kernel<typename PT::TIO, PT::PIO, typename PT::TS, PT::PS, typename PT::TAPP, BJ, BKK, ST>),
+                     dim3((unsigned)grid), dim3(NT), s, aa);
   HIP_TRY(hipGetLastError());
   return LACT_OK;
 }
@@ -498,7 +525,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
   {
     const int64_t n4 = (int64_t)n * DD / 4;
     KernelTimer kt(LACT_K_SNAP, s);
-    hipLaunchKernelGGL(snap_kernel<TS>, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), 0, s, P.W1, P.W2, P.W3,
+    LACT_LAUNCH(snap_kernel<TS>, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), s, P.W1, P.W2, P.W3,
                        slot(0, 0), slot(0, 1), slot(0, 2), sizeof(TS) == 2 ? slot(0, 3) : nullptr, (int64_t)n * DD, D);
     HIP_TRY(hipGetLastError());
   }
@@ -603,7 +630,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       {
         KernelTimer kt(LACT_K_NS, s);
         const int64_t rows = (int64_t)n * 3 * D;
-        hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(NT), 0, s,
+        LACT_LAUNCH(reduce_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(NT), s,
                            reinterpret_cast<const float*>(ws + w.part), (int64_t)n * 3 * DD, S, U, rowsq, rows, D);
         HIP_TRY(hipGetLastError());
       }
@@ -673,10 +700,10 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       oa.rpw = opt_rpw(D);
       const dim3 og((unsigned)(n * 3 * (D / (4 * oa.rpw))));
       const int vpl = (oa.rpw * D + 255) / 256;
-      if (vpl == 1) hipLaunchKernelGGL((opt_kernel<TS, 1>), og, dim3(NT), 0, s, oa);
-      else if (vpl == 2) hipLaunchKernelGGL((opt_kernel<TS, 2>), og, dim3(NT), 0, s, oa);
-      else if (vpl == 3) hipLaunchKernelGGL((opt_kernel<TS, 3>), og, dim3(NT), 0, s, oa);
-      else hipLaunchKernelGGL((opt_kernel<TS, 4>), og, dim3(NT), 0, s, oa);
+      if (vpl == 1) LACT_LAUNCH((opt_kernel<TS, 1>), og, dim3(NT), s, oa);
+      else if (vpl == 2) LACT_LAUNCH((opt_kernel<TS, 2>), og, dim3(NT), s, oa);
+      else if (vpl == 3) LACT_LAUNCH((opt_kernel<TS, 3>), og, dim3(NT), s, oa);
+      else LACT_LAUNCH((opt_kernel<TS, 4>), og, dim3(NT), s, oa);
       HIP_TRY(hipGetLastError());
     }
     ++nu;

@@ -490,6 +490,18 @@ lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
   return LACT_OK;
 }
 
+// o = Hq W2^T with the apply tile (bf16 operands only); returns false when
+// the profile has no such path
+template <typename PT, int BJ>
+bool launch_app_out(const AppFwdArgs& aa, int64_t grid, hipStream_t s, lact_status* st) {
+  if constexpr (sizeof(typename PT::TIO) == 2 && sizeof(typename PT::TS) == 2 && sizeof(typename PT::TAPP) == 2) {
+    LACT_LAUNCH((dapp_fwd_kernel<BJ, 32, 3, true>), dim3((unsigned)grid), dim3(NT), s, aa);
+    *st = hipGetLastError() == hipSuccess ? LACT_OK : fail(LACT_ERR_HIP, "output launch failed");
+    return true;
+  }
+  return false;
+}
+
 template <typename PT, int BJ>
 lact_status launch_app_fwd(const AppFwdArgs& aa, int64_t grid, hipStream_t s) {
   if constexpr (sizeof(typename PT::TIO) == 2 && sizeof(typename PT::TS) == 2) {
@@ -723,6 +735,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
         ag.h0 = h0;
         ag.W1 = slot(u, 0);
         ag.W3 = slot(u, 2);
+        ag.W2 = slot(u, 1);
         groups.push_back(ag);
         h0 += st.app_len;
       }
@@ -754,7 +767,21 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       lact_status r = abj == 128 ? launch_app_fwd<PT, 128>(aa, grid, s) : launch_app_fwd<PT, 64>(aa, grid, s);
       if (r) return r;
     }
-    // o[t, r] = sum_j Hq[t, j] W2[r, j]
+    // o[t, r] = sum_j Hq[t, j] W2[r, j]: the apply tile in output mode
+    // (same grid), or the generic GEMM for profiles without a bf16 path
+    {
+      aa.o = P.o;
+      lact_status st = LACT_OK;
+      bool done;
+      {
+        KernelTimer kt(LACT_K_OUT, s);
+        done = abj == 128 ? launch_app_out<PT, 128>(aa, grid, s, &st) : launch_app_out<PT, 64>(aa, grid, s, &st);
+      }
+      if (done) {
+        if (st) return st;
+        continue;
+      }
+    }
     GemmArgs g = gemm_args();
     g.ngroups = ng;
     int64_t wgs128 = 0;

@@ -216,6 +216,42 @@ __device__ __forceinline__ void dpipeline_il(int nk, I&& issue_one, C&& compute)
   }
 }
 
+// dpipeline_il for workgroups whose waves issue different numbers of loads
+// per stage: LPS_A for waves with `wide` set, LPS_B for the others.  The
+// vmcnt target of each wait is that wave's own count of later stages' loads.
+template <int NST, int LPS_A, int LPS_B, class I, class C>
+__device__ __forceinline__ void dpipeline_il2(int nk, bool wide, I&& issue_one, C&& compute) {
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk)
+#pragma unroll
+      for (int i = 0; i < LPS_A; ++i) issue_one(s, s, i);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int later = min(NST - 2, nk - 1 - kt);
+    if (later >= 2) {
+      if (wide) wait_vm<2 * LPS_A>();
+      else wait_vm<2 * LPS_B>();
+    } else if (later == 1) {
+      if (wide) wait_vm<LPS_A>();
+      else wait_vm<LPS_B>();
+    } else {
+      wait_vm<0>();
+    }
+    bar();
+    const int ns = kt + NST - 1;
+    const bool nxt = ns < nk;
+    const int nb = ns % NST;
+    compute(kt % NST, [&](int slot, int nslots) {
+      if (nxt) {
+#pragma unroll
+        for (int i = 0; i < LPS_A; ++i)
+          if (i * nslots >= slot * LPS_A && i * nslots < (slot + 1) * LPS_A) issue_one(ns, nb, i);
+      }
+    });
+  }
+}
+
 // =========================================================================
 // bf16 GEMM (same contract as gemm_kernel; A, B bf16).  T x T output tile,
 // 8 waves: wave w owns quadrant (w & 3) of the tile and k half (w >> 2) of
@@ -386,17 +422,16 @@ constexpr int upd_w_waves(int bj, int bkk) {
 // 8 waves: wave w owns tokens 32 (w >> 1) .. +31 and hidden columns
 // (BJ / 2)(w & 1) .. +BJ/2-1 of the 128 x BJ tile (two waves per SIMD keep
 // the MFMA pipes fed).  K and V tiles are loaded by all eight waves, the W
-// tiles by the first upd_w_waves; with a two-stage ring every wait is for
-// all of a wave's loads, so unequal per-wave load counts are fine.
+// tiles by the first upd_w_waves; each wave waits on its own load count.
 template <int BJ, int BKK, int NST>
 __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
-  static_assert(NST == 2, "per-wave load counts differ: only full waits");
   constexpr int NWV = DG_THREADS / WAVE;
   constexpr int WW = upd_w_waves(BJ, BKK);
   using TX = DTile<FBT, BKK, NWV>;   // K, V: 128 tokens x BKK
   using TW = DTile<BJ, BKK, WW>;     // W1, W3, W2^T rows: BJ x BKK
   constexpr int STAGE = 2 * TX::BYTES + 3 * TW::BYTES;
   constexpr int LPS = 2 * TX::INSTR + 3 * TW::INSTR;   // loads per stage of a W-loading wave
+  constexpr int LPS_X = 2 * TX::INSTR;                 // ... of the other waves
   constexpr int FM = 2, FN = BJ / 32;
   constexpr int ET_BYTES = 3 * BJ * FBT * 2;   // update terms of the tile, staged for full-line stores
   static_assert(ET_BYTES <= NST * STAGE, "staging fits the ring");
@@ -484,7 +519,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
       }
     }
   };
-  dpipeline_il<NST, LPS>(D / BKK, issue_one, compute);
+  dpipeline_il2<NST, LPS, LPS_X>(D / BKK, wload, issue_one, compute);
 
   // Epilogue: SwiGLU backward terms into an LDS copy of the tile's E rows
   // (row = term x hidden column, 128 tokens = 256 bytes, 16-byte chunks
@@ -553,12 +588,16 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
 
 // =========================================================================
 // bf16 apply forward tile (same contract as app_fwd_kernel)
-template <int BJ, int BKK, int NST>
+template <int BJ, int BKK, int NST, bool OUT = false>
 __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
+  // OUT = false: Hq = silu(q W1^T) * (q W3^T) into the Hq buffer.
+  // OUT = true:  o = Hq W2^T, the same tiling with one product (A = Hq rows,
+  //              B = W2 rows, both contracted over the hidden index).
+  constexpr int NB = OUT ? 1 : 2;
   using TX = DTile<FBT, BKK>;
   using TW = DTile<BJ, BKK>;
-  constexpr int STAGE = TX::BYTES + 2 * TW::BYTES;
-  constexpr int LPS = TX::INSTR + 2 * TW::INSTR;
+  constexpr int STAGE = TX::BYTES + NB * TW::BYTES;
+  constexpr int LPS = TX::INSTR + NB * TW::INSTR;
   constexpr int FN = BJ / 32;
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -578,19 +617,23 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
   const int64_t tend = G.t0 + G.len;
   const int j0 = jb * BJ;
   const int64_t DD = (int64_t)D * D;
-  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + inst * a.x_bs;
-  const bf16_t* W1 = reinterpret_cast<const bf16_t*>(G.W1) + inst * DD;
-  const bf16_t* W3 = reinterpret_cast<const bf16_t*>(G.W3) + inst * DD;
+  // A operand rows: queries (q rows t) or their gated hidden (Hq rows h0 + t - t0)
+  const bf16_t* X = OUT ? reinterpret_cast<const bf16_t*>(a.H) + inst * a.h_bs
+                        : reinterpret_cast<const bf16_t*>(a.q) + inst * a.x_bs;
+  const int64_t xr0 = OUT ? G.h0 + (t0 - G.t0) : t0;
+  const int64_t xrmax = OUT ? G.h0 + (tend - G.t0) - 1 : tend - 1;
+  const bf16_t* B1 = reinterpret_cast<const bf16_t*>(OUT ? G.W2 : G.W1) + inst * DD;
+  const bf16_t* B3 = reinterpret_cast<const bf16_t*>(G.W3) + inst * DD;
 
-  const typename TX::Plan pq = TX::plan(Q, D, t0, tend - 1, 0, wave, lane);
-  const typename TW::Plan p1 = TW::plan(W1, D, j0, D - 1, 0, wave, lane);
-  const typename TW::Plan p3 = TW::plan(W3, D, j0, D - 1, 0, wave, lane);
+  const typename TX::Plan pq = TX::plan(X, D, xr0, xrmax, 0, wave, lane);
+  const typename TW::Plan p1 = TW::plan(B1, D, j0, D - 1, 0, wave, lane);
+  const typename TW::Plan p3 = TW::plan(OUT ? B1 : B3, D, j0, D - 1, 0, wave, lane);
   auto issue_one = [&](int s, int buf, int idx) {
     char* st = smem + buf * STAGE;
     const int64_t off = (int64_t)s * BKK * 2;
     if (idx < TX::INSTR) TX::issue_one(st, pq, off, wave, idx);
     else if (idx < TX::INSTR + TW::INSTR) TW::issue_one(st + TX::BYTES, p1, off, wave, idx - TX::INSTR);
-    else TW::issue_one(st + TX::BYTES + TW::BYTES, p3, off, wave, idx - TX::INSTR - TW::INSTR);
+    else if constexpr (!OUT) TW::issue_one(st + TX::BYTES + TW::BYTES, p3, off, wave, idx - TX::INSTR - TW::INSTR);
   };
   f32x4 accA[4][FN], accB[4][FN];
 #pragma unroll
@@ -608,14 +651,14 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         f1[j] = dfrag_row<TW>(st + TX::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
-        f3[j] = dfrag_row<TW>(st + TX::BYTES + TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+        if constexpr (!OUT) f3[j] = dfrag_row<TW>(st + TX::BYTES + TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           accA[i][j] = mfma(f1[j], fq[i], accA[i][j]);   // swapped: lane owns 4 columns of one token
-          accB[i][j] = mfma(f3[j], fq[i], accB[i][j]);
+          if constexpr (!OUT) accB[i][j] = mfma(f3[j], fq[i], accB[i][j]);
         }
         hook((kk / 32) * 4 + i, NSLOT);
       }
@@ -623,12 +666,13 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
   };
   dpipeline_il<NST, LPS>(D / BKK, issue_one, compute);
 
-  bf16_t* H = reinterpret_cast<bf16_t*>(a.H) + inst * a.h_bs;
+  // output rows: o rows t, or Hq rows h0 + t - t0
+  bf16_t* Y = OUT ? reinterpret_cast<bf16_t*>(a.o) + inst * a.x_bs : reinterpret_cast<bf16_t*>(a.H) + inst * a.h_bs;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t t = t0 + wm * 64 + i * 16 + (lane & 15);
     if (t >= tend) continue;
-    bf16_t* Hr = H + (G.h0 + (t - G.t0)) * (int64_t)D;
+    bf16_t* Yr = Y + (OUT ? t : G.h0 + (t - G.t0)) * (int64_t)D;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = j0 + wn * (BJ / 2) + j * 16 + 4 * (lane >> 4);
@@ -636,9 +680,9 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float x = accA[i][j][r];
-        h[r] = x * fast_sigmoid(x) * accB[i][j][r];
+        h[r] = OUT ? x : x * fast_sigmoid(x) * accB[i][j][r];
       }
-      store4(Hr + col, h);
+      store4(Yr + col, h);
     }
   }
 }

@@ -189,6 +189,7 @@ struct AppGroup {
   int64_t h0;            // row offset of the group in the Hq buffer
   const void* W1;        // snapshot [n, D, D]
   const void* W3;
+  const void* W2;
   int tiles;             // workgroups of this group
 };
 
@@ -199,6 +200,7 @@ struct AppFwdArgs {
   int64_t x_bs;
   void* H;               // [n, h_rows, D]
   int64_t h_bs;
+  void* o;               // output mode: [n, seq, D] (x_bs per instance)
   int D;
 };
 

@@ -527,6 +527,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
   using TAPP = typename PT::TAPP;
   const int n = p.n_inst, D = p.d;
   if (n == 0) return LACT_OK;
+  const bool part16 = PT::PREC == 1 && p.opt != LACT_OPT_MUON;
   const int64_t DD = (int64_t)D * D;
   const int64_t x_bs = seq_stride * D;
   char* ws = P.ws;
@@ -610,7 +611,10 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       g.kpad = ua.ldE;             // the update forward zero-fills E up to ldE
       g.batch = n;
       g.splits = S;
-      lact_status r = launch_gemm<TREC, PT::PREC, false, TIO, PT::PIO, true, float>(g, dw_tile(p), LACT_K_DW, s);
+      // the plain-bf16 recurrence keeps its token-split partials in bf16
+      // (fp32 accumulation inside each split, fp32 sum of the splits)
+      lact_status r = part16 ? launch_gemm<TREC, PT::PREC, false, TIO, PT::PIO, true, bf16_t>(g, dw_tile(p), LACT_K_DW, s)
+                             : launch_gemm<TREC, PT::PREC, false, TIO, PT::PIO, true, float>(g, dw_tile(p), LACT_K_DW, s);
       if (r) return r;
     }
     OptArgs oa;
@@ -632,7 +636,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     oa.snap[2] = slot(nu + 1, 1);
     oa.snapT2 = sizeof(TS) == 2 ? slot(nu + 1, 3) : nullptr;
     if (p.opt != LACT_OPT_MUON) {
-      oa.src = reinterpret_cast<const float*>(ws + w.part);
+      oa.src = ws + w.part;
       oa.src_ss = (int64_t)n * 3 * DD;
       oa.splits = S;
     } else {
@@ -712,10 +716,17 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       oa.rpw = opt_rpw(D);
       const dim3 og((unsigned)(n * 3 * (D / (4 * oa.rpw))));
       const int vpl = (oa.rpw * D + 255) / 256;
-      if (vpl == 1) LACT_LAUNCH((opt_kernel<TS, 1>), og, dim3(NT), s, oa);
-      else if (vpl == 2) LACT_LAUNCH((opt_kernel<TS, 2>), og, dim3(NT), s, oa);
-      else if (vpl == 3) LACT_LAUNCH((opt_kernel<TS, 3>), og, dim3(NT), s, oa);
-      else LACT_LAUNCH((opt_kernel<TS, 4>), og, dim3(NT), s, oa);
+      if (part16) {
+        if (vpl == 1) LACT_LAUNCH((opt_kernel<TS, 1, bf16_t>), og, dim3(NT), s, oa);
+        else if (vpl == 2) LACT_LAUNCH((opt_kernel<TS, 2, bf16_t>), og, dim3(NT), s, oa);
+        else if (vpl == 3) LACT_LAUNCH((opt_kernel<TS, 3, bf16_t>), og, dim3(NT), s, oa);
+        else LACT_LAUNCH((opt_kernel<TS, 4, bf16_t>), og, dim3(NT), s, oa);
+      } else {
+        if (vpl == 1) LACT_LAUNCH((opt_kernel<TS, 1>), og, dim3(NT), s, oa);
+        else if (vpl == 2) LACT_LAUNCH((opt_kernel<TS, 2>), og, dim3(NT), s, oa);
+        else if (vpl == 3) LACT_LAUNCH((opt_kernel<TS, 3>), og, dim3(NT), s, oa);
+        else LACT_LAUNCH((opt_kernel<TS, 4>), og, dim3(NT), s, oa);
+      }
       HIP_TRY(hipGetLastError());
     }
     ++nu;

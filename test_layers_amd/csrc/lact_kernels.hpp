@@ -464,7 +464,7 @@ __global__ __launch_bounds__(NT) void reduce_rows_kernel(const float* P, int64_t
 // src: per instance the stacked direction [U1; U3; U2] ([3D, D], natural
 // layouts) as `splits` partials summed in order.  One wave per row.
 struct OptArgs {
-  const float* src;
+  const void* src;       // partials (fp32, or bf16 in the plain-bf16 recurrence) or Muon's direction
   int64_t src_ss;        // elements between partials
   int splits;
   float* W[3];           // W1, W3, W2 (matching the stacked source blocks)
@@ -492,7 +492,7 @@ __host__ __device__ constexpr int opt_rpw(int D) { return D <= 256 ? 4 : D <= 51
 // float4 (always in bounds) and drop it, so every load is a plain 16-byte
 // load issued before any arithmetic consumes it.  Row sums of squares are
 // wave reductions per row.
-template <typename TS, int VPL>
+template <typename TS, int VPL, typename TP = float>
 __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
   __shared__ uint16_t s_t[4096];   // transposed-snapshot staging: rows_wg x D bf16 (rows_wg * D <= 4096)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -508,11 +508,19 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
   const int span = rpw * nv;
   const int row0 = rb * rows_wg + wave * rpw;
   const int64_t base4 = (int64_t)row0 * nv;
-  const float4* src = reinterpret_cast<const float4*>(a.src + inst * 3 * DD + mat * DD) + base4;
+  const TP* src = reinterpret_cast<const TP*>(a.src) + inst * 3 * DD + mat * DD + base4 * 4;
+  // four consecutive partial values as floats
+  auto ldp = [](const TP* p) -> float4 {
+    if constexpr (sizeof(TP) == 4) {
+      return *reinterpret_cast<const float4*>(p);
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      return make_float4(bf2f(v.x & 0xffffu), bf2f(v.x >> 16), bf2f(v.y & 0xffffu), bf2f(v.y >> 16));
+    }
+  };
   float4* W = reinterpret_cast<float4*>(a.W[mat] + inst * DD) + base4;
   float4* M = a.M[mat] ? reinterpret_cast<float4*>(a.M[mat] + inst * DD) + base4 : nullptr;
   TS* snap = a.snap[mat] ? reinterpret_cast<TS*>(a.snap[mat]) + inst * DD + base4 * 4 : nullptr;
-  const int64_t ss4 = a.src_ss / 4;
 
   int ix[VPL], rid[VPL];
   bool ok[VPL];
@@ -541,7 +549,7 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
     for (int s = 0; s < OPT_MAXS; ++s) {
       if (s0 + s < a.splits) {
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) x[s][i] = src[(int64_t)(s0 + s) * ss4 + ix[i]];
+        for (int i = 0; i < VPL; ++i) x[s][i] = ldp(src + (int64_t)(s0 + s) * a.src_ss + (int64_t)ix[i] * 4);
       } else {
 #pragma unroll
         for (int i = 0; i < VPL; ++i) x[s][i] = z4;

@@ -50,8 +50,15 @@ def rel_err(x, ref):
     return float(np.max(np.abs(x - ref)) / den) if den > 0 else float(np.max(np.abs(x)))
 
 
-def compare(wl: W.Workload, inp: W.Inputs, gpu, order=None, renorm=True, instances=None):
-    """Oracle instance by instance; returns {tensor: max over instances of err}."""
+def fro_ratio(x, ref):
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / den) if den > 0 else float(np.linalg.norm(x))
+
+
+def compare(wl: W.Workload, inp: W.Inputs, gpu, order=None, renorm=True, instances=None, fro=None):
+    """Oracle instance by instance; returns {tensor: max over instances of err}.
+    If `fro` is a dict it receives the Frobenius ratios ||gpu - ref|| / ||ref||
+    (max over instances) as well."""
     keys = ["o", "W1", "W2", "W3"] + (["M1", "M2", "M3"] if wl.opt == W.OPT_MOMENTUM else [])
     errs = {k: 0.0 for k in keys}
     idx = range(wl.n_inst) if instances is None else instances
@@ -68,4 +75,6 @@ def compare(wl: W.Workload, inp: W.Inputs, gpu, order=None, renorm=True, instanc
             if key == "o":
                 g, r = g[mask], r[mask]
             errs[key] = max(errs[key], rel_err(g, r))
+            if fro is not None:
+                fro[key] = max(fro.get(key, 0.0), fro_ratio(g, r))
     return errs

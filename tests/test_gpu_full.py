@@ -30,6 +30,8 @@ def test_full_size_config(lact, cid):
     gpu = run_gpu(wl, inp, torch, lact)
     log(f"  gpu done; oracle over {wl.n_inst} instances")
     t = time.time()
-    errs = compare(wl, inp, gpu)
+    fro = {}
+    errs = compare(wl, inp, gpu, fro=fro)
     log(f"  oracle {time.time() - t:.1f}s errs={ {k: f'{v:.2e}' for k, v in errs.items()} } gate={wl.tol}")
+    log(f"  frobenius ratios { {k: f'{v:.2e}' for k, v in fro.items()} }")
     assert max(errs.values()) <= wl.tol, errs

@@ -203,7 +203,8 @@ void build_plan(int32_t order, const std::vector<int64_t>& b, const std::vector<
 constexpr int LDS_MAX = 160 * 1024;
 
 // workgroups of 128x128 GEMM tiles -> tile edge
-int gemm_tile(int64_t wgs128) { return wgs128 >= 200 ? 128 : 64; }
+// 128-wide tiles only for grids that stay several rounds deep with them
+int gemm_tile(int64_t wgs128) { return wgs128 >= 4 * NCU ? 128 : 64; }
 
 // the column-k operand tile of the contraction must not overhang D
 int dw_tile(const lact_problem& p) { return p.d % 128 == 0 ? 128 : 64; }
@@ -215,13 +216,25 @@ int64_t round128(int64_t x) { return (x + 127) / 128 * 128; }
 void dw_split(const lact_problem& p, int64_t C, int& S, int64_t& kps) {
   const int bt = dw_tile(p);
   const int64_t tiles = (int64_t)(3 * p.d / bt) * (p.d / bt) * std::max(1, p.n_inst);
-  // about one (8-wave) workgroup per CU, with instances x splits a multiple
-  // of the 8 XCDs so that every XCD receives whole (instance, split) groups
-  int64_t s = std::max<int64_t>(1, (256 + tiles / 2) / tiles);
+  // Split count: the filled fraction of the last round of (one-per-CU)
+  // workgroups, minus a charge per split for the partial set it writes and
+  // the optimiser re-reads (3D^2 fp32 per instance, against ~5DC bf16 of E
+  // and k, v traffic: ~0.2 D / C); ties go to instances x splits a multiple
+  // of the 8 XCDs (every XCD then receives whole (instance, split) groups).
   const int64_t n = std::max(1, p.n_inst);
-  for (int k = 0; k < 8 && (n * s) % 8 != 0; ++k) ++s;
-  if ((n * s) % 8 != 0) s = std::max<int64_t>(1, (512 + tiles / 2) / tiles);
-  s = std::min<int64_t>(s, std::max<int64_t>(1, C / 256));
+  const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, C / 256));
+  const double charge = 0.2 * (double)p.d / (double)std::max<int64_t>(1, C);
+  int64_t s = 1;
+  double best = -1e9;
+  for (int64_t c = 1; c <= smax; ++c) {
+    const int64_t wgs = tiles * c;
+    const double fill = (double)wgs / (double)(((wgs + NCU - 1) / NCU) * NCU);
+    const double score = fill - charge * (double)c + ((n * c) % 8 == 0 ? 0.005 : 0.0);
+    if (score > best + 1e-12) {
+      best = score;
+      s = c;
+    }
+  }
   s = std::max<int64_t>(1, std::min<int64_t>(s, 64));
   kps = round128((C + s - 1) / s);
   S = (int)((C + kps - 1) / kps);
@@ -234,9 +247,11 @@ int upd_bj(const lact_problem& p, int64_t C) {
   const int64_t tt = (C + FBT - 1) / FBT;
   int best = 64;
   double best_eff = -1;
-  const bool direct = profile_of(p) == PBF16;   // direct-load tiles fit BJ <= 96
+  // direct-load tiles fit BJ <= 96; the register-path (multi-plane) tiles
+  // are free of register spills only at BJ = 64
+  const bool direct = profile_of(p) == PBF16;
   for (int bj : {128, 96, 64}) {
-    if (direct && bj == 128) continue;
+    if (bj == 128 || (!direct && bj != 64)) continue;
     if (p.d % bj) continue;
     const int64_t wgs = tt * (p.d / bj) * p.n_inst;
     const int64_t rounds = (wgs + 255) / 256;

@@ -307,6 +307,7 @@ __device__ __forceinline__ void pipeline(int nk, F&& fetch, P&& put, C&& compute
 // L2).  Map it to a logical index so that each XCD receives one contiguous
 // block of logical indices: tiles that share operands then share an L2.
 constexpr int NXCD = 8;
+constexpr int NCU = 256;   // compute units (32 per XCD)
 __device__ __forceinline__ int xcd_remap(int b, int nwg) {
   const int per = nwg / NXCD, rem = nwg % NXCD;
   const int x = b % NXCD, s = b / NXCD;

@@ -109,10 +109,20 @@ def video_schedule(n_clean: int, chunk: int) -> Tuple[Tuple[int, ...], Tuple[int
     return tuple(b), tuple(flags)
 
 
-def _viewset_schedule():
+def video_schedule_noisy_first(n_clean: int, chunk: int) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
+    """[N1, C1, N2, C2, ..., N_n, C_n]: every clean chunk preceded by a noisy
+    one that reads the weights the clean chunk reads."""
+    flags = [APPLY, UPDATE | APPLY] * n_clean
+    b = [i * chunk for i in range(len(flags) + 1)]
+    return tuple(b), tuple(flags)
+
+
+def _viewset_schedule(prefill: bool = False):
+    """Posed-view set: update on the 48 x 64 x 64 = 196,608 input tokens, then
+    apply to 4,096 target tokens; with prefill, also apply to the inputs."""
     n_in = 48 * (512 // 8) * (512 // 8)   # 196,608 input tokens
     n_tgt = 4096
-    return (0, n_in, n_in + n_tgt), (UPDATE, APPLY)
+    return (0, n_in, n_in + n_tgt), ((UPDATE | APPLY) if prefill else UPDATE, APPLY)
 
 
 def _make_configs() -> Dict[int, Workload]:
@@ -131,6 +141,13 @@ def _make_configs() -> Dict[int, Workload]:
                     OPT_GD, DTYPE_BF16, False, 1, 2e-2)
     b, f = video_schedule(12, 4680)
     c[5] = Workload(5, "video_d128_bf16_muon", 40, 128, b[-1], b, f, APPLY_THEN_UPDATE,
+                    OPT_MUON, DTYPE_BF16, True, 3, 2e-2)
+    # schedule variants of the same layers
+    b, f = _viewset_schedule(prefill=True)
+    c[6] = Workload(6, "viewset_prefill_d128_bf16_gd", 6, 128, b[-1], b, f, UPDATE_THEN_APPLY,
+                    OPT_GD, DTYPE_BF16, False, 1, 2e-2)
+    b, f = video_schedule_noisy_first(12, 4680)
+    c[7] = Workload(7, "video_noisy_first_d128_bf16_muon", 40, 128, b[-1], b, f, APPLY_THEN_UPDATE,
                     OPT_MUON, DTYPE_BF16, True, 3, 2e-2)
     return c
 

@@ -118,11 +118,27 @@ def _small_video():
     return dataclasses.replace(c, n_inst=3, L=b[-1], bounds=b, flags=f)
 
 
+def _small_prefill():
+    c = W.CONFIGS[6]
+    b, f = (0, 4000, 4500), (W.UPDATE | W.APPLY, W.APPLY)
+    import dataclasses
+    return dataclasses.replace(c, n_inst=2, L=4500, bounds=b, flags=f)
+
+
+def _small_video_noisy_first():
+    c = W.CONFIGS[7]
+    import dataclasses
+    b, f = W.video_schedule_noisy_first(3, 700)
+    return dataclasses.replace(c, n_inst=3, L=b[-1], bounds=b, flags=f)
+
+
 SMALL[4] = _small_viewset()
 SMALL[5] = _small_video()
+SMALL[6] = _small_prefill()
+SMALL[7] = _small_video_noisy_first()
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7])
 def test_layer_reduced_size(lact, cid):
     wl = SMALL[cid]
     log(f"layer reduced cfg{cid}: n={wl.n_inst} D={wl.D} L={wl.L} chunks={wl.n_chunks}")

@@ -24,6 +24,13 @@ def test_schedules():
     assert c[5].n_chunks == 23 and c[5].L == 107640
     assert c[5].flags[:4] == (3, W.APPLY, 3, W.APPLY) and c[5].flags[-1] == 3
     assert sum(1 for f in c[5].flags if f & W.UPDATE) == 12
+    # schedule variants: view-set prefill also applies to the inputs; the
+    # noisy-first video schedule has 12 noisy + 12 clean chunks (112,320 tokens)
+    assert c[6].bounds == c[4].bounds and c[6].flags == (W.UPDATE | W.APPLY, W.APPLY)
+    assert c[6].order == W.UPDATE_THEN_APPLY
+    assert c[7].L == 24 * 4680 == 112320 and c[7].n_chunks == 24
+    assert c[7].flags[:4] == (W.APPLY, 3, W.APPLY, 3) and c[7].flags[-1] == 3
+    assert sum(1 for f in c[7].flags if f & W.UPDATE) == 12
     assert W.uniform_schedule(10, 4) == ((0, 4, 8, 10), (3, 3, 3))
 
 

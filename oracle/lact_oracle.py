@@ -60,6 +60,7 @@ UPDATE_THEN_APPLY = 1
 OPT_GD = 0
 OPT_MOMENTUM = 1
 OPT_MUON = 2
+OPT_MUON_MOMENTUM = 3
 
 NS_COEFFS = (3.4445, -4.7750, 2.0315)
 NS_EPS = 1e-7
@@ -171,6 +172,15 @@ def update_step(W, M, K, V, lr, beta, opt, renorm=True, ns_steps=5):
     elif opt == OPT_MUON:
         Wn = [w + newton_schulz5(u, ns_steps) for w, u in zip(W, U)]
         Mn = M
+    elif opt == OPT_MUON_MOMENTUM:
+        # momentum with per-token beta ([LaCT-GSYQ] §1.2) whose buffer is then
+        # orthogonalised ([LaCT-DPSHK] §2.2.1, eqs. 9-10) -- the two options
+        # combined by orthogonalising the momentum buffer (reading: the
+        # pages list the options separately; this composition reduces to
+        # Muon when beta = 0)
+        bm = float(np.mean(beta))
+        Mn = [momentum_step(m, u, bm) for m, u in zip(M, U)]
+        Wn = [w - newton_schulz5(m, ns_steps) for w, m in zip(W, Mn)]
     else:
         raise ValueError(f"unknown optimiser {opt}")
     if renorm:

@@ -34,6 +34,10 @@ MUTATIONS = {
                   "Wn = [w - newton_schulz5(u, ns_steps) for w, u in zip(W, U)]"),
     "apply_W1_for_W3": ("B = X @ W3.T\n    return", "B = X @ W1.T\n    return"),
     "apply_only_chunk_updates": ("if f & UPDATE:\n            bt", "if True:\n            bt"),
+    "muon_momentum_orthogonalises_U": ("Wn = [w - newton_schulz5(m, ns_steps) for w, m in zip(W, Mn)]",
+                                       "Wn = [w + newton_schulz5(u, ns_steps) for w, u in zip(W, U)]"),
+    "muon_momentum_plus": ("Wn = [w - newton_schulz5(m, ns_steps) for w, m in zip(W, Mn)]",
+                           "Wn = [w + newton_schulz5(m, ns_steps) for w, m in zip(W, Mn)]"),
 }
 
 

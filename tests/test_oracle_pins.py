@@ -391,3 +391,46 @@ def test_muon_step_is_ns_of_the_descent_direction():
         step = Wn[j] - W[j]
         assert np.max(np.abs(step - ref)) <= 1e-5 * np.max(np.abs(ref)), j
         assert np.sum(g * step) < 0
+
+
+def test_muon_momentum_with_zero_beta_is_muon():
+    """Momentum + Muon with beta = 0: the buffer is minus this chunk's
+    direction and the step equals Muon's, bitwise (NS5 is exactly odd)."""
+    rng = np.random.default_rng(31)
+    D, C = 7, 9
+    W = rand_state(D, 0.8, rng)
+    K, V, lr = rand_chunk(C, D, rng, lr_scale=0.3)
+    M0 = [rng.standard_normal((D, D)) for _ in range(3)]
+    for renorm in (True, False):
+        Wa, Ma = O.update_step(W, M0, K, V, lr, np.zeros(C), O.OPT_MUON_MOMENTUM, renorm=renorm)
+        Wb, _ = O.update_step(W, M0, K, V, lr, None, O.OPT_MUON, renorm=renorm)
+        U = O.chunk_grads(*W, K, V, lr)
+        for j in range(3):
+            assert np.array_equal(Wa[j], Wb[j]), (renorm, j)
+            assert np.array_equal(Ma[j], -U[j]), (renorm, j)
+
+
+def test_muon_momentum_orthogonalises_the_momentum_buffer():
+    """Two chunks, constant beta, no renorm: the buffer is the geometric sum
+    of finite-difference gradients and each step is the SVD closed form of
+    the quintic map of that buffer, subtracted from W."""
+    rng = np.random.default_rng(32)
+    D, C, b = 5, 6, 0.7
+    W0 = rand_state(D, 0.7, rng)
+    K1, V1, lr1 = rand_chunk(C, D, rng, lr_scale=0.5)
+    K2, V2, lr2 = rand_chunk(C, D, rng, lr_scale=0.5)
+    beta = np.full(C, b)
+    M0 = [np.zeros((D, D))] * 3
+    W1, M1 = O.update_step(W0, M0, K1, V1, lr1, beta, O.OPT_MUON_MOMENTUM, renorm=False)
+    W2, M2 = O.update_step(W1, M1, K2, V2, lr2, beta, O.OPT_MUON_MOMENTUM, renorm=False)
+    for j in range(3):
+        g1 = fd_grad(W0, K1, V1, lr1, j)
+        m1 = g1                                   # b * 0 + g1
+        w1 = W0[j] - ns_closed_form(m1)[0]
+        assert np.max(np.abs(M1[j] - m1)) <= 1e-6 * np.max(np.abs(m1)), j
+        assert np.max(np.abs(W1[j] - w1)) <= 1e-5 * np.max(np.abs(w1)), j
+        g2 = fd_grad(W1, K2, V2, lr2, j)
+        m2 = b * M1[j] + g2
+        w2 = W1[j] - ns_closed_form(m2)[0]
+        assert np.max(np.abs(M2[j] - m2)) <= 1e-6 * np.max(np.abs(m2)), j
+        assert np.max(np.abs(W2[j] - w2)) <= 1e-5 * np.max(np.abs(w2)), j

@@ -26,7 +26,10 @@ MUTATIONS = {
     "ns_coefficient": ("NS_COEFFS = (3.4445, -4.7750, 2.0315)", "NS_COEFFS = (3.4445, -4.7750, 2.0)"),
     "ns_product_order": ("X = a * X + B @ X", "X = a * X + X @ B"),
     "momentum_sign": ("return beta_mean * M - U", "return beta_mean * M + U"),
-    "momentum_last_beta": ("bm = float(np.mean(beta))", "bm = float(beta[-1])"),
+    "momentum_last_beta": ("bm = float(np.mean(beta))\n        Mn = [momentum_step(m, u, bm) for m, u in zip(M, U)]\n"
+                           "        Wn = [w - m for w, m in zip(W, Mn)]",
+                           "bm = float(beta[-1])\n        Mn = [momentum_step(m, u, bm) for m, u in zip(M, U)]\n"
+                           "        Wn = [w - m for w, m in zip(W, Mn)]"),
     "order_swapped": ("if (f & APPLY) and (order == APPLY_THEN_UPDATE or not (f & UPDATE)):",
                       "if (f & APPLY) and (order == UPDATE_THEN_APPLY or not (f & UPDATE)):"),
     "gd_sign": ("Wn = [w + u for w, u in zip(W, U)]", "Wn = [w - u for w, u in zip(W, U)]"),

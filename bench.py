@@ -52,7 +52,7 @@ def kernel_flops(wl, lact):
         lact.K_OUT: 2.0 * app * D * D * n,                  # Hq W2^T
         lact.K_DW: 6.0 * upd * D * D * n,                   # three contractions over tokens
         lact.K_OPT: 0.0,
-        lact.K_NS: (30.0 * D ** 3 * 3 * n * n_upd) if wl.opt == W.OPT_MUON else 0.0,
+        lact.K_NS: (30.0 * D ** 3 * 3 * n * n_upd) if wl.opt in (W.OPT_MUON, W.OPT_MUON_MOMENTUM) else 0.0,
         lact.K_SNAP: 0.0,
     }
 
@@ -154,7 +154,7 @@ def main():
         else torch.from_numpy(np.ascontiguousarray(x)).cuda())
     q, k, v, lr, beta = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.lr), dev(inp.beta)
     Ws = [dev(inp.W1), dev(inp.W2), dev(inp.W3)]
-    Ms = [torch.zeros_like(w) for w in Ws] if wl.opt == W.OPT_MOMENTUM else [None] * 3
+    Ms = [torch.zeros_like(w) for w in Ws] if wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM) else [None] * 3
     o = torch.zeros_like(q)
     p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes)
     bounds, flags = list(wl.bounds), list(wl.flags)
@@ -225,7 +225,7 @@ def main():
         "data": "synthetic (seeded generator; no dataset, random-init fast weights)",
         "config": {"workload": wl.name, "n_inst": wl.n_inst, "d": wl.D, "dh": wl.D, "seq_len": wl.L,
                    "max_chunk": wl.max_chunk, "n_chunks": wl.n_chunks,
-                   "opt": ["gd", "momentum", "muon"][wl.opt],
+                   "opt": ["gd", "momentum", "muon", "muon_momentum"][wl.opt],
                    "order": ["apply_then_update", "update_then_apply"][wl.order],
                    "rec_planes": wl.rec_planes, "global_batch": 1},
         "algorithmic_tflop_per_step": flops / 1e12,

@@ -29,6 +29,9 @@
  *     GD: W' = W + U.  MOMENTUM: M <- mean_chunk(beta) M - U, W' = W - M.
  *     MUON: W' = W + NS(U), NS = ns_iters quintic Newton-Schulz steps with
  *     (a, b, c) = (3.4445, -4.7750, 2.0315) on X0 = U / (||U||_F + 1e-7).
+ *     MUON_MOMENTUM: M <- mean_chunk(beta) M - U, W' = W - NS(M) (the two
+ *     options combined by orthogonalising the momentum buffer; with beta = 0
+ *     it is MUON).
  *   - Renormalisation (unless LACT_NO_RENORM): every row of each updated
  *     matrix (rows of the stored [rows x cols] arrays: an output unit's
  *     fan-in) is rescaled to the L2 norm it had before the update.
@@ -78,7 +81,12 @@ typedef enum {
 } lact_status;
 
 typedef enum { LACT_DTYPE_F32 = 0, LACT_DTYPE_BF16 = 1 } lact_dtype;
-typedef enum { LACT_OPT_GD = 0, LACT_OPT_MOMENTUM = 1, LACT_OPT_MUON = 2 } lact_opt;
+typedef enum {
+    LACT_OPT_GD = 0,
+    LACT_OPT_MOMENTUM = 1,
+    LACT_OPT_MUON = 2,
+    LACT_OPT_MUON_MOMENTUM = 3   /* Newton-Schulz of the momentum buffer */
+} lact_opt;
 typedef enum { LACT_APPLY_THEN_UPDATE = 0, LACT_UPDATE_THEN_APPLY = 1 } lact_order;
 
 /* per-chunk schedule flags */
@@ -117,8 +125,9 @@ size_t lact_workspace_size(const lact_problem* p, int64_t L, int64_t chunk, int3
  * epilogue, weight-gradient contractions over the chunk, optimiser, row
  * renormalisation) for Lc tokens per instance.  k, v are [n, seq_stride, D]
  * (the first Lc tokens of each instance are used), lr [n, seq_stride, 3],
- * beta [n, seq_stride] (MOMENTUM only, else may be NULL).  W1..W3 are read
- * and overwritten with the updated weights; M1..M3 likewise for MOMENTUM
+ * beta [n, seq_stride] (MOMENTUM and MUON_MOMENTUM, else may be NULL).  W1..W3
+ * are read and overwritten with the updated weights; M1..M3 likewise for
+ * MOMENTUM and MUON_MOMENTUM
  * (else may be NULL).  Lc == 0 is a no-op.
  */
 lact_status lact_chunk_update(const lact_problem* p, const void* k, const void* v,
@@ -148,7 +157,7 @@ lact_status lact_apply(const lact_problem* p, const void* q, int64_t Lq, int64_t
  * LACT_UPDATE_THEN_APPLY -- it is applied after its own update.  An
  * APPLY-only chunk reads the current weights; an UPDATE-only chunk writes no
  * output.  Rows of o outside APPLY chunks are left untouched.  The final
- * state is written back to W1..W3 (and M1..M3 for MOMENTUM).
+ * state is written back to W1..W3 (and M1..M3 for MOMENTUM, MUON_MOMENTUM).
  */
 lact_status lact_layer_forward(const lact_problem* p, const void* q, const void* k,
                                const void* v, const float* lr, const float* beta, int64_t L,

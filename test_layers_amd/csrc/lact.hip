@@ -129,6 +129,8 @@ Prof profile_of(const lact_problem& p) {
   int rp = p.rec_planes == 0 ? 1 : p.rec_planes;
   return rp == 1 ? PBF16 : rp == 2 ? PBF16X2 : PBF16X3;
 }
+bool uses_momentum(int opt) { return opt == LACT_OPT_MOMENTUM || opt == LACT_OPT_MUON_MOMENTUM; }
+bool uses_ns(int opt) { return opt == LACT_OPT_MUON || opt == LACT_OPT_MUON_MOMENTUM; }
 size_t io_size(const lact_problem& p) { return p.io_dtype == LACT_DTYPE_F32 ? 4 : 2; }
 size_t rec_size(Prof f) { return f == PBF16 ? 2 : 4; }   // update terms storage
 size_t app_size(Prof f) { return f == PF32 ? 4 : 2; }    // gated hidden of the queries
@@ -312,9 +314,9 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   w.h = take(n * (size_t)h_rows * D * app_size(f));
   const size_t mats = n * 3 * D * D * sizeof(float);
   w.part = take(plan.max_upd > 0 ? (size_t)S * mats : 0);
-  w.bpart = take(p.opt == LACT_OPT_MOMENTUM ? n * (size_t)w.max_tt * sizeof(float) : 0);
+  w.bpart = take(uses_momentum(p.opt) ? n * (size_t)w.max_tt * sizeof(float) : 0);
   w.snap = take(w.snap_slot * (size_t)w.nslots);
-  if (p.opt == LACT_OPT_MUON && plan.max_upd > 0) {
+  if (uses_ns(p.opt) && plan.max_upd > 0) {
     w.u = take(mats);
     w.am = take(mats);
     w.bm = take(mats);
@@ -335,8 +337,8 @@ lact_status validate_problem(const lact_problem* p) {
     return fail(LACT_ERR_UNSUPPORTED, "d = %d: need a multiple of 64 in [64, 1024]", p->d);
   if (p->io_dtype != LACT_DTYPE_F32 && p->io_dtype != LACT_DTYPE_BF16)
     return fail(LACT_ERR_INVALID_ARG, "io_dtype = %d", p->io_dtype);
-  if (p->opt < LACT_OPT_GD || p->opt > LACT_OPT_MUON) return fail(LACT_ERR_INVALID_ARG, "opt = %d", p->opt);
-  if (p->opt == LACT_OPT_MUON && (p->ns_iters < 1 || p->ns_iters > 16))
+  if (p->opt < LACT_OPT_GD || p->opt > LACT_OPT_MUON_MOMENTUM) return fail(LACT_ERR_INVALID_ARG, "opt = %d", p->opt);
+  if (uses_ns(p->opt) && (p->ns_iters < 1 || p->ns_iters > 16))
     return fail(LACT_ERR_INVALID_ARG, "ns_iters = %d: need 1..16", p->ns_iters);
   if (p->rec_planes < 0 || p->rec_planes > 3) return fail(LACT_ERR_INVALID_ARG, "rec_planes = %d", p->rec_planes);
   if (p->flags & ~LACT_NO_RENORM) return fail(LACT_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
@@ -542,7 +544,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
   using TAPP = typename PT::TAPP;
   const int n = p.n_inst, D = p.d;
   if (n == 0) return LACT_OK;
-  const bool part16 = PT::PREC == 1 && p.opt != LACT_OPT_MUON;
+  const bool part16 = PT::PREC == 1 && !uses_ns(p.opt);
   const int64_t DD = (int64_t)D * D;
   const int64_t x_bs = seq_stride * D;
   char* ws = P.ws;
@@ -571,7 +573,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     ua.x_bs = x_bs;
     ua.lr = P.lr;
     ua.lr_bs = seq_stride * 3;
-    ua.beta = p.opt == LACT_OPT_MOMENTUM ? P.beta : nullptr;
+    ua.beta = uses_momentum(p.opt) ? P.beta : nullptr;
     ua.beta_bs = seq_stride;
     ua.bpart = reinterpret_cast<float*>(ws + w.bpart);
     if (PT::UPD_FROM_SNAP) {
@@ -650,7 +652,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     oa.snap[1] = slot(nu + 1, 2);
     oa.snap[2] = slot(nu + 1, 1);
     oa.snapT2 = sizeof(TS) == 2 ? slot(nu + 1, 3) : nullptr;
-    if (p.opt != LACT_OPT_MUON) {
+    if (!uses_ns(p.opt)) {
       oa.src = ws + w.part;
       oa.src_ss = (int64_t)n * 3 * DD;
       oa.splits = S;
@@ -661,8 +663,20 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       {
         KernelTimer kt(LACT_K_NS, s);
         const int64_t rows = (int64_t)n * 3 * D;
+        // momentum + Muon: the Newton-Schulz input is the new momentum buffer
+        // M' = mean(beta) M - U, also written back to the state
+        RowsMomentum rm;
+        memset(&rm, 0, sizeof(rm));
+        if (p.opt == LACT_OPT_MUON_MOMENTUM) {
+          rm.M[0] = P.M1;
+          rm.M[1] = P.M3;
+          rm.M[2] = P.M2;
+          rm.bpart = reinterpret_cast<const float*>(ws + w.bpart);
+          rm.nbp = ua.tiles_t;
+          rm.inv_len = 1.0f / (float)C;
+        }
         LACT_LAUNCH(reduce_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(NT), s,
-                           reinterpret_cast<const float*>(ws + w.part), (int64_t)n * 3 * DD, S, U, rowsq, rows, D);
+                           reinterpret_cast<const float*>(ws + w.part), (int64_t)n * 3 * DD, S, U, rowsq, rows, D, rm);
         HIP_TRY(hipGetLastError());
       }
       float* Am = reinterpret_cast<float*>(ws + w.am);
@@ -905,7 +919,7 @@ lact_status lact_layer_forward(const lact_problem* p, const void* q, const void*
     NEED(k, 16);
     NEED(v, 16);
     NEED(lr, 4);
-    if (p->opt == LACT_OPT_MOMENTUM) {
+    if (uses_momentum(p->opt)) {
       NEED(beta, 4);
       NEED(M1, 16);
       NEED(M2, 16);
@@ -956,7 +970,7 @@ lact_status lact_chunk_update(const lact_problem* p, const void* k, const void* 
   NEED(k, 16);
   NEED(v, 16);
   NEED(lr, 4);
-  if (p->opt == LACT_OPT_MOMENTUM) {
+  if (uses_momentum(p->opt)) {
     NEED(beta, 4);
     NEED(M1, 16);
     NEED(M2, 16);

@@ -436,11 +436,33 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
 // =========================================================================
 // split-K reduction for the Muon path: U = sum_s P[s]; rowsq = per-row sum of
 // squares of U.  One wave per row of the stacked [n * 3D, D] matrix.
+// momentum + Muon: the buffer M' = mean(beta) M - U replaces U as the
+// Newton-Schulz input and is written back to the state (M[mat] in the order
+// of the stacked blocks U1 | U3 | U2; null M: plain Muon)
+struct RowsMomentum {
+  float* M[3];
+  const float* bpart;    // [n, nbp] beta partial sums
+  int nbp;
+  float inv_len;
+};
+
 __global__ __launch_bounds__(NT) void reduce_rows_kernel(const float* P, int64_t p_ss, int splits,
-                                                        float* U, float* rowsq, int64_t rows, int D) {
+                                                        float* U, float* rowsq, int64_t rows, int D,
+                                                        RowsMomentum rm) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (NT / WAVE) + (threadIdx.x >> 6);
   if (row >= rows) return;
+  const bool mom = rm.M[0] != nullptr;
+  const int64_t inst = row / (3 * (int64_t)D);
+  const int mat = (int)((row / D) % 3);
+  float bm = 0.f;
+  float* Mrow = nullptr;
+  if (mom) {
+    float sb = 0.f;
+    for (int i = lane; i < rm.nbp; i += WAVE) sb += rm.bpart[inst * rm.nbp + i];
+    bm = wave_sum(sb) * rm.inv_len;
+    Mrow = rm.M[mat] + (inst * D + row % D) * (int64_t)D;
+  }
   float ss = 0.f;
   for (int e4 = lane; e4 < D / 4; e4 += WAVE) {
     const float4* src = reinterpret_cast<const float4*>(P + row * D) + e4;
@@ -451,6 +473,11 @@ __global__ __launch_bounds__(NT) void reduce_rows_kernel(const float* P, int64_t
       u.y += x.y;
       u.z += x.z;
       u.w += x.w;
+    }
+    if (mom) {
+      const float4 m = reinterpret_cast<const float4*>(Mrow)[e4];
+      u = make_float4(bm * m.x - u.x, bm * m.y - u.y, bm * m.z - u.z, bm * m.w - u.w);
+      reinterpret_cast<float4*>(Mrow)[e4] = u;
     }
     reinterpret_cast<float4*>(U + row * D)[e4] = u;
     ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
@@ -474,7 +501,7 @@ struct OptArgs {
   float inv_len;         // 1 / chunk length
   int D;
   int rpw;               // rows per wave: 4 (D <= 256), 2 (D <= 512) or 1
-  int opt;               // 0 GD, 1 momentum, 2 Muon
+  int opt;               // 0 GD, 1 momentum, 2 Muon, 3 momentum + Muon
   int renorm;
   // snapshot of the new weights (bf16 or fp32, natural layout) and, for
   // bf16, the transposed W2 snapshot used by the next update's forward
@@ -579,6 +606,9 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
     if (a.opt == 1) {
       mm[i] = make_float4(bm * m[i].x - u[i].x, bm * m[i].y - u[i].y, bm * m[i].z - u[i].z, bm * m[i].w - u[i].w);
       xn[i] = make_float4(w[i].x - mm[i].x, w[i].y - mm[i].y, w[i].z - mm[i].z, w[i].w - mm[i].w);
+    } else if (a.opt == 3) {   // momentum + Muon: W - NS(M'), the buffer already advanced
+      mm[i] = z4;
+      xn[i] = make_float4(w[i].x - u[i].x, w[i].y - u[i].y, w[i].z - u[i].z, w[i].w - u[i].w);
     } else {
       mm[i] = z4;
       xn[i] = make_float4(w[i].x + u[i].x, w[i].y + u[i].y, w[i].z + u[i].z, w[i].w + u[i].w);

@@ -27,6 +27,7 @@ DTYPE_BF16 = 1
 OPT_GD = 0
 OPT_MOMENTUM = 1
 OPT_MUON = 2
+OPT_MUON_MOMENTUM = 3
 APPLY_THEN_UPDATE = 0
 UPDATE_THEN_APPLY = 1
 CHUNK_UPDATE = 1

@@ -45,6 +45,7 @@ UPDATE_THEN_APPLY = 1
 OPT_GD = 0
 OPT_MOMENTUM = 1
 OPT_MUON = 2
+OPT_MUON_MOMENTUM = 3   # Newton-Schulz of the momentum buffer
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -149,6 +150,10 @@ def _make_configs() -> Dict[int, Workload]:
     b, f = video_schedule_noisy_first(12, 4680)
     c[7] = Workload(7, "video_noisy_first_d128_bf16_muon", 40, 128, b[-1], b, f, APPLY_THEN_UPDATE,
                     OPT_MUON, DTYPE_BF16, True, 3, 2e-2)
+    # optimiser variant: the 3B-LM layer with momentum + Muon
+    b, f = uniform_schedule(32768, 4096)
+    c[8] = Workload(8, "lm3b_d512_bf16_muon_momentum", 6, 512, 32768, b, f, APPLY_THEN_UPDATE,
+                    OPT_MUON_MOMENTUM, DTYPE_BF16, True, 2, 2e-2)
     return c
 
 
@@ -207,7 +212,7 @@ def _draw_instance(wl: Workload, seed: int, inst: int):
     zlr = rng.standard_normal((L, 3))
     lr = np.logaddexp(0.0, zlr - 5.0)            # softplus
     beta = None
-    if wl.opt == OPT_MOMENTUM:
+    if wl.opt in (OPT_MOMENTUM, OPT_MUON_MOMENTUM):
         zb = rng.standard_normal(L)
         beta = 1.0 / (1.0 + np.exp(-(zb + 2.2)))
     s = 1.0 / np.sqrt(D)
@@ -263,5 +268,5 @@ def algorithmic_flops(wl: Workload) -> Dict[str, float]:
             app += b - a
     fu = 12.0 * D * D * upd * n
     fa = 6.0 * D * D * app * n
-    fns = (30.0 * D ** 3 * 3 * n_upd * n) if wl.opt == OPT_MUON else 0.0
+    fns = (30.0 * D ** 3 * 3 * n_upd * n) if wl.opt in (OPT_MUON, OPT_MUON_MOMENTUM) else 0.0
     return {"update": fu, "apply": fa, "ns": fns, "total": fu + fa + fns}

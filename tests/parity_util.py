@@ -35,7 +35,7 @@ def run_gpu(wl: W.Workload, inp: W.Inputs, torch, lact, rec_planes=None, order=N
     beta = to_dev(inp.beta, torch)
     Ws = [to_dev(inp.W1, torch).clone(), to_dev(inp.W2, torch).clone(), to_dev(inp.W3, torch).clone()]
     Ms = [None] * 3
-    if wl.opt == W.OPT_MOMENTUM:
+    if wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM):
         Ms = [torch.zeros_like(w) for w in Ws]
     o = torch.zeros_like(q) if o_init is None else o_init
     lact.layer_forward(q, k, v, lr, beta, *Ws, *Ms, o, order=wl.order if order is None else order,
@@ -59,7 +59,7 @@ def compare(wl: W.Workload, inp: W.Inputs, gpu, order=None, renorm=True, instanc
     """Oracle instance by instance; returns {tensor: max over instances of err}.
     If `fro` is a dict it receives the Frobenius ratios ||gpu - ref|| / ||ref||
     (max over instances) as well."""
-    keys = ["o", "W1", "W2", "W3"] + (["M1", "M2", "M3"] if wl.opt == W.OPT_MOMENTUM else [])
+    keys = ["o", "W1", "W2", "W3"] + (["M1", "M2", "M3"] if wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM) else [])
     errs = {k: 0.0 for k in keys}
     idx = range(wl.n_inst) if instances is None else instances
     for i in idx:

@@ -78,6 +78,8 @@ def test_null_problem():
     (dict(io_dtype=5), lact.ERR_INVALID_ARG),
     (dict(opt=9), lact.ERR_INVALID_ARG),
     (dict(opt=lact.OPT_MUON, ns_iters=0), lact.ERR_INVALID_ARG),
+    (dict(opt=lact.OPT_MUON_MOMENTUM, ns_iters=17), lact.ERR_INVALID_ARG),
+    (dict(opt=4), lact.ERR_INVALID_ARG),
     (dict(rec_planes=4), lact.ERR_INVALID_ARG),
     (dict(n_inst=-1), lact.ERR_INVALID_ARG),
 ])
@@ -116,6 +118,8 @@ def test_bad_schedule(args):
     (dict(W2=None), lact.OPT_GD),
     (dict(beta=None), lact.OPT_MOMENTUM),
     (dict(M3=None), lact.OPT_MOMENTUM),
+    (dict(beta=None), lact.OPT_MUON_MOMENTUM),
+    (dict(M1=None), lact.OPT_MUON_MOMENTUM),
     (dict(k=FAKE + 2), lact.OPT_GD),
     (dict(W1=FAKE + 4), lact.OPT_GD),
     (dict(ws=FAKE + 16), lact.OPT_GD),

@@ -65,7 +65,7 @@ def test_apply_respects_seq_stride_and_leaves_other_rows(lact):
 
 
 # ------------------------------------------------------------------ one chunk update
-@pytest.mark.parametrize("opt", [W.OPT_GD, W.OPT_MOMENTUM, W.OPT_MUON])
+@pytest.mark.parametrize("opt", [W.OPT_GD, W.OPT_MOMENTUM, W.OPT_MUON, W.OPT_MUON_MOMENTUM])
 @pytest.mark.parametrize("io,planes", [(W.DTYPE_F32, 3), (W.DTYPE_BF16, 1), (W.DTYPE_BF16, 2),
                                        (W.DTYPE_BF16, 3)])
 @pytest.mark.parametrize("D", [64, 128])
@@ -78,8 +78,9 @@ def test_chunk_update_matches_oracle(lact, opt, io, planes, D):
     M0 = [rng.standard_normal((n, D, D)).astype(np.float32) * 0.01 for _ in range(3)]
     k, v, lr = to_dev(inp.k, torch), to_dev(inp.v, torch), to_dev(inp.lr, torch)
     Ws = [to_dev(w, torch).clone() for w in (inp.W1, inp.W2, inp.W3)]
-    Ms = [to_dev(m, torch).clone() for m in M0] if opt == W.OPT_MOMENTUM else [None] * 3
-    lact.chunk_update(k, v, lr, to_dev(beta, torch) if opt == W.OPT_MOMENTUM else None,
+    mom = opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    Ms = [to_dev(m, torch).clone() for m in M0] if mom else [None] * 3
+    lact.chunk_update(k, v, lr, to_dev(beta, torch) if mom else None,
                       *Ws, *Ms, opt=opt, rec_planes=planes)
     torch.cuda.synchronize()
     errs = {}
@@ -89,7 +90,7 @@ def test_chunk_update_matches_oracle(lact, opt, io, planes, D):
                                O.f64(inp.lr[i]), O.f64(beta[i]), opt)
         for j, nm in enumerate(["W1", "W2", "W3"]):
             errs[nm] = max(errs.get(nm, 0), rel_err(from_dev(Ws[j], torch)[i], Wr[j]))
-            if opt == W.OPT_MOMENTUM:
+            if mom:
                 errs["M" + nm[1]] = max(errs.get("M" + nm[1], 0), rel_err(from_dev(Ms[j], torch)[i], Mr[j]))
     log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
     gate = _gate(io) if planes == 1 or io == W.DTYPE_F32 else 1e-3
@@ -136,9 +137,10 @@ SMALL[4] = _small_viewset()
 SMALL[5] = _small_video()
 SMALL[6] = _small_prefill()
 SMALL[7] = _small_video_noisy_first()
+SMALL[8] = W.CONFIGS[8].scaled(n_inst=2, L=2 * 1024 + 300, chunk=1024)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_layer_reduced_size(lact, cid):
     wl = SMALL[cid]
     log(f"layer reduced cfg{cid}: n={wl.n_inst} D={wl.D} L={wl.L} chunks={wl.n_chunks}")

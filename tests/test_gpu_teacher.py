@@ -32,7 +32,7 @@ def _f64(t):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cid", [2, 3, 5])
+@pytest.mark.parametrize("cid", [2, 3, 5, 8])
 def test_teacher_forced_chunks(lact, cid):
     wl = W.CONFIGS[cid]
     assert wl.order == W.APPLY_THEN_UPDATE
@@ -43,7 +43,7 @@ def test_teacher_forced_chunks(lact, cid):
     q, k, v, lr = to_dev(inp.q, torch), to_dev(inp.k, torch), to_dev(inp.v, torch), to_dev(inp.lr, torch)
     beta = to_dev(inp.beta, torch)
     Ws = [to_dev(inp.W1, torch).clone(), to_dev(inp.W2, torch).clone(), to_dev(inp.W3, torch).clone()]
-    mom = wl.opt == W.OPT_MOMENTUM
+    mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
     Ms = [torch.zeros_like(w) for w in Ws] if mom else [None] * 3
     o = torch.zeros_like(q)
     p = lact.problem(n, D, wl.io_dtype, wl.opt, wl.rec_planes)

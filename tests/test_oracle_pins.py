@@ -103,7 +103,7 @@ def make_seq(n_chunks, C, D, rng):
     return q, k, v, lr, beta, W, b
 
 
-@pytest.mark.parametrize("opt", [O.OPT_GD, O.OPT_MOMENTUM, O.OPT_MUON])
+@pytest.mark.parametrize("opt", [O.OPT_GD, O.OPT_MOMENTUM, O.OPT_MUON, O.OPT_MUON_MOMENTUM])
 def test_causality_apply_then_update(opt):
     rng = np.random.default_rng(7)
     n, C, D = 4, 6, 5
@@ -122,7 +122,7 @@ def test_causality_apply_then_update(opt):
         if name == "q":
             assert not np.array_equal(out["o"][sl], ref["o"][sl])
             assert np.array_equal(out["o"][b[c + 2]:], ref["o"][b[c + 2]:])
-        elif name in ("k", "v", "lr") or (name == "beta" and opt == O.OPT_MOMENTUM):
+        elif name in ("k", "v", "lr") or (name == "beta" and opt in (O.OPT_MOMENTUM, O.OPT_MUON_MOMENTUM)):
             assert np.array_equal(out["o"][sl], ref["o"][sl]), name
             assert not np.array_equal(out["o"][b[c + 2]:], ref["o"][b[c + 2]:]), name
 
@@ -192,7 +192,7 @@ def test_video_schedule_noisy_chunks_only_read():
 
 
 # ---------------------------------------------------------------- renorm
-@pytest.mark.parametrize("opt", [O.OPT_GD, O.OPT_MOMENTUM, O.OPT_MUON])
+@pytest.mark.parametrize("opt", [O.OPT_GD, O.OPT_MOMENTUM, O.OPT_MUON, O.OPT_MUON_MOMENTUM])
 def test_row_norms_invariant(opt):
     rng = np.random.default_rng(11)
     D, C = 7, 9
@@ -249,7 +249,7 @@ def test_ns5_singular_value_band():
 
 
 # ---------------------------------------------------------------- special cases
-@pytest.mark.parametrize("opt", [O.OPT_GD, O.OPT_MOMENTUM, O.OPT_MUON])
+@pytest.mark.parametrize("opt", [O.OPT_GD, O.OPT_MOMENTUM, O.OPT_MUON, O.OPT_MUON_MOMENTUM])
 @pytest.mark.parametrize("order", [O.APPLY_THEN_UPDATE, O.UPDATE_THEN_APPLY])
 def test_zero_lr_is_a_plain_swiglu_mlp(opt, order):
     rng = np.random.default_rng(5)
@@ -323,7 +323,7 @@ def test_momentum_uses_chunk_mean_of_beta():
 
 
 # ---------------------------------------------------------------- state carry
-@pytest.mark.parametrize("opt", [O.OPT_GD, O.OPT_MOMENTUM, O.OPT_MUON])
+@pytest.mark.parametrize("opt", [O.OPT_GD, O.OPT_MOMENTUM, O.OPT_MUON, O.OPT_MUON_MOMENTUM])
 def test_resume_equals_single_call(opt):
     rng = np.random.default_rng(13)
     n, C, D = 5, 4, 6

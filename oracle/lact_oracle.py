@@ -24,8 +24,10 @@ Sources (page title, then the labelled part of the page):
   [LaCT-GSYQ] "LaCT架构核心思想解析" (gsyq.cn):
       §1.2 -- three fast-weight matrices per layer; momentum with a per-token
       beta: M is scaled by the chunk mean of beta and the gradient is added,
-      then W <- L2norm(W - M); §2.1 -- lr is [b, l, 3 * nh] rearranged to
-      [(b nh), l, 3].
+      then W <- L2norm(W - M); q and k pass through silu and are divided by
+      their norm over d before use; §2.1 -- lr is [b, l, 3 * nh] rearranged
+      to [(b nh), l, 3]; the layer output is multiplied per head and token by
+      silu of a linear projection of the input (one scalar per token).
 
 Conventions (readings where the pages are silent; each is listed in the
 design notes):
@@ -188,16 +190,35 @@ def update_step(W, M, K, V, lr, beta, opt, renorm=True, ns_steps=5):
     return Wn, Mn
 
 
+# ------------------------------------------------------------ input / output scaling
+
+def qk_preprocess(x):
+    """[LaCT-GSYQ] §1.2: silu, then each token's vector divided by its L2
+    norm over d (no epsilon is printed; none is added)."""
+    s = silu(f64(x))
+    return s / np.sqrt(np.sum(s * s, axis=-1, keepdims=True))
+
+
+def output_scale(o, z):
+    """[LaCT-GSYQ] §2.1: per-token output scale silu(z) of a given
+    pre-activation z [L] (the projection itself is outside the layer)."""
+    return o * silu(f64(z))[:, None]
+
+
 # ------------------------------------------------------------ layer
 
 def forward_instance(q, k, v, lr, beta, W1, W2, W3, bounds: Sequence[int],
                      flags: Sequence[int], order: int, opt: int, renorm=True,
-                     M=None, ns_steps=5):
-    """One instance ([L, D] inputs) through the chunk schedule.
+                     M=None, ns_steps=5, qk_prep=False, oz=None):
+    """One instance ([L, D] inputs) through the chunk schedule.  qk_prep: q
+    and k are raw and pre-processed first; oz: per-token output-scale
+    pre-activation [L] (or None).
 
     Returns dict(o [L, D] float64 with zeros on rows of non-APPLY chunks,
     o_mask [L] bool, W1, W2, W3, M1, M2, M3 (final state))."""
     q, k, v, lr = f64(q), f64(k), f64(v), f64(lr)
+    if qk_prep:
+        q, k = qk_preprocess(q), qk_preprocess(k)
     beta = None if beta is None else f64(beta)
     W = [f64(W1), f64(W2), f64(W3)]
     if M is None:
@@ -219,6 +240,8 @@ def forward_instance(q, k, v, lr, beta, W1, W2, W3, bounds: Sequence[int],
         if (f & APPLY) and order == UPDATE_THEN_APPLY and (f & UPDATE):
             o[a:b] = apply(W[0], W[1], W[2], q[a:b])
             mask[a:b] = True
+    if oz is not None:
+        o = output_scale(o, oz)
     return {"o": o, "o_mask": mask, "W1": W[0], "W2": W[1], "W3": W[2],
             "M1": M[0], "M2": M[1], "M3": M[2]}
 

@@ -63,9 +63,11 @@ class Workload:
     order: int
     opt: int
     io_dtype: int
-    qk_prep: bool         # silu + L2 normalisation of q, k
+    qk_prep: bool         # silu + L2 normalisation of q, k (in the generator)
     rec_planes: int       # bf16 planes used for the state recurrence on the GPU
     tol: float            # parity gate, max-abs error relative to max |ref|
+    layer_qk_prep: bool = False   # q, k handed over raw; the layer pre-processes them
+    out_scale: bool = False       # per-token output-scale pre-activation oz [n, L]
 
     @property
     def n_chunks(self) -> int:
@@ -150,6 +152,11 @@ def _make_configs() -> Dict[int, Workload]:
     b, f = video_schedule_noisy_first(12, 4680)
     c[7] = Workload(7, "video_noisy_first_d128_bf16_muon", 40, 128, b[-1], b, f, APPLY_THEN_UPDATE,
                     OPT_MUON, DTYPE_BF16, True, 3, 2e-2)
+    # raw q, k pre-processed by the layer, and the per-token output scale:
+    # the 760M-LM layer with its input/output scaling inside the layer
+    b, f = uniform_schedule(32768, 2048)
+    c[9] = Workload(9, "lm760m_d384_bf16_momentum_raw_qk_scaled", 4, 384, 32768, b, f, APPLY_THEN_UPDATE,
+                    OPT_MOMENTUM, DTYPE_BF16, False, 1, 2e-2, layer_qk_prep=True, out_scale=True)
     # optimiser variant: the 3B-LM layer with momentum + Muon
     b, f = uniform_schedule(32768, 4096)
     c[8] = Workload(8, "lm3b_d512_bf16_muon_momentum", 6, 512, 32768, b, f, APPLY_THEN_UPDATE,
@@ -192,6 +199,7 @@ class Inputs:
     W1: np.ndarray     # [n, D, D] float32   (dh x d)
     W2: np.ndarray     # [n, D, D] float32   (d x dh)
     W3: np.ndarray     # [n, D, D] float32   (dh x d)
+    oz: Optional[np.ndarray] = None   # [n, L] float32 output-scale pre-activation
 
 
 def _qk_prep(x: np.ndarray) -> np.ndarray:
@@ -219,6 +227,8 @@ def _draw_instance(wl: Workload, seed: int, inst: int):
     W1 = rng.standard_normal((D, D)) * s
     W2 = rng.standard_normal((D, D)) * s
     W3 = rng.standard_normal((D, D)) * s
+    # output-scale pre-activation (drawn last: earlier draws are unchanged)
+    oz = rng.standard_normal(L) if wl.out_scale else None
 
     def io(x):
         x32 = x.astype(np.float32)
@@ -226,7 +236,8 @@ def _draw_instance(wl: Workload, seed: int, inst: int):
 
     return (io(q), io(k), io(v), lr.astype(np.float32),
             None if beta is None else beta.astype(np.float32),
-            W1.astype(np.float32), W2.astype(np.float32), W3.astype(np.float32))
+            W1.astype(np.float32), W2.astype(np.float32), W3.astype(np.float32),
+            None if oz is None else oz.astype(np.float32))
 
 
 def generate(wl: Workload, seed: int = 0, threads: int = 8) -> Inputs:
@@ -236,14 +247,15 @@ def generate(wl: Workload, seed: int = 0, threads: int = 8) -> Inputs:
         parts = list(ex.map(lambda i: _draw_instance(wl, seed, i), range(wl.n_inst)))
     st = lambda j: np.stack([p[j] for p in parts])
     beta = st(4) if parts[0][4] is not None else None
-    return Inputs(st(0), st(1), st(2), st(3), beta, st(5), st(6), st(7))
+    oz = st(8) if parts[0][8] is not None else None
+    return Inputs(st(0), st(1), st(2), st(3), beta, st(5), st(6), st(7), oz)
 
 
 def generate_instance(wl: Workload, inst: int, seed: int = 0) -> Inputs:
     """One instance (n = 1 arrays), identical to row `inst` of generate()."""
     p = _draw_instance(wl, seed, inst)
     e = lambda a: None if a is None else a[None]
-    return Inputs(e(p[0]), e(p[1]), e(p[2]), e(p[3]), e(p[4]), e(p[5]), e(p[6]), e(p[7]))
+    return Inputs(e(p[0]), e(p[1]), e(p[2]), e(p[3]), e(p[4]), e(p[5]), e(p[6]), e(p[7]), e(p[8]))
 
 
 # ---------------------------------------------------------------- work counts

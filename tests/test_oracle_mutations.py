@@ -39,6 +39,8 @@ MUTATIONS = {
     "apply_only_chunk_updates": ("if f & UPDATE:\n            bt", "if True:\n            bt"),
     "muon_momentum_orthogonalises_U": ("Wn = [w - newton_schulz5(m, ns_steps) for w, m in zip(W, Mn)]",
                                        "Wn = [w + newton_schulz5(u, ns_steps) for w, u in zip(W, U)]"),
+    "qk_prep_no_norm": ("return s / np.sqrt(np.sum(s * s, axis=-1, keepdims=True))", "return s"),
+    "output_scale_sigmoid": ("return o * silu(f64(z))[:, None]", "return o * sigmoid(f64(z))[:, None]"),
     "muon_momentum_plus": ("Wn = [w - newton_schulz5(m, ns_steps) for w, m in zip(W, Mn)]",
                            "Wn = [w + newton_schulz5(m, ns_steps) for w, m in zip(W, Mn)]"),
 }

@@ -434,3 +434,59 @@ def test_muon_momentum_orthogonalises_the_momentum_buffer():
         w2 = W1[j] - ns_closed_form(m2)[0]
         assert np.max(np.abs(M2[j] - m2)) <= 1e-6 * np.max(np.abs(m2)), j
         assert np.max(np.abs(W2[j] - w2)) <= 1e-5 * np.max(np.abs(w2)), j
+
+
+# ---------------------------------------------------------------- q/k pre-processing, output scale
+def test_qk_preprocess_is_unit_norm_along_silu():
+    """Each pre-processed token vector has unit norm and points along the
+    element-wise silu of the raw vector (silu checked against the library
+    logistic function)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(41)
+    for scale in (0.1, 1.0, 8.0):
+        x = rng.standard_normal((17, 9)) * scale
+        y = O.qk_preprocess(x)
+        assert np.max(np.abs(np.linalg.norm(y, axis=1) - 1.0)) <= 1e-14
+        s = x * expit(x)
+        ratio = s / y
+        assert np.max(np.abs(ratio / ratio[:, :1] - 1.0)) <= 1e-12
+        assert np.all(ratio > 0)
+    # silu(0) = 0 and silu(x) -> x for large x
+    y = O.qk_preprocess(np.array([[0.0, 40.0, 30.0]]))
+    assert y[0, 0] == 0.0
+    assert np.allclose(y[0, 1:], np.array([40.0, 30.0]) / 50.0, rtol=1e-12, atol=0)
+
+
+def test_layer_on_raw_qk_equals_layer_on_preprocessed_inputs():
+    """The layer with in-layer q/k pre-processing equals the layer fed the
+    generator's independently pre-processed q, k (fp64, no rounding)."""
+    from test_layers_amd import workloads as Wk
+    rng = np.random.default_rng(42)
+    n, C, D = 3, 5, 6
+    q, k, v, lr, beta, W, b = make_seq(n, C, D, rng)
+    fl = [3] * n
+    raw = O.forward_instance(q, k, v, lr, beta, *W, b, fl, 0, O.OPT_MOMENTUM, qk_prep=True)
+    pre = O.forward_instance(Wk._qk_prep(q), Wk._qk_prep(k), v, lr, beta, *W, b, fl, 0, O.OPT_MOMENTUM)
+    for key in ("o", "W1", "W2", "W3", "M1", "M2", "M3"):
+        assert np.max(np.abs(raw[key] - pre[key])) <= 1e-12 * max(1.0, np.max(np.abs(pre[key]))), key
+
+
+def test_output_scale_special_values():
+    """silu(0) = 0 zeroes every row; a pre-activation of 40 (logistic rounds
+    to exactly 1 in fp64) scales by exactly 40; it touches no state."""
+    rng = np.random.default_rng(43)
+    n, C, D = 3, 4, 5
+    q, k, v, lr, beta, W, b = make_seq(n, C, D, rng)
+    fl = [3] * n
+    base = O.forward_instance(q, k, v, lr, beta, *W, b, fl, 0, O.OPT_GD)
+    z0 = O.forward_instance(q, k, v, lr, beta, *W, b, fl, 0, O.OPT_GD, oz=np.zeros(n * C))
+    z40 = O.forward_instance(q, k, v, lr, beta, *W, b, fl, 0, O.OPT_GD, oz=np.full(n * C, 40.0))
+    zm = rng.standard_normal(n * C)
+    zr = O.forward_instance(q, k, v, lr, beta, *W, b, fl, 0, O.OPT_GD, oz=zm)
+    assert np.all(z0["o"] == 0.0)
+    assert np.array_equal(z40["o"], 40.0 * base["o"])
+    for t in range(n * C):   # one scalar per token
+        r = zr["o"][t] / base["o"][t]
+        assert np.max(np.abs(r - r[0])) <= 1e-12 * abs(r[0])
+    for key in ("W1", "W2", "W3"):
+        assert np.array_equal(zr[key], base[key])

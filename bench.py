@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default: the 760M LM layer)")
+    ap.add_argument("--config", type=int, default=2, help="workload id 1..9 (default: the 760M LM layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work to sample")
     ap.add_argument("--copy-calib", action="store_true",
@@ -54,6 +54,7 @@ def kernel_flops(wl, lact):
         lact.K_OPT: 0.0,
         lact.K_NS: (30.0 * D ** 3 * 3 * n * n_upd) if wl.opt in (W.OPT_MUON, W.OPT_MUON_MOMENTUM) else 0.0,
         lact.K_SNAP: 0.0,
+        lact.K_PREP: 0.0,
     }
 
 
@@ -83,7 +84,8 @@ def cpu_baseline(wl, inp, budget):
         i = done % wl.n_inst
         O.forward_instance(inp.q[i], inp.k[i], inp.v[i], inp.lr[i],
                            None if inp.beta is None else inp.beta[i],
-                           inp.W1[i], inp.W2[i], inp.W3[i], wl.bounds, wl.flags, wl.order, wl.opt)
+                           inp.W1[i], inp.W2[i], inp.W3[i], wl.bounds, wl.flags, wl.order, wl.opt,
+                           qk_prep=wl.layer_qk_prep, oz=inp.oz[i] if wl.out_scale else None)
         done += 1
     dt = time.perf_counter() - t0
     tokens = wl.tokens * done / wl.n_inst
@@ -153,10 +155,11 @@ def main():
         torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() if x.dtype == np.uint16
         else torch.from_numpy(np.ascontiguousarray(x)).cuda())
     q, k, v, lr, beta = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.lr), dev(inp.beta)
+    oz = dev(inp.oz) if wl.out_scale else None
     Ws = [dev(inp.W1), dev(inp.W2), dev(inp.W3)]
     Ms = [torch.zeros_like(w) for w in Ws] if wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM) else [None] * 3
     o = torch.zeros_like(q)
-    p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes)
+    p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes, qk_prep=wl.layer_qk_prep)
     bounds, flags = list(wl.bounds), list(wl.flags)
     ws = torch.empty(lact.workspace_size(p, wl.L, 0, wl.order, bounds, flags), dtype=torch.uint8,
                      device="cuda")
@@ -164,8 +167,8 @@ def main():
 
     def step():
         lact.layer_forward(q, k, v, lr, beta, *Ws, *Ms, o, order=wl.order, opt=wl.opt,
-                           bounds=bounds, flags=flags, rec_planes=wl.rec_planes, workspace=ws,
-                           stream=stream)
+                           bounds=bounds, flags=flags, rec_planes=wl.rec_planes,
+                           qk_prep=wl.layer_qk_prep, oz=oz, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -227,7 +230,8 @@ def main():
                    "max_chunk": wl.max_chunk, "n_chunks": wl.n_chunks,
                    "opt": ["gd", "momentum", "muon", "muon_momentum"][wl.opt],
                    "order": ["apply_then_update", "update_then_apply"][wl.order],
-                   "rec_planes": wl.rec_planes, "global_batch": 1},
+                   "rec_planes": wl.rec_planes, "layer_qk_prep": wl.layer_qk_prep,
+                   "output_scale": wl.out_scale, "global_batch": 1},
         "algorithmic_tflop_per_step": flops / 1e12,
         "layer_frac_bf16_peak": flops / (ms_per_step * 1e-3) / PEAK_BF16,
         "roofline": roof,

@@ -20,8 +20,9 @@
  *       update-then-apply for posed image sets, video updates only on clean
  *       chunks).
  *   "LaCT架构核心思想解析" (gsyq.cn) §1.2 (three fast-weight matrices,
- *       momentum with per-token beta, W <- L2norm(W - M)) and §2.1
- *       (lr laid out as [(b nh), l, 3]).
+ *       momentum with per-token beta, W <- L2norm(W - M), silu and L2
+ *       normalisation of q and k) and §2.1 (lr laid out as [(b nh), l, 3];
+ *       the layer output scaled per token by silu of a projection).
  *
  * Conventions fixed by this library where the pages leave a choice:
  *   - lr[..., j-1] scales the gradient of W_j (j = 1, 2, 3).
@@ -95,6 +96,12 @@ typedef enum { LACT_APPLY_THEN_UPDATE = 0, LACT_UPDATE_THEN_APPLY = 1 } lact_ord
 
 /* lact_problem.flags */
 #define LACT_NO_RENORM 1u
+/* q and k arrive raw: before use, every token's q and k vector x becomes
+ * silu(x) / ||silu(x)||_2 over its D features ("LaCT架构核心思想解析" §1.2;
+ * no epsilon, so a token whose silu is identically zero gives non-finite
+ * values).  The caller's q and k are not modified; the pre-processed copies
+ * live in the workspace. */
+#define LACT_QK_PREP 2u
 
 typedef struct {
     int32_t n_inst;     /* B * nh independent instances (>= 0) */
@@ -108,7 +115,7 @@ typedef struct {
                            1 = bf16, 2 = bf16x2, 3 = bf16x3 (fp32-grade);
                            0 = default (3 for F32 io, else 1).  F32 io always
                            uses 3 planes for every product. */
-    uint32_t flags;     /* LACT_NO_RENORM */
+    uint32_t flags;     /* LACT_NO_RENORM | LACT_QK_PREP */
 } lact_problem;
 
 /*
@@ -166,6 +173,23 @@ lact_status lact_layer_forward(const lact_problem* p, const void* q, const void*
                                float* W3, float* M1, float* M2, float* M3, void* o, void* ws,
                                size_t ws_bytes, void* stream);
 
+/*
+ * lact_layer_forward followed by the per-token output scale of
+ * "LaCT架构核心思想解析" §2.1: every written row t of o is multiplied by
+ * silu(oz[t]), where oz [n, L] float32 (device) holds the pre-activation of
+ * that scale (the linear projection producing it is the caller's).  oz may
+ * be NULL only when no chunk is APPLY; all other arguments, the workspace
+ * size and the error behaviour are those of lact_layer_forward.  The scale
+ * is applied inside the output product's epilogue (no extra pass over o).
+ */
+lact_status lact_layer_forward_scaled(const lact_problem* p, const void* q, const void* k,
+                                      const void* v, const float* lr, const float* beta,
+                                      const float* oz, int64_t L, int64_t chunk, int32_t order,
+                                      const int64_t* bounds, const uint8_t* flags,
+                                      int32_t n_chunks, float* W1, float* W2, float* W3,
+                                      float* M1, float* M2, float* M3, void* o, void* ws,
+                                      size_t ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* lact_status_str(lact_status s);
 
@@ -186,7 +210,8 @@ const char* lact_last_error(void);
 #define LACT_K_OPT 4       /* optimiser step + row renormalisation + weight snapshot */
 #define LACT_K_NS 5        /* Newton-Schulz products and reductions */
 #define LACT_K_SNAP 6      /* snapshot of the caller's weights at call start */
-#define LACT_K_COUNT 7
+#define LACT_K_PREP 7      /* q / k pre-processing (LACT_QK_PREP) */
+#define LACT_K_COUNT 8
 lact_status lact_timing_enable(int32_t kclass, int32_t on);
 lact_status lact_timing_read(int32_t kclass, double* total_ms, int64_t* launches);
 

@@ -270,6 +270,8 @@ int upd_bj(const lact_problem& p, int64_t C) {
 // --------------------------------------------------------------- workspace layout
 struct Ws {
   size_t e = 0, h = 0, part = 0, bpart = 0, snap = 0, u = 0, am = 0, bm = 0, xa = 0, xb = 0, rowsq = 0, total = 0;
+  size_t qp = 0, kp = 0;  // pre-processed q / k ([n, prep_rows, D], LACT_QK_PREP)
+  int64_t prep_rows = 0;
   size_t snap_slot = 0;   // bytes per snapshot slot (W1, W2, W3, W2^T)
   int S = 1;
   int nslots = 1;
@@ -293,9 +295,10 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   // the token split count is not monotone in the chunk length (rounding of
   // the split size), so size the partials for the largest count of any step
   int S = 1, nupd = 0;
-  int64_t h_rows = 0;
+  int64_t h_rows = 0, rows = 0;
   for (const Step& st : plan.steps) {
     h_rows += st.app_len;
+    rows = std::max(rows, std::max(st.app_t0 + st.app_len, st.upd_t0 + st.upd_len));
     if (st.upd_len == 0) continue;
     ++nupd;
     int s_ = 1;
@@ -324,6 +327,12 @@ Ws layout(const lact_problem& p, const Plan& plan) {
     w.xb = take(mats);
     w.rowsq = take(n * 3 * D * sizeof(float));
   }
+  if (p.flags & LACT_QK_PREP) {
+    const size_t el = f == PF32 ? 4 : 2;
+    w.prep_rows = rows;
+    w.qp = take(plan.max_app > 0 ? n * (size_t)rows * D * el : 0);
+    w.kp = take(plan.max_upd > 0 ? n * (size_t)rows * D * el : 0);
+  }
   w.total = off;
   return w;
 }
@@ -341,7 +350,7 @@ lact_status validate_problem(const lact_problem* p) {
   if (uses_ns(p->opt) && (p->ns_iters < 1 || p->ns_iters > 16))
     return fail(LACT_ERR_INVALID_ARG, "ns_iters = %d: need 1..16", p->ns_iters);
   if (p->rec_planes < 0 || p->rec_planes > 3) return fail(LACT_ERR_INVALID_ARG, "rec_planes = %d", p->rec_planes);
-  if (p->flags & ~LACT_NO_RENORM) return fail(LACT_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
+  if (p->flags & ~(LACT_NO_RENORM | LACT_QK_PREP)) return fail(LACT_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   return LACT_OK;
 }
 
@@ -397,6 +406,7 @@ struct Ptrs {
   float* M2 = nullptr;
   float* M3 = nullptr;
   void* o = nullptr;
+  const float* oz = nullptr;   // per-token output-scale pre-activation [n, seq]
   char* ws = nullptr;
 };
 
@@ -552,6 +562,41 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
   // snapshot slot k holds the weights after k updates: W1, W2, W3, W2^T
   auto slot = [&](int k, int m) -> void* { return ws + w.snap + (size_t)k * w.snap_slot + (size_t)m * snap_mat; };
 
+  // raw q / k: pre-processed copies, packed per instance, replace them
+  const void* qx = P.q;
+  const void* kx = P.k;
+  int64_t q_bs = x_bs, k_bs = x_bs;
+  if (p.flags & LACT_QK_PREP) {
+    QkPrepArgs pa;
+    memset(&pa, 0, sizeof(pa));
+    int nm = 0;
+    if (plan.max_app > 0) {
+      pa.src[nm] = P.q;
+      pa.dst[nm++] = ws + w.qp;
+      qx = ws + w.qp;
+      q_bs = w.prep_rows * D;
+    }
+    if (plan.max_upd > 0) {
+      pa.src[nm] = P.k;
+      pa.dst[nm++] = ws + w.kp;
+      kx = ws + w.kp;
+      k_bs = w.prep_rows * D;
+    }
+    pa.src_bs = x_bs;
+    pa.rows = w.prep_rows;
+    const int64_t nblk = (w.prep_rows + QP_ROWS - 1) / QP_ROWS;
+    const int64_t blocks = (int64_t)nm * n * nblk;
+    pa.nblk = (int)std::min<int64_t>(nblk, 0x7fffffff);
+    pa.n = n;
+    pa.D = D;
+    if (blocks > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+    if (blocks > 0) {
+      KernelTimer kt(LACT_K_PREP, s);
+      LACT_LAUNCH(qk_prep_kernel<TIO>, dim3((unsigned)blocks), dim3(NT), s, pa);
+      HIP_TRY(hipGetLastError());
+    }
+  }
+
   {
     const int64_t n4 = (int64_t)n * DD / 4;
     KernelTimer kt(LACT_K_SNAP, s);
@@ -568,9 +613,10 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     // forward products on k, v and the SwiGLU backward terms
     UpdFwdArgs ua;
     memset(&ua, 0, sizeof(ua));
-    ua.k = P.k;
+    ua.k = kx;
     ua.v = P.v;
     ua.x_bs = x_bs;
+    ua.k_bs = k_bs;
     ua.lr = P.lr;
     ua.lr_bs = seq_stride * 3;
     ua.beta = uses_momentum(p.opt) ? P.beta : nullptr;
@@ -611,12 +657,13 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       g.g[0].A = ws + w.e;         // (m, t) = E[m, t]: rows U1 | U3 | U2^T terms
       g.lda = ua.ldE;
       g.a_bs = 3 * D * ua.ldE;
-      g.g[0].B = static_cast<const char*>(P.k) + (size_t)st.upd_t0 * D * io_size(p);
+      g.g[0].B = static_cast<const char*>(kx) + (size_t)st.upd_t0 * D * io_size(p);
       g.B2 = static_cast<const char*>(P.v) + (size_t)st.upd_t0 * D * io_size(p);
       g.m_switch = 2 * D;
       g.trans_from = 2 * D;        // the U2 block is stored as U2 (not U2^T)
       g.ldb = D;
-      g.b_bs = x_bs;
+      g.b_bs = k_bs;
+      g.b2_bs = x_bs;
       g.g[0].C = ws + w.part;
       g.ldc = D;
       g.c_bs = 3 * DD;
@@ -782,14 +829,18 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       if (st.upd_len > 0) ++u;
     }
   }
-  const int abj = D % 128 == 0 ? 128 : 64;
+  // the fp32 register-path apply tile spills at 128 hidden columns
+  const int abj = (D % 128 == 0 && profile_of(p) != PF32) ? 128 : 64;
   for (size_t g0 = 0; g0 < groups.size(); g0 += MAXG) {
     const int ng = (int)std::min<size_t>(MAXG, groups.size() - g0);
     AppFwdArgs aa;
     memset(&aa, 0, sizeof(aa));
     aa.ngroups = ng;
-    aa.q = P.q;
+    aa.q = qx;
+    aa.q_bs = q_bs;
     aa.x_bs = x_bs;
+    aa.oz = P.oz;
+    aa.oz_bs = seq_stride;
     aa.H = ws + w.h;
     aa.h_bs = w.h_rows * D;
     aa.D = D;
@@ -834,6 +885,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
         if (slot(k, 0) == ag.W1) u = k;
       g.g[i].B = slot(u, 1);
       g.g[i].C = static_cast<char*>(P.o) + (size_t)ag.t0 * D * io_size(p);
+      g.g[i].rs = P.oz ? P.oz + ag.t0 : nullptr;
       g.g[i].M = (int)ag.len;
       wgs128 += ((ag.len + 127) / 128) * std::max(1, D / 128) * n;
     }
@@ -843,6 +895,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     g.b_bs = DD;
     g.ldc = D;
     g.c_bs = x_bs;
+    g.rs_bs = seq_stride;
     g.N = D;
     g.K = g.kps = D;
     g.batch = n;
@@ -893,10 +946,14 @@ size_t lact_workspace_size(const lact_problem* p, int64_t L, int64_t chunk, int3
   return std::max<size_t>(layout(*p, plan).total, 256);
 }
 
-lact_status lact_layer_forward(const lact_problem* p, const void* q, const void* k, const void* v, const float* lr,
-                               const float* beta, int64_t L, int64_t chunk, int32_t order, const int64_t* bounds,
-                               const uint8_t* flags, int32_t n_chunks, float* W1, float* W2, float* W3, float* M1,
-                               float* M2, float* M3, void* o, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+lact_status layer_forward_impl(const lact_problem* p, const void* q, const void* k, const void* v, const float* lr,
+                               const float* beta, const float* oz, bool scaled, int64_t L, int64_t chunk,
+                               int32_t order, const int64_t* bounds, const uint8_t* flags, int32_t n_chunks,
+                               float* W1, float* W2, float* W3, float* M1, float* M2, float* M3, void* o, void* ws,
+                               size_t ws_bytes, void* stream) {
   g_err.clear();
   lact_status r = validate_problem(p);
   if (r) return r;
@@ -914,6 +971,7 @@ lact_status lact_layer_forward(const lact_problem* p, const void* q, const void*
   if (any_app) {
     NEED(q, 16);
     NEED(o, 16);
+    if (scaled) NEED(oz, 4);
   }
   if (any_upd) {
     NEED(k, 16);
@@ -945,8 +1003,29 @@ lact_status lact_layer_forward(const lact_problem* p, const void* q, const void*
   P.M2 = M2;
   P.M3 = M3;
   P.o = o;
+  P.oz = any_app ? oz : nullptr;
   P.ws = static_cast<char*>(ws);
   return dispatch(*p, P, L, plan, w, static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+extern "C" {
+
+lact_status lact_layer_forward(const lact_problem* p, const void* q, const void* k, const void* v, const float* lr,
+                               const float* beta, int64_t L, int64_t chunk, int32_t order, const int64_t* bounds,
+                               const uint8_t* flags, int32_t n_chunks, float* W1, float* W2, float* W3, float* M1,
+                               float* M2, float* M3, void* o, void* ws, size_t ws_bytes, void* stream) {
+  return layer_forward_impl(p, q, k, v, lr, beta, nullptr, false, L, chunk, order, bounds, flags, n_chunks, W1, W2,
+                            W3, M1, M2, M3, o, ws, ws_bytes, stream);
+}
+
+lact_status lact_layer_forward_scaled(const lact_problem* p, const void* q, const void* k, const void* v,
+                                      const float* lr, const float* beta, const float* oz, int64_t L, int64_t chunk,
+                                      int32_t order, const int64_t* bounds, const uint8_t* flags, int32_t n_chunks,
+                                      float* W1, float* W2, float* W3, float* M1, float* M2, float* M3, void* o,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  return layer_forward_impl(p, q, k, v, lr, beta, oz, true, L, chunk, order, bounds, flags, n_chunks, W1, W2, W3, M1,
+                            M2, M3, o, ws, ws_bytes, stream);
 }
 
 lact_status lact_chunk_update(const lact_problem* p, const void* k, const void* v, const float* lr, const float* beta,

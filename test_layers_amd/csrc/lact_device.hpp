@@ -62,6 +62,37 @@ __device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
 __device__ __forceinline__ void store4(bf16_t* p, const float (&v)[4]) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  v[0] = x.x;
+  v[1] = x.y;
+  v[2] = x.z;
+  v[3] = x.w;
+}
+__device__ __forceinline__ void load4(const bf16_t* p, float (&v)[4]) {
+  const uint2 x = *reinterpret_cast<const uint2*>(p);
+  v[0] = bf2f(x.x & 0xffffu);
+  v[1] = bf2f(x.x >> 16);
+  v[2] = bf2f(x.y & 0xffffu);
+  v[3] = bf2f(x.y >> 16);
+}
+
+// one 16-byte chunk of a row as floats (4 fp32 or 8 bf16 values)
+__device__ __forceinline__ void load_chunk(const float* p, float (&v)[4]) { load4(p, v); }
+__device__ __forceinline__ void load_chunk(const bf16_t* p, float (&v)[8]) {
+  const uint4 x = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf2f(w[i] & 0xffffu);
+    v[2 * i + 1] = bf2f(w[i] >> 16);
+  }
+}
+__device__ __forceinline__ void store_chunk(float* p, const float (&v)[4]) { store4(p, v); }
+__device__ __forceinline__ void store_chunk(bf16_t* p, const float (&v)[8]) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
@@ -322,5 +353,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // logistic function with the hardware reciprocal (1 ulp) instead of an IEEE division
 __device__ __forceinline__ float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+// x sigmoid(x) with an IEEE division (x -> -inf gives -0, x -> +inf gives x)
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
 }  // namespace lact

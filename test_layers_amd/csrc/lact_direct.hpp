@@ -292,8 +292,8 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
   const int m0 = tm * T, n0 = tn * T;
 
   const bf16_t* A = reinterpret_cast<const bf16_t*>(G.A) + b * g.a_bs;
-  const void* Bsrc = (g.B2 != nullptr && m0 >= g.m_switch) ? g.B2 : G.B;
-  const bf16_t* B = reinterpret_cast<const bf16_t*>(Bsrc) + b * g.b_bs;
+  const bool second_b = g.B2 != nullptr && m0 >= g.m_switch;
+  const bf16_t* B = reinterpret_cast<const bf16_t*>(second_b ? g.B2 : G.B) + b * (second_b ? g.b2_bs : g.b_bs);
   const int64_t kbeg = (int64_t)split * g.kps;
   const int64_t kend = min(g.K, kbeg + g.kps);
   const int nk = kbeg < kend ? (int)((kend - kbeg + BKK - 1) / BKK) : 0;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   const int64_t tend = a.upd_t0 + a.upd_len;
   const int j0 = jb * BJ;
   const int64_t DD = (int64_t)D * D;
-  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + inst * a.x_bs;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + inst * a.k_bs;
   const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + inst * a.x_bs;
   const bf16_t* W1 = reinterpret_cast<const bf16_t*>(a.W1) + inst * DD;
   const bf16_t* W3 = reinterpret_cast<const bf16_t*>(a.W3) + inst * DD;
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
   const int64_t DD = (int64_t)D * D;
   // A operand rows: queries (q rows t) or their gated hidden (Hq rows h0 + t - t0)
   const bf16_t* X = OUT ? reinterpret_cast<const bf16_t*>(a.H) + inst * a.h_bs
-                        : reinterpret_cast<const bf16_t*>(a.q) + inst * a.x_bs;
+                        : reinterpret_cast<const bf16_t*>(a.q) + inst * a.q_bs;
   const int64_t xr0 = OUT ? G.h0 + (t0 - G.t0) : t0;
   const int64_t xrmax = OUT ? G.h0 + (tend - G.t0) - 1 : tend - 1;
   const bf16_t* B1 = reinterpret_cast<const bf16_t*>(OUT ? G.W2 : G.W1) + inst * DD;
@@ -673,6 +673,8 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
     const int64_t t = t0 + wm * 64 + i * 16 + (lane & 15);
     if (t >= tend) continue;
     bf16_t* Yr = Y + (OUT ? t : G.h0 + (t - G.t0)) * (int64_t)D;
+    // per-token output scale (output mode only)
+    const float ys = (OUT && a.oz != nullptr) ? silu(a.oz[inst * a.oz_bs + t]) : 1.f;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = j0 + wn * (BJ / 2) + j * 16 + 4 * (lane >> 4);
@@ -680,7 +682,7 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float x = accA[i][j][r];
-        h[r] = OUT ? x : x * fast_sigmoid(x) * accB[i][j][r];
+        h[r] = OUT ? x * ys : x * fast_sigmoid(x) * accB[i][j][r];
       }
       store4(Yr + col, h);
     }

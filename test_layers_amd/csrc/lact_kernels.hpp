@@ -37,7 +37,8 @@ __device__ __forceinline__ void load_tile(typename LoaderSel<T, P, ROWS, BK, NT,
 struct UpdFwdArgs {
   const void* k;
   const void* v;
-  int64_t x_bs;          // elements between instances in k/v (seq_stride * D)
+  int64_t x_bs;          // elements between instances in v (seq_stride * D)
+  int64_t k_bs;          // elements between instances in k
   const float* lr;
   int64_t lr_bs;
   const float* beta;     // momentum: per-token beta (partial sums per token block), else null
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(NT) void upd_fwd_kernel(UpdFwdArgs a) {
   const int64_t tend = a.upd_t0 + a.upd_len;
   const int j0 = jb * BJ;
   const int64_t DD = (int64_t)D * D;
-  const TIO* K = reinterpret_cast<const TIO*>(a.k) + inst * a.x_bs;
+  const TIO* K = reinterpret_cast<const TIO*>(a.k) + inst * a.k_bs;
   const TIO* V = reinterpret_cast<const TIO*>(a.v) + inst * a.x_bs;
   const TW* W1 = reinterpret_cast<const TW*>(a.W1) + inst * DD;
   const TW* W3 = reinterpret_cast<const TW*>(a.W3) + inst * DD;
@@ -197,10 +198,13 @@ struct AppFwdArgs {
   AppGroup g[MAXG];
   int ngroups;
   const void* q;
-  int64_t x_bs;
+  int64_t q_bs;          // elements between instances in q
+  int64_t x_bs;          // elements between instances in o
   void* H;               // [n, h_rows, D]
   int64_t h_bs;
   void* o;               // output mode: [n, seq, D] (x_bs per instance)
+  const float* oz;       // output mode: o[t, :] *= silu(oz[t]) (NULL: no scale)
+  int64_t oz_bs;
   int D;
 };
 
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(NT) void app_fwd_kernel(AppFwdArgs a) {
   const int64_t tend = G.t0 + G.len;
   const int j0 = jb * BJ;
   const int64_t DD = (int64_t)D * D;
-  const TIO* Q = reinterpret_cast<const TIO*>(a.q) + inst * a.x_bs;
+  const TIO* Q = reinterpret_cast<const TIO*>(a.q) + inst * a.q_bs;
   const TW* W1 = reinterpret_cast<const TW*>(G.W1) + inst * DD;
   const TW* W3 = reinterpret_cast<const TW*>(G.W3) + inst * DD;
 
@@ -298,6 +302,7 @@ struct GemmGroup {
   const void* A;
   const void* B;
   void* C;
+  const float* rs;       // optional: row m of C is scaled by silu(rs[b * rs_bs + m])
   int M;
   int tiles;             // workgroups of this group
 };
@@ -307,6 +312,8 @@ struct GemmArgs {
   int ngroups;
   int64_t lda, a_bs, ldb, b_bs, ldc, c_bs, c_ss;
   const void* B2;        // B operand for m-tiles at or beyond m_switch (group 0 only)
+  int64_t b2_bs;         // its batch stride
+  int64_t rs_bs;
   int m_switch;
   int trans_from;
   const float* Cin;
@@ -349,8 +356,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   const int m0 = tm * BM, n0 = tn * BN;
 
   const TA* A = reinterpret_cast<const TA*>(G.A) + b * g.a_bs;
-  const void* Bsrc = (g.B2 != nullptr && m0 >= g.m_switch) ? g.B2 : G.B;
-  const TB* B = reinterpret_cast<const TB*>(Bsrc) + b * g.b_bs;
+  const bool second_b = g.B2 != nullptr && m0 >= g.m_switch;
+  const TB* B = reinterpret_cast<const TB*>(second_b ? g.B2 : G.B) + b * (second_b ? g.b2_bs : g.b_bs);
   const int64_t kbeg = (int64_t)split * g.kps;
   const int64_t kend = min(g.K, kbeg + g.kps);
 
@@ -407,13 +414,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
     if (m >= M) continue;
+    const float am = G.rs ? alpha * silu(G.rs[(int64_t)b * g.rs_bs + m]) : alpha;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int nq = n0 + wn * (BN / 2) + j * 16 + 4 * (lane >> 4);   // 4 columns nq .. nq+3
       if (nq >= g.N) continue;
       float val[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) val[r] = alpha * acc[i][j][r];
+      for (int r = 0; r < 4; ++r) val[r] = am * acc[i][j][r];
       if (Cin) {
         const float4 c = *reinterpret_cast<const float4*>(Cin + (int64_t)m * g.ldcin + nq);
         val[0] += beta * c.x;
@@ -663,6 +671,85 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
           *reinterpret_cast<uint4*>(T + (int64_t)j * D + 8) = *reinterpret_cast<const uint4*>(s_t + j * 16 + 8);
         }
       }
+    }
+  }
+}
+
+// =========================================================================
+// q / k pre-processing ("LaCT架构核心思想解析" §1.2): each token's feature
+// vector x [D] becomes silu(x) / ||silu(x)||_2 (no epsilon: a token whose
+// silu is identically zero yields non-finite values, as the formula does).
+// Matrix m reads src[m] (instance stride src_bs) and writes dst[m] packed as
+// [n, rows, D].  A workgroup takes QP_ROWS consecutive token rows as one
+// flat run of 16-byte chunks (every lane busy, several loads in flight per
+// lane); per-chunk partial sums of squares go through LDS and each row's
+// total is summed by one wave in a fixed order (bitwise reproducible).
+struct QkPrepArgs {
+  const void* src[2];
+  void* dst[2];
+  int64_t src_bs;
+  int64_t rows;          // tokens per instance
+  int nblk;              // workgroups per (matrix, instance): ceil(rows / QP_ROWS)
+  int n;
+  int D;
+};
+
+constexpr int QP_ROWS = 16;
+
+// grid: nmat * n * nblk workgroups; workgroup b takes rows
+// [QP_ROWS * (b % nblk), +QP_ROWS) of instance (b / nblk) % n of matrix
+// b / (nblk * n)
+template <typename TIO>
+__global__ __launch_bounds__(NT) void qk_prep_kernel(QkPrepArgs a) {
+  constexpr int VE = 16 / (int)sizeof(TIO);            // elements per 16-byte chunk
+  constexpr int MAXCPR = 1024 / VE;                    // chunks per row at D = 1024
+  constexpr int MAXCH = QP_ROWS * MAXCPR / NT;         // chunks per thread at D = 1024
+  __shared__ float s_part[QP_ROWS * MAXCPR];
+  __shared__ float s_inv[QP_ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cpr = a.D / VE;
+  const int b = blockIdx.x;
+  const int mi = b / a.nblk, blk = b % a.nblk;
+  const int m = mi / a.n, inst = mi % a.n;
+  const int64_t t0 = (int64_t)blk * QP_ROWS;
+  const int nrows = (int)min((int64_t)QP_ROWS, a.rows - t0);
+  const int nch = nrows * cpr;
+  const TIO* X = reinterpret_cast<const TIO*>(a.src[m]) + inst * a.src_bs + t0 * a.D;
+  TIO* Y = reinterpret_cast<TIO*>(a.dst[m]) + (inst * a.rows + t0) * a.D;
+  // chunk c of the run is element offset (c / cpr) * D + (c % cpr) * VE = c * VE
+  // in both the source rows (contiguous within an instance) and the packed copy
+  float v[MAXCH][VE];
+#pragma unroll
+  for (int i = 0; i < MAXCH; ++i) {
+    const int c = tid + i * NT;
+    if (c < nch) {
+      load_chunk(X + (int64_t)c * VE, v[i]);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        v[i][e] = silu(v[i][e]);
+        ss += v[i][e] * v[i][e];
+      }
+      s_part[c] = ss;
+    }
+  }
+  __syncthreads();
+  for (int r = wave; r < nrows; r += NT / 64) {
+    float ss = 0.f;
+    for (int j = lane; j < cpr; j += 64) ss += s_part[r * cpr + j];
+    ss = wave_sum(ss);
+    if (lane == 0) s_inv[r] = 1.0f / sqrtf(ss);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MAXCH; ++i) {
+    const int c = tid + i * NT;
+    if (c < nch) {
+      const float inv = s_inv[c / cpr];
+      float w[VE];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) w[e] = v[i][e] * inv;
+      store_chunk(Y + (int64_t)c * VE, w);
     }
   }
 }

@@ -33,13 +33,15 @@ UPDATE_THEN_APPLY = 1
 CHUNK_UPDATE = 1
 CHUNK_APPLY = 2
 NO_RENORM = 1
+QK_PREP = 2
 
-K_UPD, K_APP, K_OUT, K_DW, K_OPT, K_NS, K_SNAP = range(7)
+K_UPD, K_APP, K_OUT, K_DW, K_OPT, K_NS, K_SNAP, K_PREP = range(8)
 K_NAMES = {K_UPD: "update_fwd", K_APP: "apply_fwd", K_OUT: "apply_out", K_DW: "dw", K_OPT: "opt",
-           K_NS: "newton_schulz", K_SNAP: "snapshot"}
+           K_NS: "newton_schulz", K_SNAP: "snapshot", K_PREP: "qk_prep"}
 
 EXPORTS = ["lact_workspace_size", "lact_chunk_update", "lact_apply", "lact_layer_forward",
-           "lact_status_str", "lact_last_error", "lact_timing_enable", "lact_timing_read"]
+           "lact_layer_forward_scaled", "lact_status_str", "lact_last_error", "lact_timing_enable",
+           "lact_timing_read"]
 
 
 class LactError(RuntimeError):
@@ -76,6 +78,9 @@ def lib() -> ctypes.CDLL:
     L.lact_layer_forward.restype = i32
     L.lact_layer_forward.argtypes = [P, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32,
                                      vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lact_layer_forward_scaled.restype = i32
+    L.lact_layer_forward_scaled.argtypes = [P, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32,
+                                            vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.lact_status_str.restype = ctypes.c_char_p
     L.lact_status_str.argtypes = [i32]
     L.lact_last_error.restype = ctypes.c_char_p
@@ -98,9 +103,9 @@ def check(status: int) -> None:
 
 
 def problem(n_inst: int, d: int, io_dtype: int, opt: int, rec_planes: int = 0, ns_iters: int = 5,
-            renorm: bool = True, dh: Optional[int] = None) -> Problem:
+            renorm: bool = True, dh: Optional[int] = None, qk_prep: bool = False) -> Problem:
     return Problem(n_inst, d, d if dh is None else dh, io_dtype, opt, ns_iters, rec_planes,
-                   0 if renorm else NO_RENORM)
+                   (0 if renorm else NO_RENORM) | (QK_PREP if qk_prep else 0))
 
 
 # ----------------------------------------------------------------- raw-pointer calls
@@ -129,6 +134,13 @@ def layer_forward_ptr(p: Problem, q, k, v, lr, beta, L, chunk, order, bounds, fl
     bp, fp, nc, _keep = _sched(bounds, flags)
     return lib().lact_layer_forward(ctypes.byref(p), q, k, v, lr, beta, L, chunk, order, bp, fp, nc,
                                     W1, W2, W3, M1, M2, M3, o, ws, ws_bytes, stream)
+
+
+def layer_forward_scaled_ptr(p: Problem, q, k, v, lr, beta, oz, L, chunk, order, bounds, flags,
+                             W1, W2, W3, M1, M2, M3, o, ws, ws_bytes, stream) -> int:
+    bp, fp, nc, _keep = _sched(bounds, flags)
+    return lib().lact_layer_forward_scaled(ctypes.byref(p), q, k, v, lr, beta, oz, L, chunk, order,
+                                           bp, fp, nc, W1, W2, W3, M1, M2, M3, o, ws, ws_bytes, stream)
 
 
 def chunk_update_ptr(p: Problem, k, v, lr, beta, Lc, seq_stride, W1, W2, W3, M1, M2, M3,
@@ -198,36 +210,45 @@ def _workspace(nbytes, workspace, device):
 def layer_forward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, o=None, *,
                   chunk: int = 0, order: int = APPLY_THEN_UPDATE, opt: int = OPT_GD,
                   bounds=None, flags=None, rec_planes: int = 0, ns_iters: int = 5,
-                  renorm: bool = True, workspace=None, stream=None):
+                  renorm: bool = True, qk_prep: bool = False, oz=None, workspace=None,
+                  stream=None):
     """q, k, v [n, L, D] (fp32 or bf16), lr [n, L, 3] fp32, beta [n, L] fp32
     (momentum) or None, W1, W2, W3 [n, D, D] fp32 (updated in place), M1..M3
-    (momentum state, updated in place).  Returns o [n, L, D] (allocated with
-    torch.zeros if not given; rows of non-APPLY chunks keep their values)."""
+    (momentum state, updated in place).  qk_prep: q and k are raw (the library
+    applies silu and the per-token L2 normalisation).  oz [n, L] fp32: the
+    output rows are scaled by silu(oz) (lact_layer_forward_scaled).  Returns o
+    [n, L, D] (allocated with torch.zeros if not given; rows of non-APPLY
+    chunks keep their values)."""
     torch = _torch()
     n, L, D = q.shape
     io = _io_dtype(q)
-    p = problem(n, D, io, opt, rec_planes, ns_iters, renorm)
+    p = problem(n, D, io, opt, rec_planes, ns_iters, renorm, qk_prep=qk_prep)
     if o is None:
         o = torch.zeros_like(q)
     need = workspace_size(p, L, chunk, order, bounds, flags)
     ws = _workspace(need, workspace, q.device)
     f32 = torch.float32
-    st = layer_forward_ptr(p, _ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"),
-                           _ptr(lr, f32, "lr"), _ptr(beta, f32, "beta"), L, chunk, order, bounds, flags,
-                           _ptr(W1, f32, "W1"), _ptr(W2, f32, "W2"), _ptr(W3, f32, "W3"),
-                           _ptr(M1, f32, "M1"), _ptr(M2, f32, "M2"), _ptr(M3, f32, "M3"),
-                           _ptr(o, q.dtype, "o"), ws.data_ptr(), ws.numel(), _stream(stream))
+    head = (p, _ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"),
+            _ptr(lr, f32, "lr"), _ptr(beta, f32, "beta"))
+    tail = (L, chunk, order, bounds, flags,
+            _ptr(W1, f32, "W1"), _ptr(W2, f32, "W2"), _ptr(W3, f32, "W3"),
+            _ptr(M1, f32, "M1"), _ptr(M2, f32, "M2"), _ptr(M3, f32, "M3"),
+            _ptr(o, q.dtype, "o"), ws.data_ptr(), ws.numel(), _stream(stream))
+    if oz is None:
+        st = layer_forward_ptr(*head, *tail)
+    else:
+        st = layer_forward_scaled_ptr(*head, _ptr(oz, f32, "oz"), *tail)
     check(st)
     return o
 
 
 def chunk_update(k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, Lc: Optional[int] = None,
                  opt: int = OPT_GD, rec_planes: int = 0, ns_iters: int = 5, renorm: bool = True,
-                 workspace=None, stream=None):
+                 qk_prep: bool = False, workspace=None, stream=None):
     torch = _torch()
     n, S, D = k.shape
     Lc = S if Lc is None else Lc
-    p = problem(n, D, _io_dtype(k), opt, rec_planes, ns_iters, renorm)
+    p = problem(n, D, _io_dtype(k), opt, rec_planes, ns_iters, renorm, qk_prep=qk_prep)
     ws = _workspace(workspace_size(p, Lc, max(Lc, 1)), workspace, k.device)
     f32 = torch.float32
     check(chunk_update_ptr(p, _ptr(k, k.dtype, "k"), _ptr(v, k.dtype, "v"), _ptr(lr, f32, "lr"),
@@ -236,11 +257,12 @@ def chunk_update(k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, Lc: O
                            _ptr(M3, f32, "M3"), ws.data_ptr(), ws.numel(), _stream(stream)))
 
 
-def apply(q, W1, W2, W3, o=None, *, Lq: Optional[int] = None, workspace=None, stream=None):
+def apply(q, W1, W2, W3, o=None, *, Lq: Optional[int] = None, qk_prep: bool = False,
+          workspace=None, stream=None):
     torch = _torch()
     n, S, D = q.shape
     Lq = S if Lq is None else Lq
-    p = problem(n, D, _io_dtype(q), OPT_GD)
+    p = problem(n, D, _io_dtype(q), OPT_GD, qk_prep=qk_prep)
     if o is None:
         o = torch.zeros_like(q)
     ws = _workspace(workspace_size(p, Lq, max(Lq, 1)), workspace, q.device)

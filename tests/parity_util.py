@@ -38,9 +38,11 @@ def run_gpu(wl: W.Workload, inp: W.Inputs, torch, lact, rec_planes=None, order=N
     if wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM):
         Ms = [torch.zeros_like(w) for w in Ws]
     o = torch.zeros_like(q) if o_init is None else o_init
+    oz = to_dev(inp.oz, torch) if wl.out_scale else None
     lact.layer_forward(q, k, v, lr, beta, *Ws, *Ms, o, order=wl.order if order is None else order,
                        opt=wl.opt, bounds=list(wl.bounds), flags=list(wl.flags),
-                       rec_planes=wl.rec_planes if rec_planes is None else rec_planes, renorm=renorm)
+                       rec_planes=wl.rec_planes if rec_planes is None else rec_planes, renorm=renorm,
+                       qk_prep=wl.layer_qk_prep, oz=oz)
     torch.cuda.synchronize()
     return {"o": o, "W1": Ws[0], "W2": Ws[1], "W3": Ws[2], "M1": Ms[0], "M2": Ms[1], "M3": Ms[2]}
 
@@ -66,7 +68,9 @@ def compare(wl: W.Workload, inp: W.Inputs, gpu, order=None, renorm=True, instanc
         ref = O.forward_instance(inp.q[i], inp.k[i], inp.v[i], inp.lr[i],
                                  None if inp.beta is None else inp.beta[i],
                                  inp.W1[i], inp.W2[i], inp.W3[i], wl.bounds, wl.flags,
-                                 wl.order if order is None else order, wl.opt, renorm=renorm)
+                                 wl.order if order is None else order, wl.opt, renorm=renorm,
+                                 qk_prep=wl.layer_qk_prep,
+                                 oz=inp.oz[i] if wl.out_scale else None)
         mask = ref["o_mask"]
         for key in keys:
             g = gpu[key][i]

@@ -181,3 +181,42 @@ def test_valid_call_without_gpu_reports_no_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert fwd(P()) == lact.ERR_NO_DEVICE
+
+
+def fwd_scaled(p, oz=FAKE, L=512, chunk=128, ws_bytes=1 << 40, bounds=None, flags=None, **ptrs):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lr=FAKE, beta=FAKE, W1=FAKE, W2=FAKE, W3=FAKE,
+             M1=FAKE, M2=FAKE, M3=FAKE, o=FAKE, ws=FAKE)
+    a.update(ptrs)
+    return lact.layer_forward_scaled_ptr(p, a["q"], a["k"], a["v"], a["lr"], a["beta"], oz, L, chunk,
+                                         0, bounds, flags, a["W1"], a["W2"], a["W3"], a["M1"], a["M2"],
+                                         a["M3"], a["o"], a["ws"], ws_bytes, None)
+
+
+def test_qk_prep_flag_accepted_and_sized():
+    p = P(qk_prep=True)
+    assert p.flags == lact.QK_PREP
+    base = lact.workspace_size(P(), 512, 128)
+    prep = lact.workspace_size(p, 512, 128)
+    # one pre-processed copy of q and one of k: [n, L, D] bf16 each
+    assert prep - base == 2 * 2 * 512 * 128 * 2
+    # an update-only schedule keeps only the k copy
+    b1 = lact.workspace_size(P(), 512, 0, 0, [0, 512], [1])
+    p1 = lact.workspace_size(p, 512, 0, 0, [0, 512], [1])
+    assert p1 - b1 == 2 * 512 * 128 * 2
+    both = P(qk_prep=True, renorm=False)
+    assert both.flags == lact.QK_PREP | lact.NO_RENORM
+    assert fwd(both, ws_bytes=prep - 1) == lact.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_scaled_entry_validation():
+    assert fwd_scaled(P(), oz=None) == lact.ERR_INVALID_ARG
+    assert "oz" in lact.last_error()
+    assert fwd_scaled(P(), oz=FAKE + 2) == lact.ERR_INVALID_ARG
+    # no APPLY chunk: the scale is never read, so NULL is allowed
+    st = fwd_scaled(P(), oz=None, L=256, chunk=0, bounds=[0, 256], flags=[1], q=None, o=None)
+    assert st != lact.ERR_INVALID_ARG, lact.last_error()
+    assert fwd_scaled(P(n_inst=0), oz=None) == lact.OK
+    assert fwd_scaled(P(), ws_bytes=10) == lact.ERR_WORKSPACE_TOO_SMALL
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert fwd_scaled(P()) == lact.ERR_NO_DEVICE

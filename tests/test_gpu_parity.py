@@ -138,9 +138,10 @@ SMALL[5] = _small_video()
 SMALL[6] = _small_prefill()
 SMALL[7] = _small_video_noisy_first()
 SMALL[8] = W.CONFIGS[8].scaled(n_inst=2, L=2 * 1024 + 300, chunk=1024)
+SMALL[9] = W.CONFIGS[9].scaled(n_inst=2, L=3 * 512 + 200, chunk=512)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_layer_reduced_size(lact, cid):
     wl = SMALL[cid]
     log(f"layer reduced cfg{cid}: n={wl.n_inst} D={wl.D} L={wl.L} chunks={wl.n_chunks}")
@@ -194,3 +195,58 @@ def test_resume_equals_single_call(lact):
     assert torch.equal(torch.cat([o1, o2], 1), full["o"])
     for j, key in enumerate(["W1", "W2", "W3"]):
         assert torch.equal(Ws[j], full[key])
+
+
+# ------------------------------------------------------------------ raw q/k and the output scale
+@pytest.mark.parametrize("io,planes,opt", [(W.DTYPE_F32, 3, W.OPT_GD), (W.DTYPE_BF16, 1, W.OPT_MOMENTUM),
+                                           (W.DTYPE_BF16, 2, W.OPT_MUON),
+                                           (W.DTYPE_BF16, 3, W.OPT_MUON_MOMENTUM)])
+def test_layer_raw_qk_and_output_scale_every_profile(lact, io, planes, opt):
+    """Every precision profile (the fp32 one scales inside the generic output
+    GEMM, the bf16 ones inside the apply tile), with tokens whose scale
+    pre-activation is 0 or far negative (silu = 0: the row must vanish)."""
+    import dataclasses
+    wl = dataclasses.replace(W.CONFIGS[9].scaled(n_inst=2, L=900, chunk=256), io_dtype=io,
+                             rec_planes=planes, opt=opt, tol=_gate(io))
+    log(f"raw qk + scale io={io} planes={planes} opt={opt}")
+    inp = W.generate(wl, seed=11)
+    inp.oz[:, 5] = 0.0
+    inp.oz[:, 6] = -200.0
+    inp.oz[:, 7] = 60.0
+    gpu = run_gpu(wl, inp, torch, lact)
+    o = from_dev(gpu["o"], torch)
+    assert np.all(o[:, 5:7] == 0.0)
+    errs = compare(wl, inp, gpu)
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= wl.tol, errs
+
+
+@pytest.mark.parametrize("io", [W.DTYPE_F32, W.DTYPE_BF16])
+def test_chunk_entry_points_with_raw_qk_and_stride(lact, io):
+    """lact_chunk_update / lact_apply with LACT_QK_PREP and seq_stride > the
+    tokens used: the pre-processed copies are packed while v, lr and o keep
+    the caller's stride."""
+    n, S, Lc, D = 2, 700, 531, 128
+    inp = _rand_inputs(n, S, D, io, seed=21, raw=True)
+    k, v, lr, q = (to_dev(x, torch) for x in (inp.k, inp.v, inp.lr, inp.q))
+    Ws = [to_dev(w, torch).clone() for w in (inp.W1, inp.W2, inp.W3)]
+    lact.chunk_update(k, v, lr, None, *Ws, Lc=Lc, qk_prep=True)
+    o = torch.full_like(q, 3.0)
+    lact.apply(q, *Ws, o, Lq=Lc, qk_prep=True)
+    torch.cuda.synchronize()
+    g = from_dev(o, torch)
+    assert np.all(g[:, Lc:] == 3.0)
+    ew, eo = 0.0, 0.0
+    for i in range(n):
+        kh = O.qk_preprocess(inp.k[i][:Lc])
+        qh = O.qk_preprocess(inp.q[i][:Lc])
+        Wr, _ = O.update_step([O.f64(inp.W1[i]), O.f64(inp.W2[i]), O.f64(inp.W3[i])], [None] * 3,
+                              kh, O.f64(inp.v[i][:Lc]), O.f64(inp.lr[i][:Lc]), None, W.OPT_GD)
+        for j in range(3):
+            ew = max(ew, rel_err(from_dev(Ws[j], torch)[i], Wr[j]))
+        # the apply reads the GPU's updated weights: compare against the
+        # oracle's apply on exactly those
+        Wg = [from_dev(w, torch)[i] for w in Ws]
+        eo = max(eo, rel_err(g[i, :Lc], O.apply(Wg[0], Wg[1], Wg[2], qh)))
+    log(f"  io={io} W err={ew:.2e} o err={eo:.2e}")
+    assert max(ew, eo) <= _gate(io)

@@ -584,11 +584,10 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     }
     pa.src_bs = x_bs;
     pa.rows = w.prep_rows;
-    const int64_t nblk = (w.prep_rows + QP_ROWS - 1) / QP_ROWS;
-    const int64_t blocks = (int64_t)nm * n * nblk;
-    pa.nblk = (int)std::min<int64_t>(nblk, 0x7fffffff);
+    pa.total = (int64_t)nm * n * w.prep_rows;
     pa.n = n;
     pa.D = D;
+    const int64_t blocks = (pa.total + NT / QP_LANES - 1) / (NT / QP_LANES);
     if (blocks > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
     if (blocks > 0) {
       KernelTimer kt(LACT_K_PREP, s);

@@ -680,76 +680,61 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
 // vector x [D] becomes silu(x) / ||silu(x)||_2 (no epsilon: a token whose
 // silu is identically zero yields non-finite values, as the formula does).
 // Matrix m reads src[m] (instance stride src_bs) and writes dst[m] packed as
-// [n, rows, D].  A workgroup takes QP_ROWS consecutive token rows as one
-// flat run of 16-byte chunks (every lane busy, several loads in flight per
-// lane); per-chunk partial sums of squares go through LDS and each row's
-// total is summed by one wave in a fixed order (bitwise reproducible).
+// [n, rows, D].  A group of QP_LANES lanes owns one token row: lane l of the
+// group takes the row's 16-byte chunks l, l + QP_LANES, ... (each group
+// instruction covers 256 contiguous bytes), and the row's sum of squares is
+// a butterfly over the group -- no LDS and no workgroup barrier, which
+// measured faster than staging partial sums through LDS.
 struct QkPrepArgs {
   const void* src[2];
   void* dst[2];
   int64_t src_bs;
   int64_t rows;          // tokens per instance
-  int nblk;              // workgroups per (matrix, instance): ceil(rows / QP_ROWS)
+  int64_t total;         // nmat * n * rows
   int n;
   int D;
 };
 
-constexpr int QP_ROWS = 16;
+constexpr int QP_LANES = 16;
 
-// grid: nmat * n * nblk workgroups; workgroup b takes rows
-// [QP_ROWS * (b % nblk), +QP_ROWS) of instance (b / nblk) % n of matrix
-// b / (nblk * n)
 template <typename TIO>
 __global__ __launch_bounds__(NT) void qk_prep_kernel(QkPrepArgs a) {
   constexpr int VE = 16 / (int)sizeof(TIO);            // elements per 16-byte chunk
-  constexpr int MAXCPR = 1024 / VE;                    // chunks per row at D = 1024
-  constexpr int MAXCH = QP_ROWS * MAXCPR / NT;         // chunks per thread at D = 1024
-  __shared__ float s_part[QP_ROWS * MAXCPR];
-  __shared__ float s_inv[QP_ROWS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int MAXC = 1024 / VE / QP_LANES;           // chunks per lane at D = 1024
+  const int gl = threadIdx.x & (QP_LANES - 1);
+  const int64_t row = (int64_t)blockIdx.x * (NT / QP_LANES) + threadIdx.x / QP_LANES;
+  if (row >= a.total) return;                          // whole groups leave together
   const int cpr = a.D / VE;
-  const int b = blockIdx.x;
-  const int mi = b / a.nblk, blk = b % a.nblk;
-  const int m = mi / a.n, inst = mi % a.n;
-  const int64_t t0 = (int64_t)blk * QP_ROWS;
-  const int nrows = (int)min((int64_t)QP_ROWS, a.rows - t0);
-  const int nch = nrows * cpr;
-  const TIO* X = reinterpret_cast<const TIO*>(a.src[m]) + inst * a.src_bs + t0 * a.D;
-  TIO* Y = reinterpret_cast<TIO*>(a.dst[m]) + (inst * a.rows + t0) * a.D;
-  // chunk c of the run is element offset (c / cpr) * D + (c % cpr) * VE = c * VE
-  // in both the source rows (contiguous within an instance) and the packed copy
-  float v[MAXCH][VE];
+  const int64_t per_mat = (int64_t)a.n * a.rows;
+  const int m = (int)(row / per_mat);
+  const int64_t r = row % per_mat;
+  const TIO* x = reinterpret_cast<const TIO*>(a.src[m]) + (r / a.rows) * a.src_bs + (r % a.rows) * a.D;
+  TIO* y = reinterpret_cast<TIO*>(a.dst[m]) + r * a.D;
+  float v[MAXC][VE];
+  float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXCH; ++i) {
-    const int c = tid + i * NT;
-    if (c < nch) {
-      load_chunk(X + (int64_t)c * VE, v[i]);
-      float ss = 0.f;
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = gl + i * QP_LANES;
+    if (c < cpr) {
+      load_chunk(x + c * VE, v[i]);
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
         v[i][e] = silu(v[i][e]);
         ss += v[i][e] * v[i][e];
       }
-      s_part[c] = ss;
     }
   }
-  __syncthreads();
-  for (int r = wave; r < nrows; r += NT / 64) {
-    float ss = 0.f;
-    for (int j = lane; j < cpr; j += 64) ss += s_part[r * cpr + j];
-    ss = wave_sum(ss);
-    if (lane == 0) s_inv[r] = 1.0f / sqrtf(ss);
-  }
-  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < MAXCH; ++i) {
-    const int c = tid + i * NT;
-    if (c < nch) {
-      const float inv = s_inv[c / cpr];
+  for (int o = QP_LANES / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
+  const float inv = 1.0f / sqrtf(ss);
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = gl + i * QP_LANES;
+    if (c < cpr) {
       float w[VE];
 #pragma unroll
       for (int e = 0; e < VE; ++e) w[e] = v[i][e] * inv;
-      store_chunk(Y + (int64_t)c * VE, w);
+      store_chunk(y + c * VE, w);
     }
   }
 }

@@ -56,7 +56,7 @@ class Workload:
     cid: int
     name: str
     n_inst: int           # B * nh
-    D: int                # d == dh
+    D: int                # d: width of q, k, v, o
     L: int                # tokens per instance
     bounds: Tuple[int, ...]   # chunk boundaries, len n_chunks + 1
     flags: Tuple[int, ...]    # per chunk: UPDATE | APPLY
@@ -68,6 +68,11 @@ class Workload:
     tol: float            # parity gate, max-abs error relative to max |ref|
     layer_qk_prep: bool = False   # q, k handed over raw; the layer pre-processes them
     out_scale: bool = False       # per-token output-scale pre-activation oz [n, L]
+    Dh: Optional[int] = None      # fast-weight hidden width dh (None: dh = d)
+
+    @property
+    def dh(self) -> int:
+        return self.D if self.Dh is None else self.Dh
 
     @property
     def n_chunks(self) -> int:
@@ -161,6 +166,10 @@ def _make_configs() -> Dict[int, Workload]:
     b, f = uniform_schedule(32768, 4096)
     c[8] = Workload(8, "lm3b_d512_bf16_muon_momentum", 6, 512, 32768, b, f, APPLY_THEN_UPDATE,
                     OPT_MUON_MOMENTUM, DTYPE_BF16, True, 2, 2e-2)
+    # fast-weight width variant: the 760M-LM layer with a hidden width dh = 2d
+    b, f = uniform_schedule(32768, 2048)
+    c[10] = Workload(10, "lm760m_d384_dh768_bf16_momentum", 4, 384, 32768, b, f, APPLY_THEN_UPDATE,
+                     OPT_MOMENTUM, DTYPE_BF16, True, 1, 2e-2, Dh=768)
     return c
 
 
@@ -196,9 +205,9 @@ class Inputs:
     v: np.ndarray
     lr: np.ndarray     # [n, L, 3] float32
     beta: Optional[np.ndarray]   # [n, L] float32 (momentum only)
-    W1: np.ndarray     # [n, D, D] float32   (dh x d)
-    W2: np.ndarray     # [n, D, D] float32   (d x dh)
-    W3: np.ndarray     # [n, D, D] float32   (dh x d)
+    W1: np.ndarray     # [n, dh, d] float32
+    W2: np.ndarray     # [n, d, dh] float32
+    W3: np.ndarray     # [n, dh, d] float32
     oz: Optional[np.ndarray] = None   # [n, L] float32 output-scale pre-activation
 
 
@@ -223,10 +232,11 @@ def _draw_instance(wl: Workload, seed: int, inst: int):
     if wl.opt in (OPT_MOMENTUM, OPT_MUON_MOMENTUM):
         zb = rng.standard_normal(L)
         beta = 1.0 / (1.0 + np.exp(-(zb + 2.2)))
-    s = 1.0 / np.sqrt(D)
-    W1 = rng.standard_normal((D, D)) * s
-    W2 = rng.standard_normal((D, D)) * s
-    W3 = rng.standard_normal((D, D)) * s
+    # W ~ N(0, 1/fan-in): W1, W3 [dh, d] (fan-in d), W2 [d, dh] (fan-in dh)
+    dh = wl.dh
+    W1 = rng.standard_normal((dh, D)) / np.sqrt(D)
+    W2 = rng.standard_normal((D, dh)) / np.sqrt(dh)
+    W3 = rng.standard_normal((dh, D)) / np.sqrt(D)
     # output-scale pre-activation (drawn last: earlier draws are unchanged)
     oz = rng.standard_normal(L) if wl.out_scale else None
 
@@ -263,13 +273,13 @@ def generate_instance(wl: Workload, inst: int, seed: int = 0) -> Inputs:
 def algorithmic_flops(wl: Workload) -> Dict[str, float]:
     """Work the method must do (MFMA-countable contractions only).
 
-    update: 12 D^2 per (token, instance): the three forward products on k/v
-            (6 D^2) and the three weight-gradient contractions (6 D^2);
-    apply:   6 D^2 per (query, instance);
-    Newton-Schulz (Muon): 5 iterations x 3 products x 2 D^3 per matrix, three
-            matrices per instance per update chunk.
+    update: 12 d dh per (token, instance): the three forward products on k/v
+            (6 d dh) and the three weight-gradient contractions (6 d dh);
+    apply:   6 d dh per (query, instance);
+    Newton-Schulz (Muon, d = dh): 5 iterations x 3 products x 2 D^3 per
+            matrix, three matrices per instance per update chunk.
     """
-    D, n = wl.D, wl.n_inst
+    D, dh, n = wl.D, wl.dh, wl.n_inst
     upd = app = 0
     n_upd = 0
     for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags):
@@ -278,7 +288,7 @@ def algorithmic_flops(wl: Workload) -> Dict[str, float]:
             n_upd += 1
         if f & APPLY:
             app += b - a
-    fu = 12.0 * D * D * upd * n
-    fa = 6.0 * D * D * app * n
+    fu = 12.0 * D * dh * upd * n
+    fa = 6.0 * D * dh * app * n
     fns = (30.0 * D ** 3 * 3 * n_upd * n) if wl.opt in (OPT_MUON, OPT_MUON_MOMENTUM) else 0.0
     return {"update": fu, "apply": fa, "ns": fns, "total": fu + fa + fns}

@@ -490,3 +490,71 @@ def test_output_scale_special_values():
         assert np.max(np.abs(r - r[0])) <= 1e-12 * abs(r[0])
     for key in ("W1", "W2", "W3"):
         assert np.array_equal(zr[key], base[key])
+
+
+# ---------------------------------------------------------------- rectangular fast weights (d != dh)
+def rand_rect(d, dh, rng, scale=None):
+    """W1, W3 [dh, d] (fan-in d) and W2 [d, dh] (fan-in dh)."""
+    s1 = 1.0 / np.sqrt(d) if scale is None else scale
+    s2 = 1.0 / np.sqrt(dh) if scale is None else scale
+    return [rng.standard_normal((dh, d)) * s1, rng.standard_normal((d, dh)) * s2,
+            rng.standard_normal((dh, d)) * s1]
+
+
+@pytest.mark.parametrize("d,dh", [(4, 7), (6, 3)])
+def test_rectangular_grads_match_finite_differences(d, dh):
+    rng = np.random.default_rng(10 * d + dh)
+    W = rand_rect(d, dh, rng, 0.7)
+    K, V, lr = rand_chunk(5, d, rng, lr_scale=1.0)
+    U = O.chunk_grads(W[0], W[1], W[2], K, V, lr)
+    for j in range(3):
+        assert U[j].shape == W[j].shape
+    h = 1e-6
+    for j in range(3):
+        fd = np.zeros(W[j].shape)
+        for r in range(W[j].shape[0]):
+            for c in range(W[j].shape[1]):
+                Wp = [w.copy() for w in W]
+                Wm = [w.copy() for w in W]
+                Wp[j][r, c] += h
+                Wm[j][r, c] -= h
+                fd[r, c] = (weighted_loss(Wp, K, V, lr, j) - weighted_loss(Wm, K, V, lr, j)) / (2 * h)
+        err = np.max(np.abs(-fd - U[j])) / np.max(np.abs(U[j]))
+        assert err <= 1e-7, (j, err)
+
+
+@pytest.mark.parametrize("opt", [O.OPT_GD, O.OPT_MOMENTUM, O.OPT_MUON, O.OPT_MUON_MOMENTUM])
+def test_rectangular_row_norms_invariant(opt):
+    """Rows are fan-in vectors: length d for W1, W3 and dh for W2."""
+    rng = np.random.default_rng(21)
+    d, dh, C = 5, 8, 9
+    W0 = rand_rect(d, dh, rng)
+    W, M = W0, [np.zeros_like(w) for w in W0]
+    n0 = [np.linalg.norm(w, axis=1) for w in W0]
+    for _ in range(4):
+        K, V, lr = rand_chunk(C, d, rng, lr_scale=2.0)
+        W, M = O.update_step(W, M, K, V, lr, rng.uniform(0.5, 1, C), opt)
+        for w, w0, n in zip(W, W0, n0):
+            assert w.shape == w0.shape
+            np.testing.assert_allclose(np.linalg.norm(w, axis=1), n, rtol=1e-12)
+
+
+def test_rectangular_w2_only_update_is_linear_attention():
+    """As the square case, with a feature map h of dh features on d-wide tokens."""
+    rng = np.random.default_rng(16)
+    C, d, dh = 9, 5, 11
+    q = rng.standard_normal((C, d))
+    k = rng.standard_normal((C, d))
+    v = rng.standard_normal((C, d))
+    lr = np.zeros((C, 3))
+    lr[:, 1] = rng.uniform(0.1, 1.0, C)
+    W = rand_rect(d, dh, rng)
+    out = O.forward_instance(q, k, v, lr, None, *W, [0, C], [3], O.UPDATE_THEN_APPLY,
+                             O.OPT_GD, renorm=False)
+
+    def h(X):
+        a = X @ W[0].T
+        return a / (1 + np.exp(-a)) * (X @ W[2].T)
+    ref = h(q) @ W[1].T + ((h(q) @ h(k).T) * lr[:, 1][None, :]) @ v
+    assert out["o"].shape == (C, d)
+    assert np.max(np.abs(out["o"] - ref)) <= 1e-12 * np.max(np.abs(ref))

@@ -55,3 +55,18 @@ def test_flop_counts():
     assert abs(f["total"] - 0.348e12) / 0.348e12 < 0.01
     f = W.algorithmic_flops(W.CONFIGS[3])
     assert abs(f["total"] - 1.508e12) / 1.508e12 < 0.01
+
+
+def test_rectangular_fast_weights():
+    """dh != d: W1, W3 [dh, d], W2 [d, dh], each ~ N(0, 1/fan-in); the square
+    workloads keep their draws (same shapes, same order)."""
+    wl = W.CONFIGS[10].scaled(n_inst=2, L=64, chunk=32)
+    assert wl.D == 384 and wl.dh == 768
+    g = W.generate(wl)
+    assert g.W1.shape == (2, 768, 384) and g.W3.shape == (2, 768, 384) and g.W2.shape == (2, 384, 768)
+    assert g.q.shape == (2, 64, 384)
+    assert abs(np.std(g.W1) * np.sqrt(384) - 1) < 0.02 and abs(np.std(g.W2) * np.sqrt(768) - 1) < 0.02
+    sq = W.CONFIGS[2].scaled(n_inst=1, L=64, chunk=32)
+    assert sq.dh == sq.D
+    f = W.algorithmic_flops(W.CONFIGS[10])
+    assert f["total"] == 2 * W.algorithmic_flops(W.CONFIGS[2])["total"]

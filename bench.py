@@ -42,15 +42,15 @@ def parse():
 def kernel_flops(wl, lact):
     """Algorithmic FLOPs per step, per kernel class."""
     from test_layers_amd import workloads as W
-    D, n = wl.D, wl.n_inst
+    D, Dh, n = wl.D, wl.dh, wl.n_inst
     upd = sum(b - a for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags) if f & W.UPDATE)
     app = sum(b - a for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags) if f & W.APPLY)
     n_upd = sum(1 for f in wl.flags if f & W.UPDATE)
     return {
-        lact.K_UPD: 6.0 * upd * D * D * n,                  # K W1^T, K W3^T, V W2
-        lact.K_APP: 4.0 * app * D * D * n,                  # Q W1^T, Q W3^T
-        lact.K_OUT: 2.0 * app * D * D * n,                  # Hq W2^T
-        lact.K_DW: 6.0 * upd * D * D * n,                   # three contractions over tokens
+        lact.K_UPD: 6.0 * upd * D * Dh * n,                 # K W1^T, K W3^T, V W2
+        lact.K_APP: 4.0 * app * D * Dh * n,                 # Q W1^T, Q W3^T
+        lact.K_OUT: 2.0 * app * D * Dh * n,                 # Hq W2^T
+        lact.K_DW: 6.0 * upd * D * Dh * n,                  # three contractions over tokens
         lact.K_OPT: 0.0,
         lact.K_NS: (30.0 * D ** 3 * 3 * n * n_upd) if wl.opt in (W.OPT_MUON, W.OPT_MUON_MOMENTUM) else 0.0,
         lact.K_SNAP: 0.0,
@@ -62,8 +62,7 @@ def opt_bytes(wl, S):
     """Minimum HBM bytes of the optimiser kernel per update step: S fp32
     partials of the three direction matrices read, W (and M) read and written."""
     from test_layers_amd import workloads as W
-    D, n = wl.D, wl.n_inst
-    mats = 3 * D * D * 4 * n
+    mats = 3 * wl.D * wl.dh * 4 * wl.n_inst
     per = S * mats + 2 * mats + (2 * mats if wl.opt == W.OPT_MOMENTUM else 0)
     return per
 
@@ -159,7 +158,7 @@ def main():
     Ws = [dev(inp.W1), dev(inp.W2), dev(inp.W3)]
     Ms = [torch.zeros_like(w) for w in Ws] if wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM) else [None] * 3
     o = torch.zeros_like(q)
-    p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes, qk_prep=wl.layer_qk_prep)
+    p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes, dh=wl.dh, qk_prep=wl.layer_qk_prep)
     bounds, flags = list(wl.bounds), list(wl.flags)
     ws = torch.empty(lact.workspace_size(p, wl.L, 0, wl.order, bounds, flags), dtype=torch.uint8,
                      device="cuda")
@@ -226,7 +225,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.io_dtype == W.DTYPE_BF16 else "f32",
         "data": "synthetic (seeded generator; no dataset, random-init fast weights)",
-        "config": {"workload": wl.name, "n_inst": wl.n_inst, "d": wl.D, "dh": wl.D, "seq_len": wl.L,
+        "config": {"workload": wl.name, "n_inst": wl.n_inst, "d": wl.D, "dh": wl.dh, "seq_len": wl.L,
                    "max_chunk": wl.max_chunk, "n_chunks": wl.n_chunks,
                    "opt": ["gd", "momentum", "muon", "muon_momentum"][wl.opt],
                    "order": ["apply_then_update", "update_then_apply"][wl.order],

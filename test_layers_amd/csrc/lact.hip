@@ -217,7 +217,7 @@ int64_t round128(int64_t x) { return (x + 127) / 128 * 128; }
 
 void dw_split(const lact_problem& p, int64_t C, int& S, int64_t& kps) {
   const int bt = dw_tile(p);
-  const int64_t tiles = (int64_t)(3 * p.d / bt) * (p.d / bt) * std::max(1, p.n_inst);
+  const int64_t tiles = (int64_t)((3 * p.dh + bt - 1) / bt) * (p.d / bt) * std::max(1, p.n_inst);
   // Split count: the filled fraction of the last round of (one-per-CU)
   // workgroups, minus a charge per split for the partial set it writes and
   // the optimiser re-reads (3D^2 fp32 per instance, against ~5DC bf16 of E
@@ -254,8 +254,8 @@ int upd_bj(const lact_problem& p, int64_t C) {
   const bool direct = profile_of(p) == PBF16;
   for (int bj : {128, 96, 64}) {
     if (bj == 128 || (!direct && bj != 64)) continue;
-    if (p.d % bj) continue;
-    const int64_t wgs = tt * (p.d / bj) * p.n_inst;
+    if (p.dh % bj) continue;
+    const int64_t wgs = tt * (p.dh / bj) * p.n_inst;
     const int64_t rounds = (wgs + 255) / 256;
     const double eff = (double)wgs / (double)(rounds * 256);
     if (eff > best_eff + 1e-9) {
@@ -285,7 +285,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 Ws layout(const lact_problem& p, const Plan& plan) {
   Ws w;
   const Prof f = profile_of(p);
-  const size_t n = (size_t)std::max(0, p.n_inst), D = (size_t)p.d;
+  const size_t n = (size_t)std::max(0, p.n_inst), D = (size_t)p.d, Dh = (size_t)p.dh;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -312,10 +312,10 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   w.h_rows = h_rows;
   w.max_tt = (int)((plan.max_upd + FBT - 1) / FBT);
   const size_t snap_el = (f == PF32) ? 4 : 2;
-  w.snap_slot = align256(4 * n * D * D * snap_el);
-  w.e = take(n * 3 * D * (size_t)w.ldE * rec_size(f));
-  w.h = take(n * (size_t)h_rows * D * app_size(f));
-  const size_t mats = n * 3 * D * D * sizeof(float);
+  w.snap_slot = align256(4 * n * D * Dh * snap_el);
+  w.e = take(n * 3 * Dh * (size_t)w.ldE * rec_size(f));
+  w.h = take(n * (size_t)h_rows * Dh * app_size(f));
+  const size_t mats = n * 3 * D * Dh * sizeof(float);
   w.part = take(plan.max_upd > 0 ? (size_t)S * mats : 0);
   w.bpart = take(uses_momentum(p.opt) ? n * (size_t)w.max_tt * sizeof(float) : 0);
   w.snap = take(w.snap_slot * (size_t)w.nslots);
@@ -341,14 +341,17 @@ Ws layout(const lact_problem& p, const Plan& plan) {
 lact_status validate_problem(const lact_problem* p) {
   if (!p) return fail(LACT_ERR_INVALID_ARG, "problem is NULL");
   if (p->n_inst < 0) return fail(LACT_ERR_INVALID_ARG, "n_inst = %d < 0", p->n_inst);
-  if (p->d != p->dh) return fail(LACT_ERR_UNSUPPORTED, "d = %d != dh = %d", p->d, p->dh);
   if (p->d < 64 || p->d > 1024 || p->d % 64 != 0)
     return fail(LACT_ERR_UNSUPPORTED, "d = %d: need a multiple of 64 in [64, 1024]", p->d);
+  if (p->dh < 64 || p->dh > 1024 || p->dh % 64 != 0)
+    return fail(LACT_ERR_UNSUPPORTED, "dh = %d: need a multiple of 64 in [64, 1024]", p->dh);
   if (p->io_dtype != LACT_DTYPE_F32 && p->io_dtype != LACT_DTYPE_BF16)
     return fail(LACT_ERR_INVALID_ARG, "io_dtype = %d", p->io_dtype);
   if (p->opt < LACT_OPT_GD || p->opt > LACT_OPT_MUON_MOMENTUM) return fail(LACT_ERR_INVALID_ARG, "opt = %d", p->opt);
   if (uses_ns(p->opt) && (p->ns_iters < 1 || p->ns_iters > 16))
     return fail(LACT_ERR_INVALID_ARG, "ns_iters = %d: need 1..16", p->ns_iters);
+  if (uses_ns(p->opt) && p->d != p->dh)
+    return fail(LACT_ERR_UNSUPPORTED, "Newton-Schulz optimisers need d == dh (d = %d, dh = %d)", p->d, p->dh);
   if (p->rec_planes < 0 || p->rec_planes > 3) return fail(LACT_ERR_INVALID_ARG, "rec_planes = %d", p->rec_planes);
   if (p->flags & ~(LACT_NO_RENORM | LACT_QK_PREP)) return fail(LACT_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   return LACT_OK;
@@ -552,10 +555,10 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
   using TS = typename PT::TS;
   using TREC = typename PT::TREC;
   using TAPP = typename PT::TAPP;
-  const int n = p.n_inst, D = p.d;
+  const int n = p.n_inst, D = p.d, Dh = p.dh;
   if (n == 0) return LACT_OK;
   const bool part16 = PT::PREC == 1 && !uses_ns(p.opt);
-  const int64_t DD = (int64_t)D * D;
+  const int64_t DD = (int64_t)D * Dh;   // elements per fast-weight matrix
   const int64_t x_bs = seq_stride * D;
   char* ws = P.ws;
   const size_t snap_mat = (size_t)n * DD * sizeof(TS);
@@ -600,7 +603,8 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     const int64_t n4 = (int64_t)n * DD / 4;
     KernelTimer kt(LACT_K_SNAP, s);
     LACT_LAUNCH(snap_kernel<TS>, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), s, P.W1, P.W2, P.W3,
-                       slot(0, 0), slot(0, 1), slot(0, 2), sizeof(TS) == 2 ? slot(0, 3) : nullptr, (int64_t)n * DD, D);
+                       slot(0, 0), slot(0, 1), slot(0, 2), sizeof(TS) == 2 ? slot(0, 3) : nullptr, (int64_t)n * DD, D,
+                       Dh);
     HIP_TRY(hipGetLastError());
   }
 
@@ -633,12 +637,13 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     ua.E = ws + w.e;
     ua.ldE = round128(C);
     ua.D = D;
+    ua.Dh = Dh;
     ua.upd_t0 = st.upd_t0;
     ua.upd_len = C;
     ua.tiles_t = (int)((C + FBT - 1) / FBT);
     {
       const int bj = upd_bj(p, C);
-      const int64_t grid = (int64_t)n * ua.tiles_t * (D / bj);
+      const int64_t grid = (int64_t)n * ua.tiles_t * (Dh / bj);
       if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
       KernelTimer kt(LACT_K_UPD, s);
       lact_status r = bj == 128 ? launch_upd_fwd<PT, 128>(ua, grid, s)
@@ -655,11 +660,12 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       GemmArgs g = gemm_args();
       g.g[0].A = ws + w.e;         // (m, t) = E[m, t]: rows U1 | U3 | U2^T terms
       g.lda = ua.ldE;
-      g.a_bs = 3 * D * ua.ldE;
+      g.a_bs = 3 * Dh * ua.ldE;
       g.g[0].B = static_cast<const char*>(kx) + (size_t)st.upd_t0 * D * io_size(p);
       g.B2 = static_cast<const char*>(P.v) + (size_t)st.upd_t0 * D * io_size(p);
-      g.m_switch = 2 * D;
-      g.trans_from = 2 * D;        // the U2 block is stored as U2 (not U2^T)
+      g.m_switch = 2 * Dh;
+      g.trans_from = 2 * Dh;       // the U2 block is stored as U2 [d, dh] (not U2^T)
+      g.ldc_t = Dh;
       g.ldb = D;
       g.b_bs = k_bs;
       g.b2_bs = x_bs;
@@ -667,7 +673,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       g.ldc = D;
       g.c_bs = 3 * DD;
       g.c_ss = (int64_t)n * 3 * DD;
-      g.g[0].M = 3 * D;
+      g.g[0].M = 3 * Dh;
       g.N = D;
       g.K = C;
       g.kps = kps;
@@ -688,7 +694,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     oa.M[0] = P.M1;
     oa.M[1] = P.M3;
     oa.M[2] = P.M2;
-    oa.D = D;
+    oa.mat_el = DD;
     oa.opt = p.opt;
     oa.renorm = (p.flags & LACT_NO_RENORM) ? 0 : 1;
     oa.bpart = reinterpret_cast<const float*>(ws + w.bpart);
@@ -786,11 +792,18 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       oa.src_ss = 0;
       oa.splits = 1;
     }
-    {
+    // one launch when the three matrices share their shape, else W1 and W3
+    // (dh rows of d) and W2 (d rows of dh) separately
+    const int nparts = D == Dh ? 1 : 2;
+    for (int part = 0; part < nparts; ++part) {
       KernelTimer kt(LACT_K_OPT, s);
-      oa.rpw = opt_rpw(D);
-      const dim3 og((unsigned)(n * 3 * (D / (4 * oa.rpw))));
-      const int vpl = (oa.rpw * D + 255) / 256;
+      oa.mat0 = part == 0 ? 0 : 2;
+      oa.nmat = nparts == 1 ? 3 : part == 0 ? 2 : 1;
+      oa.R = part == 0 ? Dh : D;
+      oa.L = part == 0 ? D : Dh;
+      oa.rpw = opt_rpw(oa.L);
+      const dim3 og((unsigned)(n * oa.nmat * (oa.R / (4 * oa.rpw))));
+      const int vpl = (oa.rpw * oa.L + 255) / 256;
       if (part16) {
         if (vpl == 1) LACT_LAUNCH((opt_kernel<TS, 1, bf16_t>), og, dim3(NT), s, oa);
         else if (vpl == 2) LACT_LAUNCH((opt_kernel<TS, 2, bf16_t>), og, dim3(NT), s, oa);
@@ -828,8 +841,9 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       if (st.upd_len > 0) ++u;
     }
   }
-  // the fp32 register-path apply tile spills at 128 hidden columns
-  const int abj = (D % 128 == 0 && profile_of(p) != PF32) ? 128 : 64;
+  // the column block serves both the forward (dh columns) and the output
+  // mode (d columns); the fp32 register-path apply tile spills at 128
+  const int abj = (D % 128 == 0 && Dh % 128 == 0 && profile_of(p) != PF32) ? 128 : 64;
   for (size_t g0 = 0; g0 < groups.size(); g0 += MAXG) {
     const int ng = (int)std::min<size_t>(MAXG, groups.size() - g0);
     AppFwdArgs aa;
@@ -841,26 +855,34 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     aa.oz = P.oz;
     aa.oz_bs = seq_stride;
     aa.H = ws + w.h;
-    aa.h_bs = w.h_rows * D;
+    aa.h_bs = w.h_rows * Dh;
     aa.D = D;
+    aa.Dh = Dh;
+    // workgroups per group: token tiles x column blocks (cols wide) x instances
+    auto set_tiles = [&](int cols, int64_t& grid) -> lact_status {
+      grid = 0;
+      for (int i = 0; i < ng; ++i) {
+        const int64_t t = ((aa.g[i].len + FBT - 1) / FBT) * (cols / abj) * n;
+        if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+        aa.g[i].tiles = (int)t;
+        grid += t;
+      }
+      if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+      return LACT_OK;
+    };
+    for (int i = 0; i < ng; ++i) aa.g[i] = groups[g0 + i];
     int64_t grid = 0;
-    for (int i = 0; i < ng; ++i) {
-      aa.g[i] = groups[g0 + i];
-      const int64_t t = ((aa.g[i].len + FBT - 1) / FBT) * (D / abj) * n;
-      if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
-      aa.g[i].tiles = (int)t;
-      grid += t;
-    }
-    if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+    if (lact_status r = set_tiles(Dh, grid)) return r;
     {
       KernelTimer kt(LACT_K_APP, s);
       lact_status r = abj == 128 ? launch_app_fwd<PT, 128>(aa, grid, s) : launch_app_fwd<PT, 64>(aa, grid, s);
       if (r) return r;
     }
     // o[t, r] = sum_j Hq[t, j] W2[r, j]: the apply tile in output mode
-    // (same grid), or the generic GEMM for profiles without a bf16 path
+    // (d column blocks), or the generic GEMM for profiles without a bf16 path
     {
       aa.o = P.o;
+      if (lact_status r = set_tiles(D, grid)) return r;
       lact_status st = LACT_OK;
       bool done;
       {
@@ -877,7 +899,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     int64_t wgs128 = 0;
     for (int i = 0; i < ng; ++i) {
       const AppGroup& ag = aa.g[i];
-      g.g[i].A = static_cast<const char*>(aa.H) + (size_t)ag.h0 * D * app_size(profile_of(p));
+      g.g[i].A = static_cast<const char*>(aa.H) + (size_t)ag.h0 * Dh * app_size(profile_of(p));
       int u = 0;
       // the snapshot this group reads is the one its W1 came from
       for (int k = 0; k < w.nslots; ++k)
@@ -888,15 +910,15 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       g.g[i].M = (int)ag.len;
       wgs128 += ((ag.len + 127) / 128) * std::max(1, D / 128) * n;
     }
-    g.lda = D;
-    g.a_bs = w.h_rows * D;
-    g.ldb = D;
+    g.lda = Dh;
+    g.a_bs = w.h_rows * Dh;
+    g.ldb = Dh;          // W2 [d, dh]: row n = output unit n
     g.b_bs = DD;
     g.ldc = D;
     g.c_bs = x_bs;
     g.rs_bs = seq_stride;
     g.N = D;
-    g.K = g.kps = D;
+    g.K = g.kps = Dh;
     g.batch = n;
     lact_status r =
         launch_gemm<TAPP, PT::PAPP, false, TS, PT::PS, false, TIO>(g, gemm_tile(wgs128), LACT_K_OUT, s);

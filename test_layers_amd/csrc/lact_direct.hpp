@@ -403,7 +403,8 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
       if (trans) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          io_traits<TC>::store(C + (int64_t)(g.trans_from + nq + r) * g.ldc + (m - g.trans_from), val[r]);
+          io_traits<TC>::store(C + (int64_t)g.trans_from * g.ldc + (int64_t)(nq + r) * g.ldc_t + (m - g.trans_from),
+                               val[r]);
       } else {
         store4(C + (int64_t)m * g.ldc + nq, val);
       }
@@ -441,8 +442,8 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int D = a.D;
-  const int njb = D / BJ;
+  const int D = a.D, Dh = a.Dh;
+  const int njb = Dh / BJ;
   const int per_inst = a.tiles_t * njb;
   const int lbid = xcd_remap(blockIdx.x, gridDim.x);
   const int inst = lbid / per_inst;
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   const int64_t t0 = a.upd_t0 + (int64_t)tb * FBT;
   const int64_t tend = a.upd_t0 + a.upd_len;
   const int j0 = jb * BJ;
-  const int64_t DD = (int64_t)D * D;
+  const int64_t DD = (int64_t)D * Dh;
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + inst * a.k_bs;
   const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + inst * a.x_bs;
   const bf16_t* W1 = reinterpret_cast<const bf16_t*>(a.W1) + inst * DD;
@@ -470,9 +471,10 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   const bool wload = wave < WW;
   const typename TX::Plan pk = TX::plan(K, D, t0, tend - 1, 0, wave, lane);
   const typename TX::Plan pv = TX::plan(V, D, t0, tend - 1, 0, wave, lane);
-  const typename TW::Plan p1 = TW::plan(W1, D, j0, D - 1, 0, wload ? wave : 0, lane);
-  const typename TW::Plan p3 = TW::plan(W3, D, j0, D - 1, 0, wload ? wave : 0, lane);
-  const typename TW::Plan p2 = TW::plan(W2T, D, j0, D - 1, 0, wload ? wave : 0, lane);
+  // W1, W3 and W2^T rows: hidden units j0 .. j0 + BJ - 1 (of dh), d long
+  const typename TW::Plan p1 = TW::plan(W1, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
+  const typename TW::Plan p3 = TW::plan(W3, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
+  const typename TW::Plan p2 = TW::plan(W2T, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
   auto issue_one = [&](int s, int buf, int idx) {
     char* st = smem + buf * STAGE;
     const int64_t off = (int64_t)s * BKK * 2;
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   __syncthreads();
   // E rows U1 | U3 | U2-terms, token-fastest; the tile's 128 tokens lie
   // inside the row's ldE (zero terms past the chunk end)
-  bf16_t* E = reinterpret_cast<bf16_t*>(a.E) + inst * 3 * (int64_t)D * a.ldE + (t0 - a.upd_t0);
+  bf16_t* E = reinterpret_cast<bf16_t*>(a.E) + inst * 3 * (int64_t)Dh * a.ldE + (t0 - a.upd_t0);
   constexpr int ROWS = 3 * BJ;
   for (int r0 = 0; r0 < ROWS; r0 += 4 * NWV) {
     const int row = r0 + wave * 4 + (lane >> 4);
@@ -581,7 +583,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
       const int c = lane & 15;
       const uint4 v = *reinterpret_cast<const uint4*>(et + row * (FBT * 2) + ((c ^ (row & 15)) << 4));
       const int m = row / BJ, col = row % BJ;
-      *reinterpret_cast<uint4*>(E + (int64_t)(m * D + j0 + col) * a.ldE + c * 8) = v;
+      *reinterpret_cast<uint4*>(E + (int64_t)(m * Dh + j0 + col) * a.ldE + c * 8) = v;
     }
   }
 }
@@ -602,12 +604,15 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int D = a.D;
+  const int D = a.D, Dh = a.Dh;
+  // forward: contraction over d, output columns = hidden units (dh);
+  // output mode: contraction over dh, output columns = o's d features
+  const int KLEN = OUT ? Dh : D, NCOL = OUT ? D : Dh;
   int bid = xcd_remap(blockIdx.x, gridDim.x);
   int gi = 0;
   while (gi + 1 < a.ngroups && bid >= a.g[gi].tiles) bid -= a.g[gi++].tiles;
   const AppGroup& G = a.g[gi];
-  const int njb = D / BJ;
+  const int njb = NCOL / BJ;
   const int tiles_t = (int)((G.len + FBT - 1) / FBT);
   const int per_inst = tiles_t * njb;
   const int inst = bid / per_inst;
@@ -616,7 +621,7 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
   const int64_t t0 = G.t0 + (int64_t)tb * FBT;
   const int64_t tend = G.t0 + G.len;
   const int j0 = jb * BJ;
-  const int64_t DD = (int64_t)D * D;
+  const int64_t DD = (int64_t)D * Dh;
   // A operand rows: queries (q rows t) or their gated hidden (Hq rows h0 + t - t0)
   const bf16_t* X = OUT ? reinterpret_cast<const bf16_t*>(a.H) + inst * a.h_bs
                         : reinterpret_cast<const bf16_t*>(a.q) + inst * a.q_bs;
@@ -625,9 +630,9 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
   const bf16_t* B1 = reinterpret_cast<const bf16_t*>(OUT ? G.W2 : G.W1) + inst * DD;
   const bf16_t* B3 = reinterpret_cast<const bf16_t*>(G.W3) + inst * DD;
 
-  const typename TX::Plan pq = TX::plan(X, D, xr0, xrmax, 0, wave, lane);
-  const typename TW::Plan p1 = TW::plan(B1, D, j0, D - 1, 0, wave, lane);
-  const typename TW::Plan p3 = TW::plan(OUT ? B1 : B3, D, j0, D - 1, 0, wave, lane);
+  const typename TX::Plan pq = TX::plan(X, KLEN, xr0, xrmax, 0, wave, lane);
+  const typename TW::Plan p1 = TW::plan(B1, KLEN, j0, NCOL - 1, 0, wave, lane);
+  const typename TW::Plan p3 = TW::plan(OUT ? B1 : B3, KLEN, j0, NCOL - 1, 0, wave, lane);
   auto issue_one = [&](int s, int buf, int idx) {
     char* st = smem + buf * STAGE;
     const int64_t off = (int64_t)s * BKK * 2;
@@ -664,7 +669,7 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
       }
     }
   };
-  dpipeline_il<NST, LPS>(D / BKK, issue_one, compute);
+  dpipeline_il<NST, LPS>(KLEN / BKK, issue_one, compute);
 
   // output rows: o rows t, or Hq rows h0 + t - t0
   bf16_t* Y = OUT ? reinterpret_cast<bf16_t*>(a.o) + inst * a.x_bs : reinterpret_cast<bf16_t*>(a.H) + inst * a.h_bs;
@@ -672,7 +677,7 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int64_t t = t0 + wm * 64 + i * 16 + (lane & 15);
     if (t >= tend) continue;
-    bf16_t* Yr = Y + (OUT ? t : G.h0 + (t - G.t0)) * (int64_t)D;
+    bf16_t* Yr = Y + (OUT ? t : G.h0 + (t - G.t0)) * (int64_t)NCOL;
     // per-token output scale (output mode only)
     const float ys = (OUT && a.oz != nullptr) ? silu(a.oz[inst * a.oz_bs + t]) : 1.f;
 #pragma unroll

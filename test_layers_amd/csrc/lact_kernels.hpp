@@ -44,12 +44,13 @@ struct UpdFwdArgs {
   const float* beta;     // momentum: per-token beta (partial sums per token block), else null
   int64_t beta_bs;
   float* bpart;          // [n, tiles_t] beta partial sums
-  const void* W1;        // [n, D, D] (bf16 snapshot or fp32 master)
+  const void* W1;        // [n, dh, d] (bf16 snapshot or fp32 master)
   const void* W3;
   const void* W2x;       // bf16: W2^T snapshot [n, dh, d]; fp32: W2 master [n, d, dh]
-  void* E;               // [n, 3D, ldE] update terms, token-fastest: rows U1 | U3 | U2^T terms
+  void* E;               // [n, 3 dh, ldE] update terms, token-fastest: rows U1 | U3 | U2^T terms
   int64_t ldE;
-  int D;
+  int D;                 // d: width of k, v (the products' contraction)
+  int Dh;                // dh: hidden width (the products' output columns)
   int64_t upd_t0;
   int64_t upd_len;
   int tiles_t;           // token blocks per instance
@@ -71,8 +72,8 @@ __global__ __launch_bounds__(NT) void upd_fwd_kernel(UpdFwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int D = a.D;
-  const int njb = D / BJ;
+  const int D = a.D, Dh = a.Dh;
+  const int njb = Dh / BJ;
   const int per_inst = a.tiles_t * njb;
   const int lbid = xcd_remap(blockIdx.x, gridDim.x);
   const int inst = lbid / per_inst;
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(NT) void upd_fwd_kernel(UpdFwdArgs a) {
   const int64_t t0 = a.upd_t0 + (int64_t)tb * FBT;
   const int64_t tend = a.upd_t0 + a.upd_len;
   const int j0 = jb * BJ;
-  const int64_t DD = (int64_t)D * D;
+  const int64_t DD = (int64_t)D * Dh;
   const TIO* K = reinterpret_cast<const TIO*>(a.k) + inst * a.k_bs;
   const TIO* V = reinterpret_cast<const TIO*>(a.v) + inst * a.x_bs;
   const TW* W1 = reinterpret_cast<const TW*>(a.W1) + inst * DD;
@@ -112,9 +113,9 @@ __global__ __launch_bounds__(NT) void upd_fwd_kernel(UpdFwdArgs a) {
     const int k0 = kt * BK;
     LK[r].load(K, D, t0, tend, k0, tid);
     LV[r].load(V, D, t0, tend, k0, tid);
-    L1[r].load(W1, D, j0, D, k0, tid);
-    L3[r].load(W3, D, j0, D, k0, tid);
-    load_tile<TW, PW, BJ, BK, W2COL>(L2[r], W2, D, j0, D, k0, D, tid);
+    L1[r].load(W1, D, j0, Dh, k0, tid);
+    L3[r].load(W3, D, j0, Dh, k0, tid);
+    load_tile<TW, PW, BJ, BK, W2COL>(L2[r], W2, W2COL ? Dh : D, j0, Dh, k0, D, tid);
   };
   auto put = [&](auto set, auto buf) {
     constexpr int r = decltype(set)::value;
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(NT) void upd_fwd_kernel(UpdFwdArgs a) {
 
   // SwiGLU backward epilogue; every token of the padded row is written (zeros
   // past the chunk end) so the contraction can read whole 16-byte vectors.
-  TREC* E = reinterpret_cast<TREC*>(a.E) + inst * 3 * (int64_t)D * a.ldE;
+  TREC* E = reinterpret_cast<TREC*>(a.E) + inst * 3 * (int64_t)Dh * a.ldE;
   const float* lr = a.lr + inst * a.lr_bs;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -174,8 +175,8 @@ __global__ __launch_bounds__(NT) void upd_fwd_kernel(UpdFwdArgs a) {
         u2[r] = e2[r] * s * b;
       }
       store4(E + (int64_t)col * a.ldE + trel, u1);
-      store4(E + (int64_t)(D + col) * a.ldE + trel, u3);
-      store4(E + (int64_t)(2 * D + col) * a.ldE + trel, u2);
+      store4(E + (int64_t)(Dh + col) * a.ldE + trel, u3);
+      store4(E + (int64_t)(2 * Dh + col) * a.ldE + trel, u2);
     }
   }
 }
@@ -188,7 +189,7 @@ struct AppGroup {
   int64_t t0;            // first token of the group's apply range
   int64_t len;
   int64_t h0;            // row offset of the group in the Hq buffer
-  const void* W1;        // snapshot [n, D, D]
+  const void* W1;        // snapshot [n, dh, d] (W3 alike; W2 [n, d, dh])
   const void* W3;
   const void* W2;
   int tiles;             // workgroups of this group
@@ -200,12 +201,13 @@ struct AppFwdArgs {
   const void* q;
   int64_t q_bs;          // elements between instances in q
   int64_t x_bs;          // elements between instances in o
-  void* H;               // [n, h_rows, D]
+  void* H;               // [n, h_rows, dh]
   int64_t h_bs;
-  void* o;               // output mode: [n, seq, D] (x_bs per instance)
+  void* o;               // output mode: [n, seq, d] (x_bs per instance)
   const float* oz;       // output mode: o[t, :] *= silu(oz[t]) (NULL: no scale)
   int64_t oz_bs;
-  int D;
+  int D;                 // d: width of q and o
+  int Dh;                // dh: hidden width
 };
 
 template <typename TIO, int PIO, typename TW, int PW, typename TAPP, int BJ, int BK, int STAGES>
@@ -217,12 +219,12 @@ __global__ __launch_bounds__(NT) void app_fwd_kernel(AppFwdArgs a) {
   constexpr int FN = BJ / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int D = a.D;
+  const int D = a.D, Dh = a.Dh;
   int bid = xcd_remap(blockIdx.x, gridDim.x);
   int gi = 0;
   while (gi + 1 < a.ngroups && bid >= a.g[gi].tiles) bid -= a.g[gi++].tiles;
   const AppGroup& G = a.g[gi];
-  const int njb = D / BJ;
+  const int njb = Dh / BJ;
   const int tiles_t = (int)((G.len + FBT - 1) / FBT);
   const int per_inst = tiles_t * njb;
   const int inst = bid / per_inst;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(NT) void app_fwd_kernel(AppFwdArgs a) {
   const int64_t t0 = G.t0 + (int64_t)tb * FBT;
   const int64_t tend = G.t0 + G.len;
   const int j0 = jb * BJ;
-  const int64_t DD = (int64_t)D * D;
+  const int64_t DD = (int64_t)D * Dh;
   const TIO* Q = reinterpret_cast<const TIO*>(a.q) + inst * a.q_bs;
   const TW* W1 = reinterpret_cast<const TW*>(G.W1) + inst * DD;
   const TW* W3 = reinterpret_cast<const TW*>(G.W3) + inst * DD;
@@ -247,8 +249,8 @@ __global__ __launch_bounds__(NT) void app_fwd_kernel(AppFwdArgs a) {
     constexpr int r = decltype(set)::value;
     const int k0 = kt * BK;
     LQ[r].load(Q, D, t0, tend, k0, tid);
-    L1[r].load(W1, D, j0, D, k0, tid);
-    L3[r].load(W3, D, j0, D, k0, tid);
+    L1[r].load(W1, D, j0, Dh, k0, tid);
+    L3[r].load(W3, D, j0, Dh, k0, tid);
   };
   auto put = [&](auto set, auto buf) {
     constexpr int r = decltype(set)::value;
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(NT) void app_fwd_kernel(AppFwdArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int64_t t = t0 + wm * 64 + i * 16 + (lane & 15);
     if (t >= tend) continue;
-    TAPP* Hr = H + (G.h0 + (t - G.t0)) * (int64_t)D;
+    TAPP* Hr = H + (G.h0 + (t - G.t0)) * (int64_t)Dh;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = j0 + wn * (BJ / 2) + j * 16 + 4 * (lane >> 4);
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(NT) void app_fwd_kernel(AppFwdArgs a) {
 // Groups share every stride and N, K; each has its own A, B, C and M.  K may
 // be split: split s covers k in [s*kps, min(K, (s+1)*kps)) and writes its
 // own partial C + s * c_ss.  Rows m >= trans_from are stored transposed into
-// the square block that starts at row trans_from.
+// the block that starts at element trans_from * ldc, with row stride ldc_t.
 struct GemmGroup {
   const void* A;
   const void* B;
@@ -316,6 +318,7 @@ struct GemmArgs {
   int64_t rs_bs;
   int m_switch;
   int trans_from;
+  int64_t ldc_t;         // row stride of the transposed block
   const float* Cin;
   int64_t ldcin, cin_bs;
   int N;
@@ -433,7 +436,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
         // row m of the block is stored as column m - trans_from
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          io_traits<TC>::store(C + (int64_t)(g.trans_from + nq + r) * g.ldc + (m - g.trans_from), val[r]);
+          io_traits<TC>::store(C + (int64_t)g.trans_from * g.ldc + (int64_t)(nq + r) * g.ldc_t + (m - g.trans_from),
+                               val[r]);
       } else {
         store4(C + (int64_t)m * g.ldc + nq, val);
       }
@@ -496,8 +500,10 @@ __global__ __launch_bounds__(NT) void reduce_rows_kernel(const float* P, int64_t
 
 // =========================================================================
 // optimiser step + row renormalisation + snapshot of the new weights.
-// src: per instance the stacked direction [U1; U3; U2] ([3D, D], natural
-// layouts) as `splits` partials summed in order.  One wave per row.
+// src: per instance the stacked direction [U1; U3; U2] (three d x dh blocks
+// in natural layouts: U1, U3 [dh, d], U2 [d, dh]) as `splits` partials
+// summed in order.  One wave per row; a launch covers matrices mat0 ..
+// mat0 + nmat - 1, which share their row count and length.
 struct OptArgs {
   const void* src;       // partials (fp32, or bf16 in the plain-bf16 recurrence) or Muon's direction
   int64_t src_ss;        // elements between partials
@@ -507,8 +513,11 @@ struct OptArgs {
   const float* bpart;    // momentum: beta partial sums [n, nbp]
   int nbp;
   float inv_len;         // 1 / chunk length
-  int D;
-  int rpw;               // rows per wave: 4 (D <= 256), 2 (D <= 512) or 1
+  int R;                 // rows of each matrix handled (dh for W1, W3; d for W2)
+  int L;                 // row length (d for W1, W3; dh for W2)
+  int mat0, nmat;        // matrices mat0 .. mat0 + nmat - 1 of the stacked source
+  int64_t mat_el;        // elements per matrix (d * dh)
+  int rpw;               // rows per wave: 4 (L <= 256), 2 (L <= 512) or 1
   int opt;               // 0 GD, 1 momentum, 2 Muon, 3 momentum + Muon
   int renorm;
   // snapshot of the new weights (bf16 or fp32, natural layout) and, for
@@ -519,27 +528,27 @@ struct OptArgs {
 
 constexpr int OPT_MAXS = 4;               // partials loaded per batch
 
-__host__ __device__ constexpr int opt_rpw(int D) { return D <= 256 ? 4 : D <= 512 ? 2 : 1; }
+__host__ __device__ constexpr int opt_rpw(int L) { return L <= 256 ? 4 : L <= 512 ? 2 : 1; }
 
 // Optimiser step, one matrix row block per workgroup.  A wave owns rpw
-// consecutive rows, i.e. one contiguous span of rpw * D floats that its lanes
+// consecutive rows, i.e. one contiguous span of rpw * L floats that its lanes
 // cover with VPL float4 each (lane + 64 i); lanes past the span load its last
 // float4 (always in bounds) and drop it, so every load is a plain 16-byte
 // load issued before any arithmetic consumes it.  Row sums of squares are
 // wave reductions per row.
 template <typename TS, int VPL, typename TP = float>
 __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
-  __shared__ uint16_t s_t[4096];   // transposed-snapshot staging: rows_wg x D bf16 (rows_wg * D <= 4096)
+  __shared__ uint16_t s_t[4096];   // transposed-snapshot staging: rows_wg x L bf16 (rows_wg * L <= 4096)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int D = a.D, rpw = a.rpw, rows_wg = 4 * rpw;
-  const int rblocks = D / rows_wg;
+  const int L = a.L, R = a.R, rpw = a.rpw, rows_wg = 4 * rpw;
+  const int rblocks = R / rows_wg;
   int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int rb = bid % rblocks;
   bid /= rblocks;
-  const int mat = bid % 3;
-  const int inst = bid / 3;
-  const int64_t DD = (int64_t)D * D;
-  const int nv = D / 4;
+  const int mat = a.mat0 + bid % a.nmat;
+  const int inst = bid / a.nmat;
+  const int64_t DD = a.mat_el;
+  const int nv = L / 4;
   const int span = rpw * nv;
   const int row0 = rb * rows_wg + wave * rpw;
   const int64_t base4 = (int64_t)row0 * nv;
@@ -656,19 +665,20 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
   }
   if constexpr (sizeof(TS) == 2) {
     if (stage_t) {
-      // W2^T[j, r0 .. r0 + rows_wg - 1]: rows_wg contiguous bf16 per j
+      // W2^T[j, r0 .. r0 + rows_wg - 1] (W2^T is [dh, d]: L rows of R):
+      // rows_wg contiguous bf16 per j
       __syncthreads();
       uint16_t* T = reinterpret_cast<uint16_t*>(a.snapT2) + inst * DD + rb * rows_wg;
       if (rows_wg == 4) {
-        for (int j = tid; j < D; j += NT)
-          *reinterpret_cast<uint2*>(T + (int64_t)j * D) = *reinterpret_cast<const uint2*>(s_t + j * 4);
+        for (int j = tid; j < L; j += NT)
+          *reinterpret_cast<uint2*>(T + (int64_t)j * R) = *reinterpret_cast<const uint2*>(s_t + j * 4);
       } else if (rows_wg == 8) {
-        for (int j = tid; j < D; j += NT)
-          *reinterpret_cast<uint4*>(T + (int64_t)j * D) = *reinterpret_cast<const uint4*>(s_t + j * 8);
+        for (int j = tid; j < L; j += NT)
+          *reinterpret_cast<uint4*>(T + (int64_t)j * R) = *reinterpret_cast<const uint4*>(s_t + j * 8);
       } else {
-        for (int j = tid; j < D; j += NT) {
-          *reinterpret_cast<uint4*>(T + (int64_t)j * D) = *reinterpret_cast<const uint4*>(s_t + j * 16);
-          *reinterpret_cast<uint4*>(T + (int64_t)j * D + 8) = *reinterpret_cast<const uint4*>(s_t + j * 16 + 8);
+        for (int j = tid; j < L; j += NT) {
+          *reinterpret_cast<uint4*>(T + (int64_t)j * R) = *reinterpret_cast<const uint4*>(s_t + j * 16);
+          *reinterpret_cast<uint4*>(T + (int64_t)j * R + 8) = *reinterpret_cast<const uint4*>(s_t + j * 16 + 8);
         }
       }
     }
@@ -743,7 +753,7 @@ __global__ __launch_bounds__(NT) void qk_prep_kernel(QkPrepArgs a) {
 // snapshot of caller weights: fp32 -> TS (natural) and, for bf16, W2^T
 template <typename TS>
 __global__ __launch_bounds__(NT) void snap_kernel(const float* W1, const float* W2, const float* W3, void* s1,
-                                                   void* s2, void* s3, void* sT2, int64_t n_dd, int D) {
+                                                   void* s2, void* s3, void* sT2, int64_t n_dd, int D, int Dh) {
   const int64_t i4 = (int64_t)blockIdx.x * NT + threadIdx.x;   // float4 index
   if (i4 * 4 >= n_dd) return;
   const float* src[3] = {W1, W2, W3};
@@ -759,9 +769,10 @@ __global__ __launch_bounds__(NT) void snap_kernel(const float* W1, const float* 
       const float4 x = reinterpret_cast<const float4*>(W2)[i4];
       const float v[4] = {x.x, x.y, x.z, x.w};
       const int64_t e = i4 * 4;
-      const int64_t DD = (int64_t)D * D;
+      // W2 is [d, dh]; W2^T is [dh, d]
+      const int64_t DD = (int64_t)D * Dh;
       const int64_t inst = e / DD, rem = e % DD;
-      const int r = (int)(rem / D), c = (int)(rem % D);
+      const int r = (int)(rem / Dh), c = (int)(rem % Dh);
       uint16_t* T = reinterpret_cast<uint16_t*>(sT2) + inst * DD;
 #pragma unroll
       for (int q = 0; q < 4; ++q) T[(int64_t)(c + q) * D + r] = (uint16_t)f2bf(v[q]);

@@ -212,8 +212,9 @@ def layer_forward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, o=No
                   bounds=None, flags=None, rec_planes: int = 0, ns_iters: int = 5,
                   renorm: bool = True, qk_prep: bool = False, oz=None, workspace=None,
                   stream=None):
-    """q, k, v [n, L, D] (fp32 or bf16), lr [n, L, 3] fp32, beta [n, L] fp32
-    (momentum) or None, W1, W2, W3 [n, D, D] fp32 (updated in place), M1..M3
+    """q, k, v [n, L, d] (fp32 or bf16), lr [n, L, 3] fp32, beta [n, L] fp32
+    (momentum) or None, W1, W3 [n, dh, d] and W2 [n, d, dh] fp32 (updated in
+    place; dh is read from W1's shape), M1..M3
     (momentum state, updated in place).  qk_prep: q and k are raw (the library
     applies silu and the per-token L2 normalisation).  oz [n, L] fp32: the
     output rows are scaled by silu(oz) (lact_layer_forward_scaled).  Returns o
@@ -222,7 +223,7 @@ def layer_forward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, o=No
     torch = _torch()
     n, L, D = q.shape
     io = _io_dtype(q)
-    p = problem(n, D, io, opt, rec_planes, ns_iters, renorm, qk_prep=qk_prep)
+    p = problem(n, D, io, opt, rec_planes, ns_iters, renorm, dh=W1.shape[1], qk_prep=qk_prep)
     if o is None:
         o = torch.zeros_like(q)
     need = workspace_size(p, L, chunk, order, bounds, flags)
@@ -248,7 +249,7 @@ def chunk_update(k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, Lc: O
     torch = _torch()
     n, S, D = k.shape
     Lc = S if Lc is None else Lc
-    p = problem(n, D, _io_dtype(k), opt, rec_planes, ns_iters, renorm, qk_prep=qk_prep)
+    p = problem(n, D, _io_dtype(k), opt, rec_planes, ns_iters, renorm, dh=W1.shape[1], qk_prep=qk_prep)
     ws = _workspace(workspace_size(p, Lc, max(Lc, 1)), workspace, k.device)
     f32 = torch.float32
     check(chunk_update_ptr(p, _ptr(k, k.dtype, "k"), _ptr(v, k.dtype, "v"), _ptr(lr, f32, "lr"),
@@ -262,7 +263,7 @@ def apply(q, W1, W2, W3, o=None, *, Lq: Optional[int] = None, qk_prep: bool = Fa
     torch = _torch()
     n, S, D = q.shape
     Lq = S if Lq is None else Lq
-    p = problem(n, D, _io_dtype(q), OPT_GD, qk_prep=qk_prep)
+    p = problem(n, D, _io_dtype(q), OPT_GD, dh=W1.shape[1], qk_prep=qk_prep)
     if o is None:
         o = torch.zeros_like(q)
     ws = _workspace(workspace_size(p, Lq, max(Lq, 1)), workspace, q.device)

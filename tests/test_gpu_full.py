@@ -19,7 +19,7 @@ def lact():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
 def test_full_size_config(lact, cid):
     wl = W.CONFIGS[cid]
     t = time.time()

@@ -139,9 +139,10 @@ SMALL[6] = _small_prefill()
 SMALL[7] = _small_video_noisy_first()
 SMALL[8] = W.CONFIGS[8].scaled(n_inst=2, L=2 * 1024 + 300, chunk=1024)
 SMALL[9] = W.CONFIGS[9].scaled(n_inst=2, L=3 * 512 + 200, chunk=512)
+SMALL[10] = W.CONFIGS[10].scaled(n_inst=2, L=3 * 512 + 200, chunk=512)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
 def test_layer_reduced_size(lact, cid):
     wl = SMALL[cid]
     log(f"layer reduced cfg{cid}: n={wl.n_inst} D={wl.D} L={wl.L} chunks={wl.n_chunks}")
@@ -250,3 +251,75 @@ def test_chunk_entry_points_with_raw_qk_and_stride(lact, io):
         eo = max(eo, rel_err(g[i, :Lc], O.apply(Wg[0], Wg[1], Wg[2], qh)))
     log(f"  io={io} W err={ew:.2e} o err={eo:.2e}")
     assert max(ew, eo) <= _gate(io)
+
+
+# ------------------------------------------------------------------ rectangular fast weights (d != dh)
+def _rect_inputs(n, L, d, dh, io, seed):
+    import dataclasses
+    wl = dataclasses.replace(W.Workload(99, "unit", n, d, L, (0, L), (3,), 0, W.OPT_GD, io, True, 1,
+                                        _gate(io)), Dh=dh)
+    return W.generate(wl, seed=seed)
+
+
+@pytest.mark.parametrize("d,dh", [(128, 256), (384, 192), (64, 128)])
+@pytest.mark.parametrize("io", [W.DTYPE_F32, W.DTYPE_BF16])
+def test_apply_rectangular(lact, d, dh, io):
+    log(f"apply d={d} dh={dh} io={io}")
+    n, L = 2, 300
+    inp = _rect_inputs(n, L, d, dh, io, seed=d + dh + io)
+    q = to_dev(inp.q, torch)
+    Ws = [to_dev(w, torch) for w in (inp.W1, inp.W2, inp.W3)]
+    o = lact.apply(q, *Ws)
+    torch.cuda.synchronize()
+    g = from_dev(o, torch)
+    assert g.shape == (n, L, d)
+    err = max(rel_err(g[i], O.apply(O.f64(inp.W1[i]), O.f64(inp.W2[i]), O.f64(inp.W3[i]), O.f64(inp.q[i])))
+              for i in range(n))
+    log(f"  err={err:.3e}")
+    assert err <= _gate(io)
+
+
+@pytest.mark.parametrize("opt", [W.OPT_GD, W.OPT_MOMENTUM])
+@pytest.mark.parametrize("io,planes", [(W.DTYPE_F32, 3), (W.DTYPE_BF16, 1), (W.DTYPE_BF16, 2),
+                                       (W.DTYPE_BF16, 3)])
+@pytest.mark.parametrize("d,dh", [(128, 256), (192, 64)])
+def test_chunk_update_rectangular(lact, opt, io, planes, d, dh):
+    log(f"chunk_update d={d} dh={dh} opt={opt} io={io} planes={planes}")
+    n, Lc = 2, 300
+    inp = _rect_inputs(n, Lc, d, dh, io, seed=7 * d + dh + opt)
+    rng = np.random.default_rng(3)
+    beta = rng.uniform(0.5, 0.99, (n, Lc)).astype(np.float32)
+    M0 = [(rng.standard_normal(w.shape) * 0.01).astype(np.float32) for w in (inp.W1, inp.W2, inp.W3)]
+    k, v, lr = to_dev(inp.k, torch), to_dev(inp.v, torch), to_dev(inp.lr, torch)
+    Ws = [to_dev(w, torch).clone() for w in (inp.W1, inp.W2, inp.W3)]
+    mom = opt == W.OPT_MOMENTUM
+    Ms = [to_dev(m, torch).clone() for m in M0] if mom else [None] * 3
+    lact.chunk_update(k, v, lr, to_dev(beta, torch) if mom else None, *Ws, *Ms, opt=opt, rec_planes=planes)
+    torch.cuda.synchronize()
+    errs = {}
+    for i in range(n):
+        Wr, Mr = O.update_step([O.f64(inp.W1[i]), O.f64(inp.W2[i]), O.f64(inp.W3[i])],
+                               [O.f64(m[i]) for m in M0], O.f64(inp.k[i]), O.f64(inp.v[i]),
+                               O.f64(inp.lr[i]), O.f64(beta[i]), opt)
+        for j, nm in enumerate(["W1", "W2", "W3"]):
+            errs[nm] = max(errs.get(nm, 0), rel_err(from_dev(Ws[j], torch)[i], Wr[j]))
+            if mom:
+                errs["M" + nm[1]] = max(errs.get("M" + nm[1], 0), rel_err(from_dev(Ms[j], torch)[i], Mr[j]))
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    gate = _gate(io) if planes == 1 or io == W.DTYPE_F32 else 1e-3
+    assert max(errs.values()) <= gate, errs
+
+
+@pytest.mark.parametrize("io,planes", [(W.DTYPE_F32, 3), (W.DTYPE_BF16, 1), (W.DTYPE_BF16, 2)])
+def test_layer_rectangular_every_profile(lact, io, planes):
+    """The full layer with dh < d and dh > d (ragged last chunk), every profile."""
+    import dataclasses
+    for d, dh in [(128, 64), (64, 192)]:
+        wl = dataclasses.replace(W.CONFIGS[10].scaled(n_inst=2, L=700, chunk=256), D=d, Dh=dh, io_dtype=io,
+                                 rec_planes=planes, tol=_gate(io))
+        log(f"layer d={d} dh={dh} io={io} planes={planes}")
+        inp = W.generate(wl, seed=5)
+        gpu = run_gpu(wl, inp, torch, lact)
+        errs = compare(wl, inp, gpu)
+        log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+        assert max(errs.values()) <= wl.tol, errs

@@ -32,7 +32,7 @@ def _f64(t):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cid", [2, 3, 5, 8])
+@pytest.mark.parametrize("cid", [2, 3, 5, 8, 10])
 def test_teacher_forced_chunks(lact, cid):
     wl = W.CONFIGS[cid]
     assert wl.order == W.APPLY_THEN_UPDATE
@@ -46,7 +46,7 @@ def test_teacher_forced_chunks(lact, cid):
     mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
     Ms = [torch.zeros_like(w) for w in Ws] if mom else [None] * 3
     o = torch.zeros_like(q)
-    p = lact.problem(n, D, wl.io_dtype, wl.opt, wl.rec_planes)
+    p = lact.problem(n, D, wl.io_dtype, wl.opt, wl.rec_planes, dh=wl.dh)
     esz = q.element_size()
     C = wl.max_chunk
     ws = torch.empty(max(lact.workspace_size(p, C, C), 256), dtype=torch.uint8, device="cuda")
@@ -58,7 +58,7 @@ def test_teacher_forced_chunks(lact, cid):
         t0, t1 = wl.bounds[c], wl.bounds[c + 1]
         Lc = t1 - t0
         Wc = [[_f64(w[i]) for w in Ws] for i in inst]
-        Mc = [[_f64(m[i]) for m in Ms] if mom else [np.zeros((D, D))] * 3 for i in inst]
+        Mc = [[_f64(m[i]) for m in Ms] if mom else [np.zeros_like(w) for w in Wc[j]] for j, i in enumerate(inst)]
         if f & W.APPLY:   # apply-then-update: the chunk's queries read the weights before its update
             lact.check(lact.apply_ptr(p, q.data_ptr() + t0 * D * esz, Lc, L, *[w.data_ptr() for w in Ws],
                                       o.data_ptr() + t0 * D * esz, ws.data_ptr(), ws.numel(),

@@ -325,7 +325,7 @@ Ws layout(const lact_problem& p, const Plan& plan) {
     w.bm = take(mats);
     w.xa = take(mats);
     w.xb = take(mats);
-    w.rowsq = take(n * 3 * D * sizeof(float));
+    w.rowsq = take(n * (2 * Dh + D) * sizeof(float));
   }
   if (p.flags & LACT_QK_PREP) {
     const size_t el = f == PF32 ? 4 : 2;
@@ -350,8 +350,6 @@ lact_status validate_problem(const lact_problem* p) {
   if (p->opt < LACT_OPT_GD || p->opt > LACT_OPT_MUON_MOMENTUM) return fail(LACT_ERR_INVALID_ARG, "opt = %d", p->opt);
   if (uses_ns(p->opt) && (p->ns_iters < 1 || p->ns_iters > 16))
     return fail(LACT_ERR_INVALID_ARG, "ns_iters = %d: need 1..16", p->ns_iters);
-  if (uses_ns(p->opt) && p->d != p->dh)
-    return fail(LACT_ERR_UNSUPPORTED, "Newton-Schulz optimisers need d == dh (d = %d, dh = %d)", p->d, p->dh);
   if (p->rec_planes < 0 || p->rec_planes > 3) return fail(LACT_ERR_INVALID_ARG, "rec_planes = %d", p->rec_planes);
   if (p->flags & ~(LACT_NO_RENORM | LACT_QK_PREP)) return fail(LACT_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   return LACT_OK;
@@ -714,7 +712,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       float* rowsq = reinterpret_cast<float*>(ws + w.rowsq);
       {
         KernelTimer kt(LACT_K_NS, s);
-        const int64_t rows = (int64_t)n * 3 * D;
+        const int64_t rows = (int64_t)n * (2 * Dh + D);
         // momentum + Muon: the Newton-Schulz input is the new momentum buffer
         // M' = mean(beta) M - U, also written back to the state
         RowsMomentum rm;
@@ -728,65 +726,158 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
           rm.inv_len = 1.0f / (float)C;
         }
         LACT_LAUNCH(reduce_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(NT), s,
-                           reinterpret_cast<const float*>(ws + w.part), (int64_t)n * 3 * DD, S, U, rowsq, rows, D, rm);
+                           reinterpret_cast<const float*>(ws + w.part), (int64_t)n * 3 * DD, S, U, rowsq, rows, D, Dh,
+                           rm);
         HIP_TRY(hipGetLastError());
       }
       float* Am = reinterpret_cast<float*>(ws + w.am);
       float* Bm = reinterpret_cast<float*>(ws + w.bm);
       float* X[2] = {reinterpret_cast<float*>(ws + w.xa), reinterpret_cast<float*>(ws + w.xb)};
-      const int nb = 3 * n;
-      const int64_t w128 = (int64_t)((D + 127) / 128) * ((D + 127) / 128) * nb;
-      const int tile = gemm_tile(w128);
       const float ca = 3.4445f, cb = -4.7750f, cc = 2.0315f;
       const float* Xin = U;
-      for (int it = 0; it < p.ns_iters; ++it) {
-        const bool first = it == 0;
-        float* Xout = X[it & 1];
-        GemmArgs g = gemm_args();
-        g.lda = g.ldb = g.ldc = g.ldcin = D;
-        g.a_bs = g.b_bs = g.c_bs = g.cin_bs = DD;
-        g.g[0].M = D;
-        g.N = D;
-        g.K = g.kps = D;
-        g.batch = nb;
-        // A = X X^T (X = s U on the first step)
-        g.g[0].A = Xin;
-        g.g[0].B = Xin;
-        g.g[0].C = Am;
-        if (first) {
-          g.rowsq = rowsq;
-          g.rowsq_n = D;
-          g.alpha_pow = 2;
+      if (D == Dh) {
+        // every matrix square: one batch of 3n
+        const int nb = 3 * n;
+        const int64_t w128 = (int64_t)((D + 127) / 128) * ((D + 127) / 128) * nb;
+        const int tile = gemm_tile(w128);
+        for (int it = 0; it < p.ns_iters; ++it) {
+          const bool first = it == 0;
+          float* Xout = X[it & 1];
+          GemmArgs g = gemm_args();
+          g.lda = g.ldb = g.ldc = g.ldcin = D;
+          g.a_bs = g.b_bs = g.c_bs = g.cin_bs = DD;
+          g.g[0].M = D;
+          g.N = D;
+          g.K = g.kps = D;
+          g.batch = nb;
+          // A = X X^T (X = s U on the first step)
+          g.g[0].A = Xin;
+          g.g[0].B = Xin;
+          g.g[0].C = Am;
+          if (first) {
+            g.g[0].rowsq = rowsq;
+            g.rowsq_bs = D;
+            g.rowsq_n = D;
+            g.alpha_pow = 2;
+          }
+          lact_status r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
+          if (r) return r;
+          // B = b A + c A A   (A is symmetric: A A = A A^T)
+          g.g[0].rowsq = nullptr;
+          g.alpha_pow = 0;
+          g.g[0].A = Am;
+          g.g[0].B = Am;
+          g.g[0].C = Bm;
+          g.g[0].Cin = Am;
+          g.alpha = cc;
+          g.beta = cb;
+          r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
+          if (r) return r;
+          // X' = a X + B X
+          g.g[0].A = Bm;
+          g.g[0].B = Xin;  // element (n = j, k) = X[k, j]: column-k source
+          g.g[0].C = Xout;
+          g.g[0].Cin = Xin;
+          g.alpha = 1.f;
+          g.beta = ca;
+          if (first) {
+            g.g[0].rowsq = rowsq;
+            g.alpha_pow = 1;
+            g.beta_pow = 1;
+          }
+          r = launch_gemm<float, PT::PREC, false, float, PT::PREC, true, float>(g, tile, LACT_K_NS, s);
+          if (r) return r;
+          Xin = Xout;
         }
-        lact_status r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
-        if (r) return r;
-        // B = b A + c A A   (A is symmetric: A A = A A^T)
-        g.rowsq = nullptr;
-        g.alpha_pow = 0;
-        g.g[0].A = Am;
-        g.g[0].B = Am;
-        g.g[0].C = Bm;
-        g.Cin = Am;
-        g.alpha = cc;
-        g.beta = cb;
-        r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
-        if (r) return r;
-        // X' = a X + B X
-        g.g[0].A = Bm;
-        g.g[0].B = Xin;  // element (n = j, k) = X[k, j]: column-k source
-        g.g[0].C = Xout;
-        g.Cin = Xin;
-        g.alpha = 1.f;
-        g.beta = ca;
-        if (first) {
-          g.rowsq = rowsq;
-          g.rowsq_n = D;
-          g.alpha_pow = 1;
-          g.beta_pow = 1;
+      } else {
+        // W1, W3 are [dh, d] and W2 is [d, dh]: every Gram matrix is the
+        // smaller side, r = min(d, dh), so one group uses X X^T and
+        // X' = a X + B X, the other X^T X and X' = a X + X B (the same map:
+        // NS(X^T) = NS(X)^T).  Matrices sit at their offsets in each
+        // instance's [U1 | U3 | U2] block; the Gram matrices at the same
+        // offsets of Am, Bm.
+        const int rr = std::min(D, Dh);
+        struct NsPart {
+          int nmat;
+          int64_t off[2];
+          int rows, cols;
+          int rq_off[2];
+        };
+        const NsPart parts[2] = {{2, {0, DD}, Dh, D, {0, Dh}}, {1, {2 * DD, 0}, D, Dh, {2 * Dh, 0}}};
+        const int64_t IB = 3 * DD;   // instance stride of the stacked blocks
+        for (int it = 0; it < p.ns_iters; ++it) {
+          const bool first = it == 0;
+          float* Xout = X[it & 1];
+          for (const NsPart& pt : parts) {
+            const bool xxT = pt.rows <= pt.cols;   // Gram on the rows side
+            const int64_t w128 = (int64_t)((rr + 127) / 128) * ((rr + 127) / 128) * n * pt.nmat;
+            const int tile = gemm_tile(w128);
+            GemmArgs g = gemm_args();
+            g.ngroups = pt.nmat;
+            g.a_bs = g.b_bs = g.c_bs = g.cin_bs = IB;
+            g.batch = n;
+            // Gram: X X^T (rows-k reads of X) or X^T X (column-k reads of X)
+            for (int i = 0; i < pt.nmat; ++i) {
+              g.g[i].A = Xin + pt.off[i];
+              g.g[i].B = Xin + pt.off[i];
+              g.g[i].C = Am + pt.off[i];
+              g.g[i].M = rr;
+              if (first) g.g[i].rowsq = rowsq + pt.rq_off[i];
+            }
+            g.lda = g.ldb = pt.cols;
+            g.ldc = rr;
+            g.N = rr;
+            g.K = g.kps = xxT ? pt.cols : pt.rows;
+            if (first) {
+              g.rowsq_bs = 2 * Dh + D;
+              g.rowsq_n = pt.rows;
+              g.alpha_pow = 2;
+            }
+            lact_status r = xxT ? launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s)
+                                : launch_gemm<float, PT::PREC, true, float, PT::PREC, true, float>(g, tile, LACT_K_NS, s);
+            if (r) return r;
+            // B = b A + c A A   (A symmetric)
+            for (int i = 0; i < pt.nmat; ++i) {
+              g.g[i].A = Am + pt.off[i];
+              g.g[i].B = Am + pt.off[i];
+              g.g[i].C = Bm + pt.off[i];
+              g.g[i].Cin = Am + pt.off[i];
+              g.g[i].rowsq = nullptr;
+            }
+            g.alpha_pow = g.beta_pow = 0;
+            g.lda = g.ldb = g.ldc = g.ldcin = rr;
+            g.N = rr;
+            g.K = g.kps = rr;
+            g.alpha = cc;
+            g.beta = cb;
+            r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
+            if (r) return r;
+            // X' = a X + B X (rows side) or a X + X B (columns side)
+            for (int i = 0; i < pt.nmat; ++i) {
+              g.g[i].A = xxT ? Bm + pt.off[i] : Xin + pt.off[i];
+              g.g[i].B = xxT ? Xin + pt.off[i] : Bm + pt.off[i];
+              g.g[i].C = Xout + pt.off[i];
+              g.g[i].Cin = Xin + pt.off[i];
+              g.g[i].M = pt.rows;
+              if (first) g.g[i].rowsq = rowsq + pt.rq_off[i];
+            }
+            g.lda = xxT ? rr : pt.cols;
+            g.ldb = xxT ? pt.cols : rr;   // rows side: element (n = j, k) = X[k, j]; else B[n, k] = B[k, n]
+            g.ldc = g.ldcin = pt.cols;
+            g.N = pt.cols;
+            g.K = g.kps = rr;
+            g.alpha = 1.f;
+            g.beta = ca;
+            if (first) {
+              g.alpha_pow = 1;
+              g.beta_pow = 1;
+            }
+            r = xxT ? launch_gemm<float, PT::PREC, false, float, PT::PREC, true, float>(g, tile, LACT_K_NS, s)
+                    : launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
+            if (r) return r;
+          }
+          Xin = Xout;
         }
-        r = launch_gemm<float, PT::PREC, false, float, PT::PREC, true, float>(g, tile, LACT_K_NS, s);
-        if (r) return r;
-        Xin = Xout;
       }
       oa.src = Xin;
       oa.src_ss = 0;

@@ -365,10 +365,10 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
   }
 
   float alpha = g.alpha, beta = g.beta;
-  if (g.rowsq != nullptr) {
+  if (G.rowsq != nullptr) {
     if (wave == 0) {
       float sq = 0.f;
-      const float* rq = g.rowsq + (int64_t)b * g.rowsq_n;
+      const float* rq = G.rowsq + (int64_t)b * g.rowsq_bs;
       for (int i = lane; i < g.rowsq_n; i += WAVE) sq += rq[i];
       sq = wave_sum(sq);
       if (lane == 0) s_scale = 1.0f / (sqrtf(sq) + 1e-7f);
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
   }
   if (kh == 1) return;
   TC* C = reinterpret_cast<TC*>(G.C) + b * g.c_bs + split * g.c_ss;
-  const float* Cin = g.Cin ? g.Cin + b * g.cin_bs : nullptr;
+  const float* Cin = G.Cin ? G.Cin + b * g.cin_bs : nullptr;
   const bool trans = m0 >= g.trans_from;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {

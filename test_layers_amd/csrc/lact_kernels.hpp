@@ -305,6 +305,8 @@ struct GemmGroup {
   const void* B;
   void* C;
   const float* rs;       // optional: row m of C is scaled by silu(rs[b * rs_bs + m])
+  const float* Cin;      // optional: C += beta * Cin (batch stride cin_bs, row stride ldcin)
+  const float* rowsq;    // optional Frobenius scale source (see GemmArgs), this group's first row
   int M;
   int tiles;             // workgroups of this group
 };
@@ -319,16 +321,15 @@ struct GemmArgs {
   int m_switch;
   int trans_from;
   int64_t ldc_t;         // row stride of the transposed block
-  const float* Cin;
   int64_t ldcin, cin_bs;
   int N;
   int64_t K, kps;
   int64_t kpad;          // row-k operands are readable, and zero, from K up to kpad (0: no padding)
   int batch, splits;
   float alpha, beta;
-  // optional scale s = 1 / (sqrt(sum of rowsq[b * rowsq_n ...]) + 1e-7):
+  // optional scale s = 1 / (sqrt(sum of G.rowsq[b * rowsq_bs ... + rowsq_n)) + 1e-7):
   // alpha *= s^alpha_pow, beta *= s^beta_pow
-  const float* rowsq;
+  int64_t rowsq_bs;
   int rowsq_n, alpha_pow, beta_pow;
 };
 
@@ -397,10 +398,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   pipeline<STAGES>((int)nk, fetch, put, compute);
 
   float alpha = g.alpha, beta = g.beta;
-  if (g.rowsq != nullptr) {
+  if (G.rowsq != nullptr) {
     if (wave == 0) {
       float s = 0.f;
-      const float* rq = g.rowsq + (int64_t)b * g.rowsq_n;
+      const float* rq = G.rowsq + (int64_t)b * g.rowsq_bs;
       for (int i = lane; i < g.rowsq_n; i += WAVE) s += rq[i];
       s = wave_sum(s);
       if (lane == 0) s_scale = 1.0f / (sqrtf(s) + 1e-7f);
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < g.beta_pow; ++i) beta *= sc;
   }
   TC* C = reinterpret_cast<TC*>(G.C) + b * g.c_bs + split * g.c_ss;
-  const float* Cin = g.Cin ? g.Cin + b * g.cin_bs : nullptr;
+  const float* Cin = G.Cin ? G.Cin + b * g.cin_bs : nullptr;
   const bool trans = m0 >= g.trans_from;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -447,7 +448,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
 
 // =========================================================================
 // split-K reduction for the Muon path: U = sum_s P[s]; rowsq = per-row sum of
-// squares of U.  One wave per row of the stacked [n * 3D, D] matrix.
+// squares of U.  One wave per row of the stacked blocks (2 dh + d rows per
+// instance).
 // momentum + Muon: the buffer M' = mean(beta) M - U replaces U as the
 // Newton-Schulz input and is written back to the state (M[mat] in the order
 // of the stacked blocks U1 | U3 | U2; null M: plain Muon)
@@ -459,25 +461,33 @@ struct RowsMomentum {
 };
 
 __global__ __launch_bounds__(NT) void reduce_rows_kernel(const float* P, int64_t p_ss, int splits,
-                                                        float* U, float* rowsq, int64_t rows, int D,
+                                                        float* U, float* rowsq, int64_t rows, int D, int Dh,
                                                         RowsMomentum rm) {
+  // per instance the stacked blocks U1 [dh, d], U3 [dh, d], U2 [d, dh]:
+  // 2 dh + d rows, d long in the first two blocks and dh long in the third
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (NT / WAVE) + (threadIdx.x >> 6);
   if (row >= rows) return;
   const bool mom = rm.M[0] != nullptr;
-  const int64_t inst = row / (3 * (int64_t)D);
-  const int mat = (int)((row / D) % 3);
+  const int64_t DD = (int64_t)D * Dh;
+  const int64_t rpi = 2 * (int64_t)Dh + D;
+  const int64_t inst = row / rpi;
+  const int r = (int)(row % rpi);
+  const int mat = r < Dh ? 0 : r < 2 * Dh ? 1 : 2;
+  const int len = mat < 2 ? D : Dh;
+  const int64_t moff = mat < 2 ? (int64_t)(r - mat * Dh) * D : (int64_t)(r - 2 * Dh) * Dh;   // within the matrix
+  const int64_t base = inst * 3 * DD + mat * DD + moff;
   float bm = 0.f;
   float* Mrow = nullptr;
   if (mom) {
     float sb = 0.f;
     for (int i = lane; i < rm.nbp; i += WAVE) sb += rm.bpart[inst * rm.nbp + i];
     bm = wave_sum(sb) * rm.inv_len;
-    Mrow = rm.M[mat] + (inst * D + row % D) * (int64_t)D;
+    Mrow = rm.M[mat] + inst * DD + moff;
   }
   float ss = 0.f;
-  for (int e4 = lane; e4 < D / 4; e4 += WAVE) {
-    const float4* src = reinterpret_cast<const float4*>(P + row * D) + e4;
+  for (int e4 = lane; e4 < len / 4; e4 += WAVE) {
+    const float4* src = reinterpret_cast<const float4*>(P + base) + e4;
     float4 u = src[0];
     for (int s = 1; s < splits; ++s) {
       const float4 x = src[s * p_ss / 4];
@@ -491,7 +501,7 @@ __global__ __launch_bounds__(NT) void reduce_rows_kernel(const float* P, int64_t
       u = make_float4(bm * m.x - u.x, bm * m.y - u.y, bm * m.z - u.z, bm * m.w - u.w);
       reinterpret_cast<float4*>(Mrow)[e4] = u;
     }
-    reinterpret_cast<float4*>(U + row * D)[e4] = u;
+    reinterpret_cast<float4*>(U + base)[e4] = u;
     ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
   }
   ss = wave_sum(ss);

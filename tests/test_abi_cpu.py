@@ -73,8 +73,6 @@ def test_null_problem():
 @pytest.mark.parametrize("kw,code", [
     (dict(d=128, dh=96), lact.ERR_UNSUPPORTED),
     (dict(d=128, dh=2048), lact.ERR_UNSUPPORTED),
-    (dict(d=128, dh=64, opt=lact.OPT_MUON), lact.ERR_UNSUPPORTED),
-    (dict(d=128, dh=256, opt=lact.OPT_MUON_MOMENTUM), lact.ERR_UNSUPPORTED),
     (dict(d=96), lact.ERR_UNSUPPORTED),
     (dict(d=32), lact.ERR_UNSUPPORTED),
     (dict(d=2048), lact.ERR_UNSUPPORTED),
@@ -226,14 +224,15 @@ def test_scaled_entry_validation():
 
 
 def test_rectangular_fast_weights_accepted_and_sized():
-    """d != dh (multiples of 64) is accepted for GD and momentum; the
+    """d != dh (multiples of 64) is accepted for every optimiser; the
     workspace grows with dh where the hidden width is stored."""
     for dh in (64, 256):
         p = P(d=128, dh=dh)
         assert p.dh == dh
         if not __import__("torch").cuda.is_available():
             assert fwd(p) == lact.ERR_NO_DEVICE, lact.last_error()
-        assert fwd(P(d=128, dh=dh, opt=lact.OPT_MOMENTUM)) != lact.ERR_UNSUPPORTED
+        for opt in (lact.OPT_MOMENTUM, lact.OPT_MUON, lact.OPT_MUON_MOMENTUM):
+            assert fwd(P(d=128, dh=dh, opt=opt)) not in (lact.ERR_UNSUPPORTED, lact.ERR_INVALID_ARG)
     a = lact.workspace_size(P(d=128, dh=128), 512, 128)
     b = lact.workspace_size(P(d=128, dh=256), 512, 128)
     assert b > a

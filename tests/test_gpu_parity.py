@@ -279,9 +279,16 @@ def test_apply_rectangular(lact, d, dh, io):
     assert err <= _gate(io)
 
 
-@pytest.mark.parametrize("opt", [W.OPT_GD, W.OPT_MOMENTUM])
-@pytest.mark.parametrize("io,planes", [(W.DTYPE_F32, 3), (W.DTYPE_BF16, 1), (W.DTYPE_BF16, 2),
-                                       (W.DTYPE_BF16, 3)])
+# Newton-Schulz in one bf16 plane is not part of this grid: the quintic map's
+# slope near a zero singular value is a^5 ~ 487, so the bf16 rounding of its
+# products is amplified to 1.6-2.1e-2 on 128 x 256 matrices (at the 2e-2
+# gate); the Muon workloads run two or three planes.
+RECT_CASES = [(opt, io, planes) for opt in (W.OPT_GD, W.OPT_MOMENTUM, W.OPT_MUON, W.OPT_MUON_MOMENTUM)
+              for io, planes in ((W.DTYPE_F32, 3), (W.DTYPE_BF16, 1), (W.DTYPE_BF16, 2), (W.DTYPE_BF16, 3))
+              if not (planes == 1 and opt in (W.OPT_MUON, W.OPT_MUON_MOMENTUM))]
+
+
+@pytest.mark.parametrize("opt,io,planes", RECT_CASES)
 @pytest.mark.parametrize("d,dh", [(128, 256), (192, 64)])
 def test_chunk_update_rectangular(lact, opt, io, planes, d, dh):
     log(f"chunk_update d={d} dh={dh} opt={opt} io={io} planes={planes}")
@@ -292,7 +299,7 @@ def test_chunk_update_rectangular(lact, opt, io, planes, d, dh):
     M0 = [(rng.standard_normal(w.shape) * 0.01).astype(np.float32) for w in (inp.W1, inp.W2, inp.W3)]
     k, v, lr = to_dev(inp.k, torch), to_dev(inp.v, torch), to_dev(inp.lr, torch)
     Ws = [to_dev(w, torch).clone() for w in (inp.W1, inp.W2, inp.W3)]
-    mom = opt == W.OPT_MOMENTUM
+    mom = opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
     Ms = [to_dev(m, torch).clone() for m in M0] if mom else [None] * 3
     lact.chunk_update(k, v, lr, to_dev(beta, torch) if mom else None, *Ws, *Ms, opt=opt, rec_planes=planes)
     torch.cuda.synchronize()
@@ -310,14 +317,17 @@ def test_chunk_update_rectangular(lact, opt, io, planes, d, dh):
     assert max(errs.values()) <= gate, errs
 
 
-@pytest.mark.parametrize("io,planes", [(W.DTYPE_F32, 3), (W.DTYPE_BF16, 1), (W.DTYPE_BF16, 2)])
-def test_layer_rectangular_every_profile(lact, io, planes):
+@pytest.mark.parametrize("io,planes,opt", [(W.DTYPE_F32, 3, W.OPT_MOMENTUM), (W.DTYPE_BF16, 1, W.OPT_MOMENTUM),
+                                           (W.DTYPE_BF16, 2, W.OPT_MOMENTUM), (W.DTYPE_F32, 3, W.OPT_MUON_MOMENTUM),
+                                           (W.DTYPE_BF16, 2, W.OPT_MUON_MOMENTUM),
+                                           (W.DTYPE_BF16, 3, W.OPT_MUON)])
+def test_layer_rectangular_every_profile(lact, io, planes, opt):
     """The full layer with dh < d and dh > d (ragged last chunk), every profile."""
     import dataclasses
     for d, dh in [(128, 64), (64, 192)]:
         wl = dataclasses.replace(W.CONFIGS[10].scaled(n_inst=2, L=700, chunk=256), D=d, Dh=dh, io_dtype=io,
-                                 rec_planes=planes, tol=_gate(io))
-        log(f"layer d={d} dh={dh} io={io} planes={planes}")
+                                 rec_planes=planes, opt=opt, tol=_gate(io))
+        log(f"layer d={d} dh={dh} io={io} planes={planes} opt={opt}")
         inp = W.generate(wl, seed=5)
         gpu = run_gpu(wl, inp, torch, lact)
         errs = compare(wl, inp, gpu)

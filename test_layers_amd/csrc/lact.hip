@@ -267,6 +267,11 @@ int upd_bj(const lact_problem& p, int64_t C) {
 }
 
 
+// the whole apply in one kernel with the tile's gated hidden kept in LDS:
+// bf16 apply operands and a hidden width of one 128-column block (there the
+// apply is bound by HBM traffic, which the fused kernel halves)
+bool fused_apply(const lact_problem& p) { return profile_of(p) != PF32 && p.dh == 128 && p.d % 128 == 0; }
+
 // --------------------------------------------------------------- workspace layout
 struct Ws {
   size_t e = 0, h = 0, part = 0, bpart = 0, snap = 0, u = 0, am = 0, bm = 0, xa = 0, xb = 0, rowsq = 0, total = 0;
@@ -314,7 +319,7 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   const size_t snap_el = (f == PF32) ? 4 : 2;
   w.snap_slot = align256(4 * n * D * Dh * snap_el);
   w.e = take(n * 3 * Dh * (size_t)w.ldE * rec_size(f));
-  w.h = take(n * (size_t)h_rows * Dh * app_size(f));
+  w.h = take(fused_apply(p) ? 0 : n * (size_t)h_rows * Dh * app_size(f));
   const size_t mats = n * 3 * D * Dh * sizeof(float);
   w.part = take(plan.max_upd > 0 ? (size_t)S * mats : 0);
   w.bpart = take(uses_momentum(p.opt) ? n * (size_t)w.max_tt * sizeof(float) : 0);
@@ -931,6 +936,35 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       }
       if (st.upd_len > 0) ++u;
     }
+  }
+  if (fused_apply(p)) {
+    for (size_t g0 = 0; g0 < groups.size(); g0 += MAXG) {
+      const int ng = (int)std::min<size_t>(MAXG, groups.size() - g0);
+      AppFwdArgs aa;
+      memset(&aa, 0, sizeof(aa));
+      aa.ngroups = ng;
+      aa.q = qx;
+      aa.q_bs = q_bs;
+      aa.x_bs = x_bs;
+      aa.o = P.o;
+      aa.oz = P.oz;
+      aa.oz_bs = seq_stride;
+      aa.D = D;
+      aa.Dh = Dh;
+      int64_t grid = 0;
+      for (int i = 0; i < ng; ++i) {
+        aa.g[i] = groups[g0 + i];
+        const int64_t t = ((aa.g[i].len + FBT - 1) / FBT) * n;
+        if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+        aa.g[i].tiles = (int)t;
+        grid += t;
+      }
+      if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+      KernelTimer kt(LACT_K_APP, s);
+      LACT_LAUNCH((dapp_fused_kernel<128, 32, 2>), dim3((unsigned)grid), dim3(NT), s, aa);
+      HIP_TRY(hipGetLastError());
+    }
+    return LACT_OK;
   }
   // the column block serves both the forward (dh columns) and the output
   // mode (d columns); the fp32 register-path apply tile spills at 128

@@ -694,4 +694,165 @@ __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {
   }
 }
 
+// =========================================================================
+// Fused apply for a hidden width of one column block (dh = BJ): o = W2
+// (silu(W1 q) * (W3 q)) for one 128-token tile of one apply group, the
+// tile's gated hidden Hq kept in LDS and never written to HBM.  At this
+// width the apply is bound by HBM traffic, and Hq's write and re-read would
+// move as many bytes as q and o themselves.  Phase 1 computes Hq (the
+// apply tile's forward, contraction over d) into LDS, cut into the dh / BKK
+// k-stage tiles that phase 2 reads; phase 2 runs o = Hq W2^T over the
+// output blocks with only the W2 tiles streamed.  The 32 KB of Hq and a
+// two-stage ring leave room for two workgroups per CU.  4 waves: wave w
+// owns tokens 64 (w >> 1) .. +63 and columns (BJ / 2)(w & 1) .. +BJ/2-1.
+template <int BJ, int BKK, int NST>
+__global__ __launch_bounds__(NT, 2) void dapp_fused_kernel(AppFwdArgs a) {
+  using TX = DTile<FBT, BKK>;   // query stage tiles and the Hq k-stage tiles
+  using TW = DTile<BJ, BKK>;    // W1, W3 (phase 1) and W2 (phase 2) rows
+  constexpr int STAGE = TX::BYTES + 2 * TW::BYTES;
+  constexpr int LPS1 = TX::INSTR + 2 * TW::INSTR;
+  constexpr int LPS2 = TW::INSTR;
+  constexpr int FN = BJ / 32;
+  constexpr int NKH = BJ / BKK;   // k-stage tiles of Hq (dh = BJ)
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+  __shared__ __attribute__((aligned(1024))) char hq[NKH * TX::BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int D = a.D;   // a.Dh == BJ
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int gi = 0;
+  while (gi + 1 < a.ngroups && bid >= a.g[gi].tiles) bid -= a.g[gi++].tiles;
+  const AppGroup& G = a.g[gi];
+  const int tiles_t = (int)((G.len + FBT - 1) / FBT);
+  const int inst = bid / tiles_t, tb = bid % tiles_t;
+  const int64_t t0 = G.t0 + (int64_t)tb * FBT;
+  const int64_t tend = G.t0 + G.len;
+  const int64_t DD = (int64_t)D * BJ;
+  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.q) + inst * a.q_bs;
+  const bf16_t* W1 = reinterpret_cast<const bf16_t*>(G.W1) + inst * DD;
+  const bf16_t* W3 = reinterpret_cast<const bf16_t*>(G.W3) + inst * DD;
+  const bf16_t* W2 = reinterpret_cast<const bf16_t*>(G.W2) + inst * DD;
+
+  // ---- phase 1: Hq = silu(Q W1^T) * (Q W3^T) into LDS (contraction over d)
+  {
+    const typename TX::Plan pq = TX::plan(Q, D, t0, tend - 1, 0, wave, lane);
+    const typename TW::Plan p1 = TW::plan(W1, D, 0, BJ - 1, 0, wave, lane);
+    const typename TW::Plan p3 = TW::plan(W3, D, 0, BJ - 1, 0, wave, lane);
+    auto issue_one = [&](int s, int buf, int idx) {
+      char* st = smem + buf * STAGE;
+      const int64_t off = (int64_t)s * BKK * 2;
+      if (idx < TX::INSTR) TX::issue_one(st, pq, off, wave, idx);
+      else if (idx < TX::INSTR + TW::INSTR) TW::issue_one(st + TX::BYTES, p1, off, wave, idx - TX::INSTR);
+      else TW::issue_one(st + TX::BYTES + TW::BYTES, p3, off, wave, idx - TX::INSTR - TW::INSTR);
+    };
+    f32x4 accA[4][FN], accB[4][FN];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) accA[i][j] = accB[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int buf, auto&& hook) {
+      const char* st = smem + buf * STAGE;
+      constexpr int NSLOT = (BKK / 32) * 4;
+#pragma unroll
+      for (int kk = 0; kk < BKK; kk += 32) {
+        bf16x8 fq[4], f1[FN], f3[FN];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fq[i] = dfrag_row<TX>(st, wm * 64 + i * 16, kk, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          f1[j] = dfrag_row<TW>(st + TX::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+          f3[j] = dfrag_row<TW>(st + TX::BYTES + TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            accA[i][j] = mfma(f1[j], fq[i], accA[i][j]);   // swapped: lane owns 4 columns of one token
+            accB[i][j] = mfma(f3[j], fq[i], accB[i][j]);
+          }
+          hook((kk / 32) * 4 + i, NSLOT);
+        }
+      }
+    };
+    dpipeline_il<NST, LPS1>(D / BKK, issue_one, compute);
+    // hidden columns c .. c+3 of token row tl -> k-stage tile c / BKK of Hq
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tl = wm * 64 + i * 16 + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int c = wn * (BJ / 2) + j * 16 + 4 * (lane >> 4);
+        float h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = accA[i][j][r];
+          h[r] = x * fast_sigmoid(x) * accB[i][j][r];
+        }
+        const int cc = c % BKK;
+        char* dst = hq + (c / BKK) * TX::BYTES + TX::phys(tl, cc >> 3) * 16 + ((cc >> 2) & 1) * 8;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+      }
+    }
+  }
+  __syncthreads();   // Hq visible to every wave; the ring is free
+
+  // ---- phase 2: o[:, o0 .. o0 + BJ) = Hq W2[o0 .., :]^T (contraction over dh)
+  bf16_t* O = reinterpret_cast<bf16_t*>(a.o) + inst * a.x_bs;
+  float ys[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = min(t0 + wm * 64 + i * 16 + (lane & 15), tend - 1);
+    ys[i] = a.oz != nullptr ? silu(a.oz[inst * a.oz_bs + t]) : 1.f;
+  }
+  const int nob = D / BJ;
+  for (int ob = 0; ob < nob; ++ob) {
+    const int o0 = ob * BJ;
+    const typename TW::Plan p2 = TW::plan(W2, BJ, o0, D - 1, 0, wave, lane);
+    auto issue_one = [&](int s, int buf, int idx) {
+      TW::issue_one(smem + buf * STAGE, p2, (int64_t)s * BKK * 2, wave, idx);
+    };
+    f32x4 acc[4][FN];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int sidx = 0;
+    auto compute = [&](int buf, auto&& hook) {
+      const char* st = smem + buf * STAGE;
+      const char* ht = hq + sidx * TX::BYTES;
+      constexpr int NSLOT = (BKK / 32) * 4;
+#pragma unroll
+      for (int kk = 0; kk < BKK; kk += 32) {
+        bf16x8 fh[4], fw[FN];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fh[i] = dfrag_row<TX>(ht, wm * 64 + i * 16, kk, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fw[j] = dfrag_row<TW>(st, wn * (BJ / 2) + j * 16, kk, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma(fw[j], fh[i], acc[i][j]);
+          hook((kk / 32) * 4 + i, NSLOT);
+        }
+      }
+      ++sidx;
+    };
+    dpipeline_il<NST, LPS2>(NKH, issue_one, compute);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + wm * 64 + i * 16 + (lane & 15);
+      if (t >= tend) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = o0 + wn * (BJ / 2) + j * 16 + 4 * (lane >> 4);
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = acc[i][j][r] * ys[i];
+        store4(O + t * (int64_t)D + col, y);
+      }
+    }
+    if (ob + 1 < nob) bar();   // every wave is done with the ring before the next block's loads
+  }
+}
+
 }  // namespace lact

@@ -261,7 +261,7 @@ def _rect_inputs(n, L, d, dh, io, seed):
     return W.generate(wl, seed=seed)
 
 
-@pytest.mark.parametrize("d,dh", [(128, 256), (384, 192), (64, 128)])
+@pytest.mark.parametrize("d,dh", [(128, 256), (384, 192), (64, 128), (256, 128), (384, 128)])
 @pytest.mark.parametrize("io", [W.DTYPE_F32, W.DTYPE_BF16])
 def test_apply_rectangular(lact, d, dh, io):
     log(f"apply d={d} dh={dh} io={io}")

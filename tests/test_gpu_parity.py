@@ -333,3 +333,24 @@ def test_layer_rectangular_every_profile(lact, io, planes, opt):
         errs = compare(wl, inp, gpu)
         log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
         assert max(errs.values()) <= wl.tol, errs
+
+
+# ------------------------------------------------------------------ the largest widths
+@pytest.mark.parametrize("d,dh,io,planes,opt", [
+    (1024, 1024, W.DTYPE_BF16, 1, W.OPT_MOMENTUM),
+    (1024, 1024, W.DTYPE_BF16, 2, W.OPT_MUON),
+    (1024, 1024, W.DTYPE_F32, 3, W.OPT_GD),
+    (1024, 128, W.DTYPE_BF16, 1, W.OPT_MOMENTUM),   # fused apply, eight output blocks
+    (64, 1024, W.DTYPE_BF16, 2, W.OPT_MUON_MOMENTUM),
+])
+def test_layer_maximum_width(lact, d, dh, io, planes, opt):
+    """The largest widths the library accepts (1024), ragged chunks."""
+    import dataclasses
+    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=1, L=700, chunk=256), D=d, Dh=dh, io_dtype=io,
+                             rec_planes=planes, opt=opt, tol=_gate(io))
+    log(f"layer d={d} dh={dh} io={io} planes={planes} opt={opt}")
+    inp = W.generate(wl, seed=9)
+    gpu = run_gpu(wl, inp, torch, lact)
+    errs = compare(wl, inp, gpu)
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= wl.tol, errs

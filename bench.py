@@ -171,12 +171,18 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    # per-step boundaries as events on the layer's stream (no host sync inside
+    # the timed loop); the wall clock around the loop gives `value`
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     ms_per_step = dt / args.steps * 1e3
     tokens = wl.tokens
     value = tokens * args.steps / dt
@@ -223,6 +229,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

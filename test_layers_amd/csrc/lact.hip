@@ -477,8 +477,15 @@ lact_status launch_gemm_t(const GemmArgs& g, int64_t grid, hipStream_t s) {
 template <typename TA, int PA, bool CA, typename TB, int PB, bool CB, typename TC>
 lact_status launch_gemm(GemmArgs g, int tile, int kclass, hipStream_t s) {
   int64_t grid = 0;
+  if (g.sym) {
+    if constexpr (sizeof(TA) == 2 && sizeof(TB) == 2)
+      return fail(LACT_ERR_UNSUPPORTED, "internal: symmetric products run on the register-path GEMM");
+    for (int i = 0; i < g.ngroups; ++i)
+      if (g.g[i].M != g.N) return fail(LACT_ERR_UNSUPPORTED, "internal: symmetric product of a non-square block");
+  }
   for (int i = 0; i < g.ngroups; ++i) {
-    const int64_t t = (int64_t)((g.g[i].M + tile - 1) / tile) * ((g.N + tile - 1) / tile) * g.batch * g.splits;
+    const int64_t tt = (g.N + tile - 1) / tile;
+    const int64_t t = (g.sym ? tt * (tt + 1) / 2 : (int64_t)((g.g[i].M + tile - 1) / tile) * tt) * g.batch * g.splits;
     if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
     g.g[i].tiles = (int)t;
     grid += t;
@@ -755,7 +762,11 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
           g.N = D;
           g.K = g.kps = D;
           g.batch = nb;
-          // A = X X^T (X = s U on the first step)
+          // A = X X^T (X = s U on the first step); A and B are symmetric, so
+          // only their upper-triangle tiles run (mirrored on store) once
+          // that saves enough tiles (measured: 38.6 -> 31.7 us per product
+          // at D = 512, no gain at D = 128)
+          g.sym = D >= 256;
           g.g[0].A = Xin;
           g.g[0].B = Xin;
           g.g[0].C = Am;
@@ -779,6 +790,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
           r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
           if (r) return r;
           // X' = a X + B X
+          g.sym = 0;
           g.g[0].A = Bm;
           g.g[0].B = Xin;  // element (n = j, k) = X[k, j]: column-k source
           g.g[0].C = Xout;
@@ -821,6 +833,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
             g.ngroups = pt.nmat;
             g.a_bs = g.b_bs = g.c_bs = g.cin_bs = IB;
             g.batch = n;
+            g.sym = rr >= 256;   // the Gram matrix and b A + c A A are symmetric
             // Gram: X X^T (rows-k reads of X) or X^T X (column-k reads of X)
             for (int i = 0; i < pt.nmat; ++i) {
               g.g[i].A = Xin + pt.off[i];
@@ -858,6 +871,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
             r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
             if (r) return r;
             // X' = a X + B X (rows side) or a X + X B (columns side)
+            g.sym = 0;
             for (int i = 0; i < pt.nmat; ++i) {
               g.g[i].A = xxT ? Bm + pt.off[i] : Xin + pt.off[i];
               g.g[i].B = xxT ? Xin + pt.off[i] : Bm + pt.off[i];

@@ -331,6 +331,10 @@ struct GemmArgs {
   // alpha *= s^alpha_pow, beta *= s^beta_pow
   int64_t rowsq_bs;
   int rowsq_n, alpha_pow, beta_pow;
+  // symmetric result (M == N, e.g. a Gram matrix X X^T or a product of
+  // symmetric matrices): only tiles on or above the diagonal run, and the
+  // off-diagonal ones also store their mirror image
+  int sym;
 };
 
 template <typename TA, int PA, bool CA, typename TB, int PB, bool CB, typename TC, int BM, int BN, int BK, int STAGES>
@@ -351,12 +355,19 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   const int M = G.M;
   const int tn_count = (g.N + BN - 1) / BN;
   const int tm_count = (M + BM - 1) / BM;
-  const int tiles = tm_count * tn_count;
+  const int tiles = g.sym ? tn_count * (tn_count + 1) / 2 : tm_count * tn_count;
   const int tile = bid % tiles;
   bid /= tiles;
   const int split = bid % g.splits;
   const int b = bid / g.splits;
-  const int tm = tile / tn_count, tn = tile % tn_count;
+  int tm = tile / tn_count, tn = tile % tn_count;
+  if (g.sym) {   // upper triangle, row by row: row tm holds tiles tn = tm .. tn_count - 1
+    int rem = tile;
+    tm = 0;
+    while (rem >= tn_count - tm) rem -= tn_count - tm++;
+    tn = tm + rem;
+  }
+  const bool mirror = g.sym && tn != tm;
   const int m0 = tm * BM, n0 = tn * BN;
 
   const TA* A = reinterpret_cast<const TA*>(G.A) + b * g.a_bs;
@@ -441,6 +452,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
                                val[r]);
       } else {
         store4(C + (int64_t)m * g.ldc + nq, val);
+        if (mirror) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) io_traits<TC>::store(C + (int64_t)(nq + r) * g.ldc + m, val[r]);
+        }
       }
     }
   }

@@ -354,3 +354,25 @@ def test_layer_maximum_width(lact, d, dh, io, planes, opt):
     errs = compare(wl, inp, gpu)
     log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
     assert max(errs.values()) <= wl.tol, errs
+
+
+# ------------------------------------------------------------------ degenerate inputs
+@pytest.mark.parametrize("opt", [W.OPT_GD, W.OPT_MOMENTUM, W.OPT_MUON, W.OPT_MUON_MOMENTUM])
+def test_zero_learning_rates_leave_the_state_unchanged(lact, opt):
+    """lr = 0: U = 0, NS5(0) = 0 and the renorm ratio is exactly 1, so W (and
+    M = 0) come back bit-identical, and every output row is the plain SwiGLU
+    MLP of the initial weights."""
+    import dataclasses
+    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=700, chunk=256), D=128, opt=opt, rec_planes=2)
+    inp = W.generate(wl, seed=13)
+    inp.lr[:] = 0.0
+    gpu = run_gpu(wl, inp, torch, lact)
+    for j, key in enumerate(["W1", "W2", "W3"]):
+        assert torch.equal(gpu[key], to_dev(getattr(inp, key), torch)), key
+        if gpu["M" + key[1]] is not None:
+            assert not torch.any(gpu["M" + key[1]]), "M"
+    g = from_dev(gpu["o"], torch)
+    err = max(rel_err(g[i], O.apply(O.f64(inp.W1[i]), O.f64(inp.W2[i]), O.f64(inp.W3[i]), O.f64(inp.q[i])))
+              for i in range(wl.n_inst))
+    log(f"  opt={opt} o err={err:.2e}")
+    assert err <= wl.tol

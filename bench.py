@@ -205,6 +205,9 @@ def main():
     if "apply_out" not in per:
         # the fused apply kernel also runs the output product
         kf[lact.K_APP] += kf[lact.K_OUT]
+    if "dw" not in per:
+        # the fused update kernel also runs the weight-gradient contraction
+        kf[lact.K_UPD] += kf[lact.K_DW]
     dom = max(per.items(), key=lambda kv: kv[1]["ms_per_step"])
     dname, d = dom
     if kf[d["kc"]] > 0:

@@ -243,6 +243,22 @@ void dw_split(const lact_problem& p, int64_t C, int& S, int64_t& kps) {
   if (S < 1) S = 1;
 }
 
+// long chunks at d = dh = 128 in plain bf16 run the update forward and the
+// contraction as one kernel (the update terms stay in LDS)
+bool fused_update(const lact_problem& p, int64_t C) {
+  return profile_of(p) == PBF16 && p.d == UDW_D && p.dh == UDW_D && C >= 4096;
+}
+
+// its token split: about one workgroup per CU (n instances x 2 hidden
+// blocks per split), every split non-empty
+void udw_split(const lact_problem& p, int64_t C, int& S, int& tps) {
+  const int64_t tt = (C + FBT - 1) / FBT;
+  const int64_t per = 2 * (int64_t)std::max(1, p.n_inst);
+  const int64_t s0 = std::max<int64_t>(1, std::min<int64_t>(tt, NCU / per));
+  tps = (int)((tt + s0 - 1) / s0);
+  S = (int)((tt + tps - 1) / tps);
+}
+
 // hidden-column block of the update forward tile: the one whose workgroup
 // count fills the chip best (ties go to the wider block)
 int upd_bj(const lact_problem& p, int64_t C) {
@@ -309,6 +325,10 @@ Ws layout(const lact_problem& p, const Plan& plan) {
     int s_ = 1;
     int64_t kps = 0;
     dw_split(p, st.upd_len, s_, kps);
+    if (fused_update(p, st.upd_len)) {
+      int tps = 0;
+      udw_split(p, st.upd_len, s_, tps);
+    }
     S = std::max(S, s_);
   }
   w.S = S;
@@ -651,7 +671,28 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     ua.upd_t0 = st.upd_t0;
     ua.upd_len = C;
     ua.tiles_t = (int)((C + FBT - 1) / FBT);
-    {
+    const bool fused = fused_update(p, C);
+    int S = 1;
+    int64_t kps = 0;
+    if (fused) {
+      // update forward + contraction in one kernel, fp32 partials per split
+      if constexpr (PT::UPD_FROM_SNAP) {
+        int tps = 0;
+        udw_split(p, C, S, tps);
+        if (S > w.S) return fail(LACT_ERR_UNSUPPORTED, "internal: token split %d exceeds workspace plan %d", S, w.S);
+        UpdDwArgs ud;
+        memset(&ud, 0, sizeof(ud));
+        ud.u = ua;
+        ud.part = reinterpret_cast<float*>(ws + w.part);
+        ud.part_ss = (int64_t)n * 3 * DD;
+        ud.tps = tps;
+        ud.splits = S;
+        const int64_t grid = (int64_t)n * S * (UDW_D / 64);
+        KernelTimer kt(LACT_K_UPD, s);
+        LACT_LAUNCH((dupd_dw_kernel<64>), dim3((unsigned)grid), dim3(DG_THREADS), s, ud);
+        HIP_TRY(hipGetLastError());
+      }
+    } else {
       const int bj = upd_bj(p, C);
       const int64_t grid = (int64_t)n * ua.tiles_t * (Dh / bj);
       if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
@@ -662,11 +703,9 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       if (r) return r;
     }
     // weight-gradient contraction over the chunk's tokens (split over tokens)
-    int S;
-    int64_t kps;
-    dw_split(p, C, S, kps);
+    if (!fused) dw_split(p, C, S, kps);
     if (S > w.S) return fail(LACT_ERR_UNSUPPORTED, "internal: token split %d exceeds workspace plan %d", S, w.S);
-    {
+    if (!fused) {
       GemmArgs g = gemm_args();
       g.g[0].A = ws + w.e;         // (m, t) = E[m, t]: rows U1 | U3 | U2^T terms
       g.lda = ua.ldE;
@@ -914,7 +953,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       oa.rpw = opt_rpw(oa.L);
       const dim3 og((unsigned)(n * oa.nmat * (oa.R / (4 * oa.rpw))));
       const int vpl = (oa.rpw * oa.L + 255) / 256;
-      if (part16) {
+      if (part16 && !fused) {
         if (vpl == 1) LACT_LAUNCH((opt_kernel<TS, 1, bf16_t>), og, dim3(NT), s, oa);
         else if (vpl == 2) LACT_LAUNCH((opt_kernel<TS, 2, bf16_t>), og, dim3(NT), s, oa);
         else if (vpl == 3) LACT_LAUNCH((opt_kernel<TS, 3, bf16_t>), og, dim3(NT), s, oa);

@@ -589,6 +589,241 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
 }
 
 // =========================================================================
+// Fused update for long chunks at d = dh = 128 (plain bf16): the update
+// forward of each 128-token tile (as in dupd_fwd_kernel) followed at once by
+// the tile's share of the weight-gradient contraction, so the update terms E
+// never reach HBM (at this width their write and re-read are most of the
+// update's traffic).  After the forward both k stages of the tile's K and V
+// are still in the LDS ring; the tile's update terms (bf16) are staged in
+// the ring's W regions, which the forward has finished with; the tile's
+// contribution to U1, U3 (hidden rows j0 .. j0 + BJ - 1, all d columns) and
+// to U2 (all d rows, columns j0 ..) is accumulated in registers over the
+// workgroup's run of tiles, and one fp32 partial per workgroup is stored
+// (the optimiser sums the partials in a fixed order).
+struct UpdDwArgs {
+  UpdFwdArgs u;          // chunk, inputs, snapshot of the weights (E unused)
+  float* part;           // partials [splits, n, U1 | U3 | U2]
+  int64_t part_ss;       // elements between partials
+  int tps;               // token tiles per split
+  int splits;
+};
+
+constexpr int UDW_D = 128;   // d = dh handled by the fused update
+
+template <int BJ>
+__global__ __launch_bounds__(DG_THREADS) void dupd_dw_kernel(UpdDwArgs g) {
+  const UpdFwdArgs& a = g.u;
+  constexpr int BKK = 64, NK = UDW_D / BKK;
+  constexpr int NWV = DG_THREADS / WAVE;
+  static_assert(upd_w_waves(BJ, BKK) == NWV, "every wave loads W tiles");
+  using TX = DTile<FBT, BKK, NWV>;   // K, V: 128 tokens x BKK (rows = tokens)
+  using TW = DTile<BJ, BKK, NWV>;    // W1, W3, W2^T rows: BJ x BKK
+  constexpr int STAGE = 2 * TX::BYTES + 3 * TW::BYTES;
+  constexpr int LPS = 2 * TX::INSTR + 3 * TW::INSTR;
+  constexpr int FM = 2, FN = BJ / 32;
+  constexpr int EROWS = 3 * BJ;                     // update-term rows (U1 | U3 | U2 terms) x 128 tokens
+  constexpr int EHALF = 3 * TW::BYTES / (FBT * 2);  // rows that fit one stage's W region
+  static_assert(NK == 2 && 2 * EHALF >= EROWS && EHALF % 16 == 0, "update terms fit the two W regions");
+  __shared__ __attribute__((aligned(1024))) char smem[NK * STAGE];
+  __shared__ float s_red[2];
+  __shared__ float s_lr[FBT * 3];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;     // forward: 32-token group, half of the BJ columns
+  const int jh = wave >> 2, cq = wave & 3;     // contraction: 32 hidden rows x 32 d columns
+  const int D = UDW_D;
+  const int njb = UDW_D / BJ;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int jb = bid % njb;
+  bid /= njb;
+  const int split = bid % g.splits;
+  const int inst = bid / g.splits;
+  const int j0 = jb * BJ;
+  const int64_t DD = (int64_t)D * D;
+  const int64_t tend = a.upd_t0 + a.upd_len;
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + inst * a.k_bs;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + inst * a.x_bs;
+  const typename TW::Plan p1 = TW::plan(reinterpret_cast<const bf16_t*>(a.W1) + inst * DD, D, j0, D - 1, 0, wave, lane);
+  const typename TW::Plan p3 = TW::plan(reinterpret_cast<const bf16_t*>(a.W3) + inst * DD, D, j0, D - 1, 0, wave, lane);
+  const typename TW::Plan p2 = TW::plan(reinterpret_cast<const bf16_t*>(a.W2x) + inst * DD, D, j0, D - 1, 0, wave, lane);
+  // update-term row r (term r / BJ, hidden column r % BJ): 256 bytes of 128
+  // tokens, 16-byte chunks swizzled by the row, in stage r / EHALF's W region
+  auto erow = [&](int r) -> char* {
+    return smem + (r / EHALF) * STAGE + 2 * TX::BYTES + (r % EHALF) * (FBT * 2);
+  };
+
+  f32x4 cu1[2][2], cu3[2][2], cu2[2][2];   // [c frag][j frag] for U1, U3; [j frag][c frag] for U2
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) cu1[x][y] = cu3[x][y] = cu2[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int tb_end = min(a.tiles_t, (split + 1) * g.tps);
+  for (int tb = split * g.tps; tb < tb_end; ++tb) {
+    const int64_t t0 = a.upd_t0 + (int64_t)tb * FBT;
+    float lrv = 0.f, bval = 0.f;
+    {
+      const float* lr = a.lr + inst * a.lr_bs + t0 * 3;
+      if (tid < FBT * 3 && t0 + tid / 3 < tend) lrv = lr[tid];
+      if (a.beta != nullptr && jb == 0 && tid < FBT && t0 + tid < tend) bval = a.beta[inst * a.beta_bs + t0 + tid];
+    }
+    const typename TX::Plan pk = TX::plan(K, D, t0, tend - 1, 0, wave, lane);
+    const typename TX::Plan pv = TX::plan(V, D, t0, tend - 1, 0, wave, lane);
+    // both k stages at once: the ring is free (the previous tile ended with a barrier)
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      char* st = smem + s * STAGE;
+      const int64_t off = (int64_t)s * BKK * 2;
+      char* w = st + 2 * TX::BYTES;
+#pragma unroll
+      for (int i = 0; i < TX::INSTR; ++i) TX::issue_one(st, pk, off, wave, i);
+#pragma unroll
+      for (int i = 0; i < TX::INSTR; ++i) TX::issue_one(st + TX::BYTES, pv, off, wave, i);
+#pragma unroll
+      for (int i = 0; i < TW::INSTR; ++i) TW::issue_one(w, p1, off, wave, i);
+#pragma unroll
+      for (int i = 0; i < TW::INSTR; ++i) TW::issue_one(w + TW::BYTES, p3, off, wave, i);
+#pragma unroll
+      for (int i = 0; i < TW::INSTR; ++i) TW::issue_one(w + 2 * TW::BYTES, p2, off, wave, i);
+    }
+    f32x4 accA[FM][FN], accB[FM][FN], accG[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) accA[i][j] = accB[i][j] = accG[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      if (s == 0) wait_vm<LPS>();
+      else wait_vm<0>();
+      bar();
+      const char* st = smem + s * STAGE;
+      const char* w = st + 2 * TX::BYTES;
+#pragma unroll
+      for (int kk = 0; kk < BKK; kk += 32) {
+        bf16x8 fk[FM], fv[FM], f1[FN], f3[FN], f2[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          fk[i] = dfrag_row<TX>(st, wm * 32 + i * 16, kk, lane);
+          fv[i] = dfrag_row<TX>(st + TX::BYTES, wm * 32 + i * 16, kk, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          f1[j] = dfrag_row<TW>(w, wn * (BJ / 2) + j * 16, kk, lane);
+          f3[j] = dfrag_row<TW>(w + TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+          f2[j] = dfrag_row<TW>(w + 2 * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            accA[i][j] = mfma(fk[i], f1[j], accA[i][j]);
+            accB[i][j] = mfma(fk[i], f3[j], accB[i][j]);
+            accG[i][j] = mfma(fv[i], f2[j], accG[i][j]);
+          }
+      }
+    }
+    bar();   // every wave is done with the W tiles: the update terms may replace them
+    if (tid < FBT * 3) s_lr[tid] = lrv;
+    if (a.beta != nullptr && jb == 0) {
+      const float bs = wave_sum(bval);
+      if (lane == 0 && wave < 2) s_red[wave] = bs;
+    }
+    __syncthreads();
+    if (a.beta != nullptr && jb == 0 && tid == 0) a.bpart[(int64_t)inst * a.tiles_t + tb] = s_red[0] + s_red[1];
+    // SwiGLU backward terms (zero past the chunk end: lr is zero there)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int tl = wm * 32 + i * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
+      float e1[4], e2[4], e3[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e1[r] = s_lr[(tl + r) * 3 + 0];
+        e2[r] = s_lr[(tl + r) * 3 + 1];
+        e3[r] = s_lr[(tl + r) * 3 + 2];
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = wn * (BJ / 2) + j * 16 + (lane & 15);
+        float u1[4], u3[4], u2[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = accA[i][j][r], bb = accB[i][j][r], gg = accG[i][j][r];
+          const float sg = fast_sigmoid(x);
+          const float sx = x * sg;
+          const float sp = sg * (1.0f + x * (1.0f - sg));
+          u1[r] = e1[r] * gg * bb * sp;
+          u3[r] = e3[r] * gg * sx;
+          u2[r] = e2[r] * sx * bb;
+        }
+        const int chunk = tl >> 3, half = (tl >> 2) & 1;
+        const float* terms[3] = {u1, u3, u2};
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+          const int row = m * BJ + col;
+          char* dst = erow(row) + ((chunk ^ (row & 15)) << 4) + (half << 3);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(terms[m][0], terms[m][1]),
+                                                      pack_bf16x2(terms[m][2], terms[m][3]));
+        }
+      }
+    }
+    __syncthreads();
+    // contraction over the tile's tokens: U1[j, c] += sum_t E1[t, j] K[t, c],
+    // U3 likewise, U2[c, j] += sum_t V[t, c] H[t, j]; this wave: hidden rows
+    // j0 + 32 jh .. +31, d columns 32 cq .. +31 (k stage cq / 2 of K, V)
+    {
+      const char* kt = smem + (cq >> 1) * STAGE;
+      const char* vt = kt + TX::BYTES;
+      const int cn = 32 * (cq & 1);
+#pragma unroll
+      for (int kk = 0; kk < FBT; kk += 32) {
+        bf16x8 fa1[2], fa3[2], fa2[2], fbk[2], fbv[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int jr = 32 * jh + 16 * i + (lane & 15);
+          const int chunk = (kk >> 3) + (lane >> 4);
+          fa1[i] = *reinterpret_cast<const bf16x8*>(erow(jr) + ((chunk ^ (jr & 15)) << 4));
+          fa3[i] = *reinterpret_cast<const bf16x8*>(erow(BJ + jr) + ((chunk ^ ((BJ + jr) & 15)) << 4));
+          fa2[i] = *reinterpret_cast<const bf16x8*>(erow(2 * BJ + jr) + ((chunk ^ ((2 * BJ + jr) & 15)) << 4));
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          fbk[c] = dfrag_col<TX>(kt, cn + 16 * c, kk, lane);
+          fbv[c] = dfrag_col<TX>(vt, cn + 16 * c, kk, lane);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            cu1[c][i] = mfma(fbk[c], fa1[i], cu1[c][i]);   // lane: hidden row j, 4 consecutive d columns
+            cu3[c][i] = mfma(fbk[c], fa3[i], cu3[c][i]);
+            cu2[i][c] = mfma(fa2[i], fbv[c], cu2[i][c]);   // lane: d row c, 4 consecutive hidden columns
+          }
+      }
+    }
+    __syncthreads();   // the ring is free for the next tile
+  }
+
+  // this workgroup's partial: U1, U3 rows j0 .. j0 + BJ - 1 and U2 columns
+  // j0 .. j0 + BJ - 1 (zeros if the split has no tile)
+  float* P = g.part + (int64_t)split * g.part_ss + (int64_t)inst * 3 * DD;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = j0 + 32 * jh + 16 * i + (lane & 15);
+      const int cc = 32 * cq + 16 * c + 4 * (lane >> 4);
+      const float y1[4] = {cu1[c][i][0], cu1[c][i][1], cu1[c][i][2], cu1[c][i][3]};
+      const float y3[4] = {cu3[c][i][0], cu3[c][i][1], cu3[c][i][2], cu3[c][i][3]};
+      store4(P + (int64_t)j * D + cc, y1);
+      store4(P + DD + (int64_t)j * D + cc, y3);
+      const int c2 = 32 * cq + 16 * c + (lane & 15);
+      const int j2 = j0 + 32 * jh + 16 * i + 4 * (lane >> 4);
+      const float y2[4] = {cu2[i][c][0], cu2[i][c][1], cu2[i][c][2], cu2[i][c][3]};
+      store4(P + 2 * DD + (int64_t)c2 * D + j2, y2);
+    }
+}
+
+// =========================================================================
 // bf16 apply forward tile (same contract as app_fwd_kernel)
 template <int BJ, int BKK, int NST, bool OUT = false>
 __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {

@@ -376,3 +376,35 @@ def test_zero_learning_rates_leave_the_state_unchanged(lact, opt):
               for i in range(wl.n_inst))
     log(f"  opt={opt} o err={err:.2e}")
     assert err <= wl.tol
+
+
+# ------------------------------------------------------------------ fused update (long chunks, d = dh = 128, bf16)
+@pytest.mark.parametrize("n,Lc,opt", [(2, 4096 + 77, W.OPT_GD), (6, 9000, W.OPT_MOMENTUM), (6, 6000, W.OPT_MUON),
+                                      (3, 20000, W.OPT_MUON_MOMENTUM)])
+def test_long_chunk_update_fused(lact, n, Lc, opt):
+    """Chunks of >= 4,096 tokens at d = dh = 128 in plain bf16 run the update
+    forward and the contraction as one kernel (several token tiles per split,
+    ragged last tile, beta partial sums for momentum); seq_stride > Lc."""
+    log(f"fused update n={n} Lc={Lc} opt={opt}")
+    D, S = 128, Lc + 50
+    inp = _rand_inputs(n, S, D, W.DTYPE_BF16, seed=Lc + opt)
+    rng = np.random.default_rng(8)
+    beta = rng.uniform(0.5, 0.99, (n, S)).astype(np.float32)
+    M0 = [(rng.standard_normal((n, D, D)) * 0.01).astype(np.float32) for _ in range(3)]
+    k, v, lr = to_dev(inp.k, torch), to_dev(inp.v, torch), to_dev(inp.lr, torch)
+    Ws = [to_dev(w, torch).clone() for w in (inp.W1, inp.W2, inp.W3)]
+    mom = opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    Ms = [to_dev(m, torch).clone() for m in M0] if mom else [None] * 3
+    lact.chunk_update(k, v, lr, to_dev(beta, torch) if mom else None, *Ws, *Ms, Lc=Lc, opt=opt, rec_planes=1)
+    torch.cuda.synchronize()
+    errs = {}
+    for i in range(n):
+        Wr, Mr = O.update_step([O.f64(inp.W1[i]), O.f64(inp.W2[i]), O.f64(inp.W3[i])],
+                               [O.f64(m[i]) for m in M0], O.f64(inp.k[i][:Lc]), O.f64(inp.v[i][:Lc]),
+                               O.f64(inp.lr[i][:Lc]), O.f64(beta[i][:Lc]), opt)
+        for j, nm in enumerate(["W1", "W2", "W3"]):
+            errs[nm] = max(errs.get(nm, 0), rel_err(from_dev(Ws[j], torch)[i], Wr[j]))
+            if mom:
+                errs["M" + nm[1]] = max(errs.get("M" + nm[1], 0), rel_err(from_dev(Ms[j], torch)[i], Mr[j]))
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= 2e-2, errs

@@ -249,10 +249,10 @@ bool fused_update(const lact_problem& p, int64_t C) {
   return profile_of(p) == PBF16 && p.d == UDW_D && p.dh == UDW_D && C >= 4096;
 }
 
-// its token split: about one workgroup per CU (n instances x 2 hidden
-// blocks per split), every split non-empty
+// its token split (64-token tiles): about one workgroup per CU (n
+// instances x 2 hidden blocks per split), every split non-empty
 void udw_split(const lact_problem& p, int64_t C, int& S, int& tps) {
-  const int64_t tt = (C + FBT - 1) / FBT;
+  const int64_t tt = (C + UDW2_T - 1) / UDW2_T;
   const int64_t per = 2 * (int64_t)std::max(1, p.n_inst);
   const int64_t s0 = std::max<int64_t>(1, std::min<int64_t>(tt, NCU / per));
   tps = (int)((tt + s0 - 1) / s0);
@@ -335,7 +335,8 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   w.nslots = nupd + 1;
   w.ldE = round128(plan.max_upd);
   w.h_rows = h_rows;
-  w.max_tt = (int)((plan.max_upd + FBT - 1) / FBT);
+  // beta partial sums: one per 128-token tile, or per 64-token tile of the fused update
+  w.max_tt = (int)((plan.max_upd + UDW2_T - 1) / UDW2_T);
   const size_t snap_el = (f == PF32) ? 4 : 2;
   w.snap_slot = align256(4 * n * D * Dh * snap_el);
   w.e = take(n * 3 * Dh * (size_t)w.ldE * rec_size(f));
@@ -687,9 +688,10 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
         ud.part_ss = (int64_t)n * 3 * DD;
         ud.tps = tps;
         ud.splits = S;
+        ud.nbp = (int)((C + UDW2_T - 1) / UDW2_T);
         const int64_t grid = (int64_t)n * S * (UDW_D / 64);
         KernelTimer kt(LACT_K_UPD, s);
-        LACT_LAUNCH((dupd_dw_kernel<64>), dim3((unsigned)grid), dim3(DG_THREADS), s, ud);
+        LACT_LAUNCH((dupd_dw2_kernel<64>), dim3((unsigned)grid), dim3(DG_THREADS), s, ud);
         HIP_TRY(hipGetLastError());
       }
     } else {
@@ -747,7 +749,9 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     oa.opt = p.opt;
     oa.renorm = (p.flags & LACT_NO_RENORM) ? 0 : 1;
     oa.bpart = reinterpret_cast<const float*>(ws + w.bpart);
-    oa.nbp = ua.tiles_t;
+    // beta partial sums: per 128-token tile, or per 64-token tile when fused
+    const int nbp = fused ? (int)((C + UDW2_T - 1) / UDW2_T) : ua.tiles_t;
+    oa.nbp = nbp;
     oa.inv_len = 1.0f / (float)C;
     oa.snap[0] = slot(nu + 1, 0);
     oa.snap[1] = slot(nu + 1, 2);
@@ -773,7 +777,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
           rm.M[1] = P.M3;
           rm.M[2] = P.M2;
           rm.bpart = reinterpret_cast<const float*>(ws + w.bpart);
-          rm.nbp = ua.tiles_t;
+          rm.nbp = nbp;
           rm.inv_len = 1.0f / (float)C;
         }
         LACT_LAUNCH(reduce_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(NT), s,

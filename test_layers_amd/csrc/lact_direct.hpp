@@ -52,6 +52,19 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
                : "memory", "m0");
 }
 
+// One global_load_lds_dword: 4 bytes per lane from g to LDS byte offset
+// m0 + 4 * lane (placement measured by an in-bounds probe); no register
+// outputs, completion tracked with vmcnt like dma16.
+__device__ __forceinline__ void dma4(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(m0)
+               : "memory", "m0");
+}
+
+// s_waitcnt for LDS traffic only (direct loads in flight are left alone)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
 // LDS tile of R rows x CC bf16 columns (CC = 32, 64 or 128), filled by NW
 // waves.  Chunk c (16 bytes) of row r is stored at chunk swz(r, c) of that
 // row.  The swizzle spreads the rows a fragment read touches over distinct
@@ -590,46 +603,51 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
 
 // =========================================================================
 // Fused update for long chunks at d = dh = 128 (plain bf16): the update
-// forward of each 128-token tile (as in dupd_fwd_kernel) followed at once by
+// forward of each token tile (as in dupd_fwd_kernel) followed at once by
 // the tile's share of the weight-gradient contraction, so the update terms E
 // never reach HBM (at this width their write and re-read are most of the
-// update's traffic).  After the forward both k stages of the tile's K and V
-// are still in the LDS ring; the tile's update terms (bf16) are staged in
-// the ring's W regions, which the forward has finished with; the tile's
-// contribution to U1, U3 (hidden rows j0 .. j0 + BJ - 1, all d columns) and
-// to U2 (all d rows, columns j0 ..) is accumulated in registers over the
-// workgroup's run of tiles, and one fp32 partial per workgroup is stored
-// (the optimiser sums the partials in a fixed order).
+// update's traffic).  The tile's update terms (bf16) are staged in LDS and
+// contracted at once with the tile's K and V, still in LDS from the forward;
+// the tile's contribution to U1, U3 (hidden rows j0 .. j0 + BJ - 1, all d
+// columns) and to U2 (all d rows, columns j0 ..) is accumulated in registers
+// over the workgroup's run of tiles, and one fp32 partial per workgroup is
+// stored (the optimiser sums the partials in a fixed order).
 struct UpdDwArgs {
   UpdFwdArgs u;          // chunk, inputs, snapshot of the weights (E unused)
   float* part;           // partials [splits, n, U1 | U3 | U2]
   int64_t part_ss;       // elements between partials
   int tps;               // token tiles per split
   int splits;
+  int nbp;               // beta partial sums per instance (one per token tile)
 };
 
 constexpr int UDW_D = 128;   // d = dh handled by the fused update
 
+// 64-token tiles, so that the next tile's loads overlap the current tile's
+// work: the workgroup's W rows stay in LDS for the whole run (48 KB), K, V
+// (both k stages), the learning rates and beta are double-buffered
+// (2 x 33 KB) and the update terms take 24 KB.  Learning rates and beta
+// arrive by 4-byte direct loads, so every load of a tile is counted by
+// vmcnt and a wait never drains the prefetch.
+constexpr int UDW2_T = 64;   // tokens per tile
+
 template <int BJ>
-__global__ __launch_bounds__(DG_THREADS) void dupd_dw_kernel(UpdDwArgs g) {
+__global__ __launch_bounds__(DG_THREADS) void dupd_dw2_kernel(UpdDwArgs g) {
   const UpdFwdArgs& a = g.u;
-  constexpr int BKK = 64, NK = UDW_D / BKK;
+  constexpr int BKK = 64;
   constexpr int NWV = DG_THREADS / WAVE;
-  static_assert(upd_w_waves(BJ, BKK) == NWV, "every wave loads W tiles");
-  using TX = DTile<FBT, BKK, NWV>;   // K, V: 128 tokens x BKK (rows = tokens)
-  using TW = DTile<BJ, BKK, NWV>;    // W1, W3, W2^T rows: BJ x BKK
-  constexpr int STAGE = 2 * TX::BYTES + 3 * TW::BYTES;
-  constexpr int LPS = 2 * TX::INSTR + 3 * TW::INSTR;
-  constexpr int FM = 2, FN = BJ / 32;
-  constexpr int EROWS = 3 * BJ;                     // update-term rows (U1 | U3 | U2 terms) x 128 tokens
-  constexpr int EHALF = 3 * TW::BYTES / (FBT * 2);  // rows that fit one stage's W region
-  static_assert(NK == 2 && 2 * EHALF >= EROWS && EHALF % 16 == 0, "update terms fit the two W regions");
-  __shared__ __attribute__((aligned(1024))) char smem[NK * STAGE];
-  __shared__ float s_red[2];
-  __shared__ float s_lr[FBT * 3];
+  using TT = DTile<UDW2_T, BKK, NWV>;   // 64 rows x 64 d: K, V stages (rows = tokens), W stages (rows = hidden)
+  static_assert(BJ == UDW2_T && TT::INSTR == 1 && UDW_D == 2 * BKK, "tile shapes");
+  constexpr int TB = TT::BYTES;
+  constexpr int ERB = UDW2_T * 2;         // update-term row: 64 tokens of bf16
+  __shared__ __attribute__((aligned(1024))) char s_w[6 * TB];         // W1 | W3 | W2^T, two k stages each
+  __shared__ __attribute__((aligned(1024))) char s_kv[2][4 * TB];     // K s0, K s1, V s0, V s1
+  __shared__ __attribute__((aligned(1024))) char s_e[3 * BJ * ERB];   // U1 | U3 | U2 terms x 64 tokens
+  __shared__ __attribute__((aligned(16))) float s_lr[2][UDW2_T * 3];
+  __shared__ __attribute__((aligned(16))) float s_beta[2][UDW2_T];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;     // forward: 32-token group, half of the BJ columns
+  const int wm = wave >> 2, wn = wave & 3;     // forward: 32 tokens x 16 hidden columns
   const int jh = wave >> 2, cq = wave & 3;     // contraction: 32 hidden rows x 32 d columns
   const int D = UDW_D;
   const int njb = UDW_D / BJ;
@@ -641,170 +659,167 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dw_kernel(UpdDwArgs g) {
   const int j0 = jb * BJ;
   const int64_t DD = (int64_t)D * D;
   const int64_t tend = a.upd_t0 + a.upd_len;
+  const int ntiles = (int)((a.upd_len + UDW2_T - 1) / UDW2_T);
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + inst * a.k_bs;
   const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + inst * a.x_bs;
-  const typename TW::Plan p1 = TW::plan(reinterpret_cast<const bf16_t*>(a.W1) + inst * DD, D, j0, D - 1, 0, wave, lane);
-  const typename TW::Plan p3 = TW::plan(reinterpret_cast<const bf16_t*>(a.W3) + inst * DD, D, j0, D - 1, 0, wave, lane);
-  const typename TW::Plan p2 = TW::plan(reinterpret_cast<const bf16_t*>(a.W2x) + inst * DD, D, j0, D - 1, 0, wave, lane);
-  // update-term row r (term r / BJ, hidden column r % BJ): 256 bytes of 128
-  // tokens, 16-byte chunks swizzled by the row, in stage r / EHALF's W region
-  auto erow = [&](int r) -> char* {
-    return smem + (r / EHALF) * STAGE + 2 * TX::BYTES + (r % EHALF) * (FBT * 2);
+  const float* LR = a.lr + inst * a.lr_bs;
+  const float* BETA = a.beta != nullptr ? a.beta + inst * a.beta_bs : nullptr;
+
+  // loads of tile tb into buffer b: K, V (4 per wave), then one 4-byte load
+  // per lane for waves 0-2 (learning rates) and wave 3 (beta, or a reload of
+  // learning rates when there is no beta) -- 5 loads for waves 0-3, 4 for 4-7
+  auto issue_tile = [&](int tb, int b) {
+    const int64_t t0 = a.upd_t0 + (int64_t)tb * UDW2_T;
+    const int nv = (int)min((int64_t)UDW2_T, tend - t0);
+    const typename TT::Plan pk = TT::plan(K, D, t0, tend - 1, 0, wave, lane);
+    const typename TT::Plan pv = TT::plan(V, D, t0, tend - 1, 0, wave, lane);
+    char* kv = s_kv[b];
+    TT::issue_one(kv, pk, 0, wave, 0);
+    TT::issue_one(kv + TB, pk, BKK * 2, wave, 0);
+    TT::issue_one(kv + 2 * TB, pv, 0, wave, 0);
+    TT::issue_one(kv + 3 * TB, pv, BKK * 2, wave, 0);
+    if (wave < 3) {
+      const int e = min(wave * 64 + lane, nv * 3 - 1);
+      dma4(LR + t0 * 3 + e, __builtin_amdgcn_readfirstlane(lds_off(&s_lr[b][wave * 64])));
+    } else if (wave == 3) {
+      const float* src = BETA != nullptr ? BETA + t0 + min(lane, nv - 1) : LR + t0 * 3 + min(lane, nv * 3 - 1);
+      dma4(src, __builtin_amdgcn_readfirstlane(lds_off(&s_beta[b][0])));
+    }
   };
 
-  f32x4 cu1[2][2], cu3[2][2], cu2[2][2];   // [c frag][j frag] for U1, U3; [j frag][c frag] for U2
+  f32x4 cu1[2][2], cu3[2][2], cu2[2][2];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y) cu1[x][y] = cu3[x][y] = cu2[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int tb_end = min(a.tiles_t, (split + 1) * g.tps);
-  for (int tb = split * g.tps; tb < tb_end; ++tb) {
-    const int64_t t0 = a.upd_t0 + (int64_t)tb * FBT;
-    float lrv = 0.f, bval = 0.f;
-    {
-      const float* lr = a.lr + inst * a.lr_bs + t0 * 3;
-      if (tid < FBT * 3 && t0 + tid / 3 < tend) lrv = lr[tid];
-      if (a.beta != nullptr && jb == 0 && tid < FBT && t0 + tid < tend) bval = a.beta[inst * a.beta_bs + t0 + tid];
+  const int tb0 = split * g.tps, tb1 = min(ntiles, tb0 + g.tps);
+  {
+    // the workgroup's W rows (hidden units j0 .. j0 + BJ - 1), both k stages
+    const bf16_t* Wm[3] = {reinterpret_cast<const bf16_t*>(a.W1) + inst * DD,
+                           reinterpret_cast<const bf16_t*>(a.W3) + inst * DD,
+                           reinterpret_cast<const bf16_t*>(a.W2x) + inst * DD};
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const typename TT::Plan pw = TT::plan(Wm[m], D, j0, D - 1, 0, wave, lane);
+      TT::issue_one(s_w + (2 * m) * TB, pw, 0, wave, 0);
+      TT::issue_one(s_w + (2 * m + 1) * TB, pw, BKK * 2, wave, 0);
     }
-    const typename TX::Plan pk = TX::plan(K, D, t0, tend - 1, 0, wave, lane);
-    const typename TX::Plan pv = TX::plan(V, D, t0, tend - 1, 0, wave, lane);
-    // both k stages at once: the ring is free (the previous tile ended with a barrier)
-#pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      char* st = smem + s * STAGE;
-      const int64_t off = (int64_t)s * BKK * 2;
-      char* w = st + 2 * TX::BYTES;
-#pragma unroll
-      for (int i = 0; i < TX::INSTR; ++i) TX::issue_one(st, pk, off, wave, i);
-#pragma unroll
-      for (int i = 0; i < TX::INSTR; ++i) TX::issue_one(st + TX::BYTES, pv, off, wave, i);
-#pragma unroll
-      for (int i = 0; i < TW::INSTR; ++i) TW::issue_one(w, p1, off, wave, i);
-#pragma unroll
-      for (int i = 0; i < TW::INSTR; ++i) TW::issue_one(w + TW::BYTES, p3, off, wave, i);
-#pragma unroll
-      for (int i = 0; i < TW::INSTR; ++i) TW::issue_one(w + 2 * TW::BYTES, p2, off, wave, i);
+  }
+  if (tb0 < tb1) issue_tile(tb0, 0);
+
+  for (int tb = tb0; tb < tb1; ++tb) {
+    const int b = (tb - tb0) & 1;
+    const int64_t t0 = a.upd_t0 + (int64_t)tb * UDW2_T;
+    if (tb + 1 < tb1) {
+      issue_tile(tb + 1, b ^ 1);   // that buffer was released at the end of the previous tile
+      if (wave < 4) wait_vm<5>();
+      else wait_vm<4>();
+    } else {
+      wait_vm<0>();
     }
-    f32x4 accA[FM][FN], accB[FM][FN], accG[FM][FN];
+    bar();   // this tile's K, V, learning rates and beta (and the W rows) have landed for every wave
+
+    // forward: A = K W1^T, B = K W3^T, G = V W2 on 64 tokens x 64 hidden units
+    f32x4 accA[2], accB[2], accG[2];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < 2; ++i) accA[i] = accB[i] = accG[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < FN; ++j) accA[i][j] = accB[i][j] = accG[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < UDW_D; kk += 32) {
+      const int st = kk / BKK, kl = kk % BKK;
+      const char* kt = s_kv[b] + st * TB;
+      bf16x8 fk[2], fv[2];
 #pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      if (s == 0) wait_vm<LPS>();
-      else wait_vm<0>();
-      bar();
-      const char* st = smem + s * STAGE;
-      const char* w = st + 2 * TX::BYTES;
+      for (int i = 0; i < 2; ++i) {
+        fk[i] = dfrag_row<TT>(kt, wm * 32 + i * 16, kl, lane);
+        fv[i] = dfrag_row<TT>(kt + 2 * TB, wm * 32 + i * 16, kl, lane);
+      }
+      const bf16x8 f1 = dfrag_row<TT>(s_w + st * TB, wn * 16, kl, lane);
+      const bf16x8 f3 = dfrag_row<TT>(s_w + (2 + st) * TB, wn * 16, kl, lane);
+      const bf16x8 f2 = dfrag_row<TT>(s_w + (4 + st) * TB, wn * 16, kl, lane);
 #pragma unroll
-      for (int kk = 0; kk < BKK; kk += 32) {
-        bf16x8 fk[FM], fv[FM], f1[FN], f3[FN], f2[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          fk[i] = dfrag_row<TX>(st, wm * 32 + i * 16, kk, lane);
-          fv[i] = dfrag_row<TX>(st + TX::BYTES, wm * 32 + i * 16, kk, lane);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          f1[j] = dfrag_row<TW>(w, wn * (BJ / 2) + j * 16, kk, lane);
-          f3[j] = dfrag_row<TW>(w + TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
-          f2[j] = dfrag_row<TW>(w + 2 * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            accA[i][j] = mfma(fk[i], f1[j], accA[i][j]);
-            accB[i][j] = mfma(fk[i], f3[j], accB[i][j]);
-            accG[i][j] = mfma(fv[i], f2[j], accG[i][j]);
-          }
+      for (int i = 0; i < 2; ++i) {
+        accA[i] = mfma(fk[i], f1, accA[i]);
+        accB[i] = mfma(fk[i], f3, accB[i]);
+        accG[i] = mfma(fv[i], f2, accG[i]);
       }
     }
-    bar();   // every wave is done with the W tiles: the update terms may replace them
-    if (tid < FBT * 3) s_lr[tid] = lrv;
-    if (a.beta != nullptr && jb == 0) {
-      const float bs = wave_sum(bval);
-      if (lane == 0 && wave < 2) s_red[wave] = bs;
+    // beta partial sum of this tile (chunk mean), once per tile
+    if (a.beta != nullptr && jb == 0 && wave == 0) {
+      const float bs = wave_sum(t0 + lane < tend ? s_beta[b][lane] : 0.f);
+      if (lane == 0) a.bpart[(int64_t)inst * g.nbp + tb] = bs;
     }
-    __syncthreads();
-    if (a.beta != nullptr && jb == 0 && tid == 0) a.bpart[(int64_t)inst * a.tiles_t + tb] = s_red[0] + s_red[1];
-    // SwiGLU backward terms (zero past the chunk end: lr is zero there)
+    // SwiGLU backward terms into the update-term rows (zero past the chunk end)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int tl = wm * 32 + i * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
-      float e1[4], e2[4], e3[4];
+      const int col = wn * 16 + (lane & 15);
+      float u1[4], u3[4], u2[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        e1[r] = s_lr[(tl + r) * 3 + 0];
-        e2[r] = s_lr[(tl + r) * 3 + 1];
-        e3[r] = s_lr[(tl + r) * 3 + 2];
+        const bool ok = t0 + tl + r < tend;
+        const float e1 = ok ? s_lr[b][(tl + r) * 3 + 0] : 0.f;
+        const float e2 = ok ? s_lr[b][(tl + r) * 3 + 1] : 0.f;
+        const float e3 = ok ? s_lr[b][(tl + r) * 3 + 2] : 0.f;
+        const float x = accA[i][r], bb = accB[i][r], gg = accG[i][r];
+        const float sg = fast_sigmoid(x);
+        const float sx = x * sg;
+        const float sp = sg * (1.0f + x * (1.0f - sg));
+        u1[r] = e1 * gg * bb * sp;
+        u3[r] = e3 * gg * sx;
+        u2[r] = e2 * sx * bb;
       }
+      const int chunk = tl >> 3, half = (tl >> 2) & 1;
+      const float* terms[3] = {u1, u3, u2};
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = wn * (BJ / 2) + j * 16 + (lane & 15);
-        float u1[4], u3[4], u2[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = accA[i][j][r], bb = accB[i][j][r], gg = accG[i][j][r];
-          const float sg = fast_sigmoid(x);
-          const float sx = x * sg;
-          const float sp = sg * (1.0f + x * (1.0f - sg));
-          u1[r] = e1[r] * gg * bb * sp;
-          u3[r] = e3[r] * gg * sx;
-          u2[r] = e2[r] * sx * bb;
-        }
-        const int chunk = tl >> 3, half = (tl >> 2) & 1;
-        const float* terms[3] = {u1, u3, u2};
-#pragma unroll
-        for (int m = 0; m < 3; ++m) {
-          const int row = m * BJ + col;
-          char* dst = erow(row) + ((chunk ^ (row & 15)) << 4) + (half << 3);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(terms[m][0], terms[m][1]),
-                                                      pack_bf16x2(terms[m][2], terms[m][3]));
-        }
+      for (int m = 0; m < 3; ++m) {
+        const int row = m * BJ + col;
+        char* dst = s_e + row * ERB + ((chunk ^ (row & 7)) << 4) + (half << 3);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(terms[m][0], terms[m][1]),
+                                                    pack_bf16x2(terms[m][2], terms[m][3]));
       }
     }
-    __syncthreads();
-    // contraction over the tile's tokens: U1[j, c] += sum_t E1[t, j] K[t, c],
-    // U3 likewise, U2[c, j] += sum_t V[t, c] H[t, j]; this wave: hidden rows
+    wait_lgkm0();
+    bar();   // update terms visible; the prefetch stays in flight
+
+    // contraction over the tile's 64 tokens: U1[j, c] += sum_t E1[t, j] K[t, c], U3
+    // likewise, U2[c, j] += sum_t V[t, c] H[t, j]; this wave: hidden rows
     // j0 + 32 jh .. +31, d columns 32 cq .. +31 (k stage cq / 2 of K, V)
     {
-      const char* kt = smem + (cq >> 1) * STAGE;
-      const char* vt = kt + TX::BYTES;
+      const char* kt = s_kv[b] + (cq >> 1) * TB;
+      const char* vt = kt + 2 * TB;
       const int cn = 32 * (cq & 1);
 #pragma unroll
-      for (int kk = 0; kk < FBT; kk += 32) {
+      for (int kk = 0; kk < UDW2_T; kk += 32) {
         bf16x8 fa1[2], fa3[2], fa2[2], fbk[2], fbv[2];
+        const int chunk = (kk >> 3) + (lane >> 4);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int jr = 32 * jh + 16 * i + (lane & 15);
-          const int chunk = (kk >> 3) + (lane >> 4);
-          fa1[i] = *reinterpret_cast<const bf16x8*>(erow(jr) + ((chunk ^ (jr & 15)) << 4));
-          fa3[i] = *reinterpret_cast<const bf16x8*>(erow(BJ + jr) + ((chunk ^ ((BJ + jr) & 15)) << 4));
-          fa2[i] = *reinterpret_cast<const bf16x8*>(erow(2 * BJ + jr) + ((chunk ^ ((2 * BJ + jr) & 15)) << 4));
+          fa1[i] = *reinterpret_cast<const bf16x8*>(s_e + jr * ERB + ((chunk ^ (jr & 7)) << 4));
+          fa3[i] = *reinterpret_cast<const bf16x8*>(s_e + (BJ + jr) * ERB + ((chunk ^ ((BJ + jr) & 7)) << 4));
+          fa2[i] = *reinterpret_cast<const bf16x8*>(s_e + (2 * BJ + jr) * ERB + ((chunk ^ ((2 * BJ + jr) & 7)) << 4));
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          fbk[c] = dfrag_col<TX>(kt, cn + 16 * c, kk, lane);
-          fbv[c] = dfrag_col<TX>(vt, cn + 16 * c, kk, lane);
+          fbk[c] = dfrag_col<TT>(kt, cn + 16 * c, kk, lane);
+          fbv[c] = dfrag_col<TT>(vt, cn + 16 * c, kk, lane);
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            cu1[c][i] = mfma(fbk[c], fa1[i], cu1[c][i]);   // lane: hidden row j, 4 consecutive d columns
+            cu1[c][i] = mfma(fbk[c], fa1[i], cu1[c][i]);
             cu3[c][i] = mfma(fbk[c], fa3[i], cu3[c][i]);
-            cu2[i][c] = mfma(fa2[i], fbv[c], cu2[i][c]);   // lane: d row c, 4 consecutive hidden columns
+            cu2[i][c] = mfma(fa2[i], fbv[c], cu2[i][c]);
           }
       }
     }
-    __syncthreads();   // the ring is free for the next tile
+    wait_lgkm0();
+    bar();   // every wave is done with this buffer and the update-term rows
   }
+  wait_vm<0>();   // no direct load may still be writing LDS when the workgroup ends
 
-  // this workgroup's partial: U1, U3 rows j0 .. j0 + BJ - 1 and U2 columns
-  // j0 .. j0 + BJ - 1 (zeros if the split has no tile)
   float* P = g.part + (int64_t)split * g.part_ss + (int64_t)inst * 3 * DD;
 #pragma unroll
   for (int c = 0; c < 2; ++c)

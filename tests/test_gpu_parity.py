@@ -408,3 +408,17 @@ def test_long_chunk_update_fused(lact, n, Lc, opt):
                 errs["M" + nm[1]] = max(errs.get("M" + nm[1], 0), rel_err(from_dev(Ms[j], torch)[i], Mr[j]))
     log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
     assert max(errs.values()) <= 2e-2, errs
+
+
+def test_layer_d128_persistent_apply_with_output_scale(lact):
+    """d = dh = 128 in bf16: the persistent apply (runs of 64-token tiles that
+    cross apply groups and instances, W rows reloaded on each crossing) with
+    the per-token output scale and raw q, k."""
+    import dataclasses
+    wl = dataclasses.replace(W.CONFIGS[9].scaled(n_inst=3, L=6000, chunk=1000), D=128, opt=W.OPT_GD)
+    log(f"persistent apply n={wl.n_inst} L={wl.L} chunks={wl.n_chunks}")
+    inp = W.generate(wl, seed=17)
+    gpu = run_gpu(wl, inp, torch, lact)
+    errs = compare(wl, inp, gpu)
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= wl.tol, errs

@@ -410,13 +410,13 @@ def test_long_chunk_update_fused(lact, n, Lc, opt):
     assert max(errs.values()) <= 2e-2, errs
 
 
-def test_layer_d128_persistent_apply_with_output_scale(lact):
-    """d = dh = 128 in bf16: the persistent apply (runs of 64-token tiles that
-    cross apply groups and instances, W rows reloaded on each crossing) with
-    the per-token output scale and raw q, k."""
+def test_layer_d128_fused_apply_with_output_scale(lact):
+    """d = dh = 128 in bf16: the fused apply (Hq kept in LDS) with the
+    per-token output scale in its epilogue and raw q, k, over several apply
+    groups and instances."""
     import dataclasses
     wl = dataclasses.replace(W.CONFIGS[9].scaled(n_inst=3, L=6000, chunk=1000), D=128, opt=W.OPT_GD)
-    log(f"persistent apply n={wl.n_inst} L={wl.L} chunks={wl.n_chunks}")
+    log(f"fused apply with output scale n={wl.n_inst} L={wl.L} chunks={wl.n_chunks}")
     inp = W.generate(wl, seed=17)
     gpu = run_gpu(wl, inp, torch, lact)
     errs = compare(wl, inp, gpu)

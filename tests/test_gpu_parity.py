@@ -422,3 +422,59 @@ def test_layer_d128_fused_apply_with_output_scale(lact):
     errs = compare(wl, inp, gpu)
     log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
     assert max(errs.values()) <= wl.tol, errs
+
+
+# ------------------------------------------------------------------ HIP graph capture
+@pytest.mark.parametrize("cid", [2, 4])
+def test_layer_replays_in_a_hip_graph(lact, cid):
+    """The layer only enqueues kernels on the caller's stream (no allocation,
+    memset, copy or host synchronisation), so a HIP graph can capture a whole
+    layer forward; every replay, with eager work and synchronisations between
+    replays, equals the eager call bitwise."""
+    wl = W.CONFIGS[2].scaled(n_inst=2, L=1500, chunk=512) if cid == 2 else SMALL[4]
+    inp = W.generate(wl, seed=21)
+    ref = run_gpu(wl, inp, torch, lact)
+    q, k, v, lr, beta = (to_dev(x, torch) for x in (inp.q, inp.k, inp.v, inp.lr, inp.beta))
+    W0 = [to_dev(w, torch) for w in (inp.W1, inp.W2, inp.W3)]
+    Ws = [w.clone() for w in W0]
+    mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    Ms = [torch.zeros_like(w) for w in Ws] if mom else [None] * 3
+    o = torch.zeros_like(q)
+    p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes)
+    ws = torch.empty(lact.workspace_size(p, wl.L, 0, wl.order, list(wl.bounds), list(wl.flags)),
+                     dtype=torch.uint8, device="cuda")
+
+    def layer():
+        for w, w0 in zip(Ws, W0):
+            w.copy_(w0)
+        for m in Ms:
+            if m is not None:
+                m.zero_()
+        lact.layer_forward(q, k, v, lr, beta, *Ws, *Ms, o, order=wl.order, opt=wl.opt, bounds=list(wl.bounds),
+                           flags=list(wl.flags), rec_planes=wl.rec_planes, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()                      # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+    applied = torch.zeros(wl.L, dtype=torch.bool, device="cuda")   # rows the schedule writes
+    for c, f in enumerate(wl.flags):
+        if f & W.APPLY:
+            applied[wl.bounds[c]:wl.bounds[c + 1]] = True
+    for rep in range(3):
+        o.fill_(-1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, applied], ref["o"][:, applied]), rep
+        assert bool((o[:, ~applied] == -1.0).all()), rep      # rows of non-APPLY chunks untouched
+        for j, key in enumerate(["W1", "W2", "W3"]):
+            assert torch.equal(Ws[j], ref[key]), (rep, key)
+            if mom:
+                assert torch.equal(Ms[j], ref["M" + key[1]]), (rep, key)
+        _ = float((o.float() * 2).sum())   # eager work between replays
+    log(f"  cfg{cid}: 3 graph replays equal the eager layer")

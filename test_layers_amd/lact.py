@@ -66,6 +66,16 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m test_layers_amd.build` "
                           "(the LaCT layer has no non-HIP implementation)")
+    # torch ships its own HIP runtime, reached through the unversioned name
+    # libamdhip64.so.  If liblact were loaded first, its dependency
+    # libamdhip64.so.7 would resolve to the system runtime and the process
+    # would hold two HIP (and HSA) runtimes; the second one to open the GPU
+    # sees no device.  Loading torch first makes liblact bind to the runtime
+    # that owns the tensors it is given.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     P = ctypes.POINTER(Problem)

@@ -236,3 +236,16 @@ def test_rectangular_fast_weights_accepted_and_sized():
     a = lact.workspace_size(P(d=128, dh=128), 512, 128)
     b = lact.workspace_size(P(d=128, dh=256), 512, 128)
     assert b > a
+
+
+def test_single_hip_runtime_in_process():
+    """Importing the binding before torch must not pull in a second HIP
+    runtime: torch's bundled one has to be the only one mapped, or the
+    library's calls see no device."""
+    code = ("import test_layers_amd.lact, torch\n"
+            "m = open('/proc/self/maps').read().splitlines()\n"
+            "print(sorted({l.split()[-1] for l in m if 'libamdhip64' in l}))\n")
+    r = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    libs = eval(r.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs

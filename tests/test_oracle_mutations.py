@@ -63,3 +63,46 @@ def test_planted_mistake_is_caught(name, tmp_path):
                         % (str(tmp_path), str(tmp_path), os.path.join(ROOT, "tests", "test_oracle_pins.py"))],
                        cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode == 1, f"{name} not caught:\n{r.stdout[-2000:]}\n{r.stderr[-2000:]}"
+
+
+# plausible mistakes in the backward oracle; each must make
+# tests/test_oracle_backward.py fail
+BWD_MUTATIONS = {
+    "silu_second_dropped": ("gA = gE1 * e1 * G * B * Spp", "gA = gE1 * e1 * G * B * Sp"),
+    "dK_update_term_dropped": ("dK = E1 @ gU1 + E3 @ gU3", "dK = E1 @ gU1"),
+    "dV_forward_term_dropped": ("dV = dV + gG @ W2.T", "dV = dV"),
+    "gB_lr_dropped": ("gB = gE1 * e1 * G * Sp + gH2 * e2 * S", "gB = gE1 * G * Sp + gH2 * e2 * S"),
+    "dlr_columns_swapped": ("dlr = np.stack([np.sum(gE1 * G * B * Sp, axis=1), np.sum(gH2 * S * B, axis=1),\n"
+                            "                    np.sum(gE3 * G * S, axis=1)], axis=1)",
+                            "dlr = np.stack([np.sum(gE3 * G * S, axis=1), np.sum(gH2 * S * B, axis=1),\n"
+                            "                    np.sum(gE1 * G * B * Sp, axis=1)], axis=1)"),
+    "renorm_projection_sign": ("(gY - dot * w), dot * W_old / n_old", "(gY + dot * w), dot * W_old / n_old"),
+    "renorm_old_norm_term_dropped": ("gW = [p[1] + p[0] for p in pairs]", "gW = [p[0] for p in pairs]"),
+    "ns_gram_not_symmetrised": ("g = a * g + P @ g + (gA + gA.T) @ X", "g = a * g + P @ g + gA @ X"),
+    "ns_normalisation_term_dropped": ("    if nG > 0:\n        gG = gG -", "    if False:\n        gG = gG -"),
+    "momentum_beta_grad_dropped": ("gbm = float(sum(np.sum(g * m) for g, m in zip(gMt, M)))", "gbm = 0.0"),
+    "momentum_state_grad_unscaled": ("gM = [bm * g for g in gMt]", "gM = [g for g in gMt]"),
+    "apply_vjp_W1_for_W3": ("dX = dA @ W1 + dB @ W3", "dX = dA @ W1 + dB @ W1"),
+    "update_then_apply_reads_old_state": ("dX, gWa = apply_vjp(*states[c + 1][0], q[a:b], dO[a:b])",
+                                          "dX, gWa = apply_vjp(*states[c][0], q[a:b], dO[a:b])"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_planted_backward_mistake_is_caught(name, tmp_path):
+    a, b = BWD_MUTATIONS[name]
+    src = open(os.path.join(ROOT, "oracle", "lact_backward.py")).read()
+    assert src.count(a) == 1, f"mutation anchor for {name} not found exactly once"
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "oracle", "__init__.py"), pkg / "__init__.py")
+    shutil.copy(os.path.join(ROOT, "oracle", "lact_oracle.py"), pkg / "lact_oracle.py")
+    (pkg / "lact_backward.py").write_text(src.replace(a, b))
+    env = dict(os.environ, PYTHONPATH=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-c",
+                        "import sys; sys.path.insert(0, %r); import oracle.lact_backward as ob; "
+                        "assert ob.__file__.startswith(%r); "
+                        "import pytest; sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', %r]))"
+                        % (str(tmp_path), str(tmp_path), os.path.join(ROOT, "tests", "test_oracle_backward.py"))],
+                       cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, f"{name} not caught:\n{r.stdout[-2000:]}\n{r.stderr[-2000:]}"

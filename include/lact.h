@@ -44,12 +44,12 @@
  * `stream` (a hipStream_t; NULL = the legacy default stream) without any
  * host synchronisation; completion is observed through the stream.
  *
- * Layouts (n = n_inst, D = d = dh):
+ * Layouts (n = n_inst, D = d, Dh = dh):
  *   q, k, v, o : [n, L, D]   io_dtype (F32 or BF16)
  *   lr         : [n, L, 3]   float32 (post-softplus learning rates)
  *   beta       : [n, L]      float32 (post-sigmoid momentum coefficients)
- *   W1, W3     : [n, D, D]   float32, row j = fan-in vector of hidden unit j
- *   W2         : [n, D, D]   float32, row r = fan-in vector of output unit r
+ *   W1, W3     : [n, Dh, D]  float32, row j = fan-in vector of hidden unit j
+ *   W2         : [n, D, Dh]  float32, row r = fan-in vector of output unit r
  *   M1, M2, M3 : same shapes as W1, W2, W3 (momentum state)
  *   ws         : workspace, >= lact_workspace_size(...) bytes, 256-B aligned
  *
@@ -74,7 +74,8 @@ extern "C" {
 typedef enum {
     LACT_OK = 0,
     LACT_ERR_INVALID_ARG = -1,        /* null/misaligned pointer, bad size, bad schedule */
-    LACT_ERR_UNSUPPORTED = -2,        /* d != dh, d not a multiple of 64 in [64, 1024],
+    LACT_ERR_UNSUPPORTED = -2,        /* d or dh not a multiple of 64 in [64, 1024],
+                                         a flag the entry point does not take,
                                          device is not gfx950 */
     LACT_ERR_WORKSPACE_TOO_SMALL = -3,
     LACT_ERR_NO_DEVICE = -4,          /* no HIP device visible */
@@ -106,7 +107,7 @@ typedef enum { LACT_APPLY_THEN_UPDATE = 0, LACT_UPDATE_THEN_APPLY = 1 } lact_ord
 typedef struct {
     int32_t n_inst;     /* B * nh independent instances (>= 0) */
     int32_t d;          /* model width per head */
-    int32_t dh;         /* fast-weight hidden width; must equal d */
+    int32_t dh;         /* fast-weight hidden width (a multiple of 64 in [64, 1024]) */
     int32_t io_dtype;   /* lact_dtype of q, k, v, o */
     int32_t opt;        /* lact_opt */
     int32_t ns_iters;   /* Newton-Schulz steps for MUON, 1..16 (5 = standard) */
@@ -190,6 +191,52 @@ lact_status lact_layer_forward_scaled(const lact_problem* p, const void* q, cons
                                       float* M1, float* M2, float* M3, void* o, void* ws,
                                       size_t ws_bytes, void* stream);
 
+/*
+ * Backward pass of lact_layer_forward (same problem, schedule and order
+ * arguments): vector-Jacobian products of the layer through the whole chunk
+ * recurrence.  The pages train the layer end to end but print no backward
+ * formulas; what is differentiated is exactly the forward map above (update
+ * and apply phases of "大块测试时训练（LaCT）技术解析" §2.1, eqs. 2 and 4-5;
+ * renormalisation and Newton-Schulz of §2.2.1, eqs. 8-10; momentum of
+ * "LaCT架构核心思想解析" §1.2), by the chain rule.  The gradients are those of
+ *
+ *     J = sum(dO * o) + sum_j sum(gW_j * W_j,final) + sum_j sum(gM_j * M_j,final)
+ *
+ * over o's APPLY rows, with respect to q, k, v, lr, beta and the initial
+ * state W1..W3, M1..M3 (as passed to lact_layer_forward, i.e. BEFORE it
+ * overwrote them).
+ *
+ * Inputs (device): q, k, v [n, L, D] io_dtype; lr [n, L, 3]; beta [n, L]
+ * (momentum optimisers, else may be NULL); W1..W3 initial weights, M1..M3
+ * initial momentum (momentum optimisers, else may be NULL); dO [n, L, D]
+ * io_dtype (rows outside APPLY chunks are not read); gW1..gW3, gM1..gM3
+ * cotangents of the final state, each may be NULL (= zero).  All read only.
+ * Outputs (device, float32, fully written): dq, dk, dv [n, L, D] (zero on
+ * rows outside APPLY, resp. UPDATE chunks); dlr [n, L, 3] (zero outside
+ * UPDATE chunks); dbeta [n, L] (momentum optimisers; may be NULL otherwise);
+ * dW1..dW3 (shapes of W1..W3); dM1..dM3 (shapes of M1..M3; may be NULL --
+ * for GD and MUON they equal gM).  The call recomputes the forward state
+ * trajectory itself with fp32-grade products (rec_planes is ignored) and
+ * runs every backward product fp32-grade.  LACT_QK_PREP is not supported
+ * (LACT_ERR_UNSUPPORTED).  Workspace: lact_backward_workspace_size bytes,
+ * 256-B aligned.  Errors as for lact_layer_forward; outputs are undefined
+ * after LACT_ERR_HIP.
+ */
+size_t lact_backward_workspace_size(const lact_problem* p, int64_t L, int64_t chunk, int32_t order,
+                                    const int64_t* bounds, const uint8_t* flags, int32_t n_chunks);
+
+lact_status lact_layer_backward(const lact_problem* p, const void* q, const void* k,
+                                const void* v, const float* lr, const float* beta, int64_t L,
+                                int64_t chunk, int32_t order, const int64_t* bounds,
+                                const uint8_t* flags, int32_t n_chunks, const float* W1,
+                                const float* W2, const float* W3, const float* M1,
+                                const float* M2, const float* M3, const void* dO,
+                                const float* gW1, const float* gW2, const float* gW3,
+                                const float* gM1, const float* gM2, const float* gM3, float* dq,
+                                float* dk, float* dv, float* dlr, float* dbeta, float* dW1,
+                                float* dW2, float* dW3, float* dM1, float* dM2, float* dM3,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* lact_status_str(lact_status s);
 
@@ -215,7 +262,9 @@ const char* lact_last_error(void);
 #define LACT_K_NS 5        /* Newton-Schulz products and reductions */
 #define LACT_K_SNAP 6      /* snapshot of the caller's weights at call start */
 #define LACT_K_PREP 7      /* q / k pre-processing (LACT_QK_PREP) */
-#define LACT_K_COUNT 8
+#define LACT_K_BWD_GEMM 8  /* backward: products of the reverse sweep */
+#define LACT_K_BWD_ELEM 9  /* backward: elementwise, row and reduction kernels */
+#define LACT_K_COUNT 10
 lact_status lact_timing_enable(int32_t kclass, int32_t on);
 lact_status lact_timing_read(int32_t kclass, double* total_ms, int64_t* launches);
 

@@ -17,6 +17,7 @@
 
 #include "lact.h"
 #include "lact_direct.hpp"
+#include "lact_backward.hpp"
 
 using namespace lact;
 
@@ -1119,6 +1120,8 @@ lact_status dispatch(const lact_problem& p, const Ptrs& P, int64_t seq_stride, c
   }
 }
 
+#include "lact_backward_host.hpp"
+
 }  // namespace
 
 // =================================================================== C ABI
@@ -1312,6 +1315,111 @@ lact_status lact_apply(const lact_problem* p, const void* q, int64_t Lq, int64_t
   P.o = o;
   P.ws = static_cast<char*>(ws);
   return dispatch(*p, P, seq_stride, plan, w, static_cast<hipStream_t>(stream));
+}
+
+size_t lact_backward_workspace_size(const lact_problem* p, int64_t L, int64_t chunk, int32_t order,
+                                    const int64_t* bounds, const uint8_t* flags, int32_t n_chunks) {
+  g_err.clear();
+  if (validate_problem(p) != LACT_OK) return 0;
+  std::vector<int64_t> b;
+  std::vector<uint8_t> f;
+  if (make_schedule(L, chunk, order, bounds, flags, n_chunks, b, f) != LACT_OK) return 0;
+  return std::max<size_t>(bwd_layout(*p, b, f).total, 256);
+}
+
+lact_status lact_layer_backward(const lact_problem* p, const void* q, const void* k, const void* v, const float* lr,
+                                const float* beta, int64_t L, int64_t chunk, int32_t order, const int64_t* bounds,
+                                const uint8_t* flags, int32_t n_chunks, const float* W1, const float* W2,
+                                const float* W3, const float* M1, const float* M2, const float* M3, const void* dO,
+                                const float* gW1, const float* gW2, const float* gW3, const float* gM1,
+                                const float* gM2, const float* gM3, float* dq, float* dk, float* dv, float* dlr,
+                                float* dbeta, float* dW1, float* dW2, float* dW3, float* dM1, float* dM2, float* dM3,
+                                void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  lact_status r = validate_problem(p);
+  if (r) return r;
+  if (p->flags & LACT_QK_PREP) return fail(LACT_ERR_UNSUPPORTED, "the backward pass takes pre-processed q, k only");
+  std::vector<int64_t> b;
+  std::vector<uint8_t> f;
+  r = make_schedule(L, chunk, order, bounds, flags, n_chunks, b, f);
+  if (r) return r;
+  if (p->n_inst == 0) return LACT_OK;
+  bool any_upd = false, any_app = false;
+  for (uint8_t x : f) {
+    any_upd |= (x & LACT_CHUNK_UPDATE) != 0;
+    any_app |= (x & LACT_CHUNK_APPLY) != 0;
+  }
+  const bool mom = uses_momentum(p->opt);
+  NEED(W1, 16);
+  NEED(W2, 16);
+  NEED(W3, 16);
+  NEED(dW1, 16);
+  NEED(dW2, 16);
+  NEED(dW3, 16);
+  if (L > 0) {
+    NEED(dq, 16);
+    NEED(dk, 16);
+    NEED(dv, 16);
+    NEED(dlr, 4);
+  }
+  if (any_app) {
+    NEED(q, 16);
+    NEED(dO, 16);
+  }
+  if (any_upd) {
+    NEED(k, 16);
+    NEED(v, 16);
+    NEED(lr, 4);
+  }
+  if (mom) {
+    NEED(M1, 16);
+    NEED(M2, 16);
+    NEED(M3, 16);
+    if (any_upd) {
+      NEED(beta, 4);
+      NEED(dbeta, 4);
+    }
+  }
+  for (const void* g : {(const void*)gW1, (const void*)gW2, (const void*)gW3, (const void*)gM1, (const void*)gM2,
+                        (const void*)gM3, (const void*)dM1, (const void*)dM2, (const void*)dM3, (const void*)dbeta})
+    if (g && !aligned(g, 4)) return fail(LACT_ERR_INVALID_ARG, "misaligned optional pointer");
+  if (!aligned(gW1, 16) || !aligned(gW2, 16) || !aligned(gW3, 16) || !aligned(gM1, 16) || !aligned(gM2, 16) ||
+      !aligned(gM3, 16))
+    return fail(LACT_ERR_INVALID_ARG, "state cotangents must be 16-byte aligned");
+  const BwdWs w = bwd_layout(*p, b, f);
+  NEED(ws, 256);
+  if (ws_bytes < w.total)
+    return fail(LACT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  r = check_device();
+  if (r) return r;
+  BwdPtrs P;
+  P.q = q;
+  P.k = k;
+  P.v = v;
+  P.dO = dO;
+  P.lr = lr;
+  P.beta = beta;
+  const float* Ws[3] = {W1, W2, W3};
+  const float* Ms[3] = {M1, M2, M3};
+  const float* gWs[3] = {gW1, gW2, gW3};
+  const float* gMs[3] = {gM1, gM2, gM3};
+  float* dWs[3] = {dW1, dW2, dW3};
+  float* dMs[3] = {dM1, dM2, dM3};
+  for (int j = 0; j < 3; ++j) {
+    P.W[j] = Ws[j];
+    P.M[j] = mom ? Ms[j] : nullptr;
+    P.gW[j] = gWs[j];
+    P.gM[j] = gMs[j];
+    P.dW[j] = dWs[j];
+    P.dM[j] = dMs[j];
+  }
+  P.dq = dq;
+  P.dk = dk;
+  P.dv = dv;
+  P.dlr = dlr;
+  P.dbeta = dbeta;
+  P.ws = static_cast<char*>(ws);
+  return run_backward(*p, P, L, order, b, f, w, static_cast<hipStream_t>(stream));
 }
 
 lact_status lact_timing_enable(int32_t kclass, int32_t on) {

@@ -1,0 +1,508 @@
+// Host side of the layer's backward pass: workspace layout, the replay of the
+// forward state trajectory and the reverse sweep over the chunk schedule.
+// Included by lact.hip inside its anonymous namespace, after the forward
+// dispatch (it reuses the forward's validation, schedule, product launcher
+// and chunk update).
+//
+// The reverse sweep follows the chain rule through the forward steps of
+// "大块测试时训练（LaCT）技术解析" §2.1 (apply, eq. 2; update, eqs. 4-5) and
+// §2.2.1 (renormalisation, eq. 8; Newton-Schulz, eqs. 9-10) and the momentum
+// of "LaCT架构核心思想解析" §1.2, chunk by chunk from the last to the first:
+//   apply chunk:   dq = dAq W1 + dBq W3;  dW1 += dAq^T q, dW3 += dBq^T q,
+//                  dW2 += dO^T Hq   (Hq = silu(q W1^T) (q W3^T), dHq = dO W2)
+//   update chunk:  renorm backward (per row), optimiser backward (momentum:
+//                  linear; Muon: Newton-Schulz backward through the stored
+//                  iterates), then the update terms' backward:
+//                  gE1 = k gU1^T, gE3 = k gU3^T, gH2 = v gU2,
+//                  dk = E1 gU1 + E3 gU3 + gA W1 + gB W3, dv = H2 gU2^T + gG W2^T,
+//                  dW1 += gA^T k, dW3 += gB^T k, dW2 += v^T gG.
+// Every product runs on the grouped GEMM with fp32 operands split into three
+// bf16 planes (bf16 inputs are exact in one plane).
+
+// ----------------------------------------------------------------- products
+struct BOp {
+  const void* p;
+  int64_t ld, bs;
+  bool colk;   // element (m, k) at p[k ld + m]; else at p[m ld + k]
+  bool bf16;
+};
+inline BOp bop(const void* p, int64_t ld, int64_t bs, bool colk, bool bf16 = false) {
+  return BOp{p, ld, bs, colk, bf16};
+}
+
+template <typename TA, int PA, bool CA, typename TB, int PB, bool CB>
+lact_status bgemm_t(GemmArgs& g, hipStream_t s) {
+  const int64_t t = (int64_t)((g.g[0].M + 63) / 64) * ((g.N + 63) / 64) * g.batch;
+  if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+  if (t == 0) return LACT_OK;
+  g.g[0].tiles = (int)t;
+  KernelTimer kt(LACT_K_BWD_GEMM, s);
+  return launch_gemm_t<TA, PA, CA, TB, PB, CB, float, 64>(g, t, s);
+}
+
+// C_b[m, n] = alpha sum_k A_b(m, k) B_b(n, k) + beta Cin_b[m, n] for b < batch
+// (Cin has C's strides and may be C itself; NULL: no accumulation)
+lact_status bgemm(BOp A, BOp B, float* C, int64_t ldc, int64_t c_bs, int M, int N, int64_t K, int batch, float alpha,
+                  const float* Cin, float beta, hipStream_t s) {
+  if (M <= 0 || N <= 0 || batch <= 0) return LACT_OK;
+  GemmArgs g = gemm_args();
+  g.g[0].A = A.p;
+  g.g[0].B = B.p;
+  g.g[0].C = C;
+  g.g[0].Cin = Cin;
+  g.g[0].M = M;
+  g.lda = A.ld;
+  g.a_bs = A.bs;
+  g.ldb = B.ld;
+  g.b_bs = B.bs;
+  g.ldc = ldc;
+  g.c_bs = c_bs;
+  g.ldcin = ldc;
+  g.cin_bs = c_bs;
+  g.N = N;
+  g.K = g.kps = K;
+  g.batch = batch;
+  g.alpha = alpha;
+  g.beta = beta;
+  if (!A.bf16 && !B.bf16) {
+    if (!A.colk && !B.colk) return bgemm_t<float, 3, false, float, 3, false>(g, s);
+    if (!A.colk && B.colk) return bgemm_t<float, 3, false, float, 3, true>(g, s);
+    if (A.colk && B.colk) return bgemm_t<float, 3, true, float, 3, true>(g, s);
+  } else if (A.bf16 && !B.bf16) {
+    if (!A.colk && !B.colk) return bgemm_t<bf16_t, 1, false, float, 3, false>(g, s);
+    if (!A.colk && B.colk) return bgemm_t<bf16_t, 1, false, float, 3, true>(g, s);
+    if (A.colk && B.colk) return bgemm_t<bf16_t, 1, true, float, 3, true>(g, s);
+  } else if (!A.bf16 && B.bf16) {
+    if (A.colk && B.colk) return bgemm_t<float, 3, true, bf16_t, 1, true>(g, s);
+  }
+  return fail(LACT_ERR_UNSUPPORTED, "internal: backward product form");
+}
+
+// grid of a grid-stride elementwise kernel
+inline unsigned ew_grid(int64_t total) {
+  const int64_t b = (total + NT - 1) / NT;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 8 * NCU));
+}
+
+#define BWD_LAUNCH(kernel, grid, ...)                      \
+  do {                                                     \
+    KernelTimer kt_(LACT_K_BWD_ELEM, s);                   \
+    LACT_LAUNCH(kernel, grid, dim3(NT), s, __VA_ARGS__);   \
+    HIP_TRY(hipGetLastError());                            \
+  } while (0)
+
+constexpr int BWD_NB = 32;    // partial sums per matrix (Newton-Schulz reductions)
+constexpr int BWD_NBM = 64;   // partial sums per instance (momentum)
+
+// ----------------------------------------------------------------- layout
+struct BwdWs {
+  int nu = 0;                 // update chunks
+  int64_t cmax = 0;           // longest chunk
+  size_t stW = 0, stM = 0;    // state slots: (nu + 1) x [W1 | W2 | W3] (and M)
+  size_t fws = 0, fws_bytes = 0;
+  size_t tok[9] = {};         // [n, cmax, dh] fp32 token buffers
+  size_t U = 0, step = 0, gWp = 0, gU = 0, gM = 0, gX = 0;
+  size_t X = 0, Am = 0, Pm = 0, gP = 0, gA = 0, Qm = 0, g0 = 0, g1 = 0, nrm = 0, part = 0;
+  size_t bbar = 0, mpart = 0;
+  size_t total = 0;
+};
+
+lact_problem replay_problem(const lact_problem& p) {
+  lact_problem f = p;
+  f.rec_planes = 3;   // fp32-grade recurrence
+  f.flags &= LACT_NO_RENORM;
+  return f;
+}
+
+Plan single_update(int64_t t0, int64_t len) {
+  Plan pl;
+  Step st;
+  st.upd_t0 = t0;
+  st.upd_len = len;
+  pl.steps.push_back(st);
+  pl.max_upd = len;
+  return pl;
+}
+
+BwdWs bwd_layout(const lact_problem& p, const std::vector<int64_t>& b, const std::vector<uint8_t>& f) {
+  BwdWs w;
+  const size_t n = (size_t)std::max(0, p.n_inst), D = (size_t)p.d, Dh = (size_t)p.dh;
+  const size_t DD = D * Dh, MDB = 3 * n * DD * 4;
+  const size_t m = std::min(D, Dh);
+  const lact_problem pf = replay_problem(p);
+  for (size_t c = 0; c < f.size(); ++c) {
+    const int64_t len = b[c + 1] - b[c];
+    w.cmax = std::max(w.cmax, len);
+    if (f[c] & LACT_CHUNK_UPDATE) {
+      ++w.nu;
+      w.fws_bytes = std::max(w.fws_bytes, layout(pf, single_update(b[c], len)).total);
+    }
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  w.stW = take((size_t)(w.nu + 1) * MDB);
+  if (uses_momentum(p.opt)) w.stM = take((size_t)(w.nu + 1) * MDB);
+  w.fws = take(w.fws_bytes);
+  for (int i = 0; i < 9; ++i) w.tok[i] = take(n * (size_t)w.cmax * Dh * 4);
+  w.U = take(MDB);
+  w.step = take(MDB);
+  w.gWp = take(MDB);
+  w.gU = take(MDB);
+  w.gM = take(MDB);
+  w.gX = take(MDB);
+  if (uses_ns(p.opt)) {
+    const size_t it = (size_t)p.ns_iters;
+    const size_t MMB = 3 * n * m * m * 4;
+    w.X = take((it + 1) * MDB);
+    w.Am = take(it * MMB);
+    w.Pm = take(it * MMB);
+    w.gP = take(MMB);
+    w.gA = take(MMB);
+    w.Qm = take(MMB);
+    w.g0 = take(MDB);
+    w.g1 = take(MDB);
+    w.nrm = take(3 * n * 4);
+    w.part = take(3 * n * BWD_NB * 4);
+  }
+  w.bbar = take(n * 4);
+  w.mpart = take(n * BWD_NBM * 4);
+  w.total = off;
+  return w;
+}
+
+// ----------------------------------------------------------------- the pass
+struct BwdPtrs {
+  const void *q, *k, *v, *dO;
+  const float *lr, *beta;
+  const float *W[3], *M[3], *gW[3], *gM[3];
+  float *dq, *dk, *dv, *dlr, *dbeta;
+  float *dW[3], *dM[3];
+  char* ws;
+};
+
+lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int32_t order,
+                         const std::vector<int64_t>& b, const std::vector<uint8_t>& f, const BwdWs& w,
+                         hipStream_t s) {
+  const int n = p.n_inst, D = p.d, Dh = p.dh;
+  const int64_t DD = (int64_t)D * Dh, MD = 3 * (int64_t)n * DD;
+  const int m = std::min(D, Dh), kf = std::max(D, Dh);
+  const int64_t MM = (int64_t)m * m;
+  const bool bf = p.io_dtype == LACT_DTYPE_BF16;
+  const size_t esz = bf ? 2 : 4;
+  const int64_t x_bs = L * D;          // instance stride of q, k, v, dO, dq, dk, dv
+  const int64_t buf_bs = w.cmax * Dh;  // instance stride of the token buffers
+  const bool mom = uses_momentum(p.opt), ns = uses_ns(p.opt);
+  const bool renorm = !(p.flags & LACT_NO_RENORM);
+  char* ws = P.ws;
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  // a weight-shaped set at byte offset `off` (W1 | W2 | W3, each [n, DD])
+  auto set = [&](size_t off) {
+    MatP r;
+    for (int j = 0; j < 3; ++j) r.p[j] = fp(off) + (int64_t)j * n * DD;
+    return r;
+  };
+  auto cset = [](const MatP& a) {
+    MatC r;
+    for (int j = 0; j < 3; ++j) r.p[j] = a.p[j];
+    return r;
+  };
+  auto slotW = [&](int u) { return set(w.stW + (size_t)u * MD * 4); };
+  auto slotM = [&](int u) { return set(w.stM + (size_t)u * MD * 4); };
+  float* tk[9];
+  for (int i = 0; i < 9; ++i) tk[i] = fp(w.tok[i]);
+  const MatP U = set(w.U), STEP = set(w.step), GWP = set(w.gWp), GU = set(w.gU), GM = set(w.gM), GX = set(w.gX);
+  MatP DW;
+  for (int j = 0; j < 3; ++j) DW.p[j] = P.dW[j];
+  lact_status r;
+
+  // ---- outputs start at zero (rows outside the chunks that write them stay zero)
+  BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L * D)), P.dq, (int64_t)n * L * D, 0.f);
+  BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L * D)), P.dk, (int64_t)n * L * D, 0.f);
+  BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L * D)), P.dv, (int64_t)n * L * D, 0.f);
+  BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L * 3)), P.dlr, (int64_t)n * L * 3, 0.f);
+  if (P.dbeta) BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L)), P.dbeta, (int64_t)n * L, 0.f);
+  // running cotangents of the state: W in the caller's dW arrays, M in the workspace
+  for (int j = 0; j < 3; ++j) {
+    const size_t mb = (size_t)n * DD * 4;
+    if (P.gW[j]) HIP_TRY(hipMemcpyAsync(DW.p[j], P.gW[j], mb, hipMemcpyDeviceToDevice, s));
+    else BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * DD)), DW.p[j], (int64_t)n * DD, 0.f);
+    if (P.gM[j]) HIP_TRY(hipMemcpyAsync(GM.p[j], P.gM[j], mb, hipMemcpyDeviceToDevice, s));
+    else BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * DD)), GM.p[j], (int64_t)n * DD, 0.f);
+  }
+
+  // ---- replay of the forward state trajectory: slot u = state before update u
+  {
+    const MatP s0 = slotW(0);
+    for (int j = 0; j < 3; ++j)
+      HIP_TRY(hipMemcpyAsync(s0.p[j], P.W[j], (size_t)n * DD * 4, hipMemcpyDeviceToDevice, s));
+    if (mom) {
+      const MatP m0 = slotM(0);
+      for (int j = 0; j < 3; ++j)
+        HIP_TRY(hipMemcpyAsync(m0.p[j], P.M[j], (size_t)n * DD * 4, hipMemcpyDeviceToDevice, s));
+    }
+    const lact_problem pf = replay_problem(p);
+    int u = 0;
+    for (size_t c = 0; c < f.size(); ++c) {
+      if (!(f[c] & LACT_CHUNK_UPDATE)) continue;
+      const MatP wa = slotW(u), wb = slotW(u + 1);
+      HIP_TRY(hipMemcpyAsync(wb.p[0], wa.p[0], (size_t)MD * 4, hipMemcpyDeviceToDevice, s));
+      Ptrs F;
+      F.k = P.k;
+      F.v = P.v;
+      F.lr = P.lr;
+      F.beta = P.beta;
+      F.W1 = wb.p[0];
+      F.W2 = wb.p[1];
+      F.W3 = wb.p[2];
+      if (mom) {
+        const MatP ma = slotM(u), mb = slotM(u + 1);
+        HIP_TRY(hipMemcpyAsync(mb.p[0], ma.p[0], (size_t)MD * 4, hipMemcpyDeviceToDevice, s));
+        F.M1 = mb.p[0];
+        F.M2 = mb.p[1];
+        F.M3 = mb.p[2];
+      }
+      F.ws = ws + w.fws;
+      const Plan pl = single_update(b[c], b[c + 1] - b[c]);
+      r = dispatch(pf, F, L, pl, layout(pf, pl), s);
+      if (r) return r;
+      ++u;
+    }
+  }
+
+  // ---- Newton-Schulz forward, keeping the iterates (frame layout)
+  const int iters = p.ns_iters;
+  auto Xi = [&](int i) { return fp(w.X) + (int64_t)i * MD; };
+  auto Ai = [&](int i) { return fp(w.Am) + (int64_t)i * 3 * n * MM; };
+  auto Pi = [&](int i) { return fp(w.Pm) + (int64_t)i * 3 * n * MM; };
+  const float na = 3.4445f, nb = -4.7750f, nc = 2.0315f;
+  const float ns_eps = 1e-7f;
+  auto ns_forward = [&](const MatC& G) -> lact_status {
+    MatC none;
+    none.p[0] = none.p[1] = none.p[2] = nullptr;
+    BWD_LAUNCH(bwd_dot_kernel, dim3(BWD_NB, 3 * n), G, none, fp(w.part), n, DD, BWD_NB);
+    BWD_LAUNCH(bwd_ns_init_kernel, dim3(ew_grid(MD)), G, (const float*)fp(w.part), BWD_NB, Xi(0), fp(w.nrm), n, D,
+               Dh, ns_eps);
+    for (int i = 0; i < iters; ++i) {
+      lact_status q;
+      // A = X X^T ; P = c A A + b A ; X' = P X + a X
+      if ((q = bgemm(bop(Xi(i), kf, DD, false), bop(Xi(i), kf, DD, false), Ai(i), m, MM, m, m, kf, 3 * n, 1.f,
+                     nullptr, 0.f, s)))
+        return q;
+      if ((q = bgemm(bop(Ai(i), m, MM, false), bop(Ai(i), m, MM, false), Pi(i), m, MM, m, m, m, 3 * n, nc, Ai(i),
+                     nb, s)))
+        return q;
+      if ((q = bgemm(bop(Pi(i), m, MM, false), bop(Xi(i), kf, DD, true), Xi(i + 1), kf, DD, m, kf, m, 3 * n, 1.f,
+                     Xi(i), na, s)))
+        return q;
+    }
+    return LACT_OK;
+  };
+  // cotangent of G for Y = NS(G) given gY (original layout) -> out; uses the
+  // iterates of the last ns_forward(G)
+  auto ns_backward = [&](const MatC& G, const MatC& gY, const MatP& out) -> lact_status {
+    float* g0 = fp(w.g0);
+    float* g1 = fp(w.g1);
+    BWD_LAUNCH(bwd_frame_in_kernel, dim3(ew_grid(MD)), gY, g0, n, D, Dh);
+    for (int i = iters - 1; i >= 0; --i) {
+      lact_status q;
+      // gP = g X^T
+      if ((q = bgemm(bop(g0, kf, DD, false), bop(Xi(i), kf, DD, false), fp(w.gP), m, MM, m, m, kf, 3 * n, 1.f,
+                     nullptr, 0.f, s)))
+        return q;
+      // gA = c gP A + b gP, then += c A gP
+      if ((q = bgemm(bop(fp(w.gP), m, MM, false), bop(Ai(i), m, MM, false), fp(w.gA), m, MM, m, m, m, 3 * n, nc,
+                     fp(w.gP), nb, s)))
+        return q;
+      if ((q = bgemm(bop(Ai(i), m, MM, false), bop(fp(w.gP), m, MM, true), fp(w.gA), m, MM, m, m, m, 3 * n, nc,
+                     fp(w.gA), 1.f, s)))
+        return q;
+      BWD_LAUNCH(bwd_symadd_kernel, dim3(ew_grid(3 * n * MM)), (const float*)fp(w.gA), fp(w.Qm), m,
+                 (int64_t)3 * n);
+      // g' = P g + a g + (gA + gA^T) X
+      if ((q = bgemm(bop(Pi(i), m, MM, false), bop(g0, kf, DD, true), g1, kf, DD, m, kf, m, 3 * n, 1.f, g0, na,
+                     s)))
+        return q;
+      if ((q = bgemm(bop(fp(w.Qm), m, MM, false), bop(Xi(i), kf, DD, true), g1, kf, DD, m, kf, m, 3 * n, 1.f, g1,
+                     1.f, s)))
+        return q;
+      std::swap(g0, g1);
+    }
+    // back to the original layout (into gX), then the normalisation backward
+    BWD_LAUNCH(bwd_frame_out_kernel, dim3(ew_grid(MD)), (const float*)g0, GX, 1.f, n, D, Dh);
+    BWD_LAUNCH(bwd_dot_kernel, dim3(BWD_NB, 3 * n), cset(GX), G, fp(w.part), n, DD, BWD_NB);
+    BWD_LAUNCH(bwd_ns_finish_kernel, dim3(ew_grid(MD)), cset(GX), G, (const float*)fp(w.nrm),
+               (const float*)fp(w.part), BWD_NB, out, 1.f, n, DD, ns_eps);
+    return LACT_OK;
+  };
+
+  // ---- apply backward of rows [t0, t0 + C) read with weights Wa
+  auto apply_bwd = [&](const MatC& Wa, int64_t t0, int64_t C) -> lact_status {
+    lact_status q;
+    const char* Q = static_cast<const char*>(P.q) + (size_t)t0 * D * esz;
+    const char* dO = static_cast<const char*>(P.dO) + (size_t)t0 * D * esz;
+    // Aq = q W1^T, Bq = q W3^T, dHq = dO W2
+    if ((q = bgemm(bop(Q, D, x_bs, false, bf), bop(Wa.p[0], D, DD, false), tk[0], Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    if ((q = bgemm(bop(Q, D, x_bs, false, bf), bop(Wa.p[2], D, DD, false), tk[1], Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    if ((q = bgemm(bop(dO, D, x_bs, false, bf), bop(Wa.p[1], Dh, DD, true), tk[2], Dh, buf_bs, (int)C, Dh, D, n,
+                   1.f, nullptr, 0.f, s)))
+      return q;
+    // -> dAq, dBq, Hq
+    BWD_LAUNCH(bwd_app_elem_kernel, dim3(ew_grid((int64_t)n * C * Dh)), tk[0], tk[1], tk[2], n, C, Dh, buf_bs);
+    // dW2 += dO^T Hq ; dW1 += dAq^T q ; dW3 += dBq^T q
+    if ((q = bgemm(bop(dO, D, x_bs, true, bf), bop(tk[2], Dh, buf_bs, true), DW.p[1], Dh, DD, D, Dh, C, n, 1.f,
+                   DW.p[1], 1.f, s)))
+      return q;
+    if ((q = bgemm(bop(tk[0], Dh, buf_bs, true), bop(Q, D, x_bs, true, bf), DW.p[0], D, DD, Dh, D, C, n, 1.f,
+                   DW.p[0], 1.f, s)))
+      return q;
+    if ((q = bgemm(bop(tk[1], Dh, buf_bs, true), bop(Q, D, x_bs, true, bf), DW.p[2], D, DD, Dh, D, C, n, 1.f,
+                   DW.p[2], 1.f, s)))
+      return q;
+    // dq = dAq W1 + dBq W3
+    float* dq = P.dq + t0 * D;
+    if ((q = bgemm(bop(tk[0], Dh, buf_bs, false), bop(Wa.p[0], D, DD, true), dq, D, x_bs, (int)C, D, Dh, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    return bgemm(bop(tk[1], Dh, buf_bs, false), bop(Wa.p[2], D, DD, true), dq, D, x_bs, (int)C, D, Dh, n, 1.f, dq,
+                 1.f, s);
+  };
+
+  // ---- update backward of chunk [t0, t0 + C), update ordinal u
+  auto update_bwd = [&](int u, int64_t t0, int64_t C) -> lact_status {
+    lact_status q;
+    const MatC Wb = cset(slotW(u));
+    const char* K = static_cast<const char*>(P.k) + (size_t)t0 * D * esz;
+    const char* V = static_cast<const char*>(P.v) + (size_t)t0 * D * esz;
+    float *A_ = tk[0], *B_ = tk[1], *G_ = tk[2], *E1 = tk[3], *E3 = tk[4], *H2 = tk[5], *gE1 = tk[6], *gE3 = tk[7],
+          *gH2 = tk[8];
+    // recompute A = k W1^T, B = k W3^T, G = v W2 and the update terms
+    if ((q = bgemm(bop(K, D, x_bs, false, bf), bop(Wb.p[0], D, DD, false), A_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    if ((q = bgemm(bop(K, D, x_bs, false, bf), bop(Wb.p[2], D, DD, false), B_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    if ((q = bgemm(bop(V, D, x_bs, false, bf), bop(Wb.p[1], Dh, DD, true), G_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    BWD_LAUNCH(bwd_upd_terms_kernel, dim3(ew_grid((int64_t)n * C * Dh)), (const float*)A_, (const float*)B_,
+               (const float*)G_, P.lr, L * 3, t0, E1, E3, H2, n, C, Dh, buf_bs);
+    // U1 = E1^T k, U3 = E3^T k, U2 = v^T H2
+    if ((q = bgemm(bop(E1, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), U.p[0], D, DD, Dh, D, C, n, 1.f, nullptr,
+                   0.f, s)))
+      return q;
+    if ((q = bgemm(bop(E3, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), U.p[2], D, DD, Dh, D, C, n, 1.f, nullptr,
+                   0.f, s)))
+      return q;
+    if ((q = bgemm(bop(V, D, x_bs, true, bf), bop(H2, Dh, buf_bs, true), U.p[1], Dh, DD, D, Dh, C, n, 1.f, nullptr,
+                   0.f, s)))
+      return q;
+    // the weight step W' = W + sgn step
+    MatC step;
+    float sgn = 1.f;
+    const MatC Mn = mom ? cset(slotM(u + 1)) : MatC{};
+    if (p.opt == LACT_OPT_GD) {
+      step = cset(U);
+    } else if (p.opt == LACT_OPT_MOMENTUM) {
+      step = Mn;
+      sgn = -1.f;
+    } else {
+      if ((q = ns_forward(p.opt == LACT_OPT_MUON ? cset(U) : Mn))) return q;
+      BWD_LAUNCH(bwd_frame_out_kernel, dim3(ew_grid(MD)), (const float*)Xi(iters), STEP, 1.f, n, D, Dh);
+      step = cset(STEP);
+      if (p.opt == LACT_OPT_MUON_MOMENTUM) sgn = -1.f;
+    }
+    // renorm backward: dW (cotangent of the next state) -> cotangent of W
+    // through the renorm; gW' -> GWP
+    BWD_LAUNCH(bwd_renorm_kernel, dim3((unsigned)(((int64_t)n * (2 * Dh + D) + 3) / 4)), Wb, step, sgn, DW, GWP, n,
+               D, Dh, renorm ? 1 : 0);
+    // optimiser backward -> gU
+    MatC gU = cset(GU);
+    if (p.opt == LACT_OPT_GD) {
+      gU = cset(GWP);
+    } else if (p.opt == LACT_OPT_MUON) {
+      if ((q = ns_backward(cset(U), cset(GWP), GU))) return q;
+    } else {
+      MatC gX = cset(GWP);
+      if (p.opt == LACT_OPT_MUON_MOMENTUM) {
+        if ((q = ns_backward(Mn, cset(GWP), GU))) return q;
+        gX = cset(GU);   // consumed below before GU is overwritten element by element
+      }
+      BWD_LAUNCH(bwd_beta_mean_kernel, dim3(n), P.beta, L, t0, C, fp(w.bbar));
+      BWD_LAUNCH(bwd_mom_kernel, dim3(BWD_NBM, n), GM, gX, cset(slotM(u)), (const float*)fp(w.bbar), GU,
+                 fp(w.mpart), DD, BWD_NBM);
+      BWD_LAUNCH(bwd_mom_finish_kernel, dim3((unsigned)std::min<int64_t>((C + NT - 1) / NT, 64), n),
+                 (const float*)fp(w.mpart), BWD_NBM, P.dbeta, L, t0, C);
+    }
+    // through the update terms: gE1 = k gU1^T, gE3 = k gU3^T, gH2 = v gU2
+    if ((q = bgemm(bop(K, D, x_bs, false, bf), bop(gU.p[0], D, DD, false), gE1, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    if ((q = bgemm(bop(K, D, x_bs, false, bf), bop(gU.p[2], D, DD, false), gE3, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    if ((q = bgemm(bop(V, D, x_bs, false, bf), bop(gU.p[1], Dh, DD, true), gH2, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    // dk = E1 gU1 + E3 gU3 ; dv = H2 gU2^T
+    float* dk = P.dk + t0 * D;
+    float* dv = P.dv + t0 * D;
+    if ((q = bgemm(bop(E1, Dh, buf_bs, false), bop(gU.p[0], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    if ((q = bgemm(bop(E3, Dh, buf_bs, false), bop(gU.p[2], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
+                   1.f, s)))
+      return q;
+    if ((q = bgemm(bop(H2, Dh, buf_bs, false), bop(gU.p[1], Dh, DD, false), dv, D, x_bs, (int)C, D, Dh, n, 1.f,
+                   nullptr, 0.f, s)))
+      return q;
+    // -> gA, gB, gG (in place) and dlr
+    BWD_LAUNCH(bwd_upd_elem_kernel, dim3((unsigned)(((int64_t)n * C + 3) / 4)), (const float*)A_, (const float*)B_,
+               (const float*)G_, P.lr, L * 3, t0, gE1, gE3, gH2, P.dlr, n, C, Dh, buf_bs);
+    // dk += gA W1 + gB W3 ; dv += gG W2^T
+    if ((q = bgemm(bop(gE1, Dh, buf_bs, false), bop(Wb.p[0], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
+                   1.f, s)))
+      return q;
+    if ((q = bgemm(bop(gE3, Dh, buf_bs, false), bop(Wb.p[2], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
+                   1.f, s)))
+      return q;
+    if ((q = bgemm(bop(gH2, Dh, buf_bs, false), bop(Wb.p[1], Dh, DD, false), dv, D, x_bs, (int)C, D, Dh, n, 1.f, dv,
+                   1.f, s)))
+      return q;
+    // dW1 += gA^T k ; dW3 += gB^T k ; dW2 += v^T gG
+    if ((q = bgemm(bop(gE1, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), DW.p[0], D, DD, Dh, D, C, n, 1.f, DW.p[0],
+                   1.f, s)))
+      return q;
+    if ((q = bgemm(bop(gE3, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), DW.p[2], D, DD, Dh, D, C, n, 1.f, DW.p[2],
+                   1.f, s)))
+      return q;
+    return bgemm(bop(V, D, x_bs, true, bf), bop(gH2, Dh, buf_bs, true), DW.p[1], Dh, DD, D, Dh, C, n, 1.f, DW.p[1],
+                 1.f, s);
+  };
+
+  // ---- reverse sweep
+  int u = w.nu;
+  for (int c = (int)f.size() - 1; c >= 0; --c) {
+    const int64_t t0 = b[c], C = b[c + 1] - b[c];
+    const bool U_ = f[c] & LACT_CHUNK_UPDATE, A_ = f[c] & LACT_CHUNK_APPLY;
+    // slot u: the state before this chunk (after its update: slot u + 1)
+    if (U_) --u;
+    if (A_ && U_ && order == LACT_UPDATE_THEN_APPLY)
+      if ((r = apply_bwd(cset(slotW(u + 1)), t0, C))) return r;
+    if (U_)
+      if ((r = update_bwd(u, t0, C))) return r;
+    if (A_ && (order == LACT_APPLY_THEN_UPDATE || !U_))
+      if ((r = apply_bwd(cset(slotW(u)), t0, C))) return r;
+  }
+  for (int j = 0; j < 3; ++j)
+    if (P.dM[j]) HIP_TRY(hipMemcpyAsync(P.dM[j], GM.p[j], (size_t)n * DD * 4, hipMemcpyDeviceToDevice, s));
+  return LACT_OK;
+}

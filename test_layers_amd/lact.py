@@ -35,13 +35,14 @@ CHUNK_APPLY = 2
 NO_RENORM = 1
 QK_PREP = 2
 
-K_UPD, K_APP, K_OUT, K_DW, K_OPT, K_NS, K_SNAP, K_PREP = range(8)
+K_UPD, K_APP, K_OUT, K_DW, K_OPT, K_NS, K_SNAP, K_PREP, K_BWD_GEMM, K_BWD_ELEM = range(10)
 K_NAMES = {K_UPD: "update_fwd", K_APP: "apply_fwd", K_OUT: "apply_out", K_DW: "dw", K_OPT: "opt",
-           K_NS: "newton_schulz", K_SNAP: "snapshot", K_PREP: "qk_prep"}
+           K_NS: "newton_schulz", K_SNAP: "snapshot", K_PREP: "qk_prep", K_BWD_GEMM: "bwd_gemm",
+           K_BWD_ELEM: "bwd_elem"}
 
 EXPORTS = ["lact_workspace_size", "lact_chunk_update", "lact_apply", "lact_layer_forward",
-           "lact_layer_forward_scaled", "lact_status_str", "lact_last_error", "lact_timing_enable",
-           "lact_timing_read"]
+           "lact_layer_forward_scaled", "lact_backward_workspace_size", "lact_layer_backward",
+           "lact_status_str", "lact_last_error", "lact_timing_enable", "lact_timing_read"]
 
 
 class LactError(RuntimeError):
@@ -91,6 +92,11 @@ def lib() -> ctypes.CDLL:
     L.lact_layer_forward_scaled.restype = i32
     L.lact_layer_forward_scaled.argtypes = [P, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32,
                                             vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lact_backward_workspace_size.restype = sz
+    L.lact_backward_workspace_size.argtypes = [P, i64, i64, i32, vp, vp, i32]
+    L.lact_layer_backward.restype = i32
+    L.lact_layer_backward.argtypes = ([P, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32]
+                                      + [vp] * 6 + [vp] + [vp] * 6 + [vp] * 5 + [vp] * 6 + [vp, sz, vp])
     L.lact_status_str.restype = ctypes.c_char_p
     L.lact_status_str.argtypes = [i32]
     L.lact_last_error.restype = ctypes.c_char_p
@@ -151,6 +157,24 @@ def layer_forward_scaled_ptr(p: Problem, q, k, v, lr, beta, oz, L, chunk, order,
     bp, fp, nc, _keep = _sched(bounds, flags)
     return lib().lact_layer_forward_scaled(ctypes.byref(p), q, k, v, lr, beta, oz, L, chunk, order,
                                            bp, fp, nc, W1, W2, W3, M1, M2, M3, o, ws, ws_bytes, stream)
+
+
+def backward_workspace_size(p: Problem, L: int, chunk: int = 0, order: int = 0,
+                            bounds: Optional[Sequence[int]] = None, flags: Optional[Sequence[int]] = None) -> int:
+    bp, fp, nc, _keep = _sched(bounds, flags)
+    n = lib().lact_backward_workspace_size(ctypes.byref(p), L, chunk, order, bp, fp, nc)
+    if n == 0:
+        raise LactError(ERR_INVALID_ARG, last_error())
+    return n
+
+
+def layer_backward_ptr(p: Problem, q, k, v, lr, beta, L, chunk, order, bounds, flags, W1, W2, W3, M1, M2, M3,
+                       dO, gW1, gW2, gW3, gM1, gM2, gM3, dq, dk, dv, dlr, dbeta, dW1, dW2, dW3, dM1, dM2, dM3,
+                       ws, ws_bytes, stream) -> int:
+    bp, fp, nc, _keep = _sched(bounds, flags)
+    return lib().lact_layer_backward(ctypes.byref(p), q, k, v, lr, beta, L, chunk, order, bp, fp, nc,
+                                     W1, W2, W3, M1, M2, M3, dO, gW1, gW2, gW3, gM1, gM2, gM3,
+                                     dq, dk, dv, dlr, dbeta, dW1, dW2, dW3, dM1, dM2, dM3, ws, ws_bytes, stream)
 
 
 def chunk_update_ptr(p: Problem, k, v, lr, beta, Lc, seq_stride, W1, W2, W3, M1, M2, M3,
@@ -282,6 +306,43 @@ def apply(q, W1, W2, W3, o=None, *, Lq: Optional[int] = None, qk_prep: bool = Fa
                     _ptr(W3, f32, "W3"), _ptr(o, q.dtype, "o"), ws.data_ptr(), ws.numel(),
                     _stream(stream)))
     return o
+
+
+def layer_backward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, dO, gW=None, gM=None,
+                   chunk: int = 0, order: int = APPLY_THEN_UPDATE, opt: int = OPT_GD, bounds=None, flags=None,
+                   ns_iters: int = 5, renorm: bool = True, workspace=None, stream=None):
+    """Backward of layer_forward (lact_layer_backward).  Inputs as for
+    layer_forward with W1..W3, M1..M3 the INITIAL state (read only); dO
+    [n, L, d] in q's dtype; gW, gM: None or 3-tuples of cotangents of the
+    final state.  Returns a dict of fp32 gradients dq, dk, dv, dlr, dbeta
+    (momentum optimisers, else None), dW1..dW3, dM1..dM3 (momentum
+    optimisers, else None)."""
+    torch = _torch()
+    n, L, D = q.shape
+    io = _io_dtype(q)
+    p = problem(n, D, io, opt, 3, ns_iters, renorm, dh=W1.shape[1])
+    mom = opt in (OPT_MOMENTUM, OPT_MUON_MOMENTUM)
+    f32 = torch.float32
+    out = {"dq": torch.empty(n, L, D, dtype=f32, device=q.device), "dk": torch.empty(n, L, D, dtype=f32, device=q.device),
+           "dv": torch.empty(n, L, D, dtype=f32, device=q.device), "dlr": torch.empty(n, L, 3, dtype=f32, device=q.device),
+           "dbeta": torch.empty(n, L, dtype=f32, device=q.device) if mom else None}
+    for j, w in enumerate((W1, W2, W3)):
+        out[f"dW{j + 1}"] = torch.empty_like(w)
+        out[f"dM{j + 1}"] = torch.empty_like(w) if mom else None
+    gW = (None, None, None) if gW is None else gW
+    gM = (None, None, None) if gM is None else gM
+    need = backward_workspace_size(p, L, chunk, order, bounds, flags)
+    ws = _workspace(need, workspace, q.device)
+    check(layer_backward_ptr(
+        p, _ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"), _ptr(lr, f32, "lr"),
+        _ptr(beta, f32, "beta"), L, chunk, order, bounds, flags,
+        _ptr(W1, f32, "W1"), _ptr(W2, f32, "W2"), _ptr(W3, f32, "W3"),
+        _ptr(M1, f32, "M1"), _ptr(M2, f32, "M2"), _ptr(M3, f32, "M3"), _ptr(dO, q.dtype, "dO"),
+        *[_ptr(g, f32, "gW") for g in gW], *[_ptr(g, f32, "gM") for g in gM],
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlr"]), _ptr(out["dbeta"]),
+        _ptr(out["dW1"]), _ptr(out["dW2"]), _ptr(out["dW3"]), _ptr(out["dM1"]), _ptr(out["dM2"]), _ptr(out["dM3"]),
+        ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out
 
 
 lib()  # fail at import time if the library is missing

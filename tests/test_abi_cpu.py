@@ -249,3 +249,58 @@ def test_single_hip_runtime_in_process():
     assert r.returncode == 0, r.stderr
     libs = eval(r.stdout.strip().splitlines()[-1])
     assert len(libs) == 1, libs
+
+
+# ----------------------------------------------------------------- backward entry point
+def bwd(p, L=512, chunk=128, order=0, bounds=None, flags=None, ws_bytes=None, **ptrs):
+    names = ["q", "k", "v", "lr", "beta", "W1", "W2", "W3", "M1", "M2", "M3", "dO", "gW1", "gW2", "gW3", "gM1",
+             "gM2", "gM3", "dq", "dk", "dv", "dlr", "dbeta", "dW1", "dW2", "dW3", "dM1", "dM2", "dM3", "ws"]
+    a = {n: FAKE for n in names}
+    a.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return lact.layer_backward_ptr(p, a["q"], a["k"], a["v"], a["lr"], a["beta"], L, chunk, order, bounds, flags,
+                                   a["W1"], a["W2"], a["W3"], a["M1"], a["M2"], a["M3"], a["dO"], a["gW1"],
+                                   a["gW2"], a["gW3"], a["gM1"], a["gM2"], a["gM3"], a["dq"], a["dk"], a["dv"],
+                                   a["dlr"], a["dbeta"], a["dW1"], a["dW2"], a["dW3"], a["dM1"], a["dM2"], a["dM3"],
+                                   a["ws"], ws_bytes, None)
+
+
+def test_backward_rejects_raw_qk():
+    assert bwd(P(qk_prep=True)) == lact.ERR_UNSUPPORTED
+    assert "pre-processed" in lact.last_error()
+
+
+@pytest.mark.parametrize("ptrs,opt", [
+    (dict(dW1=None), lact.OPT_GD),
+    (dict(dq=None), lact.OPT_GD),
+    (dict(dO=None), lact.OPT_GD),
+    (dict(dlr=None), lact.OPT_GD),
+    (dict(dbeta=None), lact.OPT_MOMENTUM),
+    (dict(M2=None), lact.OPT_MOMENTUM),
+    (dict(gW1=FAKE + 4), lact.OPT_GD),
+    (dict(dk=FAKE + 2), lact.OPT_GD),
+    (dict(ws=FAKE + 16), lact.OPT_GD),
+])
+def test_backward_bad_pointers(ptrs, opt):
+    assert bwd(P(opt=opt), **ptrs) == lact.ERR_INVALID_ARG, lact.last_error()
+
+
+def test_backward_optional_pointers_may_be_null():
+    # GD: beta, M, dbeta and dM unused; state cotangents optional
+    st = bwd(P(), beta=None, M1=None, M2=None, M3=None, dbeta=None, dM1=None, dM2=None, dM3=None, gW1=None,
+             gW2=None, gW3=None, gM1=None, gM2=None, gM3=None)
+    assert st not in (lact.ERR_INVALID_ARG, lact.ERR_UNSUPPORTED), lact.last_error()
+
+
+def test_backward_workspace():
+    for opt in (lact.OPT_GD, lact.OPT_MOMENTUM, lact.OPT_MUON, lact.OPT_MUON_MOMENTUM):
+        p = P(opt=opt)
+        need = lact.backward_workspace_size(p, 512, 128)
+        assert need >= lact.workspace_size(p, 512, 128)
+        assert bwd(p, ws_bytes=need - 1) == lact.ERR_WORKSPACE_TOO_SMALL
+    # more chunks keep more states
+    p = P(opt=lact.OPT_MOMENTUM)
+    assert lact.backward_workspace_size(p, 1024, 128) > lact.backward_workspace_size(p, 512, 128)
+    with pytest.raises(lact.LactError):
+        lact.backward_workspace_size(P(d=96), 512, 128)

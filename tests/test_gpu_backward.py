@@ -1,0 +1,145 @@
+"""GPU parity of the layer's backward pass (lact_layer_backward) with the fp64
+backward oracle, element by element on the same seeded inputs.
+
+err = max|gpu - ref| / max|ref| per output and instance (maximum over
+instances).  Every backward product runs fp32-grade (three bf16 planes per
+fp32 operand; bf16 inputs are exact in one plane) and the forward state
+trajectory is replayed fp32-grade, so the gate is the fp32 one, 1e-4.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import lact_backward as OB
+from test_layers_amd import workloads as W
+from parity_util import log, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL = 1e-4
+OUTS = ("dq", "dk", "dv", "dlr", "dbeta", "dW1", "dW2", "dW3", "dM1", "dM2", "dM3")
+
+
+@pytest.fixture(scope="module")
+def lact():
+    from test_layers_amd import lact as L
+    return L
+
+
+def cotangents(wl, seed, state_cot):
+    """dO in the io dtype (bf16 as uint16 bits), final-state cotangents fp32."""
+    rng = np.random.default_rng([seed, 77])
+    dO = rng.standard_normal((wl.n_inst, wl.L, wl.D)).astype(np.float32)
+    if wl.io_dtype == W.DTYPE_BF16:
+        dO = W.f32_to_bf16_bits(dO)
+    shapes = [(wl.n_inst, wl.dh, wl.D), (wl.n_inst, wl.D, wl.dh), (wl.n_inst, wl.dh, wl.D)]
+    gW = [0.1 * rng.standard_normal(s).astype(np.float32) for s in shapes] if state_cot else None
+    gM = [0.1 * rng.standard_normal(s).astype(np.float32) for s in shapes] if state_cot else None
+    return dO, gW, gM
+
+
+def run_case(lact, wl, seed=0, order=None, renorm=True, state_cot=True, M0_scale=0.0):
+    order = wl.order if order is None else order
+    inp = W.generate(wl, seed=seed)
+    dO, gW, gM = cotangents(wl, seed, state_cot)
+    mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    rng = np.random.default_rng([seed, 78])
+    M0 = [(M0_scale * rng.standard_normal(w.shape)).astype(np.float32) for w in (inp.W1, inp.W2, inp.W3)]
+    dev = lambda x: to_dev(x, torch)
+    out = lact.layer_backward(
+        dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.lr), dev(inp.beta) if mom else None,
+        dev(inp.W1), dev(inp.W2), dev(inp.W3), *([dev(m) for m in M0] if mom else [None] * 3),
+        dO=dev(dO), gW=None if gW is None else [dev(g) for g in gW],
+        gM=None if gM is None else [dev(g) for g in gM], order=order, opt=wl.opt,
+        bounds=list(wl.bounds), flags=list(wl.flags), renorm=renorm)
+    torch.cuda.synchronize()
+    ref = OB.layer_backward(inp.q, inp.k, inp.v, inp.lr, inp.beta if mom else None, inp.W1, inp.W2, inp.W3,
+                            wl.bounds, wl.flags, order, wl.opt, dO, gW, gM, renorm,
+                            M=M0 if mom else None)
+    errs = {}
+    for key in OUTS:
+        g = out.get(key)
+        if g is None:
+            continue
+        g = g.float().cpu().numpy().astype(np.float64)
+        r = ref[key]
+        e = 0.0
+        for i in range(wl.n_inst):
+            den = np.max(np.abs(r[i]))
+            e = max(e, float(np.max(np.abs(g[i] - r[i])) / den) if den > 0 else float(np.max(np.abs(g[i]))))
+        errs[key] = e
+    if not mom:
+        # GD / Muon: the momentum state passes through: dM = gM
+        assert out["dM1"] is None and out["dbeta"] is None
+    return errs
+
+
+CASES = {
+    # fp32 io, GD, three uniform chunks
+    "f32_gd": W.CONFIGS[1].scaled(n_inst=2, L=640, chunk=256),
+    # bf16 io, momentum, ragged tail
+    "bf16_momentum": W.CONFIGS[2].scaled(n_inst=2, L=3 * 256 + 100, chunk=256),
+    # bf16 io, Muon at d = 512 (3B-LM shape, reduced)
+    "bf16_muon_d512": W.CONFIGS[3].scaled(n_inst=2, L=2 * 512 + 64, chunk=512),
+    # bf16 io, momentum + Muon
+    "bf16_muon_momentum": W.CONFIGS[8].scaled(n_inst=2, L=2 * 256 + 64, chunk=256),
+    # view set: one update-only chunk then an apply-only chunk (update-then-apply)
+    "viewset": dataclasses.replace(W.CONFIGS[4], n_inst=2, L=1500, bounds=(0, 1200, 1500),
+                                   flags=(W.UPDATE, W.APPLY)),
+    # video: clean chunks update+apply, noisy chunks apply only
+    "video": dataclasses.replace(W.CONFIGS[5], n_inst=2, L=W.video_schedule(3, 200)[0][-1],
+                                 bounds=W.video_schedule(3, 200)[0], flags=W.video_schedule(3, 200)[1]),
+    # rectangular fast weights, dh > d, momentum
+    "rect_dh_gt_d": W.CONFIGS[10].scaled(n_inst=2, L=2 * 256 + 30, chunk=256),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward_parity(lact, name):
+    wl = CASES[name]
+    log(f"backward {name}: n={wl.n_inst} d={wl.D} dh={wl.dh} L={wl.L} chunks={wl.n_chunks} opt={wl.opt}")
+    errs = run_case(lact, wl, seed=1)
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("opt", [W.OPT_GD, W.OPT_MOMENTUM, W.OPT_MUON, W.OPT_MUON_MOMENTUM])
+@pytest.mark.parametrize("order", [W.APPLY_THEN_UPDATE, W.UPDATE_THEN_APPLY])
+def test_backward_optimisers_orders_renorm(lact, opt, order):
+    """Every optimiser x order, with and without renorm, nonzero initial
+    momentum, fp32 io."""
+    base = W.CONFIGS[1].scaled(n_inst=2, L=3 * 128 + 40, chunk=128)
+    wl = dataclasses.replace(base, opt=opt)
+    for renorm in (True, False):
+        errs = run_case(lact, wl, seed=2 + opt, order=order, renorm=renorm, M0_scale=0.05)
+        log(f"  opt={opt} order={order} renorm={renorm}: errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+        assert max(errs.values()) <= TOL, (renorm, errs)
+
+
+@pytest.mark.parametrize("shape", [(128, 64), (64, 192)])
+@pytest.mark.parametrize("opt", [W.OPT_MUON, W.OPT_MUON_MOMENTUM])
+def test_backward_rectangular_newton_schulz(lact, shape, opt):
+    """d != dh in both orientations: the Newton-Schulz backward transposes the
+    tall matrices, as the forward map does."""
+    D, Dh = shape
+    wl = dataclasses.replace(W.CONFIGS[1].scaled(n_inst=2, L=2 * 128 + 20, chunk=128), D=D, Dh=Dh, opt=opt)
+    errs = run_case(lact, wl, seed=5, M0_scale=0.05)
+    log(f"  d={D} dh={Dh} opt={opt}: errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= TOL, errs
+
+
+def test_backward_without_state_cotangents(lact):
+    """gW = gM = NULL means zero cotangents of the final state."""
+    wl = W.CONFIGS[2].scaled(n_inst=2, L=2 * 256, chunk=256)
+    errs = run_case(lact, wl, seed=4, state_cot=False)
+    assert max(errs.values()) <= TOL, errs
+
+
+def test_backward_no_update_passes_state_cotangent_through(lact):
+    """Apply-only schedule: dW = gW + the apply's weight gradients, dk = dv =
+    dlr = 0 exactly, dM = gM exactly."""
+    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=300, chunk=300), bounds=(0, 300), flags=(W.APPLY,))
+    errs = run_case(lact, wl, seed=6)
+    assert max(errs.values()) <= TOL, errs

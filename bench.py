@@ -1,6 +1,6 @@
 """Benchmark of the LaCT fast-weight layer forward (update + apply) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--backward]
 
 One step = one whole layer forward over the workload's sequence (every chunk:
 forward products, SwiGLU backward epilogue, weight-gradient contraction,
@@ -12,6 +12,12 @@ JSON line.
 The fast weights are not reset between steps: every step runs the same
 kernels on the state the previous step left (same work, like the next 32K
 tokens of a longer sequence).
+
+--backward measures the layer's backward pass instead (lact_layer_backward:
+gradients of q, k, v, lr, beta and the initial state for a seeded output
+cotangent; one step = one whole backward call, which replays the forward
+state trajectory and sweeps the chunks in reverse).  It computes fp32-grade,
+so its products are priced against the fp32 matrix peak.
 """
 import argparse
 import json
@@ -31,9 +37,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload id 1..9 (default: the 760M LM layer)")
+    ap.add_argument("--config", type=int, default=2, help="workload id 1..10 (default: the 760M LM layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work to sample")
+    ap.add_argument("--backward", action="store_true", help="measure the layer's backward pass")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (PMC counter calibration)")
     return ap.parse_args()
@@ -56,6 +63,67 @@ def kernel_flops(wl, lact):
         lact.K_SNAP: 0.0,
         lact.K_PREP: 0.0,
     }
+
+
+def ns_flops_per_matrix(D, Dh, iters=5):
+    """Newton-Schulz forward per matrix: per iteration X X^T (2 m^2 k), A A
+    (2 m^3), B X (2 m^2 k), with m = min(d, dh), k = max(d, dh)."""
+    m, k = min(D, Dh), max(D, Dh)
+    return iters * (4.0 * m * m * k + 2.0 * m ** 3)
+
+
+def backward_kernel_flops(wl, lact):
+    """FLOPs per backward call, per kernel class.  The call replays the
+    forward state trajectory (update chunks only: update forward, the
+    contractions and Newton-Schulz run on the forward's kernels) and then
+    runs the reverse sweep on its own products:
+      per update token 36 d dh (recomputed k W1^T, k W3^T, v W2 and the three
+      direction contractions, 12; k gU1^T, k gU3^T, v gU2, 6; dk and dv from
+      the update terms, 6, and through W, 6; dW contractions, 6),
+      per apply token 16 d dh (q W1^T, q W3^T, dO W2, 6; three dW
+      contractions, 6; dq, 4),
+      Newton-Schulz per matrix and update: its forward again plus, per
+      iteration, gX X^T, gP A, A gP, P g, Q X (6 m^2 k + 4 m^3)."""
+    from test_layers_amd import workloads as W
+    D, Dh, n = wl.D, wl.dh, wl.n_inst
+    upd = sum(b - a for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags) if f & W.UPDATE)
+    app = sum(b - a for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags) if f & W.APPLY)
+    n_upd = sum(1 for f in wl.flags if f & W.UPDATE)
+    ns = wl.opt in (W.OPT_MUON, W.OPT_MUON_MOMENTUM)
+    m, k = min(D, Dh), max(D, Dh)
+    f = {c: 0.0 for c in lact.K_NAMES}
+    f[lact.K_UPD] = 6.0 * upd * D * Dh * n
+    f[lact.K_DW] = 6.0 * upd * D * Dh * n
+    f[lact.K_NS] = ns_flops_per_matrix(D, Dh) * 3 * n * n_upd if ns else 0.0
+    f[lact.K_BWD_GEMM] = (36.0 * upd + 16.0 * app) * D * Dh * n
+    if ns:
+        f[lact.K_BWD_GEMM] += 3 * n * n_upd * (ns_flops_per_matrix(D, Dh) + 5 * (6.0 * m * m * k + 4.0 * m ** 3))
+    return f
+
+
+def cpu_baseline_backward(wl, inp, dO, budget):
+    """The backward oracle as it stands, on a bounded sample (whole instances
+    over the whole sequence until about `budget` seconds of work)."""
+    from oracle import lact_backward as OB
+    from test_layers_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    t0 = time.perf_counter()
+    done = 0
+    while time.perf_counter() - t0 < budget:
+        i = done % wl.n_inst
+        OB.backward_instance(inp.q[i], inp.k[i], inp.v[i], inp.lr[i], inp.beta[i] if mom else None,
+                             inp.W1[i], inp.W2[i], inp.W3[i], wl.bounds, wl.flags, wl.order, wl.opt, dO[i])
+        done += 1
+    dt = time.perf_counter() - t0
+    tokens = wl.tokens * done / wl.n_inst
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} instance backward passes (heads, cycling over the {wl.n_inst} of the workload), "
+                      f"whole {wl.L}-token sequence each, {dt:.1f} s, numpy fp64"}
 
 
 def opt_bytes(wl, S):
@@ -93,7 +161,8 @@ def cpu_baseline(wl, inp, budget):
                       f"whole {wl.L}-token sequence each, {dt:.1f} s, numpy fp64"}
 
 
-SRC_FILES = ("lact.hip", "lact_device.hpp", "lact_kernels.hpp", "lact_direct.hpp")
+SRC_FILES = ("lact.hip", "lact_device.hpp", "lact_kernels.hpp", "lact_direct.hpp", "lact_backward.hpp",
+             "lact_backward_host.hpp")
 
 
 def source_sha():
@@ -108,12 +177,12 @@ def source_sha():
     return h.hexdigest()
 
 
-def pmc_traffic(kernel, workload):
+def pmc_traffic(kernel, workload, fname="pmc_traffic.json"):
     """HBM bytes per launch of a kernel class from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's
     reading), or None when absent or taken on other sources."""
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", "pmc_traffic.json")
+    path = os.path.join(here, "profiles", fname)
     try:
         with open(path) as fh:
             t = json.load(fh)
@@ -156,18 +225,51 @@ def main():
     q, k, v, lr, beta = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.lr), dev(inp.beta)
     oz = dev(inp.oz) if wl.out_scale else None
     Ws = [dev(inp.W1), dev(inp.W2), dev(inp.W3)]
-    Ms = [torch.zeros_like(w) for w in Ws] if wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM) else [None] * 3
-    o = torch.zeros_like(q)
-    p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes, dh=wl.dh, qk_prep=wl.layer_qk_prep)
+    mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    Ms = [torch.zeros_like(w) for w in Ws] if mom else [None] * 3
     bounds, flags = list(wl.bounds), list(wl.flags)
-    ws = torch.empty(lact.workspace_size(p, wl.L, 0, wl.order, bounds, flags), dtype=torch.uint8,
-                     device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
-        lact.layer_forward(q, k, v, lr, beta, *Ws, *Ms, o, order=wl.order, opt=wl.opt,
-                           bounds=bounds, flags=flags, rec_planes=wl.rec_planes,
-                           qk_prep=wl.layer_qk_prep, oz=oz, workspace=ws, stream=stream)
+    if args.backward:
+        if wl.layer_qk_prep or wl.out_scale:
+            print("the backward pass takes pre-processed q, k and no output scale; pick another --config",
+                  file=sys.stderr)
+            sys.exit(2)
+        # seeded output cotangent in the io dtype
+        rng = np.random.default_rng([0, 77])
+        dO_np = rng.standard_normal((wl.n_inst, wl.L, wl.D)).astype(np.float32)
+        if wl.io_dtype == W.DTYPE_BF16:
+            dO_np = W.f32_to_bf16_bits(dO_np)
+        dO = dev(dO_np)
+        p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, 3, dh=wl.dh)
+        ws = torch.empty(lact.backward_workspace_size(p, wl.L, 0, wl.order, bounds, flags), dtype=torch.uint8,
+                         device="cuda")
+        box = {"out": None}
+
+        def step():
+            box["out"] = lact.layer_backward(q, k, v, lr, beta if mom else None, *Ws, *Ms, dO=dO, order=wl.order,
+                                             opt=wl.opt, bounds=bounds, flags=flags, out=box["out"],
+                                             workspace=ws, stream=stream)
+        kf = backward_kernel_flops(wl, lact)
+        peak, peak_name = PEAK_FP32_MFMA, "fp32"
+        metric = ("LaCT layer backward tokens/sec (gradients of q, k, v, lr, beta and the initial state; "
+                  "fp32-grade), 1xMI355X")
+        dtype = "f32"
+    else:
+        o = torch.zeros_like(q)
+        p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes, dh=wl.dh,
+                         qk_prep=wl.layer_qk_prep)
+        ws = torch.empty(lact.workspace_size(p, wl.L, 0, wl.order, bounds, flags), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():
+            lact.layer_forward(q, k, v, lr, beta, *Ws, *Ms, o, order=wl.order, opt=wl.opt,
+                               bounds=bounds, flags=flags, rec_planes=wl.rec_planes,
+                               qk_prep=wl.layer_qk_prep, oz=oz, workspace=ws, stream=stream)
+        kf = kernel_flops(wl, lact)
+        peak, peak_name = PEAK_BF16, "bf16"
+        metric = "LaCT layer tokens/sec (update+apply) and % bf16 MFMA peak, 1xMI355X"
+        dtype = "bf16" if wl.io_dtype == W.DTYPE_BF16 else "f32"
 
     for _ in range(args.warmup):
         step()
@@ -186,10 +288,9 @@ def main():
     ms_per_step = dt / args.steps * 1e3
     tokens = wl.tokens
     value = tokens * args.steps / dt
-    flops = W.algorithmic_flops(wl)["total"]
+    flops = sum(kf.values()) if args.backward else W.algorithmic_flops(wl)["total"]
 
     # per-kernel HIP-event timing over the same number of steps
-    kf = kernel_flops(wl, lact)
     for kc in lact.K_NAMES:
         lact.timing_enable(kc, True)
     for _ in range(args.steps):
@@ -208,24 +309,25 @@ def main():
     if "dw" not in per:
         # the fused update kernel also runs the weight-gradient contraction
         kf[lact.K_UPD] += kf[lact.K_DW]
+    traffic_file = "pmc_traffic_backward.json" if args.backward else "pmc_traffic.json"
     dom = max(per.items(), key=lambda kv: kv[1]["ms_per_step"])
     dname, d = dom
     if kf[d["kc"]] > 0:
         per_launch = kf[d["kc"]] / (d["launches_per_step"])
         achieved = per_launch / (d["avg_launch_us"] * 1e-6)
-        roof = {"kernel": dname, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": pmc_traffic(dname, wl.name),
-                "flops_per_launch": per_launch, "avg_launch_us": d["avg_launch_us"]}
+        roof = {"kernel": dname, "bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": pmc_traffic(dname, wl.name, traffic_file),
+                "flops_per_launch": per_launch, "avg_launch_us": d["avg_launch_us"], "peak_dtype": peak_name}
     else:
-        nb = opt_bytes(wl, 1) / d["launches_per_step"] * (1 if True else 0)
+        nb = opt_bytes(wl, 1) / d["launches_per_step"]
         achieved = nb / (d["avg_launch_us"] * 1e-6)
         roof = {"kernel": dname, "bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": pmc_traffic(dname, wl.name),
+                "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": pmc_traffic(dname, wl.name, traffic_file),
                 "bytes_per_launch": nb, "avg_launch_us": d["avg_launch_us"]}
     kernels = {k: {kk: round(vv, 4) for kk, vv in v.items() if kk != "kc"} for k, v in per.items()}
 
     out = {
-        "metric": "LaCT layer tokens/sec (update+apply) and % bf16 MFMA peak, 1xMI355X",
+        "metric": metric,
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -236,21 +338,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.io_dtype == W.DTYPE_BF16 else "f32",
+        "dtype": dtype,
         "data": "synthetic (seeded generator; no dataset, random-init fast weights)",
         "config": {"workload": wl.name, "n_inst": wl.n_inst, "d": wl.D, "dh": wl.dh, "seq_len": wl.L,
                    "max_chunk": wl.max_chunk, "n_chunks": wl.n_chunks,
                    "opt": ["gd", "momentum", "muon", "muon_momentum"][wl.opt],
                    "order": ["apply_then_update", "update_then_apply"][wl.order],
-                   "rec_planes": wl.rec_planes, "layer_qk_prep": wl.layer_qk_prep,
-                   "output_scale": wl.out_scale, "global_batch": 1},
+                   "rec_planes": 3 if args.backward else wl.rec_planes, "layer_qk_prep": wl.layer_qk_prep,
+                   "output_scale": wl.out_scale, "pass": "backward" if args.backward else "forward",
+                   "global_batch": 1},
         "algorithmic_tflop_per_step": flops / 1e12,
-        "layer_frac_bf16_peak": flops / (ms_per_step * 1e-3) / PEAK_BF16,
         "roofline": roof,
         "kernels": kernels,
     }
+    if args.backward:
+        out["layer_frac_fp32_peak"] = flops / (ms_per_step * 1e-3) / PEAK_FP32_MFMA
+    else:
+        out["layer_frac_bf16_peak"] = flops / (ms_per_step * 1e-3) / PEAK_BF16
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
+        out["cpu_baseline"] = (cpu_baseline_backward(wl, inp, dO_np, args.cpu_budget) if args.backward
+                               else cpu_baseline(wl, inp, args.cpu_budget))
     print(json.dumps(out))
 
 

@@ -310,25 +310,27 @@ def apply(q, W1, W2, W3, o=None, *, Lq: Optional[int] = None, qk_prep: bool = Fa
 
 def layer_backward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, dO, gW=None, gM=None,
                    chunk: int = 0, order: int = APPLY_THEN_UPDATE, opt: int = OPT_GD, bounds=None, flags=None,
-                   ns_iters: int = 5, renorm: bool = True, workspace=None, stream=None):
+                   ns_iters: int = 5, renorm: bool = True, out=None, workspace=None, stream=None):
     """Backward of layer_forward (lact_layer_backward).  Inputs as for
     layer_forward with W1..W3, M1..M3 the INITIAL state (read only); dO
     [n, L, d] in q's dtype; gW, gM: None or 3-tuples of cotangents of the
     final state.  Returns a dict of fp32 gradients dq, dk, dv, dlr, dbeta
     (momentum optimisers, else None), dW1..dW3, dM1..dM3 (momentum
-    optimisers, else None)."""
+    optimisers, else None); `out` (such a dict from an earlier call with the
+    same shapes) is filled instead of allocating."""
     torch = _torch()
     n, L, D = q.shape
     io = _io_dtype(q)
     p = problem(n, D, io, opt, 3, ns_iters, renorm, dh=W1.shape[1])
     mom = opt in (OPT_MOMENTUM, OPT_MUON_MOMENTUM)
     f32 = torch.float32
-    out = {"dq": torch.empty(n, L, D, dtype=f32, device=q.device), "dk": torch.empty(n, L, D, dtype=f32, device=q.device),
-           "dv": torch.empty(n, L, D, dtype=f32, device=q.device), "dlr": torch.empty(n, L, 3, dtype=f32, device=q.device),
-           "dbeta": torch.empty(n, L, dtype=f32, device=q.device) if mom else None}
-    for j, w in enumerate((W1, W2, W3)):
-        out[f"dW{j + 1}"] = torch.empty_like(w)
-        out[f"dM{j + 1}"] = torch.empty_like(w) if mom else None
+    if out is None:
+        e = lambda *shape: torch.empty(*shape, dtype=f32, device=q.device)
+        out = {"dq": e(n, L, D), "dk": e(n, L, D), "dv": e(n, L, D), "dlr": e(n, L, 3),
+               "dbeta": e(n, L) if mom else None}
+        for j, w in enumerate((W1, W2, W3)):
+            out[f"dW{j + 1}"] = torch.empty_like(w)
+            out[f"dM{j + 1}"] = torch.empty_like(w) if mom else None
     gW = (None, None, None) if gW is None else gW
     gM = (None, None, None) if gM is None else gM
     need = backward_workspace_size(p, L, chunk, order, bounds, flags)

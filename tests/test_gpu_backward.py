@@ -5,6 +5,15 @@ err = max|gpu - ref| / max|ref| per output and instance (maximum over
 instances).  Every backward product runs fp32-grade (three bf16 planes per
 fp32 operand; bf16 inputs are exact in one plane) and the forward state
 trajectory is replayed fp32-grade, so the gate is the fp32 one, 1e-4.
+
+Exception, the Newton-Schulz optimisers at full workload length: the Muon
+recurrence amplifies rounding (each chunk's step is a quintic polynomial of
+the normalised gradient), so even a plain float32 evaluation of the oracle's
+own arithmetic differs from float64 by E32 = 2.0e-4 on the 3B-LM workload
+(d = 512, 8 chunks of 4,096; max over its 6 instances) and by 1.2e-2 on the
+video workload (d = 128, 12 Muon chunks; instances 0, 13, 27, 39).  Their
+full-size gate is 5 x E32, capped at the bf16-input gate of the forward
+(2e-2).
 """
 import dataclasses
 
@@ -19,6 +28,8 @@ torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 TOL = 1e-4
+# full-size gates of the Newton-Schulz workloads (5 x the plain-fp32 error, capped at 2e-2)
+TOL_NS_FULL = {3: 1e-3, 5: 2e-2, 8: 1e-3}
 OUTS = ("dq", "dk", "dv", "dlr", "dbeta", "dW1", "dW2", "dW3", "dM1", "dM2", "dM3")
 
 
@@ -40,9 +51,11 @@ def cotangents(wl, seed, state_cot):
     return dO, gW, gM
 
 
-def run_case(lact, wl, seed=0, order=None, renorm=True, state_cot=True, M0_scale=0.0):
+def run_case(lact, wl, seed=0, order=None, renorm=True, state_cot=True, M0_scale=0.0, instances=None):
+    """Run the GPU backward on every instance; compare `instances` (default:
+    all) with the oracle."""
     order = wl.order if order is None else order
-    inp = W.generate(wl, seed=seed)
+    inp = W.generate(wl, seed=seed, threads=16)
     dO, gW, gM = cotangents(wl, seed, state_cot)
     mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
     rng = np.random.default_rng([seed, 78])
@@ -55,18 +68,22 @@ def run_case(lact, wl, seed=0, order=None, renorm=True, state_cot=True, M0_scale
         gM=None if gM is None else [dev(g) for g in gM], order=order, opt=wl.opt,
         bounds=list(wl.bounds), flags=list(wl.flags), renorm=renorm)
     torch.cuda.synchronize()
-    ref = OB.layer_backward(inp.q, inp.k, inp.v, inp.lr, inp.beta if mom else None, inp.W1, inp.W2, inp.W3,
-                            wl.bounds, wl.flags, order, wl.opt, dO, gW, gM, renorm,
-                            M=M0 if mom else None)
+    idx = list(range(wl.n_inst)) if instances is None else list(instances)
+    pick = lambda x: None if x is None else x[idx]
+    ref = OB.layer_backward(pick(inp.q), pick(inp.k), pick(inp.v), pick(inp.lr), pick(inp.beta) if mom else None,
+                            pick(inp.W1), pick(inp.W2), pick(inp.W3), wl.bounds, wl.flags, order, wl.opt,
+                            pick(dO), None if gW is None else [pick(g) for g in gW],
+                            None if gM is None else [pick(g) for g in gM], renorm,
+                            M=[pick(m) for m in M0] if mom else None)
     errs = {}
     for key in OUTS:
         g = out.get(key)
         if g is None:
             continue
-        g = g.float().cpu().numpy().astype(np.float64)
+        g = g.float().cpu().numpy().astype(np.float64)[idx]
         r = ref[key]
         e = 0.0
-        for i in range(wl.n_inst):
+        for i in range(len(idx)):
             den = np.max(np.abs(r[i]))
             e = max(e, float(np.max(np.abs(g[i] - r[i])) / den) if den > 0 else float(np.max(np.abs(g[i]))))
         errs[key] = e
@@ -143,3 +160,21 @@ def test_backward_no_update_passes_state_cotangent_through(lact):
     wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=300, chunk=300), bounds=(0, 300), flags=(W.APPLY,))
     errs = run_case(lact, wl, seed=6)
     assert max(errs.values()) <= TOL, errs
+
+
+# ----------------------------------------------------------------- full workload sizes
+FULL = {1: None, 2: None, 3: None, 4: None, 5: (0, 13, 27, 39), 8: None, 10: None}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cid", sorted(FULL))
+def test_backward_full_size(lact, cid):
+    """The backward at the full workload sizes (every instance on the GPU;
+    the oracle on all of them, or on a spread sample for the 40-head video
+    workload)."""
+    wl = W.CONFIGS[cid]
+    log(f"backward full cfg{cid} {wl.name}: n={wl.n_inst} d={wl.D} dh={wl.dh} L={wl.L} chunks={wl.n_chunks}")
+    errs = run_case(lact, wl, seed=0, instances=FULL[cid])
+    tol = TOL_NS_FULL[cid] if wl.opt in (W.OPT_MUON, W.OPT_MUON_MOMENTUM) else TOL
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} } gate={tol}")
+    assert max(errs.values()) <= tol, errs

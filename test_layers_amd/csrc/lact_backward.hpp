@@ -252,6 +252,21 @@ __global__ __launch_bounds__(NT) void bwd_mom_finish_kernel(const float* part, i
     dbeta[i * beta_bs + t0 + t] = g;
 }
 
+// Split-K reduction: C[b][m, n] = sum_s P[s][b][m, n] + beta Cin[b][m, n],
+// partials compact ([S][batch][M][N]); Cin has C's strides and may be C.
+__global__ __launch_bounds__(NT) void bwd_splitsum_kernel(const float* P, int S, int batch, int M, int N, float* C,
+                                                          int64_t ldc, int64_t c_bs, const float* Cin, float beta) {
+  const int64_t mn = (int64_t)M * N, tot = mn * batch;
+  for (int64_t e = (int64_t)blockIdx.x * NT + threadIdx.x; e < tot; e += (int64_t)gridDim.x * NT) {
+    const int64_t b = e / mn, r = e % mn;
+    const int64_t o = b * c_bs + (r / N) * ldc + r % N;
+    float v = 0.f;
+    for (int q = 0; q < S; ++q) v += P[(int64_t)q * tot + e];
+    if (Cin) v += beta * Cin[o];
+    C[o] = v;
+  }
+}
+
 // ----------------------------------------------------------------- Newton-Schulz
 // Working frame: every matrix of the set as X [m, k] with m = min(D, Dh) and
 // k = max(D, Dh) (matrices with more rows than columns are transposed, as the

@@ -20,6 +20,12 @@
 // bf16 planes (bf16 inputs are exact in one plane).
 
 // ----------------------------------------------------------------- products
+// grid of a grid-stride elementwise kernel
+inline unsigned ew_grid(int64_t total) {
+  const int64_t b = (total + NT - 1) / NT;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 8 * NCU));
+}
+
 struct BOp {
   const void* p;
   int64_t ld, bs;
@@ -32,38 +38,22 @@ inline BOp bop(const void* p, int64_t ld, int64_t bs, bool colk, bool bf16 = fal
 
 template <typename TA, int PA, bool CA, typename TB, int PB, bool CB>
 lact_status bgemm_t(GemmArgs& g, hipStream_t s) {
-  const int64_t t = (int64_t)((g.g[0].M + 63) / 64) * ((g.N + 63) / 64) * g.batch;
+  const int64_t per = (int64_t)((g.N + 63) / 64) * g.batch * g.splits;
+  int64_t t = 0;
+  for (int i = 0; i < g.ngroups; ++i) {
+    const int64_t ti = (int64_t)((g.g[i].M + 63) / 64) * per;
+    if (ti > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+    g.g[i].tiles = (int)ti;
+    t += ti;
+  }
   if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
   if (t == 0) return LACT_OK;
-  g.g[0].tiles = (int)t;
   KernelTimer kt(LACT_K_BWD_GEMM, s);
   return launch_gemm_t<TA, PA, CA, TB, PB, CB, float, 64>(g, t, s);
 }
 
-// C_b[m, n] = alpha sum_k A_b(m, k) B_b(n, k) + beta Cin_b[m, n] for b < batch
-// (Cin has C's strides and may be C itself; NULL: no accumulation)
-lact_status bgemm(BOp A, BOp B, float* C, int64_t ldc, int64_t c_bs, int M, int N, int64_t K, int batch, float alpha,
-                  const float* Cin, float beta, hipStream_t s) {
-  if (M <= 0 || N <= 0 || batch <= 0) return LACT_OK;
-  GemmArgs g = gemm_args();
-  g.g[0].A = A.p;
-  g.g[0].B = B.p;
-  g.g[0].C = C;
-  g.g[0].Cin = Cin;
-  g.g[0].M = M;
-  g.lda = A.ld;
-  g.a_bs = A.bs;
-  g.ldb = B.ld;
-  g.b_bs = B.bs;
-  g.ldc = ldc;
-  g.c_bs = c_bs;
-  g.ldcin = ldc;
-  g.cin_bs = c_bs;
-  g.N = N;
-  g.K = g.kps = K;
-  g.batch = batch;
-  g.alpha = alpha;
-  g.beta = beta;
+template <typename F>
+lact_status bgemm_form(const BOp& A, const BOp& B, GemmArgs& g, hipStream_t s) {
   if (!A.bf16 && !B.bf16) {
     if (!A.colk && !B.colk) return bgemm_t<float, 3, false, float, 3, false>(g, s);
     if (!A.colk && B.colk) return bgemm_t<float, 3, false, float, 3, true>(g, s);
@@ -78,10 +68,94 @@ lact_status bgemm(BOp A, BOp B, float* C, int64_t ldc, int64_t c_bs, int M, int 
   return fail(LACT_ERR_UNSUPPORTED, "internal: backward product form");
 }
 
-// grid of a grid-stride elementwise kernel
-inline unsigned ew_grid(int64_t total) {
-  const int64_t b = (total + NT - 1) / NT;
-  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 8 * NCU));
+// Token split of a long contraction (K = a chunk's tokens) whose output has
+// few 64 x 64 tiles: enough splits for about four workgroups per CU, at
+// least 256 of K per split.
+int bwd_splits(int64_t tiles, int64_t K) {
+  if (K < 512 || tiles >= 4 * NCU) return 1;
+  const int64_t want = (4 * NCU + tiles - 1) / tiles;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({64, want, K / 256}));
+}
+
+// one product of a group: its own A, B, C and accumulation source
+struct BGrp {
+  const void* A;
+  const void* B;
+  float* C;
+  const float* Cin;
+};
+
+// For each group i < ng: C_i,b[m, n] = alpha sum_k A_i,b(m, k) B_i,b(n, k)
+// + beta Cin_i,b[m, n] for b < batch (Cin has C's strides and may be C
+// itself; NULL: no accumulation).  A and B give the operands' layout (their
+// pointers are ignored).  Long contractions with few output tiles are split
+// over K into fp32 partials in `spl` (spl_floats of scratch), summed in
+// fixed order by bwd_splitsum_kernel.
+lact_status bgemm_g(const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t ldc, int64_t c_bs, int M, int N,
+                    int64_t K, int batch, float alpha, float beta, float* spl, size_t spl_floats, hipStream_t s) {
+  if (M <= 0 || N <= 0 || batch <= 0 || ng <= 0) return LACT_OK;
+  GemmArgs g = gemm_args();
+  g.ngroups = ng;
+  g.lda = A.ld;
+  g.a_bs = A.bs;
+  g.ldb = B.ld;
+  g.b_bs = B.bs;
+  g.N = N;
+  g.K = g.kps = K;
+  g.batch = batch;
+  g.alpha = alpha;
+  const int64_t tiles = (int64_t)((M + 63) / 64) * ((N + 63) / 64) * batch * ng;
+  int S = spl ? bwd_splits(tiles, K) : 1;
+  const int64_t mnb = (int64_t)M * N * batch;
+  while (S > 1 && (size_t)S * ng * mnb > spl_floats) --S;
+  if (S > 1) {
+    g.kps = (K + S - 1) / S;
+    g.kps = (g.kps + 31) / 32 * 32;
+    S = (int)((K + g.kps - 1) / g.kps);
+  }
+  if (S > 1) {
+    // partials [S][batch][M][N] per group
+    g.splits = S;
+    g.ldc = N;
+    g.c_bs = (int64_t)M * N;
+    g.c_ss = mnb;
+    for (int i = 0; i < ng; ++i) {
+      g.g[i].A = gs[i].A;
+      g.g[i].B = gs[i].B;
+      g.g[i].C = spl + (int64_t)i * S * mnb;
+      g.g[i].Cin = nullptr;
+      g.g[i].M = M;
+    }
+    lact_status r = bgemm_form<void>(A, B, g, s);
+    if (r) return r;
+    for (int i = 0; i < ng; ++i) {
+      KernelTimer kt(LACT_K_BWD_ELEM, s);
+      LACT_LAUNCH(bwd_splitsum_kernel, dim3(ew_grid(mnb)), dim3(NT), s, (const float*)(spl + (int64_t)i * S * mnb),
+                  S, batch, M, N, gs[i].C, ldc, c_bs, gs[i].Cin, beta);
+      HIP_TRY(hipGetLastError());
+    }
+    return LACT_OK;
+  }
+  g.ldc = ldc;
+  g.c_bs = c_bs;
+  g.ldcin = ldc;
+  g.cin_bs = c_bs;
+  g.beta = beta;
+  for (int i = 0; i < ng; ++i) {
+    g.g[i].A = gs[i].A;
+    g.g[i].B = gs[i].B;
+    g.g[i].C = gs[i].C;
+    g.g[i].Cin = gs[i].Cin;
+    g.g[i].M = M;
+  }
+  return bgemm_form<void>(A, B, g, s);
+}
+
+// one product, no split
+lact_status bgemm(BOp A, BOp B, float* C, int64_t ldc, int64_t c_bs, int M, int N, int64_t K, int batch, float alpha,
+                  const float* Cin, float beta, hipStream_t s) {
+  const BGrp g1{A.p, B.p, C, Cin};
+  return bgemm_g(&g1, 1, A, B, ldc, c_bs, M, N, K, batch, alpha, beta, nullptr, 0, s);
 }
 
 #define BWD_LAUNCH(kernel, grid, ...)                      \
@@ -104,6 +178,7 @@ struct BwdWs {
   size_t U = 0, step = 0, gWp = 0, gU = 0, gM = 0, gX = 0;
   size_t X = 0, Am = 0, Pm = 0, gP = 0, gA = 0, Qm = 0, g0 = 0, g1 = 0, nrm = 0, part = 0;
   size_t bbar = 0, mpart = 0;
+  size_t spl = 0, spl_floats = 0;   // split-K partials of the token contractions
   size_t total = 0;
 };
 
@@ -170,6 +245,14 @@ BwdWs bwd_layout(const lact_problem& p, const std::vector<int64_t>& b, const std
   }
   w.bbar = take(n * 4);
   w.mpart = take(n * BWD_NBM * 4);
+  {
+    // the token contractions: pairs of [dh, d] outputs, single [d, dh] ones
+    const int64_t tb = (int64_t)((Dh + 63) / 64) * ((D + 63) / 64) * (int64_t)n;
+    const size_t s2 = (size_t)bwd_splits(2 * tb, w.cmax) * 2 * n * DD;
+    const size_t s1 = (size_t)bwd_splits(tb, w.cmax) * n * DD;
+    w.spl_floats = std::max(s1, s2);
+    w.spl = take(w.spl_floats * 4);
+  }
   w.total = off;
   return w;
 }
@@ -344,28 +427,29 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     lact_status q;
     const char* Q = static_cast<const char*>(P.q) + (size_t)t0 * D * esz;
     const char* dO = static_cast<const char*>(P.dO) + (size_t)t0 * D * esz;
-    // Aq = q W1^T, Bq = q W3^T, dHq = dO W2
-    if ((q = bgemm(bop(Q, D, x_bs, false, bf), bop(Wa.p[0], D, DD, false), tk[0], Dh, buf_bs, (int)C, Dh, D, n, 1.f,
-                   nullptr, 0.f, s)))
-      return q;
-    if ((q = bgemm(bop(Q, D, x_bs, false, bf), bop(Wa.p[2], D, DD, false), tk[1], Dh, buf_bs, (int)C, Dh, D, n, 1.f,
-                   nullptr, 0.f, s)))
-      return q;
+    // Aq = q W1^T, Bq = q W3^T (one launch), dHq = dO W2
+    {
+      const BGrp g2[2] = {{Q, Wa.p[0], tk[0], nullptr}, {Q, Wa.p[2], tk[1], nullptr}};
+      if ((q = bgemm_g(g2, 2, bop(Q, D, x_bs, false, bf), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
+                       1.f, 0.f, nullptr, 0, s)))
+        return q;
+    }
     if ((q = bgemm(bop(dO, D, x_bs, false, bf), bop(Wa.p[1], Dh, DD, true), tk[2], Dh, buf_bs, (int)C, Dh, D, n,
                    1.f, nullptr, 0.f, s)))
       return q;
     // -> dAq, dBq, Hq
     BWD_LAUNCH(bwd_app_elem_kernel, dim3(ew_grid((int64_t)n * C * Dh)), tk[0], tk[1], tk[2], n, C, Dh, buf_bs);
-    // dW2 += dO^T Hq ; dW1 += dAq^T q ; dW3 += dBq^T q
-    if ((q = bgemm(bop(dO, D, x_bs, true, bf), bop(tk[2], Dh, buf_bs, true), DW.p[1], Dh, DD, D, Dh, C, n, 1.f,
-                   DW.p[1], 1.f, s)))
-      return q;
-    if ((q = bgemm(bop(tk[0], Dh, buf_bs, true), bop(Q, D, x_bs, true, bf), DW.p[0], D, DD, Dh, D, C, n, 1.f,
-                   DW.p[0], 1.f, s)))
-      return q;
-    if ((q = bgemm(bop(tk[1], Dh, buf_bs, true), bop(Q, D, x_bs, true, bf), DW.p[2], D, DD, Dh, D, C, n, 1.f,
-                   DW.p[2], 1.f, s)))
-      return q;
+    // dW2 += dO^T Hq ; dW1 += dAq^T q, dW3 += dBq^T q (one launch); split over tokens
+    {
+      const BGrp g1[1] = {{dO, tk[2], DW.p[1], DW.p[1]}};
+      if ((q = bgemm_g(g1, 1, bop(dO, D, x_bs, true, bf), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
+                       1.f, fp(w.spl), w.spl_floats, s)))
+        return q;
+      const BGrp g2[2] = {{tk[0], Q, DW.p[0], DW.p[0]}, {tk[1], Q, DW.p[2], DW.p[2]}};
+      if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(Q, D, x_bs, true, bf), D, DD, Dh, D, C, n, 1.f,
+                       1.f, fp(w.spl), w.spl_floats, s)))
+        return q;
+    }
     // dq = dAq W1 + dBq W3
     float* dq = P.dq + t0 * D;
     if ((q = bgemm(bop(tk[0], Dh, buf_bs, false), bop(Wa.p[0], D, DD, true), dq, D, x_bs, (int)C, D, Dh, n, 1.f,
@@ -383,28 +467,29 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     const char* V = static_cast<const char*>(P.v) + (size_t)t0 * D * esz;
     float *A_ = tk[0], *B_ = tk[1], *G_ = tk[2], *E1 = tk[3], *E3 = tk[4], *H2 = tk[5], *gE1 = tk[6], *gE3 = tk[7],
           *gH2 = tk[8];
-    // recompute A = k W1^T, B = k W3^T, G = v W2 and the update terms
-    if ((q = bgemm(bop(K, D, x_bs, false, bf), bop(Wb.p[0], D, DD, false), A_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
-                   nullptr, 0.f, s)))
-      return q;
-    if ((q = bgemm(bop(K, D, x_bs, false, bf), bop(Wb.p[2], D, DD, false), B_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
-                   nullptr, 0.f, s)))
-      return q;
+    // recompute A = k W1^T, B = k W3^T (one launch), G = v W2 and the update terms
+    {
+      const BGrp g2[2] = {{K, Wb.p[0], A_, nullptr}, {K, Wb.p[2], B_, nullptr}};
+      if ((q = bgemm_g(g2, 2, bop(K, D, x_bs, false, bf), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
+                       1.f, 0.f, nullptr, 0, s)))
+        return q;
+    }
     if ((q = bgemm(bop(V, D, x_bs, false, bf), bop(Wb.p[1], Dh, DD, true), G_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
                    nullptr, 0.f, s)))
       return q;
     BWD_LAUNCH(bwd_upd_terms_kernel, dim3(ew_grid((int64_t)n * C * Dh)), (const float*)A_, (const float*)B_,
                (const float*)G_, P.lr, L * 3, t0, E1, E3, H2, n, C, Dh, buf_bs);
-    // U1 = E1^T k, U3 = E3^T k, U2 = v^T H2
-    if ((q = bgemm(bop(E1, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), U.p[0], D, DD, Dh, D, C, n, 1.f, nullptr,
-                   0.f, s)))
-      return q;
-    if ((q = bgemm(bop(E3, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), U.p[2], D, DD, Dh, D, C, n, 1.f, nullptr,
-                   0.f, s)))
-      return q;
-    if ((q = bgemm(bop(V, D, x_bs, true, bf), bop(H2, Dh, buf_bs, true), U.p[1], Dh, DD, D, Dh, C, n, 1.f, nullptr,
-                   0.f, s)))
-      return q;
+    // U1 = E1^T k, U3 = E3^T k (one launch), U2 = v^T H2; split over tokens
+    {
+      const BGrp g2[2] = {{E1, K, U.p[0], nullptr}, {E3, K, U.p[2], nullptr}};
+      if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), D, DD, Dh, D, C, n, 1.f,
+                       0.f, fp(w.spl), w.spl_floats, s)))
+        return q;
+      const BGrp g1[1] = {{V, H2, U.p[1], nullptr}};
+      if ((q = bgemm_g(g1, 1, bop(V, D, x_bs, true, bf), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
+                       0.f, fp(w.spl), w.spl_floats, s)))
+        return q;
+    }
     // the weight step W' = W + sgn step
     MatC step;
     float sgn = 1.f;
@@ -442,13 +527,13 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
       BWD_LAUNCH(bwd_mom_finish_kernel, dim3((unsigned)std::min<int64_t>((C + NT - 1) / NT, 64), n),
                  (const float*)fp(w.mpart), BWD_NBM, P.dbeta, L, t0, C);
     }
-    // through the update terms: gE1 = k gU1^T, gE3 = k gU3^T, gH2 = v gU2
-    if ((q = bgemm(bop(K, D, x_bs, false, bf), bop(gU.p[0], D, DD, false), gE1, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
-                   nullptr, 0.f, s)))
-      return q;
-    if ((q = bgemm(bop(K, D, x_bs, false, bf), bop(gU.p[2], D, DD, false), gE3, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
-                   nullptr, 0.f, s)))
-      return q;
+    // through the update terms: gE1 = k gU1^T, gE3 = k gU3^T (one launch), gH2 = v gU2
+    {
+      const BGrp g2[2] = {{K, gU.p[0], gE1, nullptr}, {K, gU.p[2], gE3, nullptr}};
+      if ((q = bgemm_g(g2, 2, bop(K, D, x_bs, false, bf), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
+                       1.f, 0.f, nullptr, 0, s)))
+        return q;
+    }
     if ((q = bgemm(bop(V, D, x_bs, false, bf), bop(gU.p[1], Dh, DD, true), gH2, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
                    nullptr, 0.f, s)))
       return q;
@@ -477,15 +562,14 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     if ((q = bgemm(bop(gH2, Dh, buf_bs, false), bop(Wb.p[1], Dh, DD, false), dv, D, x_bs, (int)C, D, Dh, n, 1.f, dv,
                    1.f, s)))
       return q;
-    // dW1 += gA^T k ; dW3 += gB^T k ; dW2 += v^T gG
-    if ((q = bgemm(bop(gE1, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), DW.p[0], D, DD, Dh, D, C, n, 1.f, DW.p[0],
-                   1.f, s)))
+    // dW1 += gA^T k, dW3 += gB^T k (one launch) ; dW2 += v^T gG; split over tokens
+    const BGrp g2[2] = {{gE1, K, DW.p[0], DW.p[0]}, {gE3, K, DW.p[2], DW.p[2]}};
+    if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), D, DD, Dh, D, C, n, 1.f, 1.f,
+                     fp(w.spl), w.spl_floats, s)))
       return q;
-    if ((q = bgemm(bop(gE3, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), DW.p[2], D, DD, Dh, D, C, n, 1.f, DW.p[2],
-                   1.f, s)))
-      return q;
-    return bgemm(bop(V, D, x_bs, true, bf), bop(gH2, Dh, buf_bs, true), DW.p[1], Dh, DD, D, Dh, C, n, 1.f, DW.p[1],
-                 1.f, s);
+    const BGrp g1[1] = {{V, gH2, DW.p[1], DW.p[1]}};
+    return bgemm_g(g1, 1, bop(V, D, x_bs, true, bf), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f, 1.f,
+                   fp(w.spl), w.spl_floats, s);
   };
 
   // ---- reverse sweep

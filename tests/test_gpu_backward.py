@@ -10,10 +10,10 @@ Exception, the Newton-Schulz optimisers at full workload length: the Muon
 recurrence amplifies rounding (each chunk's step is a quintic polynomial of
 the normalised gradient), so even a plain float32 evaluation of the oracle's
 own arithmetic differs from float64 by E32 = 2.0e-4 on the 3B-LM workload
-(d = 512, 8 chunks of 4,096; max over its 6 instances) and by 1.2e-2 on the
-video workload (d = 128, 12 Muon chunks; instances 0, 13, 27, 39).  Their
-full-size gate is 5 x E32, capped at the bf16-input gate of the forward
-(2e-2).
+(d = 512, 8 chunks of 4,096; max over its 6 instances), 7.4e-5 with
+momentum + Muon on the same shape, and 1.2e-2 on the video workload
+(d = 128, 12 Muon chunks; instances 0, 13, 27, 39).  Their full-size gate
+is 5 x E32, capped at the bf16-input gate of the forward (2e-2).
 """
 import dataclasses
 
@@ -29,7 +29,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(),
 
 TOL = 1e-4
 # full-size gates of the Newton-Schulz workloads (5 x the plain-fp32 error, capped at 2e-2)
-TOL_NS_FULL = {3: 1e-3, 5: 2e-2, 8: 1e-3}
+TOL_NS_FULL = {3: 1e-3, 5: 2e-2, 8: 4e-4}
 OUTS = ("dq", "dk", "dv", "dlr", "dbeta", "dW1", "dW2", "dW3", "dM1", "dM2", "dM3")
 
 

@@ -33,8 +33,8 @@ from typing import Dict, Sequence
 import numpy as np
 
 from .lact_oracle import (APPLY, APPLY_THEN_UPDATE, NS_COEFFS, NS_EPS, OPT_GD, OPT_MOMENTUM, OPT_MUON,
-                          OPT_MUON_MOMENTUM, UPDATE, UPDATE_THEN_APPLY, chunk_grads, f64, momentum_step,
-                          newton_schulz5, sigmoid, silu, silu_prime, update_step)
+                          OPT_MUON_MOMENTUM, UPDATE, UPDATE_THEN_APPLY, chunk_grads, f64, forward_instance,
+                          momentum_step, newton_schulz5, qk_preprocess, sigmoid, silu, silu_prime, update_step)
 
 
 def silu_second(x):
@@ -192,16 +192,45 @@ def update_vjp(W, M, K, V, lr, beta, opt, renorm, gWn, gMn, ns_steps=5):
     return gW, gM, dK, dV, dlr, dbeta
 
 
+# ------------------------------------------------------------ input / output scaling
+
+def qk_preprocess_vjp(x, g):
+    """Cotangent of the raw x for x_hat = silu(x) / ||silu(x)|| (per token,
+    over d) given the cotangent g of x_hat: with s = silu(x), n = ||s||,
+    s_hat = s / n: dx = silu'(x) (g - s_hat (s_hat . g)) / n."""
+    x = f64(x)
+    s = silu(x)
+    n = np.sqrt(np.sum(s * s, axis=-1, keepdims=True))
+    sh = s / n
+    return silu_prime(x) * (g - sh * np.sum(sh * g, axis=-1, keepdims=True)) / n
+
+
 # ------------------------------------------------------------ layer
 
 def backward_instance(q, k, v, lr, beta, W1, W2, W3, bounds: Sequence[int], flags: Sequence[int], order: int,
-                      opt: int, dO, gW=None, gM=None, renorm=True, M=None, ns_steps=5) -> Dict[str, np.ndarray]:
+                      opt: int, dO, gW=None, gM=None, renorm=True, M=None, ns_steps=5, qk_prep=False,
+                      oz=None) -> Dict[str, np.ndarray]:
     """Reverse mode through one instance's chunk schedule.  dO [L, D] is the
     output cotangent (rows of non-APPLY chunks are ignored); gW, gM the
-    cotangents of the final state (None: zero).  Returns dq, dk, dv [L, D],
-    dlr [L, 3], dbeta [L] (zeros without momentum), dW1, dW2, dW3, dM1,
-    dM2, dM3 (cotangents of the initial state)."""
+    cotangents of the final state (None: zero).  qk_prep: q and k are raw
+    and the layer pre-processes them; oz [L]: the output rows are scaled by
+    silu(oz) (both as in `lact_oracle.forward_instance`).  Returns dq, dk, dv
+    [L, D] (of the raw q, k when qk_prep), dlr [L, 3], dbeta [L] (zeros
+    without momentum), dW1, dW2, dW3, dM1, dM2, dM3 (cotangents of the
+    initial state) and doz [L] (only with oz)."""
     q, k, v, lr, dO = f64(q), f64(k), f64(v), f64(lr), f64(dO)
+    q_raw, k_raw = q, k
+    if qk_prep:
+        q, k = qk_preprocess(q_raw), qk_preprocess(k_raw)
+    doz = None
+    if oz is not None:
+        # o_s = o * silu(z): d z_t = silu'(z_t) <dO_t, o_t>, and o sees dO * silu(z)
+        z = f64(oz)
+        # the unscaled output of every APPLY row (zero elsewhere), from the forward
+        o = forward_instance(q, k, v, lr, beta, W1, W2, W3, bounds, flags, order, opt, renorm, M=M,
+                             ns_steps=ns_steps)["o"]
+        doz = silu_prime(z) * np.sum(dO * o, axis=1)
+        dO = dO * silu(z)[:, None]
     beta = None if beta is None else f64(beta)
     W = [f64(W1), f64(W2), f64(W3)]
     M = [np.zeros_like(w) for w in W] if M is None else [f64(m) for m in M]
@@ -239,12 +268,19 @@ def backward_instance(q, k, v, lr, beta, W1, W2, W3, bounds: Sequence[int], flag
             dX, gWa = apply_vjp(*Wc, q[a:b], dO[a:b])
             dq[a:b] = dX
             gWc = [g + h for g, h in zip(gWc, gWa)]
-    return {"dq": dq, "dk": dk, "dv": dv, "dlr": dlr, "dbeta": dbeta,
-            "dW1": gWc[0], "dW2": gWc[1], "dW3": gWc[2], "dM1": gMc[0], "dM2": gMc[1], "dM3": gMc[2]}
+    if qk_prep:
+        dq = qk_preprocess_vjp(q_raw, dq)
+        dk = qk_preprocess_vjp(k_raw, dk)
+    out = {"dq": dq, "dk": dk, "dv": dv, "dlr": dlr, "dbeta": dbeta,
+           "dW1": gWc[0], "dW2": gWc[1], "dW3": gWc[2], "dM1": gMc[0], "dM2": gMc[1], "dM3": gMc[2]}
+    if doz is not None:
+        out["doz"] = doz
+    return out
+
 
 
 def layer_backward(q, k, v, lr, beta, W1, W2, W3, bounds, flags, order, opt, dO, gW=None, gM=None, renorm=True,
-                   M=None, ns_steps=5) -> Dict[str, np.ndarray]:
+                   M=None, ns_steps=5, qk_prep=False, oz=None) -> Dict[str, np.ndarray]:
     """All instances ([n, L, D] inputs, [n, ...] state and cotangents)."""
     n = q.shape[0]
     outs = []
@@ -252,5 +288,6 @@ def layer_backward(q, k, v, lr, beta, W1, W2, W3, bounds, flags, order, opt, dO,
         pick = lambda xs: None if xs is None else [x[i] for x in xs]
         outs.append(backward_instance(q[i], k[i], v[i], lr[i], None if beta is None else beta[i],
                                       W1[i], W2[i], W3[i], bounds, flags, order, opt, dO[i],
-                                      pick(gW), pick(gM), renorm, pick(M), ns_steps))
+                                      pick(gW), pick(gM), renorm, pick(M), ns_steps, qk_prep,
+                                      None if oz is None else oz[i]))
     return {key: np.stack([o[key] for o in outs]) for key in outs[0]}

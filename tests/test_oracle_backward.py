@@ -44,9 +44,9 @@ def make(seed, D, Dh, L=13):
     return x, cot
 
 
-def objective(x, cot, order, opt, renorm, bounds=BOUNDS, flags=FLAGS):
+def objective(x, cot, order, opt, renorm, bounds=BOUNDS, flags=FLAGS, qk_prep=False):
     r = O.forward_instance(x["q"], x["k"], x["v"], x["lr"], x["beta"], x["W1"], x["W2"], x["W3"], bounds, flags,
-                           order, opt, renorm, M=[x["M1"], x["M2"], x["M3"]])
+                           order, opt, renorm, M=[x["M1"], x["M2"], x["M3"]], qk_prep=qk_prep, oz=x.get("oz"))
     J = float(np.sum(cot["dO"] * r["o"]))
     J += sum(float(np.sum(g * r[n])) for g, n in zip(cot["gW"], ("W1", "W2", "W3")))
     J += sum(float(np.sum(g * r[n])) for g, n in zip(cot["gM"], ("M1", "M2", "M3")))
@@ -57,16 +57,17 @@ GRAD_OF = {"q": "dq", "k": "dk", "v": "dv", "lr": "dlr", "beta": "dbeta", "W1": 
            "M1": "dM1", "M2": "dM2", "M3": "dM3"}
 
 
-def check_fd(x, cot, order, opt, renorm, seed, h=1e-5, tol=1e-6, bounds=BOUNDS, flags=FLAGS):
+def check_fd(x, cot, order, opt, renorm, seed, h=1e-5, tol=1e-6, bounds=BOUNDS, flags=FLAGS, qk_prep=False):
     """Directional derivative of J in a random direction per input against
     the oracle's gradient.  Central differences at h and h / 2 combined by
     Richardson extrapolation (the h^2 error term cancels; Newton-Schulz makes
     J curved enough that plain central differences need h ~ 1e-7)."""
     g = B.backward_instance(x["q"], x["k"], x["v"], x["lr"], x["beta"], x["W1"], x["W2"], x["W3"], bounds,
                             flags, order, opt, cot["dO"], cot["gW"], cot["gM"], renorm,
-                            M=[x["M1"], x["M2"], x["M3"]])
+                            M=[x["M1"], x["M2"], x["M3"]], qk_prep=qk_prep, oz=x.get("oz"))
     rng = np.random.default_rng(1000 + seed)
-    for name, gname in GRAD_OF.items():
+    names = dict(GRAD_OF, **({"oz": "doz"} if "oz" in x else {}))
+    for name, gname in names.items():
         d = rng.standard_normal(x[name].shape)
 
         def central(step):
@@ -74,8 +75,8 @@ def check_fd(x, cot, order, opt, renorm, seed, h=1e-5, tol=1e-6, bounds=BOUNDS, 
             xm = dict(x)
             xp[name] = x[name] + step * d
             xm[name] = x[name] - step * d
-            return (objective(xp, cot, order, opt, renorm, bounds, flags)
-                    - objective(xm, cot, order, opt, renorm, bounds, flags)) / (2 * step)
+            return (objective(xp, cot, order, opt, renorm, bounds, flags, qk_prep)
+                    - objective(xm, cot, order, opt, renorm, bounds, flags, qk_prep)) / (2 * step)
         fd = (4 * central(h / 2) - central(h)) / 3
         an = float(np.sum(g[gname] * d))
         scale = max(abs(fd), abs(an), 1e-3)
@@ -94,6 +95,27 @@ def test_finite_differences(opt, order, renorm, shape):
     seed = 17 * opt + 5 * order + 3 * int(renorm) + D + 7 * Dh
     x, cot = make(seed, D, Dh)
     check_fd(x, cot, order, opt, renorm, seed)
+
+
+@pytest.mark.parametrize("opt", [O.OPT_MOMENTUM, O.OPT_MUON])
+@pytest.mark.parametrize("order", [O.APPLY_THEN_UPDATE, O.UPDATE_THEN_APPLY])
+def test_finite_differences_raw_qk_and_output_scale(opt, order):
+    """q and k raw (the layer applies silu and the per-token L2 norm) and
+    the output scaled by silu(oz): gradients of the raw q, k and of oz."""
+    x, cot = make(40 + opt + order, 5, 5)
+    x["oz"] = np.random.default_rng(41).standard_normal(x["q"].shape[0])
+    check_fd(x, cot, order, opt, True, 40, qk_prep=True)
+
+
+def test_qk_preprocess_vjp_alone():
+    rng = np.random.default_rng(12)
+    X, gY = rng.standard_normal((6, 7)), rng.standard_normal((6, 7))
+    gX = B.qk_preprocess_vjp(X, gY)
+    for _ in range(3):
+        d = rng.standard_normal((6, 7))
+        h = 1e-6
+        fd = (np.sum(gY * O.qk_preprocess(X + h * d)) - np.sum(gY * O.qk_preprocess(X - h * d))) / (2 * h)
+        assert abs(fd - np.sum(gX * d)) <= 1e-7 * max(1.0, abs(fd))
 
 
 def test_finite_differences_single_chunk_and_apply_only_tail():

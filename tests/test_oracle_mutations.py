@@ -85,6 +85,10 @@ BWD_MUTATIONS = {
     "apply_vjp_W1_for_W3": ("dX = dA @ W1 + dB @ W3", "dX = dA @ W1 + dB @ W1"),
     "update_then_apply_reads_old_state": ("dX, gWa = apply_vjp(*states[c + 1][0], q[a:b], dO[a:b])",
                                           "dX, gWa = apply_vjp(*states[c][0], q[a:b], dO[a:b])"),
+    "qk_prep_vjp_projection_dropped": ("(g - sh * np.sum(sh * g, axis=-1, keepdims=True)) / n", "g / n"),
+    "output_scale_grad_silu_not_derivative": ("doz = silu_prime(z) * np.sum(dO * o, axis=1)",
+                                              "doz = silu(z) * np.sum(dO * o, axis=1)"),
+    "output_scale_not_on_cotangent": ("dO = dO * silu(z)[:, None]", "dO = dO"),
 }
 
 

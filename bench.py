@@ -117,7 +117,8 @@ def cpu_baseline_backward(wl, inp, dO, budget):
     while time.perf_counter() - t0 < budget:
         i = done % wl.n_inst
         OB.backward_instance(inp.q[i], inp.k[i], inp.v[i], inp.lr[i], inp.beta[i] if mom else None,
-                             inp.W1[i], inp.W2[i], inp.W3[i], wl.bounds, wl.flags, wl.order, wl.opt, dO[i])
+                             inp.W1[i], inp.W2[i], inp.W3[i], wl.bounds, wl.flags, wl.order, wl.opt, dO[i],
+                             qk_prep=wl.layer_qk_prep, oz=inp.oz[i] if wl.out_scale else None)
         done += 1
     dt = time.perf_counter() - t0
     tokens = wl.tokens * done / wl.n_inst
@@ -231,25 +232,21 @@ def main():
     stream = torch.cuda.current_stream()
 
     if args.backward:
-        if wl.layer_qk_prep or wl.out_scale:
-            print("the backward pass takes pre-processed q, k and no output scale; pick another --config",
-                  file=sys.stderr)
-            sys.exit(2)
         # seeded output cotangent in the io dtype
         rng = np.random.default_rng([0, 77])
         dO_np = rng.standard_normal((wl.n_inst, wl.L, wl.D)).astype(np.float32)
         if wl.io_dtype == W.DTYPE_BF16:
             dO_np = W.f32_to_bf16_bits(dO_np)
         dO = dev(dO_np)
-        p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, 3, dh=wl.dh)
+        p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, 3, dh=wl.dh, qk_prep=wl.layer_qk_prep)
         ws = torch.empty(lact.backward_workspace_size(p, wl.L, 0, wl.order, bounds, flags), dtype=torch.uint8,
                          device="cuda")
         box = {"out": None}
 
         def step():
             box["out"] = lact.layer_backward(q, k, v, lr, beta if mom else None, *Ws, *Ms, dO=dO, order=wl.order,
-                                             opt=wl.opt, bounds=bounds, flags=flags, out=box["out"],
-                                             workspace=ws, stream=stream)
+                                             opt=wl.opt, bounds=bounds, flags=flags, qk_prep=wl.layer_qk_prep,
+                                             oz=oz, out=box["out"], workspace=ws, stream=stream)
         kf = backward_kernel_flops(wl, lact)
         peak, peak_name = PEAK_FP32_MFMA, "fp32"
         metric = ("LaCT layer backward tokens/sec (gradients of q, k, v, lr, beta and the initial state; "

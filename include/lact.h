@@ -206,36 +206,41 @@ lact_status lact_layer_forward_scaled(const lact_problem* p, const void* q, cons
  * state W1..W3, M1..M3 (as passed to lact_layer_forward, i.e. BEFORE it
  * overwrote them).
  *
- * Inputs (device): q, k, v [n, L, D] io_dtype; lr [n, L, 3]; beta [n, L]
- * (momentum optimisers, else may be NULL); W1..W3 initial weights, M1..M3
- * initial momentum (momentum optimisers, else may be NULL); dO [n, L, D]
- * io_dtype (rows outside APPLY chunks are not read); gW1..gW3, gM1..gM3
- * cotangents of the final state, each may be NULL (= zero).  All read only.
- * Outputs (device, float32, fully written): dq, dk, dv [n, L, D] (zero on
- * rows outside APPLY, resp. UPDATE chunks); dlr [n, L, 3] (zero outside
- * UPDATE chunks); dbeta [n, L] (momentum optimisers; may be NULL otherwise);
- * dW1..dW3 (shapes of W1..W3); dM1..dM3 (shapes of M1..M3; may be NULL --
- * for GD and MUON they equal gM).  The call recomputes the forward state
- * trajectory itself with fp32-grade products (rec_planes is ignored) and
- * runs every backward product fp32-grade.  LACT_QK_PREP is not supported
- * (LACT_ERR_UNSUPPORTED).  Workspace: lact_backward_workspace_size bytes,
- * 256-B aligned.  Errors as for lact_layer_forward; outputs are undefined
- * after LACT_ERR_HIP.
+ * Inputs (device): q, k, v [n, L, D] io_dtype (raw q, k with LACT_QK_PREP);
+ * lr [n, L, 3]; beta [n, L] (momentum optimisers, else may be NULL); oz
+ * [n, L] fp32 or NULL: the output-scale pre-activation of
+ * lact_layer_forward_scaled (NULL: the unscaled layer); W1..W3 initial
+ * weights, M1..M3 initial momentum (momentum optimisers, else may be NULL);
+ * dO [n, L, D] io_dtype, the cotangent of the (scaled) output (rows outside
+ * APPLY chunks are not read); gW1..gW3, gM1..gM3 cotangents of the final
+ * state, each may be NULL (= zero).  All read only.
+ * Outputs (device, float32, fully written): dq, dk, dv [n, L, D] (of the raw
+ * q, k with LACT_QK_PREP; zero on rows outside APPLY, resp. UPDATE chunks);
+ * dlr [n, L, 3] (zero outside UPDATE chunks); dbeta [n, L] (momentum
+ * optimisers; may be NULL otherwise); doz [n, L] (with oz; zero outside
+ * APPLY chunks); dW1..dW3 (shapes of W1..W3); dM1..dM3 (shapes of M1..M3;
+ * may be NULL -- for GD and MUON they equal gM).  The call recomputes the
+ * forward state trajectory itself with fp32-grade products (rec_planes is
+ * ignored; raw q, k are pre-processed in fp32, not rounded to the io dtype)
+ * and runs every backward product fp32-grade.  Workspace:
+ * lact_backward_workspace_size bytes, 256-B aligned.  Errors as for
+ * lact_layer_forward; outputs are undefined after LACT_ERR_HIP.
  */
 size_t lact_backward_workspace_size(const lact_problem* p, int64_t L, int64_t chunk, int32_t order,
                                     const int64_t* bounds, const uint8_t* flags, int32_t n_chunks);
 
 lact_status lact_layer_backward(const lact_problem* p, const void* q, const void* k,
-                                const void* v, const float* lr, const float* beta, int64_t L,
-                                int64_t chunk, int32_t order, const int64_t* bounds,
+                                const void* v, const float* lr, const float* beta,
+                                const float* oz, int64_t L, int64_t chunk, int32_t order,
+                                const int64_t* bounds,
                                 const uint8_t* flags, int32_t n_chunks, const float* W1,
                                 const float* W2, const float* W3, const float* M1,
                                 const float* M2, const float* M3, const void* dO,
                                 const float* gW1, const float* gW2, const float* gW3,
                                 const float* gM1, const float* gM2, const float* gM3, float* dq,
-                                float* dk, float* dv, float* dlr, float* dbeta, float* dW1,
-                                float* dW2, float* dW3, float* dM1, float* dM2, float* dM3,
-                                void* ws, size_t ws_bytes, void* stream);
+                                float* dk, float* dv, float* dlr, float* dbeta, float* doz,
+                                float* dW1, float* dW2, float* dW3, float* dM1, float* dM2,
+                                float* dM3, void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* lact_status_str(lact_status s);

@@ -1328,17 +1328,17 @@ size_t lact_backward_workspace_size(const lact_problem* p, int64_t L, int64_t ch
 }
 
 lact_status lact_layer_backward(const lact_problem* p, const void* q, const void* k, const void* v, const float* lr,
-                                const float* beta, int64_t L, int64_t chunk, int32_t order, const int64_t* bounds,
+                                const float* beta, const float* oz, int64_t L, int64_t chunk, int32_t order,
+                                const int64_t* bounds,
                                 const uint8_t* flags, int32_t n_chunks, const float* W1, const float* W2,
                                 const float* W3, const float* M1, const float* M2, const float* M3, const void* dO,
                                 const float* gW1, const float* gW2, const float* gW3, const float* gM1,
                                 const float* gM2, const float* gM3, float* dq, float* dk, float* dv, float* dlr,
-                                float* dbeta, float* dW1, float* dW2, float* dW3, float* dM1, float* dM2, float* dM3,
-                                void* ws, size_t ws_bytes, void* stream) {
+                                float* dbeta, float* doz, float* dW1, float* dW2, float* dW3, float* dM1, float* dM2,
+                                float* dM3, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   lact_status r = validate_problem(p);
   if (r) return r;
-  if (p->flags & LACT_QK_PREP) return fail(LACT_ERR_UNSUPPORTED, "the backward pass takes pre-processed q, k only");
   std::vector<int64_t> b;
   std::vector<uint8_t> f;
   r = make_schedule(L, chunk, order, bounds, flags, n_chunks, b, f);
@@ -1365,6 +1365,7 @@ lact_status lact_layer_backward(const lact_problem* p, const void* q, const void
   if (any_app) {
     NEED(q, 16);
     NEED(dO, 16);
+    if (oz) NEED(doz, 4);
   }
   if (any_upd) {
     NEED(k, 16);
@@ -1380,6 +1381,7 @@ lact_status lact_layer_backward(const lact_problem* p, const void* q, const void
       NEED(dbeta, 4);
     }
   }
+  if (!aligned(oz, 4)) return fail(LACT_ERR_INVALID_ARG, "oz is not 4-byte aligned");
   for (const void* g : {(const void*)gW1, (const void*)gW2, (const void*)gW3, (const void*)gM1, (const void*)gM2,
                         (const void*)gM3, (const void*)dM1, (const void*)dM2, (const void*)dM3, (const void*)dbeta})
     if (g && !aligned(g, 4)) return fail(LACT_ERR_INVALID_ARG, "misaligned optional pointer");
@@ -1393,12 +1395,14 @@ lact_status lact_layer_backward(const lact_problem* p, const void* q, const void
   r = check_device();
   if (r) return r;
   BwdPtrs P;
-  P.q = q;
-  P.k = k;
-  P.v = v;
+  P.q = any_app ? q : nullptr;
+  P.k = any_upd ? k : nullptr;
+  P.v = any_upd ? v : nullptr;
   P.dO = dO;
   P.lr = lr;
   P.beta = beta;
+  P.oz = any_app ? oz : nullptr;
+  P.doz = any_app && oz ? doz : nullptr;
   const float* Ws[3] = {W1, W2, W3};
   const float* Ms[3] = {M1, M2, M3};
   const float* gWs[3] = {gW1, gW2, gW3};

@@ -79,6 +79,92 @@ __global__ __launch_bounds__(NT) void bwd_app_elem_kernel(float* Aq, float* Bq, 
   }
 }
 
+// Apply backward terms with the per-token output scale o_t * silu(z_t), one
+// wave per token row, in place: dH holds dO W2 for the UNSCALED cotangent;
+// with s_t = silu(z_t): dAq = s_t dH Bq S'(Aq), dBq = s_t dH S(Aq), and dH
+// becomes s_t Hq (so that dW2 += dO^T (s Hq)); doz_t = silu'(z_t) <dH_t, Hq_t>
+// (= silu'(z_t) <dO_t, o_t>, o the unscaled output).
+__global__ __launch_bounds__(NT) void bwd_app_elem_oz_kernel(float* Aq, float* Bq, float* dH, const float* oz,
+                                                             int64_t oz_bs, int64_t t0, float* doz, int n, int64_t C,
+                                                             int Dh, int64_t buf_bs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (NT / WAVE) + (threadIdx.x >> 6);
+  if (row >= (int64_t)n * C) return;
+  const int64_t i = row / C, t = row % C;
+  const float z = oz[i * oz_bs + t0 + t];
+  const float sg = 1.0f / (1.0f + __expf(-z));
+  const float sz = z * sg, spz = sg * (1.0f + z * (1.0f - sg));
+  const int64_t base = i * buf_bs + t * Dh;
+  float dz = 0.f;
+  for (int j = lane; j < Dh; j += WAVE) {
+    const int64_t o = base + j;
+    const float a = Aq[o], b = Bq[o], g = dH[o];
+    const BwdSig q = bwd_sig(a);
+    const float hq = q.S * b;
+    dz += g * hq;
+    Aq[o] = sz * g * b * q.Sp;
+    Bq[o] = sz * g * q.S;
+    dH[o] = sz * hq;
+  }
+  dz = wave_sum(dz);
+  if (lane == 0) doz[i * oz_bs + t0 + t] = spz * dz;
+}
+
+__device__ __forceinline__ float bwd_ld(const float* p) { return *p; }
+__device__ __forceinline__ float bwd_ld(const bf16_t* p) { return __uint_as_float((uint32_t)p->x << 16); }
+
+// q / k pre-processing for the backward, kept in fp32 (the forward's
+// "LaCT架构核心思想解析" §1.2 map x -> silu(x) / ||silu(x)|| over a token's d
+// features), one wave per token row; prep = 0 copies x to fp32 unchanged.
+template <typename T>
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(const T* src, float* dst, int64_t rows, int D, int prep) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (NT / WAVE) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const T* x = src + row * D;
+  float* y = dst + row * D;
+  if (!prep) {
+    for (int j = lane; j < D; j += WAVE) y[j] = bwd_ld(x + j);
+    return;
+  }
+  float ss = 0.f;
+  for (int j = lane; j < D; j += WAVE) {
+    const float v = bwd_ld(x + j), sv = v / (1.0f + __expf(-v));
+    ss += sv * sv;
+  }
+  const float inv = 1.0f / sqrtf(wave_sum(ss));
+  for (int j = lane; j < D; j += WAVE) {
+    const float v = bwd_ld(x + j);
+    y[j] = v / (1.0f + __expf(-v)) * inv;
+  }
+}
+
+// Backward of the pre-processing, in place on the cotangent g, one wave per
+// row: with s = silu(x), n = ||s||: g <- silu'(x) (g - s (s . g) / n^2) / n.
+template <typename T>
+__global__ __launch_bounds__(NT) void bwd_prep_vjp_kernel(const T* src, float* g, int64_t rows, int D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (NT / WAVE) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const T* x = src + row * D;
+  float* gr = g + row * D;
+  float ss = 0.f, dt = 0.f;
+  for (int j = lane; j < D; j += WAVE) {
+    const float v = bwd_ld(x + j), sv = v / (1.0f + __expf(-v));
+    ss += sv * sv;
+    dt += sv * gr[j];
+  }
+  ss = wave_sum(ss);
+  dt = wave_sum(dt);
+  const float n = sqrtf(ss), c = dt / ss;
+  for (int j = lane; j < D; j += WAVE) {
+    const float v = bwd_ld(x + j);
+    const float sg = 1.0f / (1.0f + __expf(-v));
+    const float sv = v * sg, sp = sg * (1.0f + v * (1.0f - sg));
+    gr[j] = sp * (gr[j] - sv * c) / n;
+  }
+}
+
 // Update terms of the chunk: E1 = lr1 G B S'(A), E3 = lr3 G S(A),
 // H2 = lr2 S(A) B (so U1 = E1^T K, U3 = E3^T K, U2 = V^T H2).
 __global__ __launch_bounds__(NT) void bwd_upd_terms_kernel(const float* A, const float* B, const float* G,

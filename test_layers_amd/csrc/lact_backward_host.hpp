@@ -179,12 +179,17 @@ struct BwdWs {
   size_t X = 0, Am = 0, Pm = 0, gP = 0, gA = 0, Qm = 0, g0 = 0, g1 = 0, nrm = 0, part = 0;
   size_t bbar = 0, mpart = 0;
   size_t spl = 0, spl_floats = 0;   // split-K partials of the token contractions
+  size_t qf = 0, kf = 0, vf = 0;     // LACT_QK_PREP: fp32 q^, k^ and v [n, L, d]
   size_t total = 0;
 };
 
+// The replay of the forward state trajectory: fp32-grade recurrence; with
+// raw q / k it runs on the backward's own fp32 pre-processed copies (not
+// rounded to the io dtype), so its io type is fp32.
 lact_problem replay_problem(const lact_problem& p) {
   lact_problem f = p;
-  f.rec_planes = 3;   // fp32-grade recurrence
+  f.rec_planes = 3;
+  if (p.flags & LACT_QK_PREP) f.io_dtype = LACT_DTYPE_F32;
   f.flags &= LACT_NO_RENORM;
   return f;
 }
@@ -253,6 +258,12 @@ BwdWs bwd_layout(const lact_problem& p, const std::vector<int64_t>& b, const std
     w.spl_floats = std::max(s1, s2);
     w.spl = take(w.spl_floats * 4);
   }
+  if (p.flags & LACT_QK_PREP) {
+    const size_t L = (size_t)b.back();
+    w.qf = take(n * L * D * 4);
+    w.kf = take(n * L * D * 4);
+    w.vf = take(n * L * D * 4);
+  }
   w.total = off;
   return w;
 }
@@ -261,6 +272,8 @@ BwdWs bwd_layout(const lact_problem& p, const std::vector<int64_t>& b, const std
 struct BwdPtrs {
   const void *q, *k, *v, *dO;
   const float *lr, *beta;
+  const float* oz;   // per-token output-scale pre-activation [n, L] (NULL: no scale)
+  float* doz;
   const float *W[3], *M[3], *gW[3], *gM[3];
   float *dq, *dk, *dv, *dlr, *dbeta;
   float *dW[3], *dM[3];
@@ -275,7 +288,7 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   const int m = std::min(D, Dh), kf = std::max(D, Dh);
   const int64_t MM = (int64_t)m * m;
   const bool bf = p.io_dtype == LACT_DTYPE_BF16;
-  const size_t esz = bf ? 2 : 4;
+  const bool prep = (p.flags & LACT_QK_PREP) != 0;
   const int64_t x_bs = L * D;          // instance stride of q, k, v, dO, dq, dk, dv
   const int64_t buf_bs = w.cmax * Dh;  // instance stride of the token buffers
   const bool mom = uses_momentum(p.opt), ns = uses_ns(p.opt);
@@ -300,7 +313,33 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   const MatP U = set(w.U), STEP = set(w.step), GWP = set(w.gWp), GU = set(w.gU), GM = set(w.gM), GX = set(w.gX);
   MatP DW;
   for (int j = 0; j < 3; ++j) DW.p[j] = P.dW[j];
-  lact_status r;
+  lact_status r = LACT_OK;
+
+  // ---- the operands of the sweep: the caller's q, k, v in the io dtype, or
+  // (raw q / k) fp32 pre-processed copies of q, k and an fp32 copy of v
+  const void* Qs = P.q;
+  const void* Ks = P.k;
+  const void* Vs = P.v;
+  bool bq = bf, bv = bf;
+  const bool bo = bf;
+  if (prep) {
+    const int64_t rows = (int64_t)n * L;
+    const dim3 g((unsigned)((rows + 3) / 4));
+    auto conv = [&](const void* src, float* dst, int pr) -> lact_status {
+      if (!src) return LACT_OK;
+      if (bf) BWD_LAUNCH(bwd_prep_kernel<bf16_t>, g, static_cast<const bf16_t*>(src), dst, rows, D, pr);
+      else BWD_LAUNCH(bwd_prep_kernel<float>, g, static_cast<const float*>(src), dst, rows, D, pr);
+      return LACT_OK;
+    };
+    if ((r = conv(P.q, fp(w.qf), 1))) return r;
+    if ((r = conv(P.k, fp(w.kf), 1))) return r;
+    if ((r = conv(P.v, fp(w.vf), 0))) return r;
+    Qs = fp(w.qf);
+    Ks = fp(w.kf);
+    Vs = fp(w.vf);
+    bq = bv = false;
+  }
+  const size_t eq = bq ? 2 : 4, ev = bv ? 2 : 4, eo = bo ? 2 : 4;
 
   // ---- outputs start at zero (rows outside the chunks that write them stay zero)
   BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L * D)), P.dq, (int64_t)n * L * D, 0.f);
@@ -308,6 +347,7 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L * D)), P.dv, (int64_t)n * L * D, 0.f);
   BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L * 3)), P.dlr, (int64_t)n * L * 3, 0.f);
   if (P.dbeta) BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L)), P.dbeta, (int64_t)n * L, 0.f);
+  if (P.doz) BWD_LAUNCH(bwd_fill_kernel, dim3(ew_grid((int64_t)n * L)), P.doz, (int64_t)n * L, 0.f);
   // running cotangents of the state: W in the caller's dW arrays, M in the workspace
   for (int j = 0; j < 3; ++j) {
     const size_t mb = (size_t)n * DD * 4;
@@ -334,8 +374,8 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
       const MatP wa = slotW(u), wb = slotW(u + 1);
       HIP_TRY(hipMemcpyAsync(wb.p[0], wa.p[0], (size_t)MD * 4, hipMemcpyDeviceToDevice, s));
       Ptrs F;
-      F.k = P.k;
-      F.v = P.v;
+      F.k = Ks;
+      F.v = Vs;
       F.lr = P.lr;
       F.beta = P.beta;
       F.W1 = wb.p[0];
@@ -425,28 +465,32 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   // ---- apply backward of rows [t0, t0 + C) read with weights Wa
   auto apply_bwd = [&](const MatC& Wa, int64_t t0, int64_t C) -> lact_status {
     lact_status q;
-    const char* Q = static_cast<const char*>(P.q) + (size_t)t0 * D * esz;
-    const char* dO = static_cast<const char*>(P.dO) + (size_t)t0 * D * esz;
+    const char* Q = static_cast<const char*>(Qs) + (size_t)t0 * D * eq;
+    const char* dO = static_cast<const char*>(P.dO) + (size_t)t0 * D * eo;
     // Aq = q W1^T, Bq = q W3^T (one launch), dHq = dO W2
     {
       const BGrp g2[2] = {{Q, Wa.p[0], tk[0], nullptr}, {Q, Wa.p[2], tk[1], nullptr}};
-      if ((q = bgemm_g(g2, 2, bop(Q, D, x_bs, false, bf), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
+      if ((q = bgemm_g(g2, 2, bop(Q, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
                        1.f, 0.f, nullptr, 0, s)))
         return q;
     }
-    if ((q = bgemm(bop(dO, D, x_bs, false, bf), bop(Wa.p[1], Dh, DD, true), tk[2], Dh, buf_bs, (int)C, Dh, D, n,
+    if ((q = bgemm(bop(dO, D, x_bs, false, bo), bop(Wa.p[1], Dh, DD, true), tk[2], Dh, buf_bs, (int)C, Dh, D, n,
                    1.f, nullptr, 0.f, s)))
       return q;
-    // -> dAq, dBq, Hq
-    BWD_LAUNCH(bwd_app_elem_kernel, dim3(ew_grid((int64_t)n * C * Dh)), tk[0], tk[1], tk[2], n, C, Dh, buf_bs);
+    // -> dAq, dBq, Hq (with an output scale: s Hq, and doz)
+    if (P.oz)
+      BWD_LAUNCH(bwd_app_elem_oz_kernel, dim3((unsigned)(((int64_t)n * C + 3) / 4)), tk[0], tk[1], tk[2], P.oz, L,
+                 t0, P.doz, n, C, Dh, buf_bs);
+    else
+      BWD_LAUNCH(bwd_app_elem_kernel, dim3(ew_grid((int64_t)n * C * Dh)), tk[0], tk[1], tk[2], n, C, Dh, buf_bs);
     // dW2 += dO^T Hq ; dW1 += dAq^T q, dW3 += dBq^T q (one launch); split over tokens
     {
       const BGrp g1[1] = {{dO, tk[2], DW.p[1], DW.p[1]}};
-      if ((q = bgemm_g(g1, 1, bop(dO, D, x_bs, true, bf), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
+      if ((q = bgemm_g(g1, 1, bop(dO, D, x_bs, true, bo), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
                        1.f, fp(w.spl), w.spl_floats, s)))
         return q;
       const BGrp g2[2] = {{tk[0], Q, DW.p[0], DW.p[0]}, {tk[1], Q, DW.p[2], DW.p[2]}};
-      if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(Q, D, x_bs, true, bf), D, DD, Dh, D, C, n, 1.f,
+      if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(Q, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f,
                        1.f, fp(w.spl), w.spl_floats, s)))
         return q;
     }
@@ -463,18 +507,18 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   auto update_bwd = [&](int u, int64_t t0, int64_t C) -> lact_status {
     lact_status q;
     const MatC Wb = cset(slotW(u));
-    const char* K = static_cast<const char*>(P.k) + (size_t)t0 * D * esz;
-    const char* V = static_cast<const char*>(P.v) + (size_t)t0 * D * esz;
+    const char* K = static_cast<const char*>(Ks) + (size_t)t0 * D * eq;
+    const char* V = static_cast<const char*>(Vs) + (size_t)t0 * D * ev;
     float *A_ = tk[0], *B_ = tk[1], *G_ = tk[2], *E1 = tk[3], *E3 = tk[4], *H2 = tk[5], *gE1 = tk[6], *gE3 = tk[7],
           *gH2 = tk[8];
     // recompute A = k W1^T, B = k W3^T (one launch), G = v W2 and the update terms
     {
       const BGrp g2[2] = {{K, Wb.p[0], A_, nullptr}, {K, Wb.p[2], B_, nullptr}};
-      if ((q = bgemm_g(g2, 2, bop(K, D, x_bs, false, bf), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
+      if ((q = bgemm_g(g2, 2, bop(K, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
                        1.f, 0.f, nullptr, 0, s)))
         return q;
     }
-    if ((q = bgemm(bop(V, D, x_bs, false, bf), bop(Wb.p[1], Dh, DD, true), G_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+    if ((q = bgemm(bop(V, D, x_bs, false, bv), bop(Wb.p[1], Dh, DD, true), G_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
                    nullptr, 0.f, s)))
       return q;
     BWD_LAUNCH(bwd_upd_terms_kernel, dim3(ew_grid((int64_t)n * C * Dh)), (const float*)A_, (const float*)B_,
@@ -482,11 +526,11 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     // U1 = E1^T k, U3 = E3^T k (one launch), U2 = v^T H2; split over tokens
     {
       const BGrp g2[2] = {{E1, K, U.p[0], nullptr}, {E3, K, U.p[2], nullptr}};
-      if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), D, DD, Dh, D, C, n, 1.f,
+      if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f,
                        0.f, fp(w.spl), w.spl_floats, s)))
         return q;
       const BGrp g1[1] = {{V, H2, U.p[1], nullptr}};
-      if ((q = bgemm_g(g1, 1, bop(V, D, x_bs, true, bf), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
+      if ((q = bgemm_g(g1, 1, bop(V, D, x_bs, true, bv), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
                        0.f, fp(w.spl), w.spl_floats, s)))
         return q;
     }
@@ -530,11 +574,11 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     // through the update terms: gE1 = k gU1^T, gE3 = k gU3^T (one launch), gH2 = v gU2
     {
       const BGrp g2[2] = {{K, gU.p[0], gE1, nullptr}, {K, gU.p[2], gE3, nullptr}};
-      if ((q = bgemm_g(g2, 2, bop(K, D, x_bs, false, bf), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
+      if ((q = bgemm_g(g2, 2, bop(K, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
                        1.f, 0.f, nullptr, 0, s)))
         return q;
     }
-    if ((q = bgemm(bop(V, D, x_bs, false, bf), bop(gU.p[1], Dh, DD, true), gH2, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+    if ((q = bgemm(bop(V, D, x_bs, false, bv), bop(gU.p[1], Dh, DD, true), gH2, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
                    nullptr, 0.f, s)))
       return q;
     // dk = E1 gU1 + E3 gU3 ; dv = H2 gU2^T
@@ -564,11 +608,11 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
       return q;
     // dW1 += gA^T k, dW3 += gB^T k (one launch) ; dW2 += v^T gG; split over tokens
     const BGrp g2[2] = {{gE1, K, DW.p[0], DW.p[0]}, {gE3, K, DW.p[2], DW.p[2]}};
-    if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bf), D, DD, Dh, D, C, n, 1.f, 1.f,
+    if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f, 1.f,
                      fp(w.spl), w.spl_floats, s)))
       return q;
     const BGrp g1[1] = {{V, gH2, DW.p[1], DW.p[1]}};
-    return bgemm_g(g1, 1, bop(V, D, x_bs, true, bf), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f, 1.f,
+    return bgemm_g(g1, 1, bop(V, D, x_bs, true, bv), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f, 1.f,
                    fp(w.spl), w.spl_floats, s);
   };
 
@@ -585,6 +629,18 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
       if ((r = update_bwd(u, t0, C))) return r;
     if (A_ && (order == LACT_APPLY_THEN_UPDATE || !U_))
       if ((r = apply_bwd(cset(slotW(u)), t0, C))) return r;
+  }
+  // raw q / k: through the pre-processing (rows outside the chunks stay zero)
+  if (prep) {
+    const int64_t rows = (int64_t)n * L;
+    const dim3 g((unsigned)((rows + 3) / 4));
+    for (int m = 0; m < 2; ++m) {
+      const void* x = m == 0 ? P.q : P.k;
+      float* gx = m == 0 ? P.dq : P.dk;
+      if (!x) continue;
+      if (bf) BWD_LAUNCH(bwd_prep_vjp_kernel<bf16_t>, g, static_cast<const bf16_t*>(x), gx, rows, D);
+      else BWD_LAUNCH(bwd_prep_vjp_kernel<float>, g, static_cast<const float*>(x), gx, rows, D);
+    }
   }
   for (int j = 0; j < 3; ++j)
     if (P.dM[j]) HIP_TRY(hipMemcpyAsync(P.dM[j], GM.p[j], (size_t)n * DD * 4, hipMemcpyDeviceToDevice, s));

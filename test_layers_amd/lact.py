@@ -95,8 +95,8 @@ def lib() -> ctypes.CDLL:
     L.lact_backward_workspace_size.restype = sz
     L.lact_backward_workspace_size.argtypes = [P, i64, i64, i32, vp, vp, i32]
     L.lact_layer_backward.restype = i32
-    L.lact_layer_backward.argtypes = ([P, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32]
-                                      + [vp] * 6 + [vp] + [vp] * 6 + [vp] * 5 + [vp] * 6 + [vp, sz, vp])
+    L.lact_layer_backward.argtypes = ([P, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32]
+                                      + [vp] * 6 + [vp] + [vp] * 6 + [vp] * 6 + [vp] * 6 + [vp, sz, vp])
     L.lact_status_str.restype = ctypes.c_char_p
     L.lact_status_str.argtypes = [i32]
     L.lact_last_error.restype = ctypes.c_char_p
@@ -168,13 +168,14 @@ def backward_workspace_size(p: Problem, L: int, chunk: int = 0, order: int = 0,
     return n
 
 
-def layer_backward_ptr(p: Problem, q, k, v, lr, beta, L, chunk, order, bounds, flags, W1, W2, W3, M1, M2, M3,
-                       dO, gW1, gW2, gW3, gM1, gM2, gM3, dq, dk, dv, dlr, dbeta, dW1, dW2, dW3, dM1, dM2, dM3,
+def layer_backward_ptr(p: Problem, q, k, v, lr, beta, oz, L, chunk, order, bounds, flags, W1, W2, W3, M1, M2, M3,
+                       dO, gW1, gW2, gW3, gM1, gM2, gM3, dq, dk, dv, dlr, dbeta, doz, dW1, dW2, dW3, dM1, dM2, dM3,
                        ws, ws_bytes, stream) -> int:
     bp, fp, nc, _keep = _sched(bounds, flags)
-    return lib().lact_layer_backward(ctypes.byref(p), q, k, v, lr, beta, L, chunk, order, bp, fp, nc,
+    return lib().lact_layer_backward(ctypes.byref(p), q, k, v, lr, beta, oz, L, chunk, order, bp, fp, nc,
                                      W1, W2, W3, M1, M2, M3, dO, gW1, gW2, gW3, gM1, gM2, gM3,
-                                     dq, dk, dv, dlr, dbeta, dW1, dW2, dW3, dM1, dM2, dM3, ws, ws_bytes, stream)
+                                     dq, dk, dv, dlr, dbeta, doz, dW1, dW2, dW3, dM1, dM2, dM3, ws, ws_bytes,
+                                     stream)
 
 
 def chunk_update_ptr(p: Problem, k, v, lr, beta, Lc, seq_stride, W1, W2, W3, M1, M2, M3,
@@ -310,24 +311,27 @@ def apply(q, W1, W2, W3, o=None, *, Lq: Optional[int] = None, qk_prep: bool = Fa
 
 def layer_backward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, dO, gW=None, gM=None,
                    chunk: int = 0, order: int = APPLY_THEN_UPDATE, opt: int = OPT_GD, bounds=None, flags=None,
-                   ns_iters: int = 5, renorm: bool = True, out=None, workspace=None, stream=None):
+                   ns_iters: int = 5, renorm: bool = True, qk_prep: bool = False, oz=None, out=None,
+                   workspace=None, stream=None):
     """Backward of layer_forward (lact_layer_backward).  Inputs as for
     layer_forward with W1..W3, M1..M3 the INITIAL state (read only); dO
-    [n, L, d] in q's dtype; gW, gM: None or 3-tuples of cotangents of the
-    final state.  Returns a dict of fp32 gradients dq, dk, dv, dlr, dbeta
-    (momentum optimisers, else None), dW1..dW3, dM1..dM3 (momentum
-    optimisers, else None); `out` (such a dict from an earlier call with the
-    same shapes) is filled instead of allocating."""
+    [n, L, d] in q's dtype (the cotangent of the scaled output when oz is
+    given); gW, gM: None or 3-tuples of cotangents of the final state.
+    Returns a dict of fp32 gradients dq, dk, dv (of the raw q, k with
+    qk_prep), dlr, dbeta (momentum optimisers, else None), doz (with oz, else
+    None), dW1..dW3, dM1..dM3 (momentum optimisers, else None); `out` (such a
+    dict from an earlier call with the same shapes) is filled instead of
+    allocating."""
     torch = _torch()
     n, L, D = q.shape
     io = _io_dtype(q)
-    p = problem(n, D, io, opt, 3, ns_iters, renorm, dh=W1.shape[1])
+    p = problem(n, D, io, opt, 3, ns_iters, renorm, dh=W1.shape[1], qk_prep=qk_prep)
     mom = opt in (OPT_MOMENTUM, OPT_MUON_MOMENTUM)
     f32 = torch.float32
     if out is None:
         e = lambda *shape: torch.empty(*shape, dtype=f32, device=q.device)
         out = {"dq": e(n, L, D), "dk": e(n, L, D), "dv": e(n, L, D), "dlr": e(n, L, 3),
-               "dbeta": e(n, L) if mom else None}
+               "dbeta": e(n, L) if mom else None, "doz": e(n, L) if oz is not None else None}
         for j, w in enumerate((W1, W2, W3)):
             out[f"dW{j + 1}"] = torch.empty_like(w)
             out[f"dM{j + 1}"] = torch.empty_like(w) if mom else None
@@ -337,11 +341,12 @@ def layer_backward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, 
     ws = _workspace(need, workspace, q.device)
     check(layer_backward_ptr(
         p, _ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"), _ptr(lr, f32, "lr"),
-        _ptr(beta, f32, "beta"), L, chunk, order, bounds, flags,
+        _ptr(beta, f32, "beta"), _ptr(oz, f32, "oz"), L, chunk, order, bounds, flags,
         _ptr(W1, f32, "W1"), _ptr(W2, f32, "W2"), _ptr(W3, f32, "W3"),
         _ptr(M1, f32, "M1"), _ptr(M2, f32, "M2"), _ptr(M3, f32, "M3"), _ptr(dO, q.dtype, "dO"),
         *[_ptr(g, f32, "gW") for g in gW], *[_ptr(g, f32, "gM") for g in gM],
         _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlr"]), _ptr(out["dbeta"]),
+        _ptr(out.get("doz")),
         _ptr(out["dW1"]), _ptr(out["dW2"]), _ptr(out["dW3"]), _ptr(out["dM1"]), _ptr(out["dM2"]), _ptr(out["dM3"]),
         ws.data_ptr(), ws.numel(), _stream(stream)))
     return out

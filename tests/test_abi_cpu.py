@@ -253,22 +253,28 @@ def test_single_hip_runtime_in_process():
 
 # ----------------------------------------------------------------- backward entry point
 def bwd(p, L=512, chunk=128, order=0, bounds=None, flags=None, ws_bytes=None, **ptrs):
-    names = ["q", "k", "v", "lr", "beta", "W1", "W2", "W3", "M1", "M2", "M3", "dO", "gW1", "gW2", "gW3", "gM1",
-             "gM2", "gM3", "dq", "dk", "dv", "dlr", "dbeta", "dW1", "dW2", "dW3", "dM1", "dM2", "dM3", "ws"]
+    names = ["q", "k", "v", "lr", "beta", "oz", "W1", "W2", "W3", "M1", "M2", "M3", "dO", "gW1", "gW2", "gW3",
+             "gM1", "gM2", "gM3", "dq", "dk", "dv", "dlr", "dbeta", "doz", "dW1", "dW2", "dW3", "dM1", "dM2", "dM3",
+             "ws"]
     a = {n: FAKE for n in names}
     a.update(ptrs)
     if ws_bytes is None:
         ws_bytes = 1 << 40
-    return lact.layer_backward_ptr(p, a["q"], a["k"], a["v"], a["lr"], a["beta"], L, chunk, order, bounds, flags,
-                                   a["W1"], a["W2"], a["W3"], a["M1"], a["M2"], a["M3"], a["dO"], a["gW1"],
+    return lact.layer_backward_ptr(p, a["q"], a["k"], a["v"], a["lr"], a["beta"], a["oz"], L, chunk, order, bounds,
+                                   flags, a["W1"], a["W2"], a["W3"], a["M1"], a["M2"], a["M3"], a["dO"], a["gW1"],
                                    a["gW2"], a["gW3"], a["gM1"], a["gM2"], a["gM3"], a["dq"], a["dk"], a["dv"],
-                                   a["dlr"], a["dbeta"], a["dW1"], a["dW2"], a["dW3"], a["dM1"], a["dM2"], a["dM3"],
-                                   a["ws"], ws_bytes, None)
+                                   a["dlr"], a["dbeta"], a["doz"], a["dW1"], a["dW2"], a["dW3"], a["dM1"], a["dM2"],
+                                   a["dM3"], a["ws"], ws_bytes, None)
 
 
-def test_backward_rejects_raw_qk():
-    assert bwd(P(qk_prep=True)) == lact.ERR_UNSUPPORTED
-    assert "pre-processed" in lact.last_error()
+def test_backward_takes_raw_qk_and_output_scale():
+    # raw q / k and an output scale pass validation (the workspace grows by the fp32 copies)
+    p = P(qk_prep=True)
+    assert bwd(p) not in (lact.ERR_INVALID_ARG, lact.ERR_UNSUPPORTED), lact.last_error()
+    assert lact.backward_workspace_size(p, 512, 128) > lact.backward_workspace_size(P(), 512, 128)
+    assert bwd(P(), doz=None) == lact.ERR_INVALID_ARG          # oz given, doz missing
+    assert bwd(P(), oz=None, doz=None) not in (lact.ERR_INVALID_ARG,), lact.last_error()
+    assert bwd(P(), oz=FAKE + 2) == lact.ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("ptrs,opt", [

@@ -30,7 +30,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(),
 TOL = 1e-4
 # full-size gates of the Newton-Schulz workloads (5 x the plain-fp32 error, capped at 2e-2)
 TOL_NS_FULL = {3: 1e-3, 5: 2e-2, 8: 4e-4}
-OUTS = ("dq", "dk", "dv", "dlr", "dbeta", "dW1", "dW2", "dW3", "dM1", "dM2", "dM3")
+OUTS = ("dq", "dk", "dv", "dlr", "dbeta", "doz", "dW1", "dW2", "dW3", "dM1", "dM2", "dM3")
 
 
 @pytest.fixture(scope="module")
@@ -66,7 +66,8 @@ def run_case(lact, wl, seed=0, order=None, renorm=True, state_cot=True, M0_scale
         dev(inp.W1), dev(inp.W2), dev(inp.W3), *([dev(m) for m in M0] if mom else [None] * 3),
         dO=dev(dO), gW=None if gW is None else [dev(g) for g in gW],
         gM=None if gM is None else [dev(g) for g in gM], order=order, opt=wl.opt,
-        bounds=list(wl.bounds), flags=list(wl.flags), renorm=renorm)
+        bounds=list(wl.bounds), flags=list(wl.flags), renorm=renorm, qk_prep=wl.layer_qk_prep,
+        oz=dev(inp.oz) if wl.out_scale else None)
     torch.cuda.synchronize()
     idx = list(range(wl.n_inst)) if instances is None else list(instances)
     pick = lambda x: None if x is None else x[idx]
@@ -74,7 +75,8 @@ def run_case(lact, wl, seed=0, order=None, renorm=True, state_cot=True, M0_scale
                             pick(inp.W1), pick(inp.W2), pick(inp.W3), wl.bounds, wl.flags, order, wl.opt,
                             pick(dO), None if gW is None else [pick(g) for g in gW],
                             None if gM is None else [pick(g) for g in gM], renorm,
-                            M=[pick(m) for m in M0] if mom else None)
+                            M=[pick(m) for m in M0] if mom else None, qk_prep=wl.layer_qk_prep,
+                            oz=pick(inp.oz) if wl.out_scale else None)
     errs = {}
     for key in OUTS:
         g = out.get(key)
@@ -110,6 +112,8 @@ CASES = {
                                  bounds=W.video_schedule(3, 200)[0], flags=W.video_schedule(3, 200)[1]),
     # rectangular fast weights, dh > d, momentum
     "rect_dh_gt_d": W.CONFIGS[10].scaled(n_inst=2, L=2 * 256 + 30, chunk=256),
+    # raw q / k (pre-processed by the layer) and the per-token output scale
+    "raw_qk_scaled": W.CONFIGS[9].scaled(n_inst=2, L=3 * 256 + 100, chunk=256),
 }
 
 
@@ -147,6 +151,16 @@ def test_backward_rectangular_newton_schulz(lact, shape, opt):
     assert max(errs.values()) <= TOL, errs
 
 
+@pytest.mark.parametrize("order", [W.APPLY_THEN_UPDATE, W.UPDATE_THEN_APPLY])
+def test_backward_raw_qk_output_scale_muon_fp32(lact, order):
+    """Raw q / k and the output scale with fp32 inputs and Muon, both orders."""
+    base = W.CONFIGS[9].scaled(n_inst=2, L=3 * 128 + 40, chunk=128)
+    wl = dataclasses.replace(base, D=64, io_dtype=W.DTYPE_F32, opt=W.OPT_MUON)
+    errs = run_case(lact, wl, seed=8, order=order)
+    log(f"  order={order}: errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert "doz" in errs and max(errs.values()) <= TOL, errs
+
+
 def test_backward_without_state_cotangents(lact):
     """gW = gM = NULL means zero cotangents of the final state."""
     wl = W.CONFIGS[2].scaled(n_inst=2, L=2 * 256, chunk=256)
@@ -163,7 +177,7 @@ def test_backward_no_update_passes_state_cotangent_through(lact):
 
 
 # ----------------------------------------------------------------- full workload sizes
-FULL = {1: None, 2: None, 3: None, 4: None, 5: (0, 13, 27, 39), 8: None, 10: None}
+FULL = {1: None, 2: None, 3: None, 4: None, 5: (0, 13, 27, 39), 8: None, 9: None, 10: None}
 
 
 @pytest.mark.timeout(900)

@@ -192,3 +192,38 @@ def test_backward_full_size(lact, cid):
     tol = TOL_NS_FULL[cid] if wl.opt in (W.OPT_MUON, W.OPT_MUON_MOMENTUM) else TOL
     log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} } gate={tol}")
     assert max(errs.values()) <= tol, errs
+
+
+@pytest.mark.parametrize("opt", [W.OPT_MOMENTUM, W.OPT_MUON])
+def test_backward_maximum_width(lact, opt):
+    """d = dh = 1024, the widest the library takes (Newton-Schulz on
+    1024 x 1024 matrices for Muon)."""
+    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=1, L=2 * 64 + 16, chunk=64), D=1024, opt=opt)
+    errs = run_case(lact, wl, seed=9)
+    log(f"  d=1024 opt={opt}: errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= TOL, errs
+
+
+def test_backward_empty_sequence(lact):
+    """L = 0: no chunk, so dW = gW and dM = gM exactly."""
+    dev = "cuda"
+    n, D = 2, 128
+    g = torch.Generator(device="cpu").manual_seed(3)
+    Ws = [torch.randn(n, D, D, generator=g).to(dev) for _ in range(3)]
+    gW = [torch.randn(n, D, D, generator=g).to(dev) for _ in range(3)]
+    gM = [torch.randn(n, D, D, generator=g).to(dev) for _ in range(3)]
+    empty = torch.empty(n, 0, D, dtype=torch.bfloat16, device=dev)
+    out = lact.layer_backward(empty, empty, empty, torch.empty(n, 0, 3, device=dev), torch.empty(n, 0, device=dev),
+                              *Ws, *[torch.zeros_like(w) for w in Ws], dO=empty, gW=gW, gM=gM, chunk=64,
+                              opt=W.OPT_MOMENTUM)
+    torch.cuda.synchronize()
+    for j in range(3):
+        assert torch.equal(out[f"dW{j + 1}"], gW[j])
+        assert torch.equal(out[f"dM{j + 1}"], gM[j])
+
+
+def test_backward_single_token_chunk(lact):
+    """A one-token last chunk (the shortest a chunk can be)."""
+    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=257, chunk=256))
+    errs = run_case(lact, wl, seed=10)
+    assert max(errs.values()) <= TOL, errs

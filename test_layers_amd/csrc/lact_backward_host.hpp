@@ -16,8 +16,10 @@
 //                  gE1 = k gU1^T, gE3 = k gU3^T, gH2 = v gU2,
 //                  dk = E1 gU1 + E3 gU3 + gA W1 + gB W3, dv = H2 gU2^T + gG W2^T,
 //                  dW1 += gA^T k, dW3 += gB^T k, dW2 += v^T gG.
-// Every product runs on the grouped GEMM with fp32 operands split into three
-// bf16 planes (bf16 inputs are exact in one plane).
+// Every product runs on the grouped GEMM with fp32 operands split into bf16
+// planes (bf16 inputs are exact in one plane): three (fp32 grade) for the
+// Newton-Schulz products and for every product of the Newton-Schulz
+// optimisers, two (16-bit significands) for the others of GD and momentum.
 
 // ----------------------------------------------------------------- products
 // grid of a grid-stride elementwise kernel
@@ -52,18 +54,22 @@ lact_status bgemm_t(GemmArgs& g, hipStream_t s) {
   return launch_gemm_t<TA, PA, CA, TB, PB, CB, float, 64>(g, t, s);
 }
 
-template <typename F>
+// bf16 planes per fp32 operand of a backward product: two (16-bit
+// significands) or three (fp32 grade)
+template <int PL>
 lact_status bgemm_form(const BOp& A, const BOp& B, GemmArgs& g, hipStream_t s) {
   if (!A.bf16 && !B.bf16) {
-    if (!A.colk && !B.colk) return bgemm_t<float, 3, false, float, 3, false>(g, s);
-    if (!A.colk && B.colk) return bgemm_t<float, 3, false, float, 3, true>(g, s);
-    if (A.colk && B.colk) return bgemm_t<float, 3, true, float, 3, true>(g, s);
-  } else if (A.bf16 && !B.bf16) {
-    if (!A.colk && !B.colk) return bgemm_t<bf16_t, 1, false, float, 3, false>(g, s);
-    if (!A.colk && B.colk) return bgemm_t<bf16_t, 1, false, float, 3, true>(g, s);
-    if (A.colk && B.colk) return bgemm_t<bf16_t, 1, true, float, 3, true>(g, s);
-  } else if (!A.bf16 && B.bf16) {
-    if (A.colk && B.colk) return bgemm_t<float, 3, true, bf16_t, 1, true>(g, s);
+    if (!A.colk && !B.colk) return bgemm_t<float, PL, false, float, PL, false>(g, s);
+    if (!A.colk && B.colk) return bgemm_t<float, PL, false, float, PL, true>(g, s);
+    if (A.colk && B.colk) return bgemm_t<float, PL, true, float, PL, true>(g, s);
+  } else {
+    if (A.bf16 && !B.bf16) {
+      if (!A.colk && !B.colk) return bgemm_t<bf16_t, 1, false, float, PL, false>(g, s);
+      if (!A.colk && B.colk) return bgemm_t<bf16_t, 1, false, float, PL, true>(g, s);
+      if (A.colk && B.colk) return bgemm_t<bf16_t, 1, true, float, PL, true>(g, s);
+    } else if (!A.bf16 && B.bf16) {
+      if (A.colk && B.colk) return bgemm_t<float, PL, true, bf16_t, 1, true>(g, s);
+    }
   }
   return fail(LACT_ERR_UNSUPPORTED, "internal: backward product form");
 }
@@ -92,7 +98,8 @@ struct BGrp {
 // over K into fp32 partials in `spl` (spl_floats of scratch), summed in
 // fixed order by bwd_splitsum_kernel.
 lact_status bgemm_g(const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t ldc, int64_t c_bs, int M, int N,
-                    int64_t K, int batch, float alpha, float beta, float* spl, size_t spl_floats, hipStream_t s) {
+                    int64_t K, int batch, float alpha, float beta, float* spl, size_t spl_floats, hipStream_t s,
+                    bool fp32_grade = false) {
   if (M <= 0 || N <= 0 || batch <= 0 || ng <= 0) return LACT_OK;
   GemmArgs g = gemm_args();
   g.ngroups = ng;
@@ -126,7 +133,7 @@ lact_status bgemm_g(const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t 
       g.g[i].Cin = nullptr;
       g.g[i].M = M;
     }
-    lact_status r = bgemm_form<void>(A, B, g, s);
+    lact_status r = fp32_grade ? bgemm_form<3>(A, B, g, s) : bgemm_form<2>(A, B, g, s);
     if (r) return r;
     for (int i = 0; i < ng; ++i) {
       KernelTimer kt(LACT_K_BWD_ELEM, s);
@@ -148,14 +155,14 @@ lact_status bgemm_g(const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t 
     g.g[i].Cin = gs[i].Cin;
     g.g[i].M = M;
   }
-  return bgemm_form<void>(A, B, g, s);
+  return fp32_grade ? bgemm_form<3>(A, B, g, s) : bgemm_form<2>(A, B, g, s);
 }
 
-// one product, no split
-lact_status bgemm(BOp A, BOp B, float* C, int64_t ldc, int64_t c_bs, int M, int N, int64_t K, int batch, float alpha,
-                  const float* Cin, float beta, hipStream_t s) {
+// one Newton-Schulz product (fp32 grade)
+lact_status bgemm_ns(BOp A, BOp B, float* C, int64_t ldc, int64_t c_bs, int M, int N, int64_t K, int batch,
+                     float alpha, const float* Cin, float beta, hipStream_t s) {
   const BGrp g1{A.p, B.p, C, Cin};
-  return bgemm_g(&g1, 1, A, B, ldc, c_bs, M, N, K, batch, alpha, beta, nullptr, 0, s);
+  return bgemm_g(&g1, 1, A, B, ldc, c_bs, M, N, K, batch, alpha, beta, nullptr, 0, s, true);
 }
 
 #define BWD_LAUNCH(kernel, grid, ...)                      \
@@ -412,13 +419,13 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     for (int i = 0; i < iters; ++i) {
       lact_status q;
       // A = X X^T ; P = c A A + b A ; X' = P X + a X
-      if ((q = bgemm(bop(Xi(i), kf, DD, false), bop(Xi(i), kf, DD, false), Ai(i), m, MM, m, m, kf, 3 * n, 1.f,
+      if ((q = bgemm_ns(bop(Xi(i), kf, DD, false), bop(Xi(i), kf, DD, false), Ai(i), m, MM, m, m, kf, 3 * n, 1.f,
                      nullptr, 0.f, s)))
         return q;
-      if ((q = bgemm(bop(Ai(i), m, MM, false), bop(Ai(i), m, MM, false), Pi(i), m, MM, m, m, m, 3 * n, nc, Ai(i),
+      if ((q = bgemm_ns(bop(Ai(i), m, MM, false), bop(Ai(i), m, MM, false), Pi(i), m, MM, m, m, m, 3 * n, nc, Ai(i),
                      nb, s)))
         return q;
-      if ((q = bgemm(bop(Pi(i), m, MM, false), bop(Xi(i), kf, DD, true), Xi(i + 1), kf, DD, m, kf, m, 3 * n, 1.f,
+      if ((q = bgemm_ns(bop(Pi(i), m, MM, false), bop(Xi(i), kf, DD, true), Xi(i + 1), kf, DD, m, kf, m, 3 * n, 1.f,
                      Xi(i), na, s)))
         return q;
     }
@@ -433,23 +440,23 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     for (int i = iters - 1; i >= 0; --i) {
       lact_status q;
       // gP = g X^T
-      if ((q = bgemm(bop(g0, kf, DD, false), bop(Xi(i), kf, DD, false), fp(w.gP), m, MM, m, m, kf, 3 * n, 1.f,
+      if ((q = bgemm_ns(bop(g0, kf, DD, false), bop(Xi(i), kf, DD, false), fp(w.gP), m, MM, m, m, kf, 3 * n, 1.f,
                      nullptr, 0.f, s)))
         return q;
       // gA = c gP A + b gP, then += c A gP
-      if ((q = bgemm(bop(fp(w.gP), m, MM, false), bop(Ai(i), m, MM, false), fp(w.gA), m, MM, m, m, m, 3 * n, nc,
+      if ((q = bgemm_ns(bop(fp(w.gP), m, MM, false), bop(Ai(i), m, MM, false), fp(w.gA), m, MM, m, m, m, 3 * n, nc,
                      fp(w.gP), nb, s)))
         return q;
-      if ((q = bgemm(bop(Ai(i), m, MM, false), bop(fp(w.gP), m, MM, true), fp(w.gA), m, MM, m, m, m, 3 * n, nc,
+      if ((q = bgemm_ns(bop(Ai(i), m, MM, false), bop(fp(w.gP), m, MM, true), fp(w.gA), m, MM, m, m, m, 3 * n, nc,
                      fp(w.gA), 1.f, s)))
         return q;
       BWD_LAUNCH(bwd_symadd_kernel, dim3(ew_grid(3 * n * MM)), (const float*)fp(w.gA), fp(w.Qm), m,
                  (int64_t)3 * n);
       // g' = P g + a g + (gA + gA^T) X
-      if ((q = bgemm(bop(Pi(i), m, MM, false), bop(g0, kf, DD, true), g1, kf, DD, m, kf, m, 3 * n, 1.f, g0, na,
+      if ((q = bgemm_ns(bop(Pi(i), m, MM, false), bop(g0, kf, DD, true), g1, kf, DD, m, kf, m, 3 * n, 1.f, g0, na,
                      s)))
         return q;
-      if ((q = bgemm(bop(fp(w.Qm), m, MM, false), bop(Xi(i), kf, DD, true), g1, kf, DD, m, kf, m, 3 * n, 1.f, g1,
+      if ((q = bgemm_ns(bop(fp(w.Qm), m, MM, false), bop(Xi(i), kf, DD, true), g1, kf, DD, m, kf, m, 3 * n, 1.f, g1,
                      1.f, s)))
         return q;
       std::swap(g0, g1);
@@ -462,6 +469,20 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     return LACT_OK;
   };
 
+  // the sweep's products: two planes per fp32 operand for GD and momentum,
+  // three (fp32 grade) for the Newton-Schulz optimisers, whose backward
+  // amplifies the rounding of the recomputed directions U
+  const bool fp32g = ns;
+  auto gemm1 = [&](BOp A, BOp B, float* C, int64_t ldc, int64_t c_bs, int M, int N, int64_t K, int batch,
+                   float alpha, const float* Cin, float beta, hipStream_t st) {
+    const BGrp g1{A.p, B.p, C, Cin};
+    return bgemm_g(&g1, 1, A, B, ldc, c_bs, M, N, K, batch, alpha, beta, nullptr, 0, st, fp32g);
+  };
+  auto gemmg = [&](const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t ldc, int64_t c_bs, int M, int N,
+                   int64_t K, int batch, float alpha, float beta, float* spl, size_t spl_floats, hipStream_t st) {
+    return bgemm_g(gs, ng, A, B, ldc, c_bs, M, N, K, batch, alpha, beta, spl, spl_floats, st, fp32g);
+  };
+
   // ---- apply backward of rows [t0, t0 + C) read with weights Wa
   auto apply_bwd = [&](const MatC& Wa, int64_t t0, int64_t C) -> lact_status {
     lact_status q;
@@ -470,11 +491,11 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     // Aq = q W1^T, Bq = q W3^T (one launch), dHq = dO W2
     {
       const BGrp g2[2] = {{Q, Wa.p[0], tk[0], nullptr}, {Q, Wa.p[2], tk[1], nullptr}};
-      if ((q = bgemm_g(g2, 2, bop(Q, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
+      if ((q = gemmg(g2, 2, bop(Q, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
                        1.f, 0.f, nullptr, 0, s)))
         return q;
     }
-    if ((q = bgemm(bop(dO, D, x_bs, false, bo), bop(Wa.p[1], Dh, DD, true), tk[2], Dh, buf_bs, (int)C, Dh, D, n,
+    if ((q = gemm1(bop(dO, D, x_bs, false, bo), bop(Wa.p[1], Dh, DD, true), tk[2], Dh, buf_bs, (int)C, Dh, D, n,
                    1.f, nullptr, 0.f, s)))
       return q;
     // -> dAq, dBq, Hq (with an output scale: s Hq, and doz)
@@ -486,20 +507,20 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     // dW2 += dO^T Hq ; dW1 += dAq^T q, dW3 += dBq^T q (one launch); split over tokens
     {
       const BGrp g1[1] = {{dO, tk[2], DW.p[1], DW.p[1]}};
-      if ((q = bgemm_g(g1, 1, bop(dO, D, x_bs, true, bo), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
+      if ((q = gemmg(g1, 1, bop(dO, D, x_bs, true, bo), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
                        1.f, fp(w.spl), w.spl_floats, s)))
         return q;
       const BGrp g2[2] = {{tk[0], Q, DW.p[0], DW.p[0]}, {tk[1], Q, DW.p[2], DW.p[2]}};
-      if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(Q, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f,
+      if ((q = gemmg(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(Q, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f,
                        1.f, fp(w.spl), w.spl_floats, s)))
         return q;
     }
     // dq = dAq W1 + dBq W3
     float* dq = P.dq + t0 * D;
-    if ((q = bgemm(bop(tk[0], Dh, buf_bs, false), bop(Wa.p[0], D, DD, true), dq, D, x_bs, (int)C, D, Dh, n, 1.f,
+    if ((q = gemm1(bop(tk[0], Dh, buf_bs, false), bop(Wa.p[0], D, DD, true), dq, D, x_bs, (int)C, D, Dh, n, 1.f,
                    nullptr, 0.f, s)))
       return q;
-    return bgemm(bop(tk[1], Dh, buf_bs, false), bop(Wa.p[2], D, DD, true), dq, D, x_bs, (int)C, D, Dh, n, 1.f, dq,
+    return gemm1(bop(tk[1], Dh, buf_bs, false), bop(Wa.p[2], D, DD, true), dq, D, x_bs, (int)C, D, Dh, n, 1.f, dq,
                  1.f, s);
   };
 
@@ -514,11 +535,11 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     // recompute A = k W1^T, B = k W3^T (one launch), G = v W2 and the update terms
     {
       const BGrp g2[2] = {{K, Wb.p[0], A_, nullptr}, {K, Wb.p[2], B_, nullptr}};
-      if ((q = bgemm_g(g2, 2, bop(K, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
+      if ((q = gemmg(g2, 2, bop(K, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
                        1.f, 0.f, nullptr, 0, s)))
         return q;
     }
-    if ((q = bgemm(bop(V, D, x_bs, false, bv), bop(Wb.p[1], Dh, DD, true), G_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+    if ((q = gemm1(bop(V, D, x_bs, false, bv), bop(Wb.p[1], Dh, DD, true), G_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
                    nullptr, 0.f, s)))
       return q;
     BWD_LAUNCH(bwd_upd_terms_kernel, dim3(ew_grid((int64_t)n * C * Dh)), (const float*)A_, (const float*)B_,
@@ -526,11 +547,11 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     // U1 = E1^T k, U3 = E3^T k (one launch), U2 = v^T H2; split over tokens
     {
       const BGrp g2[2] = {{E1, K, U.p[0], nullptr}, {E3, K, U.p[2], nullptr}};
-      if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f,
+      if ((q = gemmg(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f,
                        0.f, fp(w.spl), w.spl_floats, s)))
         return q;
       const BGrp g1[1] = {{V, H2, U.p[1], nullptr}};
-      if ((q = bgemm_g(g1, 1, bop(V, D, x_bs, true, bv), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
+      if ((q = gemmg(g1, 1, bop(V, D, x_bs, true, bv), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
                        0.f, fp(w.spl), w.spl_floats, s)))
         return q;
     }
@@ -574,45 +595,45 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     // through the update terms: gE1 = k gU1^T, gE3 = k gU3^T (one launch), gH2 = v gU2
     {
       const BGrp g2[2] = {{K, gU.p[0], gE1, nullptr}, {K, gU.p[2], gE3, nullptr}};
-      if ((q = bgemm_g(g2, 2, bop(K, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
+      if ((q = gemmg(g2, 2, bop(K, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
                        1.f, 0.f, nullptr, 0, s)))
         return q;
     }
-    if ((q = bgemm(bop(V, D, x_bs, false, bv), bop(gU.p[1], Dh, DD, true), gH2, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
+    if ((q = gemm1(bop(V, D, x_bs, false, bv), bop(gU.p[1], Dh, DD, true), gH2, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
                    nullptr, 0.f, s)))
       return q;
     // dk = E1 gU1 + E3 gU3 ; dv = H2 gU2^T
     float* dk = P.dk + t0 * D;
     float* dv = P.dv + t0 * D;
-    if ((q = bgemm(bop(E1, Dh, buf_bs, false), bop(gU.p[0], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f,
+    if ((q = gemm1(bop(E1, Dh, buf_bs, false), bop(gU.p[0], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f,
                    nullptr, 0.f, s)))
       return q;
-    if ((q = bgemm(bop(E3, Dh, buf_bs, false), bop(gU.p[2], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
+    if ((q = gemm1(bop(E3, Dh, buf_bs, false), bop(gU.p[2], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
                    1.f, s)))
       return q;
-    if ((q = bgemm(bop(H2, Dh, buf_bs, false), bop(gU.p[1], Dh, DD, false), dv, D, x_bs, (int)C, D, Dh, n, 1.f,
+    if ((q = gemm1(bop(H2, Dh, buf_bs, false), bop(gU.p[1], Dh, DD, false), dv, D, x_bs, (int)C, D, Dh, n, 1.f,
                    nullptr, 0.f, s)))
       return q;
     // -> gA, gB, gG (in place) and dlr
     BWD_LAUNCH(bwd_upd_elem_kernel, dim3((unsigned)(((int64_t)n * C + 3) / 4)), (const float*)A_, (const float*)B_,
                (const float*)G_, P.lr, L * 3, t0, gE1, gE3, gH2, P.dlr, n, C, Dh, buf_bs);
     // dk += gA W1 + gB W3 ; dv += gG W2^T
-    if ((q = bgemm(bop(gE1, Dh, buf_bs, false), bop(Wb.p[0], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
+    if ((q = gemm1(bop(gE1, Dh, buf_bs, false), bop(Wb.p[0], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
                    1.f, s)))
       return q;
-    if ((q = bgemm(bop(gE3, Dh, buf_bs, false), bop(Wb.p[2], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
+    if ((q = gemm1(bop(gE3, Dh, buf_bs, false), bop(Wb.p[2], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
                    1.f, s)))
       return q;
-    if ((q = bgemm(bop(gH2, Dh, buf_bs, false), bop(Wb.p[1], Dh, DD, false), dv, D, x_bs, (int)C, D, Dh, n, 1.f, dv,
+    if ((q = gemm1(bop(gH2, Dh, buf_bs, false), bop(Wb.p[1], Dh, DD, false), dv, D, x_bs, (int)C, D, Dh, n, 1.f, dv,
                    1.f, s)))
       return q;
     // dW1 += gA^T k, dW3 += gB^T k (one launch) ; dW2 += v^T gG; split over tokens
     const BGrp g2[2] = {{gE1, K, DW.p[0], DW.p[0]}, {gE3, K, DW.p[2], DW.p[2]}};
-    if ((q = bgemm_g(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f, 1.f,
+    if ((q = gemmg(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f, 1.f,
                      fp(w.spl), w.spl_floats, s)))
       return q;
     const BGrp g1[1] = {{V, gH2, DW.p[1], DW.p[1]}};
-    return bgemm_g(g1, 1, bop(V, D, x_bs, true, bv), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f, 1.f,
+    return gemmg(g1, 1, bop(V, D, x_bs, true, bv), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f, 1.f,
                    fp(w.spl), w.spl_floats, s);
   };
 

@@ -220,12 +220,12 @@ lact_status lact_layer_forward_scaled(const lact_problem* p, const void* q, cons
  * optimisers; may be NULL otherwise); doz [n, L] (with oz; zero outside
  * APPLY chunks); dW1..dW3 (shapes of W1..W3); dM1..dM3 (shapes of M1..M3;
  * may be NULL -- for GD and MUON they equal gM).  The call recomputes the
- * forward state trajectory itself with fp32-grade products (rec_planes is
- * ignored; raw q, k are pre-processed in fp32, not rounded to the io dtype).
- * Its products take fp32 operands as bf16 planes with fp32 accumulation:
- * three planes (fp32 grade) for MUON and MUON_MOMENTUM, whose
- * Newton-Schulz backward amplifies rounding, two (16-bit significands) for
- * GD and MOMENTUM.  Workspace:
+ * forward state trajectory itself (rec_planes is ignored; raw q, k are
+ * pre-processed in fp32, not rounded to the io dtype).  Its products take
+ * fp32 operands as bf16 planes with fp32 accumulation: three planes (fp32
+ * grade) for MUON and MUON_MOMENTUM, whose Newton-Schulz backward amplifies
+ * rounding, and for fp32 inputs; two (16-bit significands) for GD and
+ * MOMENTUM.  Workspace:
  * lact_backward_workspace_size bytes, 256-B aligned.  Errors as for
  * lact_layer_forward; outputs are undefined after LACT_ERR_HIP.
  */

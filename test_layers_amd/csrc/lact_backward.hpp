@@ -272,64 +272,66 @@ __global__ __launch_bounds__(NT) void bwd_renorm_kernel(MatC W, MatC step, float
   }
 }
 
-// mean of beta over the chunk's rows [t0, t0 + C), one workgroup per instance
-__global__ __launch_bounds__(NT) void bwd_beta_mean_kernel(const float* beta, int64_t beta_bs, int64_t t0, int64_t C,
-                                                           float* bbar) {
-  __shared__ float red[NT / WAVE];
-  const int i = blockIdx.x;
-  float s = 0.f;
-  for (int64_t t = threadIdx.x; t < C; t += NT) s += beta[i * beta_bs + t0 + t];
-  s = wave_sum(s);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float tot = 0.f;
-    for (int w = 0; w < NT / WAVE; ++w) tot += red[w];
-    bbar[i] = tot / (float)C;
-  }
-}
-
 // Momentum backward (M_next = bbar M - U, the weight step reads M_next with
 // sign -1): gMt = gM_next - gX, where gX is the cotangent reaching M_next
 // through the weight step (gW' for MOMENTUM, the Newton-Schulz backward of
 // gW' for MUON_MOMENTUM).  Out: gM <- bbar gMt (cotangent of the old M),
 // gU = -gMt, and per-block partial sums of gMt . M_old for d(bbar).
-// Grid: (nblk, n); block b of instance i covers a slice of its 3 matrices.
-__global__ __launch_bounds__(NT) void bwd_mom_kernel(MatP gM, MatC gX, MatC Mold, const float* bbar, MatP gU,
-                                                     float* part, int64_t DD, int nblk) {
+// bbar = the mean of beta over the chunk's rows [t0, t0 + C), summed by each
+// workgroup itself (C values from L2).  Grid: (nblk, 3 matrices, n).
+__global__ __launch_bounds__(NT) void bwd_mom_kernel(MatP gM, MatC gX, MatC Mold, const float* beta, int64_t beta_bs,
+                                                     int64_t t0, int64_t C, MatP gU, float* part, int64_t DD,
+                                                     int nblk) {
   __shared__ float red[NT / WAVE];
-  const int i = blockIdx.y, b = blockIdx.x;
-  const int64_t tot = 3 * DD;
-  const int64_t per = (tot + nblk - 1) / nblk;
-  const int64_t e0 = (int64_t)b * per, e1 = min(tot, e0 + per);
-  const float bb = bbar[i];
+  __shared__ float s_bb;
+  const int b = blockIdx.x, mat = blockIdx.y, i = blockIdx.z;
+  {
+    float sb = 0.f;
+    for (int64_t t = threadIdx.x; t < C; t += NT) sb += beta[i * beta_bs + t0 + t];
+    sb = wave_sum(sb);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float tb = 0.f;
+      for (int w = 0; w < NT / WAVE; ++w) tb += red[w];
+      s_bb = tb / (float)C;
+    }
+    __syncthreads();
+  }
+  const float bb = s_bb;
+  const int64_t per = (DD + nblk - 1) / nblk;
+  const int64_t e0 = (int64_t)b * per, e1 = min(DD, e0 + per);
+  float* gm = gM.p[mat] + (int64_t)i * DD;
+  const float* gx = gX.p[mat] + (int64_t)i * DD;
+  const float* mo = Mold.p[mat] + (int64_t)i * DD;
+  float* gu = gU.p[mat] + (int64_t)i * DD;
   float s = 0.f;
   for (int64_t e = e0 + threadIdx.x; e < e1; e += NT) {
-    const int mat = (int)(e / DD);
-    const int64_t o = (int64_t)i * DD + e % DD;
-    const float gmt = gM.p[mat][o] - gX.p[mat][o];
-    s += gmt * Mold.p[mat][o];
-    gM.p[mat][o] = bb * gmt;
-    gU.p[mat][o] = -gmt;
+    const float gmt = gm[e] - gx[e];
+    s += gmt * mo[e];
+    gm[e] = bb * gmt;
+    gu[e] = -gmt;
   }
   s = wave_sum(s);
+  __syncthreads();   // red[] is reused
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
     float t = 0.f;
     for (int w = 0; w < NT / WAVE; ++w) t += red[w];
-    part[(int64_t)i * nblk + b] = t;
+    part[((int64_t)i * 3 + mat) * nblk + b] = t;
   }
 }
 
-// dbeta[t] = d(bbar) / C for the chunk's rows (bbar is the chunk mean)
+// dbeta[t] = d(bbar) / C for the chunk's rows (bbar is the chunk mean);
+// part holds 3 nblk partial sums per instance
 __global__ __launch_bounds__(NT) void bwd_mom_finish_kernel(const float* part, int nblk, float* dbeta, int64_t beta_bs,
                                                             int64_t t0, int64_t C) {
   __shared__ float s_g;
   const int i = blockIdx.y;
   if (threadIdx.x == 0) {
     float g = 0.f;
-    for (int b = 0; b < nblk; ++b) g += part[(int64_t)i * nblk + b];
+    for (int b = 0; b < 3 * nblk; ++b) g += part[(int64_t)i * 3 * nblk + b];
     s_g = g / (float)C;
   }
   __syncthreads();

@@ -173,7 +173,7 @@ lact_status bgemm_ns(BOp A, BOp B, float* C, int64_t ldc, int64_t c_bs, int M, i
   } while (0)
 
 constexpr int BWD_NB = 32;    // partial sums per matrix (Newton-Schulz reductions)
-constexpr int BWD_NBM = 64;   // partial sums per instance (momentum)
+constexpr int BWD_NBM = 64;   // partial sums per (instance, matrix) (momentum)
 
 // ----------------------------------------------------------------- layout
 struct BwdWs {
@@ -184,18 +184,20 @@ struct BwdWs {
   size_t tok[9] = {};         // [n, cmax, dh] fp32 token buffers
   size_t U = 0, step = 0, gWp = 0, gU = 0, gM = 0, gX = 0;
   size_t X = 0, Am = 0, Pm = 0, gP = 0, gA = 0, Qm = 0, g0 = 0, g1 = 0, nrm = 0, part = 0;
-  size_t bbar = 0, mpart = 0;
+  size_t mpart = 0;
   size_t spl = 0, spl_floats = 0;   // split-K partials of the token contractions
   size_t qf = 0, kf = 0, vf = 0;     // LACT_QK_PREP: fp32 q^, k^ and v [n, L, d]
   size_t total = 0;
 };
 
-// The replay of the forward state trajectory: fp32-grade recurrence; with
-// raw q / k it runs on the backward's own fp32 pre-processed copies (not
-// rounded to the io dtype), so its io type is fp32.
+// The replay of the forward state trajectory: with bf16 inputs, two bf16
+// planes per fp32 weight operand for GD and momentum, three (fp32 grade) for
+// the Newton-Schulz optimisers; fp32 inputs always take three.  With raw
+// q / k it runs on the backward's own fp32 pre-processed copies (not rounded
+// to the io dtype), so its io type is fp32.
 lact_problem replay_problem(const lact_problem& p) {
   lact_problem f = p;
-  f.rec_planes = 3;
+  f.rec_planes = uses_ns(p.opt) ? 3 : 2;
   if (p.flags & LACT_QK_PREP) f.io_dtype = LACT_DTYPE_F32;
   f.flags &= LACT_NO_RENORM;
   return f;
@@ -255,8 +257,7 @@ BwdWs bwd_layout(const lact_problem& p, const std::vector<int64_t>& b, const std
     w.nrm = take(3 * n * 4);
     w.part = take(3 * n * BWD_NB * 4);
   }
-  w.bbar = take(n * 4);
-  w.mpart = take(n * BWD_NBM * 4);
+  w.mpart = take(n * 3 * BWD_NBM * 4);
   {
     // the token contractions: pairs of [dh, d] outputs, single [d, dh] ones
     const int64_t tb = (int64_t)((Dh + 63) / 64) * ((D + 63) / 64) * (int64_t)n;
@@ -586,9 +587,8 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
         if ((q = ns_backward(Mn, cset(GWP), GU))) return q;
         gX = cset(GU);   // consumed below before GU is overwritten element by element
       }
-      BWD_LAUNCH(bwd_beta_mean_kernel, dim3(n), P.beta, L, t0, C, fp(w.bbar));
-      BWD_LAUNCH(bwd_mom_kernel, dim3(BWD_NBM, n), GM, gX, cset(slotM(u)), (const float*)fp(w.bbar), GU,
-                 fp(w.mpart), DD, BWD_NBM);
+      BWD_LAUNCH(bwd_mom_kernel, dim3(BWD_NBM, 3, n), GM, gX, cset(slotM(u)), P.beta, L, t0, C, GU, fp(w.mpart),
+                 DD, BWD_NBM);
       BWD_LAUNCH(bwd_mom_finish_kernel, dim3((unsigned)std::min<int64_t>((C + NT - 1) / NT, 64), n),
                  (const float*)fp(w.mpart), BWD_NBM, P.dbeta, L, t0, C);
     }

@@ -229,3 +229,52 @@ def test_backward_single_token_chunk(lact):
     wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=257, chunk=256))
     errs = run_case(lact, wl, seed=10)
     assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("opt", [W.OPT_MOMENTUM, W.OPT_MUON])
+def test_backward_replays_in_a_hip_graph(lact, opt):
+    """The backward only enqueues kernels and device-to-device copies on the
+    caller's stream (no allocation, memset or host synchronisation), so a HIP
+    graph can capture it; every replay, with eager work and synchronisations
+    between replays, equals the eager call bitwise and rewrites every
+    output."""
+    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=2 * 256 + 40, chunk=256), opt=opt)
+    inp = W.generate(wl, seed=23)
+    dO, gW, gM = cotangents(wl, 23, True)
+    dev = lambda x: to_dev(x, torch)
+    mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    Ws = [dev(inp.W1), dev(inp.W2), dev(inp.W3)]
+    Ms = [torch.zeros_like(w) for w in Ws] if mom else [None] * 3
+    kw = dict(dO=dev(dO), gW=[dev(g) for g in gW], gM=[dev(g) for g in gM], order=wl.order, opt=wl.opt,
+              bounds=list(wl.bounds), flags=list(wl.flags))
+    q, k, v, lr = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.lr)
+    beta = dev(inp.beta) if mom else None
+    ref = lact.layer_backward(q, k, v, lr, beta, *Ws, *Ms, **kw)
+    p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, 3)
+    ws = torch.empty(lact.backward_workspace_size(p, wl.L, 0, wl.order, list(wl.bounds), list(wl.flags)),
+                     dtype=torch.uint8, device="cuda")
+    out = {key: (None if t is None else torch.empty_like(t)) for key, t in ref.items()}
+
+    def call():
+        lact.layer_backward(q, k, v, lr, beta, *Ws, *Ms, out=out, workspace=ws, **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                        # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        for t in out.values():
+            if t is not None:
+                t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for key, t in out.items():
+            if t is not None:
+                assert torch.equal(t, ref[key]), (rep, key)
+        _ = float(out["dq"].sum())    # eager work between replays
+    log(f"  opt={opt}: 3 graph replays of the backward equal the eager call")

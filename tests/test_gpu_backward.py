@@ -278,3 +278,25 @@ def test_backward_replays_in_a_hip_graph(lact, opt):
                 assert torch.equal(t, ref[key]), (rep, key)
         _ = float(out["dq"].sum())    # eager work between replays
     log(f"  opt={opt}: 3 graph replays of the backward equal the eager call")
+
+
+@pytest.mark.parametrize("name", ["bf16_momentum", "bf16_muon_momentum", "raw_qk_scaled", "viewset"])
+def test_backward_is_deterministic(lact, name):
+    """Two backward calls on the same inputs give bitwise-identical
+    gradients (split-K partials and every reduction summed in fixed order)."""
+    wl = CASES[name]
+    inp = W.generate(wl, seed=12)
+    dO, gW, gM = cotangents(wl, 12, True)
+    dev = lambda x: to_dev(x, torch)
+    mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    Ws = [dev(inp.W1), dev(inp.W2), dev(inp.W3)]
+    Ms = [torch.zeros_like(w) for w in Ws] if mom else [None] * 3
+    call = lambda: lact.layer_backward(
+        dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.lr), dev(inp.beta) if mom else None, *Ws, *Ms, dO=dev(dO),
+        gW=[dev(g) for g in gW], gM=[dev(g) for g in gM], order=wl.order, opt=wl.opt, bounds=list(wl.bounds),
+        flags=list(wl.flags), qk_prep=wl.layer_qk_prep, oz=dev(inp.oz) if wl.out_scale else None)
+    a, b = call(), call()
+    torch.cuda.synchronize()
+    for key, t in a.items():
+        if t is not None:
+            assert torch.equal(t, b[key]), key

@@ -6,8 +6,11 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <dlfcn.h>
+
 #include <algorithm>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -101,6 +104,49 @@ struct KernelTimer {
       hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);                   \
     }                                                                                    \
   } while (0)
+
+// --------------------------------------------------------------- host trace ranges
+// With LACT_TRACE=1 in the environment the library marks its host-side
+// phases (each update chunk, the batched applies, the backward's replay and
+// reverse chunks) as roctx ranges, which `rocprofv3 --marker-trace` records
+// next to the kernels those phases enqueue.  The roctx library is opened on
+// first use; without it (or without the variable) tracing is off and costs a
+// pointer test.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+const Roctx& roctx() {
+  static const Roctx r = [] {
+    Roctx x;
+    const char* e = getenv("LACT_TRACE");
+    if (!e || strcmp(e, "1") != 0) return x;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) return x;
+    x.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    x.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (!x.push || !x.pop) x.push = nullptr, x.pop = nullptr;
+    return x;
+  }();
+  return r;
+}
+struct TraceRange {
+  bool on;
+  explicit TraceRange(const char* fmt, ...) : on(roctx().push != nullptr) {
+    if (!on) return;
+    char buf[128];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    roctx().push(buf);
+  }
+  ~TraceRange() {
+    if (on) roctx().pop();
+  }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
 
 // --------------------------------------------------------------- device check
 lact_status check_device() {
@@ -645,6 +691,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
   for (const Step& st : plan.steps) {
     if (st.upd_len == 0) continue;
     const int64_t C = st.upd_len;
+    TraceRange tr("lact update %d: tokens %lld..%lld", nu, (long long)st.upd_t0, (long long)(st.upd_t0 + C));
     // forward products on k, v and the SwiGLU backward terms
     UpdFwdArgs ua;
     memset(&ua, 0, sizeof(ua));
@@ -975,6 +1022,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
   }
 
   // ---------------------------------------------------------------- apply (all chunks)
+  TraceRange tr_apply("lact apply (all chunks)");
   std::vector<AppGroup> groups;
   {
     int u = 0;

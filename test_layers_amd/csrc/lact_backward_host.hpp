@@ -367,6 +367,7 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
 
   // ---- replay of the forward state trajectory: slot u = state before update u
   {
+    TraceRange tr("lact backward: replay of %d updates", w.nu);
     const MatP s0 = slotW(0);
     for (int j = 0; j < 3; ++j)
       HIP_TRY(hipMemcpyAsync(s0.p[j], P.W[j], (size_t)n * DD * 4, hipMemcpyDeviceToDevice, s));
@@ -642,6 +643,7 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   for (int c = (int)f.size() - 1; c >= 0; --c) {
     const int64_t t0 = b[c], C = b[c + 1] - b[c];
     const bool U_ = f[c] & LACT_CHUNK_UPDATE, A_ = f[c] & LACT_CHUNK_APPLY;
+    TraceRange tr("lact backward chunk %d: tokens %lld..%lld", c, (long long)t0, (long long)(t0 + C));
     // slot u: the state before this chunk (after its update: slot u + 1)
     if (U_) --u;
     if (A_ && U_ && order == LACT_UPDATE_THEN_APPLY)

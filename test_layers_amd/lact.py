@@ -218,6 +218,18 @@ def _ptr(t, dtype=None, name="tensor"):
     return t.data_ptr()
 
 
+def _check_shapes(**named):
+    """Every given tensor must have exactly the expected shape: the library
+    receives raw pointers and cannot detect a mis-sized buffer itself."""
+    for name, (t, shape) in named.items():
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _w_shapes(n, D, Dh):
+    return (n, Dh, D), (n, D, Dh), (n, Dh, D)
+
+
 def _io_dtype(t):
     torch = _torch()
     if t.dtype == torch.float32:
@@ -256,9 +268,16 @@ def layer_forward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, o=No
     [n, L, D] (allocated with torch.zeros if not given; rows of non-APPLY
     chunks keep their values)."""
     torch = _torch()
+    if q.dim() != 3 or W1.dim() != 3:
+        raise ValueError("q must be [n, L, d] and W1 [n, dh, d]")
     n, L, D = q.shape
+    Dh = W1.shape[1]
+    s1, s2, s3 = _w_shapes(n, D, Dh)
+    _check_shapes(k=(k, (n, L, D)), v=(v, (n, L, D)), lr=(lr, (n, L, 3)), beta=(beta, (n, L)), W1=(W1, s1),
+                  W2=(W2, s2), W3=(W3, s3), M1=(M1, s1), M2=(M2, s2), M3=(M3, s3), o=(o, (n, L, D)),
+                  oz=(oz, (n, L)))
     io = _io_dtype(q)
-    p = problem(n, D, io, opt, rec_planes, ns_iters, renorm, dh=W1.shape[1], qk_prep=qk_prep)
+    p = problem(n, D, io, opt, rec_planes, ns_iters, renorm, dh=Dh, qk_prep=qk_prep)
     if o is None:
         o = torch.zeros_like(q)
     need = workspace_size(p, L, chunk, order, bounds, flags)
@@ -282,7 +301,12 @@ def chunk_update(k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, Lc: O
                  opt: int = OPT_GD, rec_planes: int = 0, ns_iters: int = 5, renorm: bool = True,
                  qk_prep: bool = False, workspace=None, stream=None):
     torch = _torch()
+    if k.dim() != 3 or W1.dim() != 3:
+        raise ValueError("k must be [n, S, d] and W1 [n, dh, d]")
     n, S, D = k.shape
+    s1, s2, s3 = _w_shapes(n, D, W1.shape[1])
+    _check_shapes(v=(v, (n, S, D)), lr=(lr, (n, S, 3)), beta=(beta, (n, S)), W2=(W2, s2), W3=(W3, s3),
+                  M1=(M1, s1), M2=(M2, s2), M3=(M3, s3))
     Lc = S if Lc is None else Lc
     p = problem(n, D, _io_dtype(k), opt, rec_planes, ns_iters, renorm, dh=W1.shape[1], qk_prep=qk_prep)
     ws = _workspace(workspace_size(p, Lc, max(Lc, 1)), workspace, k.device)
@@ -296,7 +320,11 @@ def chunk_update(k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, Lc: O
 def apply(q, W1, W2, W3, o=None, *, Lq: Optional[int] = None, qk_prep: bool = False,
           workspace=None, stream=None):
     torch = _torch()
+    if q.dim() != 3 or W1.dim() != 3:
+        raise ValueError("q must be [n, S, d] and W1 [n, dh, d]")
     n, S, D = q.shape
+    s1, s2, s3 = _w_shapes(n, D, W1.shape[1])
+    _check_shapes(W2=(W2, s2), W3=(W3, s3), o=(o, (n, S, D)))
     Lq = S if Lq is None else Lq
     p = problem(n, D, _io_dtype(q), OPT_GD, dh=W1.shape[1], qk_prep=qk_prep)
     if o is None:
@@ -323,9 +351,24 @@ def layer_backward(q, k, v, lr, beta, W1, W2, W3, M1=None, M2=None, M3=None, *, 
     dict from an earlier call with the same shapes) is filled instead of
     allocating."""
     torch = _torch()
+    if q.dim() != 3 or W1.dim() != 3:
+        raise ValueError("q must be [n, L, d] and W1 [n, dh, d]")
     n, L, D = q.shape
+    Dh = W1.shape[1]
+    ws_ = _w_shapes(n, D, Dh)
+    _check_shapes(k=(k, (n, L, D)), v=(v, (n, L, D)), lr=(lr, (n, L, 3)), beta=(beta, (n, L)), W2=(W2, ws_[1]),
+                  W3=(W3, ws_[2]), M1=(M1, ws_[0]), M2=(M2, ws_[1]), M3=(M3, ws_[2]), dO=(dO, (n, L, D)),
+                  oz=(oz, (n, L)))
+    for name, gs in (("gW", gW), ("gM", gM)):
+        for j, g in enumerate(gs or ()):
+            _check_shapes(**{f"{name}{j + 1}": (g, ws_[j])})
+    if out is not None:
+        expect = {"dq": (n, L, D), "dk": (n, L, D), "dv": (n, L, D), "dlr": (n, L, 3), "dbeta": (n, L),
+                  "doz": (n, L), "dW1": ws_[0], "dW2": ws_[1], "dW3": ws_[2], "dM1": ws_[0], "dM2": ws_[1],
+                  "dM3": ws_[2]}
+        _check_shapes(**{f"out[{key}]": (out.get(key), shape) for key, shape in expect.items()})
     io = _io_dtype(q)
-    p = problem(n, D, io, opt, 3, ns_iters, renorm, dh=W1.shape[1], qk_prep=qk_prep)
+    p = problem(n, D, io, opt, 3, ns_iters, renorm, dh=Dh, qk_prep=qk_prep)
     mom = opt in (OPT_MOMENTUM, OPT_MUON_MOMENTUM)
     f32 = torch.float32
     if out is None:

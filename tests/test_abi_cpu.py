@@ -310,3 +310,24 @@ def test_backward_workspace():
     assert lact.backward_workspace_size(p, 1024, 128) > lact.backward_workspace_size(p, 512, 128)
     with pytest.raises(lact.LactError):
         lact.backward_workspace_size(P(d=96), 512, 128)
+
+
+def test_binding_rejects_mis_shaped_tensors():
+    """The binding checks every tensor's shape before any library call (the
+    library sees raw pointers only)."""
+    torch = pytest.importorskip("torch")
+    n, L, D = 2, 64, 128
+    q = torch.zeros(n, L, D)
+    W = [torch.zeros(n, D, D) for _ in range(3)]
+    with pytest.raises(ValueError, match="lr has shape"):
+        lact.layer_forward(q, q, q, torch.zeros(n, L, 2), None, *W)
+    with pytest.raises(ValueError, match="W2 has shape"):
+        lact.layer_forward(q, q, q, torch.zeros(n, L, 3), None, W[0], torch.zeros(n, D, 64), W[2])
+    with pytest.raises(ValueError, match="dO has shape"):
+        lact.layer_backward(q, q, q, torch.zeros(n, L, 3), None, *W, dO=torch.zeros(n, L - 1, D))
+    with pytest.raises(ValueError, match=r"out\[dq\] has shape"):
+        lact.layer_backward(q, q, q, torch.zeros(n, L, 3), None, *W, dO=q, out={"dq": torch.zeros(1)})
+    with pytest.raises(ValueError, match="v has shape"):
+        lact.chunk_update(q, torch.zeros(n, L + 1, D), torch.zeros(n, L, 3), None, *W)
+    with pytest.raises(ValueError, match="o has shape"):
+        lact.apply(q, *W, o=torch.zeros(n, L, 64))

@@ -303,6 +303,11 @@ def main():
     if "apply_out" not in per:
         # the fused apply kernel also runs the output product
         kf[lact.K_APP] += kf[lact.K_OUT]
+    elif "apply_fwd" not in per:
+        # every apply-then-update chunk's query products ran in its update
+        # forward tile (plain bf16, the same snapshot); the workloads here
+        # fuse all of their applies or none
+        kf[lact.K_UPD] += kf[lact.K_APP]
     if "dw" not in per:
         # the fused update kernel also runs the weight-gradient contraction
         kf[lact.K_UPD] += kf[lact.K_DW]

@@ -16,6 +16,7 @@
 #include <mutex>
 #include <string>
 #include <type_traits>
+#include <type_traits>
 #include <vector>
 
 #include "lact.h"
@@ -583,7 +584,10 @@ constexpr bool direct_fits(int bytes) { return bytes + 1024 <= LDS_MAX; }
 template <typename PT, int BJ>
 lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
   if constexpr (PT::UPD_FROM_SNAP && (BJ == 64 || BJ == 96)) {
-    LACT_LAUNCH((dupd_fwd_kernel<BJ, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
+    // with the chunk's queries the ring holds a third token tile: 32-wide
+    // stages, three deep, fit the LDS
+    if (ua.q != nullptr) LACT_LAUNCH((dupd_fwd_kernel<BJ, 32, 3, true>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
+    else LACT_LAUNCH((dupd_fwd_kernel<BJ, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
     HIP_TRY(hipGetLastError());
     return LACT_OK;
   }
@@ -686,9 +690,42 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     HIP_TRY(hipGetLastError());
   }
 
+  // Apply groups, one per step with queries, in step order: group i reads
+  // the snapshot taken before its step's update.  When a step's queries are
+  // the same tokens as its update (an apply-then-update chunk), the plain
+  // bf16 update forward tile also computes their gated hidden (it holds the
+  // same W1, W3 fragments); the apply then runs only the output product for
+  // that group.
+  std::vector<AppGroup> groups;
+  std::vector<char> hq_done;
+  std::vector<int> step_group(plan.steps.size(), -1);
+  {
+    int u = 0;
+    int64_t h0 = 0;
+    for (size_t si = 0; si < plan.steps.size(); ++si) {
+      const Step& st = plan.steps[si];
+      if (st.app_len > 0) {
+        AppGroup ag;
+        memset(&ag, 0, sizeof(ag));
+        ag.t0 = st.app_t0;
+        ag.len = st.app_len;
+        ag.h0 = h0;
+        ag.W1 = slot(u, 0);
+        ag.W3 = slot(u, 2);
+        ag.W2 = slot(u, 1);
+        step_group[si] = (int)groups.size();
+        groups.push_back(ag);
+        hq_done.push_back(0);
+        h0 += st.app_len;
+      }
+      if (st.upd_len > 0) ++u;
+    }
+  }
+
   // ---------------------------------------------------------------- recurrence
   int nu = 0;   // updates done so far
-  for (const Step& st : plan.steps) {
+  for (size_t si = 0; si < plan.steps.size(); ++si) {
+    const Step& st = plan.steps[si];
     if (st.upd_len == 0) continue;
     const int64_t C = st.upd_len;
     TraceRange tr("lact update %d: tokens %lld..%lld", nu, (long long)st.upd_t0, (long long)(st.upd_t0 + C));
@@ -744,6 +781,16 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       }
     } else {
       const int bj = upd_bj(p, C);
+      const int gi = step_group[si];
+      if (std::is_same<PT, ProfBF16>::value && !fused_apply(p) && (bj == 64 || bj == 96) && gi >= 0 &&
+          st.app_t0 == st.upd_t0 && st.app_len == C) {
+        ua.q = qx;
+        ua.q_bs = q_bs;
+        ua.H = ws + w.h;
+        ua.h_bs = w.h_rows * Dh;
+        ua.h0 = groups[gi].h0;
+        hq_done[gi] = 1;
+      }
       const int64_t grid = (int64_t)n * ua.tiles_t * (Dh / bj);
       if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
       KernelTimer kt(LACT_K_UPD, s);
@@ -1023,26 +1070,6 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
 
   // ---------------------------------------------------------------- apply (all chunks)
   TraceRange tr_apply("lact apply (all chunks)");
-  std::vector<AppGroup> groups;
-  {
-    int u = 0;
-    int64_t h0 = 0;
-    for (const Step& st : plan.steps) {
-      if (st.app_len > 0) {
-        AppGroup ag;
-        memset(&ag, 0, sizeof(ag));
-        ag.t0 = st.app_t0;
-        ag.len = st.app_len;
-        ag.h0 = h0;
-        ag.W1 = slot(u, 0);
-        ag.W3 = slot(u, 2);
-        ag.W2 = slot(u, 1);
-        groups.push_back(ag);
-        h0 += st.app_len;
-      }
-      if (st.upd_len > 0) ++u;
-    }
-  }
   if (fused_apply(p)) {
     for (size_t g0 = 0; g0 < groups.size(); g0 += MAXG) {
       const int ng = (int)std::min<size_t>(MAXG, groups.size() - g0);
@@ -1092,7 +1119,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     // workgroups per group: token tiles x column blocks (cols wide) x instances
     auto set_tiles = [&](int cols, int64_t& grid) -> lact_status {
       grid = 0;
-      for (int i = 0; i < ng; ++i) {
+      for (int i = 0; i < aa.ngroups; ++i) {
         const int64_t t = ((aa.g[i].len + FBT - 1) / FBT) * (cols / abj) * n;
         if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
         aa.g[i].tiles = (int)t;
@@ -1101,14 +1128,21 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
       return LACT_OK;
     };
-    for (int i = 0; i < ng; ++i) aa.g[i] = groups[g0 + i];
+    // gated hidden of the batch's groups not done by their update tile
+    int nf = 0;
+    for (int i = 0; i < ng; ++i)
+      if (!hq_done[g0 + i]) aa.g[nf++] = groups[g0 + i];
+    aa.ngroups = nf;
     int64_t grid = 0;
-    if (lact_status r = set_tiles(Dh, grid)) return r;
-    {
+    if (nf > 0) {
+      if (lact_status r = set_tiles(Dh, grid)) return r;
       KernelTimer kt(LACT_K_APP, s);
       lact_status r = abj == 128 ? launch_app_fwd<PT, 128>(aa, grid, s) : launch_app_fwd<PT, 64>(aa, grid, s);
       if (r) return r;
     }
+    // output product over every group of the batch
+    aa.ngroups = ng;
+    for (int i = 0; i < ng; ++i) aa.g[i] = groups[g0 + i];
     // o[t, r] = sum_j Hq[t, j] W2[r, j]: the apply tile in output mode
     // (d column blocks), or the generic GEMM for profiles without a bf16 path
     {

@@ -437,15 +437,22 @@ constexpr int upd_w_waves(int bj, int bkk) {
 // (BJ / 2)(w & 1) .. +BJ/2-1 of the 128 x BJ tile (two waves per SIMD keep
 // the MFMA pipes fed).  K and V tiles are loaded by all eight waves, the W
 // tiles by the first upd_w_waves; each wave waits on its own load count.
-template <int BJ, int BKK, int NST>
+// WQ: the same tokens' queries are applied on the same snapshot (an
+// apply-then-update chunk): a third token tile q shares the W1 and W3
+// fragments, and the tile also writes its gated hidden
+// Hq = silu(q W1^T) * (q W3^T) to rows h0 + (t - upd_t0) of the Hq buffer
+// (swapped MFMA operands: each lane holds 4 consecutive hidden units of one
+// token, stored as 8 bytes straight from registers).
+template <int BJ, int BKK, int NST, bool WQ = false>
 __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   constexpr int NWV = DG_THREADS / WAVE;
   constexpr int WW = upd_w_waves(BJ, BKK);
-  using TX = DTile<FBT, BKK, NWV>;   // K, V: 128 tokens x BKK
+  constexpr int NX = WQ ? 3 : 2;     // token tiles per stage: k, v (, q)
+  using TX = DTile<FBT, BKK, NWV>;   // K, V (, Q): 128 tokens x BKK
   using TW = DTile<BJ, BKK, WW>;     // W1, W3, W2^T rows: BJ x BKK
-  constexpr int STAGE = 2 * TX::BYTES + 3 * TW::BYTES;
-  constexpr int LPS = 2 * TX::INSTR + 3 * TW::INSTR;   // loads per stage of a W-loading wave
-  constexpr int LPS_X = 2 * TX::INSTR;                 // ... of the other waves
+  constexpr int STAGE = NX * TX::BYTES + 3 * TW::BYTES;
+  constexpr int LPS = NX * TX::INSTR + 3 * TW::INSTR;   // loads per stage of a W-loading wave
+  constexpr int LPS_X = NX * TX::INSTR;                 // ... of the other waves
   constexpr int FM = 2, FN = BJ / 32;
   constexpr int ET_BYTES = 3 * BJ * FBT * 2;   // update terms of the tile, staged for full-line stores
   static_assert(ET_BYTES <= NST * STAGE, "staging fits the ring");
@@ -471,6 +478,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   const bf16_t* W1 = reinterpret_cast<const bf16_t*>(a.W1) + inst * DD;
   const bf16_t* W3 = reinterpret_cast<const bf16_t*>(a.W3) + inst * DD;
   const bf16_t* W2T = reinterpret_cast<const bf16_t*>(a.W2x) + inst * DD;
+  const bf16_t* Q = WQ ? reinterpret_cast<const bf16_t*>(a.q) + inst * a.q_bs : K;
 
   // the tile's learning rates and momentum coefficients, held in registers
   // through the main loop (used by the epilogue)
@@ -484,6 +492,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   const bool wload = wave < WW;
   const typename TX::Plan pk = TX::plan(K, D, t0, tend - 1, 0, wave, lane);
   const typename TX::Plan pv = TX::plan(V, D, t0, tend - 1, 0, wave, lane);
+  const typename TX::Plan pq = TX::plan(Q, D, t0, tend - 1, 0, wave, lane);
   // W1, W3 and W2^T rows: hidden units j0 .. j0 + BJ - 1 (of dh), d long
   const typename TW::Plan p1 = TW::plan(W1, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
   const typename TW::Plan p3 = TW::plan(W3, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
@@ -491,30 +500,34 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   auto issue_one = [&](int s, int buf, int idx) {
     char* st = smem + buf * STAGE;
     const int64_t off = (int64_t)s * BKK * 2;
-    char* w = st + 2 * TX::BYTES;
+    char* w = st + NX * TX::BYTES;
+    // token tiles first (every wave issues them), then the W tiles
     if (idx < TX::INSTR) TX::issue_one(st, pk, off, wave, idx);
     else if (idx < 2 * TX::INSTR) TX::issue_one(st + TX::BYTES, pv, off, wave, idx - TX::INSTR);
+    else if (WQ && idx < 3 * TX::INSTR) TX::issue_one(st + 2 * TX::BYTES, pq, off, wave, idx - 2 * TX::INSTR);
     else if (!wload) return;
-    else if (idx < 2 * TX::INSTR + TW::INSTR) TW::issue_one(w, p1, off, wave, idx - 2 * TX::INSTR);
-    else if (idx < 2 * TX::INSTR + 2 * TW::INSTR) TW::issue_one(w + TW::BYTES, p3, off, wave, idx - 2 * TX::INSTR - TW::INSTR);
-    else TW::issue_one(w + 2 * TW::BYTES, p2, off, wave, idx - 2 * TX::INSTR - 2 * TW::INSTR);
+    else if (idx < NX * TX::INSTR + TW::INSTR) TW::issue_one(w, p1, off, wave, idx - NX * TX::INSTR);
+    else if (idx < NX * TX::INSTR + 2 * TW::INSTR) TW::issue_one(w + TW::BYTES, p3, off, wave, idx - NX * TX::INSTR - TW::INSTR);
+    else TW::issue_one(w + 2 * TW::BYTES, p2, off, wave, idx - NX * TX::INSTR - 2 * TW::INSTR);
   };
-  f32x4 accA[FM][FN], accB[FM][FN], accG[FM][FN];
+  f32x4 accA[FM][FN], accB[FM][FN], accG[FM][FN], accQ1[FM][FN], accQ3[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) accA[i][j] = accB[i][j] = accG[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j)
+      accA[i][j] = accB[i][j] = accG[i][j] = accQ1[i][j] = accQ3[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf, auto&& hook) {
     const char* st = smem + buf * STAGE;
-    const char* w = st + 2 * TX::BYTES;
+    const char* w = st + NX * TX::BYTES;
     constexpr int NSLOT = (BKK / 32) * FM;
 #pragma unroll
     for (int kk = 0; kk < BKK; kk += 32) {
-      bf16x8 fk[FM], fv[FM], f1[FN], f3[FN], f2[FN];
+      bf16x8 fk[FM], fv[FM], fq[FM], f1[FN], f3[FN], f2[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         fk[i] = dfrag_row<TX>(st, wm * 32 + i * 16, kk, lane);
         fv[i] = dfrag_row<TX>(st + TX::BYTES, wm * 32 + i * 16, kk, lane);
+        if constexpr (WQ) fq[i] = dfrag_row<TX>(st + 2 * TX::BYTES, wm * 32 + i * 16, kk, lane);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -529,12 +542,39 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
           accA[i][j] = mfma(fk[i], f1[j], accA[i][j]);
           accB[i][j] = mfma(fk[i], f3[j], accB[i][j]);
           accG[i][j] = mfma(fv[i], f2[j], accG[i][j]);
+          if constexpr (WQ) {
+            accQ1[i][j] = mfma(f1[j], fq[i], accQ1[i][j]);
+            accQ3[i][j] = mfma(f3[j], fq[i], accQ3[i][j]);
+          }
         }
         hook((kk / 32) * FM + i, NSLOT);
       }
     }
   };
   dpipeline_il2<NST, LPS, LPS_X>(D / BKK, wload, issue_one, compute);
+
+  if constexpr (WQ) {
+    // Hq rows of the tile's tokens inside the chunk (bf16, as the apply
+    // stores them); lane: token lane & 15 of the fragment, hidden units
+    // 4 (lane >> 4) .. +3
+    bf16_t* H = reinterpret_cast<bf16_t*>(a.H) + inst * a.h_bs + j0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t t = t0 + wm * 32 + i * 16 + (lane & 15);
+      if (t >= tend) continue;
+      bf16_t* Hr = H + (a.h0 + (t - a.upd_t0)) * (int64_t)Dh;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        float h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = accQ1[i][j][r];
+          h[r] = x * fast_sigmoid(x) * accQ3[i][j][r];
+        }
+        store4(Hr + wn * (BJ / 2) + j * 16 + 4 * (lane >> 4), h);
+      }
+    }
+  }
 
   // Epilogue: SwiGLU backward terms into an LDS copy of the tile's E rows
   // (row = term x hidden column, 128 tokens = 256 bytes, 16-byte chunks

@@ -54,6 +54,13 @@ struct UpdFwdArgs {
   int64_t upd_t0;
   int64_t upd_len;
   int tiles_t;           // token blocks per instance
+  // bf16 tile only: the same tokens' queries, applied on the same snapshot
+  // (null: none); Hq rows go to H + inst * h_bs, row h0 + (t - upd_t0)
+  const void* q;
+  int64_t q_bs;
+  void* H;
+  int64_t h_bs;
+  int64_t h0;
 };
 
 constexpr int FBT = 128;  // tokens per forward tile

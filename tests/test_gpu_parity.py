@@ -165,6 +165,24 @@ def test_layer_orders_and_no_renorm(lact, order):
         assert max(errs.values()) <= wl.tol, errs
 
 
+@pytest.mark.parametrize("order", [W.APPLY_THEN_UPDATE, W.UPDATE_THEN_APPLY])
+def test_layer_mixed_schedule_plain_bf16(lact, order):
+    """Plain bf16 at d = 384 on a schedule that mixes update+apply chunks
+    (apply-then-update: their queries run in the update forward tile) with an
+    apply-only chunk that merges into the next step's apply range, an
+    update-only chunk and a ragged last update+apply chunk (333 tokens)."""
+    import dataclasses
+    b = (0, 512, 700, 1212, 1724, 2057)
+    f = (W.UPDATE | W.APPLY, W.APPLY, W.UPDATE | W.APPLY, W.UPDATE, W.UPDATE | W.APPLY)
+    wl = dataclasses.replace(W.CONFIGS[2], n_inst=2, L=b[-1], bounds=b, flags=f)
+    inp = W.generate(wl, seed=5)
+    log(f"mixed schedule order={order}: bounds={b}")
+    gpu = run_gpu(wl, inp, torch, lact, order=order)
+    errs = compare(wl, inp, gpu, order=order)
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= wl.tol, errs
+
+
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, "fused_update"])
 def test_layer_is_deterministic(lact, cid):
     """Every workload (reduced) run twice gives bitwise-identical outputs and

@@ -101,6 +101,28 @@ def backward_kernel_flops(wl, lact):
     return f
 
 
+def host_info():
+    """The host the oracle is timed on: CPU model, logical CPUs, the CPUs this
+    process may run on, and the BLAS library numpy's threads come from."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": d.get("internal_api"), "threads": d.get("num_threads")} for d in threadpool_info()]
+    except Exception:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas": blas}
+
+
 def cpu_baseline_backward(wl, inp, dO, budget):
     """The backward oracle as it stands, on a bounded sample (whole instances
     over the whole sequence until about `budget` seconds of work)."""
@@ -124,7 +146,7 @@ def cpu_baseline_backward(wl, inp, dO, budget):
     tokens = wl.tokens * done / wl.n_inst
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} instance backward passes (heads, cycling over the {wl.n_inst} of the workload), "
-                      f"whole {wl.L}-token sequence each, {dt:.1f} s, numpy fp64"}
+                      f"whole {wl.L}-token sequence each, {dt:.1f} s, numpy fp64", "host": host_info()}
 
 
 def opt_bytes(wl, S):
@@ -159,7 +181,7 @@ def cpu_baseline(wl, inp, budget):
     tokens = wl.tokens * done / wl.n_inst
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} instance passes (heads, cycling over the {wl.n_inst} of the workload), "
-                      f"whole {wl.L}-token sequence each, {dt:.1f} s, numpy fp64"}
+                      f"whole {wl.L}-token sequence each, {dt:.1f} s, numpy fp64", "host": host_info()}
 
 
 SRC_FILES = ("lact.hip", "lact_device.hpp", "lact_kernels.hpp", "lact_direct.hpp", "lact_backward.hpp",

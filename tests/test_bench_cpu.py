@@ -1,0 +1,39 @@
+"""bench.py's host-side logic (no GPU): the one-GPU guard, the per-kernel
+flop split that the roofline divides by, and the host record of the oracle
+baseline."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from test_layers_amd import lact
+from test_layers_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert not r.stdout.strip()   # no JSON line for a configuration that was not measured
+
+
+@pytest.mark.parametrize("cid", sorted(W.CONFIGS))
+def test_per_kernel_flops_add_up_to_the_algorithmic_total(cid):
+    wl = W.CONFIGS[cid]
+    kf = bench.kernel_flops(wl, lact)
+    alg = W.algorithmic_flops(wl)
+    parts = kf[lact.K_UPD] + kf[lact.K_DW] + kf[lact.K_APP] + kf[lact.K_OUT]
+    assert parts == pytest.approx(alg["update"] + alg["apply"], rel=1e-12)
+    if wl.D == wl.dh:
+        assert kf[lact.K_NS] == pytest.approx(alg["total"] - alg["update"] - alg["apply"], rel=1e-12, abs=0.0)
+
+
+def test_host_record():
+    h = bench.host_info()
+    assert set(h) == {"cpu_model", "os_cpu_count", "affinity_cpus", "blas"}
+    assert h["os_cpu_count"] >= h["affinity_cpus"] >= 1

@@ -331,3 +331,14 @@ def test_binding_rejects_mis_shaped_tensors():
         lact.chunk_update(q, torch.zeros(n, L + 1, D), torch.zeros(n, L, 3), None, *W)
     with pytest.raises(ValueError, match="o has shape"):
         lact.apply(q, *W, o=torch.zeros(n, L, 64))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without liblact.so the binding raises; there is no other implementation
+    to fall back to."""
+    monkeypatch.setattr(lact, "_lib", None)
+    monkeypatch.setattr(lact, "LIB_PATH", str(tmp_path / "liblact.so"))
+    with pytest.raises(ImportError, match="not built"):
+        lact.lib()
+    with pytest.raises(ImportError):
+        lact.workspace_size(lact.problem(1, 64, 0, 0, 1), 128, 0, 0, None, None)

@@ -165,15 +165,25 @@ def test_layer_orders_and_no_renorm(lact, order):
         assert max(errs.values()) <= wl.tol, errs
 
 
+MIXED = {
+    # ragged last update+apply chunk (333 tokens)
+    "ragged": ((0, 512, 700, 1212, 1724, 2057),
+               (W.UPDATE | W.APPLY, W.APPLY, W.UPDATE | W.APPLY, W.UPDATE, W.UPDATE | W.APPLY)),
+    # a one-token update+apply chunk last, after an apply-only chunk at the start
+    "one_token": ((0, 100, 612, 1124, 1125),
+                  (W.APPLY, W.UPDATE | W.APPLY, W.UPDATE | W.APPLY, W.UPDATE | W.APPLY)),
+}
+
+
+@pytest.mark.parametrize("sched", sorted(MIXED))
 @pytest.mark.parametrize("order", [W.APPLY_THEN_UPDATE, W.UPDATE_THEN_APPLY])
-def test_layer_mixed_schedule_plain_bf16(lact, order):
-    """Plain bf16 at d = 384 on a schedule that mixes update+apply chunks
-    (apply-then-update: their queries run in the update forward tile) with an
-    apply-only chunk that merges into the next step's apply range, an
-    update-only chunk and a ragged last update+apply chunk (333 tokens)."""
+def test_layer_mixed_schedule_plain_bf16(lact, order, sched):
+    """Plain bf16 at d = 384 on schedules that mix update+apply chunks
+    (apply-then-update: their queries run in the update forward tile) with
+    apply-only chunks that merge into the next step's apply range, an
+    update-only chunk, and ragged or one-token last chunks."""
     import dataclasses
-    b = (0, 512, 700, 1212, 1724, 2057)
-    f = (W.UPDATE | W.APPLY, W.APPLY, W.UPDATE | W.APPLY, W.UPDATE, W.UPDATE | W.APPLY)
+    b, f = MIXED[sched]
     wl = dataclasses.replace(W.CONFIGS[2], n_inst=2, L=b[-1], bounds=b, flags=f)
     inp = W.generate(wl, seed=5)
     log(f"mixed schedule order={order}: bounds={b}")

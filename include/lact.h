@@ -260,10 +260,12 @@ const char* lact_last_error(void);
  */
 #define LACT_K_UPD 0       /* update forward: k W1^T, k W3^T, v W2 + SwiGLU backward terms
                               (bf16 chunks of >= 4,096 tokens at d = dh = 128: together with
-                              the weight-gradient contraction, one kernel) */
-#define LACT_K_APP 1       /* apply forward: q W1^T, q W3^T -> gated hidden (bf16 q with
-                              dh = 128: the whole apply, o = Hq W2^T included, in one
-                              kernel) */
+                              the weight-gradient contraction, one kernel; plain bf16
+                              apply-then-update chunks: also the chunk's q W1^T, q W3^T ->
+                              gated hidden) */
+#define LACT_K_APP 1       /* apply forward: q W1^T, q W3^T -> gated hidden, for applies not
+                              computed in their update's kernel (bf16 q with dh = 128: the
+                              whole apply, o = Hq W2^T included, in one kernel) */
 #define LACT_K_OUT 2       /* apply output product o = Hq W2^T (when not fused) */
 #define LACT_K_DW 3        /* weight-gradient contractions (split over tokens; when not fused) */
 #define LACT_K_OPT 4       /* optimiser step + row renormalisation + weight snapshot */

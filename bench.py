@@ -240,7 +240,7 @@ def main():
         print(json.dumps({"copy_calib_bytes": nbytes, "launches": 5}))
         return
 
-    wl = W.CONFIGS[args.config]
+    wl = W.WORKLOADS[args.config]
     inp = W.generate(wl, threads=16)
     dev = lambda x: None if x is None else (
         torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() if x.dtype == np.uint16

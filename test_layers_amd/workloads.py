@@ -133,7 +133,7 @@ def _viewset_schedule(prefill: bool = False):
     return (0, n_in, n_in + n_tgt), ((UPDATE | APPLY) if prefill else UPDATE, APPLY)
 
 
-def _make_configs() -> Dict[int, Workload]:
+def _make_workloads() -> Dict[int, Workload]:
     c = {}
     b, f = uniform_schedule(1024, 256)
     c[1] = Workload(1, "tiny_lm_d64_fp32_gd", 1, 64, 1024, b, f, APPLY_THEN_UPDATE,
@@ -173,7 +173,7 @@ def _make_configs() -> Dict[int, Workload]:
     return c
 
 
-CONFIGS: Dict[int, Workload] = _make_configs()
+WORKLOADS: Dict[int, Workload] = _make_workloads()
 
 
 # ---------------------------------------------------------------- rounding

@@ -22,9 +22,9 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert not r.stdout.strip()   # no JSON line for a configuration that was not measured
 
 
-@pytest.mark.parametrize("cid", sorted(W.CONFIGS))
+@pytest.mark.parametrize("cid", sorted(W.WORKLOADS))
 def test_per_kernel_flops_add_up_to_the_algorithmic_total(cid):
-    wl = W.CONFIGS[cid]
+    wl = W.WORKLOADS[cid]
     kf = bench.kernel_flops(wl, lact)
     alg = W.algorithmic_flops(wl)
     parts = kf[lact.K_UPD] + kf[lact.K_DW] + kf[lact.K_APP] + kf[lact.K_OUT]

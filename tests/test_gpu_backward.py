@@ -99,23 +99,23 @@ def run_case(lact, wl, seed=0, order=None, renorm=True, state_cot=True, M0_scale
 
 CASES = {
     # fp32 io, GD, three uniform chunks
-    "f32_gd": W.CONFIGS[1].scaled(n_inst=2, L=640, chunk=256),
+    "f32_gd": W.WORKLOADS[1].scaled(n_inst=2, L=640, chunk=256),
     # bf16 io, momentum, ragged tail
-    "bf16_momentum": W.CONFIGS[2].scaled(n_inst=2, L=3 * 256 + 100, chunk=256),
+    "bf16_momentum": W.WORKLOADS[2].scaled(n_inst=2, L=3 * 256 + 100, chunk=256),
     # bf16 io, Muon at d = 512 (3B-LM shape, reduced)
-    "bf16_muon_d512": W.CONFIGS[3].scaled(n_inst=2, L=2 * 512 + 64, chunk=512),
+    "bf16_muon_d512": W.WORKLOADS[3].scaled(n_inst=2, L=2 * 512 + 64, chunk=512),
     # bf16 io, momentum + Muon
-    "bf16_muon_momentum": W.CONFIGS[8].scaled(n_inst=2, L=2 * 256 + 64, chunk=256),
+    "bf16_muon_momentum": W.WORKLOADS[8].scaled(n_inst=2, L=2 * 256 + 64, chunk=256),
     # view set: one update-only chunk then an apply-only chunk (update-then-apply)
-    "viewset": dataclasses.replace(W.CONFIGS[4], n_inst=2, L=1500, bounds=(0, 1200, 1500),
+    "viewset": dataclasses.replace(W.WORKLOADS[4], n_inst=2, L=1500, bounds=(0, 1200, 1500),
                                    flags=(W.UPDATE, W.APPLY)),
     # video: clean chunks update+apply, noisy chunks apply only
-    "video": dataclasses.replace(W.CONFIGS[5], n_inst=2, L=W.video_schedule(3, 200)[0][-1],
+    "video": dataclasses.replace(W.WORKLOADS[5], n_inst=2, L=W.video_schedule(3, 200)[0][-1],
                                  bounds=W.video_schedule(3, 200)[0], flags=W.video_schedule(3, 200)[1]),
     # rectangular fast weights, dh > d, momentum
-    "rect_dh_gt_d": W.CONFIGS[10].scaled(n_inst=2, L=2 * 256 + 30, chunk=256),
+    "rect_dh_gt_d": W.WORKLOADS[10].scaled(n_inst=2, L=2 * 256 + 30, chunk=256),
     # raw q / k (pre-processed by the layer) and the per-token output scale
-    "raw_qk_scaled": W.CONFIGS[9].scaled(n_inst=2, L=3 * 256 + 100, chunk=256),
+    "raw_qk_scaled": W.WORKLOADS[9].scaled(n_inst=2, L=3 * 256 + 100, chunk=256),
 }
 
 
@@ -133,7 +133,7 @@ def test_backward_parity(lact, name):
 def test_backward_optimisers_orders_renorm(lact, opt, order):
     """Every optimiser x order, with and without renorm, nonzero initial
     momentum, fp32 io."""
-    base = W.CONFIGS[1].scaled(n_inst=2, L=3 * 128 + 40, chunk=128)
+    base = W.WORKLOADS[1].scaled(n_inst=2, L=3 * 128 + 40, chunk=128)
     wl = dataclasses.replace(base, opt=opt)
     for renorm in (True, False):
         errs = run_case(lact, wl, seed=2 + opt, order=order, renorm=renorm, M0_scale=0.05)
@@ -147,7 +147,7 @@ def test_backward_rectangular_newton_schulz(lact, shape, opt):
     """d != dh in both orientations: the Newton-Schulz backward transposes the
     tall matrices, as the forward map does."""
     D, Dh = shape
-    wl = dataclasses.replace(W.CONFIGS[1].scaled(n_inst=2, L=2 * 128 + 20, chunk=128), D=D, Dh=Dh, opt=opt)
+    wl = dataclasses.replace(W.WORKLOADS[1].scaled(n_inst=2, L=2 * 128 + 20, chunk=128), D=D, Dh=Dh, opt=opt)
     errs = run_case(lact, wl, seed=5, M0_scale=0.05)
     log(f"  d={D} dh={Dh} opt={opt}: errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
     assert max(errs.values()) <= TOL, errs
@@ -156,7 +156,7 @@ def test_backward_rectangular_newton_schulz(lact, shape, opt):
 @pytest.mark.parametrize("order", [W.APPLY_THEN_UPDATE, W.UPDATE_THEN_APPLY])
 def test_backward_raw_qk_output_scale_muon_fp32(lact, order):
     """Raw q / k and the output scale with fp32 inputs and Muon, both orders."""
-    base = W.CONFIGS[9].scaled(n_inst=2, L=3 * 128 + 40, chunk=128)
+    base = W.WORKLOADS[9].scaled(n_inst=2, L=3 * 128 + 40, chunk=128)
     wl = dataclasses.replace(base, D=64, io_dtype=W.DTYPE_F32, opt=W.OPT_MUON)
     errs = run_case(lact, wl, seed=8, order=order)
     log(f"  order={order}: errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
@@ -165,7 +165,7 @@ def test_backward_raw_qk_output_scale_muon_fp32(lact, order):
 
 def test_backward_without_state_cotangents(lact):
     """gW = gM = NULL means zero cotangents of the final state."""
-    wl = W.CONFIGS[2].scaled(n_inst=2, L=2 * 256, chunk=256)
+    wl = W.WORKLOADS[2].scaled(n_inst=2, L=2 * 256, chunk=256)
     errs = run_case(lact, wl, seed=4, state_cot=False)
     assert max(errs.values()) <= TOL, errs
 
@@ -173,7 +173,7 @@ def test_backward_without_state_cotangents(lact):
 def test_backward_no_update_passes_state_cotangent_through(lact):
     """Apply-only schedule: dW = gW + the apply's weight gradients, dk = dv =
     dlr = 0 exactly, dM = gM exactly."""
-    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=300, chunk=300), bounds=(0, 300), flags=(W.APPLY,))
+    wl = dataclasses.replace(W.WORKLOADS[2].scaled(n_inst=2, L=300, chunk=300), bounds=(0, 300), flags=(W.APPLY,))
     errs = run_case(lact, wl, seed=6)
     assert max(errs.values()) <= TOL, errs
 
@@ -188,7 +188,7 @@ def test_backward_full_size(lact, cid):
     """The backward at the full workload sizes (every instance on the GPU;
     the oracle on all of them, or on a spread sample for the 40-head video
     workload)."""
-    wl = W.CONFIGS[cid]
+    wl = W.WORKLOADS[cid]
     log(f"backward full cfg{cid} {wl.name}: n={wl.n_inst} d={wl.D} dh={wl.dh} L={wl.L} chunks={wl.n_chunks}")
     errs = run_case(lact, wl, seed=0, instances=FULL[cid])
     tol = TOL_NS_FULL[cid] if wl.opt in (W.OPT_MUON, W.OPT_MUON_MOMENTUM) else TOL
@@ -200,7 +200,7 @@ def test_backward_full_size(lact, cid):
 def test_backward_maximum_width(lact, opt):
     """d = dh = 1024, the widest the library takes (Newton-Schulz on
     1024 x 1024 matrices for Muon)."""
-    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=1, L=2 * 64 + 16, chunk=64), D=1024, opt=opt)
+    wl = dataclasses.replace(W.WORKLOADS[2].scaled(n_inst=1, L=2 * 64 + 16, chunk=64), D=1024, opt=opt)
     errs = run_case(lact, wl, seed=9)
     log(f"  d=1024 opt={opt}: errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
     assert max(errs.values()) <= TOL, errs
@@ -226,7 +226,7 @@ def test_backward_empty_sequence(lact):
 
 def test_backward_single_token_chunk(lact):
     """A one-token last chunk (the shortest a chunk can be)."""
-    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=257, chunk=256))
+    wl = dataclasses.replace(W.WORKLOADS[2].scaled(n_inst=2, L=257, chunk=256))
     errs = run_case(lact, wl, seed=10)
     assert max(errs.values()) <= TOL, errs
 
@@ -238,7 +238,7 @@ def test_backward_replays_in_a_hip_graph(lact, opt):
     graph can capture it; every replay, with eager work and synchronisations
     between replays, equals the eager call bitwise and rewrites every
     output."""
-    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=2 * 256 + 40, chunk=256), opt=opt)
+    wl = dataclasses.replace(W.WORKLOADS[2].scaled(n_inst=2, L=2 * 256 + 40, chunk=256), opt=opt)
     inp = W.generate(wl, seed=23)
     dO, gW, gM = cotangents(wl, 23, True)
     dev = lambda x: to_dev(x, torch)

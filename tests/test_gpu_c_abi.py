@@ -32,7 +32,7 @@ def test_layer_through_the_c_abi_alone(tmp_path, opt, planes):
     import dataclasses
     assert os.path.exists(EXE), "tests/c_layer_run is built by __graft_entry__.build()"
     from test_layers_amd import lact
-    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=2 * 512 + 160, chunk=512), opt=opt)
+    wl = dataclasses.replace(W.WORKLOADS[2].scaled(n_inst=2, L=2 * 512 + 160, chunk=512), opt=opt)
     inp = W.generate(wl, seed=31)
     mom = opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
     rng = np.random.default_rng([31, 77])

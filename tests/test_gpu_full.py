@@ -21,7 +21,7 @@ def lact():
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
 def test_full_size_config(lact, cid):
-    wl = W.CONFIGS[cid]
+    wl = W.WORKLOADS[cid]
     t = time.time()
     log(f"full cfg{cid} {wl.name}: n={wl.n_inst} D={wl.D} L={wl.L} chunks={wl.n_chunks} "
         f"rec_planes={wl.rec_planes}")

@@ -99,35 +99,35 @@ def test_chunk_update_matches_oracle(lact, opt, io, planes, D):
 
 # ------------------------------------------------------------------ layer at reduced sizes
 SMALL = {
-    1: W.CONFIGS[1],
-    2: W.CONFIGS[2].scaled(n_inst=2, L=3 * 512 + 200, chunk=512),
-    3: W.CONFIGS[3].scaled(n_inst=2, L=2 * 1024 + 300, chunk=1024),
+    1: W.WORKLOADS[1],
+    2: W.WORKLOADS[2].scaled(n_inst=2, L=3 * 512 + 200, chunk=512),
+    3: W.WORKLOADS[3].scaled(n_inst=2, L=2 * 1024 + 300, chunk=1024),
 }
 
 
 def _small_viewset():
-    c = W.CONFIGS[4]
+    c = W.WORKLOADS[4]
     b, f = (0, 4000, 4500), (W.UPDATE, W.APPLY)
     import dataclasses
     return dataclasses.replace(c, n_inst=2, L=4500, bounds=b, flags=f)
 
 
 def _small_video():
-    c = W.CONFIGS[5]
+    c = W.WORKLOADS[5]
     import dataclasses
     b, f = W.video_schedule(3, 700)
     return dataclasses.replace(c, n_inst=3, L=b[-1], bounds=b, flags=f)
 
 
 def _small_prefill():
-    c = W.CONFIGS[6]
+    c = W.WORKLOADS[6]
     b, f = (0, 4000, 4500), (W.UPDATE | W.APPLY, W.APPLY)
     import dataclasses
     return dataclasses.replace(c, n_inst=2, L=4500, bounds=b, flags=f)
 
 
 def _small_video_noisy_first():
-    c = W.CONFIGS[7]
+    c = W.WORKLOADS[7]
     import dataclasses
     b, f = W.video_schedule_noisy_first(3, 700)
     return dataclasses.replace(c, n_inst=3, L=b[-1], bounds=b, flags=f)
@@ -137,9 +137,9 @@ SMALL[4] = _small_viewset()
 SMALL[5] = _small_video()
 SMALL[6] = _small_prefill()
 SMALL[7] = _small_video_noisy_first()
-SMALL[8] = W.CONFIGS[8].scaled(n_inst=2, L=2 * 1024 + 300, chunk=1024)
-SMALL[9] = W.CONFIGS[9].scaled(n_inst=2, L=3 * 512 + 200, chunk=512)
-SMALL[10] = W.CONFIGS[10].scaled(n_inst=2, L=3 * 512 + 200, chunk=512)
+SMALL[8] = W.WORKLOADS[8].scaled(n_inst=2, L=2 * 1024 + 300, chunk=1024)
+SMALL[9] = W.WORKLOADS[9].scaled(n_inst=2, L=3 * 512 + 200, chunk=512)
+SMALL[10] = W.WORKLOADS[10].scaled(n_inst=2, L=3 * 512 + 200, chunk=512)
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
@@ -155,7 +155,7 @@ def test_layer_reduced_size(lact, cid):
 
 @pytest.mark.parametrize("order", [W.APPLY_THEN_UPDATE, W.UPDATE_THEN_APPLY])
 def test_layer_orders_and_no_renorm(lact, order):
-    wl = W.CONFIGS[2].scaled(n_inst=2, L=1000, chunk=384)
+    wl = W.WORKLOADS[2].scaled(n_inst=2, L=1000, chunk=384)
     inp = W.generate(wl, seed=3)
     for renorm in (True, False):
         log(f"order={order} renorm={renorm}")
@@ -184,7 +184,7 @@ def test_layer_mixed_schedule_plain_bf16(lact, order, sched):
     update-only chunk, and ragged or one-token last chunks."""
     import dataclasses
     b, f = MIXED[sched]
-    wl = dataclasses.replace(W.CONFIGS[2], n_inst=2, L=b[-1], bounds=b, flags=f)
+    wl = dataclasses.replace(W.WORKLOADS[2], n_inst=2, L=b[-1], bounds=b, flags=f)
     inp = W.generate(wl, seed=5)
     log(f"mixed schedule order={order}: bounds={b}")
     gpu = run_gpu(wl, inp, torch, lact, order=order)
@@ -200,7 +200,7 @@ def test_layer_is_deterministic(lact, cid):
     view-set layer with a 4,608-token update chunk (the fused update kernel)."""
     import dataclasses
     if cid == "fused_update":
-        wl = dataclasses.replace(W.CONFIGS[4], n_inst=2, L=4608 + 512, bounds=(0, 4608, 4608 + 512),
+        wl = dataclasses.replace(W.WORKLOADS[4], n_inst=2, L=4608 + 512, bounds=(0, 4608, 4608 + 512),
                                  flags=(W.UPDATE, W.APPLY))
     else:
         wl = SMALL[cid]
@@ -215,7 +215,7 @@ def test_layer_is_deterministic(lact, cid):
 def test_resume_equals_single_call(lact):
     """Chunks [0, c) then [c, n) with the state carried equal one call (bitwise:
     every kernel reduces in a fixed order)."""
-    wl = W.CONFIGS[2].scaled(n_inst=2, L=1536, chunk=512)
+    wl = W.WORKLOADS[2].scaled(n_inst=2, L=1536, chunk=512)
     inp = W.generate(wl, seed=6)
     full = run_gpu(wl, inp, torch, lact)
     q, k, v = to_dev(inp.q, torch), to_dev(inp.k, torch), to_dev(inp.v, torch)
@@ -245,7 +245,7 @@ def test_layer_raw_qk_and_output_scale_every_profile(lact, io, planes, opt):
     GEMM, the bf16 ones inside the apply tile), with tokens whose scale
     pre-activation is 0 or far negative (silu = 0: the row must vanish)."""
     import dataclasses
-    wl = dataclasses.replace(W.CONFIGS[9].scaled(n_inst=2, L=900, chunk=256), io_dtype=io,
+    wl = dataclasses.replace(W.WORKLOADS[9].scaled(n_inst=2, L=900, chunk=256), io_dtype=io,
                              rec_planes=planes, opt=opt, tol=_gate(io))
     log(f"raw qk + scale io={io} planes={planes} opt={opt}")
     inp = W.generate(wl, seed=11)
@@ -363,7 +363,7 @@ def test_layer_rectangular_every_profile(lact, io, planes, opt):
     """The full layer with dh < d and dh > d (ragged last chunk), every profile."""
     import dataclasses
     for d, dh in [(128, 64), (64, 192)]:
-        wl = dataclasses.replace(W.CONFIGS[10].scaled(n_inst=2, L=700, chunk=256), D=d, Dh=dh, io_dtype=io,
+        wl = dataclasses.replace(W.WORKLOADS[10].scaled(n_inst=2, L=700, chunk=256), D=d, Dh=dh, io_dtype=io,
                                  rec_planes=planes, opt=opt, tol=_gate(io))
         log(f"layer d={d} dh={dh} io={io} planes={planes} opt={opt}")
         inp = W.generate(wl, seed=5)
@@ -384,7 +384,7 @@ def test_layer_rectangular_every_profile(lact, io, planes, opt):
 def test_layer_maximum_width(lact, d, dh, io, planes, opt):
     """The largest widths the library accepts (1024), ragged chunks."""
     import dataclasses
-    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=1, L=700, chunk=256), D=d, Dh=dh, io_dtype=io,
+    wl = dataclasses.replace(W.WORKLOADS[2].scaled(n_inst=1, L=700, chunk=256), D=d, Dh=dh, io_dtype=io,
                              rec_planes=planes, opt=opt, tol=_gate(io))
     log(f"layer d={d} dh={dh} io={io} planes={planes} opt={opt}")
     inp = W.generate(wl, seed=9)
@@ -401,7 +401,7 @@ def test_zero_learning_rates_leave_the_state_unchanged(lact, opt):
     M = 0) come back bit-identical, and every output row is the plain SwiGLU
     MLP of the initial weights."""
     import dataclasses
-    wl = dataclasses.replace(W.CONFIGS[2].scaled(n_inst=2, L=700, chunk=256), D=128, opt=opt, rec_planes=2)
+    wl = dataclasses.replace(W.WORKLOADS[2].scaled(n_inst=2, L=700, chunk=256), D=128, opt=opt, rec_planes=2)
     inp = W.generate(wl, seed=13)
     inp.lr[:] = 0.0
     gpu = run_gpu(wl, inp, torch, lact)
@@ -453,7 +453,7 @@ def test_layer_d128_fused_apply_with_output_scale(lact):
     per-token output scale in its epilogue and raw q, k, over several apply
     groups and instances."""
     import dataclasses
-    wl = dataclasses.replace(W.CONFIGS[9].scaled(n_inst=3, L=6000, chunk=1000), D=128, opt=W.OPT_GD)
+    wl = dataclasses.replace(W.WORKLOADS[9].scaled(n_inst=3, L=6000, chunk=1000), D=128, opt=W.OPT_GD)
     log(f"fused apply with output scale n={wl.n_inst} L={wl.L} chunks={wl.n_chunks}")
     inp = W.generate(wl, seed=17)
     gpu = run_gpu(wl, inp, torch, lact)
@@ -469,7 +469,7 @@ def test_layer_replays_in_a_hip_graph(lact, cid):
     memset, copy or host synchronisation), so a HIP graph can capture a whole
     layer forward; every replay, with eager work and synchronisations between
     replays, equals the eager call bitwise."""
-    wl = W.CONFIGS[2].scaled(n_inst=2, L=1500, chunk=512) if cid == 2 else SMALL[4]
+    wl = W.WORKLOADS[2].scaled(n_inst=2, L=1500, chunk=512) if cid == 2 else SMALL[4]
     inp = W.generate(wl, seed=21)
     ref = run_gpu(wl, inp, torch, lact)
     q, k, v, lr, beta = (to_dev(x, torch) for x in (inp.q, inp.k, inp.v, inp.lr, inp.beta))

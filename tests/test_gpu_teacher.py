@@ -34,7 +34,7 @@ def _f64(t):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cid", [2, 3, 5, 8, 10])
 def test_teacher_forced_chunks(lact, cid):
-    wl = W.CONFIGS[cid]
+    wl = W.WORKLOADS[cid]
     assert wl.order == W.APPLY_THEN_UPDATE
     n, L, D = wl.n_inst, wl.L, wl.D
     inst = sorted({0, n - 1})

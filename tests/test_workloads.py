@@ -17,7 +17,7 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_schedules():
-    c = W.CONFIGS
+    c = W.WORKLOADS
     assert c[1].bounds == (0, 256, 512, 768, 1024) and c[1].flags == (3, 3, 3, 3)
     assert c[2].n_chunks == 16 and c[3].n_chunks == 8
     assert c[4].bounds == (0, 196608, 200704) and c[4].flags == (W.UPDATE, W.APPLY)
@@ -35,7 +35,7 @@ def test_schedules():
 
 
 def test_generator_reproducible_per_instance():
-    wl = W.CONFIGS[2].scaled(n_inst=3, L=64, chunk=32)
+    wl = W.WORKLOADS[2].scaled(n_inst=3, L=64, chunk=32)
     a = W.generate(wl)
     b = W.generate_instance(wl, 2)
     for x, y in [(a.q, b.q), (a.k, b.k), (a.lr, b.lr), (a.beta, b.beta), (a.W2, b.W2)]:
@@ -45,28 +45,28 @@ def test_generator_reproducible_per_instance():
     n = np.linalg.norm(W.to_f64(a.k), axis=-1)
     assert np.all(np.abs(n - 1) < 1e-2)
     assert np.all(a.lr > 0) and np.all((a.beta > 0) & (a.beta < 1))
-    wl1 = W.CONFIGS[1]
+    wl1 = W.WORKLOADS[1]
     g = W.generate(wl1)
     assert g.q.dtype == np.float32 and g.beta is None and g.q.shape == (1, 1024, 64)
 
 
 def test_flop_counts():
-    f = W.algorithmic_flops(W.CONFIGS[2])
+    f = W.algorithmic_flops(W.WORKLOADS[2])
     assert abs(f["total"] - 0.348e12) / 0.348e12 < 0.01
-    f = W.algorithmic_flops(W.CONFIGS[3])
+    f = W.algorithmic_flops(W.WORKLOADS[3])
     assert abs(f["total"] - 1.508e12) / 1.508e12 < 0.01
 
 
 def test_rectangular_fast_weights():
     """dh != d: W1, W3 [dh, d], W2 [d, dh], each ~ N(0, 1/fan-in); the square
     workloads keep their draws (same shapes, same order)."""
-    wl = W.CONFIGS[10].scaled(n_inst=2, L=64, chunk=32)
+    wl = W.WORKLOADS[10].scaled(n_inst=2, L=64, chunk=32)
     assert wl.D == 384 and wl.dh == 768
     g = W.generate(wl)
     assert g.W1.shape == (2, 768, 384) and g.W3.shape == (2, 768, 384) and g.W2.shape == (2, 384, 768)
     assert g.q.shape == (2, 64, 384)
     assert abs(np.std(g.W1) * np.sqrt(384) - 1) < 0.02 and abs(np.std(g.W2) * np.sqrt(768) - 1) < 0.02
-    sq = W.CONFIGS[2].scaled(n_inst=1, L=64, chunk=32)
+    sq = W.WORKLOADS[2].scaled(n_inst=1, L=64, chunk=32)
     assert sq.dh == sq.D
-    f = W.algorithmic_flops(W.CONFIGS[10])
-    assert f["total"] == 2 * W.algorithmic_flops(W.CONFIGS[2])["total"]
+    f = W.algorithmic_flops(W.WORKLOADS[10])
+    assert f["total"] == 2 * W.algorithmic_flops(W.WORKLOADS[2])["total"]

@@ -1,23 +1,26 @@
 """Benchmark of the LaCT fast-weight layer forward (update + apply) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--backward]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--backward]
 
 One step = one whole layer forward over the workload's sequence (every chunk:
 forward products, SwiGLU backward epilogue, weight-gradient contraction,
 optimiser + renorm, apply), inputs resident in HBM.  The default workload is
-the 760M-LM-shaped layer: 4 heads, d = dh = 384, 32,768 tokens in chunks of
-2,048, bf16 q/k/v, fp32 fast weights, momentum, apply-then-update.  Prints one
-JSON line.
+the largest language configuration, the 3B-LM-shaped layer: 6 heads,
+d = dh = 512, 32,768 tokens in chunks of 4,096, bf16 q/k/v, fp32 fast
+weights, Muon (5 Newton-Schulz steps) + row renormalisation,
+apply-then-update.  Prints one JSON line.
 
-The fast weights are not reset between steps: every step runs the same
-kernels on the state the previous step left (same work, like the next 32K
-tokens of a longer sequence).
+Every step starts from the same initial state: the fast weights (and the
+momentum buffer) are restored by device copies between steps, outside the
+per-step HIP events that time the layer calls.
 
 --backward measures the layer's backward pass instead (lact_layer_backward:
 gradients of q, k, v, lr, beta and the initial state for a seeded output
 cotangent; one step = one whole backward call, which replays the forward
-state trajectory and sweeps the chunks in reverse).  It computes fp32-grade,
-so its products are priced against the fp32 matrix peak.
+state trajectory and sweeps the chunks in reverse).  Its products run as
+bf16 MFMA passes over fp32 operands split into bf16 planes, so they are
+priced against the bf16 peak, algorithmically and (from committed counters)
+as executed MFMA work.
 """
 import argparse
 import json
@@ -30,6 +33,7 @@ import numpy as np
 PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
 PEAK_FP32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12         # bytes/s
+RIDGE = PEAK_BF16 / PEAK_HBM   # flop per byte where the bf16 MFMA and HBM roofs meet
 
 
 def parse():
@@ -37,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload id 1..10 (default: the 760M LM layer)")
+    ap.add_argument("--config", type=int, default=3, help="workload id 1..10 (default: the 3B LM layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work to sample")
     ap.add_argument("--backward", action="store_true", help="measure the layer's backward pass")
@@ -63,6 +67,39 @@ def kernel_flops(wl, lact):
         lact.K_SNAP: 0.0,
         lact.K_PREP: 0.0,
     }
+
+
+def kernel_bytes(wl, lact, fused):
+    """Algorithmic HBM bytes per step, per kernel class: what each kernel must
+    read or write at least -- inputs read once, layer outputs and the state
+    written once, the weights a product reads once per launch -- with the
+    intermediates that a fused path keeps on chip (update terms, gated
+    hidden, split partials, Newton-Schulz operands) counted as zero.
+    `fused` names the classes whose work runs inside another class's kernel
+    ('app_in_upd', 'dw_in_upd', 'out_in_app')."""
+    from test_layers_amd import workloads as W
+    D, Dh, n = wl.D, wl.dh, wl.n_inst
+    io = 2 if wl.io_dtype == W.DTYPE_BF16 else 4
+    snap = 2 if wl.io_dtype == W.DTYPE_BF16 else 4
+    mom = wl.opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    upd = sum(b - a for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags) if f & W.UPDATE)
+    app = sum(b - a for (a, b), f in zip(zip(wl.bounds[:-1], wl.bounds[1:]), wl.flags) if f & W.APPLY)
+    n_upd = sum(1 for f in wl.flags if f & W.UPDATE)
+    n_app = sum(1 for f in wl.flags if f & W.APPLY)
+    mat = D * Dh
+    b = {c: 0.0 for c in lact.K_NAMES}
+    b[lact.K_UPD] = n * upd * (2 * D * io + 12 + (4 if mom else 0)) + n_upd * n * 3 * mat * snap
+    if "app_in_upd" in fused:
+        b[lact.K_UPD] += n * app * D * io
+    b[lact.K_APP] = n * app * D * io + n_app * n * 2 * mat * snap
+    b[lact.K_OUT] = n * app * D * io + n_app * n * mat * snap
+    if "out_in_app" in fused:
+        b[lact.K_APP] += b[lact.K_OUT]
+    b[lact.K_DW] = n * upd * 2 * D * io
+    b[lact.K_OPT] = n_upd * n * 3 * mat * 4 * (4 if wl.opt == W.OPT_MOMENTUM else 2)
+    b[lact.K_SNAP] = n * 3 * mat * 4
+    b[lact.K_PREP] = (n * app * D * io * 2 + n * upd * D * io * 2) if wl.layer_qk_prep else 0.0
+    return b
 
 
 def ns_flops_per_matrix(D, Dh, iters=5):
@@ -149,15 +186,6 @@ def cpu_baseline_backward(wl, inp, dO, budget):
                       f"whole {wl.L}-token sequence each, {dt:.1f} s, numpy fp64", "host": host_info()}
 
 
-def opt_bytes(wl, S):
-    """Minimum HBM bytes of the optimiser kernel per update step: S fp32
-    partials of the three direction matrices read, W (and M) read and written."""
-    from test_layers_amd import workloads as W
-    mats = 3 * wl.D * wl.dh * 4 * wl.n_inst
-    per = S * mats + 2 * mats + (2 * mats if wl.opt == W.OPT_MOMENTUM else 0)
-    return per
-
-
 def cpu_baseline(wl, inp, budget):
     """The oracle as it stands, on a bounded sample of the same workload:
     whole instances (heads), each over the whole sequence, until about
@@ -200,10 +228,11 @@ def source_sha():
     return h.hexdigest()
 
 
-def pmc_traffic(kernel, workload, fname="pmc_traffic.json"):
-    """HBM bytes per launch of a kernel class from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's
-    reading), or None when absent or taken on other sources."""
+def pmc_entry(kernel, workload, fname="pmc_traffic.json"):
+    """The committed counter summary of one kernel class on one workload
+    (HBM bytes from FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's
+    reading; MFMA work where recorded), or None when absent or taken on
+    other sources."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", fname)
     try:
@@ -211,9 +240,14 @@ def pmc_traffic(kernel, workload, fname="pmc_traffic.json"):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_sha() or t.get("workload") != workload:
+    w = t.get("workloads", {}).get(workload)
+    if not w or w.get("source_sha") != source_sha():
         return None
-    k = t.get("kernels", {}).get(kernel)
+    return w.get("kernels", {}).get(kernel)
+
+
+def pmc_traffic(kernel, workload, fname="pmc_traffic.json"):
+    k = pmc_entry(kernel, workload, fname)
     if not k:
         return None
     return k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
@@ -270,12 +304,14 @@ def main():
                                              opt=wl.opt, bounds=bounds, flags=flags, qk_prep=wl.layer_qk_prep,
                                              oz=oz, out=box["out"], workspace=ws, stream=stream)
         kf = backward_kernel_flops(wl, lact)
-        peak, peak_name = PEAK_FP32_MFMA, "fp32"
+        peak, peak_name = PEAK_BF16, "bf16"
         metric = ("LaCT layer backward tokens/sec (gradients of q, k, v, lr, beta and the initial state; "
                   "fp32-grade), 1xMI355X")
         dtype = "f32"
     else:
         o = torch.zeros_like(q)
+        W0 = [w.clone() for w in Ws]
+        M0 = [None if m is None else m.clone() for m in Ms]
         p = lact.problem(wl.n_inst, wl.D, wl.io_dtype, wl.opt, wl.rec_planes, dh=wl.dh,
                          qk_prep=wl.layer_qk_prep)
         ws = torch.empty(lact.workspace_size(p, wl.L, 0, wl.order, bounds, flags), dtype=torch.uint8,
@@ -290,29 +326,43 @@ def main():
         metric = "LaCT layer tokens/sec (update+apply) and % bf16 MFMA peak, 1xMI355X"
         dtype = "bf16" if wl.io_dtype == W.DTYPE_BF16 else "f32"
 
+    def restore():
+        # the forward overwrites the state in place: every step starts from W0 (M0)
+        if not args.backward:
+            for w, w0 in zip(Ws, W0):
+                w.copy_(w0)
+            for m, m0 in zip(Ms, M0):
+                if m is not None:
+                    m.copy_(m0)
+
     for _ in range(args.warmup):
+        restore()
         step()
-    # per-step boundaries as events on the layer's stream (no host sync inside
-    # the timed loop); the wall clock around the loop gives `value`
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # one pair of events on the layer's stream around each layer call (no
+    # host sync inside the timed loop); the state restores sit between them
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    marks[0].record(stream)
     for i in range(args.steps):
+        restore()
+        starts[i].record(stream)
         step()
-        marks[i + 1].record(stream)
+        ends[i].record(stream)
     torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
-    ms_per_step = dt / args.steps * 1e3
+    wall = time.perf_counter() - t0
+    step_ms = [starts[i].elapsed_time(ends[i]) for i in range(args.steps)]
+    ms_per_step = sum(step_ms) / args.steps
+    step_ms.sort()
     tokens = wl.tokens
-    value = tokens * args.steps / dt
+    value = tokens / (ms_per_step * 1e-3)
     flops = sum(kf.values()) if args.backward else W.algorithmic_flops(wl)["total"]
 
     # per-kernel HIP-event timing over the same number of steps
     for kc in lact.K_NAMES:
         lact.timing_enable(kc, True)
     for _ in range(args.steps):
+        restore()
         step()
     torch.cuda.synchronize()
     per = {}
@@ -322,32 +372,52 @@ def main():
         if nl:
             per[name] = {"ms_per_step": ms / args.steps, "launches_per_step": nl / args.steps,
                          "avg_launch_us": ms / nl * 1e3, "kc": kc}
-    if "apply_out" not in per:
+    fused = set()
+    if "apply_out" not in per and "apply_fwd" in per:
         # the fused apply kernel also runs the output product
         kf[lact.K_APP] += kf[lact.K_OUT]
-    elif "apply_fwd" not in per:
+        fused.add("out_in_app")
+    elif "apply_fwd" not in per and "apply_out" in per:
         # every apply-then-update chunk's query products ran in its update
         # forward tile (plain bf16, the same snapshot); the workloads here
         # fuse all of their applies or none
         kf[lact.K_UPD] += kf[lact.K_APP]
-    if "dw" not in per:
+        fused.add("app_in_upd")
+    if "dw" not in per and "update_fwd" in per:
         # the fused update kernel also runs the weight-gradient contraction
         kf[lact.K_UPD] += kf[lact.K_DW]
+        fused.add("dw_in_upd")
+    kb = kernel_bytes(wl, lact, fused)
     traffic_file = "pmc_traffic_backward.json" if args.backward else "pmc_traffic.json"
     dom = max(per.items(), key=lambda kv: kv[1]["ms_per_step"])
     dname, d = dom
-    if kf[d["kc"]] > 0:
-        per_launch = kf[d["kc"]] / (d["launches_per_step"])
-        achieved = per_launch / (d["avg_launch_us"] * 1e-6)
+    fl = kf.get(d["kc"], 0.0)
+    nbytes = kb.get(d["kc"], 0.0)
+    # the roof that bounds the kernel: MFMA when its algorithmic arithmetic
+    # intensity reaches the ridge point, else HBM
+    intensity = fl / nbytes if nbytes > 0 else float("inf")
+    t_launch = d["avg_launch_us"] * 1e-6
+    if fl > 0 and intensity >= RIDGE:
+        per_launch = fl / d["launches_per_step"]
+        achieved = per_launch / t_launch
         roof = {"kernel": dname, "bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak, "traffic": pmc_traffic(dname, wl.name, traffic_file),
-                "flops_per_launch": per_launch, "avg_launch_us": d["avg_launch_us"], "peak_dtype": peak_name}
+                "flops_per_launch": per_launch, "avg_launch_us": d["avg_launch_us"], "peak_dtype": peak_name,
+                "intensity_flop_per_byte": intensity if nbytes > 0 else None}
+        ent = pmc_entry(dname, wl.name, traffic_file)
+        if ent and ent.get("mfma_flops_per_launch"):
+            # MFMA work the kernel executes (plane passes, padding and
+            # symmetric tiles included), from the committed counters
+            roof["executed_flops_per_launch"] = ent["mfma_flops_per_launch"]
+            roof["executed_frac"] = ent["mfma_flops_per_launch"] / t_launch / peak
     else:
-        nb = opt_bytes(wl, 1) / d["launches_per_step"]
-        achieved = nb / (d["avg_launch_us"] * 1e-6)
+        per_launch = nbytes / d["launches_per_step"]
+        achieved = per_launch / t_launch
         roof = {"kernel": dname, "bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": pmc_traffic(dname, wl.name, traffic_file),
-                "bytes_per_launch": nb, "avg_launch_us": d["avg_launch_us"]}
+                "bytes_per_launch": per_launch, "avg_launch_us": d["avg_launch_us"],
+                "intensity_flop_per_byte": intensity,
+                "flops_per_launch": fl / d["launches_per_step"]}
     kernels = {k: {kk: round(vv, 4) for kk, vv in v.items() if kk != "kc"} for k, v in per.items()}
 
     out = {
@@ -359,6 +429,10 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "step_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1]},
+        "timing": ("HIP events around each layer call on its stream; mean over the timed steps"
+                   + ("" if args.backward else "; W0 (and M0) restored by device copies between steps, "
+                      "outside the events")),
+        "wall_ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -375,10 +449,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
-    if args.backward:
-        out["layer_frac_fp32_peak"] = flops / (ms_per_step * 1e-3) / PEAK_FP32_MFMA
-    else:
-        out["layer_frac_bf16_peak"] = flops / (ms_per_step * 1e-3) / PEAK_BF16
+    out["layer_frac_bf16_peak"] = flops / (ms_per_step * 1e-3) / PEAK_BF16
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_backward(wl, inp, dO_np, args.cpu_budget) if args.backward
                                else cpu_baseline(wl, inp, args.cpu_budget))

@@ -114,7 +114,9 @@ typedef struct {
     int32_t rec_planes; /* bf16 planes per fp32 operand in the state
                            recurrence (update products, Newton-Schulz):
                            1 = bf16, 2 = bf16x2, 3 = bf16x3 (fp32-grade);
-                           0 = default (3 for F32 io, else 1).  F32 io always
+                           0 = default: 3 for MUON and MUON_MOMENTUM (their
+                           Newton-Schulz step amplifies rounding, about x2
+                           per chunk with one plane), else 1.  F32 io always
                            uses 3 planes for every product. */
     uint32_t flags;     /* LACT_NO_RENORM | LACT_QK_PREP */
 } lact_problem;
@@ -129,9 +131,12 @@ size_t lact_workspace_size(const lact_problem* p, int64_t L, int64_t chunk, int3
                            const int64_t* bounds, const uint8_t* flags, int32_t n_chunks);
 
 /*
- * One chunk update (steps: forward products on k and v, SwiGLU backward
+ * One chunk update ("大块测试时训练（LaCT）技术解析" §2.1, eqs. 4-5: the
+ * gradient of the chunk's loss summed over its tokens; optimiser and row
+ * renormalisation of §2.2.1, eqs. 8-10, and momentum of
+ * "LaCT架构核心思想解析" §1.2): forward products on k and v, SwiGLU backward
  * epilogue, weight-gradient contractions over the chunk, optimiser, row
- * renormalisation) for Lc tokens per instance.  k, v are [n, seq_stride, D]
+ * renormalisation, for Lc tokens per instance.  k, v are [n, seq_stride, D]
  * (the first Lc tokens of each instance are used), lr [n, seq_stride, 3],
  * beta [n, seq_stride] (MOMENTUM and MUON_MOMENTUM, else may be NULL).  W1..W3
  * are read and overwritten with the updated weights; M1..M3 likewise for
@@ -145,7 +150,9 @@ lact_status lact_chunk_update(const lact_problem* p, const void* k, const void* 
                               void* stream);
 
 /*
- * Apply the fast weights to Lq queries per instance:
+ * Apply the fast weights to Lq queries per instance
+ * ("大块测试时训练（LaCT）技术解析" §2.1, eq. 2; the SwiGLU memory of
+ * "LaCT：以大分块更新人工智能的临时记忆", "局部注意力与非线性记忆相互补充"):
  * o = W2 (silu(W1 q) * (W3 q)).  q, o are [n, seq_stride, D] (first Lq
  * tokens used).  W1..W3 are read only.
  */
@@ -154,7 +161,11 @@ lact_status lact_apply(const lact_problem* p, const void* q, int64_t Lq, int64_t
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The layer over a whole sequence of L tokens per instance.
+ * The layer over a whole sequence of L tokens per instance: chunks of it
+ * updated and applied in the order that keeps information visible only where
+ * it may be ("LaCT：以大分块更新人工智能的临时记忆", "更新顺序必须遵守信息可见范围";
+ * "LaCT架构核心思想解析" §2.2: apply-then-update for causal language), each
+ * update and apply as in lact_chunk_update and lact_apply.
  * Schedule: if bounds == NULL and flags == NULL, chunks are uniform of
  * `chunk` tokens (the last takes the remainder) and every chunk is
  * UPDATE|APPLY.  Otherwise bounds[0..n_chunks] (host array, bounds[0] = 0,

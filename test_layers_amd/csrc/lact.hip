@@ -172,13 +172,18 @@ lact_status check_device() {
 // --------------------------------------------------------------- precision profiles
 enum Prof { PF32 = 0, PBF16 = 1, PBF16X2 = 2, PBF16X3 = 3 };
 
-Prof profile_of(const lact_problem& p) {
-  if (p.io_dtype == LACT_DTYPE_F32) return PF32;
-  int rp = p.rec_planes == 0 ? 1 : p.rec_planes;
-  return rp == 1 ? PBF16 : rp == 2 ? PBF16X2 : PBF16X3;
-}
 bool uses_momentum(int opt) { return opt == LACT_OPT_MOMENTUM || opt == LACT_OPT_MUON_MOMENTUM; }
 bool uses_ns(int opt) { return opt == LACT_OPT_MUON || opt == LACT_OPT_MUON_MOMENTUM; }
+
+// rec_planes = 0 picks the default: one plane (plain bf16) for GD and
+// momentum, whose recurrence keeps bf16 rounding flat over many chunks; three
+// (fp32 grade) for the Newton-Schulz optimisers, whose recurrence amplifies
+// the rounding of every update (about x2 per chunk with one plane)
+Prof profile_of(const lact_problem& p) {
+  if (p.io_dtype == LACT_DTYPE_F32) return PF32;
+  int rp = p.rec_planes == 0 ? (uses_ns(p.opt) ? 3 : 1) : p.rec_planes;
+  return rp == 1 ? PBF16 : rp == 2 ? PBF16X2 : PBF16X3;
+}
 size_t io_size(const lact_problem& p) { return p.io_dtype == LACT_DTYPE_F32 ? 4 : 2; }
 size_t rec_size(Prof f) { return f == PBF16 ? 2 : 4; }   // update terms storage
 size_t app_size(Prof f) { return f == PF32 ? 4 : 2; }    // gated hidden of the queries

@@ -126,9 +126,15 @@ def problem(n_inst: int, d: int, io_dtype: int, opt: int, rec_planes: int = 0, n
 
 # ----------------------------------------------------------------- raw-pointer calls
 def _sched(bounds, flags):
-    # either may be None: the library reports a half-given schedule itself
+    # either may be None: the library reports a half-given schedule itself.
+    # Both given: the library reads n_chunks + 1 bounds and n_chunks flags,
+    # so their lengths must agree, and flags must fit the uint8 they become.
     if bounds is None and flags is None:
         return None, None, 0, None
+    if bounds is not None and flags is not None and len(bounds) != len(flags) + 1:
+        raise ValueError(f"schedule has {len(bounds)} bounds for {len(flags)} chunks (need chunks + 1)")
+    if flags is not None and any(not 0 <= int(x) <= 255 for x in flags):
+        raise ValueError("schedule flags must lie in 0..255")
     b = None if bounds is None else (ctypes.c_int64 * len(bounds))(*[int(x) for x in bounds])
     f = None if flags is None else (ctypes.c_uint8 * len(flags))(*[int(x) for x in flags])
     nc = len(flags) if flags is not None else len(bounds) - 1
@@ -248,7 +254,9 @@ def _stream(stream):
 def _workspace(nbytes, workspace, device):
     torch = _torch()
     if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not workspace.is_cuda:
+            raise ValueError("workspace must be a contiguous uint8 device tensor")
+        if workspace.numel() < nbytes:
             raise ValueError(f"workspace smaller than the {nbytes} bytes needed")
         return workspace
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)

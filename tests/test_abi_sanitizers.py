@@ -15,9 +15,21 @@ HIPCC = "/opt/rocm/bin/hipcc"
 CLANG = "/opt/rocm/llvm/bin/clang"
 
 
+def _device_visible() -> bool:
+    try:
+        import torch
+    except ImportError:
+        return True   # cannot tell: treat as visible
+    return torch.cuda.device_count() > 0
+
+
 @pytest.mark.skipif(not (os.path.exists(HIPCC) and os.path.exists(CLANG)), reason="ROCm compilers not found")
 @pytest.mark.timeout(600)
 def test_abi_paths_under_asan_and_ubsan(tmp_path):
+    # the driver's valid argument sets carry fake device pointers: they must
+    # stop at the device check, so this runs only where no device is visible
+    if _device_visible():
+        pytest.skip("a device is visible: the driver's fake-pointer calls are not made")
     lib = tmp_path / "liblact_san.so"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
                         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -37,3 +37,34 @@ def test_host_record():
     h = bench.host_info()
     assert set(h) == {"cpu_model", "os_cpu_count", "affinity_cpus", "blas"}
     assert h["os_cpu_count"] >= h["affinity_cpus"] >= 1
+
+
+@pytest.mark.parametrize("cid", sorted(W.WORKLOADS))
+def test_roofline_bound_follows_the_arithmetic_intensity(cid):
+    """The roofline picks the HBM roof for kernels below the ridge point:
+    the fused apply at d = dh = 128 (6 d dh flop against 4 d bytes per query:
+    1.5 dh = 192 flop/B) is HBM-bound, the update products at d = 512 are
+    not, and Newton-Schulz has no algorithmic HBM traffic at all."""
+    wl = W.WORKLOADS[cid]
+    kf = bench.kernel_flops(wl, lact)
+    kb = bench.kernel_bytes(wl, lact, {"out_in_app"})
+    app_ai = (kf[lact.K_APP] + kf[lact.K_OUT]) / kb[lact.K_APP] if kb[lact.K_APP] else None
+    if wl.D == wl.dh == 128 and wl.io_dtype == W.DTYPE_BF16 and app_ai is not None:
+        assert app_ai < bench.RIDGE
+    if wl.D == wl.dh == 512:
+        assert kf[lact.K_UPD] / kb[lact.K_UPD] > bench.RIDGE
+    assert kb[lact.K_NS] == 0.0
+
+
+def test_default_workload_is_the_largest_language_layer():
+    import bench as B
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        args = B.parse()
+    finally:
+        sys.argv = old
+    wl = W.WORKLOADS[args.config]
+    assert wl.name == "lm3b_d512_bf16_muon"
+    lm = [w for w in W.WORKLOADS.values() if w.name.startswith("lm")]
+    assert all(bench.kernel_flops(w, lact)[lact.K_UPD] <= bench.kernel_flops(wl, lact)[lact.K_UPD] for w in lm)

@@ -21,6 +21,7 @@
 
 #include "lact.h"
 #include "lact_direct.hpp"
+#include "lact_planes.hpp"
 #include "lact_backward.hpp"
 
 using namespace lact;
@@ -185,7 +186,12 @@ Prof profile_of(const lact_problem& p) {
   return rp == 1 ? PBF16 : rp == 2 ? PBF16X2 : PBF16X3;
 }
 size_t io_size(const lact_problem& p) { return p.io_dtype == LACT_DTYPE_F32 ? 4 : 2; }
-size_t rec_size(Prof f) { return f == PBF16 ? 2 : 4; }   // update terms storage
+// bf16 planes per Newton-Schulz operand
+int ns_planes(Prof f) { return f == PBF16 ? 1 : f == PBF16X2 ? 2 : 3; }
+// update terms storage per element: bf16, fp32, or two / three bf16 planes
+size_t rec_size(Prof f) { return f == PBF16 ? 2 : f == PBF16X3 ? 6 : 4; }
+// bf16 planes of the update forward's weight operands beyond the snapshot
+int weight_lo_planes(Prof f) { return f == PBF16X2 ? 1 : f == PBF16X3 ? 2 : 0; }
 size_t app_size(Prof f) { return f == PF32 ? 4 : 2; }    // gated hidden of the queries
 
 // --------------------------------------------------------------- plan
@@ -344,6 +350,8 @@ bool fused_apply(const lact_problem& p) { return profile_of(p) != PF32 && p.dh =
 // --------------------------------------------------------------- workspace layout
 struct Ws {
   size_t e = 0, h = 0, part = 0, bpart = 0, snap = 0, u = 0, am = 0, bm = 0, xa = 0, xb = 0, rowsq = 0, total = 0;
+  size_t xp0 = 0, xp1 = 0, ap = 0, bp = 0;   // Newton-Schulz operand planes (d = dh)
+  size_t wlo = 0;                            // weight operand planes 1.. of the next update
   size_t qp = 0, kp = 0;  // pre-processed q / k ([n, prep_rows, D], LACT_QK_PREP)
   int64_t prep_rows = 0;
   size_t snap_slot = 0;   // bytes per snapshot slot (W1, W2, W3, W2^T)
@@ -398,13 +406,23 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   w.part = take(plan.max_upd > 0 ? (size_t)S * mats : 0);
   w.bpart = take(uses_momentum(p.opt) ? n * (size_t)w.max_tt * sizeof(float) : 0);
   w.snap = take(w.snap_slot * (size_t)w.nslots);
+  w.wlo = take(plan.max_upd > 0 ? (size_t)weight_lo_planes(f) * 3 * n * D * Dh * sizeof(bf16_t) : 0);
   if (uses_ns(p.opt) && plan.max_upd > 0) {
-    w.u = take(mats);
-    w.am = take(mats);
-    w.bm = take(mats);
+    // square matrices keep U and A as planes only
+    w.u = take(D == Dh ? 0 : mats);
+    w.am = take(D == Dh ? 0 : mats);
+    w.bm = take(D == Dh ? 0 : mats);
     w.xa = take(mats);
     w.xb = take(mats);
     w.rowsq = take(n * (2 * Dh + D) * sizeof(float));
+    if (D == Dh) {
+      // operand planes of the square products: X (two, alternating), A, B
+      const size_t pl = (size_t)ns_planes(f) * n * 3 * D * Dh * sizeof(bf16_t);
+      w.xp0 = take(pl);
+      w.xp1 = take(pl);
+      w.ap = take(pl);
+      w.bp = take(pl);
+    }
   }
   if (p.flags & LACT_QK_PREP) {
     const size_t el = f == PF32 ? 4 : 2;
@@ -494,20 +512,24 @@ struct Ptrs {
 // plain bf16); PWU: planes of fp32 weights in the update forward when it reads
 // the master copy; TREC/PREC: update terms and Newton-Schulz operands;
 // TAPP/PAPP: gated hidden of the queries.
+// PL > 1: the multi-plane recurrence on direct-load tiles -- the weight
+// operands of the update forward stream as stored bf16 planes (plane 0 the
+// snapshot, planes 1.. written beside it by the optimiser), the update terms
+// and the Newton-Schulz operands are stored as PL bf16 planes.
 template <typename TIO_, int PIO_, typename TS_, int PS_, int PWU_, typename TREC_, int PREC_, typename TAPP_,
-          int PAPP_>
+          int PAPP_, int PL_ = 0>
 struct ProfT {
   using TIO = TIO_;
   using TS = TS_;
   using TREC = TREC_;
   using TAPP = TAPP_;
-  static constexpr int PIO = PIO_, PS = PS_, PWU = PWU_, PREC = PREC_, PAPP = PAPP_;
+  static constexpr int PIO = PIO_, PS = PS_, PWU = PWU_, PREC = PREC_, PAPP = PAPP_, PL = PL_;
   static constexpr bool UPD_FROM_SNAP = (PWU_ == 0);
 };
 using ProfF32 = ProfT<float, 3, float, 3, 3, float, 3, float, 3>;
 using ProfBF16 = ProfT<bf16_t, 1, bf16_t, 1, 0, bf16_t, 1, bf16_t, 1>;
-using ProfBF16X2 = ProfT<bf16_t, 1, bf16_t, 1, 2, float, 2, bf16_t, 1>;
-using ProfBF16X3 = ProfT<bf16_t, 1, bf16_t, 1, 3, float, 3, bf16_t, 1>;
+using ProfBF16X2 = ProfT<bf16_t, 1, bf16_t, 1, 2, float, 2, bf16_t, 1, 2>;
+using ProfBF16X3 = ProfT<bf16_t, 1, bf16_t, 1, 3, float, 3, bf16_t, 1, 3>;
 
 // k-stage depth and buffering that fit the LDS
 constexpr int pick_bk(int planes_sum) { return planes_sum <= 2 ? 64 : 32; }
@@ -588,21 +610,55 @@ constexpr bool direct_fits(int bytes) { return bytes + 1024 <= LDS_MAX; }
 
 template <typename PT, int BJ>
 lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
-  if constexpr (PT::UPD_FROM_SNAP && (BJ == 64 || BJ == 96)) {
+  if constexpr (PT::PL > 1) {
+    // weight planes from the snapshot, update terms stored as planes;
+    // 32-wide stages three deep fit the planes' tiles and the staging
+    if constexpr (BJ == 64) {
+      LACT_LAUNCH((dupd_fwd_kernel<64, 32, 3, false, PT::PL>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
+      HIP_TRY(hipGetLastError());
+      return LACT_OK;
+    } else {
+      return fail(LACT_ERR_UNSUPPORTED, "internal: plane update tile of %d columns", BJ);
+    }
+  } else if constexpr (PT::UPD_FROM_SNAP && (BJ == 64 || BJ == 96)) {
     // with the chunk's queries the ring holds a third token tile: 32-wide
     // stages, three deep, fit the LDS
     if (ua.q != nullptr) LACT_LAUNCH((dupd_fwd_kernel<BJ, 32, 3, true>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
     else LACT_LAUNCH((dupd_fwd_kernel<BJ, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
     HIP_TRY(hipGetLastError());
     return LACT_OK;
+  } else {
+    using TW = typename std::conditional<PT::UPD_FROM_SNAP, typename PT::TS, float>::type;
+    constexpr int PW = PT::UPD_FROM_SNAP ? PT::PS : PT::PWU;
+    constexpr int BKK = pick_bk(PT::PIO + PW);
+    constexpr int words = (2 * PT::PIO * FBT + 3 * PW * BJ) * (BKK + 8);
+    constexpr int ST = pick_stages(words);
+    LACT_LAUNCH((upd_fwd_kernel<typename PT::TIO, PT::PIO, TW, PW, typename PT::TREC, BJ, BKK, ST>),
+                dim3((unsigned)grid), dim3(NT), s, ua);
+    HIP_TRY(hipGetLastError());
+    return LACT_OK;
   }
-  using TW = typename std::conditional<PT::UPD_FROM_SNAP, typename PT::TS, float>::type;
-  constexpr int PW = PT::UPD_FROM_SNAP ? PT::PS : PT::PWU;
-  constexpr int BKK = pick_bk(PT::PIO + PW);
-  constexpr int words = (2 * PT::PIO * FBT + 3 * PW * BJ) * (BKK + 8);
-  constexpr int ST = pick_stages(words);
-  LACT_LAUNCH((upd_fwd_kernel<typename PT::TIO, PT::PIO, TW, PW, typename PT::TREC, BJ, BKK, ST>),
-                     dim3((unsigned)grid), dim3(NT), s, ua);
+}
+
+// weight-gradient contraction with the update terms as PL bf16 planes
+// (second operand: the chunk's k and v, column-k)
+template <int PL>
+lact_status launch_dw_planes(GemmArgs g, int tile, hipStream_t s) {
+  if (g.splits != 1 && g.kps % 64) return fail(LACT_ERR_UNSUPPORTED, "internal: contraction split %lld", (long long)g.kps);
+  if (g.K % 64 && g.kpad < (g.K + 63) / 64 * 64) return fail(LACT_ERR_UNSUPPORTED, "internal: contraction padding");
+  int64_t grid = 0;
+  for (int i = 0; i < g.ngroups; ++i) {
+    const int64_t t = (int64_t)((g.g[i].M + tile - 1) / tile) * ((g.N + tile - 1) / tile) * g.batch * g.splits;
+    if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+    g.g[i].tiles = (int)t;
+    grid += t;
+  }
+  if (grid <= 0) return LACT_OK;
+  if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+  KernelTimer kt(LACT_K_DW, s);
+  constexpr int NST = PL <= 2 ? 3 : 2;   // 48 KB (two planes) or 64 KB stages at 128-wide tiles
+  if (tile == 128) LACT_LAUNCH((dgemm_kernel<false, true, float, 128, 64, NST, PL>), dim3((unsigned)grid), dim3(DG_THREADS), s, g);
+  else LACT_LAUNCH((dgemm_kernel<false, true, float, 64, 64, NST, PL>), dim3((unsigned)grid), dim3(DG_THREADS), s, g);
   HIP_TRY(hipGetLastError());
   return LACT_OK;
 }
@@ -631,6 +687,32 @@ lact_status launch_app_fwd(const AppFwdArgs& aa, int64_t grid, hipStream_t s) {
   constexpr int ST = pick_stages(words);
   LACT_LAUNCH((app_fwd_kernel<typename PT::TIO, PT::PIO, typename PT::TS, PT::PS, typename PT::TAPP, BJ, BKK, ST>),
                      dim3((unsigned)grid), dim3(NT), s, aa);
+  HIP_TRY(hipGetLastError());
+  return LACT_OK;
+}
+
+// plane GEMM (lact_planes.hpp): P planes per operand; B column-k when colk;
+// the result's planes stored when a group has Cp
+template <int P>
+lact_status launch_pgemm(GemmArgs g, bool colk, int kclass, hipStream_t s) {
+  using S = PgSmall;
+  if (g.N % S::BN || g.K % S::BK || g.splits != 1)
+    return fail(LACT_ERR_UNSUPPORTED, "internal: plane product shape %d x %lld", g.N, (long long)g.K);
+  int64_t grid = 0;
+  const int64_t tt = g.N / S::BN;
+  for (int i = 0; i < g.ngroups; ++i) {
+    if (g.g[i].M % S::BM || (g.sym && g.g[i].M != g.N))
+      return fail(LACT_ERR_UNSUPPORTED, "internal: plane product rows %d", g.g[i].M);
+    const int64_t t = (g.sym ? tt * (tt + 1) / 2 : (g.g[i].M / S::BM) * tt) * g.batch;
+    if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+    g.g[i].tiles = (int)t;
+    grid += t;
+  }
+  if (grid <= 0) return LACT_OK;
+  if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+  KernelTimer kt(kclass, s);
+  if (colk) LACT_LAUNCH((pgemm_kernel<P, P, true, P, S>), dim3((unsigned)grid), dim3(S::THREADS), s, g);
+  else LACT_LAUNCH((pgemm_kernel<P, P, false, P, S>), dim3((unsigned)grid), dim3(S::THREADS), s, g);
   HIP_TRY(hipGetLastError());
   return LACT_OK;
 }
@@ -686,12 +768,16 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     }
   }
 
+  // weight operand planes 1.. of the multi-plane recurrence: [PL - 1][W1, W3, W2^T][n, dh, d]
+  constexpr int SP = PT::PL > 1 ? PT::PL : 1;
+  void* wlo = ws + w.wlo;
+  const int64_t wlo_ms = (int64_t)n * DD, wlo_ps = 3 * wlo_ms;
   {
     const int64_t n4 = (int64_t)n * DD / 4;
     KernelTimer kt(LACT_K_SNAP, s);
-    LACT_LAUNCH(snap_kernel<TS>, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), s, P.W1, P.W2, P.W3,
-                       slot(0, 0), slot(0, 1), slot(0, 2), sizeof(TS) == 2 ? slot(0, 3) : nullptr, (int64_t)n * DD, D,
-                       Dh);
+    LACT_LAUNCH((snap_kernel<TS, SP>), dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), s, P.W1, P.W2, P.W3,
+                slot(0, 0), slot(0, 1), slot(0, 2), sizeof(TS) == 2 ? slot(0, 3) : nullptr, (int64_t)n * DD, D,
+                Dh, wlo, wlo_ps, wlo_ms);
     HIP_TRY(hipGetLastError());
   }
 
@@ -746,10 +832,13 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     ua.beta = uses_momentum(p.opt) ? P.beta : nullptr;
     ua.beta_bs = seq_stride;
     ua.bpart = reinterpret_cast<float*>(ws + w.bpart);
-    if (PT::UPD_FROM_SNAP) {
+    if (PT::UPD_FROM_SNAP || PT::PL > 1) {
       ua.W1 = slot(nu, 0);
       ua.W3 = slot(nu, 2);
       ua.W2x = slot(nu, 3);
+      ua.Wlo = wlo;
+      ua.wlo_ps = wlo_ps;
+      ua.wlo_ms = wlo_ms;
     } else {
       ua.W1 = P.W1;
       ua.W3 = P.W3;
@@ -757,6 +846,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     }
     ua.E = ws + w.e;
     ua.ldE = round128(C);
+    ua.e_ps = (int64_t)n * 3 * Dh * ua.ldE;   // plane stride of the update terms (multi-plane)
     ua.D = D;
     ua.Dh = Dh;
     ua.upd_t0 = st.upd_t0;
@@ -833,8 +923,14 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       g.splits = S;
       // the plain-bf16 recurrence keeps its token-split partials in bf16
       // (fp32 accumulation inside each split, fp32 sum of the splits)
-      lact_status r = part16 ? launch_gemm<TREC, PT::PREC, false, TIO, PT::PIO, true, bf16_t>(g, dw_tile(p), LACT_K_DW, s)
-                             : launch_gemm<TREC, PT::PREC, false, TIO, PT::PIO, true, float>(g, dw_tile(p), LACT_K_DW, s);
+      lact_status r;
+      if constexpr (PT::PL > 1) {
+        g.a_ps = ua.e_ps;
+        r = launch_dw_planes<PT::PL>(g, dw_tile(p), s);
+      } else {
+        r = part16 ? launch_gemm<TREC, PT::PREC, false, TIO, PT::PIO, true, bf16_t>(g, dw_tile(p), LACT_K_DW, s)
+                   : launch_gemm<TREC, PT::PREC, false, TIO, PT::PIO, true, float>(g, dw_tile(p), LACT_K_DW, s);
+      }
       if (r) return r;
     }
     OptArgs oa;
@@ -857,6 +953,9 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     oa.snap[1] = slot(nu + 1, 2);
     oa.snap[2] = slot(nu + 1, 1);
     oa.snapT2 = sizeof(TS) == 2 ? slot(nu + 1, 3) : nullptr;
+    oa.wlo = wlo;
+    oa.wlo_ps = wlo_ps;
+    oa.wlo_ms = wlo_ms;
     if (!uses_ns(p.opt)) {
       oa.src = ws + w.part;
       oa.src_ss = (int64_t)n * 3 * DD;
@@ -880,9 +979,18 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
           rm.nbp = nbp;
           rm.inv_len = 1.0f / (float)C;
         }
-        LACT_LAUNCH(reduce_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(NT), s,
-                           reinterpret_cast<const float*>(ws + w.part), (int64_t)n * 3 * DD, S, U, rowsq, rows, D, Dh,
-                           rm);
+        // square matrices: U's operand planes go to the second X plane set,
+        // which the first Newton-Schulz step reads
+        bf16_t* up = D == Dh ? reinterpret_cast<bf16_t*>(ws + w.xp1) : nullptr;
+        const int64_t ups = (int64_t)n * 3 * DD;
+        const dim3 rg((unsigned)((rows + 3) / 4));
+        const float* part = reinterpret_cast<const float*>(ws + w.part);
+        // (the square path keeps U as planes only)
+        float* Uf = up ? nullptr : U;
+        if (!up) LACT_LAUNCH(reduce_rows_kernel<0>, rg, dim3(NT), s, part, ups, S, Uf, rowsq, rows, D, Dh, rm, up, ups);
+        else if (PT::PREC == 1) LACT_LAUNCH(reduce_rows_kernel<1>, rg, dim3(NT), s, part, ups, S, Uf, rowsq, rows, D, Dh, rm, up, ups);
+        else if (PT::PREC == 2) LACT_LAUNCH(reduce_rows_kernel<2>, rg, dim3(NT), s, part, ups, S, Uf, rowsq, rows, D, Dh, rm, up, ups);
+        else LACT_LAUNCH(reduce_rows_kernel<3>, rg, dim3(NT), s, part, ups, S, Uf, rowsq, rows, D, Dh, rm, up, ups);
         HIP_TRY(hipGetLastError());
       }
       float* Am = reinterpret_cast<float*>(ws + w.am);
@@ -891,53 +999,63 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       const float ca = 3.4445f, cb = -4.7750f, cc = 2.0315f;
       const float* Xin = U;
       if (D == Dh) {
-        // every matrix square: one batch of 3n
+        // every matrix square: one batch of 3n, every product on operands
+        // stored as bf16 planes by the product (or the row reduction) before
+        constexpr int PN = PT::PREC;
         const int nb = 3 * n;
-        const int64_t w128 = (int64_t)((D + 127) / 128) * ((D + 127) / 128) * nb;
-        const int tile = gemm_tile(w128);
+        bf16_t* Xp[2] = {reinterpret_cast<bf16_t*>(ws + w.xp0), reinterpret_cast<bf16_t*>(ws + w.xp1)};
+        bf16_t* Ap = reinterpret_cast<bf16_t*>(ws + w.ap);
+        bf16_t* Bp = reinterpret_cast<bf16_t*>(ws + w.bp);
+        const bf16_t* Xpin = Xp[1];   // U's planes
         for (int it = 0; it < p.ns_iters; ++it) {
-          const bool first = it == 0;
+          const bool first = it == 0, last = it + 1 == p.ns_iters;
           float* Xout = X[it & 1];
+          bf16_t* Xpout = Xp[it & 1];
           GemmArgs g = gemm_args();
           g.lda = g.ldb = g.ldc = g.ldcin = D;
           g.a_bs = g.b_bs = g.c_bs = g.cin_bs = DD;
+          g.a_ps = g.b_ps = g.cp_ps = (int64_t)nb * DD;
           g.g[0].M = D;
           g.N = D;
           g.K = g.kps = D;
           g.batch = nb;
-          // A = X X^T (X = s U on the first step); A and B are symmetric, so
-          // only their upper-triangle tiles run (mirrored on store) once
-          // that saves enough tiles (measured: 38.6 -> 31.7 us per product
-          // at D = 512, no gain at D = 128)
-          g.sym = D >= 256;
-          g.g[0].A = Xin;
-          g.g[0].B = Xin;
-          g.g[0].C = Am;
+          // A = X X^T (X = s U on the first step, s = 1 / (||U||_F + 1e-7)
+          // from the row sums of squares); A and B are symmetric, so only
+          // their upper-triangle tiles run, each also storing its mirror.
+          // Every intermediate is kept as planes only (the b A and a X terms
+          // read them back: exact in three planes, 16-bit significands in two,
+          // the precision of the products' operands)
+          g.sym = D > PgSmall::BM;
+          g.g[0].A = Xpin;
+          g.g[0].B = Xpin;
+          g.g[0].Cp = Ap;
           if (first) {
             g.g[0].rowsq = rowsq;
             g.rowsq_bs = D;
             g.rowsq_n = D;
             g.alpha_pow = 2;
           }
-          lact_status r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
+          lact_status r = launch_pgemm<PN>(g, false, LACT_K_NS, s);
           if (r) return r;
-          // B = b A + c A A   (A is symmetric: A A = A A^T)
+          // B = b A + c A A   (A is symmetric: A A = A A^T); only its planes are needed
           g.g[0].rowsq = nullptr;
           g.alpha_pow = 0;
-          g.g[0].A = Am;
-          g.g[0].B = Am;
-          g.g[0].C = Bm;
-          g.g[0].Cin = Am;
+          g.g[0].A = Ap;
+          g.g[0].B = Ap;
+          g.g[0].Cp = Bp;
+          g.g[0].Cinp = Ap;
           g.alpha = cc;
           g.beta = cb;
-          r = launch_gemm<float, PT::PREC, false, float, PT::PREC, false, float>(g, tile, LACT_K_NS, s);
+          r = launch_pgemm<PN>(g, false, LACT_K_NS, s);
           if (r) return r;
-          // X' = a X + B X
+          // X' = a X + B X  (element (n = j, k) of the second operand is X[k, j]:
+          // column-k); the last step's result is read by the optimiser in fp32
           g.sym = 0;
-          g.g[0].A = Bm;
-          g.g[0].B = Xin;  // element (n = j, k) = X[k, j]: column-k source
-          g.g[0].C = Xout;
-          g.g[0].Cin = Xin;
+          g.g[0].A = Bp;
+          g.g[0].B = Xpin;
+          g.g[0].C = last ? Xout : nullptr;
+          g.g[0].Cp = last ? nullptr : Xpout;
+          g.g[0].Cinp = Xpin;
           g.alpha = 1.f;
           g.beta = ca;
           if (first) {
@@ -945,10 +1063,12 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
             g.alpha_pow = 1;
             g.beta_pow = 1;
           }
-          r = launch_gemm<float, PT::PREC, false, float, PT::PREC, true, float>(g, tile, LACT_K_NS, s);
+          r = launch_pgemm<PN>(g, true, LACT_K_NS, s);
           if (r) return r;
           Xin = Xout;
+          Xpin = Xpout;
         }
+        (void)Am;
       } else {
         // W1, W3 are [dh, d] and W2 is [d, dh]: every Gram matrix is the
         // smaller side, r = min(d, dh), so one group uses X X^T and
@@ -1063,10 +1183,10 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
         else if (vpl == 3) LACT_LAUNCH((opt_kernel<TS, 3, bf16_t>), og, dim3(NT), s, oa);
         else LACT_LAUNCH((opt_kernel<TS, 4, bf16_t>), og, dim3(NT), s, oa);
       } else {
-        if (vpl == 1) LACT_LAUNCH((opt_kernel<TS, 1>), og, dim3(NT), s, oa);
-        else if (vpl == 2) LACT_LAUNCH((opt_kernel<TS, 2>), og, dim3(NT), s, oa);
-        else if (vpl == 3) LACT_LAUNCH((opt_kernel<TS, 3>), og, dim3(NT), s, oa);
-        else LACT_LAUNCH((opt_kernel<TS, 4>), og, dim3(NT), s, oa);
+        if (vpl == 1) LACT_LAUNCH((opt_kernel<TS, 1, float, SP>), og, dim3(NT), s, oa);
+        else if (vpl == 2) LACT_LAUNCH((opt_kernel<TS, 2, float, SP>), og, dim3(NT), s, oa);
+        else if (vpl == 3) LACT_LAUNCH((opt_kernel<TS, 3, float, SP>), og, dim3(NT), s, oa);
+        else LACT_LAUNCH((opt_kernel<TS, 4, float, SP>), og, dim3(NT), s, oa);
       }
       HIP_TRY(hipGetLastError());
     }

@@ -273,13 +273,16 @@ __device__ __forceinline__ void dpipeline_il2(int nk, bool wide, I&& issue_one, 
 // consecutive output columns.
 constexpr int DG_THREADS = 512;
 
-template <bool CA, bool CB, typename TC, int T, int BKK, int NST>
+// PA > 1: the first operand is an fp32 quantity stored as PA bf16 planes
+// (plane p at A + p * a_ps, lact_planes.hpp); the second is exact bf16 (an
+// input), so a product sums the PA plane products, smallest plane first.
+template <bool CA, bool CB, typename TC, int T, int BKK, int NST, int PA = 1>
 __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
   constexpr int NW = 8, KH = BKK / 2, NKK = KH / 32;
   using TA = typename std::conditional<CA, DTile<BKK, T, NW, true>, DTile<T, BKK, NW>>::type;
   using TB = typename std::conditional<CB, DTile<BKK, T, NW, true>, DTile<T, BKK, NW>>::type;
-  constexpr int STAGE = TA::BYTES + TB::BYTES;
-  constexpr int LPS = TA::INSTR + TB::INSTR;
+  constexpr int STAGE = PA * TA::BYTES + TB::BYTES;
+  constexpr int LPS = PA * TA::INSTR + TB::INSTR;
   constexpr int FM = T / 32, FN = T / 32;                 // quadrant T/2 x T/2
   constexpr int RED = 4 * FM * FN * 256 * 4;              // k-half reduction buffer (bytes)
   constexpr int SMEM = NST * STAGE > RED ? NST * STAGE : RED;
@@ -316,7 +319,11 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
   const int64_t kmax = g.K - 1;
 
   // column-k operands step BKK rows per stage, row-k operands BKK columns
-  const typename TA::Plan pa = CA ? TA::plan(A, g.lda, kbeg, kmax, m0, wave, lane) : TA::plan(A, g.lda, m0, M - 1, kbeg, wave, lane);
+  typename TA::Plan pa[PA];
+#pragma unroll
+  for (int p = 0; p < PA; ++p)
+    pa[p] = CA ? TA::plan(A + p * g.a_ps, g.lda, kbeg, kmax, m0, wave, lane)
+               : TA::plan(A + p * g.a_ps, g.lda, m0, M - 1, kbeg, wave, lane);
   const typename TB::Plan pb = CB ? TB::plan(B, g.ldb, kbeg, kmax, n0, wave, lane) : TB::plan(B, g.ldb, n0, g.N - 1, kbeg, wave, lane);
   const int64_t sa = CA ? (int64_t)BKK * g.lda * 2 : (int64_t)BKK * 2;
   const int64_t sb = CB ? (int64_t)BKK * g.ldb * 2 : (int64_t)BKK * 2;
@@ -324,13 +331,18 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
     char* st = smem + buf * STAGE;
     const int64_t k0 = kbeg + (int64_t)s * BKK;
     const bool ragged = k0 + BKK - 1 > kmax;   // a column-k stage past the data must clamp rows
-    if (idx < TA::INSTR) {
-      if (CA && ragged) TA::issue_one(st, A, g.lda, k0, kmax, m0, wave, lane, idx);
-      else TA::issue_one(st, pa, s * sa, wave, idx);
+    if (idx < PA * TA::INSTR) {
+#pragma unroll
+      for (int p = 0; p < PA; ++p) {
+        if (idx / TA::INSTR != p) continue;
+        const int i = idx - p * TA::INSTR;
+        if (CA && ragged) TA::issue_one(st + p * TA::BYTES, A + p * g.a_ps, g.lda, k0, kmax, m0, wave, lane, i);
+        else TA::issue_one(st + p * TA::BYTES, pa[p], s * sa, wave, i);
+      }
     } else {
-      const int i = idx - TA::INSTR;
-      if (CB && ragged) TB::issue_one(st + TA::BYTES, B, g.ldb, k0, kmax, n0, wave, lane, i);
-      else TB::issue_one(st + TA::BYTES, pb, s * sb, wave, i);
+      const int i = idx - PA * TA::INSTR;
+      if (CB && ragged) TB::issue_one(st + PA * TA::BYTES, B, g.ldb, k0, kmax, n0, wave, lane, i);
+      else TB::issue_one(st + PA * TA::BYTES, pb, s * sb, wave, i);
     }
   };
 
@@ -344,15 +356,19 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int t = 0; t < NKK; ++t) {
       const int kk = kh * KH + t * 32;
-      bf16x8 af[FM], bfr[FN];
+      bf16x8 af[PA][FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = dfrag<TA, CA>(st, wm * (T / 2) + i * 16, kk, lane);
+      for (int p = 0; p < PA; ++p)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = dfrag<TB, CB>(st + TA::BYTES, wn * (T / 2) + j * 16, kk, lane);
+        for (int i = 0; i < FM; ++i) af[p][i] = dfrag<TA, CA>(st + p * TA::BYTES, wm * (T / 2) + i * 16, kk, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = dfrag<TB, CB>(st + PA * TA::BYTES, wn * (T / 2) + j * 16, kk, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma(bfr[j], af[i], acc[i][j]);
+        for (int p = PA - 1; p >= 0; --p)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma(bfr[j], af[p][i], acc[i][j]);
         hook(t * FM + i, NKK * FM);
       }
     }
@@ -443,18 +459,26 @@ constexpr int upd_w_waves(int bj, int bkk) {
 // Hq = silu(q W1^T) * (q W3^T) to rows h0 + (t - upd_t0) of the Hq buffer
 // (swapped MFMA operands: each lane holds 4 consecutive hidden units of one
 // token, stored as 8 bytes straight from registers).
-template <int BJ, int BKK, int NST, bool WQ = false>
+// P > 1 (the multi-plane recurrence): the weights are P bf16 planes, plane 0
+// the snapshot (W1, W3, W2^T as above), planes 1.. at Wlo + (p - 1) * wlo_ps
+// + m * wlo_ms (m = 0 W1, 1 W3, 2 W2^T); K and V are exact, so each product
+// sums P plane products, smallest plane first.  The update terms are fp32
+// values stored as P bf16 planes (plane p at E + p * e_ps), the operand form
+// of the contraction that follows.
+template <int BJ, int BKK, int NST, bool WQ = false, int P = 1>
 __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   constexpr int NWV = DG_THREADS / WAVE;
   constexpr int WW = upd_w_waves(BJ, BKK);
   constexpr int NX = WQ ? 3 : 2;     // token tiles per stage: k, v (, q)
   using TX = DTile<FBT, BKK, NWV>;   // K, V (, Q): 128 tokens x BKK
-  using TW = DTile<BJ, BKK, WW>;     // W1, W3, W2^T rows: BJ x BKK
-  constexpr int STAGE = NX * TX::BYTES + 3 * TW::BYTES;
-  constexpr int LPS = NX * TX::INSTR + 3 * TW::INSTR;   // loads per stage of a W-loading wave
-  constexpr int LPS_X = NX * TX::INSTR;                 // ... of the other waves
+  using TW = DTile<BJ, BKK, WW>;     // W1, W3, W2^T rows (each plane): BJ x BKK
+  static_assert(!WQ || P == 1, "the queries' products run in the plain-bf16 tile only");
+  constexpr int STAGE = NX * TX::BYTES + 3 * P * TW::BYTES;
+  constexpr int LPS = NX * TX::INSTR + 3 * P * TW::INSTR;   // loads per stage of a W-loading wave
+  constexpr int LPS_X = NX * TX::INSTR;                     // ... of the other waves
   constexpr int FM = 2, FN = BJ / 32;
-  constexpr int ET_BYTES = 3 * BJ * FBT * 2;   // update terms of the tile, staged for full-line stores
+  constexpr int ET_PLANE = 3 * BJ * FBT * 2;   // one plane of the tile's update terms (bf16)
+  constexpr int ET_BYTES = P * ET_PLANE;       // staged for full-line stores
   static_assert(ET_BYTES <= NST * STAGE, "staging fits the ring");
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
   __shared__ float s_red[2];
@@ -493,10 +517,20 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   const typename TX::Plan pk = TX::plan(K, D, t0, tend - 1, 0, wave, lane);
   const typename TX::Plan pv = TX::plan(V, D, t0, tend - 1, 0, wave, lane);
   const typename TX::Plan pq = TX::plan(Q, D, t0, tend - 1, 0, wave, lane);
-  // W1, W3 and W2^T rows: hidden units j0 .. j0 + BJ - 1 (of dh), d long
-  const typename TW::Plan p1 = TW::plan(W1, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
-  const typename TW::Plan p3 = TW::plan(W3, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
-  const typename TW::Plan p2 = TW::plan(W2T, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
+  // W1, W3 and W2^T rows: hidden units j0 .. j0 + BJ - 1 (of dh), d long;
+  // W tile (m, p) of a stage sits at w + (m * P + p) * TW::BYTES
+  typename TW::Plan pw[3][P];
+  {
+    const bf16_t* W0[3] = {W1, W3, W2T};
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const bf16_t* src = p == 0 ? W0[m]
+                                   : reinterpret_cast<const bf16_t*>(a.Wlo) + (p - 1) * a.wlo_ps + m * a.wlo_ms + inst * DD;
+        pw[m][p] = TW::plan(src, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
+      }
+  }
   auto issue_one = [&](int s, int buf, int idx) {
     char* st = smem + buf * STAGE;
     const int64_t off = (int64_t)s * BKK * 2;
@@ -506,9 +540,14 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
     else if (idx < 2 * TX::INSTR) TX::issue_one(st + TX::BYTES, pv, off, wave, idx - TX::INSTR);
     else if (WQ && idx < 3 * TX::INSTR) TX::issue_one(st + 2 * TX::BYTES, pq, off, wave, idx - 2 * TX::INSTR);
     else if (!wload) return;
-    else if (idx < NX * TX::INSTR + TW::INSTR) TW::issue_one(w, p1, off, wave, idx - NX * TX::INSTR);
-    else if (idx < NX * TX::INSTR + 2 * TW::INSTR) TW::issue_one(w + TW::BYTES, p3, off, wave, idx - NX * TX::INSTR - TW::INSTR);
-    else TW::issue_one(w + 2 * TW::BYTES, p2, off, wave, idx - NX * TX::INSTR - 2 * TW::INSTR);
+    else {
+      const int wi = idx - NX * TX::INSTR;
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+          if (wi / TW::INSTR == m * P + p) TW::issue_one(w + (m * P + p) * TW::BYTES, pw[m][p], off, wave, wi % TW::INSTR);
+    }
   };
   f32x4 accA[FM][FN], accB[FM][FN], accG[FM][FN], accQ1[FM][FN], accQ3[FM][FN];
 #pragma unroll
@@ -522,7 +561,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
     constexpr int NSLOT = (BKK / 32) * FM;
 #pragma unroll
     for (int kk = 0; kk < BKK; kk += 32) {
-      bf16x8 fk[FM], fv[FM], fq[FM], f1[FN], f3[FN], f2[FN];
+      bf16x8 fk[FM], fv[FM], fq[FM], f1[P][FN], f3[P][FN], f2[P][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         fk[i] = dfrag_row<TX>(st, wm * 32 + i * 16, kk, lane);
@@ -530,23 +569,27 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
         if constexpr (WQ) fq[i] = dfrag_row<TX>(st + 2 * TX::BYTES, wm * 32 + i * 16, kk, lane);
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        f1[j] = dfrag_row<TW>(w, wn * (BJ / 2) + j * 16, kk, lane);
-        f3[j] = dfrag_row<TW>(w + TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
-        f2[j] = dfrag_row<TW>(w + 2 * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
-      }
+      for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          f1[p][j] = dfrag_row<TW>(w + p * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+          f3[p][j] = dfrag_row<TW>(w + (P + p) * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+          f2[p][j] = dfrag_row<TW>(w + (2 * P + p) * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+        }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          accA[i][j] = mfma(fk[i], f1[j], accA[i][j]);
-          accB[i][j] = mfma(fk[i], f3[j], accB[i][j]);
-          accG[i][j] = mfma(fv[i], f2[j], accG[i][j]);
-          if constexpr (WQ) {
-            accQ1[i][j] = mfma(f1[j], fq[i], accQ1[i][j]);
-            accQ3[i][j] = mfma(f3[j], fq[i], accQ3[i][j]);
+        for (int p = P - 1; p >= 0; --p)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            accA[i][j] = mfma(fk[i], f1[p][j], accA[i][j]);
+            accB[i][j] = mfma(fk[i], f3[p][j], accB[i][j]);
+            accG[i][j] = mfma(fv[i], f2[p][j], accG[i][j]);
+            if constexpr (WQ) {
+              accQ1[i][j] = mfma(f1[p][j], fq[i], accQ1[i][j]);
+              accQ3[i][j] = mfma(f3[p][j], fq[i], accQ3[i][j]);
+            }
           }
-        }
         hook((kk / 32) * FM + i, NSLOT);
       }
     }
@@ -618,25 +661,36 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
       for (int m = 0; m < 3; ++m) {
         const int row = m * BJ + col;
         const int off = row * (FBT * 2) + ((chunk ^ (row & 15)) << 4) + (half << 3);
-        uint2 pk2;
-        pk2.x = pack_bf16x2(terms[m][0], terms[m][1]);
-        pk2.y = pack_bf16x2(terms[m][2], terms[m][3]);
-        *reinterpret_cast<uint2*>(et + off) = pk2;
+        if constexpr (P == 1) {
+          uint2 pk2;
+          pk2.x = pack_bf16x2(terms[m][0], terms[m][1]);
+          pk2.y = pack_bf16x2(terms[m][2], terms[m][3]);
+          *reinterpret_cast<uint2*>(et + off) = pk2;
+        } else {
+          uint32_t h[4][P];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) split_planes<P>(terms[m][r], h[r]);
+#pragma unroll
+          for (int p = 0; p < P; ++p)
+            *reinterpret_cast<uint2*>(et + p * ET_PLANE + off) =
+                make_uint2(h[0][p] | (h[1][p] << 16), h[2][p] | (h[3][p] << 16));
+        }
       }
     }
   }
   __syncthreads();
-  // E rows U1 | U3 | U2-terms, token-fastest; the tile's 128 tokens lie
-  // inside the row's ldE (zero terms past the chunk end)
+  // E rows U1 | U3 | U2-terms, token-fastest (one set per plane); the tile's
+  // 128 tokens lie inside the row's ldE (zero terms past the chunk end)
   bf16_t* E = reinterpret_cast<bf16_t*>(a.E) + inst * 3 * (int64_t)Dh * a.ldE + (t0 - a.upd_t0);
   constexpr int ROWS = 3 * BJ;
-  for (int r0 = 0; r0 < ROWS; r0 += 4 * NWV) {
-    const int row = r0 + wave * 4 + (lane >> 4);
-    if (row < ROWS) {
+  for (int r0 = 0; r0 < P * ROWS; r0 += 4 * NWV) {
+    const int prow = r0 + wave * 4 + (lane >> 4);
+    if (prow < P * ROWS) {
+      const int p = prow / ROWS, row = prow % ROWS;
       const int c = lane & 15;
-      const uint4 v = *reinterpret_cast<const uint4*>(et + row * (FBT * 2) + ((c ^ (row & 15)) << 4));
+      const uint4 v = *reinterpret_cast<const uint4*>(et + p * ET_PLANE + row * (FBT * 2) + ((c ^ (row & 15)) << 4));
       const int m = row / BJ, col = row % BJ;
-      *reinterpret_cast<uint4*>(E + (int64_t)(m * Dh + j0 + col) * a.ldE + c * 8) = v;
+      *reinterpret_cast<uint4*>(E + p * a.e_ps + (int64_t)(m * Dh + j0 + col) * a.ldE + c * 8) = v;
     }
   }
 }

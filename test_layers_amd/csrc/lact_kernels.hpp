@@ -61,6 +61,11 @@ struct UpdFwdArgs {
   void* H;
   int64_t h_bs;
   int64_t h0;
+  // multi-plane recurrence (direct-load tile): weight planes 1.. and the
+  // plane stride of the stored update terms
+  const void* Wlo;       // [P - 1][3: W1, W3, W2^T][n, dh, d] bf16
+  int64_t wlo_ps, wlo_ms;
+  int64_t e_ps;
 };
 
 constexpr int FBT = 128;  // tokens per forward tile
@@ -311,6 +316,8 @@ struct GemmGroup {
   const void* A;
   const void* B;
   void* C;
+  void* Cp;              // optional (plane GEMM): C also stored as bf16 planes, plane p at Cp + p * cp_ps
+  const void* Cinp;      // optional (plane GEMM): Cin given as bf16 planes (layout of Cp) instead of fp32
   const float* rs;       // optional: row m of C is scaled by silu(rs[b * rs_bs + m])
   const float* Cin;      // optional: C += beta * Cin (batch stride cin_bs, row stride ldcin)
   const float* rowsq;    // optional Frobenius scale source (see GemmArgs), this group's first row
@@ -342,6 +349,8 @@ struct GemmArgs {
   // symmetric matrices): only tiles on or above the diagonal run, and the
   // off-diagonal ones also store their mirror image
   int sym;
+  // plane GEMM: elements between the bf16 planes of A, B and of the stored C planes
+  int64_t a_ps, b_ps, cp_ps;
 };
 
 template <typename TA, int PA, bool CA, typename TB, int PB, bool CB, typename TC, int BM, int BN, int BK, int STAGES>
@@ -482,9 +491,13 @@ struct RowsMomentum {
   float inv_len;
 };
 
+// PO > 0: U is also stored as PO bf16 planes (plane p at Up + p * up_ps, the
+// layout of U), the operand form of the plane products that follow; U (fp32)
+// may then be null.
+template <int PO>
 __global__ __launch_bounds__(NT) void reduce_rows_kernel(const float* P, int64_t p_ss, int splits,
                                                         float* U, float* rowsq, int64_t rows, int D, int Dh,
-                                                        RowsMomentum rm) {
+                                                        RowsMomentum rm, bf16_t* Up, int64_t up_ps) {
   // per instance the stacked blocks U1 [dh, d], U3 [dh, d], U2 [d, dh]:
   // 2 dh + d rows, d long in the first two blocks and dh long in the third
   const int lane = threadIdx.x & 63;
@@ -523,7 +536,17 @@ __global__ __launch_bounds__(NT) void reduce_rows_kernel(const float* P, int64_t
       u = make_float4(bm * m.x - u.x, bm * m.y - u.y, bm * m.z - u.z, bm * m.w - u.w);
       reinterpret_cast<float4*>(Mrow)[e4] = u;
     }
-    reinterpret_cast<float4*>(U + base)[e4] = u;
+    if (U) reinterpret_cast<float4*>(U + base)[e4] = u;
+    if constexpr (PO > 0) {
+      const float uv[4] = {u.x, u.y, u.z, u.w};
+      uint32_t h[4][PO];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) split_planes<PO>(uv[r], h[r]);
+#pragma unroll
+      for (int p = 0; p < PO; ++p)
+        *reinterpret_cast<uint2*>(Up + p * up_ps + base + 4 * e4) =
+            make_uint2(h[0][p] | (h[1][p] << 16), h[2][p] | (h[3][p] << 16));
+    }
     ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
   }
   ss = wave_sum(ss);
@@ -556,6 +579,10 @@ struct OptArgs {
   // bf16, the transposed W2 snapshot used by the next update's forward
   void* snap[3];
   void* snapT2;
+  // multi-plane recurrence: bf16 planes 1.. of the next update's weight
+  // operands W1, W3, W2^T (plane 0 is the snapshot), [SP - 1][3][n, dh, d]
+  void* wlo;
+  int64_t wlo_ps, wlo_ms;
 };
 
 constexpr int OPT_MAXS = 4;               // partials loaded per batch
@@ -568,9 +595,9 @@ __host__ __device__ constexpr int opt_rpw(int L) { return L <= 256 ? 4 : L <= 51
 // float4 (always in bounds) and drop it, so every load is a plain 16-byte
 // load issued before any arithmetic consumes it.  Row sums of squares are
 // wave reductions per row.
-template <typename TS, int VPL, typename TP = float>
+template <typename TS, int VPL, typename TP = float, int SP = 1>
 __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
-  __shared__ uint16_t s_t[4096];   // transposed-snapshot staging: rows_wg x L bf16 (rows_wg * L <= 4096)
+  __shared__ uint16_t s_t[SP][4096];   // transposed-snapshot staging per plane: rows_wg x L bf16 (rows_wg * L <= 4096)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = a.L, R = a.R, rpw = a.rpw, rows_wg = 4 * rpw;
   const int rblocks = R / rows_wg;
@@ -687,11 +714,24 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
     const float yy[4] = {y.x, y.y, y.z, y.w};
     if (snap) store4(snap + (int64_t)ix[i] * 4, yy);
     if constexpr (sizeof(TS) == 2) {
+      uint32_t h[4][SP];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split_planes<SP>(yy[q], h[q]);
+      if constexpr (SP > 1) {
+        if (mat < 2) {
+          uint16_t* lo = reinterpret_cast<uint16_t*>(a.wlo) + mat * a.wlo_ms + inst * DD + base4 * 4 + (int64_t)ix[i] * 4;
+#pragma unroll
+          for (int p = 1; p < SP; ++p)
+            *reinterpret_cast<uint2*>(lo + (p - 1) * a.wlo_ps) = make_uint2(h[0][p] | (h[1][p] << 16), h[2][p] | (h[3][p] << 16));
+        }
+      }
       if (stage_t) {
         const int lrow = wave * rpw + rid[i];
         const int c = 4 * (ix[i] - rid[i] * nv);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s_t[(c + q) * rows_wg + lrow] = (uint16_t)f2bf(yy[q]);
+        for (int p = 0; p < SP; ++p)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s_t[p][(c + q) * rows_wg + lrow] = (uint16_t)h[q][p];
       }
     }
   }
@@ -700,17 +740,23 @@ __global__ __launch_bounds__(NT) void opt_kernel(OptArgs a) {
       // W2^T[j, r0 .. r0 + rows_wg - 1] (W2^T is [dh, d]: L rows of R):
       // rows_wg contiguous bf16 per j
       __syncthreads();
-      uint16_t* T = reinterpret_cast<uint16_t*>(a.snapT2) + inst * DD + rb * rows_wg;
-      if (rows_wg == 4) {
-        for (int j = tid; j < L; j += NT)
-          *reinterpret_cast<uint2*>(T + (int64_t)j * R) = *reinterpret_cast<const uint2*>(s_t + j * 4);
-      } else if (rows_wg == 8) {
-        for (int j = tid; j < L; j += NT)
-          *reinterpret_cast<uint4*>(T + (int64_t)j * R) = *reinterpret_cast<const uint4*>(s_t + j * 8);
-      } else {
-        for (int j = tid; j < L; j += NT) {
-          *reinterpret_cast<uint4*>(T + (int64_t)j * R) = *reinterpret_cast<const uint4*>(s_t + j * 16);
-          *reinterpret_cast<uint4*>(T + (int64_t)j * R + 8) = *reinterpret_cast<const uint4*>(s_t + j * 16 + 8);
+#pragma unroll
+      for (int p = 0; p < SP; ++p) {
+        uint16_t* T = (p == 0 ? reinterpret_cast<uint16_t*>(a.snapT2)
+                              : reinterpret_cast<uint16_t*>(a.wlo) + (p - 1) * a.wlo_ps + 2 * a.wlo_ms) +
+                      inst * DD + rb * rows_wg;
+        const uint16_t* st = s_t[p];
+        if (rows_wg == 4) {
+          for (int j = tid; j < L; j += NT)
+            *reinterpret_cast<uint2*>(T + (int64_t)j * R) = *reinterpret_cast<const uint2*>(st + j * 4);
+        } else if (rows_wg == 8) {
+          for (int j = tid; j < L; j += NT)
+            *reinterpret_cast<uint4*>(T + (int64_t)j * R) = *reinterpret_cast<const uint4*>(st + j * 8);
+        } else {
+          for (int j = tid; j < L; j += NT) {
+            *reinterpret_cast<uint4*>(T + (int64_t)j * R) = *reinterpret_cast<const uint4*>(st + j * 16);
+            *reinterpret_cast<uint4*>(T + (int64_t)j * R + 8) = *reinterpret_cast<const uint4*>(st + j * 16 + 8);
+          }
         }
       }
     }
@@ -783,9 +829,12 @@ __global__ __launch_bounds__(NT) void qk_prep_kernel(QkPrepArgs a) {
 
 // =========================================================================
 // snapshot of caller weights: fp32 -> TS (natural) and, for bf16, W2^T
-template <typename TS>
+// SP > 1: also the weight operands' bf16 planes 1 .. SP - 1 (W1, W3 natural,
+// W2^T) at wlo + (p - 1) * wlo_ps + m * wlo_ms, m = 0 W1, 1 W3, 2 W2^T.
+template <typename TS, int SP = 1>
 __global__ __launch_bounds__(NT) void snap_kernel(const float* W1, const float* W2, const float* W3, void* s1,
-                                                   void* s2, void* s3, void* sT2, int64_t n_dd, int D, int Dh) {
+                                                   void* s2, void* s3, void* sT2, int64_t n_dd, int D, int Dh,
+                                                   void* wlo, int64_t wlo_ps, int64_t wlo_ms) {
   const int64_t i4 = (int64_t)blockIdx.x * NT + threadIdx.x;   // float4 index
   if (i4 * 4 >= n_dd) return;
   const float* src[3] = {W1, W2, W3};
@@ -795,6 +844,17 @@ __global__ __launch_bounds__(NT) void snap_kernel(const float* W1, const float* 
     const float4 x = reinterpret_cast<const float4*>(src[m])[i4];
     const float v[4] = {x.x, x.y, x.z, x.w};
     store4(reinterpret_cast<TS*>(dst[m]) + i4 * 4, v);
+    if constexpr (sizeof(TS) == 2 && SP > 1) {
+      if (m != 1) {   // W1 (plane set 0), W3 (plane set 1)
+        uint32_t h[4][SP];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) split_planes<SP>(v[q], h[q]);
+        uint16_t* lo = reinterpret_cast<uint16_t*>(wlo) + (m == 0 ? 0 : wlo_ms) + i4 * 4;
+#pragma unroll
+        for (int p = 1; p < SP; ++p)
+          *reinterpret_cast<uint2*>(lo + (p - 1) * wlo_ps) = make_uint2(h[0][p] | (h[1][p] << 16), h[2][p] | (h[3][p] << 16));
+      }
+    }
   }
   if constexpr (sizeof(TS) == 2) {
     if (sT2) {
@@ -806,8 +866,18 @@ __global__ __launch_bounds__(NT) void snap_kernel(const float* W1, const float* 
       const int64_t inst = e / DD, rem = e % DD;
       const int r = (int)(rem / Dh), c = (int)(rem % Dh);
       uint16_t* T = reinterpret_cast<uint16_t*>(sT2) + inst * DD;
+      uint32_t h[4][SP];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) T[(int64_t)(c + q) * D + r] = (uint16_t)f2bf(v[q]);
+      for (int q = 0; q < 4; ++q) split_planes<SP>(v[q], h[q]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) T[(int64_t)(c + q) * D + r] = (uint16_t)h[q][0];
+      if constexpr (SP > 1) {
+        uint16_t* TL = reinterpret_cast<uint16_t*>(wlo) + 2 * wlo_ms + inst * DD;
+#pragma unroll
+        for (int p = 1; p < SP; ++p)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) TL[(p - 1) * wlo_ps + (int64_t)(c + q) * D + r] = (uint16_t)h[q][p];
+      }
     }
   }
 }

@@ -212,7 +212,7 @@ def cpu_baseline(wl, inp, budget):
                       f"whole {wl.L}-token sequence each, {dt:.1f} s, numpy fp64", "host": host_info()}
 
 
-SRC_FILES = ("lact.hip", "lact_device.hpp", "lact_kernels.hpp", "lact_direct.hpp", "lact_backward.hpp",
+SRC_FILES = ("lact.hip", "lact_device.hpp", "lact_kernels.hpp", "lact_direct.hpp", "lact_planes.hpp", "lact_backward.hpp",
              "lact_backward_host.hpp")
 
 

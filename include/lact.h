@@ -256,6 +256,29 @@ lact_status lact_layer_backward(const lact_problem* p, const void* q, const void
                                 float* dW1, float* dW2, float* dW3, float* dM1, float* dM2,
                                 float* dM3, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Allocation-free variant of lact_layer_forward, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid it.  Same arguments and semantics as
+ * lact_layer_forward without the workspace: the library's own device scratch
+ * array takes its place.  That array has LACT_NOALLOC_SCRATCH_BYTES bytes,
+ * one copy per device (created when the library's code is loaded on the
+ * device, held until the process ends); a problem whose
+ * lact_workspace_size exceeds it is rejected with
+ * LACT_ERR_WORKSPACE_TOO_SMALL before any device work.  The call allocates
+ * and frees nothing.  Every call on a device shares that device's array:
+ * calls that overlap on one device (several streams or host threads at
+ * once) race and must be ordered by the caller, e.g. on one stream.  No
+ * result depends on the array's previous contents.
+ */
+#define LACT_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+lact_status lact_layer_forward_noalloc(const lact_problem* p, const void* q, const void* k,
+                                       const void* v, const float* lr, const float* beta, int64_t L,
+                                       int64_t chunk, int32_t order, const int64_t* bounds,
+                                       const uint8_t* flags, int32_t n_chunks, float* W1, float* W2,
+                                       float* W3, float* M1, float* M2, float* M3, void* o,
+                                       void* stream);
+
 /* Static text for a status code. */
 const char* lact_status_str(lact_status s);
 

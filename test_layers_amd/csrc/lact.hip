@@ -1362,11 +1362,39 @@ size_t lact_workspace_size(const lact_problem* p, int64_t L, int64_t chunk, int3
 }  // extern "C"
 
 namespace {
+// ------------------------------------------------------------- allocation-free entry point
+// Device scratch of lact_layer_forward_noalloc, for callers that cannot
+// allocate (HIP graph capture, serving loops): one copy per device, created
+// when the library's code object is loaded on that device and held until
+// the process ends.  Host code never uses the array's name as an address (it
+// is a host-side stand-in): the device address is taken once per device with
+// hipGetSymbolAddress, with that device current, and only it is passed on.
+static __device__ __align__(256) char scratch[LACT_NOALLOC_SCRATCH_BYTES];
+
+lact_status scratch_address(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> addr;   // per device
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(LACT_ERR_NO_DEVICE, "hipGetDevice failed");
+  std::lock_guard<std::mutex> g(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || a == nullptr)
+      return fail(LACT_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
+    addr[dev] = a;
+  }
+  *out = addr[dev];
+  return LACT_OK;
+}
+
+// ws == nullptr with use_scratch: the workspace is the device's scratch array
 lact_status layer_forward_impl(const lact_problem* p, const void* q, const void* k, const void* v, const float* lr,
                                const float* beta, const float* oz, bool scaled, int64_t L, int64_t chunk,
                                int32_t order, const int64_t* bounds, const uint8_t* flags, int32_t n_chunks,
                                float* W1, float* W2, float* W3, float* M1, float* M2, float* M3, void* o, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               size_t ws_bytes, void* stream, bool use_scratch = false) {
   g_err.clear();
   lact_status r = validate_problem(p);
   if (r) return r;
@@ -1398,11 +1426,21 @@ lact_status layer_forward_impl(const lact_problem* p, const void* q, const void*
     }
   }
   Ws w = layout(*p, plan);
-  if (w.total > 0) NEED(ws, 256);
-  if (ws_bytes < w.total)
-    return fail(LACT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  if (use_scratch) {
+    if (w.total > LACT_NOALLOC_SCRATCH_BYTES)
+      return fail(LACT_ERR_WORKSPACE_TOO_SMALL, "the problem needs %zu bytes of workspace; the allocation-free "
+                  "entry point has %zu (LACT_NOALLOC_SCRATCH_BYTES)", w.total, (size_t)LACT_NOALLOC_SCRATCH_BYTES);
+  } else {
+    if (w.total > 0) NEED(ws, 256);
+    if (ws_bytes < w.total)
+      return fail(LACT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  }
   r = check_device();
   if (r) return r;
+  if (use_scratch) {
+    r = scratch_address(&ws);
+    if (r) return r;
+  }
   Ptrs P;
   P.q = q;
   P.k = k;
@@ -1439,6 +1477,14 @@ lact_status lact_layer_forward_scaled(const lact_problem* p, const void* q, cons
                                       void* ws, size_t ws_bytes, void* stream) {
   return layer_forward_impl(p, q, k, v, lr, beta, oz, true, L, chunk, order, bounds, flags, n_chunks, W1, W2, W3, M1,
                             M2, M3, o, ws, ws_bytes, stream);
+}
+
+lact_status lact_layer_forward_noalloc(const lact_problem* p, const void* q, const void* k, const void* v,
+                                       const float* lr, const float* beta, int64_t L, int64_t chunk, int32_t order,
+                                       const int64_t* bounds, const uint8_t* flags, int32_t n_chunks, float* W1,
+                                       float* W2, float* W3, float* M1, float* M2, float* M3, void* o, void* stream) {
+  return layer_forward_impl(p, q, k, v, lr, beta, nullptr, false, L, chunk, order, bounds, flags, n_chunks, W1, W2,
+                            W3, M1, M2, M3, o, nullptr, 0, stream, true);
 }
 
 lact_status lact_chunk_update(const lact_problem* p, const void* k, const void* v, const float* lr, const float* beta,

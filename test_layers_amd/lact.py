@@ -41,8 +41,10 @@ K_NAMES = {K_UPD: "update_fwd", K_APP: "apply_fwd", K_OUT: "apply_out", K_DW: "d
            K_BWD_ELEM: "bwd_elem"}
 
 EXPORTS = ["lact_workspace_size", "lact_chunk_update", "lact_apply", "lact_layer_forward",
-           "lact_layer_forward_scaled", "lact_backward_workspace_size", "lact_layer_backward",
-           "lact_status_str", "lact_last_error", "lact_timing_enable", "lact_timing_read"]
+           "lact_layer_forward_scaled", "lact_layer_forward_noalloc", "lact_backward_workspace_size",
+           "lact_layer_backward", "lact_status_str", "lact_last_error", "lact_timing_enable", "lact_timing_read"]
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # LACT_NOALLOC_SCRATCH_BYTES
 
 
 class LactError(RuntimeError):
@@ -92,6 +94,9 @@ def lib() -> ctypes.CDLL:
     L.lact_layer_forward_scaled.restype = i32
     L.lact_layer_forward_scaled.argtypes = [P, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32,
                                             vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.lact_layer_forward_noalloc.restype = i32
+    L.lact_layer_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32,
+                                             vp, vp, vp, vp, vp, vp, vp, vp]
     L.lact_backward_workspace_size.restype = sz
     L.lact_backward_workspace_size.argtypes = [P, i64, i64, i32, vp, vp, i32]
     L.lact_layer_backward.restype = i32
@@ -163,6 +168,13 @@ def layer_forward_scaled_ptr(p: Problem, q, k, v, lr, beta, oz, L, chunk, order,
     bp, fp, nc, _keep = _sched(bounds, flags)
     return lib().lact_layer_forward_scaled(ctypes.byref(p), q, k, v, lr, beta, oz, L, chunk, order,
                                            bp, fp, nc, W1, W2, W3, M1, M2, M3, o, ws, ws_bytes, stream)
+
+
+def layer_forward_noalloc_ptr(p: Problem, q, k, v, lr, beta, L, chunk, order, bounds, flags,
+                              W1, W2, W3, M1, M2, M3, o, stream) -> int:
+    bp, fp, nc, _keep = _sched(bounds, flags)
+    return lib().lact_layer_forward_noalloc(ctypes.byref(p), q, k, v, lr, beta, L, chunk, order, bp, fp, nc,
+                                            W1, W2, W3, M1, M2, M3, o, stream)
 
 
 def backward_workspace_size(p: Problem, L: int, chunk: int = 0, order: int = 0,

@@ -413,3 +413,37 @@ def test_binding_workspace_must_be_bytes():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError, match="uint8"):
         lact._workspace(1024, torch.zeros(1024, dtype=torch.float32), "cpu")
+
+
+def noalloc(p, L=512, chunk=128, order=0, bounds=None, flags=None, **ptrs):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lr=FAKE, beta=FAKE, W1=FAKE, W2=FAKE, W3=FAKE,
+             M1=FAKE, M2=FAKE, M3=FAKE, o=FAKE)
+    a.update(ptrs)
+    return lact.layer_forward_noalloc_ptr(p, a["q"], a["k"], a["v"], a["lr"], a["beta"], L, chunk, order,
+                                          bounds, flags, a["W1"], a["W2"], a["W3"], a["M1"], a["M2"], a["M3"],
+                                          a["o"], None)
+
+
+def test_noalloc_validation():
+    """The allocation-free entry point validates like lact_layer_forward and
+    rejects, before any device work, a problem whose workspace exceeds its
+    scratch array."""
+    assert noalloc(P(n_inst=0)) == lact.OK
+    assert noalloc(P(d=96)) == lact.ERR_UNSUPPORTED
+    assert noalloc(P(), k=FAKE + 2) == lact.ERR_INVALID_ARG
+    big = P(n_inst=6, d=512, opt=lact.OPT_MUON, rec_planes=2)
+    assert lact.workspace_size(big, 32768, 4096) > lact.NOALLOC_SCRATCH_BYTES
+    assert noalloc(big, L=32768, chunk=4096) == lact.ERR_WORKSPACE_TOO_SMALL
+    assert "LACT_NOALLOC_SCRATCH_BYTES" in lact.last_error()
+
+
+@device_free
+def test_noalloc_valid_call_reports_no_device():
+    assert lact.workspace_size(P(), 512, 128) <= lact.NOALLOC_SCRATCH_BYTES
+    assert noalloc(P()) == lact.ERR_NO_DEVICE
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    txt = open(HEADER).read()
+    m = re.search(r"#define LACT_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == lact.NOALLOC_SCRATCH_BYTES

@@ -279,12 +279,16 @@ void dw_split(const lact_problem& p, int64_t C, int& S, int64_t& kps) {
   const int64_t tiles = (int64_t)((3 * p.dh + bt - 1) / bt) * (p.d / bt) * std::max(1, p.n_inst);
   // Split count: the filled fraction of the last round of (one-per-CU)
   // workgroups, minus a charge per split for the partial set it writes and
-  // the optimiser re-reads (3D^2 fp32 per instance, against ~5DC bf16 of E
-  // and k, v traffic: ~0.2 D / C); ties go to instances x splits a multiple
-  // of the 8 XCDs (every XCD then receives whole (instance, split) groups).
+  // the optimiser (or the Newton-Schulz row reduction) re-reads: 3 d dh per
+  // instance, bf16 partials in the plain-bf16 recurrence (~0.2 d / C
+  // against the E and k, v traffic), fp32 otherwise (measured on the 3B-LM
+  // layer's two-plane contraction: 3 splits 104 us, 2: 107, 4: 110, 6: 127,
+  // i.e. ~0.5 d / C); ties go to instances x splits a multiple of the 8
+  // XCDs (every XCD then receives whole (instance, split) groups).
   const int64_t n = std::max(1, p.n_inst);
   const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, C / 256));
-  const double charge = 0.2 * (double)p.d / (double)std::max<int64_t>(1, C);
+  const bool part16 = profile_of(p) == PBF16 && !uses_ns(p.opt);
+  const double charge = (part16 ? 0.2 : 0.5) * (double)p.d / (double)std::max<int64_t>(1, C);
   int64_t s = 1;
   double best = -1e9;
   for (int64_t c = 1; c <= smax; ++c) {
@@ -693,9 +697,8 @@ lact_status launch_app_fwd(const AppFwdArgs& aa, int64_t grid, hipStream_t s) {
 
 // plane GEMM (lact_planes.hpp): P planes per operand; B column-k when colk;
 // the result's planes stored when a group has Cp
-template <int P>
+template <int P, class S = PgSmall>
 lact_status launch_pgemm(GemmArgs g, bool colk, int kclass, hipStream_t s) {
-  using S = PgSmall;
   if (g.N % S::BN || g.K % S::BK || g.splits != 1)
     return fail(LACT_ERR_UNSUPPORTED, "internal: plane product shape %d x %lld", g.N, (long long)g.K);
   int64_t grid = 0;

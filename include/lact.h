@@ -40,9 +40,17 @@
  * Memory: every tensor argument is a caller-owned DEVICE pointer, contiguous,
  * innermost dimension fastest; host arrays (bounds, flags) are read during
  * the call only.  The library allocates no device memory, keeps no pointer
- * after returning, and frees nothing.  All device work is enqueued on
- * `stream` (a hipStream_t; NULL = the legacy default stream) without any
- * host synchronisation; completion is observed through the stream.
+ * after returning, and frees nothing.  All device work is enqueued
+ * asynchronously, without any host synchronisation, on `stream` (a
+ * hipStream_t; NULL = the legacy default stream) and on two helper streams
+ * the library creates once per device (default priority, kept until the
+ * process ends): the second half of each Newton-Schulz batch and the
+ * deferred applies run there, ordered after the caller's stream by events
+ * and joined back to it before the call's work on `stream` ends.
+ * Completion is therefore observed through `stream`, and a HIP graph
+ * captured from `stream` contains the helper streams' work; while such a
+ * capture is in progress no other thread may call the library on the same
+ * device.
  *
  * Layouts (n = n_inst, D = d, Dh = dh):
  *   q, k, v, o : [n, L, D]   io_dtype (F32 or BF16)

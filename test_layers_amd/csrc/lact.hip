@@ -695,6 +695,51 @@ lact_status launch_app_fwd(const AppFwdArgs& aa, int64_t grid, hipStream_t s) {
   return LACT_OK;
 }
 
+// --------------------------------------------------------------- helper streams
+// Work off the recurrence's critical path runs on two library streams per
+// device (default priority, created on first use, kept until the process
+// ends): the second half of every Newton-Schulz batch, and the deferred
+// applies, each chunk's as soon as the snapshot it reads exists.  They are
+// tied to the caller's stream by events in both directions, so a call still
+// completes, as seen from the caller's stream, when the caller's stream says
+// so, and a graph captured from the caller's stream captures them too.
+// The mutex is held while a call enqueues its work (host side only).
+struct DevAux {
+  hipStream_t ns = nullptr, app = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, ready = nullptr, done = nullptr;
+};
+std::mutex& aux_mutex() {
+  static std::mutex m;
+  return m;
+}
+// call with aux_mutex() held
+lact_status dev_aux(DevAux** out) {
+  static std::vector<DevAux> aux;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(LACT_ERR_NO_DEVICE, "hipGetDevice failed");
+  if ((int)aux.size() <= dev) aux.resize(dev + 1);
+  DevAux& a = aux[dev];
+  if (a.ns == nullptr) {
+    DevAux x;
+    if (hipStreamCreateWithFlags(&x.ns, hipStreamNonBlocking) != hipSuccess ||
+        hipStreamCreateWithFlags(&x.app, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&x.ready, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&x.done, hipEventDisableTiming) != hipSuccess)
+      return fail(LACT_ERR_HIP, "creating the helper streams and events failed");
+    a = x;
+  }
+  *out = &a;
+  return LACT_OK;
+}
+// `to` waits for everything enqueued on `from` so far
+lact_status stream_after(hipStream_t to, hipStream_t from, hipEvent_t ev) {
+  HIP_TRY(hipEventRecord(ev, from));
+  HIP_TRY(hipStreamWaitEvent(to, ev, 0));
+  return LACT_OK;
+}
+
 // plane GEMM (lact_planes.hpp): P planes per operand; B column-k when colk;
 // the result's planes stored when a group has Cp
 template <int P, class S = PgSmall>
@@ -729,6 +774,9 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
   using TAPP = typename PT::TAPP;
   const int n = p.n_inst, D = p.d, Dh = p.dh;
   if (n == 0) return LACT_OK;
+  std::lock_guard<std::mutex> aux_lock(aux_mutex());
+  DevAux* aux = nullptr;
+  if (lact_status r = dev_aux(&aux)) return r;
   const bool part16 = PT::PREC == 1 && !uses_ns(p.opt);
   const int64_t DD = (int64_t)D * Dh;   // elements per fast-weight matrix
   const int64_t x_bs = seq_stride * D;
@@ -815,6 +863,143 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       if (st.upd_len > 0) ++u;
     }
   }
+
+  // Applies of groups [ga, gb) on stream st (groups batched MAXG to a launch).
+  auto apply_groups = [&](size_t ga, size_t gb, hipStream_t st) -> lact_status {
+    if (fused_apply(p)) {
+      for (size_t g0 = ga; g0 < gb; g0 += MAXG) {
+        const int ng = (int)std::min<size_t>(MAXG, gb - g0);
+        AppFwdArgs aa;
+        memset(&aa, 0, sizeof(aa));
+        aa.ngroups = ng;
+        aa.q = qx;
+        aa.q_bs = q_bs;
+        aa.x_bs = x_bs;
+        aa.o = P.o;
+        aa.oz = P.oz;
+        aa.oz_bs = seq_stride;
+        aa.D = D;
+        aa.Dh = Dh;
+        int64_t grid = 0;
+        for (int i = 0; i < ng; ++i) {
+          aa.g[i] = groups[g0 + i];
+          const int64_t t = ((aa.g[i].len + FBT - 1) / FBT) * n;
+          if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+          aa.g[i].tiles = (int)t;
+          grid += t;
+        }
+        if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+        KernelTimer kt(LACT_K_APP, st);
+        LACT_LAUNCH((dapp_fused_kernel<128, 32, 2>), dim3((unsigned)grid), dim3(NT), st, aa);
+        HIP_TRY(hipGetLastError());
+      }
+      return LACT_OK;
+    }
+    // the column block serves both the forward (dh columns) and the output
+    // mode (d columns); the fp32 register-path apply tile spills at 128
+    const int abj = (D % 128 == 0 && Dh % 128 == 0 && profile_of(p) != PF32) ? 128 : 64;
+    for (size_t g0 = ga; g0 < gb; g0 += MAXG) {
+      const int ng = (int)std::min<size_t>(MAXG, gb - g0);
+      AppFwdArgs aa;
+      memset(&aa, 0, sizeof(aa));
+      aa.ngroups = ng;
+      aa.q = qx;
+      aa.q_bs = q_bs;
+      aa.x_bs = x_bs;
+      aa.oz = P.oz;
+      aa.oz_bs = seq_stride;
+      aa.H = ws + w.h;
+      aa.h_bs = w.h_rows * Dh;
+      aa.D = D;
+      aa.Dh = Dh;
+      // workgroups per group: token tiles x column blocks (cols wide) x instances
+      auto set_tiles = [&](int cols, int64_t& grid) -> lact_status {
+        grid = 0;
+        for (int i = 0; i < aa.ngroups; ++i) {
+          const int64_t t = ((aa.g[i].len + FBT - 1) / FBT) * (cols / abj) * n;
+          if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+          aa.g[i].tiles = (int)t;
+          grid += t;
+        }
+        if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+        return LACT_OK;
+      };
+      // gated hidden of the batch's groups not done by their update tile
+      int nf = 0;
+      for (int i = 0; i < ng; ++i)
+        if (!hq_done[g0 + i]) aa.g[nf++] = groups[g0 + i];
+      aa.ngroups = nf;
+      int64_t grid = 0;
+      if (nf > 0) {
+        if (lact_status r = set_tiles(Dh, grid)) return r;
+        KernelTimer kt(LACT_K_APP, st);
+        lact_status r = abj == 128 ? launch_app_fwd<PT, 128>(aa, grid, st) : launch_app_fwd<PT, 64>(aa, grid, st);
+        if (r) return r;
+      }
+      // output product over every group of the batch
+      aa.ngroups = ng;
+      for (int i = 0; i < ng; ++i) aa.g[i] = groups[g0 + i];
+      // o[t, r] = sum_j Hq[t, j] W2[r, j]: the apply tile in output mode
+      // (d column blocks), or the generic GEMM for profiles without a bf16 path
+      {
+        aa.o = P.o;
+        if (lact_status r = set_tiles(D, grid)) return r;
+        lact_status ost = LACT_OK;
+        bool done;
+        {
+          KernelTimer kt(LACT_K_OUT, st);
+          done = abj == 128 ? launch_app_out<PT, 128>(aa, grid, st, &ost) : launch_app_out<PT, 64>(aa, grid, st, &ost);
+        }
+        if (done) {
+          if (ost) return ost;
+          continue;
+        }
+      }
+      GemmArgs g = gemm_args();
+      g.ngroups = ng;
+      int64_t wgs128 = 0;
+      for (int i = 0; i < ng; ++i) {
+        const AppGroup& ag = aa.g[i];
+        g.g[i].A = static_cast<const char*>(aa.H) + (size_t)ag.h0 * Dh * app_size(profile_of(p));
+        int u = 0;
+        // the snapshot this group reads is the one its W1 came from
+        for (int k = 0; k < w.nslots; ++k)
+          if (slot(k, 0) == ag.W1) u = k;
+        g.g[i].B = slot(u, 1);
+        g.g[i].C = static_cast<char*>(P.o) + (size_t)ag.t0 * D * io_size(p);
+        g.g[i].rs = P.oz ? P.oz + ag.t0 : nullptr;
+        g.g[i].M = (int)ag.len;
+        wgs128 += ((ag.len + 127) / 128) * std::max(1, D / 128) * n;
+      }
+      g.lda = Dh;
+      g.a_bs = w.h_rows * Dh;
+      g.ldb = Dh;          // W2 [d, dh]: row n = output unit n
+      g.b_bs = DD;
+      g.ldc = D;
+      g.c_bs = x_bs;
+      g.rs_bs = seq_stride;
+      g.N = D;
+      g.K = g.kps = Dh;
+      g.batch = n;
+      lact_status r =
+          launch_gemm<TAPP, PT::PAPP, false, TS, PT::PS, false, TIO>(g, gemm_tile(wgs128), LACT_K_OUT, st);
+      if (r) return r;
+    }
+    return LACT_OK;
+  };
+  // Every group whose snapshot (and, when its gated hidden came from its
+  // update's tile, that update) is enqueued goes to the apply stream, after
+  // what the caller's stream holds so far.
+  size_t app_next = 0;
+  bool launched_app = false;
+  auto apply_upto = [&](size_t gb) -> lact_status {
+    if (gb <= app_next) return LACT_OK;
+    if (lact_status r = stream_after(aux->app, s, aux->ready)) return r;
+    if (lact_status r = apply_groups(app_next, gb, aux->app)) return r;
+    app_next = gb;
+    launched_app = true;
+    return LACT_OK;
+  };
 
   // ---------------------------------------------------------------- recurrence
   int nu = 0;   // updates done so far
@@ -1003,74 +1188,95 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       const float* Xin = U;
       if (D == Dh) {
         // every matrix square: one batch of 3n, every product on operands
-        // stored as bf16 planes by the product (or the row reduction) before
+        // stored as bf16 planes by the product (or the row reduction) before.
+        // The batch is cut in two halves that run on two streams: each
+        // half's chain of fifteen dependent launches leaves the chip idle
+        // between launches, which the other half fills.
         constexpr int PN = PT::PREC;
         const int nb = 3 * n;
-        bf16_t* Xp[2] = {reinterpret_cast<bf16_t*>(ws + w.xp0), reinterpret_cast<bf16_t*>(ws + w.xp1)};
-        bf16_t* Ap = reinterpret_cast<bf16_t*>(ws + w.ap);
-        bf16_t* Bp = reinterpret_cast<bf16_t*>(ws + w.bp);
-        const bf16_t* Xpin = Xp[1];   // U's planes
-        for (int it = 0; it < p.ns_iters; ++it) {
-          const bool first = it == 0, last = it + 1 == p.ns_iters;
-          float* Xout = X[it & 1];
-          bf16_t* Xpout = Xp[it & 1];
-          GemmArgs g = gemm_args();
-          g.lda = g.ldb = g.ldc = g.ldcin = D;
-          g.a_bs = g.b_bs = g.c_bs = g.cin_bs = DD;
-          g.a_ps = g.b_ps = g.cp_ps = (int64_t)nb * DD;
-          g.g[0].M = D;
-          g.N = D;
-          g.K = g.kps = D;
-          g.batch = nb;
-          // A = X X^T (X = s U on the first step, s = 1 / (||U||_F + 1e-7)
-          // from the row sums of squares); A and B are symmetric, so only
-          // their upper-triangle tiles run, each also storing its mirror.
-          // Every intermediate is kept as planes only (the b A and a X terms
-          // read them back: exact in three planes, 16-bit significands in two,
-          // the precision of the products' operands)
-          g.sym = D > PgSmall::BM;
-          g.g[0].A = Xpin;
-          g.g[0].B = Xpin;
-          g.g[0].Cp = Ap;
-          if (first) {
-            g.g[0].rowsq = rowsq;
-            g.rowsq_bs = D;
-            g.rowsq_n = D;
-            g.alpha_pow = 2;
+        const int64_t ps = (int64_t)nb * DD;   // plane stride
+        auto ns_range = [&](int b0, int nbh, hipStream_t st) -> lact_status {
+          bf16_t* Xp[2] = {reinterpret_cast<bf16_t*>(ws + w.xp0) + b0 * DD, reinterpret_cast<bf16_t*>(ws + w.xp1) + b0 * DD};
+          bf16_t* Ap = reinterpret_cast<bf16_t*>(ws + w.ap) + b0 * DD;
+          bf16_t* Bp = reinterpret_cast<bf16_t*>(ws + w.bp) + b0 * DD;
+          const bf16_t* Xpin = Xp[1];   // U's planes
+          const float* rq = rowsq + (int64_t)b0 * D;
+          for (int it = 0; it < p.ns_iters; ++it) {
+            const bool first = it == 0, last = it + 1 == p.ns_iters;
+            float* Xout = X[it & 1] + b0 * DD;
+            bf16_t* Xpout = Xp[it & 1];
+            GemmArgs g = gemm_args();
+            g.lda = g.ldb = g.ldc = g.ldcin = D;
+            g.a_bs = g.b_bs = g.c_bs = g.cin_bs = DD;
+            g.a_ps = g.b_ps = g.cp_ps = ps;
+            g.g[0].M = D;
+            g.N = D;
+            g.K = g.kps = D;
+            g.batch = nbh;
+            // A = X X^T (X = s U on the first step, s = 1 / (||U||_F + 1e-7)
+            // from the row sums of squares); A and B are symmetric, so only
+            // their upper-triangle tiles run, each also storing its mirror.
+            // Every intermediate is kept as planes only (the b A and a X terms
+            // read them back: exact in three planes, 16-bit significands in two,
+            // the precision of the products' operands)
+            g.sym = D > PgSmall::BM;
+            g.g[0].A = Xpin;
+            g.g[0].B = Xpin;
+            g.g[0].Cp = Ap;
+            if (first) {
+              g.g[0].rowsq = rq;
+              g.rowsq_bs = D;
+              g.rowsq_n = D;
+              g.alpha_pow = 2;
+            }
+            lact_status r = launch_pgemm<PN>(g, false, LACT_K_NS, st);
+            if (r) return r;
+            // B = b A + c A A   (A is symmetric: A A = A A^T); only its planes are needed
+            g.g[0].rowsq = nullptr;
+            g.alpha_pow = 0;
+            g.g[0].A = Ap;
+            g.g[0].B = Ap;
+            g.g[0].Cp = Bp;
+            g.g[0].Cinp = Ap;
+            g.alpha = cc;
+            g.beta = cb;
+            r = launch_pgemm<PN>(g, false, LACT_K_NS, st);
+            if (r) return r;
+            // X' = a X + B X  (element (n = j, k) of the second operand is X[k, j]:
+            // column-k); the last step's result is read by the optimiser in fp32
+            g.sym = 0;
+            g.g[0].A = Bp;
+            g.g[0].B = Xpin;
+            g.g[0].C = last ? Xout : nullptr;
+            g.g[0].Cp = last ? nullptr : Xpout;
+            g.g[0].Cinp = Xpin;
+            g.alpha = 1.f;
+            g.beta = ca;
+            if (first) {
+              g.g[0].rowsq = rq;
+              g.alpha_pow = 1;
+              g.beta_pow = 1;
+            }
+            r = launch_pgemm<PN>(g, true, LACT_K_NS, st);
+            if (r) return r;
+            Xpin = Xpout;
           }
-          lact_status r = launch_pgemm<PN>(g, false, LACT_K_NS, s);
-          if (r) return r;
-          // B = b A + c A A   (A is symmetric: A A = A A^T); only its planes are needed
-          g.g[0].rowsq = nullptr;
-          g.alpha_pow = 0;
-          g.g[0].A = Ap;
-          g.g[0].B = Ap;
-          g.g[0].Cp = Bp;
-          g.g[0].Cinp = Ap;
-          g.alpha = cc;
-          g.beta = cb;
-          r = launch_pgemm<PN>(g, false, LACT_K_NS, s);
-          if (r) return r;
-          // X' = a X + B X  (element (n = j, k) of the second operand is X[k, j]:
-          // column-k); the last step's result is read by the optimiser in fp32
-          g.sym = 0;
-          g.g[0].A = Bp;
-          g.g[0].B = Xpin;
-          g.g[0].C = last ? Xout : nullptr;
-          g.g[0].Cp = last ? nullptr : Xpout;
-          g.g[0].Cinp = Xpin;
-          g.alpha = 1.f;
-          g.beta = ca;
-          if (first) {
-            g.g[0].rowsq = rowsq;
-            g.alpha_pow = 1;
-            g.beta_pow = 1;
-          }
-          r = launch_pgemm<PN>(g, true, LACT_K_NS, s);
-          if (r) return r;
-          Xin = Xout;
-          Xpin = Xpout;
-        }
+          return LACT_OK;
+        };
+        const int nb0 = (nb + 1) / 2;
+        if (lact_status r = stream_after(aux->ns, s, aux->fork)) return r;
+        // the applies of the groups of steps up to this one (their snapshots
+        // and gated hidden rows exist now) run beside the Newton-Schulz chain,
+        // which leaves the chip partly idle between its launches
+        size_t ready = 0;
+        for (size_t sj = 0; sj <= si; ++sj)
+          if (step_group[sj] >= 0) ready = (size_t)step_group[sj] + 1;
+        if (lact_status r = apply_upto(ready)) return r;
+        if (lact_status r = ns_range(0, nb0, s)) return r;
+        if (nb > nb0)
+          if (lact_status r = ns_range(nb0, nb - nb0, aux->ns)) return r;
+        if (lact_status r = stream_after(s, aux->ns, aux->join)) return r;
+        Xin = X[(p.ns_iters - 1) & 1];
         (void)Am;
       } else {
         // W1, W3 are [dh, d] and W2 is [d, dh]: every Gram matrix is the
@@ -1196,128 +1402,15 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     ++nu;
   }
 
-  // ---------------------------------------------------------------- apply (all chunks)
+  // ---------------------------------------------------------------- apply
+  // the rest: on the caller's stream when no apply went beside the
+  // recurrence (without Newton-Schulz there is no idle phase to fill, and
+  // the grouped launches are larger), else after the others on the apply stream
   TraceRange tr_apply("lact apply (all chunks)");
-  if (fused_apply(p)) {
-    for (size_t g0 = 0; g0 < groups.size(); g0 += MAXG) {
-      const int ng = (int)std::min<size_t>(MAXG, groups.size() - g0);
-      AppFwdArgs aa;
-      memset(&aa, 0, sizeof(aa));
-      aa.ngroups = ng;
-      aa.q = qx;
-      aa.q_bs = q_bs;
-      aa.x_bs = x_bs;
-      aa.o = P.o;
-      aa.oz = P.oz;
-      aa.oz_bs = seq_stride;
-      aa.D = D;
-      aa.Dh = Dh;
-      int64_t grid = 0;
-      for (int i = 0; i < ng; ++i) {
-        aa.g[i] = groups[g0 + i];
-        const int64_t t = ((aa.g[i].len + FBT - 1) / FBT) * n;
-        if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
-        aa.g[i].tiles = (int)t;
-        grid += t;
-      }
-      if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
-      KernelTimer kt(LACT_K_APP, s);
-      LACT_LAUNCH((dapp_fused_kernel<128, 32, 2>), dim3((unsigned)grid), dim3(NT), s, aa);
-      HIP_TRY(hipGetLastError());
-    }
-    return LACT_OK;
-  }
-  // the column block serves both the forward (dh columns) and the output
-  // mode (d columns); the fp32 register-path apply tile spills at 128
-  const int abj = (D % 128 == 0 && Dh % 128 == 0 && profile_of(p) != PF32) ? 128 : 64;
-  for (size_t g0 = 0; g0 < groups.size(); g0 += MAXG) {
-    const int ng = (int)std::min<size_t>(MAXG, groups.size() - g0);
-    AppFwdArgs aa;
-    memset(&aa, 0, sizeof(aa));
-    aa.ngroups = ng;
-    aa.q = qx;
-    aa.q_bs = q_bs;
-    aa.x_bs = x_bs;
-    aa.oz = P.oz;
-    aa.oz_bs = seq_stride;
-    aa.H = ws + w.h;
-    aa.h_bs = w.h_rows * Dh;
-    aa.D = D;
-    aa.Dh = Dh;
-    // workgroups per group: token tiles x column blocks (cols wide) x instances
-    auto set_tiles = [&](int cols, int64_t& grid) -> lact_status {
-      grid = 0;
-      for (int i = 0; i < aa.ngroups; ++i) {
-        const int64_t t = ((aa.g[i].len + FBT - 1) / FBT) * (cols / abj) * n;
-        if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
-        aa.g[i].tiles = (int)t;
-        grid += t;
-      }
-      if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
-      return LACT_OK;
-    };
-    // gated hidden of the batch's groups not done by their update tile
-    int nf = 0;
-    for (int i = 0; i < ng; ++i)
-      if (!hq_done[g0 + i]) aa.g[nf++] = groups[g0 + i];
-    aa.ngroups = nf;
-    int64_t grid = 0;
-    if (nf > 0) {
-      if (lact_status r = set_tiles(Dh, grid)) return r;
-      KernelTimer kt(LACT_K_APP, s);
-      lact_status r = abj == 128 ? launch_app_fwd<PT, 128>(aa, grid, s) : launch_app_fwd<PT, 64>(aa, grid, s);
-      if (r) return r;
-    }
-    // output product over every group of the batch
-    aa.ngroups = ng;
-    for (int i = 0; i < ng; ++i) aa.g[i] = groups[g0 + i];
-    // o[t, r] = sum_j Hq[t, j] W2[r, j]: the apply tile in output mode
-    // (d column blocks), or the generic GEMM for profiles without a bf16 path
-    {
-      aa.o = P.o;
-      if (lact_status r = set_tiles(D, grid)) return r;
-      lact_status st = LACT_OK;
-      bool done;
-      {
-        KernelTimer kt(LACT_K_OUT, s);
-        done = abj == 128 ? launch_app_out<PT, 128>(aa, grid, s, &st) : launch_app_out<PT, 64>(aa, grid, s, &st);
-      }
-      if (done) {
-        if (st) return st;
-        continue;
-      }
-    }
-    GemmArgs g = gemm_args();
-    g.ngroups = ng;
-    int64_t wgs128 = 0;
-    for (int i = 0; i < ng; ++i) {
-      const AppGroup& ag = aa.g[i];
-      g.g[i].A = static_cast<const char*>(aa.H) + (size_t)ag.h0 * Dh * app_size(profile_of(p));
-      int u = 0;
-      // the snapshot this group reads is the one its W1 came from
-      for (int k = 0; k < w.nslots; ++k)
-        if (slot(k, 0) == ag.W1) u = k;
-      g.g[i].B = slot(u, 1);
-      g.g[i].C = static_cast<char*>(P.o) + (size_t)ag.t0 * D * io_size(p);
-      g.g[i].rs = P.oz ? P.oz + ag.t0 : nullptr;
-      g.g[i].M = (int)ag.len;
-      wgs128 += ((ag.len + 127) / 128) * std::max(1, D / 128) * n;
-    }
-    g.lda = Dh;
-    g.a_bs = w.h_rows * Dh;
-    g.ldb = Dh;          // W2 [d, dh]: row n = output unit n
-    g.b_bs = DD;
-    g.ldc = D;
-    g.c_bs = x_bs;
-    g.rs_bs = seq_stride;
-    g.N = D;
-    g.K = g.kps = Dh;
-    g.batch = n;
-    lact_status r =
-        launch_gemm<TAPP, PT::PAPP, false, TS, PT::PS, false, TIO>(g, gemm_tile(wgs128), LACT_K_OUT, s);
-    if (r) return r;
-  }
-  return LACT_OK;
+  if (!launched_app) return apply_groups(0, groups.size(), s);
+  if (lact_status r = apply_upto(groups.size())) return r;
+  // the caller's stream completes after the applies
+  return stream_after(s, aux->app, aux->done);
 }
 
 lact_status dispatch(const lact_problem& p, const Ptrs& P, int64_t seq_stride, const Plan& plan, const Ws& w,

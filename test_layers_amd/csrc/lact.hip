@@ -616,9 +616,12 @@ template <typename PT, int BJ>
 lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
   if constexpr (PT::PL > 1) {
     // weight planes from the snapshot, update terms stored as planes;
-    // 32-wide stages three deep fit the planes' tiles and the staging
+    // 32-wide stages: two deep for two planes (80 KB, two workgroups per
+    // CU, one's prologue and epilogue beside the other's products), three
+    // deep for three
     if constexpr (BJ == 64) {
-      LACT_LAUNCH((dupd_fwd_kernel<64, 32, 3, false, PT::PL>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
+      constexpr int NST = PT::PL == 2 ? 2 : 3;
+      LACT_LAUNCH((dupd_fwd_kernel<64, 32, NST, false, PT::PL>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
       HIP_TRY(hipGetLastError());
       return LACT_OK;
     } else {

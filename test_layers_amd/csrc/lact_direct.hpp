@@ -465,8 +465,12 @@ constexpr int upd_w_waves(int bj, int bkk) {
 // sums P plane products, smallest plane first.  The update terms are fp32
 // values stored as P bf16 planes (plane p at E + p * e_ps), the operand form
 // of the contraction that follows.
+// waves per SIMD the update tile is compiled for: two workgroups per CU for
+// the two-plane tile on a two-stage ring (80 KB of LDS), else one
+constexpr int upd_min_waves(int P, int NST) { return P == 2 && NST == 2 ? 4 : 1; }
+
 template <int BJ, int BKK, int NST, bool WQ = false, int P = 1>
-__global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
+__global__ __launch_bounds__(DG_THREADS, upd_min_waves(P, NST)) void dupd_fwd_kernel(UpdFwdArgs a) {
   constexpr int NWV = DG_THREADS / WAVE;
   constexpr int WW = upd_w_waves(BJ, BKK);
   constexpr int NX = WQ ? 3 : 2;     // token tiles per stage: k, v (, q)
@@ -478,11 +482,17 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   constexpr int LPS_X = NX * TX::INSTR;                     // ... of the other waves
   constexpr int FM = 2, FN = BJ / 32;
   constexpr int ET_PLANE = 3 * BJ * FBT * 2;   // one plane of the tile's update terms (bf16)
-  constexpr int ET_BYTES = P * ET_PLANE;       // staged for full-line stores
-  static_assert(ET_BYTES <= NST * STAGE, "staging fits the ring");
-  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
-  __shared__ float s_red[2];
-  __shared__ float s_lr[FBT * 3];
+  // After the main loop the ring holds the staged update terms (for
+  // full-line stores) and, at its end, the tile's learning rates and beta
+  // sums; all planes are staged at once when they fit, else one per pass.
+  constexpr int RING = NST * STAGE;
+  constexpr int LR_BYTES = FBT * 3 * 4;
+  constexpr int LR_OFF = (RING - LR_BYTES - 16) & ~15;
+  constexpr int PPASS = P * ET_PLANE <= LR_OFF ? P : 1;   // planes staged per pass
+  static_assert(PPASS * ET_PLANE <= LR_OFF, "staging fits the ring beside the learning rates");
+  __shared__ __attribute__((aligned(1024))) char smem[RING];
+  float* s_lr = reinterpret_cast<float*>(smem + LR_OFF);
+  float* s_red = reinterpret_cast<float*>(smem + LR_OFF + LR_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -518,18 +528,21 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   const typename TX::Plan pv = TX::plan(V, D, t0, tend - 1, 0, wave, lane);
   const typename TX::Plan pq = TX::plan(Q, D, t0, tend - 1, 0, wave, lane);
   // W1, W3 and W2^T rows: hidden units j0 .. j0 + BJ - 1 (of dh), d long;
-  // W tile (m, p) of a stage sits at w + (m * P + p) * TW::BYTES
-  typename TW::Plan pw[3][P];
-  {
-    const bf16_t* W0[3] = {W1, W3, W2T};
+  // W tile (m, p) of a stage sits at w + (m * P + p) * TW::BYTES.  One
+  // plane: per-lane addresses planned once; several: the planes' bases
+  // (uniform) kept and each load's address formed when it is issued, which
+  // keeps the per-lane registers of 3 P planned addresses free.
+  const bf16_t* W0[3] = {W1, W3, W2T};
+  const bf16_t* wsrc[3][P];
 #pragma unroll
-    for (int m = 0; m < 3; ++m)
+  for (int m = 0; m < 3; ++m)
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const bf16_t* src = p == 0 ? W0[m]
-                                   : reinterpret_cast<const bf16_t*>(a.Wlo) + (p - 1) * a.wlo_ps + m * a.wlo_ms + inst * DD;
-        pw[m][p] = TW::plan(src, D, j0, Dh - 1, 0, wload ? wave : 0, lane);
-      }
+    for (int p = 0; p < P; ++p)
+      wsrc[m][p] = p == 0 ? W0[m] : reinterpret_cast<const bf16_t*>(a.Wlo) + (p - 1) * a.wlo_ps + m * a.wlo_ms + inst * DD;
+  typename TW::Plan pw[3][P == 1 ? 1 : 1];
+  if constexpr (P == 1) {
+#pragma unroll
+    for (int m = 0; m < 3; ++m) pw[m][0] = TW::plan(wsrc[m][0], D, j0, Dh - 1, 0, wload ? wave : 0, lane);
   }
   auto issue_one = [&](int s, int buf, int idx) {
     char* st = smem + buf * STAGE;
@@ -546,7 +559,13 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
       for (int m = 0; m < 3; ++m)
 #pragma unroll
         for (int p = 0; p < P; ++p)
-          if (wi / TW::INSTR == m * P + p) TW::issue_one(w + (m * P + p) * TW::BYTES, pw[m][p], off, wave, wi % TW::INSTR);
+          if (wi / TW::INSTR == m * P + p) {
+            if constexpr (P == 1)
+              TW::issue_one(w + m * TW::BYTES, pw[m][0], off, wave, wi % TW::INSTR);
+            else
+              TW::issue_one(w + (m * P + p) * TW::BYTES, wsrc[m][p], D, j0, Dh - 1, (int64_t)s * BKK, wave, lane,
+                            wi % TW::INSTR);
+          }
     }
   };
   f32x4 accA[FM][FN], accB[FM][FN], accG[FM][FN], accQ1[FM][FN], accQ3[FM][FN];
@@ -558,39 +577,60 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   auto compute = [&](int buf, auto&& hook) {
     const char* st = smem + buf * STAGE;
     const char* w = st + NX * TX::BYTES;
-    constexpr int NSLOT = (BKK / 32) * FM;
+    constexpr int NSLOT = (BKK / 32) * (P == 1 ? FM : P);
 #pragma unroll
     for (int kk = 0; kk < BKK; kk += 32) {
-      bf16x8 fk[FM], fv[FM], fq[FM], f1[P][FN], f3[P][FN], f2[P][FN];
+      bf16x8 fk[FM], fv[FM], fq[FM];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         fk[i] = dfrag_row<TX>(st, wm * 32 + i * 16, kk, lane);
         fv[i] = dfrag_row<TX>(st + TX::BYTES, wm * 32 + i * 16, kk, lane);
         if constexpr (WQ) fq[i] = dfrag_row<TX>(st + 2 * TX::BYTES, wm * 32 + i * 16, kk, lane);
       }
-#pragma unroll
-      for (int p = 0; p < P; ++p)
+      if constexpr (P == 1) {
+        bf16x8 f1[FN], f3[FN], f2[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          f1[p][j] = dfrag_row<TW>(w + p * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
-          f3[p][j] = dfrag_row<TW>(w + (P + p) * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
-          f2[p][j] = dfrag_row<TW>(w + (2 * P + p) * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+          f1[j] = dfrag_row<TW>(w, wn * (BJ / 2) + j * 16, kk, lane);
+          f3[j] = dfrag_row<TW>(w + TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+          f2[j] = dfrag_row<TW>(w + 2 * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
         }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int p = P - 1; p >= 0; --p)
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            accA[i][j] = mfma(fk[i], f1[p][j], accA[i][j]);
-            accB[i][j] = mfma(fk[i], f3[p][j], accB[i][j]);
-            accG[i][j] = mfma(fv[i], f2[p][j], accG[i][j]);
+            accA[i][j] = mfma(fk[i], f1[j], accA[i][j]);
+            accB[i][j] = mfma(fk[i], f3[j], accB[i][j]);
+            accG[i][j] = mfma(fv[i], f2[j], accG[i][j]);
             if constexpr (WQ) {
-              accQ1[i][j] = mfma(f1[p][j], fq[i], accQ1[i][j]);
-              accQ3[i][j] = mfma(f3[p][j], fq[i], accQ3[i][j]);
+              accQ1[i][j] = mfma(f1[j], fq[i], accQ1[i][j]);
+              accQ3[i][j] = mfma(f3[j], fq[i], accQ3[i][j]);
             }
           }
-        hook((kk / 32) * FM + i, NSLOT);
+          hook((kk / 32) * FM + i, NSLOT);
+        }
+      } else {
+        // one weight plane at a time (smallest first): its fragments, then
+        // its products, so only one plane's fragments are live
+#pragma unroll
+        for (int p = P - 1; p >= 0; --p) {
+          bf16x8 f1[FN], f3[FN], f2[FN];
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            f1[j] = dfrag_row<TW>(w + p * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+            f3[j] = dfrag_row<TW>(w + (P + p) * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+            f2[j] = dfrag_row<TW>(w + (2 * P + p) * TW::BYTES, wn * (BJ / 2) + j * 16, kk, lane);
+          }
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              accA[i][j] = mfma(fk[i], f1[j], accA[i][j]);
+              accB[i][j] = mfma(fk[i], f3[j], accB[i][j]);
+              accG[i][j] = mfma(fv[i], f2[j], accG[i][j]);
+            }
+          hook((kk / 32) * P + (P - 1 - p), NSLOT);
+        }
       }
     }
   };
@@ -631,67 +671,70 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_fwd_kernel(UpdFwdArgs a) {
   __syncthreads();
   if (a.beta != nullptr && jb == 0 && tid == 0) a.bpart[(int64_t)inst * a.tiles_t + tb] = s_red[0] + s_red[1];
   char* et = smem;
+  bf16_t* E = reinterpret_cast<bf16_t*>(a.E) + inst * 3 * (int64_t)Dh * a.ldE + (t0 - a.upd_t0);
+  constexpr int ROWS = 3 * BJ;
+  for (int p0 = 0; p0 < P; p0 += PPASS) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int tl = wm * 32 + i * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
-    float e1[4], e2[4], e3[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      e1[r] = s_lr[(tl + r) * 3 + 0];
-      e2[r] = s_lr[(tl + r) * 3 + 1];
-      e3[r] = s_lr[(tl + r) * 3 + 2];
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = wn * (BJ / 2) + j * 16 + (lane & 15);
-      float u1[4], u3[4], u2[4];
+    for (int i = 0; i < FM; ++i) {
+      const int tl = wm * 32 + i * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
+      float e1[4], e2[4], e3[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float x = accA[i][j][r], bb = accB[i][j][r], gg = accG[i][j][r];
-        const float sg = fast_sigmoid(x);
-        const float s = x * sg;
-        const float sp = sg * (1.0f + x * (1.0f - sg));
-        u1[r] = e1[r] * gg * bb * sp;
-        u3[r] = e3[r] * gg * s;
-        u2[r] = e2[r] * s * bb;
+        e1[r] = s_lr[(tl + r) * 3 + 0];
+        e2[r] = s_lr[(tl + r) * 3 + 1];
+        e3[r] = s_lr[(tl + r) * 3 + 2];
       }
-      const int chunk = tl >> 3, half = (tl >> 2) & 1;
-      const float* terms[3] = {u1, u3, u2};
 #pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        const int row = m * BJ + col;
-        const int off = row * (FBT * 2) + ((chunk ^ (row & 15)) << 4) + (half << 3);
-        if constexpr (P == 1) {
-          uint2 pk2;
-          pk2.x = pack_bf16x2(terms[m][0], terms[m][1]);
-          pk2.y = pack_bf16x2(terms[m][2], terms[m][3]);
-          *reinterpret_cast<uint2*>(et + off) = pk2;
-        } else {
-          uint32_t h[4][P];
+      for (int j = 0; j < FN; ++j) {
+        const int col = wn * (BJ / 2) + j * 16 + (lane & 15);
+        float u1[4], u3[4], u2[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) split_planes<P>(terms[m][r], h[r]);
+        for (int r = 0; r < 4; ++r) {
+          const float x = accA[i][j][r], bb = accB[i][j][r], gg = accG[i][j][r];
+          const float sg = fast_sigmoid(x);
+          const float s = x * sg;
+          const float sp = sg * (1.0f + x * (1.0f - sg));
+          u1[r] = e1[r] * gg * bb * sp;
+          u3[r] = e3[r] * gg * s;
+          u2[r] = e2[r] * s * bb;
+        }
+        const int chunk = tl >> 3, half = (tl >> 2) & 1;
+        const float* terms[3] = {u1, u3, u2};
 #pragma unroll
-          for (int p = 0; p < P; ++p)
-            *reinterpret_cast<uint2*>(et + p * ET_PLANE + off) =
-                make_uint2(h[0][p] | (h[1][p] << 16), h[2][p] | (h[3][p] << 16));
+        for (int m = 0; m < 3; ++m) {
+          const int row = m * BJ + col;
+          const int off = row * (FBT * 2) + ((chunk ^ (row & 15)) << 4) + (half << 3);
+          if constexpr (P == 1) {
+            uint2 pk2;
+            pk2.x = pack_bf16x2(terms[m][0], terms[m][1]);
+            pk2.y = pack_bf16x2(terms[m][2], terms[m][3]);
+            *reinterpret_cast<uint2*>(et + off) = pk2;
+          } else {
+            uint32_t h[4][P];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) split_planes<P>(terms[m][r], h[r]);
+#pragma unroll
+            for (int pp = 0; pp < PPASS; ++pp)
+              *reinterpret_cast<uint2*>(et + pp * ET_PLANE + off) =
+                  make_uint2(h[0][p0 + pp] | (h[1][p0 + pp] << 16), h[2][p0 + pp] | (h[3][p0 + pp] << 16));
+          }
         }
       }
     }
-  }
-  __syncthreads();
-  // E rows U1 | U3 | U2-terms, token-fastest (one set per plane); the tile's
-  // 128 tokens lie inside the row's ldE (zero terms past the chunk end)
-  bf16_t* E = reinterpret_cast<bf16_t*>(a.E) + inst * 3 * (int64_t)Dh * a.ldE + (t0 - a.upd_t0);
-  constexpr int ROWS = 3 * BJ;
-  for (int r0 = 0; r0 < P * ROWS; r0 += 4 * NWV) {
-    const int prow = r0 + wave * 4 + (lane >> 4);
-    if (prow < P * ROWS) {
-      const int p = prow / ROWS, row = prow % ROWS;
-      const int c = lane & 15;
-      const uint4 v = *reinterpret_cast<const uint4*>(et + p * ET_PLANE + row * (FBT * 2) + ((c ^ (row & 15)) << 4));
-      const int m = row / BJ, col = row % BJ;
-      *reinterpret_cast<uint4*>(E + p * a.e_ps + (int64_t)(m * Dh + j0 + col) * a.ldE + c * 8) = v;
+    __syncthreads();
+    // E rows U1 | U3 | U2-terms, token-fastest (one set per plane); the
+    // tile's 128 tokens lie inside the row's ldE (zero terms past the chunk end)
+    for (int r0 = 0; r0 < PPASS * ROWS; r0 += 4 * NWV) {
+      const int prow = r0 + wave * 4 + (lane >> 4);
+      if (prow < PPASS * ROWS) {
+        const int pp = prow / ROWS, row = prow % ROWS;
+        const int c = lane & 15;
+        const uint4 v = *reinterpret_cast<const uint4*>(et + pp * ET_PLANE + row * (FBT * 2) + ((c ^ (row & 15)) << 4));
+        const int m = row / BJ, col = row % BJ;
+        *reinterpret_cast<uint4*>(E + (p0 + pp) * a.e_ps + (int64_t)(m * Dh + j0 + col) * a.ldE + c * 8) = v;
+      }
     }
+    if (p0 + PPASS < P) __syncthreads();   // every row read before the next pass overwrites the staging
   }
 }
 

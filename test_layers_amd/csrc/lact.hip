@@ -188,6 +188,9 @@ Prof profile_of(const lact_problem& p) {
 size_t io_size(const lact_problem& p) { return p.io_dtype == LACT_DTYPE_F32 ? 4 : 2; }
 // bf16 planes per Newton-Schulz operand
 int ns_planes(Prof f) { return f == PBF16 ? 1 : f == PBF16X2 ? 2 : 3; }
+// square matrices that fit a workgroup's LDS: the whole orthogonalisation
+// of a matrix runs in one workgroup (ns_small_kernel)
+bool ns_small(const lact_problem& p) { return p.d == p.dh && p.d <= 128; }
 // update terms storage per element: bf16, fp32, or two / three bf16 planes
 size_t rec_size(Prof f) { return f == PBF16 ? 2 : f == PBF16X3 ? 6 : 4; }
 // bf16 planes of the update forward's weight operands beyond the snapshot
@@ -412,14 +415,16 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   w.snap = take(w.snap_slot * (size_t)w.nslots);
   w.wlo = take(plan.max_upd > 0 ? (size_t)weight_lo_planes(f) * 3 * n * D * Dh * sizeof(bf16_t) : 0);
   if (uses_ns(p.opt) && plan.max_upd > 0) {
-    // square matrices keep U and A as planes only
-    w.u = take(D == Dh ? 0 : mats);
+    // larger square matrices keep U and A as planes only; small ones read U
+    // in fp32 and keep everything else in LDS
+    const bool small = ns_small(p);
+    w.u = take(D == Dh && !small ? 0 : mats);
     w.am = take(D == Dh ? 0 : mats);
     w.bm = take(D == Dh ? 0 : mats);
     w.xa = take(mats);
-    w.xb = take(mats);
+    w.xb = take(small ? 0 : mats);
     w.rowsq = take(n * (2 * Dh + D) * sizeof(float));
-    if (D == Dh) {
+    if (D == Dh && !small) {
       // operand planes of the square products: X (two, alternating), A, B
       const size_t pl = (size_t)ns_planes(f) * n * 3 * D * Dh * sizeof(bf16_t);
       w.xp0 = take(pl);
@@ -1170,9 +1175,9 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
           rm.nbp = nbp;
           rm.inv_len = 1.0f / (float)C;
         }
-        // square matrices: U's operand planes go to the second X plane set,
-        // which the first Newton-Schulz step reads
-        bf16_t* up = D == Dh ? reinterpret_cast<bf16_t*>(ws + w.xp1) : nullptr;
+        // larger square matrices: U's operand planes go to the second X plane
+        // set, which the first Newton-Schulz step reads
+        bf16_t* up = D == Dh && !ns_small(p) ? reinterpret_cast<bf16_t*>(ws + w.xp1) : nullptr;
         const int64_t ups = (int64_t)n * 3 * DD;
         const dim3 rg((unsigned)((rows + 3) / 4));
         const float* part = reinterpret_cast<const float*>(ws + w.part);
@@ -1189,7 +1194,19 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       float* X[2] = {reinterpret_cast<float*>(ws + w.xa), reinterpret_cast<float*>(ws + w.xb)};
       const float ca = 3.4445f, cb = -4.7750f, cc = 2.0315f;
       const float* Xin = U;
-      if (D == Dh) {
+      if (ns_small(p)) {
+        // one workgroup per matrix, the whole orthogonalisation in its LDS;
+        // the applies whose snapshots exist go beside it (it occupies 3n CUs)
+        size_t ready = 0;
+        for (size_t sj = 0; sj <= si; ++sj)
+          if (step_group[sj] >= 0) ready = (size_t)step_group[sj] + 1;
+        if (lact_status r = apply_upto(ready)) return r;
+        KernelTimer kt(LACT_K_NS, s);
+        if (D == 64) LACT_LAUNCH((ns_small_kernel<64, PT::PREC>), dim3((unsigned)(3 * n)), dim3(NsSmall<64>::THREADS), s, U, rowsq, X[0], p.ns_iters, ca, cb, cc);
+        else LACT_LAUNCH((ns_small_kernel<128, PT::PREC>), dim3((unsigned)(3 * n)), dim3(NsSmall<128>::THREADS), s, U, rowsq, X[0], p.ns_iters, ca, cb, cc);
+        HIP_TRY(hipGetLastError());
+        Xin = X[0];
+      } else if (D == Dh) {
         // every matrix square: one batch of 3n, every product on operands
         // stored as bf16 planes by the product (or the row reduction) before.
         // The batch is cut in two halves that run on two streams: each

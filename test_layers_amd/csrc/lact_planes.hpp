@@ -267,3 +267,169 @@ using PgSmall = PgShape<64, 64, 32, 2, 2, 1, 3>;     // 4 waves, 32 x 32 each
 using PgLarge = PgShape<128, 128, 64, 2, 2, 2, 2>;   // 8 waves, 64 x 64 each over half of every stage
 
 }  // namespace lact
+
+namespace lact {
+
+// =========================================================================
+// Newton-Schulz of small square matrices (d = dh <= 128) in one workgroup
+// per matrix: the iterate X and the Gram / polynomial matrix live in LDS as
+// fp32 for all ns_iters steps, so the fifteen products of a chunk's
+// orthogonalisation need no launch, no global round trip and no grid-wide
+// synchronisation.  Operand fragments are read from the fp32 copies and
+// split into P bf16 planes in registers; every product sums the plane pairs
+// (i, j) with i + j < P, smaller pairs first (fp32 grade at P = 3).
+//   X0 = U / (||U||_F + 1e-7);  per step:  A = X X^T,  B = b A + c A A,
+//   X <- a X + B X  ("大块测试时训练（LaCT）技术解析" §2.2.1, eqs. 9-10).
+// U: [nmat, D, D] fp32, rowsq: [nmat, D] per-row sums of squares of U
+// (the Frobenius norm), out: [nmat, D, D] fp32.
+template <int D>
+struct NsSmall {
+  static constexpr int NW = D == 128 ? 8 : 4;   // waves: 4 x 2 (D = 128) or 2 x 2 over the output
+  static constexpr int THREADS = NW * WAVE;
+  static constexpr int WGN = 2, WGM = NW / 2;
+  static constexpr int FM = D / WGM / 16, FN = D / WGN / 16;
+  static constexpr int PITCH = D + 4;            // fp32 row pitch (16-byte row reads conflict-free)
+  static constexpr int SLOT = D * PITCH * 4;
+};
+
+// eight consecutive fp32 values as P bf16 plane fragments: each plane two
+// values at a time with the packed round-to-nearest-even conversion, the
+// remainder for the next plane exact (the values and their bf16 rounding
+// share an exponent range), as split_planes does one value at a time
+template <int P>
+__device__ __forceinline__ void split8(float (&v)[8], bf16x8 (&f)[P]) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    u4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+    f[p] = __builtin_bit_cast(bf16x8, w);
+    if (p + 1 < P) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] -= __uint_as_float(w[q] << 16);
+        v[2 * q + 1] -= __uint_as_float(w[q] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+template <int D, int P>
+__global__ __launch_bounds__(NsSmall<D>::THREADS) void ns_small_kernel(const float* U, const float* rowsq, float* out,
+                                                                        int iters, float ca, float cb, float cc) {
+  using G = NsSmall<D>;
+  constexpr int FM = G::FM, FN = G::FN, PITCH = G::PITCH;
+  __shared__ __attribute__((aligned(16))) float s0[D * PITCH];   // X
+  __shared__ __attribute__((aligned(16))) float s1[D * PITCH];   // A, then B
+  __shared__ float s_scale;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / G::WGN, wn = wave % G::WGN;
+  const int64_t b = blockIdx.x;
+  const int64_t DD = (int64_t)D * D;
+  if (wave == 0) {
+    float sq = 0.f;
+    for (int i = lane; i < D; i += WAVE) sq += rowsq[b * D + i];
+    sq = wave_sum(sq);
+    if (lane == 0) s_scale = 1.0f / (sqrtf(sq) + 1e-7f);
+  }
+  __syncthreads();
+  {
+    const float sc = s_scale;
+    const float* Ub = U + b * DD;
+    for (int e = tid * 4; e < D * D; e += G::THREADS * 4) {
+      const float4 u = *reinterpret_cast<const float4*>(Ub + e);
+      *reinterpret_cast<float4*>(s0 + (e / D) * PITCH + e % D) = make_float4(sc * u.x, sc * u.y, sc * u.z, sc * u.w);
+    }
+  }
+  __syncthreads();
+
+  // fragment (16 rows x 8 k per lane-group) of a row-major fp32 slot, as P planes
+  auto frag_rows = [&](const float* sl, int r0, int kk, bf16x8 (&f)[P]) {
+    const float* src = sl + (r0 + (lane & 15)) * PITCH + kk + 8 * (lane >> 4);
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    split8<P>(v, f);
+  };
+  // fragment whose k runs down the slot's rows: element (n, k) = slot[k][n]
+  auto frag_cols = [&](const float* sl, int n0, int kk, bf16x8 (&f)[P]) {
+    const int n = n0 + (lane & 15), k0 = kk + 8 * (lane >> 4);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = sl[(k0 + e) * PITCH + n];
+    split8<P>(v, f);
+  };
+  // acc = Aop Bop^T over k: Aop rows from `sa`; Bop rows from `sb` (row
+  // reads) or its columns (COLB); swapped MFMA order, so lane holds row
+  // lane % 16 of a fragment and 4 consecutive columns
+  f32x4 acc[FM][FN];
+  auto product = [&](const float* sa, const float* sb, auto colb) {
+    constexpr bool COLB = decltype(colb)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < D; kk += 32) {
+      bf16x8 fa[FM][P], fb[FN][P];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) frag_rows(sa, wm * (D / G::WGM) + i * 16, kk, fa[i]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (COLB) frag_cols(sb, wn * (D / G::WGN) + j * 16, kk, fb[j]);
+        else frag_rows(sb, wn * (D / G::WGN) + j * 16, kk, fb[j]);
+      }
+#pragma unroll
+      for (int sp = P - 1; sp >= 0; --sp)
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+          for (int q = 0; q < P; ++q)
+            if (p + q == sp)
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma(fb[j][q], fa[i][p], acc[i][j]);
+    }
+  };
+  // v = alpha acc + beta slot (own positions), stored into `dst` after the barrier
+  auto finish = [&](float alpha, const float* sin, float beta, float* dst) {
+    float y[FM][FN][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wm * (D / G::WGM) + i * 16 + (lane & 15);
+        const int c = wn * (D / G::WGN) + j * 16 + 4 * (lane >> 4);
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (sin) x = *reinterpret_cast<const float4*>(sin + r * PITCH + c);
+        y[i][j][0] = alpha * acc[i][j][0] + beta * x.x;
+        y[i][j][1] = alpha * acc[i][j][1] + beta * x.y;
+        y[i][j][2] = alpha * acc[i][j][2] + beta * x.z;
+        y[i][j][3] = alpha * acc[i][j][3] + beta * x.w;
+      }
+    __syncthreads();   // every read of the slot being replaced is done
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wm * (D / G::WGM) + i * 16 + (lane & 15);
+        const int c = wn * (D / G::WGN) + j * 16 + 4 * (lane >> 4);
+        *reinterpret_cast<float4*>(dst + r * PITCH + c) = make_float4(y[i][j][0], y[i][j][1], y[i][j][2], y[i][j][3]);
+      }
+    __syncthreads();
+  };
+  for (int it = 0; it < iters; ++it) {
+    product(s0, s0, IC<0>{});         // A = X X^T
+    finish(1.f, nullptr, 0.f, s1);
+    product(s1, s1, IC<0>{});         // A A  (A symmetric: A A^T)
+    finish(cc, s1, cb, s1);           // B = c A A + b A
+    product(s1, s0, IC<1>{});         // B X: second operand element (n, k) = X[k][n]
+    finish(1.f, s0, ca, s0);          // X <- B X + a X
+  }
+  float* ob = out + b * DD;
+  for (int e = tid * 4; e < D * D; e += G::THREADS * 4)
+    *reinterpret_cast<float4*>(ob + e) = *reinterpret_cast<const float4*>(s0 + (e / D) * PITCH + e % D);
+}
+
+}  // namespace lact

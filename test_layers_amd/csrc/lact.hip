@@ -309,19 +309,41 @@ void dw_split(const lact_problem& p, int64_t C, int& S, int64_t& kps) {
   if (S < 1) S = 1;
 }
 
-// long chunks at d = dh = 128 in plain bf16 run the update forward and the
-// contraction as one kernel (the update terms stay in LDS)
+// long chunks at d = dh = 128 run the update forward and the contraction as
+// one kernel (the update terms stay in LDS): plain bf16 from 4,096 tokens,
+// the multi-plane recurrence (whose update terms would cross HBM as two or
+// three planes) from 1,024
 bool fused_update(const lact_problem& p, int64_t C) {
-  return profile_of(p) == PBF16 && p.d == UDW_D && p.dh == UDW_D && C >= 4096;
+  if (p.d != UDW_D || p.dh != UDW_D) return false;
+  const Prof f = profile_of(p);
+  if (f == PBF16) return C >= 4096;
+  return (f == PBF16X2 || f == PBF16X3) && C >= 1024;
 }
 
-// its token split (64-token tiles): about one workgroup per CU (n
-// instances x 2 hidden blocks per split), every split non-empty
+// its token split (64-token tiles), every split non-empty.  Plain bf16 (two
+// hidden blocks per instance): about one workgroup per CU.  Multi-plane (four
+// hidden blocks of 32, one workgroup per CU by LDS): the split count that
+// minimises rounds of workgroups x tiles per workgroup, the smaller on ties
 void udw_split(const lact_problem& p, int64_t C, int& S, int& tps) {
   const int64_t tt = (C + UDW2_T - 1) / UDW2_T;
-  const int64_t per = 2 * (int64_t)std::max(1, p.n_inst);
-  const int64_t s0 = std::max<int64_t>(1, std::min<int64_t>(tt, NCU / per));
-  tps = (int)((tt + s0 - 1) / s0);
+  const int64_t n = std::max(1, p.n_inst);
+  if (profile_of(p) == PBF16) {
+    const int64_t per = 2 * n;
+    const int64_t s0 = std::max<int64_t>(1, std::min<int64_t>(tt, NCU / per));
+    tps = (int)((tt + s0 - 1) / s0);
+  } else {
+    const int64_t per = (UDW_D / UDP_BJ) * n;
+    int64_t best = -1, bt = tt;
+    for (int64_t c = 1; c <= std::min<int64_t>(tt, 32); ++c) {
+      const int64_t t = (tt + c - 1) / c;
+      const int64_t cost = ((per * c + NCU - 1) / NCU) * t;
+      if (best < 0 || cost < best) {
+        best = cost;
+        bt = t;
+      }
+    }
+    tps = (int)bt;
+  }
   S = (int)((tt + tps - 1) / tps);
 }
 
@@ -407,7 +429,10 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   w.max_tt = (int)((plan.max_upd + UDW2_T - 1) / UDW2_T);
   const size_t snap_el = (f == PF32) ? 4 : 2;
   w.snap_slot = align256(4 * n * D * Dh * snap_el);
-  w.e = take(n * 3 * Dh * (size_t)w.ldE * rec_size(f));
+  bool unfused = false;   // the fused update keeps its update terms in LDS
+  for (const Step& st : plan.steps)
+    if (st.upd_len > 0 && !fused_update(p, st.upd_len)) unfused = true;
+  w.e = take(unfused ? n * 3 * Dh * (size_t)w.ldE * rec_size(f) : 0);
   w.h = take(fused_apply(p) ? 0 : n * (size_t)h_rows * Dh * app_size(f));
   const size_t mats = n * 3 * D * Dh * sizeof(float);
   w.part = take(plan.max_upd > 0 ? (size_t)S * mats : 0);
@@ -1068,6 +1093,23 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
         const int64_t grid = (int64_t)n * S * (UDW_D / 64);
         KernelTimer kt(LACT_K_UPD, s);
         LACT_LAUNCH((dupd_dw2_kernel<64>), dim3((unsigned)grid), dim3(DG_THREADS), s, ud);
+        HIP_TRY(hipGetLastError());
+      } else if constexpr (PT::PL > 1) {
+        int tps = 0;
+        udw_split(p, C, S, tps);
+        if (S > w.S) return fail(LACT_ERR_UNSUPPORTED, "internal: token split %d exceeds workspace plan %d", S, w.S);
+        UpdDwArgs ud;
+        memset(&ud, 0, sizeof(ud));
+        ud.u = ua;
+        ud.part = reinterpret_cast<float*>(ws + w.part);
+        ud.part_ss = (int64_t)n * 3 * DD;
+        ud.tps = tps;
+        ud.splits = S;
+        ud.nbp = (int)((C + UDW2_T - 1) / UDW2_T);
+        const int64_t grid = (int64_t)n * S * (UDW_D / UDP_BJ);
+        if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+        KernelTimer kt(LACT_K_UPD, s);
+        LACT_LAUNCH((dupd_dwp_kernel<PT::PL>), dim3((unsigned)grid), dim3(DG_THREADS), s, ud);
         HIP_TRY(hipGetLastError());
       }
     } else {

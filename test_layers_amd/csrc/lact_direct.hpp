@@ -976,6 +976,237 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dw2_kernel(UpdDwArgs g) {
 }
 
 // =========================================================================
+// Fused update at d = dh = 128 for the multi-plane recurrence (P = 2 or 3
+// stored bf16 planes of the weights and of the update terms): per 64-token
+// tile, the update forward A = K W1^T, B = K W3^T, G = V W2 over the tile's
+// tokens and the workgroup's 32 hidden units, the SwiGLU backward terms
+// ("大块测试时训练（LaCT）技术解析" §2.1, eqs. 4-5) split into P planes in
+// LDS, and at once the tile's share of U1 = E1^T K, U3 = E3^T K, U2 = V^T E2,
+// accumulated in registers over the workgroup's run of tiles; one fp32
+// partial per workgroup.  At this width the three planes of the update terms
+// would otherwise make a round trip through HBM (6 bytes per term).
+// Every product sums the plane pairs (plane p of the weights or update
+// terms with the single plane of k or v), smaller planes first.
+// LDS: the workgroup's weight rows, all planes, stay resident (24 KB per
+// plane); K and V of one tile (32 KB) are refilled from registers loaded
+// during the previous tile; the update-term planes take 12 KB each.
+constexpr int UDP_BJ = 32;   // hidden units per workgroup
+
+template <int P>
+__global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
+  const UpdFwdArgs& a = g.u;
+  constexpr int BKK = 64;
+  constexpr int NWV = DG_THREADS / WAVE;
+  constexpr int BJ = UDP_BJ;
+  using TT = DTile<UDW2_T, BKK, NWV>;   // 64 tokens x 64 d: K, V stages
+  using TW = DTile<BJ, BKK, 4>;         // 32 hidden rows x 64 d: weight stages (loaded by four waves)
+  static_assert(TT::INSTR == 1 && TW::INSTR == 1 && UDW_D == 2 * BKK && NWV == 8, "tile shapes");
+  constexpr int TB = TT::BYTES, WB = TW::BYTES;
+  constexpr int ERB = UDW2_T * 2;       // update-term row: 64 tokens of bf16
+  constexpr int EPL = 3 * BJ * ERB;     // one plane of the update terms
+  __shared__ __attribute__((aligned(1024))) char s_w[3 * P * 2 * WB];   // [matrix W1 | W3 | W2^T][plane][k stage]
+  __shared__ __attribute__((aligned(1024))) char s_kv[4 * TB];         // K s0, K s1, V s0, V s1
+  __shared__ __attribute__((aligned(1024))) char s_e[P * EPL];         // [plane][U1 | U3 | U2 terms][64 tokens]
+  __shared__ __attribute__((aligned(16))) float s_lr[UDW2_T * 3];
+  __shared__ __attribute__((aligned(16))) float s_beta[UDW2_T];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tw = wave >> 1, hw = wave & 1;   // forward: tokens 16 tw .., hidden 16 hw ..
+  const int jw = wave & 1, cq = wave >> 1;   // contraction: hidden rows 16 jw .., d columns 32 cq ..
+  const int D = UDW_D;
+  const int njb = UDW_D / BJ;
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int jb = bid % njb;
+  bid /= njb;
+  const int split = bid % g.splits;
+  const int inst = bid / g.splits;
+  const int j0 = jb * BJ;
+  const int64_t DD = (int64_t)D * D;
+  const int64_t tend = a.upd_t0 + a.upd_len;
+  const int ntiles = (int)((a.upd_len + UDW2_T - 1) / UDW2_T);
+  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + inst * a.k_bs;
+  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + inst * a.x_bs;
+  const float* LR = a.lr + inst * a.lr_bs;
+  const float* BETA = a.beta != nullptr ? a.beta + inst * a.beta_bs : nullptr;
+
+  // the workgroup's weight rows (hidden units j0 .. j0 + BJ - 1), every plane
+  // and both k stages: 6 P loads, waves 0-3 take the even ones, 4-7 the odd
+  {
+    const bf16_t* W0[3] = {reinterpret_cast<const bf16_t*>(a.W1), reinterpret_cast<const bf16_t*>(a.W3),
+                           reinterpret_cast<const bf16_t*>(a.W2x)};
+    const bf16_t* Wlo = reinterpret_cast<const bf16_t*>(a.Wlo);
+#pragma unroll
+    for (int x = 0; x < 3 * P * 2; ++x) {
+      if ((x & 1) != (wave >> 2)) continue;
+      const int m = x / (2 * P), pl = (x / 2) % P, stg = x % 2;
+      const bf16_t* base = (pl == 0 ? W0[m] : Wlo + (pl - 1) * a.wlo_ps + m * a.wlo_ms) + inst * DD;
+      TW::issue_one(s_w + x * WB, base, D, j0, D - 1, stg * BKK, wave & 3, lane, 0);
+    }
+  }
+
+  // K and V of a tile go through registers: lane q of the workgroup fetches
+  // chunk q of each 64 x 64 stage (the chunk its direct load would fetch) and
+  // later stores it at LDS position q
+  const int q = tid;
+  const int kr = q / TT::CPR, kc = TT::swz(kr, q % TT::CPR);
+  // (named registers, not an array: an array captured by the lambdas is
+  // kept in scratch memory)
+  uint4 pk0, pk1, pk2, pk3;
+  float plr = 0.f;
+  auto fetch = [&](int tb) {
+    const int64_t t0 = a.upd_t0 + (int64_t)tb * UDW2_T;
+    const int nv = (int)min((int64_t)UDW2_T, tend - t0);
+    const int64_t row = min(t0 + kr, tend - 1);
+    const uint4* kp = reinterpret_cast<const uint4*>(K + row * D + kc * 8);
+    const uint4* vp = reinterpret_cast<const uint4*>(V + row * D + kc * 8);
+    pk0 = kp[0];
+    pk1 = kp[BKK / 8];
+    pk2 = vp[0];
+    pk3 = vp[BKK / 8];
+    if (tid < 3 * UDW2_T) plr = LR[t0 * 3 + min(tid, nv * 3 - 1)];
+    else if (tid < 4 * UDW2_T && BETA != nullptr) plr = BETA[t0 + min(tid - 3 * UDW2_T, nv - 1)];
+  };
+  auto stash = [&]() {
+    *reinterpret_cast<uint4*>(s_kv + 0 * TB + q * 16) = pk0;
+    *reinterpret_cast<uint4*>(s_kv + 1 * TB + q * 16) = pk1;
+    *reinterpret_cast<uint4*>(s_kv + 2 * TB + q * 16) = pk2;
+    *reinterpret_cast<uint4*>(s_kv + 3 * TB + q * 16) = pk3;
+    if (tid < 3 * UDW2_T) s_lr[tid] = plr;
+    else if (tid < 4 * UDW2_T) s_beta[tid - 3 * UDW2_T] = plr;
+  };
+
+  f32x4 cu1[2], cu3[2], cu2[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) cu1[c] = cu3[c] = cu2[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int tb0 = split * g.tps, tb1 = min(ntiles, tb0 + g.tps);
+  if (tb0 < tb1) fetch(tb0);
+  wait_vm<0>();   // the weight rows (direct loads) and the first tile
+  if (tb0 < tb1) stash();
+  wait_lgkm0();
+  bar();
+
+  for (int tb = tb0; tb < tb1; ++tb) {
+    const int64_t t0 = a.upd_t0 + (int64_t)tb * UDW2_T;
+    if (tb + 1 < tb1) fetch(tb + 1);   // in flight during this tile
+
+    // forward on tokens 16 tw .. and hidden units 16 hw .. of the tile
+    f32x4 accA = f32x4{0.f, 0.f, 0.f, 0.f}, accB = accA, accG = accA;
+#pragma unroll
+    for (int kk = 0; kk < UDW_D; kk += 32) {
+      const int st = kk / BKK, kl = kk % BKK;
+      const bf16x8 fk = dfrag_row<TT>(s_kv + st * TB, tw * 16, kl, lane);
+      const bf16x8 fv = dfrag_row<TT>(s_kv + (2 + st) * TB, tw * 16, kl, lane);
+#pragma unroll
+      for (int pl = P - 1; pl >= 0; --pl) {
+        const bf16x8 f1 = dfrag_row<TW>(s_w + ((0 * P + pl) * 2 + st) * WB, hw * 16, kl, lane);
+        const bf16x8 f3 = dfrag_row<TW>(s_w + ((1 * P + pl) * 2 + st) * WB, hw * 16, kl, lane);
+        const bf16x8 f2 = dfrag_row<TW>(s_w + ((2 * P + pl) * 2 + st) * WB, hw * 16, kl, lane);
+        accA = mfma(fk, f1, accA);
+        accB = mfma(fk, f3, accB);
+        accG = mfma(fv, f2, accG);
+      }
+    }
+    // beta partial sum of this tile (chunk mean), once per tile
+    if (BETA != nullptr && jb == 0 && wave == 0) {
+      const float bs = wave_sum(t0 + lane < tend ? s_beta[lane] : 0.f);
+      if (lane == 0) a.bpart[(int64_t)inst * g.nbp + tb] = bs;
+    }
+    // SwiGLU backward terms, split into planes, into the update-term rows
+    // (zero past the chunk end)
+    {
+      const int tl = tw * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
+      const int col = hw * 16 + (lane & 15);
+      float u1[4], u3[4], u2[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = t0 + tl + r < tend;
+        const float e1 = ok ? s_lr[(tl + r) * 3 + 0] : 0.f;
+        const float e2 = ok ? s_lr[(tl + r) * 3 + 1] : 0.f;
+        const float e3 = ok ? s_lr[(tl + r) * 3 + 2] : 0.f;
+        const float x = accA[r], bb = accB[r], gg = accG[r];
+        const float sg = fast_sigmoid(x);
+        const float sx = x * sg;
+        const float sp = sg * (1.0f + x * (1.0f - sg));
+        u1[r] = e1 * gg * bb * sp;
+        u3[r] = e3 * gg * sx;
+        u2[r] = e2 * sx * bb;
+      }
+      const int chunk = tl >> 3, half = (tl >> 2) & 1;
+      const float* terms[3] = {u1, u3, u2};
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        const int row = m * BJ + col;
+        uint32_t h[4][P];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) split_planes<P>(terms[m][r], h[r]);
+        char* dst = s_e + row * ERB + ((chunk ^ (row & 7)) << 4) + (half << 3);
+#pragma unroll
+        for (int pl = 0; pl < P; ++pl)
+          *reinterpret_cast<uint2*>(dst + pl * EPL) = make_uint2(h[0][pl] | (h[1][pl] << 16), h[2][pl] | (h[3][pl] << 16));
+      }
+    }
+    wait_lgkm0();
+    bar();   // update terms visible
+
+    // contraction over the tile's 64 tokens: hidden rows j0 + 16 jw .. +15,
+    // d columns 32 cq .. +31 (k stage cq / 2 of K, V)
+    {
+      const char* kt = s_kv + (cq >> 1) * TB;
+      const char* vt = kt + 2 * TB;
+      const int cn = 32 * (cq & 1);
+      const int jr = 16 * jw + (lane & 15);
+#pragma unroll
+      for (int kk = 0; kk < UDW2_T; kk += 32) {
+        bf16x8 fbk[2], fbv[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          fbk[c] = dfrag_col<TT>(kt, cn + 16 * c, kk, lane);
+          fbv[c] = dfrag_col<TT>(vt, cn + 16 * c, kk, lane);
+        }
+        const int chunk = (kk >> 3) + (lane >> 4);
+        const int off = ((chunk ^ (jr & 7)) << 4);
+#pragma unroll
+        for (int pl = P - 1; pl >= 0; --pl) {
+          const char* ep = s_e + pl * EPL;
+          const bf16x8 fa1 = *reinterpret_cast<const bf16x8*>(ep + jr * ERB + off);
+          const bf16x8 fa3 = *reinterpret_cast<const bf16x8*>(ep + (BJ + jr) * ERB + off);
+          const bf16x8 fa2 = *reinterpret_cast<const bf16x8*>(ep + (2 * BJ + jr) * ERB + off);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            cu1[c] = mfma(fbk[c], fa1, cu1[c]);
+            cu3[c] = mfma(fbk[c], fa3, cu3[c]);
+            cu2[c] = mfma(fa2, fbv[c], cu2[c]);
+          }
+        }
+      }
+    }
+    wait_lgkm0();
+    bar();   // every wave is done with K, V, the learning rates and the update terms
+    if (tb + 1 < tb1) {
+      stash();   // waits for the fetch
+      wait_lgkm0();
+      bar();
+    }
+  }
+
+  float* Pp = g.part + (int64_t)split * g.part_ss + (int64_t)inst * 3 * DD;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int j = j0 + 16 * jw + (lane & 15);
+    const int cc = 32 * cq + 16 * c + 4 * (lane >> 4);
+    const float y1[4] = {cu1[c][0], cu1[c][1], cu1[c][2], cu1[c][3]};
+    const float y3[4] = {cu3[c][0], cu3[c][1], cu3[c][2], cu3[c][3]};
+    store4(Pp + (int64_t)j * D + cc, y1);
+    store4(Pp + DD + (int64_t)j * D + cc, y3);
+    const int c2 = 32 * cq + 16 * c + (lane & 15);
+    const int j2 = j0 + 16 * jw + 4 * (lane >> 4);
+    const float y2[4] = {cu2[c][0], cu2[c][1], cu2[c][2], cu2[c][3]};
+    store4(Pp + 2 * DD + (int64_t)c2 * D + j2, y2);
+  }
+}
+
+// =========================================================================
 // bf16 apply forward tile (same contract as app_fwd_kernel)
 template <int BJ, int BKK, int NST, bool OUT = false>
 __global__ __launch_bounds__(NT, 2) void dapp_fwd_kernel(AppFwdArgs a) {

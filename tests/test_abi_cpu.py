@@ -211,9 +211,15 @@ def test_workspace_size_properties():
         lact.workspace_size(P(d=96), 512, 128)
     # explicit schedule equal to the uniform one gives the same size
     assert lact.workspace_size(p, 512, 128, 0, [0, 128, 256, 384, 512], [3, 3, 3, 3]) == a
-    # the view-set schedule: one long update chunk, then the targets
+    # the view-set schedule: one long update chunk, then the targets; its
+    # update is the fused kernel, whose update terms never leave the chip, so
+    # no buffer for them is sized
     v = lact.workspace_size(P(n_inst=6, d=128), 200704, 0, 1, [0, 196608, 200704], [1, 2])
-    assert v > 6 * 196608 * 3 * 128 * 2
+    assert 0 < v < 6 * 196608 * 3 * 128 * 2
+    # 2,048-token chunks at d = 384 (separate update forward and contraction):
+    # one chunk's update terms are sized
+    u = lact.workspace_size(P(n_inst=4, d=384), 32768, 2048)
+    assert u > 4 * 2048 * 3 * 384 * 2
 
 
 @device_free

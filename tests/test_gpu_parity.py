@@ -133,6 +133,16 @@ def _small_video_noisy_first():
     return dataclasses.replace(c, n_inst=3, L=b[-1], bounds=b, flags=f)
 
 
+def _small_video_fused(noisy_first=False):
+    """Video schedule with clean chunks of 1,100 tokens: long enough for the
+    fused multi-plane update (17 token tiles of 64, the last one ragged)."""
+    import dataclasses
+    c = W.WORKLOADS[7 if noisy_first else 5]
+    sched = W.video_schedule_noisy_first if noisy_first else W.video_schedule
+    b, f = sched(3, 1100)
+    return dataclasses.replace(c, n_inst=3, L=b[-1], bounds=b, flags=f)
+
+
 SMALL[4] = _small_viewset()
 SMALL[5] = _small_video()
 SMALL[6] = _small_prefill()
@@ -142,7 +152,11 @@ SMALL[9] = W.WORKLOADS[9].scaled(n_inst=2, L=3 * 512 + 200, chunk=512)
 SMALL[10] = W.WORKLOADS[10].scaled(n_inst=2, L=3 * 512 + 200, chunk=512)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
+SMALL["video_fused"] = _small_video_fused()
+SMALL["video_noisy_first_fused"] = _small_video_fused(noisy_first=True)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, "video_fused", "video_noisy_first_fused"])
 def test_layer_reduced_size(lact, cid):
     wl = SMALL[cid]
     log(f"layer reduced cfg{cid}: n={wl.n_inst} D={wl.D} L={wl.L} chunks={wl.n_chunks}")
@@ -193,7 +207,7 @@ def test_layer_mixed_schedule_plain_bf16(lact, order, sched):
     assert max(errs.values()) <= wl.tol, errs
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, "fused_update"])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, "fused_update", "video_fused"])
 def test_layer_is_deterministic(lact, cid):
     """Every workload (reduced) run twice gives bitwise-identical outputs and
     state: no atomics, every reduction in a fixed order.  "fused_update": the
@@ -446,6 +460,40 @@ def test_long_chunk_update_fused(lact, n, Lc, opt):
                 errs["M" + nm[1]] = max(errs.get("M" + nm[1], 0), rel_err(from_dev(Ms[j], torch)[i], Mr[j]))
     log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
     assert max(errs.values()) <= 2e-2, errs
+
+
+@pytest.mark.parametrize("n,Lc,opt,planes", [(2, 1024, W.OPT_GD, 3), (3, 1024 + 77, W.OPT_MOMENTUM, 3),
+                                             (3, 4680, W.OPT_MUON, 3), (2, 3000 + 5, W.OPT_MUON_MOMENTUM, 3),
+                                             (5, 2100, W.OPT_MUON, 2), (2, 1500 + 33, W.OPT_MOMENTUM, 2)])
+def test_long_chunk_update_fused_planes(lact, n, Lc, opt, planes):
+    """Chunks of >= 1,024 tokens at d = dh = 128 with two or three weight
+    planes run the fused multi-plane update (update terms split into planes
+    in LDS, several token tiles per split, ragged last tile, beta partial
+    sums for momentum); seq_stride > Lc."""
+    log(f"fused plane update n={n} Lc={Lc} opt={opt} planes={planes}")
+    D, S = 128, Lc + 40
+    inp = _rand_inputs(n, S, D, W.DTYPE_BF16, seed=Lc + 7 * opt + planes)
+    rng = np.random.default_rng(9)
+    beta = rng.uniform(0.5, 0.99, (n, S)).astype(np.float32)
+    M0 = [(rng.standard_normal((n, D, D)) * 0.01).astype(np.float32) for _ in range(3)]
+    k, v, lr = to_dev(inp.k, torch), to_dev(inp.v, torch), to_dev(inp.lr, torch)
+    Ws = [to_dev(w, torch).clone() for w in (inp.W1, inp.W2, inp.W3)]
+    mom = opt in (W.OPT_MOMENTUM, W.OPT_MUON_MOMENTUM)
+    Ms = [to_dev(m, torch).clone() for m in M0] if mom else [None] * 3
+    lact.chunk_update(k, v, lr, to_dev(beta, torch) if mom else None, *Ws, *Ms, Lc=Lc, opt=opt,
+                      rec_planes=planes)
+    torch.cuda.synchronize()
+    errs = {}
+    for i in range(n):
+        Wr, Mr = O.update_step([O.f64(inp.W1[i]), O.f64(inp.W2[i]), O.f64(inp.W3[i])],
+                               [O.f64(m[i]) for m in M0], O.f64(inp.k[i][:Lc]), O.f64(inp.v[i][:Lc]),
+                               O.f64(inp.lr[i][:Lc]), O.f64(beta[i][:Lc]), opt)
+        for j, nm in enumerate(["W1", "W2", "W3"]):
+            errs[nm] = max(errs.get(nm, 0), rel_err(from_dev(Ws[j], torch)[i], Wr[j]))
+            if mom:
+                errs["M" + nm[1]] = max(errs.get("M" + nm[1], 0), rel_err(from_dev(Ms[j], torch)[i], Mr[j]))
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= 1e-3, errs
 
 
 def test_layer_d128_fused_apply_with_output_scale(lact):

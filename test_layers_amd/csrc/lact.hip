@@ -320,14 +320,17 @@ bool fused_update(const lact_problem& p, int64_t C) {
   return (f == PBF16X2 || f == PBF16X3) && C >= 1024;
 }
 
-// its token split (64-token tiles), every split non-empty.  Plain bf16 (two
-// hidden blocks per instance): about one workgroup per CU.  Multi-plane (four
-// hidden blocks of 32, one workgroup per CU by LDS): the split count that
-// minimises rounds of workgroups x tiles per workgroup, the smaller on ties
+// its token split, every split non-empty.  Plain bf16 (64-token tiles, two
+// hidden blocks per instance): about one workgroup per CU.  Multi-plane
+// (32-token tiles, four hidden blocks of 32, one workgroup per CU): the split
+// count that minimises rounds of workgroups x tiles per workgroup, the
+// smaller on ties
 void udw_split(const lact_problem& p, int64_t C, int& S, int& tps) {
-  const int64_t tt = (C + UDW2_T - 1) / UDW2_T;
+  const bool plain = profile_of(p) == PBF16;
+  const int64_t T = plain ? UDW2_T : UDS_T;   // tokens per tile
+  const int64_t tt = (C + T - 1) / T;
   const int64_t n = std::max(1, p.n_inst);
-  if (profile_of(p) == PBF16) {
+  if (plain) {
     const int64_t per = 2 * n;
     const int64_t s0 = std::max<int64_t>(1, std::min<int64_t>(tt, NCU / per));
     tps = (int)((tt + s0 - 1) / s0);
@@ -425,8 +428,9 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   w.nslots = nupd + 1;
   w.ldE = round128(plan.max_upd);
   w.h_rows = h_rows;
-  // beta partial sums: one per 128-token tile, or per 64-token tile of the fused update
-  w.max_tt = (int)((plan.max_upd + UDW2_T - 1) / UDW2_T);
+  // beta partial sums: one per 128-token tile, or per token tile of the fused
+  // update (64 tokens, 32 for the multi-plane one)
+  w.max_tt = (int)((plan.max_upd + UDS_T - 1) / UDS_T);
   const size_t snap_el = (f == PF32) ? 4 : 2;
   w.snap_slot = align256(4 * n * D * Dh * snap_el);
   bool unfused = false;   // the fused update keeps its update terms in LDS
@@ -1105,7 +1109,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
         ud.part_ss = (int64_t)n * 3 * DD;
         ud.tps = tps;
         ud.splits = S;
-        ud.nbp = (int)((C + UDW2_T - 1) / UDW2_T);
+        ud.nbp = (int)((C + UDS_T - 1) / UDS_T);
         const int64_t grid = (int64_t)n * S * (UDW_D / UDP_BJ);
         if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
         KernelTimer kt(LACT_K_UPD, s);
@@ -1183,8 +1187,9 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     oa.opt = p.opt;
     oa.renorm = (p.flags & LACT_NO_RENORM) ? 0 : 1;
     oa.bpart = reinterpret_cast<const float*>(ws + w.bpart);
-    // beta partial sums: per 128-token tile, or per 64-token tile when fused
-    const int nbp = fused ? (int)((C + UDW2_T - 1) / UDW2_T) : ua.tiles_t;
+    // beta partial sums: per 128-token tile, or per tile of the fused update
+    const int ftile = PT::PL > 1 ? UDS_T : UDW2_T;
+    const int nbp = fused ? (int)((C + ftile - 1) / ftile) : ua.tiles_t;
     oa.nbp = nbp;
     oa.inv_len = 1.0f / (float)C;
     oa.snap[0] = slot(nu + 1, 0);

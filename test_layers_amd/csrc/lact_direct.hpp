@@ -977,42 +977,46 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dw2_kernel(UpdDwArgs g) {
 
 // =========================================================================
 // Fused update at d = dh = 128 for the multi-plane recurrence (P = 2 or 3
-// stored bf16 planes of the weights and of the update terms): per 64-token
+// stored bf16 planes of the weights and of the update terms): per 32-token
 // tile, the update forward A = K W1^T, B = K W3^T, G = V W2 over the tile's
 // tokens and the workgroup's 32 hidden units, the SwiGLU backward terms
 // ("大块测试时训练（LaCT）技术解析" §2.1, eqs. 4-5) split into P planes in
-// LDS, and at once the tile's share of U1 = E1^T K, U3 = E3^T K, U2 = V^T E2,
+// LDS, and the tile's share of U1 = E1^T K, U3 = E3^T K, U2 = V^T E2,
 // accumulated in registers over the workgroup's run of tiles; one fp32
 // partial per workgroup.  At this width the three planes of the update terms
-// would otherwise make a round trip through HBM (6 bytes per term).
-// Every product sums the plane pairs (plane p of the weights or update
-// terms with the single plane of k or v), smaller planes first.
-// LDS: the workgroup's weight rows, all planes, stay resident (24 KB per
-// plane); K and V of one tile (32 KB) are refilled from registers loaded
-// during the previous tile; the update-term planes take 12 KB each.
+// would otherwise make a round trip through HBM (6 bytes per term).  Every
+// product sums the plane pairs (plane p of the weights or update terms with
+// the single plane of k or v), smaller planes first.
+// The waves are specialised: the four forward waves hold the weight planes
+// of their 16 hidden units in registers for the whole run and produce the
+// update terms of tile s while the four contraction waves consume those of
+// tile s - 1, one barrier per step, so the forward's VALU epilogue overlaps
+// the contraction's MFMA work on every SIMD (one wave of each kind per
+// SIMD).  K and V stream through a four-deep direct-load ring (tile s + 2 is
+// loaded while tiles s and s - 1 are read); the update-term planes are
+// double-buffered.
 constexpr int UDP_BJ = 32;   // hidden units per workgroup
+constexpr int UDS_T = 32;   // tokens per tile
 
 template <int P>
 __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
   const UpdFwdArgs& a = g.u;
   constexpr int BKK = 64;
-  constexpr int NWV = DG_THREADS / WAVE;
   constexpr int BJ = UDP_BJ;
-  using TT = DTile<UDW2_T, BKK, NWV>;   // 64 tokens x 64 d: K, V stages
-  using TW = DTile<BJ, BKK, 4>;         // 32 hidden rows x 64 d: weight stages (loaded by four waves)
-  static_assert(TT::INSTR == 1 && TW::INSTR == 1 && UDW_D == 2 * BKK && NWV == 8, "tile shapes");
-  constexpr int TB = TT::BYTES, WB = TW::BYTES;
-  constexpr int ERB = UDW2_T * 2;       // update-term row: 64 tokens of bf16
-  constexpr int EPL = 3 * BJ * ERB;     // one plane of the update terms
-  __shared__ __attribute__((aligned(1024))) char s_w[3 * P * 2 * WB];   // [matrix W1 | W3 | W2^T][plane][k stage]
-  __shared__ __attribute__((aligned(1024))) char s_kv[4 * TB];         // K s0, K s1, V s0, V s1
-  __shared__ __attribute__((aligned(1024))) char s_e[P * EPL];         // [plane][U1 | U3 | U2 terms][64 tokens]
-  __shared__ __attribute__((aligned(16))) float s_lr[UDW2_T * 3];
-  __shared__ __attribute__((aligned(16))) float s_beta[UDW2_T];
+  constexpr int NKV = 4;                  // K, V ring depth
+  using TT = DTile<UDS_T, BKK, 4>;        // 32 tokens x 64 d (K, V stages), loaded by the four contraction waves
+  static_assert(TT::INSTR == 1 && UDW_D == 2 * BKK && DG_THREADS == 8 * WAVE, "tile shapes");
+  constexpr int TB = TT::BYTES;           // 4 KB
+  constexpr int KVB = 4 * TB;             // K s0, K s1, V s0, V s1
+  constexpr int ERB = UDS_T * 2;          // update-term row: 32 tokens of bf16 (4 chunks)
+  constexpr int EPL = 3 * BJ * ERB;       // one plane: rows U1 | U3 | U2 terms
+  __shared__ __attribute__((aligned(1024))) char s_kv[NKV * KVB];
+  __shared__ __attribute__((aligned(1024))) char s_e[2 * P * EPL];
+  __shared__ __attribute__((aligned(16))) float s_lr[NKV][128];   // 96 used (3 per token)
+  __shared__ __attribute__((aligned(16))) float s_beta[NKV][64];  // 32 used
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tw = wave >> 1, hw = wave & 1;   // forward: tokens 16 tw .., hidden 16 hw ..
-  const int jw = wave & 1, cq = wave >> 1;   // contraction: hidden rows 16 jw .., d columns 32 cq ..
+  const bool fwd = wave < 4;
   const int D = UDW_D;
   const int njb = UDW_D / BJ;
   int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -1023,187 +1027,195 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
   const int j0 = jb * BJ;
   const int64_t DD = (int64_t)D * D;
   const int64_t tend = a.upd_t0 + a.upd_len;
-  const int ntiles = (int)((a.upd_len + UDW2_T - 1) / UDW2_T);
+  const int ntiles = (int)((a.upd_len + UDS_T - 1) / UDS_T);
+  const int tb0 = split * g.tps, tb1 = min(ntiles, tb0 + g.tps);
+  const int nt = max(0, tb1 - tb0);
   const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + inst * a.k_bs;
   const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + inst * a.x_bs;
   const float* LR = a.lr + inst * a.lr_bs;
   const float* BETA = a.beta != nullptr ? a.beta + inst * a.beta_bs : nullptr;
 
-  // the workgroup's weight rows (hidden units j0 .. j0 + BJ - 1), every plane
-  // and both k stages: 6 P loads, waves 0-3 take the even ones, 4-7 the odd
-  {
-    const bf16_t* W0[3] = {reinterpret_cast<const bf16_t*>(a.W1), reinterpret_cast<const bf16_t*>(a.W3),
-                           reinterpret_cast<const bf16_t*>(a.W2x)};
-    const bf16_t* Wlo = reinterpret_cast<const bf16_t*>(a.Wlo);
-#pragma unroll
-    for (int x = 0; x < 3 * P * 2; ++x) {
-      if ((x & 1) != (wave >> 2)) continue;
-      const int m = x / (2 * P), pl = (x / 2) % P, stg = x % 2;
-      const bf16_t* base = (pl == 0 ? W0[m] : Wlo + (pl - 1) * a.wlo_ps + m * a.wlo_ms) + inst * DD;
-      TW::issue_one(s_w + x * WB, base, D, j0, D - 1, stg * BKK, wave & 3, lane, 0);
+  // contraction waves: loads of local tile i into ring slot i % NKV, five per
+  // wave (K, V stages, then learning rates or beta)
+  const int cw = wave & 3;
+  auto issue_tile = [&](int i) {
+    const int64_t t0 = a.upd_t0 + (int64_t)(tb0 + i) * UDS_T;
+    const int nv = (int)min((int64_t)UDS_T, tend - t0);
+    char* kv = s_kv + (i % NKV) * KVB;
+    TT::issue_one(kv, K, D, t0, tend - 1, 0, cw, lane, 0);
+    TT::issue_one(kv + TB, K, D, t0, tend - 1, BKK, cw, lane, 0);
+    TT::issue_one(kv + 2 * TB, V, D, t0, tend - 1, 0, cw, lane, 0);
+    TT::issue_one(kv + 3 * TB, V, D, t0, tend - 1, BKK, cw, lane, 0);
+    const float* src;
+    uint32_t dst;
+    if (cw < 2) {   // learning rates: 96 values over two waves (the rest land in the padding)
+      src = LR + t0 * 3 + min(cw * 64 + lane, nv * 3 - 1);
+      dst = lds_off(&s_lr[i % NKV][cw * 64]);
+    } else if (cw == 2 && BETA != nullptr) {
+      src = BETA + t0 + min(lane, nv - 1);
+      dst = lds_off(&s_beta[i % NKV][0]);
+    } else {        // a harmless reload, so that every wave issues five loads per tile
+      src = LR + t0 * 3 + min(lane, nv * 3 - 1);
+      dst = lds_off(&s_lr[i % NKV][0]);
     }
+    dma4(src, __builtin_amdgcn_readfirstlane(dst));
+  };
+
+  if (fwd) {
+    // ---------------------------------------------------------------- forward waves
+    const int tf = wave >> 1, hf = wave & 1;   // tokens 16 tf .., hidden units j0 + 16 hf ..
+    // this wave's weight fragments, every plane: row j0 + 16 hf + lane % 16,
+    // k = 32 kk + 8 (lane / 16) .. + 7
+    bf16x8 wr[3][P][4];
+    {
+      const bf16_t* W0[3] = {reinterpret_cast<const bf16_t*>(a.W1), reinterpret_cast<const bf16_t*>(a.W3),
+                             reinterpret_cast<const bf16_t*>(a.W2x)};
+      const bf16_t* Wlo = reinterpret_cast<const bf16_t*>(a.Wlo);
+      const int64_t roff = (int64_t)(j0 + 16 * hf + (lane & 15)) * D + 8 * (lane >> 4);
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int pl = 0; pl < P; ++pl) {
+          const bf16_t* base = (pl == 0 ? W0[m] : Wlo + (pl - 1) * a.wlo_ps + m * a.wlo_ms) + inst * DD + roff;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) wr[m][pl][kk] = *reinterpret_cast<const bf16x8*>(base + 32 * kk);
+        }
+    }
+    bar();   // tile 0 has landed (the contraction waves waited for it)
+    for (int s = 0; s <= nt; ++s) {
+      if (s < nt) {
+        const int64_t t0 = a.upd_t0 + (int64_t)(tb0 + s) * UDS_T;
+        const char* kv = s_kv + (s % NKV) * KVB;
+        f32x4 accA = f32x4{0.f, 0.f, 0.f, 0.f}, accB = accA, accG = accA;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int st = kk >> 1, kl = (kk & 1) * 32;
+          const bf16x8 fk = dfrag_row<TT>(kv + st * TB, tf * 16, kl, lane);
+          const bf16x8 fv = dfrag_row<TT>(kv + (2 + st) * TB, tf * 16, kl, lane);
+#pragma unroll
+          for (int pl = P - 1; pl >= 0; --pl) {
+            accA = mfma(fk, wr[0][pl][kk], accA);
+            accB = mfma(fk, wr[1][pl][kk], accB);
+            accG = mfma(fv, wr[2][pl][kk], accG);
+          }
+        }
+        // beta partial sum of this tile (chunk mean), once per tile
+        if (BETA != nullptr && jb == 0 && wave == 0) {
+          const float bs = wave_sum(lane < UDS_T && t0 + lane < tend ? s_beta[s % NKV][lane] : 0.f);
+          if (lane == 0) a.bpart[(int64_t)inst * g.nbp + tb0 + s] = bs;
+        }
+        // SwiGLU backward terms, split into planes, into the update-term rows of
+        // buffer s % 2 (zero past the chunk end)
+        const float* lrs = s_lr[s % NKV];
+        const int tl = tf * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
+        const int col = hf * 16 + (lane & 15);
+        float u1[4], u3[4], u2[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = t0 + tl + r < tend;
+          const float e1 = ok ? lrs[(tl + r) * 3 + 0] : 0.f;
+          const float e2 = ok ? lrs[(tl + r) * 3 + 1] : 0.f;
+          const float e3 = ok ? lrs[(tl + r) * 3 + 2] : 0.f;
+          const float x = accA[r], bb = accB[r], gg = accG[r];
+          const float sg = fast_sigmoid(x);
+          const float sx = x * sg;
+          const float sp = sg * (1.0f + x * (1.0f - sg));
+          u1[r] = e1 * gg * bb * sp;
+          u3[r] = e3 * gg * sx;
+          u2[r] = e2 * sx * bb;
+        }
+        const int chunk = tl >> 3, half = (tl >> 2) & 1;
+        char* eb = s_e + (s & 1) * (P * EPL);
+        const float* terms[3] = {u1, u3, u2};
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+          const int row = m * BJ + col;
+          uint32_t h[4][P];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) split_planes<P>(terms[m][r], h[r]);
+          char* dst = eb + row * ERB + ((chunk ^ ((row >> 1) & 3)) << 4) + (half << 3);
+#pragma unroll
+          for (int pl = 0; pl < P; ++pl)
+            *reinterpret_cast<uint2*>(dst + pl * EPL) =
+                make_uint2(h[0][pl] | (h[1][pl] << 16), h[2][pl] | (h[3][pl] << 16));
+        }
+      }
+      wait_lgkm0();
+      bar();   // update terms of tile s written, tile s + 1 landed
+    }
+    return;
   }
 
-  // K and V of a tile go through registers: lane q of the workgroup fetches
-  // chunk q of each 64 x 64 stage (the chunk its direct load would fetch) and
-  // later stores it at LDS position q
-  const int q = tid;
-  const int kr = q / TT::CPR, kc = TT::swz(kr, q % TT::CPR);
-  // (named registers, not an array: an array captured by the lambdas is
-  // kept in scratch memory)
-  uint4 pk0, pk1, pk2, pk3;
-  float plr = 0.f;
-  auto fetch = [&](int tb) {
-    const int64_t t0 = a.upd_t0 + (int64_t)tb * UDW2_T;
-    const int nv = (int)min((int64_t)UDW2_T, tend - t0);
-    const int64_t row = min(t0 + kr, tend - 1);
-    const uint4* kp = reinterpret_cast<const uint4*>(K + row * D + kc * 8);
-    const uint4* vp = reinterpret_cast<const uint4*>(V + row * D + kc * 8);
-    pk0 = kp[0];
-    pk1 = kp[BKK / 8];
-    pk2 = vp[0];
-    pk3 = vp[BKK / 8];
-    if (tid < 3 * UDW2_T) plr = LR[t0 * 3 + min(tid, nv * 3 - 1)];
-    else if (tid < 4 * UDW2_T && BETA != nullptr) plr = BETA[t0 + min(tid - 3 * UDW2_T, nv - 1)];
-  };
-  auto stash = [&]() {
-    *reinterpret_cast<uint4*>(s_kv + 0 * TB + q * 16) = pk0;
-    *reinterpret_cast<uint4*>(s_kv + 1 * TB + q * 16) = pk1;
-    *reinterpret_cast<uint4*>(s_kv + 2 * TB + q * 16) = pk2;
-    *reinterpret_cast<uint4*>(s_kv + 3 * TB + q * 16) = pk3;
-    if (tid < 3 * UDW2_T) s_lr[tid] = plr;
-    else if (tid < 4 * UDW2_T) s_beta[tid - 3 * UDW2_T] = plr;
-  };
-
-  f32x4 cu1[2], cu3[2], cu2[2];
+  // ---------------------------------------------------------------- contraction waves
+  // d columns 32 cw .. + 31 (k stage cw / 2 of K, V), all 32 hidden rows:
+  // U1, U3 [hidden x d] and U2 [d x hidden], 2 x 2 fragments each
+  if (nt > 0) issue_tile(0);
+  if (nt > 1) issue_tile(1);
+  if (nt > 1) wait_vm<5>();
+  else wait_vm<0>();
+  bar();   // tile 0 landed
+  f32x4 cu1[2][2], cu3[2][2], cu2[2][2];   // [d fragment][hidden fragment]
 #pragma unroll
-  for (int c = 0; c < 2; ++c) cu1[c] = cu3[c] = cu2[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int tb0 = split * g.tps, tb1 = min(ntiles, tb0 + g.tps);
-  if (tb0 < tb1) fetch(tb0);
-  wait_vm<0>();   // the weight rows (direct loads) and the first tile
-  if (tb0 < tb1) stash();
-  wait_lgkm0();
-  bar();
-
-  for (int tb = tb0; tb < tb1; ++tb) {
-    const int64_t t0 = a.upd_t0 + (int64_t)tb * UDW2_T;
-    if (tb + 1 < tb1) fetch(tb + 1);   // in flight during this tile
-
-    // forward on tokens 16 tw .. and hidden units 16 hw .. of the tile
-    f32x4 accA = f32x4{0.f, 0.f, 0.f, 0.f}, accB = accA, accG = accA;
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int kk = 0; kk < UDW_D; kk += 32) {
-      const int st = kk / BKK, kl = kk % BKK;
-      const bf16x8 fk = dfrag_row<TT>(s_kv + st * TB, tw * 16, kl, lane);
-      const bf16x8 fv = dfrag_row<TT>(s_kv + (2 + st) * TB, tw * 16, kl, lane);
+    for (int i = 0; i < 2; ++i) cu1[c][i] = cu3[c][i] = cu2[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int cn = 32 * (cw & 1);
+  for (int s = 0; s <= nt; ++s) {
+    // slot (s + 2) % 4 held tile s - 2, read by the forward waves in step s - 2 and here in step s - 1
+    if (s + 2 < nt) issue_tile(s + 2);
+    if (s >= 1) {
+      const int i = s - 1;   // consume tile i
+      const char* kt = s_kv + (i % NKV) * KVB + (cw >> 1) * TB;
+      const char* vt = kt + 2 * TB;
+      const char* eb = s_e + (i & 1) * (P * EPL);
+      bf16x8 fbk[2], fbv[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        fbk[c] = dfrag_col<TT>(kt, cn + 16 * c, 0, lane);
+        fbv[c] = dfrag_col<TT>(vt, cn + 16 * c, 0, lane);
+      }
 #pragma unroll
       for (int pl = P - 1; pl >= 0; --pl) {
-        const bf16x8 f1 = dfrag_row<TW>(s_w + ((0 * P + pl) * 2 + st) * WB, hw * 16, kl, lane);
-        const bf16x8 f3 = dfrag_row<TW>(s_w + ((1 * P + pl) * 2 + st) * WB, hw * 16, kl, lane);
-        const bf16x8 f2 = dfrag_row<TW>(s_w + ((2 * P + pl) * 2 + st) * WB, hw * 16, kl, lane);
-        accA = mfma(fk, f1, accA);
-        accB = mfma(fk, f3, accB);
-        accG = mfma(fv, f2, accG);
-      }
-    }
-    // beta partial sum of this tile (chunk mean), once per tile
-    if (BETA != nullptr && jb == 0 && wave == 0) {
-      const float bs = wave_sum(t0 + lane < tend ? s_beta[lane] : 0.f);
-      if (lane == 0) a.bpart[(int64_t)inst * g.nbp + tb] = bs;
-    }
-    // SwiGLU backward terms, split into planes, into the update-term rows
-    // (zero past the chunk end)
-    {
-      const int tl = tw * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
-      const int col = hw * 16 + (lane & 15);
-      float u1[4], u3[4], u2[4];
+        const char* ep = eb + pl * EPL;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = t0 + tl + r < tend;
-        const float e1 = ok ? s_lr[(tl + r) * 3 + 0] : 0.f;
-        const float e2 = ok ? s_lr[(tl + r) * 3 + 1] : 0.f;
-        const float e3 = ok ? s_lr[(tl + r) * 3 + 2] : 0.f;
-        const float x = accA[r], bb = accB[r], gg = accG[r];
-        const float sg = fast_sigmoid(x);
-        const float sx = x * sg;
-        const float sp = sg * (1.0f + x * (1.0f - sg));
-        u1[r] = e1 * gg * bb * sp;
-        u3[r] = e3 * gg * sx;
-        u2[r] = e2 * sx * bb;
-      }
-      const int chunk = tl >> 3, half = (tl >> 2) & 1;
-      const float* terms[3] = {u1, u3, u2};
-#pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        const int row = m * BJ + col;
-        uint32_t h[4][P];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) split_planes<P>(terms[m][r], h[r]);
-        char* dst = s_e + row * ERB + ((chunk ^ (row & 7)) << 4) + (half << 3);
-#pragma unroll
-        for (int pl = 0; pl < P; ++pl)
-          *reinterpret_cast<uint2*>(dst + pl * EPL) = make_uint2(h[0][pl] | (h[1][pl] << 16), h[2][pl] | (h[3][pl] << 16));
-      }
-    }
-    wait_lgkm0();
-    bar();   // update terms visible
-
-    // contraction over the tile's 64 tokens: hidden rows j0 + 16 jw .. +15,
-    // d columns 32 cq .. +31 (k stage cq / 2 of K, V)
-    {
-      const char* kt = s_kv + (cq >> 1) * TB;
-      const char* vt = kt + 2 * TB;
-      const int cn = 32 * (cq & 1);
-      const int jr = 16 * jw + (lane & 15);
-#pragma unroll
-      for (int kk = 0; kk < UDW2_T; kk += 32) {
-        bf16x8 fbk[2], fbv[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          fbk[c] = dfrag_col<TT>(kt, cn + 16 * c, kk, lane);
-          fbv[c] = dfrag_col<TT>(vt, cn + 16 * c, kk, lane);
-        }
-        const int chunk = (kk >> 3) + (lane >> 4);
-        const int off = ((chunk ^ (jr & 7)) << 4);
-#pragma unroll
-        for (int pl = P - 1; pl >= 0; --pl) {
-          const char* ep = s_e + pl * EPL;
+        for (int h = 0; h < 2; ++h) {
+          const int jr = 16 * h + (lane & 15);
+          const int off = (((lane >> 4) ^ ((jr >> 1) & 3)) << 4);
           const bf16x8 fa1 = *reinterpret_cast<const bf16x8*>(ep + jr * ERB + off);
           const bf16x8 fa3 = *reinterpret_cast<const bf16x8*>(ep + (BJ + jr) * ERB + off);
           const bf16x8 fa2 = *reinterpret_cast<const bf16x8*>(ep + (2 * BJ + jr) * ERB + off);
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            cu1[c] = mfma(fbk[c], fa1, cu1[c]);
-            cu3[c] = mfma(fbk[c], fa3, cu3[c]);
-            cu2[c] = mfma(fa2, fbv[c], cu2[c]);
+            cu1[c][h] = mfma(fbk[c], fa1, cu1[c][h]);
+            cu3[c][h] = mfma(fbk[c], fa3, cu3[c][h]);
+            cu2[c][h] = mfma(fa2, fbv[c], cu2[c][h]);
           }
         }
       }
     }
+    // tile s + 1 must have landed before the barrier (tile s + 2 may be in flight)
+    if (s + 2 < nt) wait_vm<5>();
+    else wait_vm<0>();
     wait_lgkm0();
-    bar();   // every wave is done with K, V, the learning rates and the update terms
-    if (tb + 1 < tb1) {
-      stash();   // waits for the fetch
-      wait_lgkm0();
-      bar();
-    }
+    bar();
   }
 
   float* Pp = g.part + (int64_t)split * g.part_ss + (int64_t)inst * 3 * DD;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int j = j0 + 16 * jw + (lane & 15);
-    const int cc = 32 * cq + 16 * c + 4 * (lane >> 4);
-    const float y1[4] = {cu1[c][0], cu1[c][1], cu1[c][2], cu1[c][3]};
-    const float y3[4] = {cu3[c][0], cu3[c][1], cu3[c][2], cu3[c][3]};
-    store4(Pp + (int64_t)j * D + cc, y1);
-    store4(Pp + DD + (int64_t)j * D + cc, y3);
-    const int c2 = 32 * cq + 16 * c + (lane & 15);
-    const int j2 = j0 + 16 * jw + 4 * (lane >> 4);
-    const float y2[4] = {cu2[c][0], cu2[c][1], cu2[c][2], cu2[c][3]};
-    store4(Pp + 2 * DD + (int64_t)c2 * D + j2, y2);
-  }
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = j0 + 16 * h + (lane & 15);
+      const int cc = 32 * cw + 16 * c + 4 * (lane >> 4);
+      const float y1[4] = {cu1[c][h][0], cu1[c][h][1], cu1[c][h][2], cu1[c][h][3]};
+      const float y3[4] = {cu3[c][h][0], cu3[c][h][1], cu3[c][h][2], cu3[c][h][3]};
+      store4(Pp + (int64_t)j * D + cc, y1);
+      store4(Pp + DD + (int64_t)j * D + cc, y3);
+      const int c2 = 32 * cw + 16 * c + (lane & 15);
+      const int j2 = j0 + 16 * h + 4 * (lane >> 4);
+      const float y2[4] = {cu2[c][h][0], cu2[c][h][1], cu2[c][h][2], cu2[c][h][3]};
+      store4(Pp + 2 * DD + (int64_t)c2 * D + j2, y2);
+    }
 }
 
 // =========================================================================

@@ -1086,6 +1086,11 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
       if (s < nt) {
         const int64_t t0 = a.upd_t0 + (int64_t)(tb0 + s) * UDS_T;
         const char* kv = s_kv + (s % NKV) * KVB;
+        // learning rates of this lane's four tokens (12 consecutive values),
+        // read ahead of the products so that their latency is hidden
+        const int tl = tf * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
+        const float4* lrv = reinterpret_cast<const float4*>(s_lr[s % NKV] + tl * 3);
+        const float4 l0 = lrv[0], l1 = lrv[1], l2 = lrv[2];
         f32x4 accA = f32x4{0.f, 0.f, 0.f, 0.f}, accB = accA, accG = accA;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -1106,16 +1111,15 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
         }
         // SwiGLU backward terms, split into planes, into the update-term rows of
         // buffer s % 2 (zero past the chunk end)
-        const float* lrs = s_lr[s % NKV];
-        const int tl = tf * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
+        const float lrr[12] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w, l2.x, l2.y, l2.z, l2.w};
         const int col = hf * 16 + (lane & 15);
         float u1[4], u3[4], u2[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool ok = t0 + tl + r < tend;
-          const float e1 = ok ? lrs[(tl + r) * 3 + 0] : 0.f;
-          const float e2 = ok ? lrs[(tl + r) * 3 + 1] : 0.f;
-          const float e3 = ok ? lrs[(tl + r) * 3 + 2] : 0.f;
+          const float e1 = ok ? lrr[r * 3 + 0] : 0.f;
+          const float e2 = ok ? lrr[r * 3 + 1] : 0.f;
+          const float e3 = ok ? lrr[r * 3 + 2] : 0.f;
           const float x = accA[r], bb = accB[r], gg = accG[r];
           const float sg = fast_sigmoid(x);
           const float sx = x * sg;
@@ -1126,18 +1130,25 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
         }
         const int chunk = tl >> 3, half = (tl >> 2) & 1;
         char* eb = s_e + (s & 1) * (P * EPL);
-        const float* terms[3] = {u1, u3, u2};
+        float* terms[3] = {u1, u3, u2};
 #pragma unroll
         for (int m = 0; m < 3; ++m) {
           const int row = m * BJ + col;
-          uint32_t h[4][P];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) split_planes<P>(terms[m][r], h[r]);
           char* dst = eb + row * ERB + ((chunk ^ ((row >> 1) & 3)) << 4) + (half << 3);
+          // planes of the four terms, two values per conversion (the same
+          // round-to-nearest-even planes as split_planes)
+          float* v = terms[m];
 #pragma unroll
-          for (int pl = 0; pl < P; ++pl)
-            *reinterpret_cast<uint2*>(dst + pl * EPL) =
-                make_uint2(h[0][pl] | (h[1][pl] << 16), h[2][pl] | (h[3][pl] << 16));
+          for (int pl = 0; pl < P; ++pl) {
+            const uint32_t w0 = pack_bf16x2(v[0], v[1]), w1 = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(dst + pl * EPL) = make_uint2(w0, w1);
+            if (pl + 1 < P) {
+              v[0] -= __uint_as_float(w0 << 16);
+              v[1] -= __uint_as_float(w0 & 0xffff0000u);
+              v[2] -= __uint_as_float(w1 << 16);
+              v[3] -= __uint_as_float(w1 & 0xffff0000u);
+            }
+          }
         }
       }
       wait_lgkm0();

@@ -320,33 +320,23 @@ bool fused_update(const lact_problem& p, int64_t C) {
   return (f == PBF16X2 || f == PBF16X3) && C >= 1024;
 }
 
-// its token split, every split non-empty.  Plain bf16 (64-token tiles, two
-// hidden blocks per instance): about one workgroup per CU.  Multi-plane
-// (32-token tiles, four hidden blocks of 32, one workgroup per CU): the split
-// count that minimises rounds of workgroups x tiles per workgroup, the
-// smaller on ties
+// its token split (32-token tiles, 128 / udp_bj hidden blocks per instance,
+// one workgroup per CU by LDS), every split non-empty: the split count that
+// minimises rounds of workgroups x tiles per workgroup, the smaller on ties
 void udw_split(const lact_problem& p, int64_t C, int& S, int& tps) {
-  const bool plain = profile_of(p) == PBF16;
-  const int64_t T = plain ? UDW2_T : UDS_T;   // tokens per tile
-  const int64_t tt = (C + T - 1) / T;
-  const int64_t n = std::max(1, p.n_inst);
-  if (plain) {
-    const int64_t per = 2 * n;
-    const int64_t s0 = std::max<int64_t>(1, std::min<int64_t>(tt, NCU / per));
-    tps = (int)((tt + s0 - 1) / s0);
-  } else {
-    const int64_t per = (UDW_D / UDP_BJ) * n;
-    int64_t best = -1, bt = tt;
-    for (int64_t c = 1; c <= std::min<int64_t>(tt, 32); ++c) {
-      const int64_t t = (tt + c - 1) / c;
-      const int64_t cost = ((per * c + NCU - 1) / NCU) * t;
-      if (best < 0 || cost < best) {
-        best = cost;
-        bt = t;
-      }
+  const int64_t tt = (C + UDS_T - 1) / UDS_T;
+  const int planes = profile_of(p) == PBF16 ? 1 : 2;
+  const int64_t per = (UDW_D / udp_bj(planes)) * (int64_t)std::max(1, p.n_inst);
+  int64_t best = -1, bt = tt;
+  for (int64_t c = 1; c <= std::min<int64_t>(tt, 32); ++c) {
+    const int64_t t = (tt + c - 1) / c;
+    const int64_t cost = ((per * c + NCU - 1) / NCU) * t;
+    if (best < 0 || cost < best) {
+      best = cost;
+      bt = t;
     }
-    tps = (int)bt;
   }
+  tps = (int)bt;
   S = (int)((tt + tps - 1) / tps);
 }
 
@@ -428,8 +418,8 @@ Ws layout(const lact_problem& p, const Plan& plan) {
   w.nslots = nupd + 1;
   w.ldE = round128(plan.max_upd);
   w.h_rows = h_rows;
-  // beta partial sums: one per 128-token tile, or per token tile of the fused
-  // update (64 tokens, 32 for the multi-plane one)
+  // beta partial sums: one per 128-token tile, or per 32-token tile of the
+  // fused update
   w.max_tt = (int)((plan.max_upd + UDS_T - 1) / UDS_T);
   const size_t snap_el = (f == PF32) ? 4 : 2;
   w.snap_slot = align256(4 * n * D * Dh * snap_el);
@@ -1082,23 +1072,9 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     int64_t kps = 0;
     if (fused) {
       // update forward + contraction in one kernel, fp32 partials per split
-      if constexpr (PT::UPD_FROM_SNAP) {
-        int tps = 0;
-        udw_split(p, C, S, tps);
-        if (S > w.S) return fail(LACT_ERR_UNSUPPORTED, "internal: token split %d exceeds workspace plan %d", S, w.S);
-        UpdDwArgs ud;
-        memset(&ud, 0, sizeof(ud));
-        ud.u = ua;
-        ud.part = reinterpret_cast<float*>(ws + w.part);
-        ud.part_ss = (int64_t)n * 3 * DD;
-        ud.tps = tps;
-        ud.splits = S;
-        ud.nbp = (int)((C + UDW2_T - 1) / UDW2_T);
-        const int64_t grid = (int64_t)n * S * (UDW_D / 64);
-        KernelTimer kt(LACT_K_UPD, s);
-        LACT_LAUNCH((dupd_dw2_kernel<64>), dim3((unsigned)grid), dim3(DG_THREADS), s, ud);
-        HIP_TRY(hipGetLastError());
-      } else if constexpr (PT::PL > 1) {
+      if constexpr (PT::UPD_FROM_SNAP || PT::PL > 1) {
+        constexpr int FP = PT::PL > 1 ? PT::PL : 1;   // weight planes
+        constexpr int BJ = udp_bj(FP);
         int tps = 0;
         udw_split(p, C, S, tps);
         if (S > w.S) return fail(LACT_ERR_UNSUPPORTED, "internal: token split %d exceeds workspace plan %d", S, w.S);
@@ -1110,10 +1086,10 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
         ud.tps = tps;
         ud.splits = S;
         ud.nbp = (int)((C + UDS_T - 1) / UDS_T);
-        const int64_t grid = (int64_t)n * S * (UDW_D / UDP_BJ);
+        const int64_t grid = (int64_t)n * S * (UDW_D / BJ);
         if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
         KernelTimer kt(LACT_K_UPD, s);
-        LACT_LAUNCH((dupd_dwp_kernel<PT::PL>), dim3((unsigned)grid), dim3(DG_THREADS), s, ud);
+        LACT_LAUNCH((dupd_dwp_kernel<FP, BJ>), dim3((unsigned)grid), dim3(DG_THREADS), s, ud);
         HIP_TRY(hipGetLastError());
       }
     } else {
@@ -1188,8 +1164,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
     oa.renorm = (p.flags & LACT_NO_RENORM) ? 0 : 1;
     oa.bpart = reinterpret_cast<const float*>(ws + w.bpart);
     // beta partial sums: per 128-token tile, or per tile of the fused update
-    const int ftile = PT::PL > 1 ? UDS_T : UDW2_T;
-    const int nbp = fused ? (int)((C + ftile - 1) / ftile) : ua.tiles_t;
+    const int nbp = fused ? (int)((C + UDS_T - 1) / UDS_T) : ua.tiles_t;
     oa.nbp = nbp;
     oa.inv_len = 1.0f / (float)C;
     oa.snap[0] = slot(nu + 1, 0);

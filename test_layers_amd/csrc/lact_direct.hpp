@@ -739,16 +739,7 @@ __global__ __launch_bounds__(DG_THREADS, upd_min_waves(P, NST)) void dupd_fwd_ke
 }
 
 // =========================================================================
-// Fused update for long chunks at d = dh = 128 (plain bf16): the update
-// forward of each token tile (as in dupd_fwd_kernel) followed at once by
-// the tile's share of the weight-gradient contraction, so the update terms E
-// never reach HBM (at this width their write and re-read are most of the
-// update's traffic).  The tile's update terms (bf16) are staged in LDS and
-// contracted at once with the tile's K and V, still in LDS from the forward;
-// the tile's contribution to U1, U3 (hidden rows j0 .. j0 + BJ - 1, all d
-// columns) and to U2 (all d rows, columns j0 ..) is accumulated in registers
-// over the workgroup's run of tiles, and one fp32 partial per workgroup is
-// stored (the optimiser sums the partials in a fixed order).
+// Arguments of the fused update (update forward + contraction in one kernel)
 struct UpdDwArgs {
   UpdFwdArgs u;          // chunk, inputs, snapshot of the weights (E unused)
   float* part;           // partials [splits, n, U1 | U3 | U2]
@@ -760,252 +751,39 @@ struct UpdDwArgs {
 
 constexpr int UDW_D = 128;   // d = dh handled by the fused update
 
-// 64-token tiles, so that the next tile's loads overlap the current tile's
-// work: the workgroup's W rows stay in LDS for the whole run (48 KB), K, V
-// (both k stages), the learning rates and beta are double-buffered
-// (2 x 33 KB) and the update terms take 24 KB.  Learning rates and beta
-// arrive by 4-byte direct loads, so every load of a tile is counted by
-// vmcnt and a wait never drains the prefetch.
-constexpr int UDW2_T = 64;   // tokens per tile
-
-template <int BJ>
-__global__ __launch_bounds__(DG_THREADS) void dupd_dw2_kernel(UpdDwArgs g) {
-  const UpdFwdArgs& a = g.u;
-  constexpr int BKK = 64;
-  constexpr int NWV = DG_THREADS / WAVE;
-  using TT = DTile<UDW2_T, BKK, NWV>;   // 64 rows x 64 d: K, V stages (rows = tokens), W stages (rows = hidden)
-  static_assert(BJ == UDW2_T && TT::INSTR == 1 && UDW_D == 2 * BKK, "tile shapes");
-  constexpr int TB = TT::BYTES;
-  constexpr int ERB = UDW2_T * 2;         // update-term row: 64 tokens of bf16
-  __shared__ __attribute__((aligned(1024))) char s_w[6 * TB];         // W1 | W3 | W2^T, two k stages each
-  __shared__ __attribute__((aligned(1024))) char s_kv[2][4 * TB];     // K s0, K s1, V s0, V s1
-  __shared__ __attribute__((aligned(1024))) char s_e[3 * BJ * ERB];   // U1 | U3 | U2 terms x 64 tokens
-  __shared__ __attribute__((aligned(16))) float s_lr[2][UDW2_T * 3];
-  __shared__ __attribute__((aligned(16))) float s_beta[2][UDW2_T];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;     // forward: 32 tokens x 16 hidden columns
-  const int jh = wave >> 2, cq = wave & 3;     // contraction: 32 hidden rows x 32 d columns
-  const int D = UDW_D;
-  const int njb = UDW_D / BJ;
-  int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int jb = bid % njb;
-  bid /= njb;
-  const int split = bid % g.splits;
-  const int inst = bid / g.splits;
-  const int j0 = jb * BJ;
-  const int64_t DD = (int64_t)D * D;
-  const int64_t tend = a.upd_t0 + a.upd_len;
-  const int ntiles = (int)((a.upd_len + UDW2_T - 1) / UDW2_T);
-  const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + inst * a.k_bs;
-  const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + inst * a.x_bs;
-  const float* LR = a.lr + inst * a.lr_bs;
-  const float* BETA = a.beta != nullptr ? a.beta + inst * a.beta_bs : nullptr;
-
-  // loads of tile tb into buffer b: K, V (4 per wave), then one 4-byte load
-  // per lane for waves 0-2 (learning rates) and wave 3 (beta, or a reload of
-  // learning rates when there is no beta) -- 5 loads for waves 0-3, 4 for 4-7
-  auto issue_tile = [&](int tb, int b) {
-    const int64_t t0 = a.upd_t0 + (int64_t)tb * UDW2_T;
-    const int nv = (int)min((int64_t)UDW2_T, tend - t0);
-    const typename TT::Plan pk = TT::plan(K, D, t0, tend - 1, 0, wave, lane);
-    const typename TT::Plan pv = TT::plan(V, D, t0, tend - 1, 0, wave, lane);
-    char* kv = s_kv[b];
-    TT::issue_one(kv, pk, 0, wave, 0);
-    TT::issue_one(kv + TB, pk, BKK * 2, wave, 0);
-    TT::issue_one(kv + 2 * TB, pv, 0, wave, 0);
-    TT::issue_one(kv + 3 * TB, pv, BKK * 2, wave, 0);
-    if (wave < 3) {
-      const int e = min(wave * 64 + lane, nv * 3 - 1);
-      dma4(LR + t0 * 3 + e, __builtin_amdgcn_readfirstlane(lds_off(&s_lr[b][wave * 64])));
-    } else if (wave == 3) {
-      const float* src = BETA != nullptr ? BETA + t0 + min(lane, nv - 1) : LR + t0 * 3 + min(lane, nv * 3 - 1);
-      dma4(src, __builtin_amdgcn_readfirstlane(lds_off(&s_beta[b][0])));
-    }
-  };
-
-  f32x4 cu1[2][2], cu3[2][2], cu2[2][2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y) cu1[x][y] = cu3[x][y] = cu2[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int tb0 = split * g.tps, tb1 = min(ntiles, tb0 + g.tps);
-  {
-    // the workgroup's W rows (hidden units j0 .. j0 + BJ - 1), both k stages
-    const bf16_t* Wm[3] = {reinterpret_cast<const bf16_t*>(a.W1) + inst * DD,
-                           reinterpret_cast<const bf16_t*>(a.W3) + inst * DD,
-                           reinterpret_cast<const bf16_t*>(a.W2x) + inst * DD};
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      const typename TT::Plan pw = TT::plan(Wm[m], D, j0, D - 1, 0, wave, lane);
-      TT::issue_one(s_w + (2 * m) * TB, pw, 0, wave, 0);
-      TT::issue_one(s_w + (2 * m + 1) * TB, pw, BKK * 2, wave, 0);
-    }
-  }
-  if (tb0 < tb1) issue_tile(tb0, 0);
-
-  for (int tb = tb0; tb < tb1; ++tb) {
-    const int b = (tb - tb0) & 1;
-    const int64_t t0 = a.upd_t0 + (int64_t)tb * UDW2_T;
-    if (tb + 1 < tb1) {
-      issue_tile(tb + 1, b ^ 1);   // that buffer was released at the end of the previous tile
-      if (wave < 4) wait_vm<5>();
-      else wait_vm<4>();
-    } else {
-      wait_vm<0>();
-    }
-    bar();   // this tile's K, V, learning rates and beta (and the W rows) have landed for every wave
-
-    // forward: A = K W1^T, B = K W3^T, G = V W2 on 64 tokens x 64 hidden units
-    f32x4 accA[2], accB[2], accG[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) accA[i] = accB[i] = accG[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < UDW_D; kk += 32) {
-      const int st = kk / BKK, kl = kk % BKK;
-      const char* kt = s_kv[b] + st * TB;
-      bf16x8 fk[2], fv[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fk[i] = dfrag_row<TT>(kt, wm * 32 + i * 16, kl, lane);
-        fv[i] = dfrag_row<TT>(kt + 2 * TB, wm * 32 + i * 16, kl, lane);
-      }
-      const bf16x8 f1 = dfrag_row<TT>(s_w + st * TB, wn * 16, kl, lane);
-      const bf16x8 f3 = dfrag_row<TT>(s_w + (2 + st) * TB, wn * 16, kl, lane);
-      const bf16x8 f2 = dfrag_row<TT>(s_w + (4 + st) * TB, wn * 16, kl, lane);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        accA[i] = mfma(fk[i], f1, accA[i]);
-        accB[i] = mfma(fk[i], f3, accB[i]);
-        accG[i] = mfma(fv[i], f2, accG[i]);
-      }
-    }
-    // beta partial sum of this tile (chunk mean), once per tile
-    if (a.beta != nullptr && jb == 0 && wave == 0) {
-      const float bs = wave_sum(t0 + lane < tend ? s_beta[b][lane] : 0.f);
-      if (lane == 0) a.bpart[(int64_t)inst * g.nbp + tb] = bs;
-    }
-    // SwiGLU backward terms into the update-term rows (zero past the chunk end)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tl = wm * 32 + i * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
-      const int col = wn * 16 + (lane & 15);
-      float u1[4], u3[4], u2[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = t0 + tl + r < tend;
-        const float e1 = ok ? s_lr[b][(tl + r) * 3 + 0] : 0.f;
-        const float e2 = ok ? s_lr[b][(tl + r) * 3 + 1] : 0.f;
-        const float e3 = ok ? s_lr[b][(tl + r) * 3 + 2] : 0.f;
-        const float x = accA[i][r], bb = accB[i][r], gg = accG[i][r];
-        const float sg = fast_sigmoid(x);
-        const float sx = x * sg;
-        const float sp = sg * (1.0f + x * (1.0f - sg));
-        u1[r] = e1 * gg * bb * sp;
-        u3[r] = e3 * gg * sx;
-        u2[r] = e2 * sx * bb;
-      }
-      const int chunk = tl >> 3, half = (tl >> 2) & 1;
-      const float* terms[3] = {u1, u3, u2};
-#pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        const int row = m * BJ + col;
-        char* dst = s_e + row * ERB + ((chunk ^ (row & 7)) << 4) + (half << 3);
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(terms[m][0], terms[m][1]),
-                                                    pack_bf16x2(terms[m][2], terms[m][3]));
-      }
-    }
-    wait_lgkm0();
-    bar();   // update terms visible; the prefetch stays in flight
-
-    // contraction over the tile's 64 tokens: U1[j, c] += sum_t E1[t, j] K[t, c], U3
-    // likewise, U2[c, j] += sum_t V[t, c] H[t, j]; this wave: hidden rows
-    // j0 + 32 jh .. +31, d columns 32 cq .. +31 (k stage cq / 2 of K, V)
-    {
-      const char* kt = s_kv[b] + (cq >> 1) * TB;
-      const char* vt = kt + 2 * TB;
-      const int cn = 32 * (cq & 1);
-#pragma unroll
-      for (int kk = 0; kk < UDW2_T; kk += 32) {
-        bf16x8 fa1[2], fa3[2], fa2[2], fbk[2], fbv[2];
-        const int chunk = (kk >> 3) + (lane >> 4);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int jr = 32 * jh + 16 * i + (lane & 15);
-          fa1[i] = *reinterpret_cast<const bf16x8*>(s_e + jr * ERB + ((chunk ^ (jr & 7)) << 4));
-          fa3[i] = *reinterpret_cast<const bf16x8*>(s_e + (BJ + jr) * ERB + ((chunk ^ ((BJ + jr) & 7)) << 4));
-          fa2[i] = *reinterpret_cast<const bf16x8*>(s_e + (2 * BJ + jr) * ERB + ((chunk ^ ((2 * BJ + jr) & 7)) << 4));
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          fbk[c] = dfrag_col<TT>(kt, cn + 16 * c, kk, lane);
-          fbv[c] = dfrag_col<TT>(vt, cn + 16 * c, kk, lane);
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            cu1[c][i] = mfma(fbk[c], fa1[i], cu1[c][i]);
-            cu3[c][i] = mfma(fbk[c], fa3[i], cu3[c][i]);
-            cu2[i][c] = mfma(fa2[i], fbv[c], cu2[i][c]);
-          }
-      }
-    }
-    wait_lgkm0();
-    bar();   // every wave is done with this buffer and the update-term rows
-  }
-  wait_vm<0>();   // no direct load may still be writing LDS when the workgroup ends
-
-  float* P = g.part + (int64_t)split * g.part_ss + (int64_t)inst * 3 * DD;
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = j0 + 32 * jh + 16 * i + (lane & 15);
-      const int cc = 32 * cq + 16 * c + 4 * (lane >> 4);
-      const float y1[4] = {cu1[c][i][0], cu1[c][i][1], cu1[c][i][2], cu1[c][i][3]};
-      const float y3[4] = {cu3[c][i][0], cu3[c][i][1], cu3[c][i][2], cu3[c][i][3]};
-      store4(P + (int64_t)j * D + cc, y1);
-      store4(P + DD + (int64_t)j * D + cc, y3);
-      const int c2 = 32 * cq + 16 * c + (lane & 15);
-      const int j2 = j0 + 32 * jh + 16 * i + 4 * (lane >> 4);
-      const float y2[4] = {cu2[i][c][0], cu2[i][c][1], cu2[i][c][2], cu2[i][c][3]};
-      store4(P + 2 * DD + (int64_t)c2 * D + j2, y2);
-    }
-}
-
 // =========================================================================
-// Fused update at d = dh = 128 for the multi-plane recurrence (P = 2 or 3
-// stored bf16 planes of the weights and of the update terms): per 32-token
-// tile, the update forward A = K W1^T, B = K W3^T, G = V W2 over the tile's
-// tokens and the workgroup's 32 hidden units, the SwiGLU backward terms
-// ("大块测试时训练（LaCT）技术解析" §2.1, eqs. 4-5) split into P planes in
-// LDS, and the tile's share of U1 = E1^T K, U3 = E3^T K, U2 = V^T E2,
+// Fused update at d = dh = 128: per 32-token tile, the update forward
+// A = K W1^T, B = K W3^T, G = V W2 over the tile's tokens and the workgroup's
+// BJ hidden units, the SwiGLU backward terms ("大块测试时训练（LaCT）技术解析"
+// §2.1, eqs. 4-5) in LDS (split into P bf16 planes for the multi-plane
+// recurrence), and the tile's share of U1 = E1^T K, U3 = E3^T K, U2 = V^T E2,
 // accumulated in registers over the workgroup's run of tiles; one fp32
-// partial per workgroup.  At this width the three planes of the update terms
-// would otherwise make a round trip through HBM (6 bytes per term).  Every
-// product sums the plane pairs (plane p of the weights or update terms with
-// the single plane of k or v), smaller planes first.
+// partial per workgroup.  The update terms never reach HBM (at this width
+// their write and re-read, 2 or 6 bytes per term, would be most of the
+// update's traffic).  Every product sums the plane pairs (plane p of the
+// weights or update terms with the single plane of k or v), smaller planes
+// first.
 // The waves are specialised: the four forward waves hold the weight planes
-// of their 16 hidden units in registers for the whole run and produce the
-// update terms of tile s while the four contraction waves consume those of
-// tile s - 1, one barrier per step, so the forward's VALU epilogue overlaps
-// the contraction's MFMA work on every SIMD (one wave of each kind per
-// SIMD).  K and V stream through a four-deep direct-load ring (tile s + 2 is
-// loaded while tiles s and s - 1 are read); the update-term planes are
-// double-buffered.
-constexpr int UDP_BJ = 32;   // hidden units per workgroup
+// of their hidden units in registers for the whole run (64 units per
+// workgroup for plain bf16, 32 with planes) and produce the update terms of
+// tile s while the four contraction waves consume those of tile s - 1, one
+// barrier per step, so the forward's VALU epilogue overlaps the
+// contraction's MFMA work on every SIMD (one wave of each kind per SIMD).
+// K and V stream through a four-deep direct-load ring (tile s + 2 is loaded
+// while tiles s and s - 1 are read); the update terms are double-buffered.
 constexpr int UDS_T = 32;   // tokens per tile
+// hidden units per workgroup: 64 for plain bf16, 32 with weight planes
+constexpr int udp_bj(int P) { return P == 1 ? 64 : 32; }
 
-template <int P>
+template <int P, int BJ>
 __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
   const UpdFwdArgs& a = g.u;
   constexpr int BKK = 64;
-  constexpr int BJ = UDP_BJ;
   constexpr int NKV = 4;                  // K, V ring depth
+  constexpr int NH = BJ / 32;             // hidden fragments per forward wave
+  constexpr int CH = BJ / 16;             // hidden fragments per contraction wave
   using TT = DTile<UDS_T, BKK, 4>;        // 32 tokens x 64 d (K, V stages), loaded by the four contraction waves
-  static_assert(TT::INSTR == 1 && UDW_D == 2 * BKK && DG_THREADS == 8 * WAVE, "tile shapes");
+  static_assert(TT::INSTR == 1 && UDW_D == 2 * BKK && DG_THREADS == 8 * WAVE && BJ % 32 == 0, "tile shapes");
   constexpr int TB = TT::BYTES;           // 4 KB
   constexpr int KVB = 4 * TB;             // K s0, K s1, V s0, V s1
   constexpr int ERB = UDS_T * 2;          // update-term row: 32 tokens of bf16 (4 chunks)
@@ -1063,22 +841,26 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
 
   if (fwd) {
     // ---------------------------------------------------------------- forward waves
-    const int tf = wave >> 1, hf = wave & 1;   // tokens 16 tf .., hidden units j0 + 16 hf ..
-    // this wave's weight fragments, every plane: row j0 + 16 hf + lane % 16,
-    // k = 32 kk + 8 (lane / 16) .. + 7
-    bf16x8 wr[3][P][4];
+    // tokens 16 tf .., hidden units j0 + BJ / 2 * hg + 16 h .. (h < NH)
+    const int tf = wave >> 1, hg = wave & 1;
+    // this wave's weight fragments, every plane: row j0 + BJ / 2 * hg + 16 h +
+    // lane % 16, k = 32 kk + 8 (lane / 16) .. + 7
+    bf16x8 wr[3][P][4][NH];
     {
       const bf16_t* W0[3] = {reinterpret_cast<const bf16_t*>(a.W1), reinterpret_cast<const bf16_t*>(a.W3),
                              reinterpret_cast<const bf16_t*>(a.W2x)};
       const bf16_t* Wlo = reinterpret_cast<const bf16_t*>(a.Wlo);
-      const int64_t roff = (int64_t)(j0 + 16 * hf + (lane & 15)) * D + 8 * (lane >> 4);
 #pragma unroll
       for (int m = 0; m < 3; ++m)
 #pragma unroll
         for (int pl = 0; pl < P; ++pl) {
-          const bf16_t* base = (pl == 0 ? W0[m] : Wlo + (pl - 1) * a.wlo_ps + m * a.wlo_ms) + inst * DD + roff;
+          const bf16_t* base = (pl == 0 ? W0[m] : Wlo + (pl - 1) * a.wlo_ps + m * a.wlo_ms) + inst * DD;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) wr[m][pl][kk] = *reinterpret_cast<const bf16x8*>(base + 32 * kk);
+          for (int h = 0; h < NH; ++h) {
+            const int64_t roff = (int64_t)(j0 + BJ / 2 * hg + 16 * h + (lane & 15)) * D + 8 * (lane >> 4);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) wr[m][pl][kk][h] = *reinterpret_cast<const bf16x8*>(base + roff + 32 * kk);
+          }
         }
     }
     bar();   // tile 0 has landed (the contraction waves waited for it)
@@ -1091,18 +873,22 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
         const int tl = tf * 16 + 4 * (lane >> 4);   // tile-local token of element r = 0
         const float4* lrv = reinterpret_cast<const float4*>(s_lr[s % NKV] + tl * 3);
         const float4 l0 = lrv[0], l1 = lrv[1], l2 = lrv[2];
-        f32x4 accA = f32x4{0.f, 0.f, 0.f, 0.f}, accB = accA, accG = accA;
+        f32x4 accA[NH], accB[NH], accG[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) accA[h] = accB[h] = accG[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int st = kk >> 1, kl = (kk & 1) * 32;
           const bf16x8 fk = dfrag_row<TT>(kv + st * TB, tf * 16, kl, lane);
           const bf16x8 fv = dfrag_row<TT>(kv + (2 + st) * TB, tf * 16, kl, lane);
 #pragma unroll
-          for (int pl = P - 1; pl >= 0; --pl) {
-            accA = mfma(fk, wr[0][pl][kk], accA);
-            accB = mfma(fk, wr[1][pl][kk], accB);
-            accG = mfma(fv, wr[2][pl][kk], accG);
-          }
+          for (int pl = P - 1; pl >= 0; --pl)
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+              accA[h] = mfma(fk, wr[0][pl][kk][h], accA[h]);
+              accB[h] = mfma(fk, wr[1][pl][kk][h], accB[h]);
+              accG[h] = mfma(fv, wr[2][pl][kk][h], accG[h]);
+            }
         }
         // beta partial sum of this tile (chunk mean), once per tile
         if (BETA != nullptr && jb == 0 && wave == 0) {
@@ -1112,41 +898,44 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
         // SwiGLU backward terms, split into planes, into the update-term rows of
         // buffer s % 2 (zero past the chunk end)
         const float lrr[12] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w, l2.x, l2.y, l2.z, l2.w};
-        const int col = hf * 16 + (lane & 15);
-        float u1[4], u3[4], u2[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = t0 + tl + r < tend;
-          const float e1 = ok ? lrr[r * 3 + 0] : 0.f;
-          const float e2 = ok ? lrr[r * 3 + 1] : 0.f;
-          const float e3 = ok ? lrr[r * 3 + 2] : 0.f;
-          const float x = accA[r], bb = accB[r], gg = accG[r];
-          const float sg = fast_sigmoid(x);
-          const float sx = x * sg;
-          const float sp = sg * (1.0f + x * (1.0f - sg));
-          u1[r] = e1 * gg * bb * sp;
-          u3[r] = e3 * gg * sx;
-          u2[r] = e2 * sx * bb;
-        }
         const int chunk = tl >> 3, half = (tl >> 2) & 1;
         char* eb = s_e + (s & 1) * (P * EPL);
-        float* terms[3] = {u1, u3, u2};
 #pragma unroll
-        for (int m = 0; m < 3; ++m) {
-          const int row = m * BJ + col;
-          char* dst = eb + row * ERB + ((chunk ^ ((row >> 1) & 3)) << 4) + (half << 3);
-          // planes of the four terms, two values per conversion (the same
-          // round-to-nearest-even planes as split_planes)
-          float* v = terms[m];
+        for (int h = 0; h < NH; ++h) {
+          const int col = BJ / 2 * hg + 16 * h + (lane & 15);
+          float u1[4], u3[4], u2[4];
 #pragma unroll
-          for (int pl = 0; pl < P; ++pl) {
-            const uint32_t w0 = pack_bf16x2(v[0], v[1]), w1 = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(dst + pl * EPL) = make_uint2(w0, w1);
-            if (pl + 1 < P) {
-              v[0] -= __uint_as_float(w0 << 16);
-              v[1] -= __uint_as_float(w0 & 0xffff0000u);
-              v[2] -= __uint_as_float(w1 << 16);
-              v[3] -= __uint_as_float(w1 & 0xffff0000u);
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = t0 + tl + r < tend;
+            const float e1 = ok ? lrr[r * 3 + 0] : 0.f;
+            const float e2 = ok ? lrr[r * 3 + 1] : 0.f;
+            const float e3 = ok ? lrr[r * 3 + 2] : 0.f;
+            const float x = accA[h][r], bb = accB[h][r], gg = accG[h][r];
+            const float sg = fast_sigmoid(x);
+            const float sx = x * sg;
+            const float sp = sg * (1.0f + x * (1.0f - sg));
+            u1[r] = e1 * gg * bb * sp;
+            u3[r] = e3 * gg * sx;
+            u2[r] = e2 * sx * bb;
+          }
+          float* terms[3] = {u1, u3, u2};
+#pragma unroll
+          for (int m = 0; m < 3; ++m) {
+            const int row = m * BJ + col;
+            char* dst = eb + row * ERB + ((chunk ^ ((row >> 1) & 3)) << 4) + (half << 3);
+            // planes of the four terms, two values per conversion (the same
+            // round-to-nearest-even planes as split_planes)
+            float* v = terms[m];
+#pragma unroll
+            for (int pl = 0; pl < P; ++pl) {
+              const uint32_t w0 = pack_bf16x2(v[0], v[1]), w1 = pack_bf16x2(v[2], v[3]);
+              *reinterpret_cast<uint2*>(dst + pl * EPL) = make_uint2(w0, w1);
+              if (pl + 1 < P) {
+                v[0] -= __uint_as_float(w0 << 16);
+                v[1] -= __uint_as_float(w0 & 0xffff0000u);
+                v[2] -= __uint_as_float(w1 << 16);
+                v[3] -= __uint_as_float(w1 & 0xffff0000u);
+              }
             }
           }
         }
@@ -1158,18 +947,18 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
   }
 
   // ---------------------------------------------------------------- contraction waves
-  // d columns 32 cw .. + 31 (k stage cw / 2 of K, V), all 32 hidden rows:
-  // U1, U3 [hidden x d] and U2 [d x hidden], 2 x 2 fragments each
+  // d columns 32 cw .. + 31 (k stage cw / 2 of K, V), all BJ hidden rows:
+  // U1, U3 [hidden x d] and U2 [d x hidden], 2 x CH fragments each
   if (nt > 0) issue_tile(0);
   if (nt > 1) issue_tile(1);
   if (nt > 1) wait_vm<5>();
   else wait_vm<0>();
   bar();   // tile 0 landed
-  f32x4 cu1[2][2], cu3[2][2], cu2[2][2];   // [d fragment][hidden fragment]
+  f32x4 cu1[2][CH], cu3[2][CH], cu2[2][CH];   // [d fragment][hidden fragment]
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) cu1[c][i] = cu3[c][i] = cu2[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < CH; ++i) cu1[c][i] = cu3[c][i] = cu2[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int cn = 32 * (cw & 1);
   for (int s = 0; s <= nt; ++s) {
     // slot (s + 2) % 4 held tile s - 2, read by the forward waves in step s - 2 and here in step s - 1
@@ -1189,7 +978,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
       for (int pl = P - 1; pl >= 0; --pl) {
         const char* ep = eb + pl * EPL;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < CH; ++h) {
           const int jr = 16 * h + (lane & 15);
           const int off = (((lane >> 4) ^ ((jr >> 1) & 3)) << 4);
           const bf16x8 fa1 = *reinterpret_cast<const bf16x8*>(ep + jr * ERB + off);
@@ -1215,7 +1004,7 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < CH; ++h) {
       const int j = j0 + 16 * h + (lane & 15);
       const int cc = 32 * cw + 16 * c + 4 * (lane >> 4);
       const float y1[4] = {cu1[c][h][0], cu1[c][h][1], cu1[c][h][2], cu1[c][h][3]};

@@ -769,8 +769,9 @@ constexpr int UDW_D = 128;   // d = dh handled by the fused update
 // tile s while the four contraction waves consume those of tile s - 1, one
 // barrier per step, so the forward's VALU epilogue overlaps the
 // contraction's MFMA work on every SIMD (one wave of each kind per SIMD).
-// K and V stream through a four-deep direct-load ring (tile s + 2 is loaded
-// while tiles s and s - 1 are read); the update terms are double-buffered.
+// K and V stream through a direct-load ring, six deep for plain bf16 and
+// four with planes (tiles s + 1 .. s + NKV - 2 are in flight while tiles s
+// and s - 1 are read); the update terms are double-buffered.
 constexpr int UDS_T = 32;   // tokens per tile
 // hidden units per workgroup: 64 for plain bf16, 32 with weight planes
 constexpr int udp_bj(int P) { return P == 1 ? 64 : 32; }
@@ -779,7 +780,8 @@ template <int P, int BJ>
 __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
   const UpdFwdArgs& a = g.u;
   constexpr int BKK = 64;
-  constexpr int NKV = 4;                  // K, V ring depth
+  constexpr int NKV = P == 1 ? 6 : 4;     // K, V ring depth (what the LDS holds beside the update terms)
+  constexpr int LA = NKV - 2;             // tiles loaded ahead of the one the forward waves read
   constexpr int NH = BJ / 32;             // hidden fragments per forward wave
   constexpr int CH = BJ / 16;             // hidden fragments per contraction wave
   using TT = DTile<UDS_T, BKK, 4>;        // 32 tokens x 64 d (K, V stages), loaded by the four contraction waves
@@ -949,10 +951,16 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
   // ---------------------------------------------------------------- contraction waves
   // d columns 32 cw .. + 31 (k stage cw / 2 of K, V), all BJ hidden rows:
   // U1, U3 [hidden x d] and U2 [d x hidden], 2 x CH fragments each
-  if (nt > 0) issue_tile(0);
-  if (nt > 1) issue_tile(1);
-  if (nt > 1) wait_vm<5>();
-  else wait_vm<0>();
+  // wait until at most k tiles' loads (five per tile) are in flight
+  auto wait_tiles = [](int k) {
+    if (k >= 3) wait_vm<15>();
+    else if (k == 2) wait_vm<10>();
+    else if (k == 1) wait_vm<5>();
+    else wait_vm<0>();
+  };
+  static_assert(LA <= 4, "wait_tiles covers up to three tiles in flight");
+  for (int i = 0; i < LA && i < nt; ++i) issue_tile(i);
+  wait_tiles(min(LA, nt) - 1);
   bar();   // tile 0 landed
   f32x4 cu1[2][CH], cu3[2][CH], cu2[2][CH];   // [d fragment][hidden fragment]
 #pragma unroll
@@ -961,8 +969,9 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
     for (int i = 0; i < CH; ++i) cu1[c][i] = cu3[c][i] = cu2[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int cn = 32 * (cw & 1);
   for (int s = 0; s <= nt; ++s) {
-    // slot (s + 2) % 4 held tile s - 2, read by the forward waves in step s - 2 and here in step s - 1
-    if (s + 2 < nt) issue_tile(s + 2);
+    // slot (s + LA) % NKV held tile s - 2, read by the forward waves in step
+    // s - 2 and here in step s - 1
+    if (s + LA < nt) issue_tile(s + LA);
     if (s >= 1) {
       const int i = s - 1;   // consume tile i
       const char* kt = s_kv + (i % NKV) * KVB + (cw >> 1) * TB;
@@ -993,9 +1002,9 @@ __global__ __launch_bounds__(DG_THREADS) void dupd_dwp_kernel(UpdDwArgs g) {
         }
       }
     }
-    // tile s + 1 must have landed before the barrier (tile s + 2 may be in flight)
-    if (s + 2 < nt) wait_vm<5>();
-    else wait_vm<0>();
+    // tile s + 1 must have landed before the barrier (tiles s + 2 .. s + LA
+    // may be in flight)
+    wait_tiles(max(0, min(s + LA, nt - 1) - (s + 1)));
     wait_lgkm0();
     bar();
   }

@@ -66,6 +66,7 @@ def kernel_flops(wl, lact):
         lact.K_NS: (30.0 * D ** 3 * 3 * n * n_upd) if wl.opt in (W.OPT_MUON, W.OPT_MUON_MOMENTUM) else 0.0,
         lact.K_SNAP: 0.0,
         lact.K_PREP: 0.0,
+        lact.K_NSRED: 0.0,
     }
 
 
@@ -99,6 +100,9 @@ def kernel_bytes(wl, lact, fused):
     b[lact.K_OPT] = n_upd * n * 3 * mat * 4 * (4 if wl.opt == W.OPT_MOMENTUM else 2)
     b[lact.K_SNAP] = n * 3 * mat * 4
     b[lact.K_PREP] = (n * app * D * io * 2 + n * upd * D * io * 2) if wl.layer_qk_prep else 0.0
+    # the Newton-Schulz input reduction: the momentum state read and written
+    # (its partials and outputs are intermediates)
+    b[lact.K_NSRED] = n_upd * n * 3 * mat * 4 * 2 if wl.opt == W.OPT_MUON_MOMENTUM else 0.0
     return b
 
 

@@ -301,22 +301,24 @@ const char* lact_last_error(void);
  * milliseconds and the number of launches since the previous read.
  */
 #define LACT_K_UPD 0       /* update forward: k W1^T, k W3^T, v W2 + SwiGLU backward terms
-                              (bf16 chunks of >= 4,096 tokens at d = dh = 128: together with
-                              the weight-gradient contraction, one kernel; plain bf16
-                              apply-then-update chunks: also the chunk's q W1^T, q W3^T ->
-                              gated hidden) */
+                              (bf16 inputs at d = dh = 128, chunks of >= 4,096 tokens, or of
+                              >= 1,024 with weight planes: together with the weight-gradient
+                              contraction, one kernel; plain bf16 apply-then-update chunks:
+                              also the chunk's q W1^T, q W3^T -> gated hidden) */
 #define LACT_K_APP 1       /* apply forward: q W1^T, q W3^T -> gated hidden, for applies not
                               computed in their update's kernel (bf16 q with dh = 128: the
                               whole apply, o = Hq W2^T included, in one kernel) */
 #define LACT_K_OUT 2       /* apply output product o = Hq W2^T (when not fused) */
 #define LACT_K_DW 3        /* weight-gradient contractions (split over tokens; when not fused) */
 #define LACT_K_OPT 4       /* optimiser step + row renormalisation + weight snapshot */
-#define LACT_K_NS 5        /* Newton-Schulz products and reductions */
+#define LACT_K_NS 5        /* Newton-Schulz products */
 #define LACT_K_SNAP 6      /* snapshot of the caller's weights at call start */
 #define LACT_K_PREP 7      /* q / k pre-processing (LACT_QK_PREP) */
 #define LACT_K_BWD_GEMM 8  /* backward: products of the reverse sweep */
 #define LACT_K_BWD_ELEM 9  /* backward: elementwise, row and reduction kernels */
-#define LACT_K_COUNT 10
+#define LACT_K_NSRED 10    /* Newton-Schulz input: the sum of the split partials with its row
+                              sums of squares (and, with momentum, the new momentum) */
+#define LACT_K_COUNT 11
 lact_status lact_timing_enable(int32_t kclass, int32_t on);
 lact_status lact_timing_read(int32_t kclass, double* total_ms, int64_t* launches);
 

@@ -658,6 +658,9 @@ lact_status launch_upd_fwd(const UpdFwdArgs& ua, int64_t grid, hipStream_t s) {
     else LACT_LAUNCH((dupd_fwd_kernel<BJ, 64, 2>), dim3((unsigned)grid), dim3(DG_THREADS), s, ua);
     HIP_TRY(hipGetLastError());
     return LACT_OK;
+  } else if constexpr (BJ != 64) {
+    // the register-path tile is free of register spills only at 64 columns
+    return fail(LACT_ERR_UNSUPPORTED, "internal: register-path update tile of %d columns", BJ);
   } else {
     using TW = typename std::conditional<PT::UPD_FROM_SNAP, typename PT::TS, float>::type;
     constexpr int PW = PT::UPD_FROM_SNAP ? PT::PS : PT::PWU;
@@ -712,14 +715,18 @@ lact_status launch_app_fwd(const AppFwdArgs& aa, int64_t grid, hipStream_t s) {
     LACT_LAUNCH((dapp_fwd_kernel<BJ, 32, 3>), dim3((unsigned)grid), dim3(NT), s, aa);
     HIP_TRY(hipGetLastError());
     return LACT_OK;
+  } else if constexpr (BJ != 64) {
+    // the register-path tile is free of register spills only at 64 columns
+    return fail(LACT_ERR_UNSUPPORTED, "internal: register-path apply tile of %d columns", BJ);
+  } else {
+    constexpr int BKK = pick_bk(PT::PIO + PT::PS);
+    constexpr int words = (PT::PIO * FBT + 2 * PT::PS * BJ) * (BKK + 8);
+    constexpr int ST = pick_stages(words);
+    LACT_LAUNCH((app_fwd_kernel<typename PT::TIO, PT::PIO, typename PT::TS, PT::PS, typename PT::TAPP, BJ, BKK, ST>),
+                dim3((unsigned)grid), dim3(NT), s, aa);
+    HIP_TRY(hipGetLastError());
+    return LACT_OK;
   }
-  constexpr int BKK = pick_bk(PT::PIO + PT::PS);
-  constexpr int words = (PT::PIO * FBT + 2 * PT::PS * BJ) * (BKK + 8);
-  constexpr int ST = pick_stages(words);
-  LACT_LAUNCH((app_fwd_kernel<typename PT::TIO, PT::PIO, typename PT::TS, PT::PS, typename PT::TAPP, BJ, BKK, ST>),
-                     dim3((unsigned)grid), dim3(NT), s, aa);
-  HIP_TRY(hipGetLastError());
-  return LACT_OK;
 }
 
 // --------------------------------------------------------------- helper streams
@@ -1183,7 +1190,7 @@ lact_status run_steps(const lact_problem& p, const Ptrs& P, int64_t seq_stride, 
       float* U = reinterpret_cast<float*>(ws + w.u);
       float* rowsq = reinterpret_cast<float*>(ws + w.rowsq);
       {
-        KernelTimer kt(LACT_K_NS, s);
+        KernelTimer kt(LACT_K_NSRED, s);
         const int64_t rows = (int64_t)n * (2 * Dh + D);
         // momentum + Muon: the Newton-Schulz input is the new momentum buffer
         // M' = mean(beta) M - U, also written back to the state

@@ -145,6 +145,38 @@ __global__ __launch_bounds__(S::THREADS) void pgemm_kernel(GemmArgs g) {
       }
     }
   };
+  // the epilogue's input-term planes (beta Cin), loaded before the main loop
+  // so that their latency hides behind it: the quads (row, 4 columns) of the
+  // tile and, for a mirrored symmetric tile, of its mirror, as the epilogue
+  // visits them
+  constexpr int QN = BN / 4, QM = BM / 4;
+  constexpr int QPT = BM * QN / S::THREADS, QPM = BN * QM / S::THREADS;
+  static_assert(BM * QN % S::THREADS == 0 && BN * QM % S::THREADS == 0, "epilogue quads per thread");
+  constexpr int PP = PO > 0 ? PO : 1;
+  uint2 cpre[QPT][PP], cprm[QPM][PP];
+  const bf16_t* Cinp =
+      (PO > 0 && G.Cinp && !G.Cin) ? reinterpret_cast<const bf16_t*>(G.Cinp) + b * g.cin_bs : nullptr;
+  if constexpr (PO > 0) {
+    if (Cinp) {
+#pragma unroll
+      for (int q = 0; q < QPT; ++q) {
+        const int qd = tid + q * S::THREADS;
+        const int64_t off = (int64_t)(m0 + qd / QN) * g.ldcin + n0 + (qd % QN) * 4;
+#pragma unroll
+        for (int p = 0; p < PO; ++p) cpre[q][p] = *reinterpret_cast<const uint2*>(Cinp + p * g.cp_ps + off);
+      }
+      if (mirror) {
+#pragma unroll
+        for (int q = 0; q < QPM; ++q) {
+          const int qd = tid + q * S::THREADS;
+          const int64_t off = (int64_t)(n0 + qd / QM) * g.ldcin + m0 + (qd % QM) * 4;
+#pragma unroll
+          for (int p = 0; p < PO; ++p) cprm[q][p] = *reinterpret_cast<const uint2*>(Cinp + p * g.cp_ps + off);
+        }
+      }
+    }
+  }
+
   dpipeline_il<S::NST, LPS>(nk, issue_one, compute);
 
   if constexpr (KS > 1) {
@@ -187,7 +219,6 @@ __global__ __launch_bounds__(S::THREADS) void pgemm_kernel(GemmArgs g) {
   float* C = G.C ? reinterpret_cast<float*>(G.C) + b * g.c_bs : nullptr;
   bf16_t* Cp = G.Cp ? reinterpret_cast<bf16_t*>(G.Cp) + b * g.c_bs : nullptr;
   const float* Cin = G.Cin ? G.Cin + b * g.cin_bs : nullptr;
-  const bf16_t* Cinp = G.Cinp ? reinterpret_cast<const bf16_t*>(G.Cinp) + b * g.cin_bs : nullptr;
 
   // The tile goes through LDS (fp32, row = m) so that every store covers
   // whole rows: 16 bytes of fp32 or 8 bytes per bf16 plane per lane, lanes
@@ -208,7 +239,21 @@ __global__ __launch_bounds__(S::THREADS) void pgemm_kernel(GemmArgs g) {
     }
   }
   bar();
-  // v (4 consecutive values of row m, columns n .. n + 3) plus beta Cin, stored
+  // beta times the value held in the prefetched planes h, added to v
+  auto add_planes = [&](const uint2 (&h)[PP], float (&v)[4]) {
+    float c[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = PO - 1; p >= 0; --p) {   // smaller planes first
+      c[0] += bf2f(h[p].x & 0xffffu);
+      c[1] += bf2f(h[p].x >> 16);
+      c[2] += bf2f(h[p].y & 0xffffu);
+      c[3] += bf2f(h[p].y >> 16);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] += beta * c[r];
+  };
+  // v (4 consecutive values of row m, columns n .. n + 3) plus beta Cin
+  // (fp32 input; plane input already added), stored
   auto emit = [&](int64_t m, int64_t n, float (&v)[4]) {
     const int64_t off = m * g.ldc + n;
     if (Cin) {
@@ -217,20 +262,6 @@ __global__ __launch_bounds__(S::THREADS) void pgemm_kernel(GemmArgs g) {
       v[1] += beta * c.y;
       v[2] += beta * c.z;
       v[3] += beta * c.w;
-    } else if constexpr (PO > 0) {
-      if (Cinp) {
-        float c[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = PO - 1; p >= 0; --p) {   // smaller planes first
-          const uint2 h = *reinterpret_cast<const uint2*>(Cinp + p * g.cp_ps + m * g.ldcin + n);
-          c[0] += bf2f(h.x & 0xffffu);
-          c[1] += bf2f(h.x >> 16);
-          c[2] += bf2f(h.y & 0xffffu);
-          c[3] += bf2f(h.y >> 16);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] += beta * c[r];
-      }
     }
     if (C) store4(C + off, v);
     if constexpr (PO > 0) {
@@ -244,20 +275,27 @@ __global__ __launch_bounds__(S::THREADS) void pgemm_kernel(GemmArgs g) {
       }
     }
   };
-  constexpr int QN = BN / 4, QM = BM / 4;
-  for (int qd = tid; qd < BM * QN; qd += S::THREADS) {
+#pragma unroll
+  for (int q = 0; q < QPT; ++q) {
+    const int qd = tid + q * S::THREADS;
     const int r = qd / QN, c = (qd % QN) * 4;
     const float4 x = *reinterpret_cast<const float4*>(stg + r * EST + c);
     float v[4] = {x.x, x.y, x.z, x.w};
+    if constexpr (PO > 0)
+      if (Cinp) add_planes(cpre[q], v);
     emit(m0 + r, n0 + c, v);
   }
   if (!mirror) return;
   // mirrored tile: C[n0 + r, m0 + c .. +3] = staged[m = c .. c + 3][n = r]
-  for (int qd = tid; qd < BN * QM; qd += S::THREADS) {
+#pragma unroll
+  for (int q = 0; q < QPM; ++q) {
+    const int qd = tid + q * S::THREADS;
     const int r = qd / QM, c = (qd % QM) * 4;
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = stg[(c + e) * EST + r];
+    if constexpr (PO > 0)
+      if (Cinp) add_planes(cprm[q], v);
     emit(n0 + r, m0 + c, v);
   }
 }

@@ -35,10 +35,10 @@ CHUNK_APPLY = 2
 NO_RENORM = 1
 QK_PREP = 2
 
-K_UPD, K_APP, K_OUT, K_DW, K_OPT, K_NS, K_SNAP, K_PREP, K_BWD_GEMM, K_BWD_ELEM = range(10)
+K_UPD, K_APP, K_OUT, K_DW, K_OPT, K_NS, K_SNAP, K_PREP, K_BWD_GEMM, K_BWD_ELEM, K_NSRED = range(11)
 K_NAMES = {K_UPD: "update_fwd", K_APP: "apply_fwd", K_OUT: "apply_out", K_DW: "dw", K_OPT: "opt",
            K_NS: "newton_schulz", K_SNAP: "snapshot", K_PREP: "qk_prep", K_BWD_GEMM: "bwd_gemm",
-           K_BWD_ELEM: "bwd_elem"}
+           K_BWD_ELEM: "bwd_elem", K_NSRED: "ns_reduce"}
 
 EXPORTS = ["lact_workspace_size", "lact_chunk_update", "lact_apply", "lact_layer_forward",
            "lact_layer_forward_scaled", "lact_layer_forward_noalloc", "lact_backward_workspace_size",

@@ -346,8 +346,9 @@ int upd_bj(const lact_problem& p, int64_t C) {
   const int64_t tt = (C + FBT - 1) / FBT;
   int best = 64;
   double best_eff = -1;
-  // direct-load tiles fit BJ <= 96; the register-path (multi-plane) tiles
-  // are free of register spills only at BJ = 64
+  // plain-bf16 direct-load tiles fit BJ <= 96; the multi-plane tile is
+  // built for BJ = 64, and the fp32 register-path tile is free of register
+  // spills only there
   const bool direct = profile_of(p) == PBF16;
   for (int bj : {128, 96, 64}) {
     if (bj == 128 || (!direct && bj != 64)) continue;

@@ -207,6 +207,34 @@ def test_layer_mixed_schedule_plain_bf16(lact, order, sched):
     assert max(errs.values()) <= wl.tol, errs
 
 
+# d = dh = 128: update chunks long enough for the fused update (>= 4,096
+# tokens with one weight plane, >= 1,024 with planes) beside shorter ones that
+# run the separate update forward and contraction, in one call
+FUSED_MIXED = {
+    "planes": (5, 3, (0, 1100, 1400, 2700, 3000), (W.UPDATE | W.APPLY, W.UPDATE | W.APPLY, W.APPLY,
+                                                     W.UPDATE | W.APPLY)),
+    "plain": (4, 1, (0, 4200, 4700, 5000), (W.UPDATE | W.APPLY, W.UPDATE | W.APPLY, W.UPDATE | W.APPLY)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FUSED_MIXED))
+def test_layer_fused_and_separate_updates_in_one_call(lact, case):
+    """A schedule mixing fused and separate update steps at d = dh = 128 (the
+    workspace then holds the update-term buffer the separate steps need):
+    three-plane Muon (the video recipe) and plain bf16 GD (the view-set
+    recipe)."""
+    import dataclasses
+    cid, planes, b, f = FUSED_MIXED[case]
+    wl = dataclasses.replace(W.WORKLOADS[cid], n_inst=2, L=b[-1], bounds=b, flags=f, rec_planes=planes,
+                             order=W.APPLY_THEN_UPDATE)
+    inp = W.generate(wl, seed=12)
+    log(f"fused and separate updates ({case}): bounds={b}")
+    gpu = run_gpu(wl, inp, torch, lact)
+    errs = compare(wl, inp, gpu)
+    log(f"  errs={ {k: f'{v:.2e}' for k, v in errs.items()} }")
+    assert max(errs.values()) <= wl.tol, errs
+
+
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, "fused_update", "video_fused"])
 def test_layer_is_deterministic(lact, cid):
     """Every workload (reduced) run twice gives bitwise-identical outputs and

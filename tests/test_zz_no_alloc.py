@@ -49,6 +49,7 @@ def _noalloc(lact, wl, dev, Ws, Ms, o):
     (2, [(3, 1536, 512), (2, 700, 256)]),    # momentum, plain bf16 (second: ragged last chunk)
     (3, [(2, 1024, 512), (1, 512, 256)]),    # Muon, two-plane recurrence
     (5, [(4, 1400, 280), (2, 560, 280)]),    # d = 128 Muon, three-plane recurrence
+    (5, [(3, 2400, 1200), (2, 1100, 1100)]),  # ... in chunks long enough for the fused update
 ])
 def test_noalloc_matches_the_workspace_entry_point(lact, cid, sizes):
     for n, L, chunk in sizes:

@@ -322,16 +322,24 @@ bool fused_update(const lact_problem& p, int64_t C) {
 
 // its token split (32-token tiles, 128 / udp_bj hidden blocks per instance,
 // one workgroup per CU by LDS), every split non-empty: the split count that
-// minimises rounds of workgroups x tiles per workgroup, the smaller on ties
+// minimises rounds of workgroups x tiles per workgroup plus the cost of the
+// splits' fp32 partials (each written once and read once by the reduction,
+// ~5 TB/s), in units of a tile's run time (measured: ~1.0 us with one
+// plane, ~1.3 us with planes); the smaller count on ties
 void udw_split(const lact_problem& p, int64_t C, int& S, int& tps) {
   const int64_t tt = (C + UDS_T - 1) / UDS_T;
-  const int planes = profile_of(p) == PBF16 ? 1 : 2;
-  const int64_t per = (UDW_D / udp_bj(planes)) * (int64_t)std::max(1, p.n_inst);
-  int64_t best = -1, bt = tt;
+  const bool plain = profile_of(p) == PBF16;
+  const int64_t n = std::max(1, p.n_inst);
+  const int64_t per = (UDW_D / udp_bj(plain ? 1 : 2)) * n;
+  const double part_bytes = 2.0 * (double)n * 3 * UDW_D * UDW_D * sizeof(float);
+  const double split_cost = part_bytes / (5e12 * (plain ? 1.0e-6 : 1.3e-6));
+  double best = -1;
+  int64_t bt = tt;
   for (int64_t c = 1; c <= std::min<int64_t>(tt, 32); ++c) {
     const int64_t t = (tt + c - 1) / c;
-    const int64_t cost = ((per * c + NCU - 1) / NCU) * t;
-    if (best < 0 || cost < best) {
+    const int64_t cs = (tt + t - 1) / t;   // splits actually used
+    const double cost = (double)(((per * cs + NCU - 1) / NCU) * t) + split_cost * (double)cs;
+    if (best < 0 || cost < best - 1e-9) {
       best = cost;
       bt = t;
     }

@@ -313,9 +313,11 @@ namespace lact {
 // per matrix: the iterate X and the Gram / polynomial matrix live in LDS as
 // fp32 for all ns_iters steps, so the fifteen products of a chunk's
 // orthogonalisation need no launch, no global round trip and no grid-wide
-// synchronisation.  Operand fragments are read from the fp32 copies and
-// split into P bf16 planes in registers; every product sums the plane pairs
-// (i, j) with i + j < P, smaller pairs first (fp32 grade at P = 3).
+// synchronisation.  Each 32-wide k slice of an operand that all waves read
+// is split once into P bf16 planes in LDS (the B X product's B rows, read by
+// two waves each, are split in registers by those waves); every product sums
+// the plane pairs (i, j) with i + j < P, smaller pairs first (fp32 grade at
+// P = 3).
 //   X0 = U / (||U||_F + 1e-7);  per step:  A = X X^T,  B = b A + c A A,
 //   X <- a X + B X  ("大块测试时训练（LaCT）技术解析" §2.2.1, eqs. 9-10).
 // U: [nmat, D, D] fp32, rowsq: [nmat, D] per-row sums of squares of U
@@ -357,9 +359,12 @@ template <int D, int P>
 __global__ __launch_bounds__(NsSmall<D>::THREADS) void ns_small_kernel(const float* U, const float* rowsq, float* out,
                                                                         int iters, float ca, float cb, float cc) {
   using G = NsSmall<D>;
+  using TP = DTile<D, 32, G::NW>;   // one bf16 plane of a 32-wide k slice, D rows
+  static_assert(TP::CHUNKS == G::THREADS, "one 8-value chunk of a slice per thread");
   constexpr int FM = G::FM, FN = G::FN, PITCH = G::PITCH;
   __shared__ __attribute__((aligned(16))) float s0[D * PITCH];   // X
   __shared__ __attribute__((aligned(16))) float s1[D * PITCH];   // A, then B
+  __shared__ __attribute__((aligned(256))) char s_pl[P * TP::BYTES];
   __shared__ float s_scale;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / G::WGN, wn = wave % G::WGN;
@@ -390,17 +395,34 @@ __global__ __launch_bounds__(NsSmall<D>::THREADS) void ns_small_kernel(const flo
     float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     split8<P>(v, f);
   };
-  // fragment whose k runs down the slot's rows: element (n, k) = slot[k][n]
-  auto frag_cols = [&](const float* sl, int n0, int kk, bf16x8 (&f)[P]) {
-    const int n = n0 + (lane & 15), k0 = kk + 8 * (lane >> 4);
+  // The k slice [kk, kk + 32) of an operand that every wave reads, split
+  // once into P bf16 planes of s_pl (row n, k - kk) instead of once per
+  // reading wave: each thread one 8-value chunk, of a row of `sl` (ROWS) or
+  // of a column (element (n, k) = sl[k][n]); lanes run along n, so both
+  // kinds of fp32 reads are free of bank conflicts.
+  auto fill = [&](const float* sl, int kk, auto rows) {
+    constexpr bool ROWS = decltype(rows)::value;
+    const int n = tid % D, c = tid / D;
     float v[8];
+    if constexpr (ROWS) {
+      const float4 x0 = *reinterpret_cast<const float4*>(sl + n * PITCH + kk + 8 * c);
+      const float4 x1 = *reinterpret_cast<const float4*>(sl + n * PITCH + kk + 8 * c + 4);
+      v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+      v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = sl[(k0 + e) * PITCH + n];
+      for (int e = 0; e < 8; ++e) v[e] = sl[(kk + 8 * c + e) * PITCH + n];
+    }
+    bf16x8 f[P];
     split8<P>(v, f);
+#pragma unroll
+    for (int p = 0; p < P; ++p) *reinterpret_cast<bf16x8*>(s_pl + p * TP::BYTES + TP::phys(n, c) * 16) = f[p];
   };
-  // acc = Aop Bop^T over k: Aop rows from `sa`; Bop rows from `sb` (row
-  // reads) or its columns (COLB); swapped MFMA order, so lane holds row
-  // lane % 16 of a fragment and 4 consecutive columns
+  // acc = Aop Bop^T over k, swapped MFMA order (lane holds row lane % 16 of
+  // a fragment and 4 consecutive columns).  Square products (COLB = 0,
+  // sa = sb): both operands are rows of sa, read from the split slice.  B X
+  // (COLB = 1): Aop rows of sa split by each wave that reads them, Bop
+  // element (n, k) = sb[k][n] from the split slice.
   f32x4 acc[FM][FN];
   auto product = [&](const float* sa, const float* sb, auto colb) {
     constexpr bool COLB = decltype(colb)::value;
@@ -409,14 +431,24 @@ __global__ __launch_bounds__(NsSmall<D>::THREADS) void ns_small_kernel(const flo
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int kk = 0; kk < D; kk += 32) {
+      // the previous slice's planes are read by every wave (before the
+      // first slice, the barrier that ended the last update of the slots)
+      if (kk) __syncthreads();
+      fill(sb, kk, IC<COLB ? 0 : 1>{});
+      __syncthreads();
       bf16x8 fa[FM][P], fb[FN][P];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) frag_rows(sa, wm * (D / G::WGM) + i * 16, kk, fa[i]);
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (COLB) frag_rows(sa, wm * (D / G::WGM) + i * 16, kk, fa[i]);
+        else {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (COLB) frag_cols(sb, wn * (D / G::WGN) + j * 16, kk, fb[j]);
-        else frag_rows(sb, wn * (D / G::WGN) + j * 16, kk, fb[j]);
+          for (int p = 0; p < P; ++p) fa[i][p] = dfrag_row<TP>(s_pl + p * TP::BYTES, wm * (D / G::WGM) + i * 16, 0, lane);
+        }
       }
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int p = 0; p < P; ++p) fb[j][p] = dfrag_row<TP>(s_pl + p * TP::BYTES, wn * (D / G::WGN) + j * 16, 0, lane);
 #pragma unroll
       for (int sp = P - 1; sp >= 0; --sp)
 #pragma unroll

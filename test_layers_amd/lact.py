@@ -130,12 +130,30 @@ def problem(n_inst: int, d: int, io_dtype: int, opt: int, rec_planes: int = 0, n
 
 
 # ----------------------------------------------------------------- raw-pointer calls
+_SCHED_CACHE = {}
+
+
 def _sched(bounds, flags):
     # either may be None: the library reports a half-given schedule itself.
     # Both given: the library reads n_chunks + 1 bounds and n_chunks flags,
     # so their lengths must agree, and flags must fit the uint8 they become.
+    # A layer call marshals its schedule twice (workspace size, then the
+    # call), and callers repeat schedules: the converted arrays of recent
+    # schedules are kept (they are read by the library only during a call).
     if bounds is None and flags is None:
         return None, None, 0, None
+    key = (None if bounds is None else tuple(bounds), None if flags is None else tuple(flags))
+    hit = _SCHED_CACHE.get(key)
+    if hit is not None:
+        return hit
+    res = _sched_convert(bounds, flags)
+    if len(_SCHED_CACHE) >= 64:
+        _SCHED_CACHE.clear()
+    _SCHED_CACHE[key] = res
+    return res
+
+
+def _sched_convert(bounds, flags):
     if bounds is not None and flags is not None and len(bounds) != len(flags) + 1:
         raise ValueError(f"schedule has {len(bounds)} bounds for {len(flags)} chunks (need chunks + 1)")
     if flags is not None and any(not 0 <= int(x) <= 255 for x in flags):

@@ -539,13 +539,16 @@ def test_layer_d128_fused_apply_with_output_scale(lact):
 
 
 # ------------------------------------------------------------------ HIP graph capture
-@pytest.mark.parametrize("cid", [2, 4])
+@pytest.mark.parametrize("cid", [2, 4, 3, "video_fused"])
 def test_layer_replays_in_a_hip_graph(lact, cid):
     """The layer only enqueues kernels on the caller's stream (no allocation,
     memset, copy or host synchronisation), so a HIP graph can capture a whole
     layer forward; every replay, with eager work and synchronisations between
-    replays, equals the eager call bitwise."""
-    wl = W.WORKLOADS[2].scaled(n_inst=2, L=1500, chunk=512) if cid == 2 else SMALL[4]
+    replays, equals the eager call bitwise.  The Newton-Schulz layers (3:
+    d = 512, the orthogonalisation on two helper streams; video_fused:
+    d = 128, the fused update and the applies on a helper stream) fork from
+    and join the caller's stream, which the capture follows."""
+    wl = W.WORKLOADS[2].scaled(n_inst=2, L=1500, chunk=512) if cid == 2 else SMALL[cid]
     inp = W.generate(wl, seed=21)
     ref = run_gpu(wl, inp, torch, lact)
     q, k, v, lr, beta = (to_dev(x, torch) for x in (inp.q, inp.k, inp.v, inp.lr, inp.beta))

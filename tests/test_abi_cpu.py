@@ -415,6 +415,25 @@ def test_binding_rejects_inconsistent_schedule_arrays(bounds, flags):
         fwd(P(), L=256, bounds=bounds, flags=flags)
 
 
+def test_binding_schedule_cache_keys_on_values():
+    """The binding keeps converted schedules keyed by their values: a
+    repeated schedule gives the same answer, a changed one (even with the
+    same length) is converted afresh, and a bad one is still rejected after a
+    good one of the same length was cached."""
+    b, f = [0, 256, 640, 1000], [3, 3, 3]
+    a1 = lact.workspace_size(P(), 1000, 0, 0, b, f)
+    assert lact.workspace_size(P(), 1000, 0, 0, list(b), list(f)) == a1
+    assert lact.workspace_size(P(), 1000, 0, 0, tuple(b), tuple(f)) == a1
+    # a longer first chunk needs more workspace (the update terms scale with it)
+    b2 = [0, 900, 950, 1000]
+    assert lact.workspace_size(P(), 1000, 0, 0, b2, f) > a1
+    with pytest.raises(ValueError):
+        lact.workspace_size(P(), 1000, 0, 0, b, [3, 3, 300])
+    for i in range(200):   # more schedules than the cache keeps
+        assert lact.workspace_size(P(), 1000, 0, 0, [0, 256 + i, 640 + i, 1000], f) > 0
+    assert lact.workspace_size(P(), 1000, 0, 0, b, f) == a1
+
+
 def test_binding_workspace_must_be_bytes():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError, match="uint8"):

@@ -340,6 +340,25 @@ __global__ __launch_bounds__(NT) void bwd_mom_finish_kernel(const float* part, i
     dbeta[i * beta_bs + t0 + t] = g;
 }
 
+// fp32 -> P bf16 planes (the rounding of split_planes), same layout: batch
+// entries of `per` valid elements at stride bs; plane p at out + p * ps
+template <int P>
+__global__ __launch_bounds__(NT) void bwd_planes_kernel(const float* x, int64_t per, int64_t bs, int batch,
+                                                        bf16_t* out, int64_t ps) {
+  const int64_t nq = per / 4, total = nq * batch;
+  for (int64_t q = blockIdx.x * (int64_t)NT + threadIdx.x; q < total; q += (int64_t)gridDim.x * NT) {
+    const int64_t off = (q / nq) * bs + (q % nq) * 4;
+    const float4 v = *reinterpret_cast<const float4*>(x + off);
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t h[4][P];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) split_planes<P>(e[r], h[r]);
+#pragma unroll
+    for (int pl = 0; pl < P; ++pl)
+      *reinterpret_cast<uint2*>(out + pl * ps + off) = make_uint2(h[0][pl] | (h[1][pl] << 16), h[2][pl] | (h[3][pl] << 16));
+  }
+}
+
 // Split-K reduction: C[b][m, n] = sum_s P[s][b][m, n] + beta Cin[b][m, n],
 // partials compact ([S][batch][M][N]); Cin has C's strides and may be C.
 __global__ __launch_bounds__(NT) void bwd_splitsum_kernel(const float* P, int S, int batch, int M, int N, float* C,

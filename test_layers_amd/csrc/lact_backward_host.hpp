@@ -83,6 +83,43 @@ int bwd_splits(int64_t tiles, int64_t K) {
   return (int)std::max<int64_t>(1, std::min<int64_t>({64, want, K / 256}));
 }
 
+// Token contractions whose first operand is an fp32 token buffer read
+// column-k (E^T k, gA^T k, dAq^T q) against a bf16 input (k, q): the first
+// operand is split into PL bf16 planes once, in its own layout, and the
+// product runs on the direct-load GEMM (plane pairs with the exact second
+// operand, smallest plane first) instead of splitting every tile's loads in
+// registers.  apl: plane scratch, ng x PL x batch x A.bs elements.
+template <int PL>
+lact_status bgemm_planes(GemmArgs& g, int64_t a_ld, int64_t a_bs, int64_t K, bf16_t* apl, hipStream_t s) {
+  const int64_t per = K * a_ld;                  // valid elements of one batch entry
+  const int64_t ps = (int64_t)g.batch * a_bs;    // plane stride
+  for (int i = 0; i < g.ngroups; ++i) {
+    bf16_t* dst = apl + (int64_t)i * PL * ps;
+    {
+      KernelTimer kt(LACT_K_BWD_ELEM, s);
+      LACT_LAUNCH((bwd_planes_kernel<PL>), dim3(ew_grid(g.batch * per / 4)), dim3(NT), s,
+                  static_cast<const float*>(g.g[i].A), per, a_bs, g.batch, dst, ps);
+      HIP_TRY(hipGetLastError());
+    }
+    g.g[i].A = dst;
+  }
+  g.a_ps = ps;
+  int64_t grid = 0;
+  for (int i = 0; i < g.ngroups; ++i) {
+    const int64_t t = (int64_t)(g.g[i].M / 64) * (g.N / 64) * g.batch * g.splits;
+    if (t > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+    g.g[i].tiles = (int)t;
+    grid += t;
+  }
+  if (grid <= 0) return LACT_OK;
+  if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
+  KernelTimer kt(LACT_K_BWD_GEMM, s);
+  constexpr int NST = PL <= 2 ? 3 : 2;   // 24 KB (two planes) or 32 KB stages
+  LACT_LAUNCH((dgemm_kernel<true, true, float, 64, 64, NST, PL>), dim3((unsigned)grid), dim3(DG_THREADS), s, g);
+  HIP_TRY(hipGetLastError());
+  return LACT_OK;
+}
+
 // one product of a group: its own A, B, C and accumulation source
 struct BGrp {
   const void* A;
@@ -96,11 +133,20 @@ struct BGrp {
 // itself; NULL: no accumulation).  A and B give the operands' layout (their
 // pointers are ignored).  Long contractions with few output tiles are split
 // over K into fp32 partials in `spl` (spl_floats of scratch), summed in
-// fixed order by bwd_splitsum_kernel.
+// fixed order by bwd_splitsum_kernel.  With plane scratch `apl` (apl_elems
+// bf16), the token contractions of bgemm_planes' form take that path.
 lact_status bgemm_g(const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t ldc, int64_t c_bs, int M, int N,
                     int64_t K, int batch, float alpha, float beta, float* spl, size_t spl_floats, hipStream_t s,
-                    bool fp32_grade = false) {
+                    bool fp32_grade = false, bf16_t* apl = nullptr, size_t apl_elems = 0) {
   if (M <= 0 || N <= 0 || batch <= 0 || ng <= 0) return LACT_OK;
+  const int PLA = fp32_grade ? 3 : 2;
+  const bool planes = apl != nullptr && !A.bf16 && A.colk && B.bf16 && B.colk && M % 64 == 0 && N % 64 == 0 &&
+                      K % 64 == 0 && A.ld % 4 == 0 && A.bs % 4 == 0 &&
+                      (size_t)ng * PLA * (size_t)batch * (size_t)A.bs <= apl_elems;
+  auto run = [&](GemmArgs& ga) -> lact_status {
+    if (planes) return fp32_grade ? bgemm_planes<3>(ga, A.ld, A.bs, K, apl, s) : bgemm_planes<2>(ga, A.ld, A.bs, K, apl, s);
+    return fp32_grade ? bgemm_form<3>(A, B, ga, s) : bgemm_form<2>(A, B, ga, s);
+  };
   GemmArgs g = gemm_args();
   g.ngroups = ng;
   g.lda = A.ld;
@@ -116,8 +162,10 @@ lact_status bgemm_g(const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t 
   const int64_t mnb = (int64_t)M * N * batch;
   while (S > 1 && (size_t)S * ng * mnb > spl_floats) --S;
   if (S > 1) {
+    // split boundaries on whole k stages (32 wide; 64 on the plane path)
+    const int64_t kq = planes ? 64 : 32;
     g.kps = (K + S - 1) / S;
-    g.kps = (g.kps + 31) / 32 * 32;
+    g.kps = (g.kps + kq - 1) / kq * kq;
     S = (int)((K + g.kps - 1) / g.kps);
   }
   if (S > 1) {
@@ -133,7 +181,7 @@ lact_status bgemm_g(const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t 
       g.g[i].Cin = nullptr;
       g.g[i].M = M;
     }
-    lact_status r = fp32_grade ? bgemm_form<3>(A, B, g, s) : bgemm_form<2>(A, B, g, s);
+    lact_status r = run(g);
     if (r) return r;
     for (int i = 0; i < ng; ++i) {
       KernelTimer kt(LACT_K_BWD_ELEM, s);
@@ -155,7 +203,7 @@ lact_status bgemm_g(const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t 
     g.g[i].Cin = gs[i].Cin;
     g.g[i].M = M;
   }
-  return fp32_grade ? bgemm_form<3>(A, B, g, s) : bgemm_form<2>(A, B, g, s);
+  return run(g);
 }
 
 // one Newton-Schulz product (fp32 grade)
@@ -186,6 +234,7 @@ struct BwdWs {
   size_t X = 0, Am = 0, Pm = 0, gP = 0, gA = 0, Qm = 0, g0 = 0, g1 = 0, nrm = 0, part = 0;
   size_t mpart = 0;
   size_t spl = 0, spl_floats = 0;   // split-K partials of the token contractions
+  size_t apl = 0, apl_elems = 0;     // bf16 planes of a token contraction's fp32 operands
   size_t qf = 0, kf = 0, vf = 0;     // LACT_QK_PREP: fp32 q^, k^ and v [n, L, d]
   size_t total = 0;
 };
@@ -265,6 +314,9 @@ BwdWs bwd_layout(const lact_problem& p, const std::vector<int64_t>& b, const std
     const size_t s1 = (size_t)bwd_splits(tb, w.cmax) * n * DD;
     w.spl_floats = std::max(s1, s2);
     w.spl = take(w.spl_floats * 4);
+    // two groups of planes of one [n, cmax, dh] token buffer
+    w.apl_elems = 2 * (size_t)(uses_ns(p.opt) ? 3 : 2) * n * (size_t)w.cmax * Dh;
+    w.apl = take(w.apl_elems * 2);
   }
   if (p.flags & LACT_QK_PREP) {
     const size_t L = (size_t)b.back();
@@ -482,7 +534,8 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   };
   auto gemmg = [&](const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t ldc, int64_t c_bs, int M, int N,
                    int64_t K, int batch, float alpha, float beta, float* spl, size_t spl_floats, hipStream_t st) {
-    return bgemm_g(gs, ng, A, B, ldc, c_bs, M, N, K, batch, alpha, beta, spl, spl_floats, st, fp32g);
+    return bgemm_g(gs, ng, A, B, ldc, c_bs, M, N, K, batch, alpha, beta, spl, spl_floats, st, fp32g,
+                   reinterpret_cast<bf16_t*>(ws + w.apl), w.apl_elems);
   };
 
   // ---- apply backward of rows [t0, t0 + C) read with weights Wa

@@ -33,9 +33,20 @@ struct BOp {
   int64_t ld, bs;
   bool colk;   // element (m, k) at p[k ld + m]; else at p[m ld + k]
   bool bf16;
+  // an fp32 operand already split into bf16 planes: the planes of the
+  // element at pl_base + e are at pl + e + q * pl_ps
+  const bf16_t* pl = nullptr;
+  const float* pl_base = nullptr;
+  int64_t pl_ps = 0;
 };
 inline BOp bop(const void* p, int64_t ld, int64_t bs, bool colk, bool bf16 = false) {
   return BOp{p, ld, bs, colk, bf16};
+}
+inline BOp with_planes(BOp o, const bf16_t* pl, const float* base, int64_t ps) {
+  o.pl = pl;
+  o.pl_base = base;
+  o.pl_ps = ps;
+  return o;
 }
 
 template <typename TA, int PA, bool CA, typename TB, int PB, bool CB>
@@ -83,27 +94,50 @@ int bwd_splits(int64_t tiles, int64_t K) {
   return (int)std::max<int64_t>(1, std::min<int64_t>({64, want, K / 256}));
 }
 
-// Token contractions whose first operand is an fp32 token buffer read
-// column-k (E^T k, gA^T k, dAq^T q) against a bf16 input (k, q): the first
-// operand is split into PL bf16 planes once, in its own layout, and the
-// product runs on the direct-load GEMM (plane pairs with the exact second
-// operand, smallest plane first) instead of splitting every tile's loads in
-// registers.  apl: plane scratch, ng x PL x batch x A.bs elements.
-template <int PL>
-lact_status bgemm_planes(GemmArgs& g, int64_t a_ld, int64_t a_bs, int64_t K, bf16_t* apl, hipStream_t s) {
-  const int64_t per = K * a_ld;                  // valid elements of one batch entry
-  const int64_t ps = (int64_t)g.batch * a_bs;    // plane stride
+// Products with fp32 operands on the direct-load GEMM: each fp32 operand is
+// split into PL bf16 planes once, in its own layout (bf16 inputs stay one
+// exact plane), and the product sums the plane pairs in dgemm_kernel instead
+// of splitting every tile's loads in registers (the register path).
+// Scratch: `apl` holds the first operands' planes (ng x PA x batch x A.bs
+// elements), `bpl` the second's.
+inline lact_status bwd_split(const void* src, int64_t per, int64_t bs, int batch, int P, bf16_t* dst, int64_t ps,
+                             hipStream_t s) {
+  KernelTimer kt(LACT_K_BWD_ELEM, s);
+  const dim3 grid(ew_grid((int64_t)batch * per / 4));
+  if (P == 3) LACT_LAUNCH((bwd_planes_kernel<3>), grid, dim3(NT), s, static_cast<const float*>(src), per, bs, batch, dst, ps);
+  else LACT_LAUNCH((bwd_planes_kernel<2>), grid, dim3(NT), s, static_cast<const float*>(src), per, bs, batch, dst, ps);
+  HIP_TRY(hipGetLastError());
+  return LACT_OK;
+}
+
+template <bool CA, bool CB, int PA, int PB>
+lact_status bgemm_planes(GemmArgs& g, const BOp& A, const BOp& B, int64_t K, bf16_t* apl, bf16_t* bpl, hipStream_t s) {
+  // the valid rows of each operand: k rows when read column-k, else its M (N) rows
+  const int64_t a_ps = A.pl ? A.pl_ps : (int64_t)g.batch * A.bs, b_ps = B.pl ? B.pl_ps : (int64_t)g.batch * B.bs;
   for (int i = 0; i < g.ngroups; ++i) {
-    bf16_t* dst = apl + (int64_t)i * PL * ps;
-    {
-      KernelTimer kt(LACT_K_BWD_ELEM, s);
-      LACT_LAUNCH((bwd_planes_kernel<PL>), dim3(ew_grid(g.batch * per / 4)), dim3(NT), s,
-                  static_cast<const float*>(g.g[i].A), per, a_bs, g.batch, dst, ps);
-      HIP_TRY(hipGetLastError());
+    if constexpr (PA > 1) {
+      if (A.pl) {
+        g.g[i].A = A.pl + (static_cast<const float*>(g.g[i].A) - A.pl_base);
+      } else {
+        bf16_t* dst = apl + (int64_t)i * PA * a_ps;
+        const int64_t per = (CA ? K : (int64_t)g.g[i].M) * A.ld;
+        if (lact_status r = bwd_split(g.g[i].A, per, A.bs, g.batch, PA, dst, a_ps, s)) return r;
+        g.g[i].A = dst;
+      }
     }
-    g.g[i].A = dst;
+    if constexpr (PB > 1) {
+      if (B.pl) {
+        g.g[i].B = B.pl + (static_cast<const float*>(g.g[i].B) - B.pl_base);
+      } else {
+        bf16_t* dst = bpl + (int64_t)i * PB * b_ps;
+        const int64_t per = (CB ? K : (int64_t)g.N) * B.ld;
+        if (lact_status r = bwd_split(g.g[i].B, per, B.bs, g.batch, PB, dst, b_ps, s)) return r;
+        g.g[i].B = dst;
+      }
+    }
   }
-  g.a_ps = ps;
+  g.a_ps = a_ps;
+  g.b_ps = b_ps;
   int64_t grid = 0;
   for (int i = 0; i < g.ngroups; ++i) {
     const int64_t t = (int64_t)(g.g[i].M / 64) * (g.N / 64) * g.batch * g.splits;
@@ -114,10 +148,29 @@ lact_status bgemm_planes(GemmArgs& g, int64_t a_ld, int64_t a_bs, int64_t K, bf1
   if (grid <= 0) return LACT_OK;
   if (grid > 0x7fffffff) return fail(LACT_ERR_UNSUPPORTED, "grid too large");
   KernelTimer kt(LACT_K_BWD_GEMM, s);
-  constexpr int NST = PL <= 2 ? 3 : 2;   // 24 KB (two planes) or 32 KB stages
-  LACT_LAUNCH((dgemm_kernel<true, true, float, 64, 64, NST, PL>), dim3((unsigned)grid), dim3(DG_THREADS), s, g);
+  constexpr int NST = PA + PB <= 3 ? 3 : 2;   // 64-wide stages: 24 KB (three planes) to 48 KB (six)
+  LACT_LAUNCH((dgemm_kernel<CA, CB, float, 64, 64, NST, PA, PB>), dim3((unsigned)grid), dim3(DG_THREADS), s, g);
   HIP_TRY(hipGetLastError());
   return LACT_OK;
+}
+
+// the forms the backward's products take (layout of A and B, which are fp32)
+template <int PL>
+lact_status bgemm_planes_form(GemmArgs& g, const BOp& A, const BOp& B, int64_t K, bf16_t* apl, bf16_t* bpl,
+                              hipStream_t s) {
+  const bool fa = !A.bf16, fb = !B.bf16;
+  if (fa && !fb && A.colk && B.colk) return bgemm_planes<true, true, PL, 1>(g, A, B, K, apl, bpl, s);
+  if (!fa && fb && A.colk && B.colk) return bgemm_planes<true, true, 1, PL>(g, A, B, K, apl, bpl, s);
+  if (!fa && fb && !A.colk && !B.colk) return bgemm_planes<false, false, 1, PL>(g, A, B, K, apl, bpl, s);
+  if (!fa && fb && !A.colk && B.colk) return bgemm_planes<false, true, 1, PL>(g, A, B, K, apl, bpl, s);
+  if (fa && fb && !A.colk && B.colk) return bgemm_planes<false, true, PL, PL>(g, A, B, K, apl, bpl, s);
+  if (fa && fb && !A.colk && !B.colk) return bgemm_planes<false, false, PL, PL>(g, A, B, K, apl, bpl, s);
+  return fail(LACT_ERR_UNSUPPORTED, "internal: backward plane product form");
+}
+inline bool bgemm_planes_has_form(const BOp& A, const BOp& B) {
+  const bool fa = !A.bf16, fb = !B.bf16;
+  return (fa && !fb && A.colk && B.colk) || (!fa && fb && A.colk && B.colk) || (!fa && fb && !A.colk && !B.colk) ||
+         (!fa && fb && !A.colk && B.colk) || (fa && fb && !A.colk);
 }
 
 // one product of a group: its own A, B, C and accumulation source
@@ -139,12 +192,21 @@ lact_status bgemm_g(const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t 
                     int64_t K, int batch, float alpha, float beta, float* spl, size_t spl_floats, hipStream_t s,
                     bool fp32_grade = false, bf16_t* apl = nullptr, size_t apl_elems = 0) {
   if (M <= 0 || N <= 0 || batch <= 0 || ng <= 0) return LACT_OK;
-  const int PLA = fp32_grade ? 3 : 2;
-  const bool planes = apl != nullptr && !A.bf16 && A.colk && B.bf16 && B.colk && M % 64 == 0 && N % 64 == 0 &&
-                      K % 64 == 0 && A.ld % 4 == 0 && A.bs % 4 == 0 &&
-                      (size_t)ng * PLA * (size_t)batch * (size_t)A.bs <= apl_elems;
+  // fp32 operands not already split are split here: worth a launch only
+  // for large ones (token buffers); small weight-shaped ones must come split
+  const size_t PL = fp32_grade ? 3 : 2;
+  const size_t need_a = (A.bf16 || A.pl) ? 0 : (size_t)ng * PL * (size_t)batch * (size_t)A.bs;
+  const size_t need_b = (B.bf16 || B.pl) ? 0 : (size_t)ng * PL * (size_t)batch * (size_t)B.bs;
+  const size_t big = (size_t)1 << 20;   // elements
+  const bool cheap_a = A.bf16 || A.pl || (size_t)batch * (size_t)A.bs >= big;
+  const bool cheap_b = B.bf16 || B.pl || (size_t)batch * (size_t)B.bs >= big;
+  const bool planes = apl != nullptr && bgemm_planes_has_form(A, B) && cheap_a && cheap_b && M % 64 == 0 &&
+                      N % 64 == 0 && K % 64 == 0 && A.ld % 4 == 0 && A.bs % 4 == 0 && B.ld % 4 == 0 && B.bs % 4 == 0 &&
+                      need_a <= apl_elems / 2 && need_b <= apl_elems / 2;
+  bf16_t* bpl = apl ? apl + apl_elems / 2 : nullptr;
   auto run = [&](GemmArgs& ga) -> lact_status {
-    if (planes) return fp32_grade ? bgemm_planes<3>(ga, A.ld, A.bs, K, apl, s) : bgemm_planes<2>(ga, A.ld, A.bs, K, apl, s);
+    if (planes)
+      return fp32_grade ? bgemm_planes_form<3>(ga, A, B, K, apl, bpl, s) : bgemm_planes_form<2>(ga, A, B, K, apl, bpl, s);
     return fp32_grade ? bgemm_form<3>(A, B, ga, s) : bgemm_form<2>(A, B, ga, s);
   };
   GemmArgs g = gemm_args();
@@ -235,6 +297,8 @@ struct BwdWs {
   size_t mpart = 0;
   size_t spl = 0, spl_floats = 0;   // split-K partials of the token contractions
   size_t apl = 0, apl_elems = 0;     // bf16 planes of a token contraction's fp32 operands
+  size_t wpl = 0, upl = 0;           // bf16 planes of the chunk's weight set and of gU
+  size_t tpl = 0;                    // bf16 planes of three consecutive token buffers
   size_t qf = 0, kf = 0, vf = 0;     // LACT_QK_PREP: fp32 q^, k^ and v [n, L, d]
   size_t total = 0;
 };
@@ -314,9 +378,15 @@ BwdWs bwd_layout(const lact_problem& p, const std::vector<int64_t>& b, const std
     const size_t s1 = (size_t)bwd_splits(tb, w.cmax) * n * DD;
     w.spl_floats = std::max(s1, s2);
     w.spl = take(w.spl_floats * 4);
-    // two groups of planes of one [n, cmax, dh] token buffer
-    w.apl_elems = 2 * (size_t)(uses_ns(p.opt) ? 3 : 2) * n * (size_t)w.cmax * Dh;
+    // planes of the products' fp32 operands (token buffers [n, cmax, dh] or
+    // weight-shaped [n, d dh]): two groups per operand, first half for the
+    // first operands, second half for the second
+    const size_t opnd = std::max((size_t)w.cmax * Dh, DD) * n;
+    w.apl_elems = 2 * 2 * (size_t)(uses_ns(p.opt) ? 3 : 2) * opnd;
     w.apl = take(w.apl_elems * 2);
+    w.wpl = take((size_t)(uses_ns(p.opt) ? 3 : 2) * 3 * n * DD * 2);
+    w.upl = take((size_t)(uses_ns(p.opt) ? 3 : 2) * 3 * n * DD * 2);
+    w.tpl = take((size_t)(uses_ns(p.opt) ? 3 : 2) * 3 * n * (size_t)w.cmax * Dh * 2);
   }
   if (p.flags & LACT_QK_PREP) {
     const size_t L = (size_t)b.back();
@@ -530,7 +600,8 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   auto gemm1 = [&](BOp A, BOp B, float* C, int64_t ldc, int64_t c_bs, int M, int N, int64_t K, int batch,
                    float alpha, const float* Cin, float beta, hipStream_t st) {
     const BGrp g1{A.p, B.p, C, Cin};
-    return bgemm_g(&g1, 1, A, B, ldc, c_bs, M, N, K, batch, alpha, beta, nullptr, 0, st, fp32g);
+    return bgemm_g(&g1, 1, A, B, ldc, c_bs, M, N, K, batch, alpha, beta, nullptr, 0, st, fp32g,
+                   reinterpret_cast<bf16_t*>(ws + w.apl), w.apl_elems);
   };
   auto gemmg = [&](const BGrp* gs, int ng, const BOp& A, const BOp& B, int64_t ldc, int64_t c_bs, int M, int N,
                    int64_t K, int batch, float alpha, float beta, float* spl, size_t spl_floats, hipStream_t st) {
@@ -538,20 +609,44 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
                    reinterpret_cast<bf16_t*>(ws + w.apl), w.apl_elems);
   };
 
+  // weight-shaped sets (W1 | W2 | W3 contiguous) split into bf16 planes once
+  // per chunk, for the products that read them on the direct-load GEMM
+  const int PLW = fp32g ? 3 : 2;
+  const int64_t setps = 3 * (int64_t)n * DD;   // plane stride of a set's planes
+  bf16_t* WPL = reinterpret_cast<bf16_t*>(ws + w.wpl);
+  bf16_t* UPL = reinterpret_cast<bf16_t*>(ws + w.upl);
+  auto contiguous = [&](const MatC& m) { return m.p[1] == m.p[0] + (int64_t)n * DD && m.p[2] == m.p[0] + 2 * (int64_t)n * DD; };
+  auto split_set = [&](const MatC& m, bf16_t* dst) -> lact_status {
+    if (!contiguous(m)) return LACT_OK;
+    return bwd_split(m.p[0], setps, setps, 1, PLW, dst, setps, s);
+  };
+  auto wop = [&](BOp o, const MatC& m, const bf16_t* pl) { return contiguous(m) ? with_planes(o, pl, m.p[0], setps) : o; };
+  // token buffers tk[j0 .. j0 + 2] (contiguous [n, cmax, dh] each) split once
+  // after their producer, read by the products that follow
+  bf16_t* TPL = reinterpret_cast<bf16_t*>(ws + w.tpl);
+  const int64_t tps = 3 * (int64_t)n * buf_bs;
+  auto tok_contig = [&](int j0) { return tk[j0 + 1] == tk[j0] + (int64_t)n * buf_bs && tk[j0 + 2] == tk[j0] + 2 * (int64_t)n * buf_bs; };
+  auto split_tok = [&](int j0) -> lact_status {
+    if (!tok_contig(j0)) return LACT_OK;
+    return bwd_split(tk[j0], tps, tps, 1, PLW, TPL, tps, s);
+  };
+  auto tokop = [&](BOp o, int j0) { return tok_contig(j0) ? with_planes(o, TPL, tk[j0], tps) : o; };
+
   // ---- apply backward of rows [t0, t0 + C) read with weights Wa
   auto apply_bwd = [&](const MatC& Wa, int64_t t0, int64_t C) -> lact_status {
     lact_status q;
+    if ((q = split_set(Wa, WPL))) return q;
     const char* Q = static_cast<const char*>(Qs) + (size_t)t0 * D * eq;
     const char* dO = static_cast<const char*>(P.dO) + (size_t)t0 * D * eo;
     // Aq = q W1^T, Bq = q W3^T (one launch), dHq = dO W2
     {
       const BGrp g2[2] = {{Q, Wa.p[0], tk[0], nullptr}, {Q, Wa.p[2], tk[1], nullptr}};
-      if ((q = gemmg(g2, 2, bop(Q, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
-                       1.f, 0.f, nullptr, 0, s)))
+      if ((q = gemmg(g2, 2, bop(Q, D, x_bs, false, bq), wop(bop(nullptr, D, DD, false), Wa, WPL), Dh, buf_bs, (int)C,
+                       Dh, D, n, 1.f, 0.f, nullptr, 0, s)))
         return q;
     }
-    if ((q = gemm1(bop(dO, D, x_bs, false, bo), bop(Wa.p[1], Dh, DD, true), tk[2], Dh, buf_bs, (int)C, Dh, D, n,
-                   1.f, nullptr, 0.f, s)))
+    if ((q = gemm1(bop(dO, D, x_bs, false, bo), wop(bop(Wa.p[1], Dh, DD, true), Wa, WPL), tk[2], Dh, buf_bs, (int)C,
+                   Dh, D, n, 1.f, nullptr, 0.f, s)))
       return q;
     // -> dAq, dBq, Hq (with an output scale: s Hq, and doz)
     if (P.oz)
@@ -559,30 +654,32 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
                  t0, P.doz, n, C, Dh, buf_bs);
     else
       BWD_LAUNCH(bwd_app_elem_kernel, dim3(ew_grid((int64_t)n * C * Dh)), tk[0], tk[1], tk[2], n, C, Dh, buf_bs);
+    if ((q = split_tok(0))) return q;
     // dW2 += dO^T Hq ; dW1 += dAq^T q, dW3 += dBq^T q (one launch); split over tokens
     {
       const BGrp g1[1] = {{dO, tk[2], DW.p[1], DW.p[1]}};
-      if ((q = gemmg(g1, 1, bop(dO, D, x_bs, true, bo), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
-                       1.f, fp(w.spl), w.spl_floats, s)))
+      if ((q = gemmg(g1, 1, bop(dO, D, x_bs, true, bo), tokop(bop(nullptr, Dh, buf_bs, true), 0), Dh, DD, D, Dh, C, n,
+                       1.f, 1.f, fp(w.spl), w.spl_floats, s)))
         return q;
       const BGrp g2[2] = {{tk[0], Q, DW.p[0], DW.p[0]}, {tk[1], Q, DW.p[2], DW.p[2]}};
-      if ((q = gemmg(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(Q, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f,
-                       1.f, fp(w.spl), w.spl_floats, s)))
+      if ((q = gemmg(g2, 2, tokop(bop(nullptr, Dh, buf_bs, true), 0), bop(Q, D, x_bs, true, bq), D, DD, Dh, D, C, n,
+                       1.f, 1.f, fp(w.spl), w.spl_floats, s)))
         return q;
     }
     // dq = dAq W1 + dBq W3
     float* dq = P.dq + t0 * D;
-    if ((q = gemm1(bop(tk[0], Dh, buf_bs, false), bop(Wa.p[0], D, DD, true), dq, D, x_bs, (int)C, D, Dh, n, 1.f,
-                   nullptr, 0.f, s)))
+    if ((q = gemm1(tokop(bop(tk[0], Dh, buf_bs, false), 0), wop(bop(Wa.p[0], D, DD, true), Wa, WPL), dq, D, x_bs,
+                   (int)C, D, Dh, n, 1.f, nullptr, 0.f, s)))
       return q;
-    return gemm1(bop(tk[1], Dh, buf_bs, false), bop(Wa.p[2], D, DD, true), dq, D, x_bs, (int)C, D, Dh, n, 1.f, dq,
-                 1.f, s);
+    return gemm1(tokop(bop(tk[1], Dh, buf_bs, false), 0), wop(bop(Wa.p[2], D, DD, true), Wa, WPL), dq, D, x_bs,
+                 (int)C, D, Dh, n, 1.f, dq, 1.f, s);
   };
 
   // ---- update backward of chunk [t0, t0 + C), update ordinal u
   auto update_bwd = [&](int u, int64_t t0, int64_t C) -> lact_status {
     lact_status q;
     const MatC Wb = cset(slotW(u));
+    if ((q = split_set(Wb, WPL))) return q;
     const char* K = static_cast<const char*>(Ks) + (size_t)t0 * D * eq;
     const char* V = static_cast<const char*>(Vs) + (size_t)t0 * D * ev;
     float *A_ = tk[0], *B_ = tk[1], *G_ = tk[2], *E1 = tk[3], *E3 = tk[4], *H2 = tk[5], *gE1 = tk[6], *gE3 = tk[7],
@@ -590,24 +687,25 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
     // recompute A = k W1^T, B = k W3^T (one launch), G = v W2 and the update terms
     {
       const BGrp g2[2] = {{K, Wb.p[0], A_, nullptr}, {K, Wb.p[2], B_, nullptr}};
-      if ((q = gemmg(g2, 2, bop(K, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
-                       1.f, 0.f, nullptr, 0, s)))
+      if ((q = gemmg(g2, 2, bop(K, D, x_bs, false, bq), wop(bop(nullptr, D, DD, false), Wb, WPL), Dh, buf_bs, (int)C,
+                       Dh, D, n, 1.f, 0.f, nullptr, 0, s)))
         return q;
     }
-    if ((q = gemm1(bop(V, D, x_bs, false, bv), bop(Wb.p[1], Dh, DD, true), G_, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
-                   nullptr, 0.f, s)))
+    if ((q = gemm1(bop(V, D, x_bs, false, bv), wop(bop(Wb.p[1], Dh, DD, true), Wb, WPL), G_, Dh, buf_bs, (int)C, Dh,
+                   D, n, 1.f, nullptr, 0.f, s)))
       return q;
     BWD_LAUNCH(bwd_upd_terms_kernel, dim3(ew_grid((int64_t)n * C * Dh)), (const float*)A_, (const float*)B_,
                (const float*)G_, P.lr, L * 3, t0, E1, E3, H2, n, C, Dh, buf_bs);
+    if ((q = split_tok(3))) return q;
     // U1 = E1^T k, U3 = E3^T k (one launch), U2 = v^T H2; split over tokens
     {
       const BGrp g2[2] = {{E1, K, U.p[0], nullptr}, {E3, K, U.p[2], nullptr}};
-      if ((q = gemmg(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f,
-                       0.f, fp(w.spl), w.spl_floats, s)))
+      if ((q = gemmg(g2, 2, tokop(bop(nullptr, Dh, buf_bs, true), 3), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n,
+                       1.f, 0.f, fp(w.spl), w.spl_floats, s)))
         return q;
       const BGrp g1[1] = {{V, H2, U.p[1], nullptr}};
-      if ((q = gemmg(g1, 1, bop(V, D, x_bs, true, bv), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f,
-                       0.f, fp(w.spl), w.spl_floats, s)))
+      if ((q = gemmg(g1, 1, bop(V, D, x_bs, true, bv), tokop(bop(nullptr, Dh, buf_bs, true), 3), Dh, DD, D, Dh, C, n,
+                       1.f, 0.f, fp(w.spl), w.spl_floats, s)))
         return q;
     }
     // the weight step W' = W + sgn step
@@ -647,48 +745,50 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
                  (const float*)fp(w.mpart), BWD_NBM, P.dbeta, L, t0, C);
     }
     // through the update terms: gE1 = k gU1^T, gE3 = k gU3^T (one launch), gH2 = v gU2
+    if ((q = split_set(gU, UPL))) return q;
     {
       const BGrp g2[2] = {{K, gU.p[0], gE1, nullptr}, {K, gU.p[2], gE3, nullptr}};
-      if ((q = gemmg(g2, 2, bop(K, D, x_bs, false, bq), bop(nullptr, D, DD, false), Dh, buf_bs, (int)C, Dh, D, n,
-                       1.f, 0.f, nullptr, 0, s)))
+      if ((q = gemmg(g2, 2, bop(K, D, x_bs, false, bq), wop(bop(nullptr, D, DD, false), gU, UPL), Dh, buf_bs, (int)C,
+                       Dh, D, n, 1.f, 0.f, nullptr, 0, s)))
         return q;
     }
-    if ((q = gemm1(bop(V, D, x_bs, false, bv), bop(gU.p[1], Dh, DD, true), gH2, Dh, buf_bs, (int)C, Dh, D, n, 1.f,
-                   nullptr, 0.f, s)))
+    if ((q = gemm1(bop(V, D, x_bs, false, bv), wop(bop(gU.p[1], Dh, DD, true), gU, UPL), gH2, Dh, buf_bs, (int)C, Dh,
+                   D, n, 1.f, nullptr, 0.f, s)))
       return q;
     // dk = E1 gU1 + E3 gU3 ; dv = H2 gU2^T
     float* dk = P.dk + t0 * D;
     float* dv = P.dv + t0 * D;
-    if ((q = gemm1(bop(E1, Dh, buf_bs, false), bop(gU.p[0], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f,
-                   nullptr, 0.f, s)))
+    if ((q = gemm1(tokop(bop(E1, Dh, buf_bs, false), 3), wop(bop(gU.p[0], D, DD, true), gU, UPL), dk, D, x_bs, (int)C,
+                   D, Dh, n, 1.f, nullptr, 0.f, s)))
       return q;
-    if ((q = gemm1(bop(E3, Dh, buf_bs, false), bop(gU.p[2], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
-                   1.f, s)))
+    if ((q = gemm1(tokop(bop(E3, Dh, buf_bs, false), 3), wop(bop(gU.p[2], D, DD, true), gU, UPL), dk, D, x_bs, (int)C,
+                   D, Dh, n, 1.f, dk, 1.f, s)))
       return q;
-    if ((q = gemm1(bop(H2, Dh, buf_bs, false), bop(gU.p[1], Dh, DD, false), dv, D, x_bs, (int)C, D, Dh, n, 1.f,
-                   nullptr, 0.f, s)))
+    if ((q = gemm1(tokop(bop(H2, Dh, buf_bs, false), 3), wop(bop(gU.p[1], Dh, DD, false), gU, UPL), dv, D, x_bs,
+                   (int)C, D, Dh, n, 1.f, nullptr, 0.f, s)))
       return q;
     // -> gA, gB, gG (in place) and dlr
     BWD_LAUNCH(bwd_upd_elem_kernel, dim3((unsigned)(((int64_t)n * C + 3) / 4)), (const float*)A_, (const float*)B_,
                (const float*)G_, P.lr, L * 3, t0, gE1, gE3, gH2, P.dlr, n, C, Dh, buf_bs);
+    if ((q = split_tok(6))) return q;
     // dk += gA W1 + gB W3 ; dv += gG W2^T
-    if ((q = gemm1(bop(gE1, Dh, buf_bs, false), bop(Wb.p[0], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
-                   1.f, s)))
+    if ((q = gemm1(tokop(bop(gE1, Dh, buf_bs, false), 6), wop(bop(Wb.p[0], D, DD, true), Wb, WPL), dk, D, x_bs,
+                   (int)C, D, Dh, n, 1.f, dk, 1.f, s)))
       return q;
-    if ((q = gemm1(bop(gE3, Dh, buf_bs, false), bop(Wb.p[2], D, DD, true), dk, D, x_bs, (int)C, D, Dh, n, 1.f, dk,
-                   1.f, s)))
+    if ((q = gemm1(tokop(bop(gE3, Dh, buf_bs, false), 6), wop(bop(Wb.p[2], D, DD, true), Wb, WPL), dk, D, x_bs,
+                   (int)C, D, Dh, n, 1.f, dk, 1.f, s)))
       return q;
-    if ((q = gemm1(bop(gH2, Dh, buf_bs, false), bop(Wb.p[1], Dh, DD, false), dv, D, x_bs, (int)C, D, Dh, n, 1.f, dv,
-                   1.f, s)))
+    if ((q = gemm1(tokop(bop(gH2, Dh, buf_bs, false), 6), wop(bop(Wb.p[1], Dh, DD, false), Wb, WPL), dv, D, x_bs,
+                   (int)C, D, Dh, n, 1.f, dv, 1.f, s)))
       return q;
     // dW1 += gA^T k, dW3 += gB^T k (one launch) ; dW2 += v^T gG; split over tokens
     const BGrp g2[2] = {{gE1, K, DW.p[0], DW.p[0]}, {gE3, K, DW.p[2], DW.p[2]}};
-    if ((q = gemmg(g2, 2, bop(nullptr, Dh, buf_bs, true), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f, 1.f,
-                     fp(w.spl), w.spl_floats, s)))
+    if ((q = gemmg(g2, 2, tokop(bop(nullptr, Dh, buf_bs, true), 6), bop(K, D, x_bs, true, bq), D, DD, Dh, D, C, n, 1.f,
+                     1.f, fp(w.spl), w.spl_floats, s)))
       return q;
     const BGrp g1[1] = {{V, gH2, DW.p[1], DW.p[1]}};
-    return gemmg(g1, 1, bop(V, D, x_bs, true, bv), bop(nullptr, Dh, buf_bs, true), Dh, DD, D, Dh, C, n, 1.f, 1.f,
-                   fp(w.spl), w.spl_floats, s);
+    return gemmg(g1, 1, bop(V, D, x_bs, true, bv), tokop(bop(nullptr, Dh, buf_bs, true), 6), Dh, DD, D, Dh, C, n, 1.f,
+                 1.f, fp(w.spl), w.spl_floats, s);
   };
 
   // ---- reverse sweep

@@ -274,15 +274,18 @@ __device__ __forceinline__ void dpipeline_il2(int nk, bool wide, I&& issue_one, 
 constexpr int DG_THREADS = 512;
 
 // PA > 1: the first operand is an fp32 quantity stored as PA bf16 planes
-// (plane p at A + p * a_ps, lact_planes.hpp); the second is exact bf16 (an
-// input), so a product sums the PA plane products, smallest plane first.
-template <bool CA, bool CB, typename TC, int T, int BKK, int NST, int PA = 1>
+// (plane p at A + p * a_ps, lact_planes.hpp); PB > 1: the second likewise
+// (plane q at B + q * b_ps).  A product sums the plane pairs (p, q) with
+// p + q < max(PA, PB), the pairs of smaller weight first (with one exact
+// operand: its plane products, smallest plane first).
+template <bool CA, bool CB, typename TC, int T, int BKK, int NST, int PA = 1, int PB = 1>
 __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
   constexpr int NW = 8, KH = BKK / 2, NKK = KH / 32;
   using TA = typename std::conditional<CA, DTile<BKK, T, NW, true>, DTile<T, BKK, NW>>::type;
   using TB = typename std::conditional<CB, DTile<BKK, T, NW, true>, DTile<T, BKK, NW>>::type;
-  constexpr int STAGE = PA * TA::BYTES + TB::BYTES;
-  constexpr int LPS = PA * TA::INSTR + TB::INSTR;
+  constexpr int STAGE = PA * TA::BYTES + PB * TB::BYTES;
+  constexpr int LPS = PA * TA::INSTR + PB * TB::INSTR;
+  constexpr int PM = PA > PB ? PA : PB;
   constexpr int FM = T / 32, FN = T / 32;                 // quadrant T/2 x T/2
   constexpr int RED = 4 * FM * FN * 256 * 4;              // k-half reduction buffer (bytes)
   constexpr int SMEM = NST * STAGE > RED ? NST * STAGE : RED;
@@ -324,7 +327,11 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
   for (int p = 0; p < PA; ++p)
     pa[p] = CA ? TA::plan(A + p * g.a_ps, g.lda, kbeg, kmax, m0, wave, lane)
                : TA::plan(A + p * g.a_ps, g.lda, m0, M - 1, kbeg, wave, lane);
-  const typename TB::Plan pb = CB ? TB::plan(B, g.ldb, kbeg, kmax, n0, wave, lane) : TB::plan(B, g.ldb, n0, g.N - 1, kbeg, wave, lane);
+  typename TB::Plan pb[PB];
+#pragma unroll
+  for (int q = 0; q < PB; ++q)
+    pb[q] = CB ? TB::plan(B + q * g.b_ps, g.ldb, kbeg, kmax, n0, wave, lane)
+               : TB::plan(B + q * g.b_ps, g.ldb, n0, g.N - 1, kbeg, wave, lane);
   const int64_t sa = CA ? (int64_t)BKK * g.lda * 2 : (int64_t)BKK * 2;
   const int64_t sb = CB ? (int64_t)BKK * g.ldb * 2 : (int64_t)BKK * 2;
   auto issue_one = [&](int s, int buf, int idx) {
@@ -340,9 +347,15 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
         else TA::issue_one(st + p * TA::BYTES, pa[p], s * sa, wave, i);
       }
     } else {
-      const int i = idx - PA * TA::INSTR;
-      if (CB && ragged) TB::issue_one(st + PA * TA::BYTES, B, g.ldb, k0, kmax, n0, wave, lane, i);
-      else TB::issue_one(st + PA * TA::BYTES, pb, s * sb, wave, i);
+      const int ib = idx - PA * TA::INSTR;
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        if (ib / TB::INSTR != q) continue;
+        const int i = ib - q * TB::INSTR;
+        char* bt = st + PA * TA::BYTES + q * TB::BYTES;
+        if (CB && ragged) TB::issue_one(bt, B + q * g.b_ps, g.ldb, k0, kmax, n0, wave, lane, i);
+        else TB::issue_one(bt, pb[q], s * sb, wave, i);
+      }
     }
   };
 
@@ -356,19 +369,27 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int t = 0; t < NKK; ++t) {
       const int kk = kh * KH + t * 32;
-      bf16x8 af[PA][FM], bfr[FN];
+      bf16x8 af[PA][FM], bfr[PB][FN];
 #pragma unroll
       for (int p = 0; p < PA; ++p)
 #pragma unroll
         for (int i = 0; i < FM; ++i) af[p][i] = dfrag<TA, CA>(st + p * TA::BYTES, wm * (T / 2) + i * 16, kk, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = dfrag<TB, CB>(st + PA * TA::BYTES, wn * (T / 2) + j * 16, kk, lane);
+      for (int q = 0; q < PB; ++q)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[q][j] = dfrag<TB, CB>(st + PA * TA::BYTES + q * TB::BYTES, wn * (T / 2) + j * 16, kk, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int p = PA - 1; p >= 0; --p)
+        for (int sp = PM - 1; sp >= 0; --sp)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma(bfr[j], af[p][i], acc[i][j]);
+          for (int p = 0; p < PA; ++p)
+#pragma unroll
+            for (int q = 0; q < PB; ++q)
+              if (p + q == sp)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma(bfr[q][j], af[p][i], acc[i][j]);
         hook(t * FM + i, NKK * FM);
       }
     }

@@ -615,7 +615,13 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   const int64_t setps = 3 * (int64_t)n * DD;   // plane stride of a set's planes
   bf16_t* WPL = reinterpret_cast<bf16_t*>(ws + w.wpl);
   bf16_t* UPL = reinterpret_cast<bf16_t*>(ws + w.upl);
-  auto contiguous = [&](const MatC& m) { return m.p[1] == m.p[0] + (int64_t)n * DD && m.p[2] == m.p[0] + 2 * (int64_t)n * DD; };
+  // every product that reads these planes has the chunk's length as a
+  // dimension, so a chunk whose length is not a whole number of 64-wide
+  // tiles takes the register path throughout and splits nothing
+  bool chunk_planes = false;
+  auto contiguous = [&](const MatC& m) {
+    return chunk_planes && m.p[1] == m.p[0] + (int64_t)n * DD && m.p[2] == m.p[0] + 2 * (int64_t)n * DD;
+  };
   auto split_set = [&](const MatC& m, bf16_t* dst) -> lact_status {
     if (!contiguous(m)) return LACT_OK;
     return bwd_split(m.p[0], setps, setps, 1, PLW, dst, setps, s);
@@ -625,7 +631,9 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   // after their producer, read by the products that follow
   bf16_t* TPL = reinterpret_cast<bf16_t*>(ws + w.tpl);
   const int64_t tps = 3 * (int64_t)n * buf_bs;
-  auto tok_contig = [&](int j0) { return tk[j0 + 1] == tk[j0] + (int64_t)n * buf_bs && tk[j0 + 2] == tk[j0] + 2 * (int64_t)n * buf_bs; };
+  auto tok_contig = [&](int j0) {
+    return chunk_planes && tk[j0 + 1] == tk[j0] + (int64_t)n * buf_bs && tk[j0 + 2] == tk[j0] + 2 * (int64_t)n * buf_bs;
+  };
   auto split_tok = [&](int j0) -> lact_status {
     if (!tok_contig(j0)) return LACT_OK;
     return bwd_split(tk[j0], tps, tps, 1, PLW, TPL, tps, s);
@@ -635,6 +643,7 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   // ---- apply backward of rows [t0, t0 + C) read with weights Wa
   auto apply_bwd = [&](const MatC& Wa, int64_t t0, int64_t C) -> lact_status {
     lact_status q;
+    chunk_planes = C % 64 == 0;
     if ((q = split_set(Wa, WPL))) return q;
     const char* Q = static_cast<const char*>(Qs) + (size_t)t0 * D * eq;
     const char* dO = static_cast<const char*>(P.dO) + (size_t)t0 * D * eo;
@@ -679,6 +688,7 @@ lact_status run_backward(const lact_problem& p, const BwdPtrs& P, int64_t L, int
   auto update_bwd = [&](int u, int64_t t0, int64_t C) -> lact_status {
     lact_status q;
     const MatC Wb = cset(slotW(u));
+    chunk_planes = C % 64 == 0;
     if ((q = split_set(Wb, WPL))) return q;
     const char* K = static_cast<const char*>(Ks) + (size_t)t0 * D * eq;
     const char* V = static_cast<const char*>(Vs) + (size_t)t0 * D * ev;

@@ -278,6 +278,24 @@ def test_resume_equals_single_call(lact):
         assert torch.equal(Ws[j], full[key])
 
 
+@pytest.mark.parametrize("opt", [W.OPT_MOMENTUM, W.OPT_MUON])
+def test_layer_empty_sequence_leaves_the_state(lact, opt):
+    """L = 0 on the device: the call succeeds, launches nothing that touches
+    the state, and W (and M) come back bit-identical."""
+    n, D = 2, 128
+    rng = np.random.default_rng(21)
+    Ws = [torch.from_numpy((rng.standard_normal((n, D, D)) / 8).astype(np.float32)).cuda() for _ in range(3)]
+    Ms = [torch.from_numpy((rng.standard_normal((n, D, D)) / 64).astype(np.float32)).cuda() for _ in range(3)]
+    W0, M0 = [w.clone() for w in Ws], [m.clone() for m in Ms]
+    empty = torch.empty(n, 0, D, dtype=torch.bfloat16, device="cuda")
+    o = lact.layer_forward(empty, empty, empty, torch.empty(n, 0, 3, device="cuda"),
+                           torch.empty(n, 0, device="cuda"), *Ws, *Ms, chunk=64, opt=opt)
+    torch.cuda.synchronize()
+    assert o.shape == (n, 0, D)
+    for a, b in zip(Ws + Ms, W0 + M0):
+        assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------------ raw q/k and the output scale
 @pytest.mark.parametrize("io,planes,opt", [(W.DTYPE_F32, 3, W.OPT_GD), (W.DTYPE_BF16, 1, W.OPT_MOMENTUM),
                                            (W.DTYPE_BF16, 2, W.OPT_MUON),

@@ -406,6 +406,7 @@ __global__ __launch_bounds__(DG_THREADS) void dgemm_kernel(GemmArgs g) {
       for (int j = 0; j < FN; ++j)
         *reinterpret_cast<f32x4*>(red + ((q * FM + i) * FN + j) * 256 + lane * 4) = acc[i][j];
   }
+  wait_lgkm0();   // the half-1 sums are in LDS before another wave reads them
   bar();
   if (kh == 0) {
 #pragma unroll

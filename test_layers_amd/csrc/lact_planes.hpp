@@ -191,6 +191,7 @@ __global__ __launch_bounds__(S::THREADS) void pgemm_kernel(GemmArgs g) {
           for (int j = 0; j < FN; ++j)
             *reinterpret_cast<f32x4*>(red + ((quad * FM + i) * FN + j) * 256 + lane * 4) = acc[i][j];
       }
+      wait_lgkm0();   // slice r's sums are in LDS before wave set 0 reads them
       bar();
       if (ks == 0) {
 #pragma unroll
@@ -238,6 +239,7 @@ __global__ __launch_bounds__(S::THREADS) void pgemm_kernel(GemmArgs g) {
       }
     }
   }
+  wait_lgkm0();   // the staged tile is in LDS before other waves read it back
   bar();
   // beta times the value held in the prefetched planes h, added to v
   auto add_planes = [&](const uint2 (&h)[PP], float (&v)[4]) {

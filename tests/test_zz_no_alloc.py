@@ -87,3 +87,50 @@ def test_noalloc_rejects_a_problem_beyond_its_scratch(lact):
                                         None, None, None, a, None)
     assert st == lact.ERR_WORKSPACE_TOO_SMALL
     assert "LACT_NOALLOC_SCRATCH_BYTES" in lact.last_error()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("cid,n,L,chunk", [(2, 2, 1736, 512), (3, 2, 2348, 1024)])
+def test_noalloc_replays_in_a_hip_graph(lact, cid, n, L, chunk):
+    """The callers the allocation-free entry point is for may capture it: a
+    HIP graph of one call (the 3B-LM shape forks its orthogonalisation to the
+    helper streams and joins them) replays three times, with eager work and
+    synchronisations between the replays, each bitwise equal to the
+    workspace entry point's eager call."""
+    wl = W.WORKLOADS[cid].scaled(n_inst=n, L=L, chunk=chunk)
+    inp, dev = _inputs(wl, seed=41 + cid)
+    Wa, Ma = _state(inp, wl)
+    oa = torch.zeros_like(dev["q"])
+    lact.layer_forward(dev["q"], dev["k"], dev["v"], dev["lr"], dev["beta"], *Wa, *Ma, oa, order=wl.order,
+                       opt=wl.opt, bounds=list(wl.bounds), flags=list(wl.flags), rec_planes=wl.rec_planes)
+    W0, _ = _state(inp, wl)
+    Wb, Mb = _state(inp, wl)
+    ob = torch.zeros_like(dev["q"])
+
+    def call():
+        for w, w0 in zip(Wb, W0):
+            w.copy_(w0)
+        for m in Mb:
+            if m is not None:
+                m.zero_()
+        _noalloc(lact, wl, dev, Wb, Mb, ob)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        ob.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ob, oa), rep
+        for x, y in zip(Wa + Ma, Wb + Mb):
+            if x is not None:
+                assert torch.equal(x, y), rep
+        _ = float((ob.float() * 2).sum())   # eager work between replays
+    log(f"  noalloc cfg{cid}: 3 graph replays equal the workspace entry point")
